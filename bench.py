@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the VDA forward pass on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 768p_bf16]
+
+A step is one whole forward pass (frame statistics, text state, solve,
+bidirectional scan, gather, readout with RMSNorm and the sigmoid gate; plus
+prep for the long-clip workload) over one batch of seeded synthetic input
+already resident in HBM.  Prints one JSON line.  Per-stage kernel times come
+from HIP events that the library records on the launch stream between its
+kernels; the dominant stage is priced against the HBM roofline with its
+algorithmic bytes.  The oracle's time on a bounded sample of the same workload
+is reported as the CPU baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "VDA fwd+rev scan+readout frames/s & tokens/s per GPU; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+STAGE_SOURCES = {"gram": "vda_gram.hip", "gram_text": "vda_gram.hip", "solve": "vda_solve.hip",
+                 "scan": "vda_scan.hip", "gather": "vda_scan.hip", "readout": "vda_readout.hip",
+                 "prep": "vda_prep.hip"}
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (events on the launch stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, ctypes.c_void_p(stream)) == 0
+
+    def elapsed(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.lib.hipEventSynchronize(b) == 0
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+
+def algorithmic_bytes(w, stage: str) -> int:
+    """Bytes a stage must move at minimum for one launch (inputs read once, outputs written once)."""
+    esz = 2 if w.dtype == "bf16" else 4
+    tok = w.B * w.T * w.U * w.H          # token-heads
+    if stage == "gram":                  # K_t, V_t and beta_t of frames 1..T-2
+        n = w.B * max(w.T - 2, 0) * w.U * w.H
+        return n * (2 * w.d + 1) * esz
+    if stage == "readout":               # Q and the gate logits in, O out
+        return tok * 3 * w.d * esz
+    if stage == "prep":                  # Q, K, V in; Q^, K^, V^ out
+        return tok * 6 * w.d * esz
+    return 0
+
+
+def job_bytes(w) -> int:
+    """Whole-job algorithmic bytes: Q, K, V, gate, beta, alpha and text in; O out."""
+    esz = 2 if w.dtype == "bf16" else 4
+    tok = w.B * w.T * w.U * w.H
+    n = tok * (5 * w.d + 1) * esz + w.B * w.T * w.H * w.d * 4 + w.B * w.L * w.H * (2 * w.d + 1) * esz
+    return n + (tok * 6 * w.d * esz if w.prep else 0)
+
+
+def _sha(stage):
+    p = os.path.join(ROOT, "frame_wise_delta_02_amd", "csrc", STAGE_SOURCES[stage])
+    return hashlib.sha1(open(p, "rb").read()).hexdigest()[:12]
+
+
+def traffic_for(stage: str, workload: str):
+    """Measured HBM bytes per launch from the committed counter summary, if still current."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p)).get(f"{workload}:{stage}")
+    if not rec or rec.get("source_sha") != _sha(stage):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(x, w, budget_s: float):
+    """The oracle, as it stands, on whole heads of the same inputs until the budget is spent."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    wid = lambda a: oracle.widen_bf16_bits(a) if a.dtype == np.uint16 else a.astype(np.float64)
+    t0 = time.perf_counter()
+    heads = 0
+    for h in range(w.H):
+        sl = [h]
+        f = {k: wid(x[k][:, :, :, sl]) for k in ("q", "k", "v", "gate")}
+        if w.prep:
+            ws = lambda n: x[n][h * w.d:(h + 1) * w.d].astype(np.float64)
+            f["q"][0], f["k"][0], f["v"][0] = oracle.prep(f["q"][0], f["k"][0], f["v"][0], ws("wk_s"), ws("wk_t"),
+                                                          ws("wv_s"), ws("wv_t"), w.grid_h, w.grid_w)
+        oracle.forward(f["q"], f["k"], f["v"], x["alpha"][:, :, sl].astype(np.float64),
+                       wid(x["beta"][:, :, :, sl]), wid(x["k_text"][:, :, sl]), wid(x["v_text"][:, :, sl]),
+                       wid(x["beta_text"][:, :, sl]), gate=f["gate"], chunk=w.chunk)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    full = el * w.H / heads
+    return {"value": round(w.B * w.T / full, 4), "unit": "frames/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of {w.H} heads, all {w.T} frames x {w.U} tokens, {el:.1f} s; "
+                      f"scaled to the whole {w.H}-head job ({full:.1f} s)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="768p_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget; 0 skips it")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (VDA heads never "
+              f"interact, so a multi-GPU run is head-sharded with no communication inside VDA).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from frame_wise_delta_02_amd import binding as bd
+    from frame_wise_delta_02_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    x = synth.make_inputs(w)
+    t_gen = time.perf_counter() - t_gen
+    torch.cuda.set_device(0)
+
+    def dev(a):
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 else torch.from_numpy(a)
+        return t.to("cuda")
+
+    d = {k: dev(v) for k, v in x.items()}
+    desc = bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L, w.chunk, w.dtype, True)
+    ws = torch.empty(bd.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["q"])
+    if w.prep:
+        qh, kh, vh = (torch.empty_like(d[k]) for k in ("q", "k", "v"))
+    grid = (w.grid_h, w.grid_w)
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = Hip()
+
+    def prep_call():
+        st = bd.lib().vdn_vda_prepare(ctypes.byref(bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L,
+                                                                w.chunk, w.dtype, False)),
+                                      *[ctypes.c_void_p(t.data_ptr()) for t in
+                                        (d["q"], d["k"], d["v"], d["wk_s"], d["wk_t"], d["wv_s"], d["wv_t"],
+                                         qh, kh, vh)], ctypes.c_void_p(stream))
+        if st != bd.VDN_OK:
+            raise bd.VdaError(st, "vdn_vda_prepare")
+
+    def step():
+        q, k, v = (qh, kh, vh) if w.prep else (d["q"], d["k"], d["v"])
+        if w.prep:
+            prep_call()
+        bd.forward(q, k, v, d["alpha"], d["beta"], d["k_text"], d["v_text"], d["beta_text"], d["gate"], None,
+                   grid=grid, chunk=w.chunk, epilogue=True, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps -----------------------------------
+    e0, e1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    hip.record(e0, stream)
+    for _ in range(args.steps):
+        step()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = hip.elapsed(e0, e1) / args.steps
+
+    # ---- per-stage kernel times (HIP events between the library's kernels) --
+    n_st = len(bd.STAGES)
+    sets = [[hip.event() for _ in range(n_st + 1)] for _ in range(args.steps)]
+    pe0, pe1 = hip.event(), hip.event()
+    prep_ms = []
+    for evs in sets:
+        if w.prep:
+            hip.record(pe0, stream)
+            prep_call()
+            hip.record(pe1, stream)
+        bd.set_profile_events([e.value for e in evs])
+        step_q = (qh, kh, vh) if w.prep else (d["q"], d["k"], d["v"])
+        bd.forward(*step_q, d["alpha"], d["beta"], d["k_text"], d["v_text"], d["beta_text"], d["gate"], None,
+                   grid=grid, chunk=w.chunk, epilogue=True, out=out, workspace=ws)
+        bd.set_profile_events(None)
+        if w.prep:
+            prep_ms.append(hip.elapsed(pe0, pe1))
+    torch.cuda.synchronize()
+    stages = {name: 0.0 for name in bd.STAGES}
+    for evs in sets:
+        for i, name in enumerate(bd.STAGES):
+            stages[name] += hip.elapsed(evs[i], evs[i + 1]) / args.steps
+    if w.prep:
+        stages["prep"] = sum(prep_ms) / len(prep_ms)
+
+    dom = max(("gram", "readout", "prep") if w.prep else ("gram", "readout"), key=lambda s: stages[s])
+    ach = algorithmic_bytes(w, dom) / (stages[dom] * 1e-3) / 1e9
+    traffic = traffic_for(dom, w.name)
+    frames = w.B * w.T
+    rec = {
+        "metric": METRIC,
+        "value": round(frames / (ms * 1e-3), 2),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "U": w.U,
+                   "grid": f"{w.grid_h}x{w.grid_w}", "d": w.d, "text_tokens": w.L, "chunk": w.chunk,
+                   "state": "f32", "prep": w.prep},
+        "tokens_per_s": round(frames * w.U / (ms * 1e-3), 1),
+        "job_roofline": {"bound": "hbm", "algorithmic_bytes": job_bytes(w),
+                         "achieved_GBs": round(job_bytes(w) / (ms * 1e-3) / 1e9, 1),
+                         "frac": round(job_bytes(w) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": algorithmic_bytes(w, dom),
+                     "launch_ms": round(stages[dom], 4)},
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "wall_s_timed": round(wall, 3),
+        "input_gen_s": round(t_gen, 1),
+    }
+    if args.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(x, w, args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

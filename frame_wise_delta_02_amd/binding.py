@@ -1,0 +1,198 @@
+"""ctypes binding of the VDA C ABI (include/vdn_vda.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the computation runs in the HIP kernels of
+libvdn_vda.so.  A missing library is an error: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libvdn_vda.so")
+
+VDN_OK, VDN_ERR_INVALID_ARG, VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE, VDN_ERR_ALIGNMENT, VDN_ERR_HIP = range(6)
+VDN_F32, VDN_BF16 = 0, 1
+VDN_VDA_EPILOGUE = 1 << 0
+VDN_VDA_DEBUG_KEEP = 1 << 1
+
+EXPORTS = ("vdn_vda_validate", "vdn_vda_workspace_bytes", "vdn_vda_workspace_layout",
+           "vdn_vda_prepare", "vdn_vda_forward", "vdn_vda_set_profile_events",
+           "vdn_vda_status_string")
+STAGES = ("gram", "gram_text", "solve", "scan", "gather", "readout")
+
+
+class VdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32),
+                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("n_text", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("dtype", ctypes.c_int), ("flags", ctypes.c_uint32),
+                ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("stats", "pinv", "s_text", "fwd", "rev", "readout_states", "total")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m frame_wise_delta_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, sz = ctypes.c_void_p, ctypes.c_size_t
+        dp = ctypes.POINTER(Desc)
+        L.vdn_vda_validate.argtypes = [dp]
+        L.vdn_vda_validate.restype = ctypes.c_int
+        L.vdn_vda_workspace_bytes.argtypes = [dp]
+        L.vdn_vda_workspace_bytes.restype = sz
+        L.vdn_vda_workspace_layout.argtypes = [dp, ctypes.POINTER(Layout)]
+        L.vdn_vda_workspace_layout.restype = ctypes.c_int
+        L.vdn_vda_prepare.argtypes = [dp] + [p] * 11
+        L.vdn_vda_prepare.restype = ctypes.c_int
+        L.vdn_vda_forward.argtypes = [dp] + [p] * 12 + [sz, p]
+        L.vdn_vda_forward.restype = ctypes.c_int
+        L.vdn_vda_set_profile_events.argtypes = [p, ctypes.c_int]
+        L.vdn_vda_set_profile_events.restype = ctypes.c_int
+        L.vdn_vda_status_string.argtypes = [ctypes.c_int]
+        L.vdn_vda_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().vdn_vda_status_string(status).decode()
+
+
+def make_desc(B, H, T, grid_h, grid_w, d, n_text, chunk=5, dtype="bf16", epilogue=True,
+              l2_eps=1e-6, rms_eps=1e-6, flags=None) -> Desc:
+    f = (VDN_VDA_EPILOGUE if epilogue else 0) if flags is None else flags
+    dt = {"bf16": VDN_BF16, "f32": VDN_F32}.get(dtype, dtype)
+    return Desc(B, H, T, grid_h, grid_w, d, d, n_text, chunk, dt, f, l2_eps, rms_eps)
+
+
+def validate(desc: Desc) -> int:
+    return lib().vdn_vda_validate(ctypes.byref(desc))
+
+
+def workspace_bytes(desc: Desc) -> int:
+    return lib().vdn_vda_workspace_bytes(ctypes.byref(desc))
+
+
+def workspace_layout(desc: Desc) -> Layout:
+    out = Layout()
+    st = lib().vdn_vda_workspace_layout(ctypes.byref(desc), ctypes.byref(out))
+    if st != VDN_OK:
+        raise VdaError(st, "vdn_vda_workspace_layout")
+    return out
+
+
+def set_profile_events(handles):
+    """Install hipEvent_t handles (ints) for per-stage timing, or None to clear."""
+    if handles is None:
+        st = lib().vdn_vda_set_profile_events(None, 0)
+        set_profile_events._keep = None
+    else:
+        arr = (ctypes.c_void_p * len(handles))(*handles)
+        set_profile_events._keep = arr
+        st = lib().vdn_vda_set_profile_events(ctypes.cast(arr, ctypes.c_void_p), len(handles))
+    if st != VDN_OK:
+        raise VdaError(st, "vdn_vda_set_profile_events")
+
+
+# ----------------------------------------------------------------------------
+# torch marshalling
+# ----------------------------------------------------------------------------
+
+
+def _ptr(x):
+    return None if x is None else ctypes.c_void_p(x.data_ptr())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_of(x) -> str:
+    import torch
+    if x.dtype == torch.bfloat16:
+        return "bf16"
+    if x.dtype == torch.float32:
+        return "f32"
+    raise TypeError(f"unsupported dtype {x.dtype}")
+
+
+def _check(x, name, dev):
+    if x is None:
+        return
+    if not x.is_cuda or x.device != dev:
+        raise ValueError(f"{name} must be on {dev}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weight=None, *,
+            grid, chunk=5, epilogue=True, rms_eps=1e-6, out=None, workspace=None):
+    """VDA forward on prepared features; returns ``out`` [B, T, U, H, d].
+
+    Shapes as in include/vdn_vda.h.  ``grid`` = (grid_h, grid_w) with
+    grid_h * grid_w = U.  ``workspace`` (uint8, on the device) is allocated
+    when not given.
+    """
+    import torch
+    B, T, U, H, d = q.shape
+    L = 0 if k_text is None else k_text.shape[1]
+    dt = _dtype_of(q)
+    dev = q.device
+    for name, x in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta),
+                    ("k_text", k_text), ("v_text", v_text), ("beta_text", beta_text),
+                    ("gate", gate), ("rms_weight", rms_weight), ("out", out), ("workspace", workspace)):
+        _check(x, name, dev)
+    desc = make_desc(B, H, T, grid[0], grid[1], d, L, chunk, dt, epilogue, rms_eps=rms_eps)
+    st = validate(desc)
+    if st != VDN_OK:
+        raise VdaError(st, "vdn_vda_validate")
+    if out is None:
+        out = torch.empty((B, T, U, H, d), dtype=q.dtype, device=dev)
+    need = workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib().vdn_vda_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                               _ptr(k_text), _ptr(v_text), _ptr(beta_text),
+                               _ptr(gate) if epilogue else None, _ptr(rms_weight), _ptr(out),
+                               _ptr(workspace), workspace.numel(), _stream())
+    if st != VDN_OK:
+        raise VdaError(st, "vdn_vda_forward")
+    return out
+
+
+def prepare(q, k, v, wk_s, wk_t, wv_s, wv_t, *, grid, l2_eps=1e-6, n_text=0, chunk=5):
+    """Feature prep (conv, SiLU, L2); returns (q_hat, k_hat, v_hat)."""
+    import torch
+    B, T, U, H, d = q.shape
+    dev = q.device
+    for name, x in (("q", q), ("k", k), ("v", v), ("wk_s", wk_s), ("wk_t", wk_t),
+                    ("wv_s", wv_s), ("wv_t", wv_t)):
+        _check(x, name, dev)
+    desc = make_desc(B, H, T, grid[0], grid[1], d, n_text, chunk, _dtype_of(q), False, l2_eps=l2_eps)
+    q_hat, k_hat, v_hat = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = lib().vdn_vda_prepare(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(wk_s), _ptr(wk_t),
+                               _ptr(wv_s), _ptr(wv_t), _ptr(q_hat), _ptr(k_hat), _ptr(v_hat), _stream())
+    if st != VDN_OK:
+        raise VdaError(st, "vdn_vda_prepare")
+    return q_hat, k_hat, v_hat

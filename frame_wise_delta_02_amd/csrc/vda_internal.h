@@ -1,0 +1,71 @@
+// Internal declarations shared by the VDA HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vdn_vda.h"
+
+namespace vda {
+
+// ---------------------------------------------------------------------------
+// vector types for the gfx950 matrix-core builtins
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Two floats -> two bfloat16 (round to nearest even), packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Split x into hi + lo, both bfloat16: hi = bf16(x), lo = bf16(x - hi).
+// hi + lo carries about 16 significant bits of x.
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
+}
+
+// ---------------------------------------------------------------------------
+// launch plumbing
+// ---------------------------------------------------------------------------
+struct Problem {
+  int B, H, T, U, D, L, C;  // d_k = d_v = D; C = frames per chunk
+  int nc;                   // number of chunks
+  bool bf16;
+  bool epilogue;
+  float l2_eps, rms_eps;
+};
+
+// Workspace offsets in bytes (see vdn_vda_layout).
+struct Layout {
+  size_t stats, pinv, s_text, fwd, rev, rstates, total;
+};
+Layout make_layout(const Problem& p);
+
+// Bytes of one readout state slot in the readout kernel's packed format.
+size_t readout_slot_bytes(const Problem& p);
+
+// Kernels are launched through these; each returns hipGetLastError().
+hipError_t launch_gram(const Problem& p, const void* k, const void* v, const void* beta,
+                       int T_in, int U_in, int t_first, int n_frames, int slot_offset,
+                       float* stats, hipStream_t s);
+hipError_t launch_solve(const Problem& p, const float* stats, float* pinv, hipStream_t s);
+hipError_t launch_scan(const Problem& p, const float* stats, const float* pinv, const float* alpha,
+                       float* s_text, float* fwd, float* rev, hipStream_t s);
+hipError_t launch_gather(const Problem& p, const float* s_text, const float* fwd, const float* rev,
+                         void* rstates, hipStream_t s);
+hipError_t launch_readout(const Problem& p, const void* q, const void* gate, const float* rms_weight,
+                          const void* rstates, void* out, hipStream_t s);
+hipError_t launch_prep(const Problem& p, int grid_h, int grid_w, const void* q, const void* k,
+                       const void* v, const float* wk_s, const float* wk_t, const float* wv_s,
+                       const float* wv_t, void* q_hat, void* k_hat, void* v_hat, hipStream_t s);
+
+}  // namespace vda

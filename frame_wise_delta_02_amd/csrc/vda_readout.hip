@@ -1,0 +1,250 @@
+// vda_readout: o = (S_fwd + S_rev) q for every token, fused with RMSNorm over d_v
+// and the elementwise sigmoid output gate.
+//
+// Readout o_t = S_t(fwd) q_t + S_t(rev) q_t ("Video DeltaNet" summary,
+// onedev.kr/papers/80, section "어떻게 동작하나"); the linear branch's output
+// then passes RMS normalisation and its own sigmoid output gate (section
+// "무엇과 다른가"; the VDN-H3 write-up, discuss.pytorch.kr, puts the
+// elementwise sigmoid gate after RMSNorm).
+//
+// Every token of a frame reads the same d_v x d_k state (its chunk's
+// F_{c-2} + R_{c+2}, or S_T for the two anchor frames), packed beforehand into
+// matrix-core operand order by the gather kernel.  A workgroup stages that state
+// in LDS once and streams the frame's tokens in 32-token tiles, one tile per wave
+// at a time, computing O^T = S Q^T on 32x32 matrix-core tiles:
+//   * B operand = Q^T: each lane holds 8 channels of one token, read straight
+//     from global memory as 16-byte loads (no LDS round trip for Q);
+//   * A operand = S, with its rows permuted so that after the product each lane
+//     holds d_v/2 *consecutive* outputs of one token.  RMSNorm is then a sum in
+//     registers plus one cross-half lane swap, and the gate load and the output
+//     store are contiguous 16-byte accesses.
+// bfloat16 path: S = S_hi + S_lo (two bf16 parts, ~16 significant bits) on
+// v_mfma_f32_32x32x16_bf16, so the fp32 state is not truncated to 8 bits.
+// float32 path: v_mfma_f32_32x32x2f32 with the fp32 state.
+#include "vda_internal.h"
+
+namespace vda {
+namespace {
+
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void readout_bf16(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ G, const float* __restrict__ w,
+    const uint4* __restrict__ rstates, uint16_t* __restrict__ O, int T, int U, int H, int C,
+    int nc, int epilogue, float eps) {
+  constexpr int DP = D < 32 ? 32 : D;
+  constexpr int HALF = DP / 2;       // outputs per lane
+  constexpr int MT = DP / 32;
+  constexpr int KS = D / 16;
+  constexpr int NF = MT * KS * 64;   // 16-byte fragments per part (hi or lo)
+  constexpr int NO = HALF < D ? HALF : D;  // valid outputs for lane half 0
+  __shared__ uint4 sfrag[2 * NF];
+  __shared__ float sgam[DP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int blk = blockIdx.x;
+  const int h = blk % H;
+  blk /= H;
+  const int t = blk % T;
+  const int b = blk / T;
+  const int slot = (t == 0 || t == T - 1) ? nc : t / C;
+  const uint4* src = rstates + ((size_t)(b * H + h) * (nc + 1) + slot) * 2 * NF;
+  for (int i = tid; i < 2 * NF; i += 256) sfrag[i] = src[i];
+  for (int i = tid; i < DP; i += 256) sgam[i] = (w && i < D) ? w[i] : 1.f;
+  __syncthreads();
+
+  const int n = lane & 31, half = lane >> 5;
+  const int dv0 = HALF * half;               // first output channel of this lane
+  const int nout = (dv0 < D) ? NO : 0;       // outputs this lane owns
+
+  const size_t row_base = ((size_t)b * T + t) * (size_t)U;
+  const int ntiles = (U + 31) / 32;
+  for (int tile = wave; tile < ntiles; tile += 4) {
+    const int u = tile * 32 + n;
+    const bool valid = u < U;
+    const size_t row = ((row_base + (valid ? u : 0)) * H + h) * (size_t)D;
+    bf16x8 qv[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 x = valid ? *reinterpret_cast<const uint4*>(Q + row + (D / 2) * half + 8 * ks)
+                            : make_uint4(0, 0, 0, 0);
+      qv[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+    uint4 gv[HALF / 8];
+    if (epilogue) {
+#pragma unroll
+      for (int i = 0; i < HALF / 8; ++i)
+        gv[i] = (valid && 8 * i < nout) ? *reinterpret_cast<const uint4*>(G + row + dv0 + 8 * i)
+                                        : make_uint4(0, 0, 0, 0);
+    }
+    f32x16 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{0.f};
+    // k-step outer; the fence keeps the scheduler from hoisting every operand
+    // read of the tile at once (which would not fit the register budget)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 ahi = __builtin_bit_cast(bf16x8, sfrag[(mt * KS + ks) * 64 + lane]);
+        const bf16x8 alo = __builtin_bit_cast(bf16x8, sfrag[NF + (mt * KS + ks) * 64 + lane]);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, qv[ks], acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, qv[ks], acc[mt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // lane holds o[dv0 + 16*mt + r] of token u in acc[mt][r]; epilogue in place
+    if (epilogue) {
+      float ss = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ss += acc[mt][r] * acc[mt][r];
+      ss += __shfl_xor(ss, 32);
+      const float rinv = 1.f / __builtin_sqrtf(ss / (float)D + eps);
+#pragma unroll
+      for (int i = 0; i < HALF / 8; ++i) {
+        const uint32_t g4[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j0 = 8 * i + 2 * e, j1 = j0 + 1;
+          acc[j0 / 16][j0 % 16] *= rinv * sgam[dv0 + j0] * sigmoid(bf16_lo(g4[e]));
+          acc[j1 / 16][j1 % 16] *= rinv * sgam[dv0 + j1] * sigmoid(bf16_hi(g4[e]));
+        }
+      }
+    }
+    if (valid) {
+#pragma unroll
+      for (int i = 0; i < HALF / 8; ++i) {
+        if (8 * i < nout) {
+          const int m = (8 * i) / 16, r = (8 * i) % 16;
+          const uint4 o = make_uint4(pack_bf16x2(acc[m][r], acc[m][r + 1]), pack_bf16x2(acc[m][r + 2], acc[m][r + 3]),
+                                     pack_bf16x2(acc[m][r + 4], acc[m][r + 5]), pack_bf16x2(acc[m][r + 6], acc[m][r + 7]));
+          *reinterpret_cast<uint4*>(O + row + dv0 + 8 * i) = o;
+        }
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void readout_f32(
+    const float* __restrict__ Q, const float* __restrict__ G, const float* __restrict__ w,
+    const float4* __restrict__ rstates, float* __restrict__ O, int T, int U, int H, int C, int nc,
+    int epilogue, float eps) {
+  constexpr int DP = D < 32 ? 32 : D;
+  constexpr int HALF = DP / 2;
+  constexpr int MT = DP / 32;
+  constexpr int KQ = D / 8;         // float4 groups of k-steps (one channel per half per step)
+  constexpr int NF = MT * KQ * 64;
+  constexpr int NO = HALF < D ? HALF : D;
+  __shared__ float4 sfrag[NF];
+  __shared__ float sgam[DP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int blk = blockIdx.x;
+  const int h = blk % H;
+  blk /= H;
+  const int t = blk % T;
+  const int b = blk / T;
+  const int slot = (t == 0 || t == T - 1) ? nc : t / C;
+  const float4* src = rstates + ((size_t)(b * H + h) * (nc + 1) + slot) * NF;
+  for (int i = tid; i < NF; i += 256) sfrag[i] = src[i];
+  for (int i = tid; i < DP; i += 256) sgam[i] = (w && i < D) ? w[i] : 1.f;
+  __syncthreads();
+
+  const int n = lane & 31, half = lane >> 5;
+  const int dv0 = HALF * half;
+  const int nout = (dv0 < D) ? NO : 0;
+  const size_t row_base = ((size_t)b * T + t) * (size_t)U;
+  const int ntiles = (U + 31) / 32;
+  for (int tile = wave; tile < ntiles; tile += 4) {
+    const int u = tile * 32 + n;
+    const bool valid = u < U;
+    const size_t row = ((row_base + (valid ? u : 0)) * H + h) * (size_t)D;
+    float4 qv[KQ];
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq)
+      qv[kq] = valid ? *reinterpret_cast<const float4*>(Q + row + (D / 2) * half + 4 * kq)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    f32x16 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{0.f};
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const float4 a = sfrag[(mt * KQ + kq) * 64 + lane];
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qv[kq].x, acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qv[kq].y, acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qv[kq].z, acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qv[kq].w, acc[mt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (epilogue) {
+      float ss = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ss += acc[mt][r] * acc[mt][r];
+      ss += __shfl_xor(ss, 32);
+      const float rinv = 1.f / __builtin_sqrtf(ss / (float)D + eps);
+#pragma unroll
+      for (int i = 0; i < HALF / 4; ++i) {
+        if (4 * i < nout && valid) {
+          const float4 g = *reinterpret_cast<const float4*>(G + row + dv0 + 4 * i);
+          const float gg[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * i + e;
+            acc[j / 16][j % 16] *= rinv * sgam[dv0 + j] * sigmoid(gg[e]);
+          }
+        }
+      }
+    }
+    if (valid) {
+#pragma unroll
+      for (int i = 0; i < HALF / 4; ++i)
+        if (4 * i < nout) {
+          const int m = (4 * i) / 16, r = (4 * i) % 16;
+          *reinterpret_cast<float4*>(O + row + dv0 + 4 * i) =
+              make_float4(acc[m][r], acc[m][r + 1], acc[m][r + 2], acc[m][r + 3]);
+        }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_readout_d(const Problem& p, const void* q, const void* gate, const float* w,
+                            const void* rstates, void* out, hipStream_t s) {
+  const unsigned grid = (unsigned)(p.B * p.T * p.H);
+  const int epi = p.epilogue ? 1 : 0;
+  if (p.bf16)
+    hipLaunchKernelGGL(readout_bf16<D>, dim3(grid), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate), w,
+                       static_cast<const uint4*>(rstates), static_cast<uint16_t*>(out), p.T, p.U,
+                       p.H, p.C, p.nc, epi, p.rms_eps);
+  else
+    hipLaunchKernelGGL(readout_f32<D>, dim3(grid), dim3(256), 0, s,
+                       static_cast<const float*>(q), static_cast<const float*>(gate), w,
+                       static_cast<const float4*>(rstates), static_cast<float*>(out), p.T, p.U,
+                       p.H, p.C, p.nc, epi, p.rms_eps);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_readout(const Problem& p, const void* q, const void* gate, const float* rms_weight,
+                          const void* rstates, void* out, hipStream_t s) {
+  switch (p.D) {
+    case 16: return launch_readout_d<16>(p, q, gate, rms_weight, rstates, out, s);
+    case 32: return launch_readout_d<32>(p, q, gate, rms_weight, rstates, out, s);
+    case 64: return launch_readout_d<64>(p, q, gate, rms_weight, rstates, out, s);
+    case 128: return launch_readout_d<128>(p, q, gate, rms_weight, rstates, out, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace vda

@@ -1,0 +1,316 @@
+// vda_scan: the bidirectional frame recurrence of Video Delta Attention, and the
+// gather of the two directions' states for the readout.
+//
+// Text state: S_T = B_T (I + A_T)^{-1}, the frame update from a zero state over
+// the text tokens; both directions start from S_T / 2 so that the two readouts
+// together count the prompt once ("Video DeltaNet" summary, onedev.kr/papers/80,
+// section "어떻게 동작하나").  Each absorbed frame s applies
+//     S <- (S Diag(alpha_s) + B_s)(I + A_s)^{-1}
+// (section "어떻게 쓰나"); the reverse direction applies the same update in
+// reverse frame order.  Anchor frames (0, T-1) are never absorbed (section
+// "전제와 한계").  The forward scan records F_j after the last frame of chunk
+// j, the reverse scan R_j after the first frame of chunk j; a query in chunk c
+// reads F_{c-2} + R_{c+2} (S_T / 2 where a range is empty), so only F_0..F_{n-3}
+// and R_2..R_{n-1} are produced.
+//
+// Parallel form: S <- Y P^{-1} acts on the rows of S independently, so each
+// (batch, head, direction) is split into 16-row blocks that scan with no
+// communication at all.  A workgroup keeps its 16 x d block of Y in LDS and
+// multiplies by P^{-1}_s with v_mfma_f32_16x16x4f32 (full fp32).  Lanes read
+// P^{-1} as float2 so each lane owns two adjacent output columns; the next
+// frame's P^{-1}, B and alpha are prefetched into registers while the current
+// frame's MFMAs run.  Row blocks of one head go to the same XCD (blockIdx % 8)
+// so the P^{-1}_s they all read is shared in that XCD's L2.
+#include "vda_internal.h"
+
+namespace vda {
+namespace {
+
+constexpr int RB = 16;  // state rows per workgroup
+
+template <int D>
+__global__ __launch_bounds__(64 * (D / (D >= 32 ? 32 : 16)))
+void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
+               const float* __restrict__ alpha, float* __restrict__ s_text,
+               float* __restrict__ fwd, float* __restrict__ rev, int B, int H, int T, int C, int nc) {
+  constexpr int NV = D >= 32 ? 2 : 1;   // adjacent columns per lane
+  constexpr int WCOLS = 16 * NV;
+  constexpr int KS = D / 4;
+  constexpr int NRB = D / RB;
+  constexpr int LDY = D + 4;
+  typedef float vec_t __attribute__((ext_vector_type(NV)));
+  __shared__ __attribute__((aligned(16))) float ylds[2][RB * LDY];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // blockIdx -> (group, row block) with all row blocks of a group on one XCD
+  const int nblk = gridDim.x;
+  const int bid = blockIdx.x;
+  const int groups = B * H * 2;
+  int g, rbi;
+  if (NRB == 8 && groups % 8 == 0 && nblk == groups * NRB) {
+    const int xcd = bid % 8, slot = bid / 8;
+    rbi = slot % NRB;
+    g = (slot / NRB) * 8 + xcd;
+  } else {
+    rbi = bid % NRB;
+    g = bid / NRB;
+  }
+  if (g >= groups) return;
+  const int dir = g % 2;
+  const int h = (g / 2) % H;
+  const int b = g / (2 * H);
+  const int row0 = rbi * RB;
+
+  const size_t head = (size_t)(b * H + h);
+  const float* P0 = pinv + head * (T + 1) * (size_t)(D * D);
+  const float* S0 = stats + head * (T + 1) * (size_t)(2 * D * D) + (size_t)D * D;  // B part
+  const float* A0 = alpha + (size_t)b * T * H * D + (size_t)h * D;                 // + s*H*D
+
+  const int c0 = wave * WCOLS + NV * (lane & 15);
+  const int rr = 4 * (lane >> 4);  // first of this lane's 4 output rows
+
+  vec_t st[4];      // this lane's entries of S: rows rr..rr+3, columns c0..c0+NV-1
+  vec_t pf[KS];     // P^{-1} fragments of the frame being multiplied
+  vec_t bw[4], al;  // B rows and alpha of the frame whose Y is being formed
+
+  auto ld_p = [&](int s, vec_t (&dst)[KS]) {
+    const float* P = P0 + (size_t)s * D * D + c0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      dst[ks] = *reinterpret_cast<const vec_t*>(P + (4 * ks + (lane >> 4)) * D);
+  };
+  auto ld_bw = [&](int s, vec_t (&dst)[4]) {
+    const float* Bs = S0 + (size_t)s * 2 * D * D + (size_t)(row0 + rr) * D + c0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[r] = *reinterpret_cast<const vec_t*>(Bs + r * D);
+  };
+  auto ld_al = [&](int s) -> vec_t {
+    return *reinterpret_cast<const vec_t*>(A0 + (size_t)s * H * D + c0);
+  };
+  // Y = S Diag(alpha) + B into ylds[buf] (alpha = 0 for the text frame)
+  auto put_y = [&](int buf, const vec_t (&sv)[4], vec_t a, const vec_t (&bv)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      *reinterpret_cast<vec_t*>(&ylds[buf][(rr + r) * LDY + c0]) = sv[r] * a + bv[r];
+  };
+  // S = Y P^{-1} from ylds[buf]
+  auto mul = [&](int buf, const vec_t (&p)[KS]) {
+    f32x4 acc[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float* yrow = &ylds[buf][(lane & 15) * LDY + (lane >> 4)];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float a = yrow[4 * ks];
+#pragma unroll
+      for (int e = 0; e < NV; ++e)
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, p[ks][e], acc[e], 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < NV; ++e) st[r][e] = acc[e][r];
+  };
+  auto put_state = [&](float* dst) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      *reinterpret_cast<vec_t*>(dst + (size_t)(row0 + rr + r) * D + c0) = st[r];
+  };
+
+  // ---- text frame (slot T): S_T = B_T P_T^{-1} -------------------------------
+  vec_t zero4[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) zero4[r] = vec_t(0.f);
+  ld_bw(T, bw);
+  ld_p(T, pf);
+  put_y(0, zero4, vec_t(0.f), bw);
+  __syncthreads();
+  mul(0, pf);
+  if (dir == 0) put_state(s_text + head * (size_t)(D * D));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) st[r] *= 0.5f;
+
+  // ---- frame list of this direction ------------------------------------------
+  // forward: frames 1 .. min(C*(nc-2)-1, T-2); reverse: T-2 .. max(2C, 1)
+  int first, last, step;
+  if (dir == 0) {
+    first = 1;
+    last = nc >= 3 ? min(C * (nc - 2) - 1, T - 2) : 0;
+    step = 1;
+  } else {
+    first = T - 2;
+    last = nc >= 3 ? max(2 * C, 1) : T - 1;
+    step = -1;
+  }
+  const int nsteps = (dir == 0) ? max(0, last - first + 1) : max(0, first - last + 1);
+  float* out0 = (dir == 0 ? fwd : rev) + head * (size_t)nc * D * D;
+
+  // the record index after absorbing frame s (or -1)
+  auto rec_after = [&](int s) -> int {
+    if (dir == 0) {
+      const int j = s / C;  // F_j after the last absorbed frame of chunk j
+      const bool end = (s == min(C * (j + 1) - 1, T - 2));
+      return (end && j <= nc - 3) ? j : -1;
+    }
+    const int j = s / C;    // R_j after the first absorbed frame of chunk j
+    const bool beg = (s == max(C * j, 1));
+    return (beg && j >= 2) ? j : -1;
+  };
+  // chunks whose recorded state precedes every absorbed frame (empty coverage)
+  if (dir == 0) {
+    for (int j = 0; j <= nc - 3; ++j)
+      if (min(C * (j + 1) - 1, T - 2) < 1) put_state(out0 + (size_t)j * D * D);
+  } else {
+    for (int j = nc - 1; j >= 2; --j)
+      if (max(C * j, 1) > T - 2) put_state(out0 + (size_t)j * D * D);
+  }
+
+  if (nsteps > 0) {
+    int s = first;
+    ld_bw(s, bw);
+    al = ld_al(s);
+    ld_p(s, pf);
+    int buf = 1;
+    for (int i = 0; i < nsteps; ++i, s += step) {
+      put_y(buf, st, al, bw);
+      vec_t pn[KS], bn[4], an;
+      const bool more = i + 1 < nsteps;
+      if (more) {
+        ld_p(s + step, pn);
+        ld_bw(s + step, bn);
+        an = ld_al(s + step);
+      }
+      __syncthreads();
+      mul(buf, pf);
+      const int j = rec_after(s);
+      if (j >= 0) put_state(out0 + (size_t)j * D * D);
+      if (more) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) pf[ks] = pn[ks];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bw[r] = bn[r];
+        al = an;
+      }
+      buf ^= 1;
+    }
+  }
+}
+
+// Readout states: slot c < nc holds F_{c-2} + R_{c+2} (S_T/2 for a missing side),
+// slot nc holds S_T (anchor frames).  Written in the readout kernel's operand
+// order (see vda_readout.hip): for every (m-tile, k-step, lane) the lane's
+// matrix-core A-operand.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void gather_states(const float* __restrict__ s_text,
+                                                     const float* __restrict__ fwd,
+                                                     const float* __restrict__ rev,
+                                                     void* __restrict__ rstates, int nc) {
+  constexpr int DP = D < 32 ? 32 : D;
+  constexpr int HALF = DP / 2;
+  constexpr int MT = DP / 32;
+  const int slot = blockIdx.x % (nc + 1);
+  const size_t head = blockIdx.x / (nc + 1);
+  const float* ST = s_text + head * D * D;
+  const float* Fp = nullptr;
+  const float* Rp = nullptr;
+  if (slot < nc) {
+    if (slot >= 2) Fp = fwd + (head * nc + (slot - 2)) * D * D;
+    if (slot + 2 <= nc - 1) Rp = rev + (head * nc + (slot + 2)) * D * D;
+  }
+  auto value = [&](int dv, int ch) -> float {
+    if (dv >= D) return 0.f;
+    const size_t i = (size_t)dv * D + ch;
+    if (slot == nc) return ST[i];
+    const float f = Fp ? Fp[i] : 0.5f * ST[i];
+    const float r = Rp ? Rp[i] : 0.5f * ST[i];
+    return f + r;
+  };
+  auto dv_of = [&](int mt, int m) { return HALF * ((m >> 2) & 1) + 16 * mt + 4 * (m >> 3) + (m & 3); };
+
+  if constexpr (BF16) {
+    constexpr int KS = D / 16;
+    constexpr int NF = MT * KS * 64;  // fragments per half (hi or lo)
+    uint4* out = static_cast<uint4*>(rstates) + (size_t)blockIdx.x * 2 * NF;
+    for (int f = threadIdx.x; f < NF; f += blockDim.x) {
+      const int lane = f % 64, ks = (f / 64) % KS, mt = f / (64 * KS);
+      const int dv = dv_of(mt, lane & 31);
+      const int ch0 = (D / 2) * (lane >> 5) + 8 * ks;
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        __bf16 h0, l0, h1, l1;
+        split_bf16(value(dv, ch0 + 2 * e), h0, l0);
+        split_bf16(value(dv, ch0 + 2 * e + 1), h1, l1);
+        hi[e] = __builtin_bit_cast(uint32_t, bf16x2{h0, h1});
+        lo[e] = __builtin_bit_cast(uint32_t, bf16x2{l0, l1});
+      }
+      out[f] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      out[NF + f] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+  } else {
+    constexpr int KQ = D / 8;  // groups of 4 k-steps (32x32x2: one channel per half per step)
+    constexpr int NF = MT * KQ * 64;
+    float4* out = static_cast<float4*>(rstates) + (size_t)blockIdx.x * NF;
+    for (int f = threadIdx.x; f < NF; f += blockDim.x) {
+      const int lane = f % 64, kq = (f / 64) % KQ, mt = f / (64 * KQ);
+      const int dv = dv_of(mt, lane & 31);
+      const int ch0 = (D / 2) * (lane >> 5) + 4 * kq;
+      out[f] = make_float4(value(dv, ch0), value(dv, ch0 + 1), value(dv, ch0 + 2), value(dv, ch0 + 3));
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_scan_d(const Problem& p, const float* stats, const float* pinv,
+                         const float* alpha, float* s_text, float* fwd, float* rev, hipStream_t s) {
+  constexpr int NV = D >= 32 ? 2 : 1;
+  constexpr int threads = 64 * (D / (16 * NV));
+  const unsigned grid = (unsigned)(p.B * p.H * 2 * (D / RB));
+  hipLaunchKernelGGL(scan_rows<D>, dim3(grid), dim3(threads), 0, s, stats, pinv, alpha, s_text,
+                     fwd, rev, p.B, p.H, p.T, p.C, p.nc);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_gather_d(const Problem& p, const float* s_text, const float* fwd,
+                           const float* rev, void* rstates, hipStream_t s) {
+  const unsigned grid = (unsigned)(p.B * p.H * (p.nc + 1));
+  if (p.bf16)
+    hipLaunchKernelGGL((gather_states<D, true>), dim3(grid), dim3(256), 0, s, s_text, fwd, rev, rstates, p.nc);
+  else
+    hipLaunchKernelGGL((gather_states<D, false>), dim3(grid), dim3(256), 0, s, s_text, fwd, rev, rstates, p.nc);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t readout_slot_bytes(const Problem& p) {
+  const int DP = p.D < 32 ? 32 : p.D;
+  const int MT = DP / 32;
+  if (p.bf16) return (size_t)2 * MT * (p.D / 16) * 64 * 16;
+  return (size_t)MT * (p.D / 8) * 64 * 16;
+}
+
+hipError_t launch_scan(const Problem& p, const float* stats, const float* pinv, const float* alpha,
+                       float* s_text, float* fwd, float* rev, hipStream_t s) {
+  switch (p.D) {
+    case 16: return launch_scan_d<16>(p, stats, pinv, alpha, s_text, fwd, rev, s);
+    case 32: return launch_scan_d<32>(p, stats, pinv, alpha, s_text, fwd, rev, s);
+    case 64: return launch_scan_d<64>(p, stats, pinv, alpha, s_text, fwd, rev, s);
+    case 128: return launch_scan_d<128>(p, stats, pinv, alpha, s_text, fwd, rev, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gather(const Problem& p, const float* s_text, const float* fwd, const float* rev,
+                         void* rstates, hipStream_t s) {
+  switch (p.D) {
+    case 16: return launch_gather_d<16>(p, s_text, fwd, rev, rstates, s);
+    case 32: return launch_gather_d<32>(p, s_text, fwd, rev, rstates, s);
+    case 64: return launch_gather_d<64>(p, s_text, fwd, rev, rstates, s);
+    case 128: return launch_gather_d<128>(p, s_text, fwd, rev, rstates, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace vda

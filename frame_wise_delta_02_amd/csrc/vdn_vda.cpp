@@ -1,0 +1,202 @@
+// Host side of the C ABI: descriptor validation, workspace layout and the launch
+// sequence of the VDA forward pass on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "vda_internal.h"
+#include "vdn_vda.h"
+
+namespace vda {
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+hipEvent_t* g_events = nullptr;  // profiling hook (vdn_vda_set_profile_events)
+
+hipError_t mark(int i, hipStream_t s) {
+  return g_events ? hipEventRecord(g_events[i], s) : hipSuccess;
+}
+
+vdn_status check(const vdn_vda_desc* d) {
+  if (!d) return VDN_ERR_INVALID_ARG;
+  if (d->B < 1 || d->H < 1 || d->T < 1 || d->grid_h < 1 || d->grid_w < 1) return VDN_ERR_INVALID_ARG;
+  if (d->d_k < 1 || d->d_v < 1 || d->d_k > 128 || d->d_v > 128) return VDN_ERR_INVALID_ARG;
+  if (d->d_k % 16 || d->d_v % 16) return VDN_ERR_INVALID_ARG;
+  if (d->n_text < 0 || d->chunk < 1) return VDN_ERR_INVALID_ARG;
+  if (d->dtype != VDN_F32 && d->dtype != VDN_BF16) return VDN_ERR_INVALID_ARG;
+  if (d->flags & ~(uint32_t)(VDN_VDA_EPILOGUE | VDN_VDA_DEBUG_KEEP)) return VDN_ERR_INVALID_ARG;
+  if (!(d->l2_eps > 0.f) || !isfinite(d->l2_eps)) return VDN_ERR_INVALID_ARG;
+  if (!(d->rms_eps > 0.f) || !isfinite(d->rms_eps)) return VDN_ERR_INVALID_ARG;
+  // sizes must stay well inside 64-bit element counts and 32-bit grid dimensions
+  const double U = (double)d->grid_h * d->grid_w;
+  const double elems = (double)d->B * d->T * U * d->H * d->d_v;
+  if (U > 2147483647.0 || elems > 9.0e15) return VDN_ERR_INVALID_ARG;
+  if ((double)d->B * d->T * d->H * d->grid_h > 4294967295.0) return VDN_ERR_INVALID_ARG;
+  if ((double)d->B * d->n_text * d->H > 9.0e15) return VDN_ERR_INVALID_ARG;
+  if (d->d_k != d->d_v) return VDN_ERR_UNSUPPORTED;
+  if (d->d_k != 16 && d->d_k != 32 && d->d_k != 64 && d->d_k != 128) return VDN_ERR_UNSUPPORTED;
+  return VDN_OK;
+}
+
+Problem problem(const vdn_vda_desc* d) {
+  Problem p;
+  p.B = d->B;
+  p.H = d->H;
+  p.T = d->T;
+  p.U = d->grid_h * d->grid_w;
+  p.D = d->d_k;
+  p.L = d->n_text;
+  p.C = d->chunk;
+  p.nc = (d->T + d->chunk - 1) / d->chunk;
+  p.bf16 = d->dtype == VDN_BF16;
+  p.epilogue = (d->flags & VDN_VDA_EPILOGUE) != 0;
+  p.l2_eps = d->l2_eps;
+  p.rms_eps = d->rms_eps;
+  return p;
+}
+
+}  // namespace
+
+Layout make_layout(const Problem& p) {
+  const size_t heads = (size_t)p.B * p.H;
+  const size_t dd = (size_t)p.D * p.D * sizeof(float);
+  Layout l;
+  size_t o = 0;
+  l.stats = o;
+  o = up(o + heads * (p.T + 1) * 2 * dd);
+  l.pinv = o;
+  o = up(o + heads * (p.T + 1) * dd);
+  l.s_text = o;
+  o = up(o + heads * dd);
+  l.fwd = o;
+  o = up(o + heads * p.nc * dd);
+  l.rev = o;
+  o = up(o + heads * p.nc * dd);
+  l.rstates = o;
+  o = up(o + heads * (p.nc + 1) * readout_slot_bytes(p));
+  l.total = o;
+  return l;
+}
+
+}  // namespace vda
+
+using namespace vda;
+
+extern "C" {
+
+vdn_status vdn_vda_validate(const vdn_vda_desc* d) { return check(d); }
+
+size_t vdn_vda_workspace_bytes(const vdn_vda_desc* d) {
+  if (check(d) != VDN_OK) return 0;
+  return make_layout(problem(d)).total;
+}
+
+vdn_status vdn_vda_workspace_layout(const vdn_vda_desc* d, vdn_vda_layout* out) {
+  const vdn_status st = check(d);
+  if (st != VDN_OK) return st;
+  if (!out) return VDN_ERR_INVALID_ARG;
+  const Layout l = make_layout(problem(d));
+  out->stats = l.stats;
+  out->pinv = l.pinv;
+  out->s_text = l.s_text;
+  out->fwd = l.fwd;
+  out->rev = l.rev;
+  out->readout_states = l.rstates;
+  out->total = l.total;
+  return VDN_OK;
+}
+
+vdn_status vdn_vda_prepare(const vdn_vda_desc* d, const void* q, const void* k, const void* v,
+                           const float* wk_s, const float* wk_t, const float* wv_s,
+                           const float* wv_t, void* q_hat, void* k_hat, void* v_hat,
+                           hipStream_t stream) {
+  const vdn_status st = check(d);
+  if (st != VDN_OK) return st;
+  const void* ptrs[] = {q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat};
+  for (const void* p : ptrs)
+    if (!p) return VDN_ERR_INVALID_ARG;
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return VDN_ERR_ALIGNMENT;
+  if (q_hat == q || k_hat == k || v_hat == v || q_hat == k_hat || q_hat == v_hat || k_hat == v_hat)
+    return VDN_ERR_INVALID_ARG;
+  const Problem p = problem(d);
+  if (launch_prep(p, d->grid_h, d->grid_w, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat,
+                  stream) != hipSuccess)
+    return VDN_ERR_HIP;
+  return VDN_OK;
+}
+
+vdn_status vdn_vda_forward(const vdn_vda_desc* d, const void* q, const void* k, const void* v,
+                           const float* alpha, const void* beta, const void* k_text,
+                           const void* v_text, const void* beta_text, const void* gate,
+                           const float* rms_weight, void* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  const vdn_status st = check(d);
+  if (st != VDN_OK) return st;
+  const bool epi = (d->flags & VDN_VDA_EPILOGUE) != 0;
+  if (!q || !k || !v || !alpha || !beta || !out) return VDN_ERR_INVALID_ARG;
+  if (d->n_text > 0 && (!k_text || !v_text || !beta_text)) return VDN_ERR_INVALID_ARG;
+  if (epi && !gate) return VDN_ERR_INVALID_ARG;
+  const Problem p = problem(d);
+  const Layout l = make_layout(p);
+  if (!workspace || workspace_bytes < l.total) return VDN_ERR_WORKSPACE;
+  const void* need16[] = {q, k, v, alpha, out, epi ? gate : nullptr,
+                          d->n_text > 0 ? k_text : nullptr, d->n_text > 0 ? v_text : nullptr};
+  for (const void* ptr : need16)
+    if (ptr && !aligned(ptr, 16)) return VDN_ERR_ALIGNMENT;
+  const size_t esz = p.bf16 ? 2 : 4;
+  if (!aligned(beta, esz) || (d->n_text > 0 && !aligned(beta_text, esz)) ||
+      (rms_weight && !aligned(rms_weight, 4)))
+    return VDN_ERR_ALIGNMENT;
+  if (!aligned(workspace, kAlign)) return VDN_ERR_ALIGNMENT;
+
+  char* ws = static_cast<char*>(workspace);
+  float* stats = reinterpret_cast<float*>(ws + l.stats);
+  float* pinv = reinterpret_cast<float*>(ws + l.pinv);
+  float* s_text = reinterpret_cast<float*>(ws + l.s_text);
+  float* fwd = reinterpret_cast<float*>(ws + l.fwd);
+  float* rev = reinterpret_cast<float*>(ws + l.rev);
+  void* rstates = ws + l.rstates;
+
+  const int n_video = p.T > 2 ? p.T - 2 : 0;
+  hipError_t e = mark(0, stream);
+  // frame statistics of frames 1..T-2 (anchors are never absorbed), then the text frame
+  if (e == hipSuccess) e = launch_gram(p, k, v, beta, p.T, p.U, 1, n_video, 0, stats, stream);
+  if (e == hipSuccess) e = mark(1, stream);
+  if (e == hipSuccess) e = launch_gram(p, k_text, v_text, beta_text, 1, p.L, 0, 1, p.T, stats, stream);
+  if (e == hipSuccess) e = mark(2, stream);
+  if (e == hipSuccess) e = launch_solve(p, stats, pinv, stream);
+  if (e == hipSuccess) e = mark(3, stream);
+  if (e == hipSuccess) e = launch_scan(p, stats, pinv, alpha, s_text, fwd, rev, stream);
+  if (e == hipSuccess) e = mark(4, stream);
+  if (e == hipSuccess) e = launch_gather(p, s_text, fwd, rev, rstates, stream);
+  if (e == hipSuccess) e = mark(5, stream);
+  if (e == hipSuccess) e = launch_readout(p, q, gate, rms_weight, rstates, out, stream);
+  if (e == hipSuccess) e = mark(6, stream);
+  return e == hipSuccess ? VDN_OK : VDN_ERR_HIP;
+}
+
+vdn_status vdn_vda_set_profile_events(hipEvent_t* events, int n) {
+  if (events && n < VDN_VDA_STAGES + 1) return VDN_ERR_INVALID_ARG;
+  g_events = events;
+  return VDN_OK;
+}
+
+const char* vdn_vda_status_string(vdn_status s) {
+  switch (s) {
+    case VDN_OK: return "VDN_OK";
+    case VDN_ERR_INVALID_ARG: return "VDN_ERR_INVALID_ARG: bad descriptor, size or NULL pointer";
+    case VDN_ERR_UNSUPPORTED: return "VDN_ERR_UNSUPPORTED: head width not implemented (d_k = d_v in {16,32,64,128})";
+    case VDN_ERR_WORKSPACE: return "VDN_ERR_WORKSPACE: workspace missing or too small";
+    case VDN_ERR_ALIGNMENT: return "VDN_ERR_ALIGNMENT: pointer misaligned";
+    case VDN_ERR_HIP: return "VDN_ERR_HIP: kernel launch failed";
+  }
+  return "unknown vdn_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+/*
+ * vdn_vda.h -- C ABI of the MI355X (gfx950) Video Delta Attention forward pass.
+ *
+ * Video Delta Attention (VDA) is the frame-level delta-rule linear-attention
+ * branch of Video DeltaNet.  Sources, cited by page title and section:
+ *   [VDN-summary]   "프레임 단위 델타 규칙과 양방향 선형 메모리로 영상 확산 모델의
+ *                   어텐션 병목을 걷어낸 Video DeltaNet" (onedev.kr/papers/80),
+ *                   sections "어떻게 동작하나" (how it works), "무엇과 다른가"
+ *                   (how it differs), "어떻게 쓰나" (how it is used),
+ *                   "전제와 한계" (premises and limits).
+ *   [VDN-H3-writeup] "VDN-H3: MiniMax H3 영상을 재생 시간보다 빠르게 생성하는
+ *                   하이브리드 어텐션 모델" (discuss.pytorch.kr), section on the
+ *                   hybrid attention structure.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless marked "host".  Every tensor is dense,
+ *     row-major, contiguous, and 16-byte aligned (the workspace 256-byte).
+ *   - The caller owns every buffer, including the workspace.  The library never
+ *     allocates or frees device memory and keeps no state between calls.
+ *   - Work is enqueued on `stream` and the call returns without synchronising.
+ *   - The return value is the only error channel.  Arguments are checked before
+ *     anything is enqueued; on any error nothing is enqueued and outputs are
+ *     untouched.  VDN_ERR_HIP reports a failed kernel launch (the stream may then
+ *     hold part of the work).
+ *   - Calls on distinct streams with distinct workspaces may run concurrently.
+ *   - NaN/Inf inputs propagate; they are not detected.
+ *
+ * Shapes (B batch, T latent frames, U = grid_h * grid_w tokens per frame,
+ * H heads, L text tokens, d_k = d_v = d):
+ *   q, k, v, gate, out : [B, T, U, H, d]      in `dtype`
+ *   beta               : [B, T, U, H]         in `dtype`, >= 0 (write strength per token)
+ *   alpha              : [B, T, H, d_k]       float32, in [0, 1] (decay per key channel)
+ *   k_text, v_text     : [B, L, H, d]         in `dtype`
+ *   beta_text          : [B, L, H]            in `dtype`, >= 0
+ *   rms_weight         : [d_v]                float32 (RMSNorm gain), NULL = all ones
+ *   prep conv weights  : wk_s, wv_s [H*d, 5, 5], wk_t, wv_t [H*d, 5] float32;
+ *                        channel index = h * d + j.
+ */
+#ifndef VDN_VDA_H
+#define VDN_VDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VDN_OK = 0,
+  VDN_ERR_INVALID_ARG = 1, /* bad shape/size, NULL required pointer, bad flag */
+  VDN_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement */
+  VDN_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than vdn_vda_workspace_bytes() */
+  VDN_ERR_ALIGNMENT = 4,   /* a pointer misses its alignment */
+  VDN_ERR_HIP = 5          /* a kernel launch failed */
+} vdn_status;
+
+typedef enum {
+  VDN_F32 = 0,  /* IEEE binary32 */
+  VDN_BF16 = 1  /* bfloat16 */
+} vdn_dtype;
+
+enum {
+  /* Apply RMSNorm over d_v and the sigmoid output gate to the readout
+   * ([VDN-summary] "무엇과 다른가").  Requires `gate`.  Without this flag
+   * `out` receives the raw readout o = (S_fwd + S_rev) q. */
+  VDN_VDA_EPILOGUE = 1u << 0,
+  /* Keep every intermediate in the workspace at the offsets that
+   * vdn_vda_workspace_layout() reports.  This build always keeps them, so the
+   * flag changes nothing; it is accepted for callers that rely on it. */
+  VDN_VDA_DEBUG_KEEP = 1u << 1
+};
+
+/* Problem descriptor: a host struct owned by the caller, passed by pointer. */
+typedef struct {
+  int32_t B, H, T;         /* batch, heads, latent frames (T >= 1) */
+  int32_t grid_h, grid_w;  /* token grid of a latent frame; U = grid_h * grid_w */
+  int32_t d_k, d_v;        /* head widths: must be equal, one of 16, 32, 64, 128 */
+  int32_t n_text;          /* L text tokens per batch element (may be 0) */
+  int32_t chunk;           /* latent frames per VAE chunk (the pages use 5); >= 1 */
+  vdn_dtype dtype;         /* dtype of q, k, v, beta, text tensors, gate and out */
+  uint32_t flags;          /* VDN_VDA_* bits */
+  float l2_eps;            /* prep L2 normalisation: x / sqrt(sum x^2 + l2_eps); > 0 */
+  float rms_eps;           /* RMSNorm: o / sqrt(mean o^2 + rms_eps); > 0 */
+} vdn_vda_desc;
+
+/* Byte offsets (from the workspace base) of the intermediates the forward pass
+ * leaves in the workspace.  All are float32.
+ *   stats  [B, H, T+1, d_k + d_v, d_k]: rows 0..d_k-1 hold A_t = K_t^T Diag(beta_t) K_t,
+ *          rows d_k.. hold B_t = V_t^T Diag(beta_t) K_t; slot T holds the text
+ *          frame.  Anchor frames (0, T-1) are not formed.
+ *   pinv   [B, H, T+1, d_k, d_k]: (I + A_t)^{-1}; slot T = text.
+ *   s_text [B, H, d_v, d_k]: the text state S_T.
+ *   fwd    [B, H, n_c, d_v, d_k]: forward state after the last frame of chunk j.
+ *   rev    [B, H, n_c, d_v, d_k]: reverse state after the first frame of chunk j.
+ *   readout_states: the per-chunk states the readout reads, in the readout
+ *          kernel's own packed operand order (not meant for callers).
+ *   n_c = ceil(T / chunk).  Entries a query never reads are left unspecified. */
+typedef struct {
+  size_t stats, pinv, s_text, fwd, rev, readout_states, total;
+} vdn_vda_layout;
+
+/* Check a descriptor without touching the GPU.  Host only. */
+vdn_status vdn_vda_validate(const vdn_vda_desc* d);
+
+/* Workspace bytes vdn_vda_forward needs for `d`; 0 if `d` is invalid. */
+size_t vdn_vda_workspace_bytes(const vdn_vda_desc* d);
+
+/* Fill `out` (host) with the workspace offsets for `d`. */
+vdn_status vdn_vda_workspace_layout(const vdn_vda_desc* d, vdn_vda_layout* out);
+
+/*
+ * vdn_vda_prepare -- the linear branch's feature preparation
+ * ([VDN-summary] "무엇과 다른가": separable short convolution on K and V --
+ * depthwise 5x5 spatial then 5-tap temporal -- then SiLU; L2 normalisation of
+ * Q and K; no rotary embedding; "전제와 한계": the fused prep kernel).
+ *   k_hat = L2(SiLU(conv_t(conv_s(k)))), v_hat = SiLU(conv_t(conv_s(v))), q_hat = L2(q).
+ * The convolutions are cross-correlations per channel with zero padding 2 on
+ * every side (rows, columns, frames); temporal taps are centred (t-2 .. t+2)
+ * and cross chunk boundaries.  Text tokens are not convolved.
+ * q, k, v: [B, T, U, H, d] raw features; q_hat, k_hat, v_hat: same shape,
+ * out of place (must not alias the inputs).  Weights as in the header comment.
+ * Errors: VDN_ERR_INVALID_ARG (descriptor, NULL pointer), VDN_ERR_ALIGNMENT,
+ * VDN_ERR_HIP.
+ */
+vdn_status vdn_vda_prepare(const vdn_vda_desc* d,
+                           const void* q, const void* k, const void* v,
+                           const float* wk_s, const float* wk_t,
+                           const float* wv_s, const float* wv_t,
+                           void* q_hat, void* k_hat, void* v_hat,
+                           hipStream_t stream);
+
+/*
+ * vdn_vda_forward -- the VDA forward pass on prepared features.
+ * For each (batch, head):
+ *   text state ([VDN-summary] "어떻게 동작하나"): S_T = B_T (I + A_T)^{-1} over the
+ *     L text tokens (a leading virtual frame updated from a zero state);
+ *   frame statistics and update ([VDN-summary] "어떻게 쓰나"):
+ *     A_t = K_t^T Diag(beta_t) K_t,  B_t = V_t^T Diag(beta_t) K_t,
+ *     S_t = (S_{t-1} Diag(alpha_t) + B_t)(I + A_t)^{-1};
+ *   bidirectional scan ([VDN-summary] "어떻게 동작하나"; anchors excluded,
+ *     "전제와 한계"): both directions start from S_T / 2; the forward state
+ *     of a query frame covers the non-anchor frames before its softmax window
+ *     (its chunk and the neighbouring chunks), the reverse state those after it;
+ *     anchor query frames (0, T-1) read S_T only;
+ *   readout: o = (S_fwd + S_rev) q; with VDN_VDA_EPILOGUE,
+ *     out = rms_weight * o / sqrt(mean(o^2) + rms_eps) * sigmoid(gate)
+ *     ([VDN-summary] "무엇과 다른가"), else out = o.
+ * q, k must be the prepared (unit-norm) features.  k_text, v_text, beta_text
+ * may be NULL when n_text = 0 (then S_T = 0).  gate is required with
+ * VDN_VDA_EPILOGUE and ignored without it.  out is written in `dtype` with
+ * round-to-nearest-even.  The state, statistics, inverse and scan are float32.
+ * Errors: VDN_ERR_INVALID_ARG, VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE,
+ * VDN_ERR_ALIGNMENT, VDN_ERR_HIP.
+ */
+vdn_status vdn_vda_forward(const vdn_vda_desc* d,
+                           const void* q, const void* k, const void* v,
+                           const float* alpha, const void* beta,
+                           const void* k_text, const void* v_text,
+                           const void* beta_text,
+                           const void* gate, const float* rms_weight,
+                           void* out,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Profiling hook for benchmarks.  While set, vdn_vda_forward records events[0]
+ * on its stream before its first kernel and events[i] after stage i, for
+ * i = 1..VDN_VDA_STAGES: frame statistics, text statistics, solve, scan,
+ * gather, readout.  The caller creates the n >= VDN_VDA_STAGES + 1 events
+ * (hipEventCreate) and keeps them alive while set; pass NULL to clear.
+ * Process-wide and not thread-safe.  Returns VDN_ERR_INVALID_ARG if n is too
+ * small. */
+enum { VDN_VDA_STAGES = 6 };
+vdn_status vdn_vda_set_profile_events(hipEvent_t* events, int n);
+
+/* Static, human-readable name of a status code. */
+const char* vdn_vda_status_string(vdn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDN_VDA_H */

@@ -1,0 +1,93 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, call the C ABI through
+the binding, read back outputs and intermediates, and measure errors against
+the oracle.  The oracle side always decodes the host copies itself."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from frame_wise_delta_02_amd import binding as bd
+from frame_wise_delta_02_amd import synth
+
+# tolerance on the max relative error (per (batch, frame, head) slice, inf-norm)
+TOL = {"f32": 1e-3, "bf16": 2e-2}
+
+
+def say(msg: str):
+    """Name the case on stderr before a GPU step, so a crash still says what ran."""
+    print(f"[gpu] {msg}", file=sys.__stderr__, flush=True)
+
+
+def to_device(x: np.ndarray, dtype: str):
+    import torch
+    if x.dtype == np.uint16:
+        t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to("cuda")
+
+
+def to_host_f64(t) -> np.ndarray:
+    import torch
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def oracle_view(x: dict, w: synth.Workload) -> dict:
+    """float64 copies of every input, decoded independently of the GPU path."""
+    out = {}
+    for k, v in x.items():
+        if v.dtype == np.uint16:
+            out[k] = oracle.widen_bf16_bits(v)
+        else:
+            out[k] = v.astype(np.float64)
+    return out
+
+
+def run_forward(x: dict, w: synth.Workload, epilogue=True, rms_weight=None, dev_inputs=None):
+    """Run vdn_vda_forward on the inputs; returns (out, workspace, desc, device inputs)."""
+    import torch
+    d = dev_inputs or {k: to_device(v, w.dtype) for k, v in x.items()}
+    desc = bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L, w.chunk, w.dtype, epilogue)
+    ws = torch.empty(bd.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    rw = None if rms_weight is None else torch.from_numpy(rms_weight.astype(np.float32)).cuda()
+    L = w.L
+    out = bd.forward(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                     d["k_text"] if L else None, d["v_text"] if L else None,
+                     d["beta_text"] if L else None, d["gate"], rw,
+                     grid=(w.grid_h, w.grid_w), chunk=w.chunk, epilogue=epilogue, workspace=ws)
+    torch.cuda.synchronize()
+    return out, ws, desc, d
+
+
+def intermediates(ws, desc, w: synth.Workload) -> dict:
+    """float64 host copies of the workspace intermediates."""
+    import torch
+    L = bd.workspace_layout(desc)
+    B, H, T, D = w.B, w.H, w.T, w.d
+    nc = -(-T // w.chunk)
+
+    def arr(off, shape):
+        n = int(np.prod(shape)) * 4
+        return ws[off:off + n].view(torch.float32).reshape(shape).to(torch.float64).cpu().numpy()
+
+    stats = arr(L.stats, (B, H, T + 1, 2 * D, D))
+    return dict(A=stats[:, :, :, :D], B=stats[:, :, :, D:], Pinv=arr(L.pinv, (B, H, T + 1, D, D)),
+                S_T=arr(L.s_text, (B, H, D, D)), F=arr(L.fwd, (B, H, nc, D, D)),
+                R=arr(L.rev, (B, H, nc, D, D)))
+
+
+def slice_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max over (b, t, h) of ||got - ref||_inf / ||ref||_inf over that U x d slice."""
+    diff = np.abs(got - ref).max(axis=(2, 4))
+    scale = np.abs(ref).max(axis=(2, 4))
+    return float(np.max(diff / np.maximum(scale, 1e-30)))
+
+
+def mat_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max over leading axes of ||got - ref||_inf / ||ref||_inf of each trailing matrix."""
+    diff = np.abs(got - ref).max(axis=(-2, -1))
+    scale = np.abs(ref).max(axis=(-2, -1))
+    return float(np.max(diff / np.maximum(scale, 1e-30)))

@@ -1,0 +1,144 @@
+"""The C ABI without a GPU: exports, descriptor validation, workspace layout and
+argument errors that are caught before anything is enqueued."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from frame_wise_delta_02_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"^\s*(?:vdn_status|size_t|const char\*)\s+(vdn_\w+)\s*\(", txt, re.M))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bd.lib()
+    declared = _declared()
+    assert {"vdn_vda_prepare", "vdn_vda_forward", "vdn_vda_validate",
+            "vdn_vda_workspace_bytes", "vdn_vda_status_string"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(bd.EXPORTS) <= declared
+
+
+def good(**kw):
+    base = dict(B=1, H=24, T=60, grid_h=48, grid_w=84, d=128, n_text=256, chunk=5, dtype="bf16")
+    base.update(kw)
+    return bd.make_desc(**base)
+
+
+def test_valid_descriptors():
+    for d in (16, 32, 64, 128):
+        assert bd.validate(good(d=d)) == bd.VDN_OK
+    assert bd.validate(good(T=1)) == bd.VDN_OK
+    assert bd.validate(good(n_text=0)) == bd.VDN_OK
+    assert bd.validate(good(dtype="f32", chunk=1)) == bd.VDN_OK
+
+
+@pytest.mark.parametrize("field,value", [
+    ("B", 0), ("H", 0), ("T", 0), ("grid_h", 0), ("grid_w", -1), ("n_text", -1), ("chunk", 0),
+    ("d_k", 0), ("d_k", 144), ("d_k", 24), ("dtype", 7), ("flags", 1 << 5)])
+def test_invalid_descriptors(field, value):
+    desc = good()
+    setattr(desc, field, value)
+    if field == "d_k":
+        desc.d_v = value
+    assert bd.validate(desc) == bd.VDN_ERR_INVALID_ARG
+    assert bd.workspace_bytes(desc) == 0
+
+
+def test_bad_eps_and_unsupported_widths():
+    d = good()
+    d.rms_eps = 0.0
+    assert bd.validate(d) == bd.VDN_ERR_INVALID_ARG
+    d = good()
+    d.l2_eps = float("nan")
+    assert bd.validate(d) == bd.VDN_ERR_INVALID_ARG
+    d = good()
+    d.d_v = 64
+    assert bd.validate(d) == bd.VDN_ERR_UNSUPPORTED
+    assert bd.validate(good(d=48)) == bd.VDN_ERR_UNSUPPORTED
+    assert bd.lib().vdn_vda_validate(None) == bd.VDN_ERR_INVALID_ARG
+
+
+def test_workspace_layout_is_consistent():
+    for kw in (dict(), dict(d=64, T=40, H=8), dict(T=1), dict(T=23, chunk=3), dict(dtype="f32", d=16)):
+        desc = good(**kw)
+        L = bd.workspace_layout(desc)
+        B, H, T, d = desc.B, desc.H, desc.T, desc.d_k
+        nc = -(-T // desc.chunk)
+        f = 4 * d * d
+        offs = [L.stats, L.pinv, L.s_text, L.fwd, L.rev, L.readout_states, L.total]
+        assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+        assert L.pinv - L.stats >= B * H * (T + 1) * 2 * f
+        assert L.s_text - L.pinv >= B * H * (T + 1) * f
+        assert L.fwd - L.s_text >= B * H * f
+        assert L.rev - L.fwd >= B * H * nc * f
+        assert L.readout_states - L.rev >= B * H * nc * f
+        assert L.total == bd.workspace_bytes(desc)
+
+
+def test_status_strings():
+    for s in range(6):
+        assert bd.status_string(s).startswith("VDN_")
+    assert "unknown" in bd.status_string(99)
+
+
+def _fwd(desc, ptrs, ws_bytes):
+    lib = bd.lib()
+    P = [ctypes.c_void_p(p) if p else None for p in ptrs]
+    return lib.vdn_vda_forward(ctypes.byref(desc), *P, ws_bytes, None)
+
+
+# fake, never dereferenced device addresses: every call below must fail its
+# argument checks before it reaches the GPU
+A16 = 0x7f0000000000
+
+
+def _ptrs(**over):
+    names = ["q", "k", "v", "alpha", "beta", "k_text", "v_text", "beta_text", "gate", "rms_weight",
+             "out", "ws"]
+    p = {n: A16 + 0x1000000 * i for i, n in enumerate(names)}
+    p.update(over)
+    return [p[n] for n in names]
+
+
+def test_forward_argument_errors_before_launch():
+    desc = good()
+    need = bd.workspace_bytes(desc)
+    assert _fwd(desc, _ptrs(q=0), need) == bd.VDN_ERR_INVALID_ARG
+    assert _fwd(desc, _ptrs(out=0), need) == bd.VDN_ERR_INVALID_ARG
+    assert _fwd(desc, _ptrs(k_text=0), need) == bd.VDN_ERR_INVALID_ARG
+    assert _fwd(desc, _ptrs(gate=0), need) == bd.VDN_ERR_INVALID_ARG
+    assert _fwd(desc, _ptrs(ws=0), need) == bd.VDN_ERR_WORKSPACE
+    assert _fwd(desc, _ptrs(), need - 1) == bd.VDN_ERR_WORKSPACE
+    assert _fwd(desc, _ptrs(q=A16 + 8), need) == bd.VDN_ERR_ALIGNMENT
+    assert _fwd(desc, _ptrs(ws=A16 + 0x40000000 + 64), need) == bd.VDN_ERR_ALIGNMENT
+    assert _fwd(desc, _ptrs(beta=A16 + 1), need) == bd.VDN_ERR_ALIGNMENT
+    bad = good(d=48)
+    assert _fwd(bad, _ptrs(), need) == bd.VDN_ERR_UNSUPPORTED
+
+
+def test_prepare_argument_errors_before_launch():
+    lib = bd.lib()
+    desc = good(epilogue=False)
+    P = [ctypes.c_void_p(A16 + 0x1000000 * i) for i in range(10)]
+    args = list(P)
+    args[0] = None
+    assert lib.vdn_vda_prepare(ctypes.byref(desc), *args, None) == bd.VDN_ERR_INVALID_ARG
+    args = list(P)
+    args[8] = args[1]  # k_hat aliases k
+    assert lib.vdn_vda_prepare(ctypes.byref(desc), *args, None) == bd.VDN_ERR_INVALID_ARG
+    args = list(P)
+    args[2] = ctypes.c_void_p(A16 + 0x2000000 + 4)
+    assert lib.vdn_vda_prepare(ctypes.byref(desc), *args, None) == bd.VDN_ERR_ALIGNMENT

@@ -1,0 +1,183 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Every case draws seeded inputs, runs vdn_vda_forward (and vdn_vda_prepare for
+the prep workload), and compares element by element with the oracle computed on
+the same arrays.  Tolerance on the output: max relative error per (frame, head)
+slice <= 1e-3 for float32 inputs and <= 2e-2 for bfloat16 inputs (fp32 state).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from frame_wise_delta_02_amd import synth
+import gpu_harness as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _name_case(request):
+    G.say(request.node.nodeid)
+    yield
+
+
+def _oracle_heads(x, w, heads, gate=True, rms_weight=None, prepared=None):
+    """Oracle forward on the listed heads only (inputs sliced before widening)."""
+    sl = lambda a: a[:, :, :, heads] if a.ndim == 5 else a
+    f = {}
+    for k in ("q", "k", "v", "gate"):
+        src = prepared[k] if (prepared is not None and k in prepared) else sl(x[k])
+        f[k] = src if src.dtype == np.float64 else G.oracle_view({k: src}, w)[k]
+    f["beta"] = G.oracle_view({"b": x["beta"][:, :, :, heads]}, w)["b"]
+    f["alpha"] = x["alpha"][:, :, heads].astype(np.float64)
+    for k in ("k_text", "v_text"):
+        f[k] = G.oracle_view({k: x[k][:, :, heads]}, w)[k]
+    f["beta_text"] = G.oracle_view({"b": x["beta_text"][:, :, heads]}, w)["b"]
+    return oracle.forward(f["q"], f["k"], f["v"], f["alpha"], f["beta"], f["k_text"], f["v_text"],
+                          f["beta_text"], gate=f["gate"] if gate else None, rms_weight=rms_weight,
+                          chunk=w.chunk)
+
+
+def _check_intermediates(inter, ref, w, heads, tol):
+    T, nc = w.T, -(-w.T // w.chunk)
+    hs = list(heads)
+    if T > 2:
+        fr = slice(1, T - 1)
+        assert G.mat_rel_err(inter["A"][:, hs, fr], ref["A"][:, :, fr]) <= tol, "A"
+        assert G.mat_rel_err(inter["B"][:, hs, fr], ref["B"][:, :, fr]) <= tol, "B"
+        assert G.mat_rel_err(inter["Pinv"][:, hs, fr], ref["Pinv"][:, :, fr]) <= tol, "Pinv"
+    if w.L:
+        assert G.mat_rel_err(inter["S_T"][:, hs], ref["S_T"]) <= tol, "S_T"
+    if nc >= 3:
+        assert G.mat_rel_err(inter["F"][:, hs, : nc - 2], ref["F"][:, :, : nc - 2]) <= tol, "F"
+        assert G.mat_rel_err(inter["R"][:, hs, 2:], ref["R"][:, :, 2:]) <= tol, "R"
+
+
+def _run_case(w, heads=None, rms=False, check_inter=True):
+    x = synth.make_inputs(w)
+    heads = list(range(w.H)) if heads is None else heads
+    rw = np.random.default_rng(5).uniform(0.5, 1.5, w.d) if rms else None
+    tol = G.TOL[w.dtype]
+    # raw readout, with intermediates
+    out, ws, desc, dev = G.run_forward(x, w, epilogue=False)
+    ref = _oracle_heads(x, w, heads, gate=True, rms_weight=rw)
+    got = G.to_host_f64(out[:, :, :, heads])
+    err_o = G.slice_rel_err(got, ref["o"])
+    if check_inter:
+        _check_intermediates(G.intermediates(ws, desc, w), ref, w, heads, tol)
+    # with RMSNorm + gate
+    out2, _, _, _ = G.run_forward(x, w, epilogue=True, rms_weight=rw, dev_inputs=dev)
+    got2 = G.to_host_f64(out2[:, :, :, heads])
+    err_y = G.slice_rel_err(got2, ref["y"])
+    G.say(f"{w.name} T={w.T} U={w.U} H={w.H} d={w.d}: err(o)={err_o:.3e} err(y)={err_y:.3e} tol={tol}")
+    assert err_o <= tol, err_o
+    assert err_y <= tol, err_y
+    return err_o, err_y
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "stress_f32", "stress_tight_f32"])
+def test_workload_full_oracle(name):
+    _run_case(synth.WORKLOADS[name], rms=(name == "small_bf16"))
+
+
+def test_768p_full_size_sampled_heads():
+    """The benchmarked workload at full size; the oracle checks two whole heads."""
+    _run_case(synth.WORKLOADS["768p_bf16"], heads=[0, 23])
+
+
+EDGE = {
+    # several tiles and ragged tails: U = 100 (64 + 36 gram tile, 3x32 + 4 readout tile), T = 17
+    "ragged_bf16_128": synth.WORKLOADS["768p_bf16"].scaled(name="ragged_bf16_128", H=3, T=17, grid_h=10, grid_w=10, L=37),
+    "ragged_f32_128": synth.WORKLOADS["stress_f32"].scaled(name="ragged_f32_128", H=2, T=13, grid_h=7, grid_w=11, L=5),
+    "d64_bf16": synth.WORKLOADS["small_bf16"].scaled(name="d64_bf16", H=3, T=12, grid_h=5, grid_w=13, L=9),
+    "d32_bf16": synth.WORKLOADS["small_bf16"].scaled(name="d32_bf16", d=32, H=2, T=16, grid_h=6, grid_w=6, L=4),
+    "d32_f32": synth.WORKLOADS["tiny_f32"].scaled(name="d32_f32", d=32, H=2, T=11, grid_h=3, grid_w=7, L=3),
+    "d16_bf16": synth.WORKLOADS["tiny_f32"].scaled(name="d16_bf16", dtype="bf16", H=3, T=14, L=2),
+    "no_text_bf16": synth.WORKLOADS["768p_bf16"].scaled(name="no_text_bf16", H=2, T=15, grid_h=4, grid_w=9, L=0),
+    "T1_bf16": synth.WORKLOADS["768p_bf16"].scaled(name="T1_bf16", H=2, T=1, grid_h=4, grid_w=8, L=16),
+    "T2_f32": synth.WORKLOADS["stress_f32"].scaled(name="T2_f32", H=2, T=2, grid_h=4, grid_w=8, L=16),
+    "T7_f32": synth.WORKLOADS["tiny_f32"].scaled(name="T7_f32", T=7),
+    "chunk3_bf16": synth.WORKLOADS["small_bf16"].scaled(name="chunk3_bf16", H=2, T=20, grid_h=4, grid_w=10, chunk=3, L=8),
+    "chunk1_f32": synth.WORKLOADS["tiny_f32"].scaled(name="chunk1_f32", T=9, chunk=1),
+    "batch2_bf16": synth.WORKLOADS["768p_bf16"].scaled(name="batch2_bf16", B=2, H=2, T=16, grid_h=6, grid_w=11, L=12),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_cases(name):
+    _run_case(EDGE[name], rms=name.endswith("128"))
+
+
+def test_zero_writes_give_text_only_readout():
+    """beta = 0 on every video token and alpha = 1: every frame reads S_T q."""
+    w = EDGE["ragged_bf16_128"]
+    x = synth.make_inputs(w)
+    x["beta"][:] = 0
+    x["alpha"][:] = 1.0
+    out, ws, desc, _ = G.run_forward(x, w, epilogue=False)
+    ST = G.intermediates(ws, desc, w)["S_T"]
+    q = G.oracle_view({"q": x["q"]}, w)["q"]
+    want = np.einsum("btuhk,bhvk->btuhv", q, ST)
+    got = G.to_host_f64(out)
+    assert G.slice_rel_err(got, want) <= G.TOL[w.dtype]
+
+
+def test_deterministic_rerun():
+    w = EDGE["ragged_bf16_128"]
+    x = synth.make_inputs(w)
+    import torch
+    o1, _, _, dev = G.run_forward(x, w, epilogue=True)
+    o2, _, _, _ = G.run_forward(x, w, epilogue=True, dev_inputs=dev)
+    assert torch.equal(o1, o2)
+
+
+# ---------------------------------------------------------------------------
+# prep (conv, SiLU, L2) and the fused long clip
+# ---------------------------------------------------------------------------
+
+
+def _prep_case(w, heads):
+    import torch
+    from frame_wise_delta_02_amd import binding as bd
+    x = synth.make_inputs(w)
+    dev = {k: G.to_device(v, w.dtype) for k, v in x.items()}
+    G.say(f"prepare {w.name} T={w.T} grid={w.grid_h}x{w.grid_w} H={w.H}")
+    qh, kh, vh = bd.prepare(dev["q"], dev["k"], dev["v"], dev["wk_s"], dev["wk_t"], dev["wv_s"], dev["wv_t"],
+                            grid=(w.grid_h, w.grid_w))
+    torch.cuda.synchronize()
+    prepared = {}
+    errs = {}
+    for h in heads:
+        sl = lambda a: a[0, :, :, h:h + 1]
+        f = G.oracle_view({"q": sl(x["q"]), "k": sl(x["k"]), "v": sl(x["v"])}, w)
+        ws_ = lambda n: x[n][h * w.d:(h + 1) * w.d].astype(np.float64)
+        rq, rk, rv = oracle.prep(f["q"], f["k"], f["v"], ws_("wk_s"), ws_("wk_t"), ws_("wv_s"), ws_("wv_t"),
+                                 w.grid_h, w.grid_w, l2_eps=1e-6)
+        for name, ref, got in (("q", rq, qh), ("k", rk, kh), ("v", rv, vh)):
+            g = G.to_host_f64(got[0, :, :, h:h + 1])
+            errs[name] = max(errs.get(name, 0.0), G.slice_rel_err(g[None], ref[None]))
+            prepared.setdefault(name, []).append(ref)
+    G.say(f"prep errors {errs}")
+    for name, e in errs.items():
+        assert e <= (1e-2 if w.dtype == "bf16" else 1e-5), (name, e)
+    return x, dev, (qh, kh, vh), {k: np.concatenate(v, axis=2)[None] for k, v in prepared.items()}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prepare_small(dtype):
+    w = synth.WORKLOADS["long_prep_bf16"].scaled(name=f"prep_small_{dtype}", dtype=dtype, H=2, T=9,
+                                                   grid_h=6, grid_w=10, L=8)
+    _prep_case(w, heads=[0, 1])
+
+
+def test_long_prep_full_size_sampled_head():
+    """The long fused clip at full size: prepare + forward; the oracle checks one whole head."""
+    w = synth.WORKLOADS["long_prep_bf16"]
+    x, dev, (qh, kh, vh), prepared = _prep_case(w, heads=[5])
+    dev2 = dict(dev, q=qh, k=kh, v=vh)
+    out, _, _, _ = G.run_forward(x, w, epilogue=True, dev_inputs=dev2)
+    ref = _oracle_heads(x, w, [5], gate=True, prepared={**prepared, "gate": x["gate"][:, :, :, [5]]})
+    err = G.slice_rel_err(G.to_host_f64(out[:, :, :, [5]]), ref["y"])
+    G.say(f"long_prep_bf16 head 5: err(y)={err:.3e}")
+    assert err <= G.TOL["bf16"], err
