@@ -9,9 +9,14 @@
 // true Gram matrix (symmetric positive semidefinite) after rounding, so I + A_t
 // always has a Cholesky factor.
 //
-// bfloat16 inputs: the contraction runs on v_mfma_f32_16x16x32_bf16 with fp32
-// accumulation.  The token axis is the contraction axis but is the strided axis
-// in memory ([.., U, H, d] layout), so each 64-token tile is staged through LDS
+// bfloat16 inputs: the contraction runs on v_mfma_f32_16x16x32_f16 with fp32
+// accumulation.  The scaled operands sqrt(beta) k and sqrt(beta) v are rounded
+// to IEEE half, not bfloat16: the inputs are exact in either, but the products
+// keep 11 significant bits instead of 8 at the same matrix-core rate on gfx950
+// (keys are unit vectors, so |sqrt(beta) k| <= sqrt(beta); a value entry with
+// |sqrt(beta) v| beyond 65504 would overflow the half range).
+// The token axis is the contraction axis but is the strided axis in memory
+// ([.., U, H, d] layout), so each 64-token tile is staged through LDS
 // transposed: every loader thread reads 8 tokens x 8 channels (coalesced 16-byte
 // loads along d), scales and rounds them, transposes the 8x8 block in registers
 // and writes 8 rows of 16 bytes.  Rows are 128 bytes (64 tokens) with an XOR
@@ -62,32 +67,31 @@ __global__ __launch_bounds__(256, 1) void gram_bf16(
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   uint4 reg0[8], reg1[8];
-  float sb0[8], sb1[8];
+  uint32_t sb0[8], sb1[8];  // raw beta bits; bit 16 set when the token exists
 
-  auto load = [&](uint4 (&reg)[8], float (&sb)[8], int u0) {
+  // Loads are branch-free: a token past the end of the frame (or a thread
+  // that does not load) reads a valid row and is zeroed through its beta, so
+  // the compiler can keep every load of a tile in flight at once.
+  auto load = [&](uint4 (&reg)[8], uint32_t (&sb)[8], int u0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int u = u0 + tg * 8 + j;
-      if (loader && u < U) {
-        const size_t row = (tok0 + u) * (size_t)H + h;
-        reg[j] = *reinterpret_cast<const uint4*>(src + row * D + ch);
-        sb[j] = bf16_to_f32(beta[row]);
-      } else {
-        reg[j] = make_uint4(0, 0, 0, 0);
-        sb[j] = 0.f;
-      }
+      const bool ok = loader && u < U;
+      const size_t row = (tok0 + (ok ? u : 0)) * (size_t)H + h;
+      reg[j] = *reinterpret_cast<const uint4*>(src + row * D + ch);
+      sb[j] = (uint32_t)beta[row] | (ok ? 0x10000u : 0u);
     }
   };
 
-  auto store = [&](const uint4 (&reg)[8], const float (&sb)[8], int buf) {
+  auto store = [&](const uint4 (&reg)[8], const uint32_t (&sb)[8], int buf) {
     if (!loader) return;
     uint32_t w[8][4];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float s = __builtin_sqrtf(sb[j]);
+      const float s = (sb[j] & 0x10000u) ? __builtin_sqrtf(bf16_to_f32((uint16_t)sb[j])) : 0.f;
       const uint32_t x[4] = {reg[j].x, reg[j].y, reg[j].z, reg[j].w};
 #pragma unroll
-      for (int d = 0; d < 4; ++d) w[j][d] = pack_bf16x2(bf16_lo(x[d]) * s, bf16_hi(x[d]) * s);
+      for (int d = 0; d < 4; ++d) w[j][d] = pack_f16x2(bf16_lo(x[d]) * s, bf16_hi(x[d]) * s);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -108,20 +112,20 @@ __global__ __launch_bounds__(256, 1) void gram_bf16(
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int q = 4 * s + (lane >> 4);
-      bf16x8 afr[MTW];
+      f16x8 afr[MTW];
 #pragma unroll
       for (int mi = 0; mi < MTW; ++mi) {
         const int r = 16 * min(wave * MTW + mi, MT - 1) + (lane & 15);
-        afr[mi] = *reinterpret_cast<const bf16x8*>(base + r * 128 + 16 * (q ^ swz(r)));
+        afr[mi] = *reinterpret_cast<const f16x8*>(base + r * 128 + 16 * (q ^ swz(r)));
       }
 #pragma unroll
       for (int nj = 0; nj < NT; ++nj) {
         const int r = 16 * nj + (lane & 15);
-        const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(base + r * 128 + 16 * (q ^ swz(r)));
+        const f16x8 bfr = *reinterpret_cast<const f16x8*>(base + r * 128 + 16 * (q ^ swz(r)));
 #pragma unroll
         for (int mi = 0; mi < MTW; ++mi)
-          if (wave * MTW + mi < MT)
-            acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mi], bfr, acc[mi][nj], 0, 0, 0);
+          if (MT % 4 == 0 || wave * MTW + mi < MT)
+            acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[mi], bfr, acc[mi][nj], 0, 0, 0);
       }
     }
   };
@@ -196,18 +200,15 @@ __global__ __launch_bounds__(256, 2) void gram_f32(
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int unit = tid + 256 * i;
-      const int tok = unit / (R / 4), c4 = unit % (R / 4);
+      const int tok = (unit % UNITS) / (R / 4), c4 = unit % (R / 4);
       const int u = u0 + tok;
-      if (unit < UNITS && u < U) {
-        const float* src = (c4 < D / 4) ? K : V;
-        const int ch = (c4 % (D / 4)) * 4;
-        const size_t row = (tok0 + u) * (size_t)H + h;
-        reg[i] = *reinterpret_cast<const float4*>(src + row * D + ch);
-        sb[i] = beta[row];
-      } else {
-        reg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        sb[i] = 0.f;
-      }
+      const bool ok = unit < UNITS && u < U;
+      const float* src = (c4 < D / 4) ? K : V;
+      const int ch = (c4 % (D / 4)) * 4;
+      const size_t row = (tok0 + (ok ? u : 0)) * (size_t)H + h;
+      reg[i] = *reinterpret_cast<const float4*>(src + row * D + ch);
+      const float bv = beta[row];
+      sb[i] = ok ? bv : 0.f;
     }
   };
   auto store = [&](int buf) {

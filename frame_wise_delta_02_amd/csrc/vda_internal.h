@@ -13,6 +13,8 @@ namespace vda {
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -23,6 +25,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 // Two floats -> two bfloat16 (round to nearest even), packed low/high.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Two floats -> two IEEE halves (round to nearest even), packed low/high.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2 r = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, r);
 }
 

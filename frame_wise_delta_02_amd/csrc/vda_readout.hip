@@ -39,6 +39,8 @@ __global__ __launch_bounds__(256, 2) void readout_bf16(
   constexpr int KS = D / 16;
   constexpr int NF = MT * KS * 64;   // 16-byte fragments per part (hi or lo)
   constexpr int NO = HALF < D ? HALF : D;  // valid outputs for lane half 0
+  constexpr int NG = HALF / 8;       // 16-byte gate / output vectors per lane
+  constexpr int STAGE = (2 * NF + 255) / 256;
   __shared__ uint4 sfrag[2 * NF];
   __shared__ float sgam[DP];
 
@@ -49,35 +51,40 @@ __global__ __launch_bounds__(256, 2) void readout_bf16(
   const int t = blk % T;
   const int b = blk / T;
   const int slot = (t == 0 || t == T - 1) ? nc : t / C;
-  const uint4* src = rstates + ((size_t)(b * H + h) * (nc + 1) + slot) * 2 * NF;
-  for (int i = tid; i < 2 * NF; i += 256) sfrag[i] = src[i];
-  for (int i = tid; i < DP; i += 256) sgam[i] = (w && i < D) ? w[i] : 1.f;
+  {
+    const uint4* src = rstates + ((size_t)(b * H + h) * (nc + 1) + slot) * 2 * NF;
+    uint4 tmp[STAGE];  // all staging loads in flight before the first LDS write
+#pragma unroll
+    for (int i = 0; i < STAGE; ++i) tmp[i] = src[min(tid + 256 * i, 2 * NF - 1)];
+#pragma unroll
+    for (int i = 0; i < STAGE; ++i)
+      if (tid + 256 * i < 2 * NF) sfrag[tid + 256 * i] = tmp[i];
+    for (int i = tid; i < DP; i += 256) sgam[i] = (w && i < D) ? w[i] : 1.f;
+  }
   __syncthreads();
 
   const int n = lane & 31, half = lane >> 5;
   const int dv0 = HALF * half;               // first output channel of this lane
   const int nout = (dv0 < D) ? NO : 0;       // outputs this lane owns
-
   const size_t row_base = ((size_t)b * T + t) * (size_t)U;
   const int ntiles = (U + 31) / 32;
-  for (int tile = wave; tile < ntiles; tile += 4) {
+
+  // branch-free loads: a token past the end reads token 0 and is not stored
+  auto fetch = [&](int tile, bf16x8 (&qv)[KS], uint4 (&gv)[NG]) {
     const int u = tile * 32 + n;
-    const bool valid = u < U;
-    const size_t row = ((row_base + (valid ? u : 0)) * H + h) * (size_t)D;
-    bf16x8 qv[KS];
+    const size_t row = ((row_base + (u < U ? u : 0)) * H + h) * (size_t)D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 x = valid ? *reinterpret_cast<const uint4*>(Q + row + (D / 2) * half + 8 * ks)
-                            : make_uint4(0, 0, 0, 0);
-      qv[ks] = __builtin_bit_cast(bf16x8, x);
-    }
-    uint4 gv[HALF / 8];
+    for (int ks = 0; ks < KS; ++ks)
+      qv[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Q + row + (D / 2) * half + 8 * ks));
     if (epilogue) {
+      const uint16_t* gp = G + row + (nout ? dv0 : 0);
 #pragma unroll
-      for (int i = 0; i < HALF / 8; ++i)
-        gv[i] = (valid && 8 * i < nout) ? *reinterpret_cast<const uint4*>(G + row + dv0 + 8 * i)
-                                        : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < NG; ++i) gv[i] = *reinterpret_cast<const uint4*>(gp + 8 * (8 * i < NO ? i : 0));
     }
+  };
+
+  auto process = [&](int tile, const bf16x8 (&qv)[KS], const uint4 (&gv)[NG]) {
+    const int u = tile * 32 + n;
     f32x16 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{0.f};
@@ -104,7 +111,7 @@ __global__ __launch_bounds__(256, 2) void readout_bf16(
       ss += __shfl_xor(ss, 32);
       const float rinv = 1.f / __builtin_sqrtf(ss / (float)D + eps);
 #pragma unroll
-      for (int i = 0; i < HALF / 8; ++i) {
+      for (int i = 0; i < NG; ++i) {
         const uint32_t g4[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -114,9 +121,10 @@ __global__ __launch_bounds__(256, 2) void readout_bf16(
         }
       }
     }
-    if (valid) {
+    if (u < U) {
+      const size_t row = ((row_base + u) * H + h) * (size_t)D;
 #pragma unroll
-      for (int i = 0; i < HALF / 8; ++i) {
+      for (int i = 0; i < NG; ++i) {
         if (8 * i < nout) {
           const int m = (8 * i) / 16, r = (8 * i) % 16;
           const uint4 o = make_uint4(pack_bf16x2(acc[m][r], acc[m][r + 1]), pack_bf16x2(acc[m][r + 2], acc[m][r + 3]),
@@ -125,6 +133,19 @@ __global__ __launch_bounds__(256, 2) void readout_bf16(
         }
       }
     }
+  };
+
+  // two register sets: tile i+4 is in flight while tile i is multiplied
+  bf16x8 qa[KS], qb[KS];
+  uint4 ga[NG], gb[NG];
+  int tile = wave;
+  if (tile < ntiles) fetch(tile, qa, ga);
+  for (; tile < ntiles; tile += 8) {
+    if (tile + 4 < ntiles) fetch(tile + 4, qb, gb);
+    process(tile, qa, ga);
+    if (tile + 4 >= ntiles) break;
+    if (tile + 8 < ntiles) fetch(tile + 8, qa, ga);
+    process(tile + 4, qb, gb);
   }
 }
 
@@ -149,9 +170,17 @@ __global__ __launch_bounds__(256, 2) void readout_f32(
   const int t = blk % T;
   const int b = blk / T;
   const int slot = (t == 0 || t == T - 1) ? nc : t / C;
-  const float4* src = rstates + ((size_t)(b * H + h) * (nc + 1) + slot) * NF;
-  for (int i = tid; i < NF; i += 256) sfrag[i] = src[i];
-  for (int i = tid; i < DP; i += 256) sgam[i] = (w && i < D) ? w[i] : 1.f;
+  {
+    constexpr int STAGE = (NF + 255) / 256;
+    const float4* src = rstates + ((size_t)(b * H + h) * (nc + 1) + slot) * NF;
+    float4 tmp[STAGE];
+#pragma unroll
+    for (int i = 0; i < STAGE; ++i) tmp[i] = src[min(tid + 256 * i, NF - 1)];
+#pragma unroll
+    for (int i = 0; i < STAGE; ++i)
+      if (tid + 256 * i < NF) sfrag[tid + 256 * i] = tmp[i];
+    for (int i = tid; i < DP; i += 256) sgam[i] = (w && i < D) ? w[i] : 1.f;
+  }
   __syncthreads();
 
   const int n = lane & 31, half = lane >> 5;
@@ -165,9 +194,7 @@ __global__ __launch_bounds__(256, 2) void readout_f32(
     const size_t row = ((row_base + (valid ? u : 0)) * H + h) * (size_t)D;
     float4 qv[KQ];
 #pragma unroll
-    for (int kq = 0; kq < KQ; ++kq)
-      qv[kq] = valid ? *reinterpret_cast<const float4*>(Q + row + (D / 2) * half + 4 * kq)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int kq = 0; kq < KQ; ++kq) qv[kq] = *reinterpret_cast<const float4*>(Q + row + (D / 2) * half + 4 * kq);
     f32x16 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{0.f};
@@ -191,10 +218,11 @@ __global__ __launch_bounds__(256, 2) void readout_f32(
         for (int r = 0; r < 16; ++r) ss += acc[mt][r] * acc[mt][r];
       ss += __shfl_xor(ss, 32);
       const float rinv = 1.f / __builtin_sqrtf(ss / (float)D + eps);
+      const float* gp = G + row + (nout ? dv0 : 0);
 #pragma unroll
       for (int i = 0; i < HALF / 4; ++i) {
-        if (4 * i < nout && valid) {
-          const float4 g = *reinterpret_cast<const float4*>(G + row + dv0 + 4 * i);
+        if (4 * i < NO) {
+          const float4 g = *reinterpret_cast<const float4*>(gp + 4 * i);
           const float gg[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
