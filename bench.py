@@ -132,6 +132,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="768p_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget; 0 skips it")
+    ap.add_argument("--copy-gib", type=float, default=0.0,
+                    help="instead of the forward pass, time a plain device copy of this many GiB "
+                         "(the reference for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (VDA heads never "
@@ -141,6 +144,23 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_gib > 0:
+        n = int(args.copy_gib * (1 << 30))
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(el * 1e3, 4),
+                          "GBs": round(2 * n / el / 1e9, 1)}), flush=True)
+        return 0
 
     from frame_wise_delta_02_amd import binding as bd
     from frame_wise_delta_02_amd import synth

@@ -41,6 +41,31 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
   lo = (__bf16)(x - (float)hi);
 }
 
+// Raw buffer resource over [base, base + bytes): loads at or past `bytes`
+// return zero and stores there are dropped (gfx9 descriptor, word 3 = 0x00020000).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, 0);
+}
+
+// Workgroup barrier for LDS exchange only.  __syncthreads() is a full
+// workgroup fence, so it also waits for every global load in flight
+// (s_waitcnt vmcnt(0)) and drains any software prefetch.  Here each wave only
+// waits for its own LDS operations (lgkmcnt(0); gfx9 s_waitcnt encoding with
+// vmcnt and expcnt left at their maxima) before s_barrier; the signal fences
+// keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---------------------------------------------------------------------------
 // launch plumbing
 // ---------------------------------------------------------------------------

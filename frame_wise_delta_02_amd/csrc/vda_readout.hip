@@ -26,23 +26,24 @@
 namespace vda {
 namespace {
 
-__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
-template <int D>
+template <int D, bool EPI, bool GAMMA>
 __global__ __launch_bounds__(256, 2) void readout_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ G, const float* __restrict__ w,
     const uint4* __restrict__ rstates, uint16_t* __restrict__ O, int T, int U, int H, int C,
-    int nc, int epilogue, float eps) {
+    int nc, float eps) {
   constexpr int DP = D < 32 ? 32 : D;
   constexpr int HALF = DP / 2;       // outputs per lane
   constexpr int MT = DP / 32;
   constexpr int KS = D / 16;
   constexpr int NF = MT * KS * 64;   // 16-byte fragments per part (hi or lo)
-  constexpr int NO = HALF < D ? HALF : D;  // valid outputs for lane half 0
   constexpr int NG = HALF / 8;       // 16-byte gate / output vectors per lane
+  constexpr int CH = D / 8;          // 16-byte chunks per token row
   constexpr int STAGE = (2 * NF + 255) / 256;
+  constexpr int OREADS = (16 * CH + 63) / 64;
   __shared__ uint4 sfrag[2 * NF];
-  __shared__ float sgam[DP];
+  __shared__ uint4 ostage[4][16 * CH];  // per wave: 16 output rows, chunk index XOR-swizzled
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int blk = blockIdx.x;
@@ -59,32 +60,40 @@ __global__ __launch_bounds__(256, 2) void readout_bf16(
 #pragma unroll
     for (int i = 0; i < STAGE; ++i)
       if (tid + 256 * i < 2 * NF) sfrag[tid + 256 * i] = tmp[i];
-    for (int i = tid; i < DP; i += 256) sgam[i] = (w && i < D) ? w[i] : 1.f;
   }
   __syncthreads();
 
-  const int n = lane & 31, half = lane >> 5;
-  const int dv0 = HALF * half;               // first output channel of this lane
-  const int nout = (dv0 < D) ? NO : 0;       // outputs this lane owns
-  const size_t row_base = ((size_t)b * T + t) * (size_t)U;
-  const int ntiles = (U + 31) / 32;
+  // Buffer descriptors over this frame and head: tokens past U read zero and
+  // their stores are dropped, so the tail tile and the prefetch past the last
+  // tile need no clamping.
+  const size_t fbase = (((size_t)b * T + t) * U * H + h) * (size_t)D;
+  const uint32_t rowbytes = (uint32_t)H * D * 2;
+  const uint32_t nbytes = U > 0 ? (uint32_t)(U - 1) * rowbytes + D * 2 : 0;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + fbase, nbytes);
+  const __amdgpu_buffer_rsrc_t orr = make_rsrc(O + fbase, nbytes);
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc(EPI ? G + fbase : Q + fbase, nbytes);
 
-  // branch-free loads: a token past the end reads token 0 and is not stored
+  const int n = lane & 31, half = lane >> 5;
+  const int dv0 = HALF * half;                 // first output channel of this lane
+  const bool owns = dv0 < D;                   // false only for the padding half at d = 16
+  const uint32_t qoff = (uint32_t)n * rowbytes + (D / 2) * half * 2;
+  const uint32_t goff = owns ? (uint32_t)n * rowbytes + dv0 * 2 : 0x80000000u;
+  const int ntiles = (U + 31) / 32;
+  const int per_wave = (ntiles + 3) / 4;
+  const int steps = (per_wave + 1) & ~1;       // even: the loop has no exit in the middle
+  uint4* ost = ostage[wave];
+
   auto fetch = [&](int tile, bf16x8 (&qv)[KS], uint4 (&gv)[NG]) {
-    const int u = tile * 32 + n;
-    const size_t row = ((row_base + (u < U ? u : 0)) * H + h) * (size_t)D;
+    const uint32_t tb = (uint32_t)tile * 32 * rowbytes;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qv[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Q + row + (D / 2) * half + 8 * ks));
-    if (epilogue) {
-      const uint16_t* gp = G + row + (nout ? dv0 : 0);
+    for (int ks = 0; ks < KS; ++ks) qv[ks] = __builtin_bit_cast(bf16x8, buf_load16(qr, qoff + tb + 16 * ks));
+    if constexpr (EPI) {
 #pragma unroll
-      for (int i = 0; i < NG; ++i) gv[i] = *reinterpret_cast<const uint4*>(gp + 8 * (8 * i < NO ? i : 0));
+      for (int i = 0; i < NG; ++i) gv[i] = buf_load16(gr, goff + tb + 16 * i);
     }
   };
 
   auto process = [&](int tile, const bf16x8 (&qv)[KS], const uint4 (&gv)[NG]) {
-    const int u = tile * 32 + n;
     f32x16 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{0.f};
@@ -101,50 +110,82 @@ __global__ __launch_bounds__(256, 2) void readout_bf16(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // lane holds o[dv0 + 16*mt + r] of token u in acc[mt][r]; epilogue in place
-    if (epilogue) {
+    // lane holds o[dv0 + 16*mt + r] of token n in acc[mt][r]; epilogue in place
+    if constexpr (EPI) {
       float ss = 0.f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) ss += acc[mt][r] * acc[mt][r];
       ss += __shfl_xor(ss, 32);
-      const float rinv = 1.f / __builtin_sqrtf(ss / (float)D + eps);
+      const float rinv = __builtin_amdgcn_rsqf(ss / (float)D + eps);
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         const uint32_t g4[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j0 = 8 * i + 2 * e, j1 = j0 + 1;
-          acc[j0 / 16][j0 % 16] *= rinv * sgam[dv0 + j0] * sigmoid(bf16_lo(g4[e]));
-          acc[j1 / 16][j1 % 16] *= rinv * sgam[dv0 + j1] * sigmoid(bf16_hi(g4[e]));
+          acc[j0 / 16][j0 % 16] *= rinv * sigmoid(bf16_lo(g4[e]));
+          acc[j1 / 16][j1 % 16] *= rinv * sigmoid(bf16_hi(g4[e]));
+        }
+      }
+      if constexpr (GAMMA) {
+        // RMSNorm gain: every lane of a half needs the same gains, so they are
+        // read at uniform addresses (scalar loads) and selected per half
+#pragma unroll
+        for (int j = 0; j < HALF; ++j) {
+          const float g0 = w[j];
+          const float g1 = w[HALF + j < D ? HALF + j : j];
+          acc[j / 16][j % 16] *= half ? g1 : g0;
         }
       }
     }
-    if (u < U) {
-      const size_t row = ((row_base + u) * H + h) * (size_t)D;
+    uint4 ov[NG];
 #pragma unroll
-      for (int i = 0; i < NG; ++i) {
-        if (8 * i < nout) {
-          const int m = (8 * i) / 16, r = (8 * i) % 16;
-          const uint4 o = make_uint4(pack_bf16x2(acc[m][r], acc[m][r + 1]), pack_bf16x2(acc[m][r + 2], acc[m][r + 3]),
-                                     pack_bf16x2(acc[m][r + 4], acc[m][r + 5]), pack_bf16x2(acc[m][r + 6], acc[m][r + 7]));
-          *reinterpret_cast<uint4*>(O + row + dv0 + 8 * i) = o;
+    for (int i = 0; i < NG; ++i) {
+      const int m = (8 * i) / 16, r = (8 * i) % 16;
+      ov[i] = make_uint4(pack_bf16x2(acc[m][r], acc[m][r + 1]), pack_bf16x2(acc[m][r + 2], acc[m][r + 3]),
+                         pack_bf16x2(acc[m][r + 4], acc[m][r + 5]), pack_bf16x2(acc[m][r + 6], acc[m][r + 7]));
+    }
+    // Output through LDS, 16 tokens at a time, so that every store instruction
+    // writes whole 256-byte rows (16 lanes per token row) instead of 16-byte
+    // pieces of 64 different rows.
+    const uint32_t tb = (uint32_t)tile * 32 * rowbytes;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int nr = n - 16 * rd;
+      if (owns && nr >= 0 && nr < 16) {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+          const int c = dv0 / 8 + i;
+          ost[nr * CH + (c ^ (nr & (CH - 1)))] = ov[i];
         }
       }
+      __builtin_amdgcn_wave_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+      for (int k = 0; k < OREADS; ++k) {
+        const int e = k * 64 + lane;
+        if (e < 16 * CH) {
+          const int tr = e / CH, c = e % CH;
+          const uint4 v = ost[tr * CH + (c ^ (tr & (CH - 1)))];
+          buf_store16(v, orr, tb + (uint32_t)(16 * rd + tr) * rowbytes + 16 * c);
+        }
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_wave_barrier();
     }
   };
 
   // two register sets: tile i+4 is in flight while tile i is multiplied
   bf16x8 qa[KS], qb[KS];
   uint4 ga[NG], gb[NG];
-  int tile = wave;
-  if (tile < ntiles) fetch(tile, qa, ga);
-  for (; tile < ntiles; tile += 8) {
-    if (tile + 4 < ntiles) fetch(tile + 4, qb, gb);
+  fetch(wave, qa, ga);
+  for (int k = 0; k < steps; k += 2) {
+    const int tile = wave + 4 * k;
+    fetch(tile + 4, qb, gb);
     process(tile, qa, ga);
-    if (tile + 4 >= ntiles) break;
-    if (tile + 8 < ntiles) fetch(tile + 8, qa, ga);
+    fetch(tile + 8, qa, ga);
     process(tile + 4, qb, gb);
   }
 }
@@ -249,11 +290,22 @@ hipError_t launch_readout_d(const Problem& p, const void* q, const void* gate, c
                             const void* rstates, void* out, hipStream_t s) {
   const unsigned grid = (unsigned)(p.B * p.T * p.H);
   const int epi = p.epilogue ? 1 : 0;
-  if (p.bf16)
-    hipLaunchKernelGGL(readout_bf16<D>, dim3(grid), dim3(256), 0, s,
+  const bool gam = w != nullptr;
+  if (p.bf16 && p.epilogue && gam)
+    hipLaunchKernelGGL((readout_bf16<D, true, true>), dim3(grid), dim3(256), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate), w,
                        static_cast<const uint4*>(rstates), static_cast<uint16_t*>(out), p.T, p.U,
-                       p.H, p.C, p.nc, epi, p.rms_eps);
+                       p.H, p.C, p.nc, p.rms_eps);
+  else if (p.bf16 && p.epilogue)
+    hipLaunchKernelGGL((readout_bf16<D, true, false>), dim3(grid), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate), w,
+                       static_cast<const uint4*>(rstates), static_cast<uint16_t*>(out), p.T, p.U,
+                       p.H, p.C, p.nc, p.rms_eps);
+  else if (p.bf16)
+    hipLaunchKernelGGL((readout_bf16<D, false, false>), dim3(grid), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate), w,
+                       static_cast<const uint4*>(rstates), static_cast<uint16_t*>(out), p.T, p.U,
+                       p.H, p.C, p.nc, p.rms_eps);
   else
     hipLaunchKernelGGL(readout_f32<D>, dim3(grid), dim3(256), 0, s,
                        static_cast<const float*>(q), static_cast<const float*>(gate), w,

@@ -73,11 +73,13 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   vec_t pf[KS];     // P^{-1} fragments of the frame being multiplied
   vec_t bw[4], al;  // B rows and alpha of the frame whose Y is being formed
 
+  // k-step ks of lane group g = lane / 16 covers channel (d/4) g + ks, so each
+  // lane reads a contiguous run of Y (128-bit LDS loads) and of P^{-1} rows
+  const int kg = (D / 4) * (lane >> 4);
   auto ld_p = [&](int s, vec_t (&dst)[KS]) {
-    const float* P = P0 + (size_t)s * D * D + c0;
+    const float* P = P0 + (size_t)s * D * D + c0 + (size_t)kg * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      dst[ks] = *reinterpret_cast<const vec_t*>(P + (4 * ks + (lane >> 4)) * D);
+    for (int ks = 0; ks < KS; ++ks) dst[ks] = *reinterpret_cast<const vec_t*>(P + ks * D);
   };
   auto ld_bw = [&](int s, vec_t (&dst)[4]) {
     const float* Bs = S0 + (size_t)s * 2 * D * D + (size_t)(row0 + rr) * D + c0;
@@ -93,23 +95,27 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
     for (int r = 0; r < 4; ++r)
       *reinterpret_cast<vec_t*>(&ylds[buf][(rr + r) * LDY + c0]) = sv[r] * a + bv[r];
   };
-  // S = Y P^{-1} from ylds[buf]
+  // S = Y P^{-1} from ylds[buf]; two accumulators per tile (even and odd k-step
+  // groups) keep four independent matrix-core chains in flight
   auto mul = [&](int buf, const vec_t (&p)[KS]) {
-    f32x4 acc[NV];
+    f32x4 acc[NV][2];
 #pragma unroll
-    for (int e = 0; e < NV; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float* yrow = &ylds[buf][(lane & 15) * LDY + (lane >> 4)];
+    for (int e = 0; e < NV; ++e) acc[e][0] = acc[e][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float* yrow = &ylds[buf][(lane & 15) * LDY + kg];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const float a = yrow[4 * ks];
+    for (int k4 = 0; k4 < KS / 4; ++k4) {
+      const float4 a4 = *reinterpret_cast<const float4*>(yrow + 4 * k4);
+      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-      for (int e = 0; e < NV; ++e)
-        acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, p[ks][e], acc[e], 0, 0, 0);
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < NV; ++e)
+          acc[e][q & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], p[4 * k4 + q][e], acc[e][q & 1], 0, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int e = 0; e < NV; ++e) st[r][e] = acc[e][r];
+      for (int e = 0; e < NV; ++e) st[r][e] = acc[e][0][r] + acc[e][1][r];
   };
   auto put_state = [&](float* dst) {
 #pragma unroll
@@ -124,7 +130,7 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   ld_bw(T, bw);
   ld_p(T, pf);
   put_y(0, zero4, vec_t(0.f), bw);
-  __syncthreads();
+  lds_barrier();
   mul(0, pf);
   if (dir == 0) put_state(s_text + head * (size_t)(D * D));
 #pragma unroll
@@ -180,7 +186,7 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
         ld_bw(s + step, bn);
         an = ld_al(s + step);
       }
-      __syncthreads();
+      lds_barrier();
       mul(buf, pf);
       const int j = rec_after(s);
       if (j >= 0) put_state(out0 + (size_t)j * D * D);

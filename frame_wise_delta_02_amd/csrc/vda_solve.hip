@@ -1,37 +1,42 @@
-// vda_solve: (I + A_t)^{-1} for every frame of every head, by Cholesky.
+// vda_solve: (I + A_t)^{-1} for every frame of every head, by Cholesky in LDS.
 //
 // The frame update S_t = (S_{t-1} Diag(alpha_t) + B_t)(I + A_t)^{-1} is solved in
 // the d_k x d_k key space ("Video DeltaNet" summary, onedev.kr/papers/80, section
 // "어떻게 쓰나"); the VDN-H3 write-up (discuss.pytorch.kr, hybrid attention
-// structure) notes that A_t is positive semidefinite, so P_t = I + A_t is
+// structure) notes that A_t is positive semidefinite, so P = I + A_t is
 // symmetric positive definite and has a Cholesky factor.  One workgroup
-// inverts one P_t:
-//   1. P = L L^T            right-looking blocked Cholesky, 8x8 blocks
-//   2. Y = L^{-1}           blocked forward substitution on the identity
-//   3. P^{-1} = Y^T Y       accumulated over block rows of Y
-// The matrix is distributed as 8x8 register blocks over (d/8)^2 threads; each
-// block step broadcasts one block column (or row) through LDS, so every
-// trailing update is a register-resident rank-8 update.  Everything is fp32.
-// The scan consumes P^{-1} directly: S M_t + J_t = (S Diag(alpha_t) + B_t) P^{-1},
-// so neither M_t nor J_t is ever formed in memory.
+// (4 waves) inverts one P, held in LDS:
+//   1. P = L L^T, right-looking over 16-column panels.  One wave factors the
+//      16x16 diagonal block in registers (lane = row, readlane broadcasts) and
+//      inverts it; the panel solve L_ik = P_ik L_kk^{-T} and the trailing
+//      update P_ij -= L_ik L_jk^T run on v_mfma_f32_16x16x4f32 in all waves.
+//   2. W = L^{-1} by blocked substitution down each block column (columns
+//      spread over the waves), stored transposed in P's unused upper triangle.
+//   3. P^{-1} = W^T W on the same matrix cores, written from the accumulators
+//      straight to global memory (both triangles).
+// Everything is fp32.  The scan consumes P^{-1} directly:
+// S M_t + J_t = (S Diag(alpha_t) + B_t) P^{-1}, so M_t and J_t are never formed.
 #include "vda_internal.h"
 
 namespace vda {
 namespace {
 
-constexpr int PAD = 68;  // floats per 8x8 block in LDS (64 + 4 avoids bank conflicts)
+constexpr int WDS = 17;  // row stride of the 16x16 diagonal-inverse blocks in LDS
+
+__device__ __forceinline__ float rdlane(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 
 template <int D>
-__global__ __launch_bounds__((D / 8) * (D / 8) > 64 ? (D / 8) * (D / 8) : 64)
-void solve_chol(const float* __restrict__ stats, float* __restrict__ pinv, int H, int T,
-                int n_video) {
-  constexpr int NT = D / 8;
-  constexpr int NTH = NT * NT;
-  __shared__ __attribute__((aligned(16))) float sdiag[64];
-  __shared__ __attribute__((aligned(16))) float scol[2][NT][PAD];  // L blocks, transposed [m][r]
-  __shared__ __attribute__((aligned(16))) float srow[2][NT][PAD];  // Y blocks, row-major [m][c]
+__global__ __launch_bounds__(256, 2) void solve_mfma(const float* __restrict__ stats,
+                                                    float* __restrict__ pinv, int H, int T,
+                                                    int n_video) {
+  constexpr int NB = D / 16;     // 16-wide panels
+  constexpr int LDP = D + 4;     // padded LDS row (conflict-free operand reads)
+  __shared__ __attribute__((aligned(16))) float P[D * LDP];
+  __shared__ float Wd[NB][16 * WDS];   // inverses of the diagonal blocks of L
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_slots = n_video + 1;
   int blk = blockIdx.x;
   const int si = blk % n_slots;
@@ -41,179 +46,153 @@ void solve_chol(const float* __restrict__ stats, float* __restrict__ pinv, int H
   const int slot = (si < n_video) ? 1 + si : T;  // video frames 1..T-2, then the text slot T
   const size_t mat = (size_t)(b * H + h) * (T + 1) + slot;
   const float* A = stats + mat * (size_t)(2 * D * D);
-  float* P = pinv + mat * (size_t)(D * D);
+  float* Pout = pinv + mat * (size_t)(D * D);
 
-  const bool active = tid < NTH;
-  const int ti = active ? tid / NT : 0, tj = active ? tid % NT : 0;
+  // lane roles for 16x16x4 MFMA operands / results
+  const int lm = lane & 15, lg = lane >> 4;
 
-  float a[8][8];
+  // ---- load P = I + A ------------------------------------------------------
+  for (int e = tid; e < D * D / 4; e += 256) {
+    const int r = e / (D / 4), c4 = e % (D / 4);
+    float4 x = reinterpret_cast<const float4*>(A + r * D)[c4];
+    const int c = 4 * c4;
+    x.x += (r == c) ? 1.f : 0.f;
+    x.y += (r == c + 1) ? 1.f : 0.f;
+    x.z += (r == c + 2) ? 1.f : 0.f;
+    x.w += (r == c + 3) ? 1.f : 0.f;
+    *reinterpret_cast<float4*>(&P[r * LDP + c]) = x;
+  }
+  __syncthreads();
+
+  // C (+)= sum over 4 k-steps of A(16x16) B(16x16); operand fetchers take (s)
+  auto tile_mma = [&](f32x4 acc, auto a_of, auto b_of) {
 #pragma unroll
-  for (int r = 0; r < 8; ++r)
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a_of(s), b_of(s), acc, 0, 0, 0);
+    return acc;
+  };
+
+  // ---- 1. Cholesky ------------------------------------------------------------
+  for (int k = 0; k < NB; ++k) {
+    if (wave == 0) {
+      const int i = lm;  // row of the diagonal block owned by this lane
+      float a[16];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) a[r][c] = 0.f;
-  if (active && ti >= tj) {
+      for (int c = 0; c < 16; ++c) a[c] = P[(16 * k + i) * LDP + 16 * k + c];
+      // hardware sqrt and reciprocal (about 1 ulp): this loop is the serial
+      // critical path of the whole inversion
+      float rdiag = 0.f;  // 1 / L[i][i] of this lane's row
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float4* src = reinterpret_cast<const float4*>(A + (8 * ti + r) * D + 8 * tj);
-      const float4 x0 = src[0], x1 = src[1];
-      a[r][0] = x0.x; a[r][1] = x0.y; a[r][2] = x0.z; a[r][3] = x0.w;
-      a[r][4] = x1.x; a[r][5] = x1.y; a[r][6] = x1.z; a[r][7] = x1.w;
+      for (int j = 0; j < 16; ++j) {
+        const float d = __builtin_amdgcn_sqrtf(rdlane(a[j], j));
+        const float inv = __builtin_amdgcn_rcpf(d);
+        const float l = (i > j) ? a[j] * inv : (i == j ? d : 0.f);
+        if (i == j) rdiag = inv;
+        a[j] = l;
+#pragma unroll
+        for (int c = j + 1; c < 16; ++c) a[c] -= l * rdlane(l, c);
+      }
+      // column c = lane of W_kk = L_kk^{-1} by forward substitution
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float sacc = (r == i) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < r; ++m) sacc -= rdlane(a[m], r) * x[m];
+        x[r] = sacc * rdlane(rdiag, r);
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) P[(16 * k + i) * LDP + 16 * k + c] = (c <= i) ? a[c] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Wd[k][r * WDS + i] = x[r];
+      }
     }
-    if (ti == tj) {
+    __syncthreads();
+    // panel: L_ik = P_ik W_kk^T, in place
+    for (int i = k + 1 + wave; i < NB; i += 4) {
+      const float* Pi = &P[(16 * i + lm) * LDP + 16 * k + lg];
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc = tile_mma(acc, [&](int s) { return Pi[4 * s]; },
+                     [&](int s) { return Wd[k][lm * WDS + 4 * s + lg]; });
 #pragma unroll
-      for (int r = 0; r < 8; ++r) a[r][r] += 1.f;
+      for (int r = 0; r < 4; ++r) P[(16 * i + 4 * lg + r) * LDP + 16 * k + lm] = acc[r];
     }
+    __syncthreads();
+    // trailing update of the lower blocks: P_ij -= L_ik L_jk^T, k < j <= i
+    {
+      const int m = NB - 1 - k;  // trailing blocks per side
+      const int ntr = m * (m + 1) / 2;
+      for (int idx = wave; idx < ntr; idx += 4) {
+        int i = 0, rem = idx;  // idx -> (i, j) over the lower triangle, row by row
+        while (rem > i) { rem -= i + 1; ++i; }
+        const int bi = k + 1 + i, bj = k + 1 + rem;
+        f32x4 acc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = P[(16 * bi + 4 * lg + r) * LDP + 16 * bj + lm];
+        const float* Li = &P[(16 * bi + lm) * LDP + 16 * k + lg];
+        const float* Lj = &P[(16 * bj + lm) * LDP + 16 * k + lg];
+        acc = tile_mma(acc, [&](int s) { return -Li[4 * s]; }, [&](int s) { return Lj[4 * s]; });
+#pragma unroll
+        for (int r = 0; r < 4; ++r) P[(16 * bi + 4 * lg + r) * LDP + 16 * bj + lm] = acc[r];
+      }
+    }
+    __syncthreads();
   }
 
-  // ---- 1. Cholesky: P = L L^T (lower), block column by block column ----------
-  for (int p = 0; p < NT; ++p) {
-    if (active && ti == p && tj == p) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float d = __builtin_sqrtf(a[j][j]);
-        const float inv = 1.f / d;
-        a[j][j] = d;
-#pragma unroll
-        for (int i = j + 1; i < 8; ++i) a[i][j] *= inv;
-#pragma unroll
-        for (int i = j + 1; i < 8; ++i)
-#pragma unroll
-          for (int c = j + 1; c <= i; ++c) a[i][c] -= a[i][j] * a[c][j];
+  // ---- 2. W = L^{-1}: block column j, top to bottom ---------------------------
+  // W_jj = Wd[j]; W_ij = -W_ii sum_{m=j}^{i-1} L_im W_mj.  W_ij (i > j) is kept
+  // transposed in the upper block (j, i).  Columns j and NB-1-j share a wave.
+  // The diagonal blocks of P are dead after step 1 (W_jj lives in Wd), so wave
+  // w uses diagonal block (w, w) as scratch to relayout a result into an operand.
+  auto Wb = [&](int m, int j, int kk, int n) -> float {  // W_mj[kk][n], m >= j
+    return (m == j) ? Wd[j][kk * WDS + n] : P[(16 * j + n) * LDP + 16 * m + kk];
+  };
+  float* Tx = &P[16 * wave * LDP + 16 * wave];
+  for (int pass = 0; pass < 2; ++pass) {
+    const int j = pass == 0 ? wave : NB - 1 - wave;
+    if (j < 0 || j >= NB || (pass == 1 && j < 4)) continue;
+    for (int i = j + 1; i < NB; ++i) {
+      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int m = j; m < i; ++m) {
+        const float* Lim = &P[(16 * i + lm) * LDP + 16 * m + lg];
+        t = tile_mma(t, [&](int s) { return Lim[4 * s]; }, [&](int s) { return Wb(m, j, 4 * s + lg, lm); });
       }
+      // relayout T through this wave's scratch, then W_ij = -W_ii T
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
+      for (int r = 0; r < 4; ++r) Tx[(4 * lg + r) * LDP + lm] = t[r];
+      __builtin_amdgcn_wave_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      f32x4 w = f32x4{0.f, 0.f, 0.f, 0.f};
+      w = tile_mma(w, [&](int s) { return -Wd[i][lm * WDS + 4 * s + lg]; },
+                   [&](int s) { return Tx[(4 * s + lg) * LDP + lm]; });
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int c = r + 1; c < 8; ++c) a[r][c] = 0.f;
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) sdiag[r * 8 + c] = a[r][c];
-    }
-    __syncthreads();
-    if (active && tj == p && ti > p) {
-      // X L_pp^T = A_ip, solved row by row
-      float invd[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) invd[c] = 1.f / sdiag[c * 8 + c];
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          float x = a[r][c];
-#pragma unroll
-          for (int m = 0; m < c; ++m) x -= a[r][m] * sdiag[c * 8 + m];
-          a[r][c] = x * invd[c];
-        }
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) scol[0][ti][m * 8 + r] = a[r][m];
-    }
-    __syncthreads();
-    if (active && ti > p && tj > p && ti >= tj) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float4* li = reinterpret_cast<const float4*>(&scol[0][ti][m * 8]);
-        const float4* lj = reinterpret_cast<const float4*>(&scol[0][tj][m * 8]);
-        const float4 i0 = li[0], i1 = li[1], j0 = lj[0], j1 = lj[1];
-        const float vi[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-        const float vj[8] = {j0.x, j0.y, j0.z, j0.w, j1.x, j1.y, j1.z, j1.w};
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) a[r][c] -= vi[r] * vj[c];
-      }
+      for (int r = 0; r < 4; ++r) P[(16 * j + lm) * LDP + 16 * i + 4 * lg + r] = w[r];
     }
   }
   __syncthreads();
 
-  // ---- 2. Y = L^{-1} (lower), block row by block row -------------------------
-  float y[8][8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) y[r][c] = (active && ti == tj && r == c) ? 1.f : 0.f;
-  for (int p = 0; p < NT; ++p) {
-    const int pb = p & 1;
-    if (active && tj == p && ti >= p) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) scol[pb][ti][m * 8 + r] = a[r][m];
-    }
-    __syncthreads();
-    if (active && ti == p && tj <= p) {
-      const float* L = scol[pb][p];  // L[r][m] = L[m * 8 + r]
-      float invd[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) invd[r] = 1.f / L[r * 8 + r];
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          float x = y[r][c];
-#pragma unroll
-          for (int m = 0; m < r; ++m) x -= L[m * 8 + r] * y[m][c];
-          y[r][c] = x * invd[r];
-        }
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) srow[0][tj][r * 8 + c] = y[r][c];
-    }
-    __syncthreads();
-    if (active && ti > p && tj <= p) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float4* li = reinterpret_cast<const float4*>(&scol[pb][ti][m * 8]);
-        const float4* yj = reinterpret_cast<const float4*>(&srow[0][tj][m * 8]);
-        const float4 i0 = li[0], i1 = li[1], j0 = yj[0], j1 = yj[1];
-        const float vi[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-        const float vj[8] = {j0.x, j0.y, j0.z, j0.w, j1.x, j1.y, j1.z, j1.w};
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) y[r][c] -= vi[r] * vj[c];
+  // ---- 3. P^{-1} = W^T W: lower blocks (i >= j), both triangles written -------
+  {
+    constexpr int NT = NB * (NB + 1) / 2;
+    for (int idx = wave; idx < NT; idx += 4) {
+      int i = 0, rem = idx;
+      while (rem > i) { rem -= i + 1; ++i; }
+      const int bi = i, bj = rem;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int m = bi; m < NB; ++m) {
+        // A = W_mi^T: A[p][kk] = W_mi[kk][p];  B = W_mj
+        acc = tile_mma(acc, [&](int s) { return Wb(m, bi, 4 * s + lg, lm); },
+                       [&](int s) { return Wb(m, bj, 4 * s + lg, lm); });
       }
-    }
-  }
-  __syncthreads();
-
-  // ---- 3. P^{-1} = Y^T Y, one block row of Y at a time ------------------------
 #pragma unroll
-  for (int r = 0; r < 8; ++r)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) a[r][c] = 0.f;
-  for (int k = 0; k < NT; ++k) {
-    const int kb = k & 1;
-    if (active && ti == k && tj <= k) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) srow[kb][tj][r * 8 + c] = y[r][c];
-    }
-    __syncthreads();
-    if (active && ti <= k && tj <= k) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float4* yi = reinterpret_cast<const float4*>(&srow[kb][ti][m * 8]);
-        const float4* yj = reinterpret_cast<const float4*>(&srow[kb][tj][m * 8]);
-        const float4 i0 = yi[0], i1 = yi[1], j0 = yj[0], j1 = yj[1];
-        const float vi[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-        const float vj[8] = {j0.x, j0.y, j0.z, j0.w, j1.x, j1.y, j1.z, j1.w};
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) a[r][c] += vi[r] * vj[c];
+      for (int r = 0; r < 4; ++r) Pout[(16 * bi + 4 * lg + r) * D + 16 * bj + lm] = acc[r];
+      if (bi != bj) {
+        *reinterpret_cast<float4*>(&Pout[(16 * bj + lm) * D + 16 * bi + 4 * lg]) =
+            make_float4(acc[0], acc[1], acc[2], acc[3]);
       }
-    }
-  }
-  if (active) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      float4* dst = reinterpret_cast<float4*>(P + (8 * ti + r) * D + 8 * tj);
-      dst[0] = make_float4(a[r][0], a[r][1], a[r][2], a[r][3]);
-      dst[1] = make_float4(a[r][4], a[r][5], a[r][6], a[r][7]);
     }
   }
 }
@@ -222,8 +201,7 @@ template <int D>
 hipError_t launch_solve_d(const Problem& p, const float* stats, float* pinv, hipStream_t s) {
   const int n_video = p.T > 2 ? p.T - 2 : 0;
   const unsigned grid = (unsigned)(p.B * p.H * (n_video + 1));
-  constexpr int threads = (D / 8) * (D / 8) > 64 ? (D / 8) * (D / 8) : 64;
-  hipLaunchKernelGGL(solve_chol<D>, dim3(grid), dim3(threads), 0, s, stats, pinv, p.H, p.T, n_video);
+  hipLaunchKernelGGL(solve_mfma<D>, dim3(grid), dim3(256), 0, s, stats, pinv, p.H, p.T, n_video);
   return hipGetLastError();
 }
 
