@@ -9,15 +9,18 @@
 //
 // Every token of a frame reads the same d_v x d_k state (its chunk's
 // F_{c-2} + R_{c+2}, or S_T for the two anchor frames), packed beforehand into
-// matrix-core operand order by the gather kernel.  A workgroup stages that state
-// in LDS once and streams the frame's tokens in 32-token tiles, one tile per wave
-// at a time, computing O^T = S Q^T on 32x32 matrix-core tiles:
-//   * B operand = Q^T: each lane holds 8 channels of one token, read straight
-//     from global memory as 16-byte loads (no LDS round trip for Q);
+// matrix-core operand order by the gather kernel.  A workgroup of 8 waves stages
+// that state in LDS once and streams the frame's tokens in 32-token tiles, one
+// tile per wave at a time, computing O^T = S Q^T on 32x32 matrix-core tiles:
+//   * every global access (Q, gate, output) is a coalesced row access, lanes on
+//     consecutive 16-byte chunks of a few token rows; a per-wave LDS tile
+//     (XOR-swizzled, conflict-free both ways) turns rows into operand order
+//     and the results back into rows;
+//   * B operand = Q^T: each lane holds 8 channels of one token;
 //   * A operand = S, with its rows permuted so that after the product each lane
 //     holds d_v/2 *consecutive* outputs of one token.  RMSNorm is then a sum in
-//     registers plus one cross-half lane swap, and the gate load and the output
-//     store are contiguous 16-byte accesses.
+//     registers plus one cross-half lane swap, and the gate and output move
+//     between registers and the LDS tile as whole 16-byte chunks.
 // bfloat16 path: S = S_hi + S_lo (two bf16 parts, ~16 significant bits) on
 // v_mfma_f32_32x32x16_bf16, so the fp32 state is not truncated to 8 bits.
 // float32 path: v_mfma_f32_32x32x2f32 with the fp32 state.
@@ -29,10 +32,11 @@ namespace {
 __device__ __forceinline__ float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 template <int D, bool EPI, bool GAMMA>
-__global__ __launch_bounds__(256, 2) void readout_bf16(
+__global__ __launch_bounds__(512, 1) void readout_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ G, const float* __restrict__ w,
     const uint4* __restrict__ rstates, uint16_t* __restrict__ O, int T, int U, int H, int C,
     int nc, float eps) {
+  constexpr int NW = 8;              // waves per workgroup
   constexpr int DP = D < 32 ? 32 : D;
   constexpr int HALF = DP / 2;       // outputs per lane
   constexpr int MT = DP / 32;
@@ -40,10 +44,14 @@ __global__ __launch_bounds__(256, 2) void readout_bf16(
   constexpr int NF = MT * KS * 64;   // 16-byte fragments per part (hi or lo)
   constexpr int NG = HALF / 8;       // 16-byte gate / output vectors per lane
   constexpr int CH = D / 8;          // 16-byte chunks per token row
-  constexpr int STAGE = (2 * NF + 255) / 256;
-  constexpr int OREADS = (16 * CH + 63) / 64;
+  constexpr int RPI = 64 / CH;       // token rows covered by one coalesced wave access
+  constexpr int NL = 32 / RPI;       // coalesced accesses per 32-token tile
+  constexpr int SWM = (CH < 8 ? CH : 8) - 1;             // swizzle: XOR mask on the chunk
+  constexpr int SWS = CH >= 8 ? 0 : (CH == 4 ? 1 : 2);   // log2 of the rows sharing 128 bytes
+  constexpr int STAGE = (2 * NF + 64 * NW - 1) / (64 * NW);
   __shared__ uint4 sfrag[2 * NF];
-  __shared__ uint4 ostage[4][16 * CH];  // per wave: 16 output rows, chunk index XOR-swizzled
+  __shared__ uint4 xbuf[NW][32 * CH];  // per wave: one 32-token tile, row-major, swizzled
+  __shared__ float4 sgam[GAMMA ? DP / 4 : 1];  // RMSNorm gain, padded with ones to DP
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int blk = blockIdx.x;
@@ -56,10 +64,13 @@ __global__ __launch_bounds__(256, 2) void readout_bf16(
     const uint4* src = rstates + ((size_t)(b * H + h) * (nc + 1) + slot) * 2 * NF;
     uint4 tmp[STAGE];  // all staging loads in flight before the first LDS write
 #pragma unroll
-    for (int i = 0; i < STAGE; ++i) tmp[i] = src[min(tid + 256 * i, 2 * NF - 1)];
+    for (int i = 0; i < STAGE; ++i) tmp[i] = src[min(tid + 64 * NW * i, 2 * NF - 1)];
 #pragma unroll
     for (int i = 0; i < STAGE; ++i)
-      if (tid + 256 * i < 2 * NF) sfrag[tid + 256 * i] = tmp[i];
+      if (tid + 64 * NW * i < 2 * NF) sfrag[tid + 64 * NW * i] = tmp[i];
+    if constexpr (GAMMA) {
+      if (tid < DP) reinterpret_cast<float*>(sgam)[tid] = tid < D ? w[tid] : 1.f;
+    }
   }
   __syncthreads();
 
@@ -73,27 +84,52 @@ __global__ __launch_bounds__(256, 2) void readout_bf16(
   const __amdgpu_buffer_rsrc_t orr = make_rsrc(O + fbase, nbytes);
   const __amdgpu_buffer_rsrc_t gr = make_rsrc(EPI ? G + fbase : Q + fbase, nbytes);
 
+  // Global traffic is coalesced: access i of a tile covers token rows
+  // RPI*i .. RPI*i + RPI-1, consecutive lanes on consecutive 16-byte chunks.
+  // The per-wave LDS tile turns rows into matrix-core operand order and back.
+  const int lrow = lane / CH, lch = lane % CH;
+  const uint32_t loff = (uint32_t)lrow * rowbytes + 16 * lch;
+  auto pos = [](int r, int c) { return r * CH + (c ^ ((r >> SWS) & SWM)); };
+
   const int n = lane & 31, half = lane >> 5;
   const int dv0 = HALF * half;                 // first output channel of this lane
   const bool owns = dv0 < D;                   // false only for the padding half at d = 16
-  const uint32_t qoff = (uint32_t)n * rowbytes + (D / 2) * half * 2;
-  const uint32_t goff = owns ? (uint32_t)n * rowbytes + dv0 * 2 : 0x80000000u;
   const int ntiles = (U + 31) / 32;
-  const int per_wave = (ntiles + 3) / 4;
+  const int per_wave = (ntiles + NW - 1) / NW;
   const int steps = (per_wave + 1) & ~1;       // even: the loop has no exit in the middle
-  uint4* ost = ostage[wave];
+  uint4* X = xbuf[wave];
 
-  auto fetch = [&](int tile, bf16x8 (&qv)[KS], uint4 (&gv)[NG]) {
-    const uint32_t tb = (uint32_t)tile * 32 * rowbytes;
+  auto fetch = [&](int tile, uint4 (&qv)[NL], uint4 (&gv)[NL]) {
+    const uint32_t tb = (uint32_t)tile * 32 * rowbytes + loff;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qv[ks] = __builtin_bit_cast(bf16x8, buf_load16(qr, qoff + tb + 16 * ks));
+    for (int i = 0; i < NL; ++i) qv[i] = buf_load16(qr, tb + (uint32_t)(RPI * i) * rowbytes);
     if constexpr (EPI) {
 #pragma unroll
-      for (int i = 0; i < NG; ++i) gv[i] = buf_load16(gr, goff + tb + 16 * i);
+      for (int i = 0; i < NL; ++i) gv[i] = buf_load16(gr, tb + (uint32_t)(RPI * i) * rowbytes);
     }
   };
+  // LDS accesses of one wave execute in order; these fences only keep the
+  // compiler from moving them across one another.
+  auto fence = [] {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_wave_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
 
-  auto process = [&](int tile, const bf16x8 (&qv)[KS], const uint4 (&gv)[NG]) {
+  auto process = [&](int tile, const uint4 (&qv)[NL], const uint4 (&gv)[NL]) {
+    // Q^T operand: lane (n, half) takes channels 8 * ((CH/2) * half + ks) .. + 7 of token n
+#pragma unroll
+    for (int i = 0; i < NL; ++i) X[pos(RPI * i + lrow, lch)] = qv[i];
+    fence();
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, X[pos(n, (CH / 2) * half + ks)]);
+    fence();
+    // the gate rows wait in the same LDS tile until the epilogue
+    if constexpr (EPI) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) X[pos(RPI * i + lrow, lch)] = gv[i];
+    }
     f32x16 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{0.f};
@@ -105,11 +141,12 @@ __global__ __launch_bounds__(256, 2) void readout_bf16(
       for (int mt = 0; mt < MT; ++mt) {
         const bf16x8 ahi = __builtin_bit_cast(bf16x8, sfrag[(mt * KS + ks) * 64 + lane]);
         const bf16x8 alo = __builtin_bit_cast(bf16x8, sfrag[NF + (mt * KS + ks) * 64 + lane]);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, qv[ks], acc[mt], 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, qv[ks], acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, qf[ks], acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, qf[ks], acc[mt], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    fence();
     // lane holds o[dv0 + 16*mt + r] of token n in acc[mt][r]; epilogue in place
     if constexpr (EPI) {
       float ss = 0.f;
@@ -121,72 +158,49 @@ __global__ __launch_bounds__(256, 2) void readout_bf16(
       const float rinv = __builtin_amdgcn_rsqf(ss / (float)D + eps);
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
-        const uint32_t g4[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
+        const uint4 gq = owns ? X[pos(n, dv0 / 8 + i)] : make_uint4(0, 0, 0, 0);
+        const uint32_t g4[4] = {gq.x, gq.y, gq.z, gq.w};
+        float gm[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+        if constexpr (GAMMA) {  // gains of channels dv0 + 8i .. + 7, read where they are used
+          const float4 a = sgam[(dv0 + 8 * i) / 4], c = sgam[(dv0 + 8 * i) / 4 + 1];
+          gm[0] = a.x; gm[1] = a.y; gm[2] = a.z; gm[3] = a.w;
+          gm[4] = c.x; gm[5] = c.y; gm[6] = c.z; gm[7] = c.w;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j0 = 8 * i + 2 * e, j1 = j0 + 1;
-          acc[j0 / 16][j0 % 16] *= rinv * sigmoid(bf16_lo(g4[e]));
-          acc[j1 / 16][j1 % 16] *= rinv * sigmoid(bf16_hi(g4[e]));
-        }
-      }
-      if constexpr (GAMMA) {
-        // RMSNorm gain: every lane of a half needs the same gains, so they are
-        // read at uniform addresses (scalar loads) and selected per half
-#pragma unroll
-        for (int j = 0; j < HALF; ++j) {
-          const float g0 = w[j];
-          const float g1 = w[HALF + j < D ? HALF + j : j];
-          acc[j / 16][j % 16] *= half ? g1 : g0;
+          acc[j0 / 16][j0 % 16] *= rinv * gm[2 * e] * sigmoid(bf16_lo(g4[e]));
+          acc[j1 / 16][j1 % 16] *= rinv * gm[2 * e + 1] * sigmoid(bf16_hi(g4[e]));
         }
       }
     }
-    uint4 ov[NG];
+    // outputs back to rows in the same LDS tile (each lane overwrites only the
+    // gate chunks it has read), then out as coalesced row stores
+    if (owns) {
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int m = (8 * i) / 16, r = (8 * i) % 16;
-      ov[i] = make_uint4(pack_bf16x2(acc[m][r], acc[m][r + 1]), pack_bf16x2(acc[m][r + 2], acc[m][r + 3]),
-                         pack_bf16x2(acc[m][r + 4], acc[m][r + 5]), pack_bf16x2(acc[m][r + 6], acc[m][r + 7]));
-    }
-    // Output through LDS, 16 tokens at a time, so that every store instruction
-    // writes whole 256-byte rows (16 lanes per token row) instead of 16-byte
-    // pieces of 64 different rows.
-    const uint32_t tb = (uint32_t)tile * 32 * rowbytes;
-#pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-      const int nr = n - 16 * rd;
-      if (owns && nr >= 0 && nr < 16) {
-#pragma unroll
-        for (int i = 0; i < NG; ++i) {
-          const int c = dv0 / 8 + i;
-          ost[nr * CH + (c ^ (nr & (CH - 1)))] = ov[i];
-        }
+      for (int i = 0; i < NG; ++i) {
+        const int m = (8 * i) / 16, r = (8 * i) % 16;
+        X[pos(n, dv0 / 8 + i)] =
+            make_uint4(pack_bf16x2(acc[m][r], acc[m][r + 1]), pack_bf16x2(acc[m][r + 2], acc[m][r + 3]),
+                       pack_bf16x2(acc[m][r + 4], acc[m][r + 5]), pack_bf16x2(acc[m][r + 6], acc[m][r + 7]));
       }
-      __builtin_amdgcn_wave_barrier();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-#pragma unroll
-      for (int k = 0; k < OREADS; ++k) {
-        const int e = k * 64 + lane;
-        if (e < 16 * CH) {
-          const int tr = e / CH, c = e % CH;
-          const uint4 v = ost[tr * CH + (c ^ (tr & (CH - 1)))];
-          buf_store16(v, orr, tb + (uint32_t)(16 * rd + tr) * rowbytes + 16 * c);
-        }
-      }
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_wave_barrier();
     }
+    fence();
+    const uint32_t tb = (uint32_t)tile * 32 * rowbytes + loff;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) buf_store16(X[pos(RPI * i + lrow, lch)], orr, tb + (uint32_t)(RPI * i) * rowbytes);
+    fence();
   };
 
-  // two register sets: tile i+4 is in flight while tile i is multiplied
-  bf16x8 qa[KS], qb[KS];
-  uint4 ga[NG], gb[NG];
+  // two register sets: tile i + NW is in flight while tile i is multiplied
+  uint4 qa[NL], qb[NL], ga[NL], gb[NL];
   fetch(wave, qa, ga);
   for (int k = 0; k < steps; k += 2) {
-    const int tile = wave + 4 * k;
-    fetch(tile + 4, qb, gb);
+    const int tile = wave + NW * k;
+    fetch(tile + NW, qb, gb);
     process(tile, qa, ga);
-    fetch(tile + 8, qa, ga);
-    process(tile + 4, qb, gb);
+    fetch(tile + 2 * NW, qa, ga);
+    process(tile + NW, qb, gb);
   }
 }
 
@@ -292,17 +306,17 @@ hipError_t launch_readout_d(const Problem& p, const void* q, const void* gate, c
   const int epi = p.epilogue ? 1 : 0;
   const bool gam = w != nullptr;
   if (p.bf16 && p.epilogue && gam)
-    hipLaunchKernelGGL((readout_bf16<D, true, true>), dim3(grid), dim3(256), 0, s,
+    hipLaunchKernelGGL((readout_bf16<D, true, true>), dim3(grid), dim3(512), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate), w,
                        static_cast<const uint4*>(rstates), static_cast<uint16_t*>(out), p.T, p.U,
                        p.H, p.C, p.nc, p.rms_eps);
   else if (p.bf16 && p.epilogue)
-    hipLaunchKernelGGL((readout_bf16<D, true, false>), dim3(grid), dim3(256), 0, s,
+    hipLaunchKernelGGL((readout_bf16<D, true, false>), dim3(grid), dim3(512), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate), w,
                        static_cast<const uint4*>(rstates), static_cast<uint16_t*>(out), p.T, p.U,
                        p.H, p.C, p.nc, p.rms_eps);
   else if (p.bf16)
-    hipLaunchKernelGGL((readout_bf16<D, false, false>), dim3(grid), dim3(256), 0, s,
+    hipLaunchKernelGGL((readout_bf16<D, false, false>), dim3(grid), dim3(512), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate), w,
                        static_cast<const uint4*>(rstates), static_cast<uint16_t*>(out), p.T, p.U,
                        p.H, p.C, p.nc, p.rms_eps);
