@@ -17,13 +17,18 @@
 // |sqrt(beta) v| beyond 65504 would overflow the half range).
 // The token axis is the contraction axis but is the strided axis in memory
 // ([.., U, H, d] layout), so each 64-token tile is staged through LDS
-// transposed: every loader thread reads 4 tokens x 8 channels (coalesced 16-byte
-// loads along d; K and V come from different waves), scales and rounds them,
-// transposes the 4x8 block in registers and writes 8 rows of 8 bytes.  Rows are
-// 128 bytes (64 tokens) with an XOR swizzle of the 16-byte chunk index so that
-// the MFMA operand reads hit distinct banks.  Eight waves split the (2d x d)
-// output 4 x 2, so each holds 64 accumulators; two LDS buffers and two register
-// stages keep two tiles of loads in flight behind the current tile's MFMAs.
+// transposed, one row per channel (128 bytes = 64 tokens, the 16-byte chunk
+// index XOR-swizzled so that matrix-core operand reads hit distinct banks).
+// The workgroup is split by role, one wave of each role per SIMD, so that the
+// conversion work of one overlaps the matrix work of the other:
+//   * 4 producer waves (2 on K, 2 on V) read coalesced token rows, each thread
+//     d/16 tokens x 8 channels, scale by sqrt(beta) and round to half; pairing
+//     two tokens of one channel in each packed conversion gives the transposed
+//     row piece directly, written as one 16-byte LDS store at d = 128;
+//   * 4 consumer waves run the MFMAs, each holding a (2d/4 x d) output block.
+// Two register stages keep two tiles of loads in flight ahead of the tile
+// being written, and two LDS buffers let the consumers read one tile while
+// the producers write the next; one LDS barrier per tile separates them.
 //
 // float32 inputs: v_mfma_f32_16x16x4f32 takes one token per lane, so tiles are
 // staged in natural token-major order (rows padded by 16 floats).
@@ -40,142 +45,160 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(
     const uint16_t* __restrict__ beta, float* __restrict__ stats,
     int T_in, int U, int H, int t_first, int n_frames, int slot_offset, int T_slots) {
   constexpr int R = 2 * D;          // rows of [Z | W]^T
-  constexpr int CGT = D / 8;        // 16-byte channel groups per token and tensor
-  constexpr int PER_T = CGT * 16;   // loader threads per tensor: 16 groups of 4 tokens
+  constexpr int CGT = D / 8;        // 16-byte channel groups per token
+  constexpr int TPT = CGT / 2;      // tokens per producer thread and tile (128 threads per tensor)
   constexpr int MT = R / 16, NT = D / 16;
-  constexpr int WM = MT >= 4 ? 4 : MT, WN = NT >= 2 ? 2 : 1;  // wave grid over output tiles
-  constexpr int MTW = MT / WM, NTW = NT / WN;
+  constexpr int WM = MT >= 4 ? 4 : MT;  // consumer waves, each MT/WM row tiles x all NT column tiles
+  constexpr int MTW = MT / WM;
+  constexpr int NS = 2;             // producer register stages
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][R * 128];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // block decode kept in scalar registers: the buffer descriptors built from it
+  // must be provably wave-uniform
   int blk = blockIdx.x;
-  const int h = blk % H;
+  const int h = sgpr(blk % H);
   blk /= H;
-  const int fi = blk % n_frames;
-  const int b = blk / n_frames;
+  const int fi = sgpr(blk % n_frames);
+  const int b = sgpr(blk / n_frames);
   const int t = t_first + fi;
   const size_t tok0 = ((size_t)b * T_in + t) * (size_t)U;
+  // tiles processed: a multiple of the stage count, so the loops below have no
+  // exit in the middle; tiles wholly past the end are zero and touch no memory
+  const int nstep = ((U + 63) / 64 + NS - 1) / NS * NS;
 
-  // loader role: PER_T threads read K and PER_T read V, each 4 consecutive
-  // tokens x 8 channels per tile.  Buffer loads
-  // over this frame and head return zero past the last token, so the tail tile
-  // and the prefetch past the end need no clamping: a zero beta zeroes the token.
-  // even waves load K, odd waves V (readfirstlane: the choice, and with it the
-  // buffer descriptor, is provably wave-uniform and lives in scalar registers)
-  const int which = __builtin_amdgcn_readfirstlane(wave & 1);
-  const int local = (wave >> 1) * 64 + lane;
-  const bool loader = local < PER_T;
-  const int cg = local % CGT, tg = (local / CGT) & 15;
-  const uint32_t rowbytes = (uint32_t)H * D * 2;  // bytes between consecutive tokens
-  const uint32_t xbytes = U > 0 ? (uint32_t)(U - 1) * rowbytes + D * 2 : 0;
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc((which ? V : K) + (tok0 * H + h) * (size_t)D, xbytes);
-  const __amdgpu_buffer_rsrc_t br =
-      make_rsrc(beta + tok0 * H + h, U > 0 ? (uint32_t)(U - 1) * H * 2 + 2 : 0);
-  const uint32_t xoff0 = (loader ? (uint32_t)(tg * 4) * rowbytes : xbytes) + cg * 16;
-  const uint32_t boff0 = (loader ? (uint32_t)(tg * 4) : (uint32_t)U) * H * 2;
-  const int rowbase = which * D + cg * 8;  // first LDS row this thread writes
+  if (wave < 4) {
+    // ---- producers ----------------------------------------------------------
+    // Buffer loads over this frame and head return zero past the last token, so
+    // the tail tile and the loads past the end need no clamping: a zero beta
+    // zeroes the token.  The tensor choice, and with it the buffer descriptor,
+    // is wave-uniform.
+    const int which = wave >> 1;
+    const int local = (wave & 1) * 64 + lane;
+    const int cg = local % CGT, tq = local / CGT;
+    const int tok = TPT * tq;  // first of this thread's TPT consecutive tokens in the tile
+    const uint32_t rowbytes = (uint32_t)H * D * 2;  // bytes between consecutive tokens
+    const uint32_t xbytes = U > 0 ? (uint32_t)(U - 1) * rowbytes + D * 2 : 0;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc((which ? V : K) + (tok0 * H + h) * (size_t)D, xbytes);
+    const __amdgpu_buffer_rsrc_t br =
+        make_rsrc(beta + tok0 * H + h, U > 0 ? (uint32_t)(U - 1) * H * 2 + 2 : 0);
+    const uint32_t xoff0 = (uint32_t)tok * rowbytes + cg * 16;
+    // Each producer wave covers 32 consecutive tokens of a tile, so one beta load
+    // per lane (lanes l and l+32 read the same token) and one square root serve
+    // the wave; a thread takes its tokens' sqrt(beta) from lanes tl .. tl+TPT-1.
+    const uint32_t boff0 = (uint32_t)(32 * (wave & 1) + (lane & 31)) * H * 2;
+    const int tl = TPT * (lane / CGT);  // this thread's first token within the wave's 32
+    // this thread writes channels 8cg .. 8cg+7 (rows), tokens tok .. tok+TPT-1
+    const int row0 = which * D + 8 * cg;
+    const int q = tok / 8, hb = 2 * (tok % 8);
 
-  const int wm = wave % WM, wn = (wave / WM) % WN;
-  const bool mma = wave < WM * WN;
-
-  f32x4 acc[MTW][NTW];
+    uint4 x[NS][TPT];
+    uint32_t sb[NS];  // raw beta bits of token 32 * (wave & 1) + (lane & 31)
+    auto load = [&](int s, int it) {
+      const uint32_t xo = xoff0 + (uint32_t)(it * 64) * rowbytes;
 #pragma unroll
-  for (int i = 0; i < MTW; ++i)
+      for (int j = 0; j < TPT; ++j) x[s][j] = buf_load16(xr, xo + j * rowbytes);
+      sb[s] = __builtin_amdgcn_raw_buffer_load_b16(br, boff0 + (uint32_t)(it * 64) * H * 2, 0, 0);
+    };
+    auto store = [&](int s, int buf) {
+      const int sq = __float_as_int(__builtin_amdgcn_sqrtf(bf16_to_f32((uint16_t)sb[s])));
+      float sc[TPT];
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  uint4 reg0[4], reg1[4];
-  uint32_t sb0[4], sb1[4];  // raw beta bits (zero past the last token)
-  const int ntile = (U + 63) / 64;
-
-  auto load = [&](uint4 (&reg)[4], uint32_t (&sb)[4], int it) {
-    const uint32_t xo = xoff0 + (uint32_t)(it * 64) * rowbytes;
-    const uint32_t bo = boff0 + (uint32_t)(it * 64) * H * 2;
+      for (int j = 0; j < TPT; ++j) sc[j] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (tl + j), sq));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      reg[j] = buf_load16(xr, xo + j * rowbytes);
-      sb[j] = __builtin_amdgcn_raw_buffer_load_b16(br, bo + j * H * 2, 0, 0);
-    }
-  };
-
-  // scale by sqrt(beta), round to half, transpose 4 tokens x 8 channels, and
-  // write one 8-byte piece (4 tokens) to each of 8 LDS rows
-  auto store = [&](const uint4 (&reg)[4], const uint32_t (&sb)[4], int buf) {
-    if (!loader) return;
-    uint32_t w[4][4];
+      for (int i = 0; i < 8; ++i) {
+        float v[TPT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float sc = __builtin_amdgcn_sqrtf(bf16_to_f32((uint16_t)sb[j]));
-      const uint32_t x[4] = {reg[j].x, reg[j].y, reg[j].z, reg[j].w};
-#pragma unroll
-      for (int d = 0; d < 4; ++d) w[j][d] = pack_f16x2(bf16_lo(x[d]) * sc, bf16_hi(x[d]) * sc);
-    }
-    const int q = tg >> 1, hb = (tg & 1) * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t o[2];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const uint32_t a = w[2 * p][i >> 1], c = w[2 * p + 1][i >> 1];
-        o[p] = (i & 1) ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
+        for (int j = 0; j < TPT; ++j) {
+          const uint32_t wd = (i >> 1) == 0 ? x[s][j].x : (i >> 1) == 1 ? x[s][j].y : (i >> 1) == 2 ? x[s][j].z : x[s][j].w;
+          v[j] = ((i & 1) ? bf16_hi(wd) : bf16_lo(wd)) * sc[j];
+        }
+        const int r = row0 + i;
+        uint8_t* dst = lds[buf] + r * 128 + 16 * (q ^ swz(r)) + hb;
+        if constexpr (TPT == 8) {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]),
+                                                      pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7]));
+        } else if constexpr (TPT == 4) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]));
+        } else if constexpr (TPT == 2) {
+          *reinterpret_cast<uint32_t*>(dst) = pack_f16x2(v[0], v[1]);
+        } else {
+          *reinterpret_cast<_Float16*>(dst) = (_Float16)v[0];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one row's values live at a time
       }
-      const int r = rowbase + i;
-      *reinterpret_cast<uint2*>(lds[buf] + r * 128 + 16 * (q ^ swz(r)) + hb) = make_uint2(o[0], o[1]);
-    }
-  };
+    };
 
-  auto compute = [&](int buf) {
-    if (!mma) return;
-    const uint8_t* base = lds[buf];
+    // tile i+1 is written while the consumers multiply tile i; the stage it
+    // came from is refilled at once with tile i+1+NS
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int q = 4 * s + (lane >> 4);
-      f16x8 afr[MTW];
-#pragma unroll
-      for (int mi = 0; mi < MTW; ++mi) {
-        const int r = 16 * (wm * MTW + mi) + (lane & 15);
-        afr[mi] = *reinterpret_cast<const f16x8*>(base + r * 128 + 16 * (q ^ swz(r)));
-      }
-#pragma unroll
-      for (int nj = 0; nj < NTW; ++nj) {
-        const int r = 16 * (wn * NTW + nj) + (lane & 15);
-        const f16x8 bfr = *reinterpret_cast<const f16x8*>(base + r * 128 + 16 * (q ^ swz(r)));
-#pragma unroll
-        for (int mi = 0; mi < MTW; ++mi)
-          acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[mi], bfr, acc[mi][nj], 0, 0, 0);
-      }
-    }
-  };
-
-  // Software pipeline: tile i sits in LDS buffer i&1 while tiles i+1 and i+2
-  // are in flight in the two register stages.
-  // The trip count is rounded up to even so the loop has no exit in the middle;
-  // a tile wholly past the end loads zeros without touching memory.
-  load(reg0, sb0, 0);
-  load(reg1, sb1, 1);
-  store(reg0, sb0, 0);
-  lds_barrier();
-  for (int it = 0; it < ntile; it += 2) {
-    load(reg0, sb0, it + 2);
-    compute(0);
-    store(reg1, sb1, 1);
+    for (int s = 0; s < NS; ++s) load(s, s);
+    store(0, 0);
+    load(0, NS);
     lds_barrier();
-    load(reg1, sb1, it + 3);
-    compute(1);
-    store(reg0, sb0, 0);
-    lds_barrier();
-  }
+    for (int it = 0; it < nstep; it += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int s = (u + 1) % NS;  // stage holding tile it+u+1
+        store(s, (u + 1) & 1);
+        load(s, it + u + 1 + NS);
+        lds_barrier();
+      }
+    }
+  } else {
+    // ---- consumers ----------------------------------------------------------
+    const int wm = wave - 4;
+    const bool mma = wm < WM;
+    f32x4 acc[MTW][NT];
+#pragma unroll
+    for (int i = 0; i < MTW; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (mma) {
-    float* out = stats + ((size_t)(b * H + h) * T_slots + (t + slot_offset)) * (size_t)(R * D);
+    auto compute = [&](int buf) {
+      const uint8_t* base = lds[buf];
 #pragma unroll
-    for (int mi = 0; mi < MTW; ++mi)
+      for (int ks = 0; ks < 2; ++ks) {
+        const int qq = 4 * ks + (lane >> 4);
+        f16x8 afr[MTW];
 #pragma unroll
-      for (int nj = 0; nj < NTW; ++nj)
+        for (int mi = 0; mi < MTW; ++mi) {
+          const int r = 16 * (wm * MTW + mi) + (lane & 15);
+          afr[mi] = *reinterpret_cast<const f16x8*>(base + r * 128 + 16 * (qq ^ swz(r)));
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          out[(16 * (wm * MTW + mi) + 4 * (lane >> 4) + r) * D + 16 * (wn * NTW + nj) + (lane & 15)] =
-              acc[mi][nj][r];
+        for (int nj = 0; nj < NT; ++nj) {
+          const int r = 16 * nj + (lane & 15);
+          const f16x8 bfr = *reinterpret_cast<const f16x8*>(base + r * 128 + 16 * (qq ^ swz(r)));
+#pragma unroll
+          for (int mi = 0; mi < MTW; ++mi)
+            acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[mi], bfr, acc[mi][nj], 0, 0, 0);
+        }
+        // one k-step of operands live at a time (beside 128 accumulators at d = 128)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    lds_barrier();
+    for (int it = 0; it < nstep; it += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        if (mma) compute(u & 1);
+        lds_barrier();
+      }
+    }
+
+    if (mma) {
+      float* out = stats + ((size_t)(b * H + h) * T_slots + (t + slot_offset)) * (size_t)(R * D);
+#pragma unroll
+      for (int mi = 0; mi < MTW; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NT; ++nj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            out[(16 * (wm * MTW + mi) + 4 * (lane >> 4) + r) * D + 16 * nj + (lane & 15)] = acc[mi][nj][r];
+    }
   }
 }
 

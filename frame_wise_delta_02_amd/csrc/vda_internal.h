@@ -53,6 +53,16 @@ __device__ __forceinline__ void buf_store16(uint4 v, __amdgpu_buffer_rsrc_t r, u
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, 0);
 }
 
+// A wave-uniform value forced into a scalar register.  The optimiser drops
+// __builtin_amdgcn_readfirstlane on values it already considers uniform, and
+// may then compute them in vector registers anyway; a buffer descriptor built
+// from such a value turns every load into a waterfall loop.  The asm is opaque.
+__device__ __forceinline__ int sgpr(int v) {
+  int r;
+  asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(r) : "v"(v));
+  return r;
+}
+
 // Workgroup barrier for LDS exchange only.  __syncthreads() is a full
 // workgroup fence, so it also waits for every global load in flight
 // (s_waitcnt vmcnt(0)) and drains any software prefetch.  Here each wave only
