@@ -21,6 +21,8 @@
 // frame's P^{-1}, B and alpha are prefetched into registers while the current
 // frame's MFMAs run.  Row blocks of one head go to the same XCD (blockIdx % 8)
 // so the P^{-1}_s they all read is shared in that XCD's L2.
+#include <type_traits>
+
 #include "vda_internal.h"
 
 namespace vda {
@@ -223,30 +225,47 @@ __global__ __launch_bounds__(256) void gather_states(const float* __restrict__ s
     if (slot >= 2) Fp = fwd + (head * nc + (slot - 2)) * D * D;
     if (slot + 2 <= nc - 1) Rp = rev + (head * nc + (slot + 2)) * D * D;
   }
-  auto value = [&](int dv, int ch) -> float {
-    if (dv >= D) return 0.f;
-    const size_t i = (size_t)dv * D + ch;
-    if (slot == nc) return ST[i];
-    const float f = Fp ? Fp[i] : 0.5f * ST[i];
-    const float r = Rp ? Rp[i] : 0.5f * ST[i];
-    return f + r;
-  };
   auto dv_of = [&](int mt, int m) { return HALF * ((m >> 2) & 1) + 16 * mt + 4 * (m >> 3) + (m & 3); };
+  // The slot's state is wf F + wr R: a missing side reads S_T with weight 1/2,
+  // and the anchor slot reads S_T twice with weight 1/2 (x/2 + x/2 = x exactly
+  // for normal numbers),
+  // so every fragment is four float4 loads with no branch.
+  const float* Fs = Fp ? Fp : ST;
+  const float* Rs = Rp ? Rp : ST;
+  const float wf = Fp ? 1.f : 0.5f, wr = Rp ? 1.f : 0.5f;
+  // row dv, channels ch .. ch + 4*NQ - 1 (zero past d); loads before arithmetic
+  auto rowvals = [&](int dv, int ch, float4* o, auto nq) {
+    constexpr int NQ = decltype(nq)::value;
+    const size_t i = (size_t)(dv < D ? dv : 0) * D + ch;
+    float4 f[NQ], r[NQ];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      f[j] = *reinterpret_cast<const float4*>(Fs + i + 4 * j);
+      r[j] = *reinterpret_cast<const float4*>(Rs + i + 4 * j);
+    }
+    const float z = dv < D ? 1.f : 0.f;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j)
+      o[j] = make_float4(z * (wf * f[j].x + wr * r[j].x), z * (wf * f[j].y + wr * r[j].y),
+                         z * (wf * f[j].z + wr * r[j].z), z * (wf * f[j].w + wr * r[j].w));
+  };
 
   if constexpr (BF16) {
     constexpr int KS = D / 16;
     constexpr int NF = MT * KS * 64;  // fragments per half (hi or lo)
     uint4* out = static_cast<uint4*>(rstates) + (size_t)blockIdx.x * 2 * NF;
+#pragma unroll 2
     for (int f = threadIdx.x; f < NF; f += blockDim.x) {
       const int lane = f % 64, ks = (f / 64) % KS, mt = f / (64 * KS);
-      const int dv = dv_of(mt, lane & 31);
-      const int ch0 = (D / 2) * (lane >> 5) + 8 * ks;
+      float4 v[2];
+      rowvals(dv_of(mt, lane & 31), (D / 2) * (lane >> 5) + 8 * ks, v, std::integral_constant<int, 2>());
+      const float x[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         __bf16 h0, l0, h1, l1;
-        split_bf16(value(dv, ch0 + 2 * e), h0, l0);
-        split_bf16(value(dv, ch0 + 2 * e + 1), h1, l1);
+        split_bf16(x[2 * e], h0, l0);
+        split_bf16(x[2 * e + 1], h1, l1);
         hi[e] = __builtin_bit_cast(uint32_t, bf16x2{h0, h1});
         lo[e] = __builtin_bit_cast(uint32_t, bf16x2{l0, l1});
       }
@@ -257,11 +276,12 @@ __global__ __launch_bounds__(256) void gather_states(const float* __restrict__ s
     constexpr int KQ = D / 8;  // groups of 4 k-steps (32x32x2: one channel per half per step)
     constexpr int NF = MT * KQ * 64;
     float4* out = static_cast<float4*>(rstates) + (size_t)blockIdx.x * NF;
+#pragma unroll 2
     for (int f = threadIdx.x; f < NF; f += blockDim.x) {
       const int lane = f % 64, kq = (f / 64) % KQ, mt = f / (64 * KQ);
-      const int dv = dv_of(mt, lane & 31);
-      const int ch0 = (D / 2) * (lane >> 5) + 4 * kq;
-      out[f] = make_float4(value(dv, ch0), value(dv, ch0 + 1), value(dv, ch0 + 2), value(dv, ch0 + 3));
+      float4 v[1];
+      rowvals(dv_of(mt, lane & 31), (D / 2) * (lane >> 5) + 4 * kq, v, std::integral_constant<int, 1>());
+      out[f] = v[0];
     }
   }
 }

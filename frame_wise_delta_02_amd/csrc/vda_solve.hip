@@ -52,15 +52,29 @@ __global__ __launch_bounds__(256, 2) void solve_mfma(const float* __restrict__ s
   const int lm = lane & 15, lg = lane >> 4;
 
   // ---- load P = I + A ------------------------------------------------------
-  for (int e = tid; e < D * D / 4; e += 256) {
-    const int r = e / (D / 4), c4 = e % (D / 4);
-    float4 x = reinterpret_cast<const float4*>(A + r * D)[c4];
-    const int c = 4 * c4;
-    x.x += (r == c) ? 1.f : 0.f;
-    x.y += (r == c + 1) ? 1.f : 0.f;
-    x.z += (r == c + 2) ? 1.f : 0.f;
-    x.w += (r == c + 3) ? 1.f : 0.f;
-    *reinterpret_cast<float4*>(&P[r * LDP + c]) = x;
+  // every load is issued before the first LDS store: a load-store loop waits a
+  // full memory round trip per iteration
+  {
+    constexpr int NV4 = D * D / 4;               // float4 of A
+    constexpr int PER = (NV4 + 255) / 256;
+    float4 x[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + 256 * i;
+      x[i] = (NV4 % 256 == 0 || e < NV4) ? reinterpret_cast<const float4*>(A)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + 256 * i;
+      if (NV4 % 256 == 0 || e < NV4) {
+        const int r = e / (D / 4), c = 4 * (e % (D / 4));
+        x[i].x += (r == c) ? 1.f : 0.f;
+        x[i].y += (r == c + 1) ? 1.f : 0.f;
+        x[i].z += (r == c + 2) ? 1.f : 0.f;
+        x[i].w += (r == c + 3) ? 1.f : 0.f;
+        *reinterpret_cast<float4*>(&P[r * LDP + c]) = x[i];
+      }
+    }
   }
   __syncthreads();
 
