@@ -39,11 +39,28 @@ namespace {
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
+// One part of a launch: frames t_first .. t_first + n_frames - 1 of inputs laid
+// out [B, T_in, U, H, d], written to stats slots t + slot_offset.
+template <typename TIO>
+struct GramArgs {
+  const TIO* K;
+  const TIO* V;
+  const TIO* beta;
+  int T_in, U, t_first, n_frames, slot_offset;
+};
+
 template <int D>
-__global__ __launch_bounds__(512, 1) void gram_bf16(
-    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ beta, float* __restrict__ stats,
-    int T_in, int U, int H, int t_first, int n_frames, int slot_offset, int T_slots) {
+__global__ __launch_bounds__(512, 1) void gram_bf16(GramArgs<uint16_t> part0, GramArgs<uint16_t> part1,
+                                                    int nblk0, float* __restrict__ stats, int H,
+                                                    int T_slots) {
+  // blocks 0 .. nblk0-1 run part 0 (the video frames), the rest part 1 (the
+  // text frame, short: it fills the last round of the video blocks)
+  const bool second = (int)blockIdx.x >= nblk0;
+  const GramArgs<uint16_t> g = second ? part1 : part0;
+  const uint16_t* __restrict__ K = g.K;
+  const uint16_t* __restrict__ V = g.V;
+  const uint16_t* __restrict__ beta = g.beta;
+  const int T_in = g.T_in, U = g.U, t_first = g.t_first, n_frames = g.n_frames, slot_offset = g.slot_offset;
   constexpr int R = 2 * D;          // rows of [Z | W]^T
   constexpr int CGT = D / 8;        // 16-byte channel groups per token
   constexpr int TPT = CGT / 2;      // tokens per producer thread and tile (128 threads per tensor)
@@ -57,7 +74,7 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // block decode kept in scalar registers: the buffer descriptors built from it
   // must be provably wave-uniform
-  int blk = blockIdx.x;
+  int blk = (int)blockIdx.x - (second ? nblk0 : 0);
   const int h = sgpr(blk % H);
   blk /= H;
   const int fi = sgpr(blk % n_frames);
@@ -203,10 +220,14 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void gram_f32(
-    const float* __restrict__ K, const float* __restrict__ V, const float* __restrict__ beta,
-    float* __restrict__ stats, int T_in, int U, int H, int t_first, int n_frames,
-    int slot_offset, int T_slots) {
+__global__ __launch_bounds__(256, 2) void gram_f32(GramArgs<float> part0, GramArgs<float> part1, int nblk0,
+                                                   float* __restrict__ stats, int H, int T_slots) {
+  const bool second = (int)blockIdx.x >= nblk0;
+  const GramArgs<float> g = second ? part1 : part0;
+  const float* __restrict__ K = g.K;
+  const float* __restrict__ V = g.V;
+  const float* __restrict__ beta = g.beta;
+  const int T_in = g.T_in, U = g.U, t_first = g.t_first, n_frames = g.n_frames, slot_offset = g.slot_offset;
   constexpr int R = 2 * D;
   constexpr int TT = 16;           // tokens per tile
   constexpr int LD = R + 16;       // padded floats per token row
@@ -217,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void gram_f32(
   __shared__ __attribute__((aligned(16))) float lds[2][TT * LD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int blk = blockIdx.x;
+  int blk = (int)blockIdx.x - (second ? nblk0 : 0);
   const int h = blk % H;
   blk /= H;
   const int fi = blk % n_frames;
@@ -314,35 +335,40 @@ __global__ __launch_bounds__(256, 2) void gram_f32(
 }
 
 template <int D>
-hipError_t launch_gram_d(const Problem& p, const void* k, const void* v, const void* beta,
-                         int T_in, int U_in, int t_first, int n_frames, int slot_offset,
-                         float* stats, hipStream_t s) {
-  const unsigned grid = (unsigned)(p.B * n_frames * p.H);
+hipError_t launch_gram_d(const Problem& p, const GramPart* parts, int nparts, float* stats, hipStream_t s) {
+  const GramPart none = parts[0];
+  const GramPart& a = parts[0];
+  const GramPart& c = nparts > 1 ? parts[1] : none;
+  const int nblk0 = p.B * a.n_frames * p.H;
+  const unsigned grid = (unsigned)(nblk0 + (nparts > 1 ? p.B * c.n_frames * p.H : 0));
+  if (grid == 0) return hipSuccess;
   if (p.bf16) {
-    hipLaunchKernelGGL(gram_bf16<D>, dim3(grid), dim3(512), 0, s,
-                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                       static_cast<const uint16_t*>(beta), stats, T_in, U_in, p.H, t_first,
-                       n_frames, slot_offset, p.T + 1);
+    auto arg = [](const GramPart& q) {
+      return GramArgs<uint16_t>{static_cast<const uint16_t*>(q.k), static_cast<const uint16_t*>(q.v),
+                                static_cast<const uint16_t*>(q.beta), q.T_in, q.U, q.t_first, q.n_frames,
+                                q.slot_offset};
+    };
+    hipLaunchKernelGGL(gram_bf16<D>, dim3(grid), dim3(512), 0, s, arg(a), arg(c), nblk0, stats, p.H, p.T + 1);
   } else {
-    hipLaunchKernelGGL(gram_f32<D>, dim3(grid), dim3(256), 0, s,
-                       static_cast<const float*>(k), static_cast<const float*>(v),
-                       static_cast<const float*>(beta), stats, T_in, U_in, p.H, t_first,
-                       n_frames, slot_offset, p.T + 1);
+    auto arg = [](const GramPart& q) {
+      return GramArgs<float>{static_cast<const float*>(q.k), static_cast<const float*>(q.v),
+                             static_cast<const float*>(q.beta), q.T_in, q.U, q.t_first, q.n_frames,
+                             q.slot_offset};
+    };
+    hipLaunchKernelGGL(gram_f32<D>, dim3(grid), dim3(256), 0, s, arg(a), arg(c), nblk0, stats, p.H, p.T + 1);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gram(const Problem& p, const void* k, const void* v, const void* beta,
-                       int T_in, int U_in, int t_first, int n_frames, int slot_offset,
-                       float* stats, hipStream_t s) {
-  if (n_frames <= 0) return hipSuccess;
+hipError_t launch_gram(const Problem& p, const GramPart* parts, int nparts, float* stats, hipStream_t s) {
+  if (nparts < 1 || nparts > 2) return hipErrorInvalidValue;
   switch (p.D) {
-    case 16: return launch_gram_d<16>(p, k, v, beta, T_in, U_in, t_first, n_frames, slot_offset, stats, s);
-    case 32: return launch_gram_d<32>(p, k, v, beta, T_in, U_in, t_first, n_frames, slot_offset, stats, s);
-    case 64: return launch_gram_d<64>(p, k, v, beta, T_in, U_in, t_first, n_frames, slot_offset, stats, s);
-    case 128: return launch_gram_d<128>(p, k, v, beta, T_in, U_in, t_first, n_frames, slot_offset, stats, s);
+    case 16: return launch_gram_d<16>(p, parts, nparts, stats, s);
+    case 32: return launch_gram_d<32>(p, parts, nparts, stats, s);
+    case 64: return launch_gram_d<64>(p, parts, nparts, stats, s);
+    case 128: return launch_gram_d<128>(p, parts, nparts, stats, s);
     default: return hipErrorInvalidValue;
   }
 }

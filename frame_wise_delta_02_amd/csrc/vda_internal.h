@@ -97,9 +97,17 @@ Layout make_layout(const Problem& p);
 size_t readout_slot_bytes(const Problem& p);
 
 // Kernels are launched through these; each returns hipGetLastError().
-hipError_t launch_gram(const Problem& p, const void* k, const void* v, const void* beta,
-                       int T_in, int U_in, int t_first, int n_frames, int slot_offset,
-                       float* stats, hipStream_t s);
+// One part of a gram launch: frames t_first .. t_first + n_frames - 1 of K, V,
+// beta laid out [B, T_in, U, H, d] (beta [B, T_in, U, H]), into stats slots
+// t + slot_offset.  A launch takes one or two parts; the second part's blocks
+// come after the first's.
+struct GramPart {
+  const void* k;
+  const void* v;
+  const void* beta;
+  int T_in, U, t_first, n_frames, slot_offset;
+};
+hipError_t launch_gram(const Problem& p, const GramPart* parts, int nparts, float* stats, hipStream_t s);
 hipError_t launch_solve(const Problem& p, const float* stats, float* pinv, hipStream_t s);
 hipError_t launch_scan(const Problem& p, const float* stats, const float* pinv, const float* alpha,
                        float* s_text, float* fwd, float* rev, hipStream_t s);

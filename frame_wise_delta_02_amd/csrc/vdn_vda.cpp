@@ -165,11 +165,14 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d, const void* q, const void* k, 
 
   const int n_video = p.T > 2 ? p.T - 2 : 0;
   hipError_t e = mark(0, stream);
-  // frame statistics of frames 1..T-2 (anchors are never absorbed), then the text frame
-  if (e == hipSuccess) e = launch_gram(p, k, v, beta, p.T, p.U, 1, n_video, 0, stats, stream);
+  // frame statistics of frames 1..T-2 (anchors are never absorbed) and of the
+  // text frame (slot T) in one launch: the short text blocks run last, in the
+  // final round of the video blocks
+  const GramPart parts[2] = {{k, v, beta, p.T, p.U, 1, n_video, 0},
+                             {k_text, v_text, beta_text, 1, p.L, 0, 1, p.T}};
+  if (e == hipSuccess) e = launch_gram(p, parts, 2, stats, stream);
   if (e == hipSuccess) e = mark(1, stream);
-  if (e == hipSuccess) e = launch_gram(p, k_text, v_text, beta_text, 1, p.L, 0, 1, p.T, stats, stream);
-  if (e == hipSuccess) e = mark(2, stream);
+  if (e == hipSuccess) e = mark(2, stream);  // the text statistics are part of the launch above
   if (e == hipSuccess) e = launch_solve(p, stats, pinv, stream);
   if (e == hipSuccess) e = mark(3, stream);
   if (e == hipSuccess) e = launch_scan(p, stats, pinv, alpha, s_text, fwd, rev, stream);
