@@ -93,6 +93,15 @@ struct Layout {
 };
 Layout make_layout(const Problem& p);
 
+// Format of the inverse (I + A_t)^{-1} in the workspace.  float32 [d][d] for
+// float32 inputs and for d = 16.  For bfloat16 inputs with d >= 32 the same
+// d*d*4 bytes hold it split into two bfloat16 planes, hi then lo
+// (P^{-1} ~ hi + lo, about 16 significant bits), each in the scan's
+// v_mfma_f32_16x16x32_bf16 B-operand order: 16-byte fragment
+// f = ((2w + e) * (d/32) + ks) * 64 + l holds P^{-1}[32 ks + 8 (l/16) + j]
+// [32 w + 2 (l%16) + e] for j = 0..7.
+inline bool pinv_split(const Problem& p) { return p.bf16 && p.D >= 32; }
+
 // Bytes of one readout state slot in the readout kernel's packed format.
 size_t readout_slot_bytes(const Problem& p);
 

@@ -15,12 +15,23 @@
 //
 // Parallel form: S <- Y P^{-1} acts on the rows of S independently, so each
 // (batch, head, direction) is split into 16-row blocks that scan with no
-// communication at all.  A workgroup keeps its 16 x d block of Y in LDS and
-// multiplies by P^{-1}_s with v_mfma_f32_16x16x4f32 (full fp32).  Lanes read
-// P^{-1} as float2 so each lane owns two adjacent output columns; the next
+// communication at all.  A workgroup keeps its 16 x d block of Y in LDS; each
+// lane owns two adjacent columns of the state (fp32, in registers).  The next
 // frame's P^{-1}, B and alpha are prefetched into registers while the current
 // frame's MFMAs run.  Row blocks of one head go to the same XCD (blockIdx % 8)
 // so the P^{-1}_s they all read is shared in that XCD's L2.
+//
+// The product Y P^{-1} runs in one of two ways:
+//  * float32 inputs, or d = 16: v_mfma_f32_16x16x4f32 on fp32 operands.
+//  * bfloat16 inputs, d >= 32: both operands split into bfloat16 hi + lo
+//    (Y when it is formed, P^{-1} by the solve), and Y P^{-1} ~ Yh Ph + Yh Pl +
+//    Yl Ph on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Each term is
+//    exact in fp32; the split keeps about 16 significant bits of each operand
+//    and the dropped Yl Pl is below 2^-16 of |Y||P|, two orders below the
+//    bfloat16 rounding of the output.  The state stays fp32.  This is three
+//    matrix-core passes at 16x the fp32 rate: a frame step costs about 3/16 of
+//    the fp32 matrix-core time, which bounds the scan when two workgroups share
+//    a CU.
 #include <type_traits>
 
 #include "vda_internal.h"
@@ -30,18 +41,38 @@ namespace {
 
 constexpr int RB = 16;  // state rows per workgroup
 
+// P^{-1} fragments of one frame for one lane
+template <int D, bool SPLIT>
+struct PFrag;
 template <int D>
+struct PFrag<D, false> {  // column pair c0, c0+1 (c0 = 16*NV*wave + NV*(lane%16)), k = (d/4)(lane/16) + ks
+  typedef float vec_t __attribute__((ext_vector_type(D >= 32 ? 2 : 1)));
+  vec_t v[D / 4];
+};
+template <int D>
+struct PFrag<D, true> {   // [e][ks]: fragment (2*wave + e, ks) of the hi and lo planes
+  uint4 hi[2][D / 32], lo[2][D / 32];
+};
+
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(64 * (D / (D >= 32 ? 32 : 16)))
 void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
                const float* __restrict__ alpha, float* __restrict__ s_text,
                float* __restrict__ fwd, float* __restrict__ rev, int B, int H, int T, int C, int nc) {
+  static_assert(!SPLIT || D >= 32, "the bfloat16 split needs k-steps of 32");
   constexpr int NV = D >= 32 ? 2 : 1;   // adjacent columns per lane
   constexpr int WCOLS = 16 * NV;
   constexpr int KS = D / 4;
+  constexpr int KS2 = D / 32;            // k-steps of the split product
   constexpr int NRB = D / RB;
-  constexpr int LDY = D + 4;
+  constexpr int LDY = D + 4;             // fp32 Y row (floats)
+  constexpr int LDYS = D + 8;            // bfloat16 Y row (elements; 16-B aligned rows)
+  constexpr int NFR = D * D / 8;         // 16-B fragments per plane
   typedef float vec_t __attribute__((ext_vector_type(NV)));
-  __shared__ __attribute__((aligned(16))) float ylds[2][RB * LDY];
+  constexpr int YBYTES = SPLIT ? 2 * 2 * RB * LDYS * 2 : 2 * RB * LDY * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char ybytes[YBYTES];
+  float* ylds = reinterpret_cast<float*>(ybytes);            // [2][RB * LDY]      (fp32 path)
+  __bf16* ysp = reinterpret_cast<__bf16*>(ybytes);           // [2 buf][2 plane][RB * LDYS]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // blockIdx -> (group, row block) with all row blocks of a group on one XCD
@@ -71,17 +102,28 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   const int c0 = wave * WCOLS + NV * (lane & 15);
   const int rr = 4 * (lane >> 4);  // first of this lane's 4 output rows
 
-  vec_t st[4];      // this lane's entries of S: rows rr..rr+3, columns c0..c0+NV-1
-  vec_t pf[KS];     // P^{-1} fragments of the frame being multiplied
-  vec_t bw[4], al;  // B rows and alpha of the frame whose Y is being formed
+  vec_t st[4];          // this lane's entries of S: rows rr..rr+3, columns c0..c0+NV-1
+  PFrag<D, SPLIT> pf;   // P^{-1} fragments of the frame being multiplied
+  vec_t bw[4], al;      // B rows and alpha of the frame whose Y is being formed
 
-  // k-step ks of lane group g = lane / 16 covers channel (d/4) g + ks, so each
-  // lane reads a contiguous run of Y (128-bit LDS loads) and of P^{-1} rows
+  // fp32 path: k-step ks of lane group g = lane / 16 covers channel (d/4) g + ks,
+  // so each lane reads a contiguous run of Y (128-bit LDS loads) and of P^{-1} rows
   const int kg = (D / 4) * (lane >> 4);
-  auto ld_p = [&](int s, vec_t (&dst)[KS]) {
-    const float* P = P0 + (size_t)s * D * D + c0 + (size_t)kg * D;
+  auto ld_p = [&](int s, PFrag<D, SPLIT>& dst) {
+    if constexpr (SPLIT) {
+      const uint4* F = reinterpret_cast<const uint4*>(P0 + (size_t)s * D * D) + (size_t)(2 * wave * KS2) * 64 + lane;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) dst[ks] = *reinterpret_cast<const vec_t*>(P + ks * D);
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int ks = 0; ks < KS2; ++ks) {
+          dst.hi[e][ks] = F[(e * KS2 + ks) * 64];
+          dst.lo[e][ks] = F[NFR + (e * KS2 + ks) * 64];
+        }
+    } else {
+      const float* P = P0 + (size_t)s * D * D + c0 + (size_t)kg * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) dst.v[ks] = *reinterpret_cast<const vec_t*>(P + ks * D);
+    }
   };
   auto ld_bw = [&](int s, vec_t (&dst)[4]) {
     const float* Bs = S0 + (size_t)s * 2 * D * D + (size_t)(row0 + rr) * D + c0;
@@ -91,33 +133,76 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   auto ld_al = [&](int s) -> vec_t {
     return *reinterpret_cast<const vec_t*>(A0 + (size_t)s * H * D + c0);
   };
-  // Y = S Diag(alpha) + B into ylds[buf] (alpha = 0 for the text frame)
+  // Y = S Diag(alpha) + B into buffer buf (alpha = 0 for the text frame)
   auto put_y = [&](int buf, const vec_t (&sv)[4], vec_t a, const vec_t (&bv)[4]) {
+    if constexpr (SPLIT) {
+      __bf16* yh = ysp + (2 * buf) * (RB * LDYS);
+      __bf16* yl = yh + RB * LDYS;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      *reinterpret_cast<vec_t*>(&ylds[buf][(rr + r) * LDY + c0]) = sv[r] * a + bv[r];
-  };
-  // S = Y P^{-1} from ylds[buf]; two accumulators per tile (even and odd k-step
-  // groups) keep four independent matrix-core chains in flight
-  auto mul = [&](int buf, const vec_t (&p)[KS]) {
-    f32x4 acc[NV][2];
+      for (int r = 0; r < 4; ++r) {
+        const vec_t y = sv[r] * a + bv[r];
+        __bf16 h0, l0, h1, l1;
+        split_bf16(y[0], h0, l0);
+        split_bf16(y[1], h1, l1);
+        *reinterpret_cast<bf16x2*>(&yh[(rr + r) * LDYS + c0]) = bf16x2{h0, h1};
+        *reinterpret_cast<bf16x2*>(&yl[(rr + r) * LDYS + c0]) = bf16x2{l0, l1};
+      }
+    } else {
 #pragma unroll
-    for (int e = 0; e < NV; ++e) acc[e][0] = acc[e][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float* yrow = &ylds[buf][(lane & 15) * LDY + kg];
-#pragma unroll
-    for (int k4 = 0; k4 < KS / 4; ++k4) {
-      const float4 a4 = *reinterpret_cast<const float4*>(yrow + 4 * k4);
-      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int e = 0; e < NV; ++e)
-          acc[e][q & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], p[4 * k4 + q][e], acc[e][q & 1], 0, 0, 0);
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<vec_t*>(&ylds[buf * (RB * LDY) + (rr + r) * LDY + c0]) = sv[r] * a + bv[r];
     }
+  };
+  // S = Y P^{-1} from buffer buf
+  auto mul = [&](int buf, const PFrag<D, SPLIT>& p) {
+    if constexpr (SPLIT) {
+      // A operand: row lane%16, k = 32 ks + 8 (lane/16) .. +7; one accumulator
+      // per term keeps six independent matrix-core chains in flight
+      const __bf16* yh = ysp + (2 * buf) * (RB * LDYS) + (lane & 15) * LDYS + 8 * (lane >> 4);
+      const __bf16* yl = yh + RB * LDYS;
+      f32x4 acc[2][3];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+      for (int e = 0; e < 2; ++e) acc[e][0] = acc[e][1] = acc[e][2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < NV; ++e) st[r][e] = acc[e][0][r] + acc[e][1][r];
+      for (int ks = 0; ks < KS2; ++ks) {
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(yh + 32 * ks);
+        const bf16x8 alo = *reinterpret_cast<const bf16x8*>(yl + 32 * ks);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const bf16x8 ph = __builtin_bit_cast(bf16x8, p.hi[e][ks]);
+          const bf16x8 pl = __builtin_bit_cast(bf16x8, p.lo[e][ks]);
+          acc[e][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, ph, acc[e][0], 0, 0, 0);
+          acc[e][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, pl, acc[e][1], 0, 0, 0);
+          acc[e][2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, ph, acc[e][2], 0, 0, 0);
+        }
+      }
+      // tile e, lane l, reg r: S[4 (l/16) + r][32 wave + 2 (l%16) + e]
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) st[r][e] = acc[e][0][r] + (acc[e][1][r] + acc[e][2][r]);
+    } else {
+      // two accumulators per tile (even and odd k-step groups) keep four
+      // independent matrix-core chains in flight
+      f32x4 acc[NV][2];
+#pragma unroll
+      for (int e = 0; e < NV; ++e) acc[e][0] = acc[e][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const float* yrow = &ylds[buf * (RB * LDY) + (lane & 15) * LDY + kg];
+#pragma unroll
+      for (int k4 = 0; k4 < KS / 4; ++k4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(yrow + 4 * k4);
+        const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < NV; ++e)
+            acc[e][q & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], p.v[4 * k4 + q][e], acc[e][q & 1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < NV; ++e) st[r][e] = acc[e][0][r] + acc[e][1][r];
+    }
   };
   auto put_state = [&](float* dst) {
 #pragma unroll
@@ -181,7 +266,8 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
     int buf = 1;
     for (int i = 0; i < nsteps; ++i, s += step) {
       put_y(buf, st, al, bw);
-      vec_t pn[KS], bn[4], an;
+      PFrag<D, SPLIT> pn;
+      vec_t bn[4], an;
       const bool more = i + 1 < nsteps;
       if (more) {
         ld_p(s + step, pn);
@@ -193,8 +279,7 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
       const int j = rec_after(s);
       if (j >= 0) put_state(out0 + (size_t)j * D * D);
       if (more) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) pf[ks] = pn[ks];
+        pf = pn;
 #pragma unroll
         for (int r = 0; r < 4; ++r) bw[r] = bn[r];
         al = an;
@@ -292,8 +377,15 @@ hipError_t launch_scan_d(const Problem& p, const float* stats, const float* pinv
   constexpr int NV = D >= 32 ? 2 : 1;
   constexpr int threads = 64 * (D / (16 * NV));
   const unsigned grid = (unsigned)(p.B * p.H * 2 * (D / RB));
-  hipLaunchKernelGGL(scan_rows<D>, dim3(grid), dim3(threads), 0, s, stats, pinv, alpha, s_text,
-                     fwd, rev, p.B, p.H, p.T, p.C, p.nc);
+  if constexpr (D >= 32) {
+    if (pinv_split(p)) {
+      hipLaunchKernelGGL((scan_rows<D, true>), dim3(grid), dim3(threads), 0, s, stats, pinv, alpha,
+                         s_text, fwd, rev, p.B, p.H, p.T, p.C, p.nc);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((scan_rows<D, false>), dim3(grid), dim3(threads), 0, s, stats, pinv, alpha,
+                     s_text, fwd, rev, p.B, p.H, p.T, p.C, p.nc);
   return hipGetLastError();
 }
 

@@ -12,9 +12,13 @@
 //      update P_ij -= L_ik L_jk^T run on v_mfma_f32_16x16x4f32 in all waves.
 //   2. W = L^{-1} by blocked substitution down each block column (columns
 //      spread over the waves), stored transposed in P's unused upper triangle.
-//   3. P^{-1} = W^T W on the same matrix cores, written from the accumulators
-//      straight to global memory (both triangles).
-// Everything is fp32.  The scan consumes P^{-1} directly:
+//   3. P^{-1} = W^T W on the same matrix cores.  With float32 inputs (or
+//      d = 16) it is written from the accumulators straight to global memory
+//      (both triangles).  With bfloat16 inputs and d >= 32 it is split into
+//      bfloat16 hi + lo planes, relaid through LDS into the scan's matrix-core
+//      operand order (the split layout described with pinv_split) and written
+//      coalesced.
+// The arithmetic is fp32.  The scan consumes P^{-1} directly:
 // S M_t + J_t = (S Diag(alpha_t) + B_t) P^{-1}, so M_t and J_t are never formed.
 #include "vda_internal.h"
 
@@ -27,7 +31,7 @@ __device__ __forceinline__ float rdlane(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(256, 2) void solve_mfma(const float* __restrict__ stats,
                                                     float* __restrict__ pinv, int H, int T,
                                                     int n_video) {
@@ -188,25 +192,90 @@ __global__ __launch_bounds__(256, 2) void solve_mfma(const float* __restrict__ s
   }
   __syncthreads();
 
-  // ---- 3. P^{-1} = W^T W: lower blocks (i >= j), both triangles written -------
-  {
-    constexpr int NT = NB * (NB + 1) / 2;
+  // ---- 3. P^{-1} = W^T W: lower blocks (i >= j) --------------------------------
+  constexpr int NT = NB * (NB + 1) / 2;
+  auto lower_tile = [&](int idx, int& bi, int& bj) {
+    int i = 0, rem = idx;
+    while (rem > i) { rem -= i + 1; ++i; }
+    bi = i;
+    bj = rem;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = bi; m < NB; ++m) {
+      // A = W_mi^T: A[p][kk] = W_mi[kk][p];  B = W_mj
+      acc = tile_mma(acc, [&](int s) { return Wb(m, bi, 4 * s + lg, lm); },
+                     [&](int s) { return Wb(m, bj, 4 * s + lg, lm); });
+    }
+    return acc;
+  };
+  if constexpr (!SPLIT) {
     for (int idx = wave; idx < NT; idx += 4) {
-      int i = 0, rem = idx;
-      while (rem > i) { rem -= i + 1; ++i; }
-      const int bi = i, bj = rem;
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int m = bi; m < NB; ++m) {
-        // A = W_mi^T: A[p][kk] = W_mi[kk][p];  B = W_mj
-        acc = tile_mma(acc, [&](int s) { return Wb(m, bi, 4 * s + lg, lm); },
-                       [&](int s) { return Wb(m, bj, 4 * s + lg, lm); });
-      }
+      int bi, bj;
+      const f32x4 acc = lower_tile(idx, bi, bj);
 #pragma unroll
       for (int r = 0; r < 4; ++r) Pout[(16 * bi + 4 * lg + r) * D + 16 * bj + lm] = acc[r];
       if (bi != bj) {
         *reinterpret_cast<float4*>(&Pout[(16 * bj + lm) * D + 16 * bi + 4 * lg]) =
             make_float4(acc[0], acc[1], acc[2], acc[3]);
       }
+    }
+  } else {
+    // every tile of this wave stays in registers until all waves are done
+    // reading W from LDS; then P's storage holds Z_hi, Z_lo with
+    // Z[c][k] = P^{-1}[k][c] (symmetric), rows of D + 4 bfloat16
+    constexpr int NPW = (NT + 3) / 4;
+    constexpr int LDZ = D + 4;
+    f32x4 res[NPW];
+    int tb[NPW];
+#pragma unroll
+    for (int it = 0; it < NPW; ++it) {
+      const int idx = wave + 4 * it;
+      res[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tb[it] = -1;
+      if (idx < NT) {
+        int bi, bj;
+        res[it] = lower_tile(idx, bi, bj);
+        tb[it] = bi * NB + bj;
+      }
+    }
+    __syncthreads();
+    __bf16* Zh = reinterpret_cast<__bf16*>(P);
+    __bf16* Zl = Zh + D * LDZ;
+    static_assert(2 * D * LDZ * 2 == D * LDP * 4, "Z planes fill P's storage exactly");
+#pragma unroll
+    for (int it = 0; it < NPW; ++it) {
+      if (tb[it] < 0) continue;
+      const int bi = tb[it] / NB, bj = tb[it] % NB;
+      __bf16 h[4], l[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) split_bf16(res[it][r], h[r], l[r]);
+      // lane value r is P^{-1}[16 bi + 4 lg + r][16 bj + lm]
+      const int o = (16 * bj + lm) * LDZ + 16 * bi + 4 * lg;
+      *reinterpret_cast<uint2*>(Zh + o) = make_uint2(__builtin_bit_cast(uint32_t, bf16x2{h[0], h[1]}),
+                                                     __builtin_bit_cast(uint32_t, bf16x2{h[2], h[3]}));
+      *reinterpret_cast<uint2*>(Zl + o) = make_uint2(__builtin_bit_cast(uint32_t, bf16x2{l[0], l[1]}),
+                                                     __builtin_bit_cast(uint32_t, bf16x2{l[2], l[3]}));
+      if (bi != bj) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          Zh[(16 * bi + 4 * lg + r) * LDZ + 16 * bj + lm] = h[r];
+          Zl[(16 * bi + 4 * lg + r) * LDZ + 16 * bj + lm] = l[r];
+        }
+      }
+    }
+    __syncthreads();
+    // fragment f of a plane: 8 consecutive k of one column
+    constexpr int NFR = D * D / 8;
+    constexpr int KS2 = D / 32;
+    uint4* Fo = reinterpret_cast<uint4*>(Pout);
+#pragma unroll 4
+    for (int f = tid; f < NFR; f += 256) {
+      const int fl = f & 63, ks = (f >> 6) % KS2, we = (f >> 6) / KS2;
+      const int c = 32 * (we >> 1) + 2 * (fl & 15) + (we & 1);
+      const int o = c * LDZ + 32 * ks + 8 * (fl >> 4);
+      const uint2 h0 = *reinterpret_cast<const uint2*>(Zh + o), h1 = *reinterpret_cast<const uint2*>(Zh + o + 4);
+      const uint2 l0 = *reinterpret_cast<const uint2*>(Zl + o), l1 = *reinterpret_cast<const uint2*>(Zl + o + 4);
+      Fo[f] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+      Fo[NFR + f] = make_uint4(l0.x, l0.y, l1.x, l1.y);
     }
   }
 }
@@ -215,7 +284,13 @@ template <int D>
 hipError_t launch_solve_d(const Problem& p, const float* stats, float* pinv, hipStream_t s) {
   const int n_video = p.T > 2 ? p.T - 2 : 0;
   const unsigned grid = (unsigned)(p.B * p.H * (n_video + 1));
-  hipLaunchKernelGGL(solve_mfma<D>, dim3(grid), dim3(256), 0, s, stats, pinv, p.H, p.T, n_video);
+  if constexpr (D >= 32) {
+    if (pinv_split(p)) {
+      hipLaunchKernelGGL((solve_mfma<D, true>), dim3(grid), dim3(256), 0, s, stats, pinv, p.H, p.T, n_video);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((solve_mfma<D, false>), dim3(grid), dim3(256), 0, s, stats, pinv, p.H, p.T, n_video);
   return hipGetLastError();
 }
 

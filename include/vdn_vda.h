@@ -87,11 +87,16 @@ typedef struct {
 } vdn_vda_desc;
 
 /* Byte offsets (from the workspace base) of the intermediates the forward pass
- * leaves in the workspace.  All are float32.
+ * leaves in the workspace.  All are float32 except pinv with bfloat16 inputs.
  *   stats  [B, H, T+1, d_k + d_v, d_k]: rows 0..d_k-1 hold A_t = K_t^T Diag(beta_t) K_t,
  *          rows d_k.. hold B_t = V_t^T Diag(beta_t) K_t; slot T holds the text
  *          frame.  Anchor frames (0, T-1) are not formed.
- *   pinv   [B, H, T+1, d_k, d_k]: (I + A_t)^{-1}; slot T = text.
+ *   pinv   [B, H, T+1, d_k, d_k]: (I + A_t)^{-1}; slot T = text.  With
+ *          VDN_BF16 and d_k >= 32 each slot's d_k*d_k*4 bytes instead hold
+ *          P = (I + A_t)^{-1} as two bfloat16 planes, hi then lo (P ~ hi + lo),
+ *          each as 16-byte fragments: fragment f = ((2w + e)(d_k/32) + s)*64 + l
+ *          holds P[32s + 8(l/16) + j][32w + 2(l%16) + e] for j = 0..7
+ *          (w < d_k/32, e < 2, s < d_k/32, l < 64).
  *   s_text [B, H, d_v, d_k]: the text state S_T.
  *   fwd    [B, H, n_c, d_v, d_k]: forward state after the last frame of chunk j.
  *   rev    [B, H, n_c, d_v, d_k]: reverse state after the first frame of chunk j.
@@ -151,7 +156,10 @@ vdn_status vdn_vda_prepare(const vdn_vda_desc* d,
  * q, k must be the prepared (unit-norm) features.  k_text, v_text, beta_text
  * may be NULL when n_text = 0 (then S_T = 0).  gate is required with
  * VDN_VDA_EPILOGUE and ignored without it.  out is written in `dtype` with
- * round-to-nearest-even.  The state, statistics, inverse and scan are float32.
+ * round-to-nearest-even.  The state, statistics, inverse and scan are float32;
+ * with VDN_BF16 and d_k >= 32 the scan's product Y (I + A_t)^{-1} takes both
+ * operands as bfloat16 hi + lo pairs (three bfloat16 matrix-core products,
+ * fp32 accumulation, about 2^-16 relative per frame step).
  * Errors: VDN_ERR_INVALID_ARG, VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE,
  * VDN_ERR_ALIGNMENT, VDN_ERR_HIP.
  */

@@ -74,9 +74,36 @@ def intermediates(ws, desc, w: synth.Workload) -> dict:
         return ws[off:off + n].view(torch.float32).reshape(shape).to(torch.float64).cpu().numpy()
 
     stats = arr(L.stats, (B, H, T + 1, 2 * D, D))
-    return dict(A=stats[:, :, :, :D], B=stats[:, :, :, D:], Pinv=arr(L.pinv, (B, H, T + 1, D, D)),
+    if w.dtype == "bf16" and D >= 32:
+        n = B * H * (T + 1) * D * D * 4
+        raw = ws[L.pinv:L.pinv + n].view(torch.int16).reshape(B * H * (T + 1), 2, D * D).cpu().numpy()
+        pinv = decode_split_pinv(raw, D).reshape(B, H, T + 1, D, D)
+    else:
+        pinv = arr(L.pinv, (B, H, T + 1, D, D))
+    return dict(A=stats[:, :, :, :D], B=stats[:, :, :, D:], Pinv=pinv,
                 S_T=arr(L.s_text, (B, H, D, D)), F=arr(L.fwd, (B, H, nc, D, D)),
                 R=arr(L.rev, (B, H, nc, D, D)))
+
+
+def decode_split_pinv(raw: np.ndarray, D: int) -> np.ndarray:
+    """(n, 2, D*D) bfloat16 bit patterns (hi plane, lo plane) -> (n, D, D) float64.
+
+    Plane layout (include/vdn_vda.h, pinv): 16-byte fragment
+    f = ((2w + e) * (D/32) + ks) * 64 + l holds P[32 ks + 8 (l//16) + j][32 w + 2 (l%16) + e],
+    j = 0..7.
+    """
+    f = np.arange(D * D // 8)
+    lane, ks, we = f % 64, (f // 64) % (D // 32), (f // 64) // (D // 32)
+    col = 32 * (we // 2) + 2 * (lane % 16) + we % 2
+    row0 = 32 * ks + 8 * (lane // 16)
+    rows = (row0[:, None] + np.arange(8)[None, :]).ravel()
+    cols = np.repeat(col, 8)
+    bits = raw.astype(np.int64) & 0xFFFF
+    vals = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    full = vals[:, 0] + vals[:, 1]
+    out = np.empty((raw.shape[0], D, D))
+    out[:, rows, cols] = full
+    return out
 
 
 def slice_rel_err(got: np.ndarray, ref: np.ndarray) -> float:

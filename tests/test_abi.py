@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from frame_wise_delta_02_amd import binding as bd
@@ -142,3 +143,33 @@ def test_prepare_argument_errors_before_launch():
     args = list(P)
     args[2] = ctypes.c_void_p(A16 + 0x2000000 + 4)
     assert lib.vdn_vda_prepare(ctypes.byref(desc), *args, None) == bd.VDN_ERR_ALIGNMENT
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_split_pinv_decoder_round_trip(D):
+    """The test-side decoder of the bfloat16 hi/lo inverse planes inverts an
+    encoder written from the layout's definition in include/vdn_vda.h."""
+    import gpu_harness as G
+    rng = np.random.default_rng(D)
+    P = rng.standard_normal((2, D, D)).astype(np.float32)
+
+    def bf16_bits(x):  # round to nearest even, as the kernels convert
+        u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+        return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+    hi = bf16_bits(P)
+    hi_f = (hi.astype(np.uint32) << 16).view(np.float32)
+    lo = bf16_bits(P - hi_f)
+    raw = np.zeros((2, 2, D * D), np.uint16)
+    for n in range(2):
+        for w in range(D // 32):
+            for e in range(2):
+                for s in range(D // 32):
+                    for lane in range(64):
+                        f = ((2 * w + e) * (D // 32) + s) * 64 + lane
+                        for j in range(8):
+                            r, c = 32 * s + 8 * (lane // 16) + j, 32 * w + 2 * (lane % 16) + e
+                            raw[n, 0, 8 * f + j] = hi[n, r, c]
+                            raw[n, 1, 8 * f + j] = lo[n, r, c]
+    got = G.decode_split_pinv(raw.view(np.int16), D)
+    assert np.abs(got - P).max() <= 2.0 ** -16 * np.abs(P).max()
