@@ -30,8 +30,7 @@
 //    and the dropped Yl Pl is below 2^-16 of |Y||P|, two orders below the
 //    bfloat16 rounding of the output.  The state stays fp32.  This is three
 //    matrix-core passes at 16x the fp32 rate: a frame step costs about 3/16 of
-//    the fp32 matrix-core time, which bounds the scan when two workgroups share
-//    a CU.
+//    the fp32 matrix-core time.
 #include <type_traits>
 
 #include "vda_internal.h"
@@ -39,7 +38,12 @@
 namespace vda {
 namespace {
 
-constexpr int RB = 16;  // state rows per workgroup
+// 16-row m-tiles per workgroup: the split path takes 32 rows, so a workgroup
+// loads each P^{-1}_s once for twice the rows (the per-CU load path, not the
+// matrix cores, bounds a frame step there) and B*H*2*d/32 workgroups stay
+// within one per CU at 768p.
+template <bool SPLIT>
+constexpr int scan_mtiles() { return SPLIT ? 2 : 1; }
 
 // P^{-1} fragments of one frame for one lane
 template <int D, bool SPLIT>
@@ -60,7 +64,9 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
                const float* __restrict__ alpha, float* __restrict__ s_text,
                float* __restrict__ fwd, float* __restrict__ rev, int B, int H, int T, int C, int nc) {
   static_assert(!SPLIT || D >= 32, "the bfloat16 split needs k-steps of 32");
-  constexpr int NV = D >= 32 ? 2 : 1;   // adjacent columns per lane
+  constexpr int MT = scan_mtiles<SPLIT>();
+  constexpr int RB = 16 * MT;            // state rows per workgroup
+  constexpr int NV = D >= 32 ? 2 : 1;    // adjacent columns per lane
   constexpr int WCOLS = 16 * NV;
   constexpr int KS = D / 4;
   constexpr int KS2 = D / 32;            // k-steps of the split product
@@ -80,7 +86,7 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   const int bid = blockIdx.x;
   const int groups = B * H * 2;
   int g, rbi;
-  if (NRB == 8 && groups % 8 == 0 && nblk == groups * NRB) {
+  if (groups % 8 == 0 && nblk == groups * NRB) {
     const int xcd = bid % 8, slot = bid / 8;
     rbi = slot % NRB;
     g = (slot / NRB) * 8 + xcd;
@@ -100,90 +106,111 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   const float* A0 = alpha + (size_t)b * T * H * D + (size_t)h * D;                 // + s*H*D
 
   const int c0 = wave * WCOLS + NV * (lane & 15);
-  const int rr = 4 * (lane >> 4);  // first of this lane's 4 output rows
+  const int rr = 4 * (lane >> 4);  // first of this lane's 4 rows in each m-tile
 
-  vec_t st[4];          // this lane's entries of S: rows rr..rr+3, columns c0..c0+NV-1
-  PFrag<D, SPLIT> pf;   // P^{-1} fragments of the frame being multiplied
-  vec_t bw[4], al;      // B rows and alpha of the frame whose Y is being formed
+  vec_t st[MT][4];  // this lane's entries of S: rows 16 mt + rr + r, columns c0..c0+NV-1
+  // two register sets, A and B, of a frame's P^{-1} fragments, B rows and
+  // alpha: one is multiplied while the other is loading
+  PFrag<D, SPLIT> pfA, pfB;
+  vec_t bwA[MT][4], bwB[MT][4], alA, alB;
 
   // fp32 path: k-step ks of lane group g = lane / 16 covers channel (d/4) g + ks,
   // so each lane reads a contiguous run of Y (128-bit LDS loads) and of P^{-1} rows
   const int kg = (D / 4) * (lane >> 4);
-  auto ld_p = [&](int s, PFrag<D, SPLIT>& dst) {
+  // split path: the fragments of k-step ks of frame s (both column tiles, hi and lo)
+  auto ld_p_ks = [&](int s, int ks, PFrag<D, SPLIT>& dst) {
     if constexpr (SPLIT) {
       const uint4* F = reinterpret_cast<const uint4*>(P0 + (size_t)s * D * D) + (size_t)(2 * wave * KS2) * 64 + lane;
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
+      for (int e = 0; e < 2; ++e) {
+        dst.hi[e][ks] = F[(e * KS2 + ks) * 64];
+        dst.lo[e][ks] = F[NFR + (e * KS2 + ks) * 64];
+      }
+    }
+  };
+  auto ld_p = [&](int s, PFrag<D, SPLIT>& dst) {
+    if constexpr (SPLIT) {
 #pragma unroll
-        for (int ks = 0; ks < KS2; ++ks) {
-          dst.hi[e][ks] = F[(e * KS2 + ks) * 64];
-          dst.lo[e][ks] = F[NFR + (e * KS2 + ks) * 64];
-        }
+      for (int ks = 0; ks < KS2; ++ks) ld_p_ks(s, ks, dst);
     } else {
       const float* P = P0 + (size_t)s * D * D + c0 + (size_t)kg * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) dst.v[ks] = *reinterpret_cast<const vec_t*>(P + ks * D);
     }
   };
-  auto ld_bw = [&](int s, vec_t (&dst)[4]) {
+  auto ld_bw = [&](int s, vec_t (&dst)[MT][4]) {
     const float* Bs = S0 + (size_t)s * 2 * D * D + (size_t)(row0 + rr) * D + c0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dst[r] = *reinterpret_cast<const vec_t*>(Bs + r * D);
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[mt][r] = *reinterpret_cast<const vec_t*>(Bs + (16 * mt + r) * D);
   };
   auto ld_al = [&](int s) -> vec_t {
     return *reinterpret_cast<const vec_t*>(A0 + (size_t)s * H * D + c0);
   };
   // Y = S Diag(alpha) + B into buffer buf (alpha = 0 for the text frame)
-  auto put_y = [&](int buf, const vec_t (&sv)[4], vec_t a, const vec_t (&bv)[4]) {
-    if constexpr (SPLIT) {
-      __bf16* yh = ysp + (2 * buf) * (RB * LDYS);
-      __bf16* yl = yh + RB * LDYS;
+  auto put_y = [&](int buf, const vec_t (&sv)[MT][4], vec_t a, const vec_t (&bv)[MT][4]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const vec_t y = sv[r] * a + bv[r];
-        __bf16 h0, l0, h1, l1;
-        split_bf16(y[0], h0, l0);
-        split_bf16(y[1], h1, l1);
-        *reinterpret_cast<bf16x2*>(&yh[(rr + r) * LDYS + c0]) = bf16x2{h0, h1};
-        *reinterpret_cast<bf16x2*>(&yl[(rr + r) * LDYS + c0]) = bf16x2{l0, l1};
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<vec_t*>(&ylds[buf * (RB * LDY) + (rr + r) * LDY + c0]) = sv[r] * a + bv[r];
-    }
-  };
-  // S = Y P^{-1} from buffer buf
-  auto mul = [&](int buf, const PFrag<D, SPLIT>& p) {
-    if constexpr (SPLIT) {
-      // A operand: row lane%16, k = 32 ks + 8 (lane/16) .. +7; one accumulator
-      // per term keeps six independent matrix-core chains in flight
-      const __bf16* yh = ysp + (2 * buf) * (RB * LDYS) + (lane & 15) * LDYS + 8 * (lane >> 4);
-      const __bf16* yl = yh + RB * LDYS;
-      f32x4 acc[2][3];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) acc[e][0] = acc[e][1] = acc[e][2] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS2; ++ks) {
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(yh + 32 * ks);
-        const bf16x8 alo = *reinterpret_cast<const bf16x8*>(yl + 32 * ks);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const bf16x8 ph = __builtin_bit_cast(bf16x8, p.hi[e][ks]);
-          const bf16x8 pl = __builtin_bit_cast(bf16x8, p.lo[e][ks]);
-          acc[e][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, ph, acc[e][0], 0, 0, 0);
-          acc[e][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, pl, acc[e][1], 0, 0, 0);
-          acc[e][2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, ph, acc[e][2], 0, 0, 0);
+        const vec_t y = sv[mt][r] * a + bv[mt][r];
+        const int row = 16 * mt + rr + r;
+        if constexpr (SPLIT) {
+          __bf16* yh = ysp + (2 * buf) * (RB * LDYS);
+          __bf16* yl = yh + RB * LDYS;
+          __bf16 h0, l0, h1, l1;
+          split_bf16(y[0], h0, l0);
+          split_bf16(y[1], h1, l1);
+          *reinterpret_cast<bf16x2*>(&yh[row * LDYS + c0]) = bf16x2{h0, h1};
+          *reinterpret_cast<bf16x2*>(&yl[row * LDYS + c0]) = bf16x2{l0, l1};
+        } else {
+          *reinterpret_cast<vec_t*>(&ylds[buf * (RB * LDY) + row * LDY + c0]) = y;
         }
       }
-      // tile e, lane l, reg r: S[4 (l/16) + r][32 wave + 2 (l%16) + e]
+  };
+  // S = Y P^{-1} from buffer buf.  Split path: with sn >= 0, k-step ks also
+  // issues frame sn's fragments of k-step ks into pn, so the per-CU load path
+  // streams the next frame while the matrix cores work on this one.
+  auto mul = [&](int buf, const PFrag<D, SPLIT>& p, int sn, PFrag<D, SPLIT>& pn) {
+    if constexpr (SPLIT) {
+      // A operand of m-tile mt: row 16 mt + lane%16, k = 32 ks + 8 (lane/16) .. +7.
+      // The three terms of a tile share one accumulator: four independent
+      // matrix-core chains (m-tile x column tile), each at most 3*(d/32) long.
+      const __bf16* yh = ysp + (2 * buf) * (RB * LDYS) + (lane & 15) * LDYS + 8 * (lane >> 4);
+      const __bf16* yl = yh + RB * LDYS;
+      f32x4 acc[MT][2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 2; ++e) st[r][e] = acc[e][0][r] + (acc[e][1][r] + acc[e][2][r]);
+      for (int ks = 0; ks < KS2; ++ks) {
+        if (sn >= 0) ld_p_ks(sn, ks, pn);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const bf16x8 ah = *reinterpret_cast<const bf16x8*>(yh + 16 * mt * LDYS + 32 * ks);
+          const bf16x8 alo = *reinterpret_cast<const bf16x8*>(yl + 16 * mt * LDYS + 32 * ks);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const bf16x8 ph = __builtin_bit_cast(bf16x8, p.hi[e][ks]);
+            const bf16x8 pl = __builtin_bit_cast(bf16x8, p.lo[e][ks]);
+            acc[mt][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, ph, acc[mt][e], 0, 0, 0);
+            acc[mt][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, pl, acc[mt][e], 0, 0, 0);
+            acc[mt][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, ph, acc[mt][e], 0, 0, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep each k-step's loads beside its products
+      }
+      // m-tile mt, column tile e, lane l, reg r: S[16 mt + 4 (l/16) + r][32 wave + 2 (l%16) + e]
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) st[mt][r][e] = acc[mt][e][r];
     } else {
       // two accumulators per tile (even and odd k-step groups) keep four
       // independent matrix-core chains in flight
+      static_assert(SPLIT || MT == 1, "the fp32 product takes one m-tile");
       f32x4 acc[NV][2];
 #pragma unroll
       for (int e = 0; e < NV; ++e) acc[e][0] = acc[e][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -201,27 +228,16 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int e = 0; e < NV; ++e) st[r][e] = acc[e][0][r] + acc[e][1][r];
+        for (int e = 0; e < NV; ++e) st[0][r][e] = acc[e][0][r] + acc[e][1][r];
     }
   };
   auto put_state = [&](float* dst) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      *reinterpret_cast<vec_t*>(dst + (size_t)(row0 + rr + r) * D + c0) = st[r];
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<vec_t*>(dst + (size_t)(row0 + 16 * mt + rr + r) * D + c0) = st[mt][r];
   };
-
-  // ---- text frame (slot T): S_T = B_T P_T^{-1} -------------------------------
-  vec_t zero4[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) zero4[r] = vec_t(0.f);
-  ld_bw(T, bw);
-  ld_p(T, pf);
-  put_y(0, zero4, vec_t(0.f), bw);
-  lds_barrier();
-  mul(0, pf);
-  if (dir == 0) put_state(s_text + head * (size_t)(D * D));
-#pragma unroll
-  for (int r = 0; r < 4; ++r) st[r] *= 0.5f;
 
   // ---- frame list of this direction ------------------------------------------
   // forward: frames 1 .. min(C*(nc-2)-1, T-2); reverse: T-2 .. max(2C, 1)
@@ -237,6 +253,33 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   }
   const int nsteps = (dir == 0) ? max(0, last - first + 1) : max(0, first - last + 1);
   float* out0 = (dir == 0 ? fwd : rev) + head * (size_t)nc * D * D;
+  const auto rec = make_rsrc(out0, (uint32_t)nc * D * D * 4);  // this head's nc records
+
+  // ---- text frame (slot T): S_T = B_T P_T^{-1} -------------------------------
+  // Set B holds the text frame.  The first absorbed frame's loads (set A) are
+  // in flight during its product; with no frame to absorb they re-read the
+  // text slot and frame 0's alpha (in bounds, never used).
+  vec_t zero4[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) zero4[mt][r] = vec_t(0.f);
+  ld_bw(T, bwB);
+  ld_p(T, pfB);
+  put_y(0, zero4, vec_t(0.f), bwB);
+  {
+    const int s1 = nsteps > 0 ? first : T;
+    ld_bw(s1, bwA);
+    alA = ld_al(nsteps > 0 ? first : 0);
+    ld_p(s1, pfA);
+  }
+  lds_barrier();
+  mul(0, pfB, -1, pfA);
+  if (dir == 0) put_state(s_text + head * (size_t)(D * D));
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st[mt][r] *= 0.5f;
 
   // the record index after absorbing frame s (or -1)
   auto rec_after = [&](int s) -> int {
@@ -258,34 +301,48 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
       if (max(C * j, 1) > T - 2) put_state(out0 + (size_t)j * D * D);
   }
 
-  if (nsteps > 0) {
-    int s = first;
-    ld_bw(s, bw);
-    al = ld_al(s);
-    ld_p(s, pf);
-    int buf = 1;
-    for (int i = 0; i < nsteps; ++i, s += step) {
-      put_y(buf, st, al, bw);
-      PFrag<D, SPLIT> pn;
-      vec_t bn[4], an;
-      const bool more = i + 1 < nsteps;
-      if (more) {
-        ld_p(s + step, pn);
-        ld_bw(s + step, bn);
-        an = ld_al(s + step);
-      }
-      lds_barrier();
-      mul(buf, pf);
-      const int j = rec_after(s);
-      if (j >= 0) put_state(out0 + (size_t)j * D * D);
-      if (more) {
-        pf = pn;
+  // One frame step: form Y from the current set, load the next frame into the
+  // other set (unconditionally: the last step re-reads its own frame), and
+  // multiply.  The loop body runs two steps with the sets swapped, so no
+  // register copy waits for a load and the product only waits for the loads
+  // issued one step earlier (the load counter is in order).
+  auto frame = [&](int i, int s, int buf, const PFrag<D, SPLIT>& pc, const vec_t (&bc)[MT][4], vec_t ac,
+                   PFrag<D, SPLIT>& pn, vec_t (&bn)[MT][4], vec_t& an) {
+    const int sn = i + 1 < nsteps ? s + step : s;
+    put_y(buf, st, ac, bc);
+    ld_bw(sn, bn);  // needed first (next step's Y), so issued first
+    an = ld_al(sn);
+    if constexpr (!SPLIT) ld_p(sn, pn);  // the split path loads P^{-1} inside the product
+    // keep the loads here, ahead of the product (the compiler would otherwise
+    // sink them below it, next to their first use)
+    asm volatile("" ::: "memory");
+    lds_barrier();
+    mul(buf, pc, SPLIT ? sn : -1, pn);
+    // record without a branch: the store is always issued and lands past the
+    // buffer's end (dropped by the buffer unit) unless frame s ends a record,
+    // so every step issues the same memory operations and the load waits need
+    // not allow for a store that may or may not be in flight
+    const int j = rec_after(s);
+    const uint32_t jo = j >= 0 ? (uint32_t)j * (uint32_t)(D * D * 4) : 0x80000000u;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bw[r] = bn[r];
-        al = an;
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t o = jo + (uint32_t)(((row0 + 16 * mt + rr + r) * D + c0) * 4);
+        if constexpr (NV == 2)
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, st[mt][r]),
+                                                rec, o, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, st[mt][r][0]), rec, o, 0, 0);
       }
-      buf ^= 1;
-    }
+  };
+  // drain every load and store of the prologue once, so that the wait counts
+  // inside the loop only have to account for the loop's own memory operations
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int i = 0, s = first; i < nsteps; i += 2, s += 2 * step) {
+    frame(i, s, 1, pfA, bwA, alA, pfB, bwB, alB);
+    if (i + 1 >= nsteps) break;
+    frame(i + 1, s + step, 0, pfB, bwB, alB, pfA, bwA, alA);
   }
 }
 
@@ -376,14 +433,15 @@ hipError_t launch_scan_d(const Problem& p, const float* stats, const float* pinv
                          const float* alpha, float* s_text, float* fwd, float* rev, hipStream_t s) {
   constexpr int NV = D >= 32 ? 2 : 1;
   constexpr int threads = 64 * (D / (16 * NV));
-  const unsigned grid = (unsigned)(p.B * p.H * 2 * (D / RB));
   if constexpr (D >= 32) {
     if (pinv_split(p)) {
+      const unsigned grid = (unsigned)(p.B * p.H * 2 * (D / (16 * scan_mtiles<true>())));
       hipLaunchKernelGGL((scan_rows<D, true>), dim3(grid), dim3(threads), 0, s, stats, pinv, alpha,
                          s_text, fwd, rev, p.B, p.H, p.T, p.C, p.nc);
       return hipGetLastError();
     }
   }
+  const unsigned grid = (unsigned)(p.B * p.H * 2 * (D / (16 * scan_mtiles<false>())));
   hipLaunchKernelGGL((scan_rows<D, false>), dim3(grid), dim3(threads), 0, s, stats, pinv, alpha,
                      s_text, fwd, rev, p.B, p.H, p.T, p.C, p.nc);
   return hipGetLastError();
