@@ -148,16 +148,18 @@ def _prep_case(w, heads):
     torch.cuda.synchronize()
     prepared = {}
     errs = {}
-    for h in heads:
-        sl = lambda a: a[0, :, :, h:h + 1]
-        f = G.oracle_view({"q": sl(x["q"]), "k": sl(x["k"]), "v": sl(x["v"])}, w)
-        ws_ = lambda n: x[n][h * w.d:(h + 1) * w.d].astype(np.float64)
-        rq, rk, rv = oracle.prep(f["q"], f["k"], f["v"], ws_("wk_s"), ws_("wk_t"), ws_("wv_s"), ws_("wv_t"),
-                                 w.grid_h, w.grid_w, l2_eps=1e-6)
-        for name, ref, got in (("q", rq, qh), ("k", rk, kh), ("v", rv, vh)):
-            g = G.to_host_f64(got[0, :, :, h:h + 1])
-            errs[name] = max(errs.get(name, 0.0), G.slice_rel_err(g[None], ref[None]))
-            prepared.setdefault(name, []).append(ref)
+    for b in range(w.B):
+        for h in heads:
+            sl = lambda a: a[b, :, :, h:h + 1]
+            f = G.oracle_view({"q": sl(x["q"]), "k": sl(x["k"]), "v": sl(x["v"])}, w)
+            ws_ = lambda n: x[n][h * w.d:(h + 1) * w.d].astype(np.float64)
+            rq, rk, rv = oracle.prep(f["q"], f["k"], f["v"], ws_("wk_s"), ws_("wk_t"), ws_("wv_s"), ws_("wv_t"),
+                                     w.grid_h, w.grid_w, l2_eps=1e-6)
+            for name, ref, got in (("q", rq, qh), ("k", rk, kh), ("v", rv, vh)):
+                g = G.to_host_f64(got[b, :, :, h:h + 1])
+                errs[name] = max(errs.get(name, 0.0), G.slice_rel_err(g[None], ref[None]))
+                if b == 0:
+                    prepared.setdefault(name, []).append(ref)
     G.say(f"prep errors {errs}")
     for name, e in errs.items():
         assert e <= (1e-2 if w.dtype == "bf16" else 1e-5), (name, e)
@@ -169,6 +171,22 @@ def test_prepare_small(dtype):
     w = synth.WORKLOADS["long_prep_bf16"].scaled(name=f"prep_small_{dtype}", dtype=dtype, H=2, T=9,
                                                    grid_h=6, grid_w=10, L=8)
     _prep_case(w, heads=[0, 1])
+
+
+# The d = 128 bfloat16 prep runs 8 x 12 output tiles that sweep every frame:
+# ragged tiles in both directions, clips shorter than the 5 temporal taps, and
+# the head-per-XCD block order (H divisible by 8) with two batch elements.
+PREP_EDGE = {
+    "prep_T1_ragged": dict(H=2, T=1, grid_h=9, grid_w=13, L=4),
+    "prep_T2_ragged": dict(H=1, T=2, grid_h=9, grid_w=13, L=4),
+    "prep_B2_H8_tiles": dict(B=2, H=8, T=7, grid_h=17, grid_w=25, L=4),
+}
+
+
+@pytest.mark.parametrize("name", list(PREP_EDGE))
+def test_prepare_edges(name):
+    w = synth.WORKLOADS["long_prep_bf16"].scaled(name=name, **PREP_EDGE[name])
+    _prep_case(w, heads=list(range(min(w.H, 3))) + ([w.H - 1] if w.H > 3 else []))
 
 
 def test_long_prep_full_size_sampled_head():
