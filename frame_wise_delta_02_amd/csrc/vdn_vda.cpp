@@ -38,6 +38,10 @@ vdn_status check(const vdn_vda_desc* d) {
   if (U > 2147483647.0 || elems > 9.0e15) return VDN_ERR_INVALID_ARG;
   if ((double)d->B * d->T * d->H * d->grid_h > 4294967295.0) return VDN_ERR_INVALID_ARG;
   if ((double)d->B * d->n_text * d->H > 9.0e15) return VDN_ERR_INVALID_ARG;
+  // the scan's chunk records of one head must stay below 2^31 bytes: steps that
+  // record nothing store at offset 2^31, past that buffer
+  if ((double)((d->T + d->chunk - 1) / d->chunk) * d->d_k * d->d_v * 4.0 >= 2147483648.0)
+    return VDN_ERR_INVALID_ARG;
   if (d->d_k != d->d_v) return VDN_ERR_UNSUPPORTED;
   if (d->d_k != 16 && d->d_k != 32 && d->d_k != 64 && d->d_k != 128) return VDN_ERR_UNSUPPORTED;
   return VDN_OK;

@@ -173,3 +173,12 @@ def test_split_pinv_decoder_round_trip(D):
                             raw[n, 1, 8 * f + j] = lo[n, r, c]
     got = G.decode_split_pinv(raw.view(np.int16), D)
     assert np.abs(got - P).max() <= 2.0 ** -16 * np.abs(P).max()
+
+
+def test_chunk_record_limit():
+    """Each head's chunk records (n_c * d_k * d_v * 4 bytes) must stay below 2^31
+    bytes: the scan sends steps that record nothing to offset 2^31 of that buffer."""
+    assert bd.validate(good(T=32767, chunk=1, grid_h=1, grid_w=1, H=1)) == bd.VDN_OK
+    assert bd.validate(good(T=32768, chunk=1, grid_h=1, grid_w=1, H=1)) == bd.VDN_ERR_INVALID_ARG
+    assert bd.validate(good(T=32768, chunk=2, grid_h=1, grid_w=1, H=1)) == bd.VDN_OK
+    assert bd.validate(good(T=131072, chunk=4, grid_h=1, grid_w=1, H=1, d=64)) == bd.VDN_OK
