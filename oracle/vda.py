@@ -245,12 +245,29 @@ def scan_states(M, J, S_T, T, C):
     return F, R
 
 
-def query_states(F, R, S_T, t, T, C):
+def bridge_decay(alpha, frames):
+    """Per key channel, the product of alpha over ``frames``: absorbing those
+    frames with zero writes (beta = 0, so A = 0 and B = 0) turns the frame
+    update S <- (S Diag(alpha_s) + B_s)(I + A_s)^{-1} into S <- S Diag(alpha_s)."""
+    d = np.ones(alpha.shape[-1])
+    for s in frames:
+        d = d * alpha[s]
+    return d
+
+
+def query_states(F, R, S_T, t, T, C, bridge_alpha=None):
     """(S_fwd, S_rev) read by query frame t.
 
     Forward: the state that has absorbed every non-anchor frame before the
     query's window, F[c-2]; reverse: every non-anchor frame after it, R[c+2];
     S_T / 2 where the range is empty.  Anchors read S_T / 2 twice (R1).
+
+    With ``bridge_alpha`` (alpha [T, d_k]) the VDA-Gather decay bridge
+    ([VDN-summary] "전제와 한계": VDA-Gather applies a decay bridge, not defined
+    further) is applied, read as: the frames between the summarised range and
+    the query chunk -- all of chunk c-1 forward, all of chunk c+1 in reverse,
+    anchor frames included -- are absorbed with zero writes, S <- S Diag(alpha_s).
+    Anchor queries are unchanged.
     """
     nc = num_chunks(T, C)
     half = S_T / 2.0
@@ -259,6 +276,11 @@ def query_states(F, R, S_T, t, T, C):
     c = t // C
     sf = F[c - 2] if c >= 2 else half
     sr = R[c + 2] if c + 2 <= nc - 1 else half
+    if bridge_alpha is not None:
+        if c >= 1:
+            sf = sf * bridge_decay(bridge_alpha, range(C * (c - 1), C * c))[None, :]
+        if c + 1 <= nc - 1:
+            sr = sr * bridge_decay(bridge_alpha, range(C * (c + 1), min(C * (c + 2), T)))[None, :]
     return sf, sr
 
 
@@ -285,13 +307,14 @@ def epilogue(o, g, gamma=None, eps=1e-6):
 
 
 def forward_head(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, chunk=5,
-                 frames=None):
+                 frames=None, bridge=False):
     """States and raw readout of one (batch element, head).
 
     q, k: [T, U, d_k]; v: [T, U, d_v]; alpha: [T, d_k]; beta: [T, U];
     k_txt: [L, d_k]; v_txt: [L, d_v]; beta_txt: [L].
     ``frames`` limits which query frames get a readout (all by default);
-    the states always use every frame.
+    the states always use every frame.  ``bridge`` applies the decay bridge
+    (query_states).
     Returns a dict with S_T, A, B, Pinv, M, J, F, R and o ([T, U, d_v],
     zero rows for frames not read out).
     """
@@ -309,13 +332,13 @@ def forward_head(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, chunk=5,
     F, R = scan_states(M, J, S_T, T, chunk)
     o = np.zeros((T, U, dv))
     for t in (range(T) if frames is None else frames):
-        sf, sr = query_states(F, R, S_T, t, T, chunk)
+        sf, sr = query_states(F, R, S_T, t, T, chunk, alpha if bridge else None)
         o[t] = readout(q[t], sf, sr)
     return dict(S_T=S_T, A=A, B=Bw, Pinv=Pinv, M=M, J=J, F=F, R=R, o=o)
 
 
 def forward(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, gate=None,
-            rms_weight=None, chunk=5, rms_eps=1e-6, heads=None):
+            rms_weight=None, chunk=5, rms_eps=1e-6, heads=None, bridge=False):
     """VDA forward over all batch elements and heads (or the listed heads).
 
     Layouts as the boundary takes them: q, k, v, gate [B, T, U, H, d];
@@ -323,7 +346,7 @@ def forward(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, gate=None,
     beta_txt [B, L, H].  All float64.  Returns a dict with the per-head
     intermediates stacked as [B, H, ...], the raw readout ``o`` and, when a
     gate is given, the epilogue output ``y`` (both [B, T, U, H, d_v]; heads
-    not computed are zero).
+    not computed are zero).  ``bridge`` applies the decay bridge.
     """
     Bn, T, U, H, dk = k.shape
     dv = v.shape[-1]
@@ -335,7 +358,7 @@ def forward(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, gate=None,
             r = forward_head(q[b, :, :, h], k[b, :, :, h], v[b, :, :, h],
                              alpha[b, :, h], beta[b, :, :, h],
                              k_txt[b, :, h], v_txt[b, :, h], beta_txt[b, :, h],
-                             chunk=chunk)
+                             chunk=chunk, bridge=bridge)
             o[b, :, :, h] = r.pop("o")
             for name, val in r.items():
                 inter.setdefault(name, np.zeros((Bn, H) + val.shape))[b, h] = val

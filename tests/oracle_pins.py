@@ -10,6 +10,7 @@ Pins (the oracle function each one constrains in brackets):
   P3  one token, unit key == the token delta rule with beta/(1+beta)   [frame_update]
   P4  ||Diag(alpha)(I+A)^-1||_2 <= 1, A PSD                 [frame_stats, transition]
   P5  text counted once; pure-decay closed form             [text_state, scan_states, query_states, readout]
+  P5b decay bridge: pure-decay closed form with the bridged chunks   [query_states, bridge_decay]
   P6  coverage partitions the clip; closed-form ranges      [coverage]
   P7  time reversal                                          [scan_states, query_states]
   P8  linearity in (V, V_text)                               [whole raw readout]
@@ -181,6 +182,48 @@ def check_p5_text_once(rng, C=5, tol=1e-13):
             if t in (0, T - 1) or T <= 2 * C:
                 want = x["q"][t] @ r["S_T"].T
                 assert np.abs(r["o"][t] - want).max() <= tol * 10, (T, t)
+
+
+def check_p5b_bridge_closed_form(rng, C=5, tol=1e-13):
+    """Decay bridge: with zero video writes every frame absorbed on either side
+    only decays, so a non-anchor query in chunk c reads S_T (D_f + D_r) q / 2 with
+    D_f = prod alpha over frames 1 .. Cc-1 (c >= 2), 0 .. C-1 (c = 1), none (c = 0),
+    D_r = prod alpha over C(c+1) .. T-2 (c <= nc-3), C(nc-1) .. T-1 (c = nc-2),
+    none (c = nc-1): the summarised frames plus the bridged chunk next to the
+    query's.  Anchor queries read S_T q, with or without writes."""
+    def run(x, bridge):
+        return V.forward_head(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["k_txt"],
+                              x["v_txt"], x["beta_txt"], chunk=C, bridge=bridge)
+    for T in (2, 5, 7, 10, 12, 20, 23, 31):
+        nc = -(-T // C)
+        x = rand_head(rng, T=T)
+        x["beta"][:] = 0.0
+        r = run(x, True)
+        a = x["alpha"]
+        for t in range(T):
+            if t in (0, T - 1):
+                want = x["q"][t] @ r["S_T"].T
+                assert np.abs(r["o"][t] - want).max() <= tol * 10, (T, t)
+                continue
+            c = t // C
+            fwd = range(1, C * c) if c >= 2 else (range(0, C) if c == 1 else range(0))
+            if c <= nc - 3:
+                rev = range(C * (c + 1), T - 1)
+            elif c == nc - 2:
+                rev = range(C * (nc - 1), T)
+            else:
+                rev = range(0)
+            Df = np.prod(a[list(fwd)], axis=0) if len(fwd) else np.ones(a.shape[1])
+            Dr = np.prod(a[list(rev)], axis=0) if len(rev) else np.ones(a.shape[1])
+            want = x["q"][t] @ (0.5 * r["S_T"] * (Df + Dr)[None, :]).T
+            assert np.abs(r["o"][t] - want).max() <= tol * 10, (T, t, c)
+        # with writes the bridge leaves anchors and the states themselves alone
+        y = rand_head(rng, T=T)
+        rb, r0 = run(y, True), run(y, False)
+        for name in ("S_T", "F", "R", "Pinv"):
+            assert np.array_equal(rb[name], r0[name]), name
+        for t in (0, T - 1):
+            assert np.abs(rb["o"][t] - y["q"][t] @ rb["S_T"].T).max() <= tol * 10
 
 
 def check_p6_coverage(C=5, Ts=(1, 2, 3, 7, 10, 15, 20, 23, 30, 40, 60, 120)):

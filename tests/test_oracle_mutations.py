@@ -12,7 +12,7 @@ import oracle_pins as P
 
 _orig = {name: getattr(V, name) for name in (
     "frame_stats", "transition", "frame_update", "text_state", "scan_states",
-    "query_states", "coverage", "window_frames", "epilogue", "prep", "readout")}
+    "query_states", "bridge_decay", "coverage", "window_frames", "epilogue", "prep", "readout")}
 
 
 def _all_checks():
@@ -22,6 +22,7 @@ def _all_checks():
         lambda: P.check_p2_lstsq(rng, trials=5),
         lambda: P.check_p3_one_token(rng, trials=5),
         lambda: P.check_p5_text_once(rng),
+        lambda: P.check_p5b_bridge_closed_form(rng),
         lambda: P.check_p6_coverage(),
         P.check_golden_coverage,
         P.check_golden_hand_cases,
@@ -35,7 +36,7 @@ def _all_checks():
     for c in checks:
         try:
             c()
-        except Exception:  # noqa: BLE001 - any failure counts as caught
+        except AssertionError:  # a pin fails; any other exception is a broken mutant
             failed += 1
     return failed
 
@@ -75,12 +76,24 @@ def _scan_rev_off_by_one(M, J, S_T, T, C):
     return F, R2
 
 
-def _query_fwd_one_chunk_late(F, R, S_T, t, T, C):
-    sf, sr = _orig["query_states"](F, R, S_T, t, T, C)
+def _query_fwd_one_chunk_late(F, R, S_T, t, T, C, bridge_alpha=None):
+    sf, sr = _orig["query_states"](F, R, S_T, t, T, C, bridge_alpha)
     c = t // C
     if t not in V.anchors(T) and c >= 1:
         sf = F[c - 1]
     return sf, sr
+
+
+def _query_bridge_own_chunk(F, R, S_T, t, T, C, bridge_alpha=None):
+    sf, sr = _orig["query_states"](F, R, S_T, t, T, C, None)
+    if bridge_alpha is not None and t not in V.anchors(T):
+        c = t // C
+        sf = sf * V.bridge_decay(bridge_alpha, range(C * c, min(C * (c + 1), T)))[None, :]
+    return sf, sr
+
+
+def _bridge_drops_last_frame(alpha, frames):
+    return _orig["bridge_decay"](alpha, list(frames)[:-1])
 
 
 def _window_shifted(t, T, C):
@@ -118,6 +131,8 @@ MUTANTS = {
     "scan starts from S_T, not S_T/2": ("scan_states", _scan_full_text),
     "reverse boundary state one chunk off": ("scan_states", _scan_rev_off_by_one),
     "forward state one chunk late": ("query_states", _query_fwd_one_chunk_late),
+    "bridge decays the query's own chunk": ("query_states", _query_bridge_own_chunk),
+    "bridge misses a frame": ("bridge_decay", _bridge_drops_last_frame),
     "window shifted at the clip edges": ("window_frames", _window_shifted),
     "RMSNorm without the square root": ("epilogue", _epilogue_no_sqrt),
     "gate sign flipped": ("epilogue", _epilogue_gate_sign),

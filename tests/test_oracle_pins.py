@@ -54,6 +54,11 @@ def test_p5_text_counted_once():
     P.check_p5_text_once(np.random.default_rng(5))
 
 
+def test_p5b_bridge_closed_form():
+    P.check_p5b_bridge_closed_form(np.random.default_rng(15))
+    P.check_p5b_bridge_closed_form(np.random.default_rng(16), C=3)
+
+
 def test_p6_coverage_partition():
     P.check_p6_coverage()
     P.check_p6_coverage(C=3, Ts=(1, 2, 4, 9, 11, 30))
