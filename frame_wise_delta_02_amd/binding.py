@@ -17,6 +17,7 @@ VDN_OK, VDN_ERR_INVALID_ARG, VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE, VDN_ERR_ALI
 VDN_F32, VDN_BF16 = 0, 1
 VDN_VDA_EPILOGUE = 1 << 0
 VDN_VDA_DEBUG_KEEP = 1 << 1
+VDN_VDA_DECAY_BRIDGE = 1 << 2
 
 EXPORTS = ("vdn_vda_validate", "vdn_vda_workspace_bytes", "vdn_vda_workspace_layout",
            "vdn_vda_prepare", "vdn_vda_forward", "vdn_vda_set_profile_events",
@@ -147,12 +148,12 @@ def _check(x, name, dev):
 
 
 def forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weight=None, *,
-            grid, chunk=5, epilogue=True, rms_eps=1e-6, out=None, workspace=None):
+            grid, chunk=5, epilogue=True, rms_eps=1e-6, out=None, workspace=None, bridge=False):
     """VDA forward on prepared features; returns ``out`` [B, T, U, H, d].
 
     Shapes as in include/vdn_vda.h.  ``grid`` = (grid_h, grid_w) with
     grid_h * grid_w = U.  ``workspace`` (uint8, on the device) is allocated
-    when not given.
+    when not given.  ``bridge`` sets VDN_VDA_DECAY_BRIDGE.
     """
     import torch
     B, T, U, H, d = q.shape
@@ -163,7 +164,8 @@ def forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weig
                     ("k_text", k_text), ("v_text", v_text), ("beta_text", beta_text),
                     ("gate", gate), ("rms_weight", rms_weight), ("out", out), ("workspace", workspace)):
         _check(x, name, dev)
-    desc = make_desc(B, H, T, grid[0], grid[1], d, L, chunk, dt, epilogue, rms_eps=rms_eps)
+    desc = make_desc(B, H, T, grid[0], grid[1], d, L, chunk, dt, epilogue, rms_eps=rms_eps,
+                     flags=(VDN_VDA_EPILOGUE if epilogue else 0) | (VDN_VDA_DECAY_BRIDGE if bridge else 0))
     st = validate(desc)
     if st != VDN_OK:
         raise VdaError(st, "vdn_vda_validate")

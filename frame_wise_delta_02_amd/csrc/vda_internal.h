@@ -84,6 +84,7 @@ struct Problem {
   int nc;                   // number of chunks
   bool bf16;
   bool epilogue;
+  bool bridge;  // VDN_VDA_DECAY_BRIDGE
   float l2_eps, rms_eps;
 };
 
@@ -121,7 +122,7 @@ hipError_t launch_solve(const Problem& p, const float* stats, float* pinv, hipSt
 hipError_t launch_scan(const Problem& p, const float* stats, const float* pinv, const float* alpha,
                        float* s_text, float* fwd, float* rev, hipStream_t s);
 hipError_t launch_gather(const Problem& p, const float* s_text, const float* fwd, const float* rev,
-                         void* rstates, hipStream_t s);
+                         const float* alpha, void* rstates, hipStream_t s);
 hipError_t launch_readout(const Problem& p, const void* q, const void* gate, const float* rms_weight,
                           const void* rstates, void* out, hipStream_t s);
 hipError_t launch_prep(const Problem& p, int grid_h, int grid_w, const void* q, const void* k,

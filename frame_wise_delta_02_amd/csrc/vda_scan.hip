@@ -347,19 +347,40 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
 }
 
 // Readout states: slot c < nc holds F_{c-2} + R_{c+2} (S_T/2 for a missing side),
-// slot nc holds S_T (anchor frames).  Written in the readout kernel's operand
-// order (see vda_readout.hip): for every (m-tile, k-step, lane) the lane's
-// matrix-core A-operand.
+// slot nc holds S_T (anchor frames).  With the decay bridge, slot c < nc holds
+// F_{c-2} Diag(df) + R_{c+2} Diag(dr), df (dr) the per-key-channel product of
+// alpha over chunk c-1 (c+1): those frames absorbed with zero writes, anchors
+// included (ones where the chunk does not exist).  Written in the readout
+// kernel's operand order (see vda_readout.hip): for every (m-tile, k-step,
+// lane) the lane's matrix-core A-operand.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void gather_states(const float* __restrict__ s_text,
                                                      const float* __restrict__ fwd,
                                                      const float* __restrict__ rev,
-                                                     void* __restrict__ rstates, int nc) {
+                                                     const float* __restrict__ alpha,
+                                                     void* __restrict__ rstates, int nc, int T, int H,
+                                                     int C, int bridge) {
   constexpr int DP = D < 32 ? 32 : D;
   constexpr int HALF = DP / 2;
   constexpr int MT = DP / 32;
   const int slot = blockIdx.x % (nc + 1);
   const size_t head = blockIdx.x / (nc + 1);
+  // per-key-channel bridge factors of this slot (alpha [B, T, H, D])
+  __shared__ float dfw[D], drv[D];
+  if (threadIdx.x < D) {
+    const int k = threadIdx.x, b = (int)(head / H), h = (int)(head % H);
+    float df = 1.f, dr = 1.f;
+    if (bridge && slot < nc) {
+      if (slot >= 1)
+        for (int s = C * (slot - 1); s < C * slot; ++s) df *= alpha[(((size_t)b * T + s) * H + h) * D + k];
+      if (slot + 1 <= nc - 1)
+        for (int s = C * (slot + 1); s < min(C * (slot + 2), T); ++s)
+          dr *= alpha[(((size_t)b * T + s) * H + h) * D + k];
+    }
+    dfw[k] = df;
+    drv[k] = dr;
+  }
+  __syncthreads();
   const float* ST = s_text + head * D * D;
   const float* Fp = nullptr;
   const float* Rp = nullptr;
@@ -387,9 +408,13 @@ __global__ __launch_bounds__(256) void gather_states(const float* __restrict__ s
     }
     const float z = dv < D ? 1.f : 0.f;
 #pragma unroll
-    for (int j = 0; j < NQ; ++j)
-      o[j] = make_float4(z * (wf * f[j].x + wr * r[j].x), z * (wf * f[j].y + wr * r[j].y),
-                         z * (wf * f[j].z + wr * r[j].z), z * (wf * f[j].w + wr * r[j].w));
+    for (int j = 0; j < NQ; ++j) {
+      const int c = ch + 4 * j;
+      o[j] = make_float4(z * (wf * f[j].x * dfw[c] + wr * r[j].x * drv[c]),
+                         z * (wf * f[j].y * dfw[c + 1] + wr * r[j].y * drv[c + 1]),
+                         z * (wf * f[j].z * dfw[c + 2] + wr * r[j].z * drv[c + 2]),
+                         z * (wf * f[j].w * dfw[c + 3] + wr * r[j].w * drv[c + 3]));
+    }
   };
 
   if constexpr (BF16) {
@@ -449,12 +474,14 @@ hipError_t launch_scan_d(const Problem& p, const float* stats, const float* pinv
 
 template <int D>
 hipError_t launch_gather_d(const Problem& p, const float* s_text, const float* fwd,
-                           const float* rev, void* rstates, hipStream_t s) {
+                           const float* rev, const float* alpha, void* rstates, hipStream_t s) {
   const unsigned grid = (unsigned)(p.B * p.H * (p.nc + 1));
   if (p.bf16)
-    hipLaunchKernelGGL((gather_states<D, true>), dim3(grid), dim3(256), 0, s, s_text, fwd, rev, rstates, p.nc);
+    hipLaunchKernelGGL((gather_states<D, true>), dim3(grid), dim3(256), 0, s, s_text, fwd, rev, alpha, rstates,
+                       p.nc, p.T, p.H, p.C, p.bridge ? 1 : 0);
   else
-    hipLaunchKernelGGL((gather_states<D, false>), dim3(grid), dim3(256), 0, s, s_text, fwd, rev, rstates, p.nc);
+    hipLaunchKernelGGL((gather_states<D, false>), dim3(grid), dim3(256), 0, s, s_text, fwd, rev, alpha, rstates,
+                       p.nc, p.T, p.H, p.C, p.bridge ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -479,12 +506,12 @@ hipError_t launch_scan(const Problem& p, const float* stats, const float* pinv, 
 }
 
 hipError_t launch_gather(const Problem& p, const float* s_text, const float* fwd, const float* rev,
-                         void* rstates, hipStream_t s) {
+                         const float* alpha, void* rstates, hipStream_t s) {
   switch (p.D) {
-    case 16: return launch_gather_d<16>(p, s_text, fwd, rev, rstates, s);
-    case 32: return launch_gather_d<32>(p, s_text, fwd, rev, rstates, s);
-    case 64: return launch_gather_d<64>(p, s_text, fwd, rev, rstates, s);
-    case 128: return launch_gather_d<128>(p, s_text, fwd, rev, rstates, s);
+    case 16: return launch_gather_d<16>(p, s_text, fwd, rev, alpha, rstates, s);
+    case 32: return launch_gather_d<32>(p, s_text, fwd, rev, alpha, rstates, s);
+    case 64: return launch_gather_d<64>(p, s_text, fwd, rev, alpha, rstates, s);
+    case 128: return launch_gather_d<128>(p, s_text, fwd, rev, alpha, rstates, s);
     default: return hipErrorInvalidValue;
   }
 }

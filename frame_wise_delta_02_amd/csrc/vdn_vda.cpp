@@ -29,7 +29,8 @@ vdn_status check(const vdn_vda_desc* d) {
   if (d->d_k % 16 || d->d_v % 16) return VDN_ERR_INVALID_ARG;
   if (d->n_text < 0 || d->chunk < 1) return VDN_ERR_INVALID_ARG;
   if (d->dtype != VDN_F32 && d->dtype != VDN_BF16) return VDN_ERR_INVALID_ARG;
-  if (d->flags & ~(uint32_t)(VDN_VDA_EPILOGUE | VDN_VDA_DEBUG_KEEP)) return VDN_ERR_INVALID_ARG;
+  if (d->flags & ~(uint32_t)(VDN_VDA_EPILOGUE | VDN_VDA_DEBUG_KEEP | VDN_VDA_DECAY_BRIDGE))
+    return VDN_ERR_INVALID_ARG;
   if (!(d->l2_eps > 0.f) || !isfinite(d->l2_eps)) return VDN_ERR_INVALID_ARG;
   if (!(d->rms_eps > 0.f) || !isfinite(d->rms_eps)) return VDN_ERR_INVALID_ARG;
   // sizes must stay well inside 64-bit element counts and 32-bit grid dimensions
@@ -59,6 +60,7 @@ Problem problem(const vdn_vda_desc* d) {
   p.nc = (d->T + d->chunk - 1) / d->chunk;
   p.bf16 = d->dtype == VDN_BF16;
   p.epilogue = (d->flags & VDN_VDA_EPILOGUE) != 0;
+  p.bridge = (d->flags & VDN_VDA_DECAY_BRIDGE) != 0;
   p.l2_eps = d->l2_eps;
   p.rms_eps = d->rms_eps;
   return p;
@@ -181,7 +183,7 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d, const void* q, const void* k, 
   if (e == hipSuccess) e = mark(3, stream);
   if (e == hipSuccess) e = launch_scan(p, stats, pinv, alpha, s_text, fwd, rev, stream);
   if (e == hipSuccess) e = mark(4, stream);
-  if (e == hipSuccess) e = launch_gather(p, s_text, fwd, rev, rstates, stream);
+  if (e == hipSuccess) e = launch_gather(p, s_text, fwd, rev, alpha, rstates, stream);
   if (e == hipSuccess) e = mark(5, stream);
   if (e == hipSuccess) e = launch_readout(p, q, gate, rms_weight, rstates, out, stream);
   if (e == hipSuccess) e = mark(6, stream);

@@ -70,7 +70,16 @@ enum {
   /* Keep every intermediate in the workspace at the offsets that
    * vdn_vda_workspace_layout() reports.  This build always keeps them, so the
    * flag changes nothing; it is accepted for callers that rely on it. */
-  VDN_VDA_DEBUG_KEEP = 1u << 1
+  VDN_VDA_DEBUG_KEEP = 1u << 1,
+  /* VDA-Gather's decay bridge ([VDN-summary] "전제와 한계" names it without a
+   * definition; reading used here): a non-anchor query in chunk c reads
+   * F_{c-2} Diag(prod of alpha_s over chunk c-1) forward and
+   * R_{c+2} Diag(prod of alpha_s over chunk c+1) in reverse -- the frames
+   * between the summarised range and the query chunk, anchor frames included,
+   * absorbed with zero writes (S <- S Diag(alpha_s)).  Chunk 0 has no forward
+   * bridge, the last chunk no reverse bridge; anchor queries are unchanged.
+   * Without the flag a query reads the boundary states as they are. */
+  VDN_VDA_DECAY_BRIDGE = 1u << 2
 };
 
 /* Problem descriptor: a host struct owned by the caller, passed by pointer. */
@@ -150,6 +159,8 @@ vdn_status vdn_vda_prepare(const vdn_vda_desc* d,
  *     of a query frame covers the non-anchor frames before its softmax window
  *     (its chunk and the neighbouring chunks), the reverse state those after it;
  *     anchor query frames (0, T-1) read S_T only;
+ *     with VDN_VDA_DECAY_BRIDGE the two states are first decayed across the
+ *     chunks next to the query's (see the flag);
  *   readout: o = (S_fwd + S_rev) q; with VDN_VDA_EPILOGUE,
  *     out = rms_weight * o / sqrt(mean(o^2) + rms_eps) * sigmoid(gate)
  *     ([VDN-summary] "무엇과 다른가"), else out = o.

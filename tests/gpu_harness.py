@@ -46,7 +46,7 @@ def oracle_view(x: dict, w: synth.Workload) -> dict:
     return out
 
 
-def run_forward(x: dict, w: synth.Workload, epilogue=True, rms_weight=None, dev_inputs=None):
+def run_forward(x: dict, w: synth.Workload, epilogue=True, rms_weight=None, dev_inputs=None, bridge=False):
     """Run vdn_vda_forward on the inputs; returns (out, workspace, desc, device inputs)."""
     import torch
     d = dev_inputs or {k: to_device(v, w.dtype) for k, v in x.items()}
@@ -57,7 +57,8 @@ def run_forward(x: dict, w: synth.Workload, epilogue=True, rms_weight=None, dev_
     out = bd.forward(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
                      d["k_text"] if L else None, d["v_text"] if L else None,
                      d["beta_text"] if L else None, d["gate"], rw,
-                     grid=(w.grid_h, w.grid_w), chunk=w.chunk, epilogue=epilogue, workspace=ws)
+                     grid=(w.grid_h, w.grid_w), chunk=w.chunk, epilogue=epilogue, workspace=ws,
+                     bridge=bridge)
     torch.cuda.synchronize()
     return out, ws, desc, d
 

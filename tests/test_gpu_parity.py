@@ -22,7 +22,7 @@ def _name_case(request):
     yield
 
 
-def _oracle_heads(x, w, heads, gate=True, rms_weight=None, prepared=None):
+def _oracle_heads(x, w, heads, gate=True, rms_weight=None, prepared=None, bridge=False):
     """Oracle forward on the listed heads only (inputs sliced before widening)."""
     sl = lambda a: a[:, :, :, heads] if a.ndim == 5 else a
     f = {}
@@ -36,7 +36,7 @@ def _oracle_heads(x, w, heads, gate=True, rms_weight=None, prepared=None):
     f["beta_text"] = G.oracle_view({"b": x["beta_text"][:, :, heads]}, w)["b"]
     return oracle.forward(f["q"], f["k"], f["v"], f["alpha"], f["beta"], f["k_text"], f["v_text"],
                           f["beta_text"], gate=f["gate"] if gate else None, rms_weight=rms_weight,
-                          chunk=w.chunk)
+                          chunk=w.chunk, bridge=bridge)
 
 
 def _check_intermediates(inter, ref, w, heads, tol):
@@ -54,20 +54,20 @@ def _check_intermediates(inter, ref, w, heads, tol):
         assert G.mat_rel_err(inter["R"][:, hs, 2:], ref["R"][:, :, 2:]) <= tol, "R"
 
 
-def _run_case(w, heads=None, rms=False, check_inter=True):
+def _run_case(w, heads=None, rms=False, check_inter=True, bridge=False):
     x = synth.make_inputs(w)
     heads = list(range(w.H)) if heads is None else heads
     rw = np.random.default_rng(5).uniform(0.5, 1.5, w.d) if rms else None
     tol = G.TOL[w.dtype]
     # raw readout, with intermediates
-    out, ws, desc, dev = G.run_forward(x, w, epilogue=False)
-    ref = _oracle_heads(x, w, heads, gate=True, rms_weight=rw)
+    out, ws, desc, dev = G.run_forward(x, w, epilogue=False, bridge=bridge)
+    ref = _oracle_heads(x, w, heads, gate=True, rms_weight=rw, bridge=bridge)
     got = G.to_host_f64(out[:, :, :, heads])
     err_o = G.slice_rel_err(got, ref["o"])
     if check_inter:
         _check_intermediates(G.intermediates(ws, desc, w), ref, w, heads, tol)
     # with RMSNorm + gate
-    out2, _, _, _ = G.run_forward(x, w, epilogue=True, rms_weight=rw, dev_inputs=dev)
+    out2, _, _, _ = G.run_forward(x, w, epilogue=True, rms_weight=rw, dev_inputs=dev, bridge=bridge)
     got2 = G.to_host_f64(out2[:, :, :, heads])
     err_y = G.slice_rel_err(got2, ref["y"])
     G.say(f"{w.name} T={w.T} U={w.U} H={w.H} d={w.d}: err(o)={err_o:.3e} err(y)={err_y:.3e} tol={tol}")
@@ -107,6 +107,23 @@ EDGE = {
 @pytest.mark.parametrize("name", list(EDGE))
 def test_edge_cases(name):
     _run_case(EDGE[name], rms=name.endswith("128") or name in ("d16_bf16", "d32_bf16"))
+
+
+# VDA-Gather's decay bridge (VDN_VDA_DECAY_BRIDGE): every chunk position,
+# a short last chunk, both dtypes and the narrow widths.
+BRIDGE = {
+    "bridge_bf16_128": EDGE["ragged_bf16_128"],
+    "bridge_f32_128": EDGE["ragged_f32_128"],
+    "bridge_chunk3_bf16": EDGE["chunk3_bf16"],
+    "bridge_d16_f32": EDGE["T7_f32"].scaled(name="bridge_d16_f32", T=23),
+    "bridge_768p": synth.WORKLOADS["768p_bf16"],
+}
+
+
+@pytest.mark.parametrize("name", list(BRIDGE))
+def test_decay_bridge(name):
+    w = BRIDGE[name]
+    _run_case(w, heads=[0, w.H - 1] if w.H > 4 else None, bridge=True)
 
 
 def test_zero_writes_give_text_only_readout():
