@@ -91,42 +91,63 @@ __global__ __launch_bounds__(256, 2) void solve_mfma(const float* __restrict__ s
   };
 
   // ---- 1. Cholesky ------------------------------------------------------------
-  for (int k = 0; k < NB; ++k) {
-    if (wave == 0) {
-      const int i = lm;  // row of the diagonal block owned by this lane
-      float a[16];
+  // One wave factors diagonal block k in registers (lane = row, readlane
+  // broadcasts; hardware sqrt and reciprocal, about 1 ulp) and writes L_kk and
+  // W_kk = L_kk^{-1}.  This serial chain is the critical path of the whole
+  // inversion, so it runs ahead: during step k's trailing update, wave 0 first
+  // updates block (k+1, k+1) and then factors it, while waves 1-3 update the
+  // other trailing blocks.
+  auto factor_diag = [&](int k) {
+    const int i = lm;  // row of the diagonal block owned by this lane
+    float a[16];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) a[c] = P[(16 * k + i) * LDP + 16 * k + c];
-      // hardware sqrt and reciprocal (about 1 ulp): this loop is the serial
-      // critical path of the whole inversion
-      float rdiag = 0.f;  // 1 / L[i][i] of this lane's row
+    for (int c = 0; c < 16; ++c) a[c] = P[(16 * k + i) * LDP + 16 * k + c];
+    float rdiag = 0.f;  // 1 / L[i][i] of this lane's row
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float d = __builtin_amdgcn_sqrtf(rdlane(a[j], j));
-        const float inv = __builtin_amdgcn_rcpf(d);
-        const float l = (i > j) ? a[j] * inv : (i == j ? d : 0.f);
-        if (i == j) rdiag = inv;
-        a[j] = l;
+    for (int j = 0; j < 16; ++j) {
+      const float d = __builtin_amdgcn_sqrtf(rdlane(a[j], j));
+      const float inv = __builtin_amdgcn_rcpf(d);
+      const float l = (i > j) ? a[j] * inv : (i == j ? d : 0.f);
+      if (i == j) rdiag = inv;
+      a[j] = l;
 #pragma unroll
-        for (int c = j + 1; c < 16; ++c) a[c] -= l * rdlane(l, c);
-      }
-      // column c = lane of W_kk = L_kk^{-1} by forward substitution
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float sacc = (r == i) ? 1.f : 0.f;
-#pragma unroll
-        for (int m = 0; m < r; ++m) sacc -= rdlane(a[m], r) * x[m];
-        x[r] = sacc * rdlane(rdiag, r);
-      }
-      if (lane < 16) {
-#pragma unroll
-        for (int c = 0; c < 16; ++c) P[(16 * k + i) * LDP + 16 * k + c] = (c <= i) ? a[c] : 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Wd[k][r * WDS + i] = x[r];
-      }
+      for (int c = j + 1; c < 16; ++c) a[c] -= l * rdlane(l, c);
     }
-    __syncthreads();
+    // column c = lane of W_kk = L_kk^{-1} by forward substitution
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float sacc = (r == i) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) sacc -= rdlane(a[m], r) * x[m];
+      x[r] = sacc * rdlane(rdiag, r);
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) P[(16 * k + i) * LDP + 16 * k + c] = (c <= i) ? a[c] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Wd[k][r * WDS + i] = x[r];
+    }
+  };
+  // trailing tile idx of step k (idx -> (i, j) over the lower triangle, row by
+  // row; idx 0 is block (k+1, k+1)): P_ij -= L_ik L_jk^T
+  auto trailing_tile = [&](int k, int idx) {
+    int i = 0, rem = idx;
+    while (rem > i) { rem -= i + 1; ++i; }
+    const int bi = k + 1 + i, bj = k + 1 + rem;
+    f32x4 acc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = P[(16 * bi + 4 * lg + r) * LDP + 16 * bj + lm];
+    const float* Li = &P[(16 * bi + lm) * LDP + 16 * k + lg];
+    const float* Lj = &P[(16 * bj + lm) * LDP + 16 * k + lg];
+    acc = tile_mma(acc, [&](int s) { return -Li[4 * s]; }, [&](int s) { return Lj[4 * s]; });
+#pragma unroll
+    for (int r = 0; r < 4; ++r) P[(16 * bi + 4 * lg + r) * LDP + 16 * bj + lm] = acc[r];
+  };
+
+  if (wave == 0) factor_diag(0);
+  __syncthreads();
+  for (int k = 0; k < NB; ++k) {
     // panel: L_ik = P_ik W_kk^T, in place
     for (int i = k + 1 + wave; i < NB; i += 4) {
       const float* Pi = &P[(16 * i + lm) * LDP + 16 * k + lg];
@@ -137,22 +158,21 @@ __global__ __launch_bounds__(256, 2) void solve_mfma(const float* __restrict__ s
       for (int r = 0; r < 4; ++r) P[(16 * i + 4 * lg + r) * LDP + 16 * k + lm] = acc[r];
     }
     __syncthreads();
-    // trailing update of the lower blocks: P_ij -= L_ik L_jk^T, k < j <= i
+    // trailing update of the lower blocks, k < j <= i, with diagonal block
+    // k+1 updated and factored first by wave 0
     {
       const int m = NB - 1 - k;  // trailing blocks per side
       const int ntr = m * (m + 1) / 2;
-      for (int idx = wave; idx < ntr; idx += 4) {
-        int i = 0, rem = idx;  // idx -> (i, j) over the lower triangle, row by row
-        while (rem > i) { rem -= i + 1; ++i; }
-        const int bi = k + 1 + i, bj = k + 1 + rem;
-        f32x4 acc;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = P[(16 * bi + 4 * lg + r) * LDP + 16 * bj + lm];
-        const float* Li = &P[(16 * bi + lm) * LDP + 16 * k + lg];
-        const float* Lj = &P[(16 * bj + lm) * LDP + 16 * k + lg];
-        acc = tile_mma(acc, [&](int s) { return -Li[4 * s]; }, [&](int s) { return Lj[4 * s]; });
-#pragma unroll
-        for (int r = 0; r < 4; ++r) P[(16 * bi + 4 * lg + r) * LDP + 16 * bj + lm] = acc[r];
+      if (m > 0) {
+        if (wave == 0) {
+          trailing_tile(k, 0);
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          __builtin_amdgcn_wave_barrier();
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          factor_diag(k + 1);
+        } else {
+          for (int idx = wave; idx < ntr; idx += 3) trailing_tile(k, idx);
+        }
       }
     }
     __syncthreads();
