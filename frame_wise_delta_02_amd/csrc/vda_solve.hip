@@ -145,6 +145,38 @@ __global__ __launch_bounds__(256, 2) void solve_mfma(const float* __restrict__ s
     for (int r = 0; r < 4; ++r) P[(16 * bi + 4 * lg + r) * LDP + 16 * bj + lm] = acc[r];
   };
 
+  // two trailing tiles at once (the second may be absent: it then repeats the
+  // first and is not stored), so two matrix-core chains run side by side
+  auto trailing_pair = [&](int k, int idx0, int idx1) {
+    const bool two = idx1 >= 0;
+    int bi[2], bj[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int i = 0, rem = (u == 0 || !two) ? idx0 : idx1;
+      while (rem > i) { rem -= i + 1; ++i; }
+      bi[u] = k + 1 + i;
+      bj[u] = k + 1 + rem;
+    }
+    f32x4 acc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[u][r] = P[(16 * bi[u] + 4 * lg + r) * LDP + 16 * bj[u] + lm];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(-P[(16 * bi[u] + lm) * LDP + 16 * k + 4 * s4 + lg],
+                                                      P[(16 * bj[u] + lm) * LDP + 16 * k + 4 * s4 + lg],
+                                                      acc[u], 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) P[(16 * bi[0] + 4 * lg + r) * LDP + 16 * bj[0] + lm] = acc[0][r];
+    if (two) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) P[(16 * bi[1] + 4 * lg + r) * LDP + 16 * bj[1] + lm] = acc[1][r];
+    }
+  };
+
   if (wave == 0) factor_diag(0);
   __syncthreads();
   for (int k = 0; k < NB; ++k) {
@@ -171,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void solve_mfma(const float* __restrict__ s
           __atomic_signal_fence(__ATOMIC_SEQ_CST);
           factor_diag(k + 1);
         } else {
-          for (int idx = wave; idx < ntr; idx += 3) trailing_tile(k, idx);
+          for (int idx = wave; idx < ntr; idx += 6) trailing_pair(k, idx, idx + 3 < ntr ? idx + 3 : -1);
         }
       }
     }
@@ -191,11 +223,20 @@ __global__ __launch_bounds__(256, 2) void solve_mfma(const float* __restrict__ s
     const int j = pass == 0 ? wave : NB - 1 - wave;
     if (j < 0 || j >= NB || (pass == 1 && j < 4)) continue;
     for (int i = j + 1; i < NB; ++i) {
-      f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int m = j; m < i; ++m) {
-        const float* Lim = &P[(16 * i + lm) * LDP + 16 * m + lg];
-        t = tile_mma(t, [&](int s) { return Lim[4 * s]; }, [&](int s) { return Wb(m, j, 4 * s + lg, lm); });
+      // two accumulators (even and odd m) halve the dependent matrix-core chain
+      f32x4 t0 = f32x4{0.f, 0.f, 0.f, 0.f}, t1 = t0;
+      int m = j;
+      for (; m + 1 < i; m += 2) {
+        const float* L0 = &P[(16 * i + lm) * LDP + 16 * m + lg];
+        const float* L1 = L0 + 16;
+        t0 = tile_mma(t0, [&](int s) { return L0[4 * s]; }, [&](int s) { return Wb(m, j, 4 * s + lg, lm); });
+        t1 = tile_mma(t1, [&](int s) { return L1[4 * s]; }, [&](int s) { return Wb(m + 1, j, 4 * s + lg, lm); });
       }
+      if (m < i) {
+        const float* L0 = &P[(16 * i + lm) * LDP + 16 * m + lg];
+        t0 = tile_mma(t0, [&](int s) { return L0[4 * s]; }, [&](int s) { return Wb(m, j, 4 * s + lg, lm); });
+      }
+      const f32x4 t = t0 + t1;
       // relayout T through this wave's scratch, then W_ij = -W_ii T
 #pragma unroll
       for (int r = 0; r < 4; ++r) Tx[(4 * lg + r) * LDP + lm] = t[r];
@@ -219,13 +260,20 @@ __global__ __launch_bounds__(256, 2) void solve_mfma(const float* __restrict__ s
     while (rem > i) { rem -= i + 1; ++i; }
     bi = i;
     bj = rem;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int m = bi; m < NB; ++m) {
-      // A = W_mi^T: A[p][kk] = W_mi[kk][p];  B = W_mj
-      acc = tile_mma(acc, [&](int s) { return Wb(m, bi, 4 * s + lg, lm); },
-                     [&](int s) { return Wb(m, bj, 4 * s + lg, lm); });
+    // A = W_mi^T: A[p][kk] = W_mi[kk][p];  B = W_mj.  Even and odd m go to two
+    // accumulators (two independent matrix-core chains).
+    f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, a1 = a0;
+    int m = bi;
+    for (; m + 1 < NB; m += 2) {
+      a0 = tile_mma(a0, [&](int s) { return Wb(m, bi, 4 * s + lg, lm); },
+                    [&](int s) { return Wb(m, bj, 4 * s + lg, lm); });
+      a1 = tile_mma(a1, [&](int s) { return Wb(m + 1, bi, 4 * s + lg, lm); },
+                    [&](int s) { return Wb(m + 1, bj, 4 * s + lg, lm); });
     }
-    return acc;
+    if (m < NB)
+      a0 = tile_mma(a0, [&](int s) { return Wb(m, bi, 4 * s + lg, lm); },
+                    [&](int s) { return Wb(m, bj, 4 * s + lg, lm); });
+    return a0 + a1;
   };
   if constexpr (!SPLIT) {
     for (int idx = wave; idx < NT; idx += 4) {
