@@ -63,8 +63,8 @@ def algorithmic_bytes(w, stage: str) -> int:
         return n * (2 * w.d + 1) * esz
     if stage == "readout":               # Q and the gate logits in, O out
         return tok * 3 * w.d * esz
-    if stage == "prep":                  # Q, K, V in; Q^, K^, V^ out
-        return tok * 6 * w.d * esz
+    if stage == "prep":                  # K, V in; K^, V^ out (Q's L2 is fused into the readout)
+        return tok * 4 * w.d * esz
     return 0
 
 
@@ -73,7 +73,7 @@ def job_bytes(w) -> int:
     esz = 2 if w.dtype == "bf16" else 4
     tok = w.B * w.T * w.U * w.H
     n = tok * (5 * w.d + 1) * esz + w.B * w.T * w.H * w.d * 4 + w.B * w.L * w.H * (2 * w.d + 1) * esz
-    return n + (tok * 6 * w.d * esz if w.prep else 0)
+    return n + (tok * 4 * w.d * esz if w.prep else 0)
 
 
 def _sha(stage):
@@ -180,26 +180,34 @@ def main() -> int:
     ws = torch.empty(bd.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(d["q"])
     if w.prep:
-        qh, kh, vh = (torch.empty_like(d[k]) for k in ("q", "k", "v"))
+        kh, vh = torch.empty_like(d["k"]), torch.empty_like(d["v"])
     grid = (w.grid_h, w.grid_w)
     stream = torch.cuda.current_stream().cuda_stream
     hip = Hip()
 
+    # the long clip: conv + SiLU (+ L2 for K) in the prep kernels; the query's L2
+    # normalisation is fused into the readout (VDN_VDA_QUERY_L2), q goes in raw
+    pdesc = bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L, w.chunk, w.dtype, False,
+                         flags=bd.VDN_VDA_QUERY_L2)
+
     def prep_call():
-        st = bd.lib().vdn_vda_prepare(ctypes.byref(bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L,
-                                                                w.chunk, w.dtype, False)),
-                                      *[ctypes.c_void_p(t.data_ptr()) for t in
-                                        (d["q"], d["k"], d["v"], d["wk_s"], d["wk_t"], d["wv_s"], d["wv_t"],
-                                         qh, kh, vh)], ctypes.c_void_p(stream))
+        ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+        st = bd.lib().vdn_vda_prepare(ctypes.byref(pdesc), None, ptr(d["k"]), ptr(d["v"]), ptr(d["wk_s"]),
+                                      ptr(d["wk_t"]), ptr(d["wv_s"]), ptr(d["wv_t"]), None, ptr(kh), ptr(vh),
+                                      ctypes.c_void_p(stream))
         if st != bd.VDN_OK:
             raise bd.VdaError(st, "vdn_vda_prepare")
 
+    step_q = (d["q"], kh, vh) if w.prep else (d["q"], d["k"], d["v"])
+
+    def fwd():
+        bd.forward(*step_q, d["alpha"], d["beta"], d["k_text"], d["v_text"], d["beta_text"], d["gate"], None,
+                   grid=grid, chunk=w.chunk, epilogue=True, out=out, workspace=ws, query_l2=w.prep)
+
     def step():
-        q, k, v = (qh, kh, vh) if w.prep else (d["q"], d["k"], d["v"])
         if w.prep:
             prep_call()
-        bd.forward(q, k, v, d["alpha"], d["beta"], d["k_text"], d["v_text"], d["beta_text"], d["gate"], None,
-                   grid=grid, chunk=w.chunk, epilogue=True, out=out, workspace=ws)
+        fwd()
 
     for _ in range(args.warmup):
         step()
@@ -228,9 +236,7 @@ def main() -> int:
             prep_call()
             hip.record(pe1, stream)
         bd.set_profile_events([e.value for e in evs])
-        step_q = (qh, kh, vh) if w.prep else (d["q"], d["k"], d["v"])
-        bd.forward(*step_q, d["alpha"], d["beta"], d["k_text"], d["v_text"], d["beta_text"], d["gate"], None,
-                   grid=grid, chunk=w.chunk, epilogue=True, out=out, workspace=ws)
+        fwd()
         bd.set_profile_events(None)
         if w.prep:
             prep_ms.append(hip.elapsed(pe0, pe1))

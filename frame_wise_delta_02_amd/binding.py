@@ -18,6 +18,7 @@ VDN_F32, VDN_BF16 = 0, 1
 VDN_VDA_EPILOGUE = 1 << 0
 VDN_VDA_DEBUG_KEEP = 1 << 1
 VDN_VDA_DECAY_BRIDGE = 1 << 2
+VDN_VDA_QUERY_L2 = 1 << 3
 
 EXPORTS = ("vdn_vda_validate", "vdn_vda_workspace_bytes", "vdn_vda_workspace_layout",
            "vdn_vda_prepare", "vdn_vda_forward", "vdn_vda_set_profile_events",
@@ -148,12 +149,14 @@ def _check(x, name, dev):
 
 
 def forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weight=None, *,
-            grid, chunk=5, epilogue=True, rms_eps=1e-6, out=None, workspace=None, bridge=False):
+            grid, chunk=5, epilogue=True, rms_eps=1e-6, out=None, workspace=None, bridge=False,
+            query_l2=False, l2_eps=1e-6):
     """VDA forward on prepared features; returns ``out`` [B, T, U, H, d].
 
     Shapes as in include/vdn_vda.h.  ``grid`` = (grid_h, grid_w) with
     grid_h * grid_w = U.  ``workspace`` (uint8, on the device) is allocated
-    when not given.  ``bridge`` sets VDN_VDA_DECAY_BRIDGE.
+    when not given.  ``bridge`` sets VDN_VDA_DECAY_BRIDGE; ``query_l2`` sets
+    VDN_VDA_QUERY_L2 (``q`` is then the raw query, normalised with ``l2_eps``).
     """
     import torch
     B, T, U, H, d = q.shape
@@ -164,8 +167,9 @@ def forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weig
                     ("k_text", k_text), ("v_text", v_text), ("beta_text", beta_text),
                     ("gate", gate), ("rms_weight", rms_weight), ("out", out), ("workspace", workspace)):
         _check(x, name, dev)
-    desc = make_desc(B, H, T, grid[0], grid[1], d, L, chunk, dt, epilogue, rms_eps=rms_eps,
-                     flags=(VDN_VDA_EPILOGUE if epilogue else 0) | (VDN_VDA_DECAY_BRIDGE if bridge else 0))
+    desc = make_desc(B, H, T, grid[0], grid[1], d, L, chunk, dt, epilogue, l2_eps=l2_eps, rms_eps=rms_eps,
+                     flags=(VDN_VDA_EPILOGUE if epilogue else 0) | (VDN_VDA_DECAY_BRIDGE if bridge else 0)
+                     | (VDN_VDA_QUERY_L2 if query_l2 else 0))
     st = validate(desc)
     if st != VDN_OK:
         raise VdaError(st, "vdn_vda_validate")
@@ -183,18 +187,25 @@ def forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weig
     return out
 
 
-def prepare(q, k, v, wk_s, wk_t, wv_s, wv_t, *, grid, l2_eps=1e-6, n_text=0, chunk=5):
-    """Feature prep (conv, SiLU, L2); returns (q_hat, k_hat, v_hat)."""
+def prepare(q, k, v, wk_s, wk_t, wv_s, wv_t, *, grid, l2_eps=1e-6, n_text=0, chunk=5, query_l2=False):
+    """Feature prep (conv, SiLU, L2); returns (q_hat, k_hat, v_hat).
+
+    With ``query_l2`` (VDN_VDA_QUERY_L2) the query is left to the forward pass:
+    ``q`` may be None and q_hat is returned as None.
+    """
     import torch
-    B, T, U, H, d = q.shape
-    dev = q.device
+    B, T, U, H, d = k.shape
+    dev = k.device
     for name, x in (("q", q), ("k", k), ("v", v), ("wk_s", wk_s), ("wk_t", wk_t),
                     ("wv_s", wv_s), ("wv_t", wv_t)):
         _check(x, name, dev)
-    desc = make_desc(B, H, T, grid[0], grid[1], d, n_text, chunk, _dtype_of(q), False, l2_eps=l2_eps)
-    q_hat, k_hat, v_hat = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    st = lib().vdn_vda_prepare(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(wk_s), _ptr(wk_t),
-                               _ptr(wv_s), _ptr(wv_t), _ptr(q_hat), _ptr(k_hat), _ptr(v_hat), _stream())
+    desc = make_desc(B, H, T, grid[0], grid[1], d, n_text, chunk, _dtype_of(k), False, l2_eps=l2_eps,
+                     flags=VDN_VDA_QUERY_L2 if query_l2 else 0)
+    q_hat = None if query_l2 else torch.empty_like(q)
+    k_hat, v_hat = torch.empty_like(k), torch.empty_like(v)
+    st = lib().vdn_vda_prepare(ctypes.byref(desc), None if query_l2 else _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(wk_s), _ptr(wk_t), _ptr(wv_s), _ptr(wv_t),
+                               None if query_l2 else _ptr(q_hat), _ptr(k_hat), _ptr(v_hat), _stream())
     if st != VDN_OK:
         raise VdaError(st, "vdn_vda_prepare")
     return q_hat, k_hat, v_hat

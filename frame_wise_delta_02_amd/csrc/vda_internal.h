@@ -85,6 +85,7 @@ struct Problem {
   bool bf16;
   bool epilogue;
   bool bridge;  // VDN_VDA_DECAY_BRIDGE
+  bool qnorm;   // VDN_VDA_QUERY_L2: the readout normalises the raw query
   float l2_eps, rms_eps;
 };
 

@@ -406,6 +406,7 @@ hipError_t launch_prep_t(const Problem& p, int gh, int gw, const void* q, const 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (p.qnorm) return hipSuccess;  // the readout normalises the query itself
   const size_t rows = (size_t)p.B * p.T * p.U * p.H;
   const size_t threads = rows * (D / 8);
   hipLaunchKernelGGL((prep_l2<D, TIO>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,

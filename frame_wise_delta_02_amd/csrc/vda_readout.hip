@@ -24,6 +24,11 @@
 // bfloat16 path: S = S_hi + S_lo (two bf16 parts, ~16 significant bits) on
 // v_mfma_f32_32x32x16_bf16, so the fp32 state is not truncated to 8 bits.
 // float32 path: v_mfma_f32_32x32x2f32 with the fp32 state.
+// Query L2 normalisation may be fused here (the flag VDN_VDA_QUERY_L2): the
+// readout before RMSNorm is linear in q, so the kernel multiplies the raw
+// query's products by 1/sqrt(|q|^2 + l2_eps), the squared norm summed in
+// float32 from the operand registers (each half-wave holds half the channels
+// of a token, the other half one lane swap away).
 #include "vda_internal.h"
 
 namespace vda {
@@ -31,11 +36,11 @@ namespace {
 
 __device__ __forceinline__ float sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
-template <int D, bool EPI, bool GAMMA>
+template <int D, bool EPI, bool GAMMA, bool QN>
 __global__ __launch_bounds__(512, 1) void readout_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ G, const float* __restrict__ w,
     const uint4* __restrict__ rstates, uint16_t* __restrict__ O, int T, int U, int H, int C,
-    int nc, float eps) {
+    int nc, float eps, float l2eps) {
   constexpr int NW = 8;              // waves per workgroup
   constexpr int DP = D < 32 ? 32 : D;
   constexpr int HALF = DP / 2;       // outputs per lane
@@ -125,6 +130,24 @@ __global__ __launch_bounds__(512, 1) void readout_bf16(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, X[pos(n, (CH / 2) * half + ks)]);
     fence();
+    // 1 / |q| of token n (raw query, fused L2 normalisation); 1 otherwise
+    float qscale = 1.f;
+    if constexpr (QN) {
+      float qs = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 u = __builtin_bit_cast(uint4, qf[ks]);
+        const uint32_t q4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = bf16_lo(q4[e]), c = bf16_hi(q4[e]);
+          qs += a * a;
+          qs += c * c;
+        }
+      }
+      qs += __shfl_xor(qs, 32);
+      qscale = __builtin_amdgcn_rsqf(qs + l2eps);
+    }
     // the gate rows wait in the same LDS tile until the epilogue
     if constexpr (EPI) {
 #pragma unroll
@@ -155,7 +178,8 @@ __global__ __launch_bounds__(512, 1) void readout_bf16(
 #pragma unroll
         for (int r = 0; r < 16; ++r) ss += acc[mt][r] * acc[mt][r];
       ss += __shfl_xor(ss, 32);
-      const float rinv = __builtin_amdgcn_rsqf(ss / (float)D + eps);
+      // o = qscale * acc, so mean(o^2) = qscale^2 * ss / D
+      const float rinv = __builtin_amdgcn_rsqf(ss * (qscale * qscale) / (float)D + eps) * qscale;
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         const uint4 gq = owns ? X[pos(n, dv0 / 8 + i)] : make_uint4(0, 0, 0, 0);
@@ -173,6 +197,11 @@ __global__ __launch_bounds__(512, 1) void readout_bf16(
           acc[j1 / 16][j1 % 16] *= rinv * gm[2 * e + 1] * sigmoid(bf16_hi(g4[e]));
         }
       }
+    } else if constexpr (QN) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mt][r] *= qscale;
     }
     // outputs back to rows in the same LDS tile (each lane overwrites only the
     // gate chunks it has read), then out as coalesced row stores
@@ -208,7 +237,7 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void readout_f32(
     const float* __restrict__ Q, const float* __restrict__ G, const float* __restrict__ w,
     const float4* __restrict__ rstates, float* __restrict__ O, int T, int U, int H, int C, int nc,
-    int epilogue, float eps) {
+    int epilogue, int qnorm, float eps, float l2eps) {
   constexpr int DP = D < 32 ? 32 : D;
   constexpr int HALF = DP / 2;
   constexpr int MT = DP / 32;
@@ -250,6 +279,15 @@ __global__ __launch_bounds__(256, 2) void readout_f32(
     float4 qv[KQ];
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq) qv[kq] = *reinterpret_cast<const float4*>(Q + row + (D / 2) * half + 4 * kq);
+    float qscale = 1.f;  // 1 / |q| under the fused query normalisation
+    if (qnorm) {
+      float qs = 0.f;
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq)
+        qs += qv[kq].x * qv[kq].x + qv[kq].y * qv[kq].y + qv[kq].z * qv[kq].z + qv[kq].w * qv[kq].w;
+      qs += __shfl_xor(qs, 32);
+      qscale = 1.f / __builtin_sqrtf(qs + l2eps);
+    }
     f32x16 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{0.f};
@@ -272,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void readout_f32(
 #pragma unroll
         for (int r = 0; r < 16; ++r) ss += acc[mt][r] * acc[mt][r];
       ss += __shfl_xor(ss, 32);
-      const float rinv = 1.f / __builtin_sqrtf(ss / (float)D + eps);
+      const float rinv = qscale / __builtin_sqrtf(ss * (qscale * qscale) / (float)D + eps);
       const float* gp = G + row + (nout ? dv0 : 0);
 #pragma unroll
       for (int i = 0; i < HALF / 4; ++i) {
@@ -286,6 +324,11 @@ __global__ __launch_bounds__(256, 2) void readout_f32(
           }
         }
       }
+    } else if (qnorm) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mt][r] *= qscale;
     }
     if (valid) {
 #pragma unroll
@@ -299,32 +342,38 @@ __global__ __launch_bounds__(256, 2) void readout_f32(
   }
 }
 
+template <int D, bool EPI, bool GAMMA, bool QN>
+void launch_readout_bf16(const Problem& p, const void* q, const void* gate, const float* w,
+                         const void* rstates, void* out, hipStream_t s) {
+  hipLaunchKernelGGL((readout_bf16<D, EPI, GAMMA, QN>), dim3((unsigned)(p.B * p.T * p.H)), dim3(512), 0, s,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate), w,
+                     static_cast<const uint4*>(rstates), static_cast<uint16_t*>(out), p.T, p.U, p.H, p.C,
+                     p.nc, p.rms_eps, p.l2_eps);
+}
+
+template <int D, bool QN>
+void launch_readout_q(const Problem& p, const void* q, const void* gate, const float* w,
+                      const void* rstates, void* out, hipStream_t s) {
+  if (p.epilogue && w)
+    launch_readout_bf16<D, true, true, QN>(p, q, gate, w, rstates, out, s);
+  else if (p.epilogue)
+    launch_readout_bf16<D, true, false, QN>(p, q, gate, w, rstates, out, s);
+  else
+    launch_readout_bf16<D, false, false, QN>(p, q, gate, w, rstates, out, s);
+}
+
 template <int D>
 hipError_t launch_readout_d(const Problem& p, const void* q, const void* gate, const float* w,
                             const void* rstates, void* out, hipStream_t s) {
-  const unsigned grid = (unsigned)(p.B * p.T * p.H);
-  const int epi = p.epilogue ? 1 : 0;
-  const bool gam = w != nullptr;
-  if (p.bf16 && p.epilogue && gam)
-    hipLaunchKernelGGL((readout_bf16<D, true, true>), dim3(grid), dim3(512), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate), w,
-                       static_cast<const uint4*>(rstates), static_cast<uint16_t*>(out), p.T, p.U,
-                       p.H, p.C, p.nc, p.rms_eps);
-  else if (p.bf16 && p.epilogue)
-    hipLaunchKernelGGL((readout_bf16<D, true, false>), dim3(grid), dim3(512), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate), w,
-                       static_cast<const uint4*>(rstates), static_cast<uint16_t*>(out), p.T, p.U,
-                       p.H, p.C, p.nc, p.rms_eps);
+  if (p.bf16 && p.qnorm)
+    launch_readout_q<D, true>(p, q, gate, w, rstates, out, s);
   else if (p.bf16)
-    hipLaunchKernelGGL((readout_bf16<D, false, false>), dim3(grid), dim3(512), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate), w,
-                       static_cast<const uint4*>(rstates), static_cast<uint16_t*>(out), p.T, p.U,
-                       p.H, p.C, p.nc, p.rms_eps);
+    launch_readout_q<D, false>(p, q, gate, w, rstates, out, s);
   else
-    hipLaunchKernelGGL(readout_f32<D>, dim3(grid), dim3(256), 0, s,
+    hipLaunchKernelGGL(readout_f32<D>, dim3((unsigned)(p.B * p.T * p.H)), dim3(256), 0, s,
                        static_cast<const float*>(q), static_cast<const float*>(gate), w,
                        static_cast<const float4*>(rstates), static_cast<float*>(out), p.T, p.U,
-                       p.H, p.C, p.nc, epi, p.rms_eps);
+                       p.H, p.C, p.nc, p.epilogue ? 1 : 0, p.qnorm ? 1 : 0, p.rms_eps, p.l2_eps);
   return hipGetLastError();
 }
 

@@ -29,7 +29,8 @@ vdn_status check(const vdn_vda_desc* d) {
   if (d->d_k % 16 || d->d_v % 16) return VDN_ERR_INVALID_ARG;
   if (d->n_text < 0 || d->chunk < 1) return VDN_ERR_INVALID_ARG;
   if (d->dtype != VDN_F32 && d->dtype != VDN_BF16) return VDN_ERR_INVALID_ARG;
-  if (d->flags & ~(uint32_t)(VDN_VDA_EPILOGUE | VDN_VDA_DEBUG_KEEP | VDN_VDA_DECAY_BRIDGE))
+  if (d->flags & ~(uint32_t)(VDN_VDA_EPILOGUE | VDN_VDA_DEBUG_KEEP | VDN_VDA_DECAY_BRIDGE |
+                             VDN_VDA_QUERY_L2))
     return VDN_ERR_INVALID_ARG;
   if (!(d->l2_eps > 0.f) || !isfinite(d->l2_eps)) return VDN_ERR_INVALID_ARG;
   if (!(d->rms_eps > 0.f) || !isfinite(d->rms_eps)) return VDN_ERR_INVALID_ARG;
@@ -61,6 +62,7 @@ Problem problem(const vdn_vda_desc* d) {
   p.bf16 = d->dtype == VDN_BF16;
   p.epilogue = (d->flags & VDN_VDA_EPILOGUE) != 0;
   p.bridge = (d->flags & VDN_VDA_DECAY_BRIDGE) != 0;
+  p.qnorm = (d->flags & VDN_VDA_QUERY_L2) != 0;
   p.l2_eps = d->l2_eps;
   p.rms_eps = d->rms_eps;
   return p;
@@ -123,14 +125,17 @@ vdn_status vdn_vda_prepare(const vdn_vda_desc* d, const void* q, const void* k, 
                            hipStream_t stream) {
   const vdn_status st = check(d);
   if (st != VDN_OK) return st;
-  const void* ptrs[] = {q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat};
-  for (const void* p : ptrs)
-    if (!p) return VDN_ERR_INVALID_ARG;
-  for (const void* p : ptrs)
-    if (!aligned(p, 16)) return VDN_ERR_ALIGNMENT;
-  if (q_hat == q || k_hat == k || v_hat == v || q_hat == k_hat || q_hat == v_hat || k_hat == v_hat)
-    return VDN_ERR_INVALID_ARG;
   const Problem p = problem(d);
+  // under VDN_VDA_QUERY_L2 the query is normalised by the forward pass instead
+  if (p.qnorm) q = q_hat = nullptr;
+  const void* ptrs[] = {k, v, wk_s, wk_t, wv_s, wv_t, k_hat, v_hat, q, q_hat};
+  const int nreq = p.qnorm ? 8 : 10;
+  for (int i = 0; i < nreq; ++i)
+    if (!ptrs[i]) return VDN_ERR_INVALID_ARG;
+  for (int i = 0; i < nreq; ++i)
+    if (!aligned(ptrs[i], 16)) return VDN_ERR_ALIGNMENT;
+  if (k_hat == k || v_hat == v || k_hat == v_hat) return VDN_ERR_INVALID_ARG;
+  if (!p.qnorm && (q_hat == q || q_hat == k_hat || q_hat == v_hat)) return VDN_ERR_INVALID_ARG;
   if (launch_prep(p, d->grid_h, d->grid_w, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat,
                   stream) != hipSuccess)
     return VDN_ERR_HIP;

@@ -79,7 +79,14 @@ enum {
    * absorbed with zero writes (S <- S Diag(alpha_s)).  Chunk 0 has no forward
    * bridge, the last chunk no reverse bridge; anchor queries are unchanged.
    * Without the flag a query reads the boundary states as they are. */
-  VDN_VDA_DECAY_BRIDGE = 1u << 2
+  VDN_VDA_DECAY_BRIDGE = 1u << 2,
+  /* Fuse the query's L2 normalisation ([VDN-summary] "무엇과 다른가") into the
+   * readout.  vdn_vda_forward then takes the raw q and reads every
+   * (token, head) row as q / sqrt(sum q^2 + l2_eps), the norm taken in float32
+   * from the exact inputs, so q_hat is never materialised (nor rounded to
+   * `dtype`).  vdn_vda_prepare leaves the query alone under this flag: its q
+   * and q_hat are ignored and may be NULL. */
+  VDN_VDA_QUERY_L2 = 1u << 3
 };
 
 /* Problem descriptor: a host struct owned by the caller, passed by pointer. */
@@ -136,6 +143,8 @@ vdn_status vdn_vda_workspace_layout(const vdn_vda_desc* d, vdn_vda_layout* out);
  * and cross chunk boundaries.  Text tokens are not convolved.
  * q, k, v: [B, T, U, H, d] raw features; q_hat, k_hat, v_hat: same shape,
  * out of place (must not alias the inputs).  Weights as in the header comment.
+ * With VDN_VDA_QUERY_L2 in d->flags q and q_hat are ignored (may be NULL) and
+ * the forward pass normalises the query instead.
  * Errors: VDN_ERR_INVALID_ARG (descriptor, NULL pointer), VDN_ERR_ALIGNMENT,
  * VDN_ERR_HIP.
  */
@@ -164,7 +173,8 @@ vdn_status vdn_vda_prepare(const vdn_vda_desc* d,
  *   readout: o = (S_fwd + S_rev) q; with VDN_VDA_EPILOGUE,
  *     out = rms_weight * o / sqrt(mean(o^2) + rms_eps) * sigmoid(gate)
  *     ([VDN-summary] "무엇과 다른가"), else out = o.
- * q, k must be the prepared (unit-norm) features.  k_text, v_text, beta_text
+ * q, k must be the prepared (unit-norm) features; with VDN_VDA_QUERY_L2, q is
+ * the raw query and the readout normalises it (see the flag).  k_text, v_text, beta_text
  * may be NULL when n_text = 0 (then S_T = 0).  gate is required with
  * VDN_VDA_EPILOGUE and ignored without it.  out is written in `dtype` with
  * round-to-nearest-even.  The state, statistics, inverse and scan are float32;

@@ -46,11 +46,13 @@ def oracle_view(x: dict, w: synth.Workload) -> dict:
     return out
 
 
-def run_forward(x: dict, w: synth.Workload, epilogue=True, rms_weight=None, dev_inputs=None, bridge=False):
+def run_forward(x: dict, w: synth.Workload, epilogue=True, rms_weight=None, dev_inputs=None, bridge=False,
+                query_l2=False):
     """Run vdn_vda_forward on the inputs; returns (out, workspace, desc, device inputs)."""
     import torch
     d = dev_inputs or {k: to_device(v, w.dtype) for k, v in x.items()}
-    desc = bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L, w.chunk, w.dtype, epilogue)
+    desc = bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L, w.chunk, w.dtype, epilogue,
+                        flags=(bd.VDN_VDA_EPILOGUE if epilogue else 0) | (bd.VDN_VDA_QUERY_L2 if query_l2 else 0))
     ws = torch.empty(bd.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
     rw = None if rms_weight is None else torch.from_numpy(rms_weight.astype(np.float32)).cuda()
     L = w.L
@@ -58,7 +60,7 @@ def run_forward(x: dict, w: synth.Workload, epilogue=True, rms_weight=None, dev_
                      d["k_text"] if L else None, d["v_text"] if L else None,
                      d["beta_text"] if L else None, d["gate"], rw,
                      grid=(w.grid_h, w.grid_w), chunk=w.chunk, epilogue=epilogue, workspace=ws,
-                     bridge=bridge)
+                     bridge=bridge, query_l2=query_l2)
     torch.cuda.synchronize()
     return out, ws, desc, d
 

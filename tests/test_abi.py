@@ -182,3 +182,30 @@ def test_chunk_record_limit():
     assert bd.validate(good(T=32768, chunk=1, grid_h=1, grid_w=1, H=1)) == bd.VDN_ERR_INVALID_ARG
     assert bd.validate(good(T=32768, chunk=2, grid_h=1, grid_w=1, H=1)) == bd.VDN_OK
     assert bd.validate(good(T=131072, chunk=4, grid_h=1, grid_w=1, H=1, d=64)) == bd.VDN_OK
+
+
+def test_query_l2_flag():
+    """VDN_VDA_QUERY_L2 is a valid flag; under it vdn_vda_prepare neither requires
+    nor checks q and q_hat, and still checks everything else before a launch."""
+    flags = bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_QUERY_L2
+    assert bd.validate(good(flags=flags)) == bd.VDN_OK
+    assert bd.validate(good(flags=bd.VDN_VDA_QUERY_L2 | bd.VDN_VDA_DECAY_BRIDGE)) == bd.VDN_OK
+    lib = bd.lib()
+    desc = good(flags=bd.VDN_VDA_QUERY_L2)
+    P = [ctypes.c_void_p(A16 + 0x1000000 * i) for i in range(10)]
+    args = list(P)
+    args[0] = args[7] = None   # q, q_hat absent
+    args[1] = None             # k absent
+    assert lib.vdn_vda_prepare(ctypes.byref(desc), *args, None) == bd.VDN_ERR_INVALID_ARG
+    args = list(P)
+    args[0] = ctypes.c_void_p(A16 + 4)  # a misaligned q is ignored ...
+    args[8] = args[1]                   # ... so the k_hat alias is what fails
+    assert lib.vdn_vda_prepare(ctypes.byref(desc), *args, None) == bd.VDN_ERR_INVALID_ARG
+    args = list(P)
+    args[0] = args[7] = None
+    args[9] = ctypes.c_void_p(A16 + 0x9000000 + 2)  # v_hat misaligned
+    assert lib.vdn_vda_prepare(ctypes.byref(desc), *args, None) == bd.VDN_ERR_ALIGNMENT
+    # without the flag a missing q is an error
+    args = list(P)
+    args[0] = None
+    assert lib.vdn_vda_prepare(ctypes.byref(good(epilogue=False)), *args, None) == bd.VDN_ERR_INVALID_ARG

@@ -206,8 +206,25 @@ def test_prepare_edges(name):
     _prep_case(w, heads=list(range(min(w.H, 3))) + ([w.H - 1] if w.H > 3 else []))
 
 
+def _fused_query_prepare(dev, w, kh, vh):
+    """prepare under VDN_VDA_QUERY_L2: no q_hat, and k_hat, v_hat bit-identical to the unfused call."""
+    import torch
+    from frame_wise_delta_02_amd import binding as bd
+    G.say(f"prepare (query left to the readout) {w.name}")
+    qn, kf, vf = bd.prepare(None, dev["k"], dev["v"], dev["wk_s"], dev["wk_t"], dev["wv_s"], dev["wv_t"],
+                            grid=(w.grid_h, w.grid_w), query_l2=True)
+    torch.cuda.synchronize()
+    assert qn is None
+    assert torch.equal(kf.view(torch.int16) if kf.dtype == torch.bfloat16 else kf,
+                       kh.view(torch.int16) if kh.dtype == torch.bfloat16 else kh)
+    assert torch.equal(vf.view(torch.int16) if vf.dtype == torch.bfloat16 else vf,
+                       vh.view(torch.int16) if vh.dtype == torch.bfloat16 else vh)
+    return kf, vf
+
+
 def test_long_prep_full_size_sampled_head():
-    """The long fused clip at full size: prepare + forward; the oracle checks one whole head."""
+    """The long clip at full size: prepare + forward, then the same with the query's
+    L2 normalisation fused into the readout; the oracle checks one whole head."""
     w = synth.WORKLOADS["long_prep_bf16"]
     x, dev, (qh, kh, vh), prepared = _prep_case(w, heads=[5])
     dev2 = dict(dev, q=qh, k=kh, v=vh)
@@ -216,3 +233,39 @@ def test_long_prep_full_size_sampled_head():
     err = G.slice_rel_err(G.to_host_f64(out[:, :, :, [5]]), ref["y"])
     G.say(f"long_prep_bf16 head 5: err(y)={err:.3e}")
     assert err <= G.TOL["bf16"], err
+    del out, qh
+    kf, vf = _fused_query_prepare(dev, w, kh, vh)
+    out2, _, _, _ = G.run_forward(x, w, epilogue=True, dev_inputs=dict(dev, k=kf, v=vf), query_l2=True)
+    err2 = G.slice_rel_err(G.to_host_f64(out2[:, :, :, [5]]), ref["y"])
+    G.say(f"long_prep_bf16 head 5, fused query L2: err(y)={err2:.3e}")
+    assert err2 <= G.TOL["bf16"], err2
+
+
+# The query's L2 normalisation fused into the readout (VDN_VDA_QUERY_L2): raw q
+# into the forward pass, for both readout kernels, every head width, with and
+# without the epilogue and the RMSNorm gain.
+QL2 = {
+    "ql2_bf16_128": dict(H=2, T=9, grid_h=6, grid_w=10, L=8),
+    "ql2_bf16_64_ragged": dict(H=3, T=11, grid_h=7, grid_w=9, L=8, d=64),
+    "ql2_bf16_32": dict(H=2, T=7, grid_h=5, grid_w=13, L=4, d=32),
+    "ql2_bf16_16": dict(H=2, T=6, grid_h=4, grid_w=9, L=4, d=16),
+    "ql2_f32_128": dict(H=2, T=8, grid_h=6, grid_w=7, L=8, dtype="f32"),
+    "ql2_f32_16": dict(H=2, T=6, grid_h=5, grid_w=5, L=4, d=16, dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", list(QL2))
+def test_query_l2_fused(name):
+    w = synth.WORKLOADS["long_prep_bf16"].scaled(name=name, **QL2[name])
+    heads = list(range(w.H))
+    x, dev, (qh, kh, vh), prepared = _prep_case(w, heads=heads)
+    kf, vf = _fused_query_prepare(dev, w, kh, vh)
+    rw = np.random.default_rng(11).uniform(0.5, 1.5, w.d)
+    dev2 = dict(dev, k=kf, v=vf)  # q stays raw
+    tol = G.TOL[w.dtype]
+    for epi, gain in ((False, None), (True, None), (True, rw)):
+        out, _, _, _ = G.run_forward(x, w, epilogue=epi, rms_weight=gain, dev_inputs=dev2, query_l2=True)
+        ref = _oracle_heads(x, w, heads, gate=True, rms_weight=gain, prepared=prepared)
+        err = G.slice_rel_err(G.to_host_f64(out), ref["y" if epi else "o"])
+        G.say(f"{name} epilogue={epi} gain={gain is not None}: err={err:.3e} tol={tol}")
+        assert err <= tol, (epi, gain is not None, err)
