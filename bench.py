@@ -131,6 +131,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="768p_bf16")
+    ap.add_argument("--scan", choices=["auto", "frames", "chunks"], default="auto",
+                    help="force the frame-by-frame or the chunk-composed scan (auto: the library picks)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget; 0 skips it")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="instead of the forward pass, time a plain device copy of this many GiB "
@@ -202,7 +204,8 @@ def main() -> int:
 
     def fwd():
         bd.forward(*step_q, d["alpha"], d["beta"], d["k_text"], d["v_text"], d["beta_text"], d["gate"], None,
-                   grid=grid, chunk=w.chunk, epilogue=True, out=out, workspace=ws, query_l2=w.prep)
+                   grid=grid, chunk=w.chunk, epilogue=True, out=out, workspace=ws, query_l2=w.prep,
+                   scan=None if args.scan == "auto" else args.scan)
 
     def step():
         if w.prep:
@@ -267,7 +270,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "U": w.U,
                    "grid": f"{w.grid_h}x{w.grid_w}", "d": w.d, "text_tokens": w.L, "chunk": w.chunk,
-                   "state": "f32", "prep": w.prep},
+                   "state": "f32", "prep": w.prep, "scan": args.scan},
         "tokens_per_s": round(frames * w.U / (ms * 1e-3), 1),
         "job_roofline": {"bound": "hbm", "algorithmic_bytes": job_bytes(w),
                          "achieved_GBs": round(job_bytes(w) / (ms * 1e-3) / 1e9, 1),

@@ -19,6 +19,9 @@ VDN_VDA_EPILOGUE = 1 << 0
 VDN_VDA_DEBUG_KEEP = 1 << 1
 VDN_VDA_DECAY_BRIDGE = 1 << 2
 VDN_VDA_QUERY_L2 = 1 << 3
+VDN_VDA_SCAN_FRAMES = 1 << 4
+VDN_VDA_SCAN_CHUNKS = 1 << 5
+_SCAN_FLAGS = {None: 0, "frames": VDN_VDA_SCAN_FRAMES, "chunks": VDN_VDA_SCAN_CHUNKS}
 
 EXPORTS = ("vdn_vda_validate", "vdn_vda_workspace_bytes", "vdn_vda_workspace_layout",
            "vdn_vda_prepare", "vdn_vda_forward", "vdn_vda_set_profile_events",
@@ -43,7 +46,7 @@ class Desc(ctypes.Structure):
 
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("stats", "pinv", "s_text", "fwd", "rev", "readout_states", "total")]
+                ("stats", "pinv", "s_text", "fwd", "rev", "readout_states", "chunk_m", "chunk_j", "total")]
 
 
 _lib = None
@@ -150,13 +153,14 @@ def _check(x, name, dev):
 
 def forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weight=None, *,
             grid, chunk=5, epilogue=True, rms_eps=1e-6, out=None, workspace=None, bridge=False,
-            query_l2=False, l2_eps=1e-6):
+            query_l2=False, l2_eps=1e-6, scan=None):
     """VDA forward on prepared features; returns ``out`` [B, T, U, H, d].
 
     Shapes as in include/vdn_vda.h.  ``grid`` = (grid_h, grid_w) with
     grid_h * grid_w = U.  ``workspace`` (uint8, on the device) is allocated
     when not given.  ``bridge`` sets VDN_VDA_DECAY_BRIDGE; ``query_l2`` sets
-    VDN_VDA_QUERY_L2 (``q`` is then the raw query, normalised with ``l2_eps``).
+    VDN_VDA_QUERY_L2 (``q`` is then the raw query, normalised with ``l2_eps``);
+    ``scan`` = "frames" or "chunks" forces that scan (None: the library picks).
     """
     import torch
     B, T, U, H, d = q.shape
@@ -169,7 +173,7 @@ def forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weig
         _check(x, name, dev)
     desc = make_desc(B, H, T, grid[0], grid[1], d, L, chunk, dt, epilogue, l2_eps=l2_eps, rms_eps=rms_eps,
                      flags=(VDN_VDA_EPILOGUE if epilogue else 0) | (VDN_VDA_DECAY_BRIDGE if bridge else 0)
-                     | (VDN_VDA_QUERY_L2 if query_l2 else 0))
+                     | (VDN_VDA_QUERY_L2 if query_l2 else 0) | _SCAN_FLAGS[scan])
     st = validate(desc)
     if st != VDN_OK:
         raise VdaError(st, "vdn_vda_validate")

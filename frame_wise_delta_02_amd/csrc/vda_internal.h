@@ -86,12 +86,13 @@ struct Problem {
   bool epilogue;
   bool bridge;  // VDN_VDA_DECAY_BRIDGE
   bool qnorm;   // VDN_VDA_QUERY_L2: the readout normalises the raw query
+  bool chunked; // scan over chunk-composed pairs (M_c, J_c) instead of frame by frame
   float l2_eps, rms_eps;
 };
 
 // Workspace offsets in bytes (see vdn_vda_layout).
 struct Layout {
-  size_t stats, pinv, s_text, fwd, rev, rstates, total;
+  size_t stats, pinv, s_text, fwd, rev, rstates, chunk_m, chunk_j, total;
 };
 Layout make_layout(const Problem& p);
 
@@ -120,8 +121,11 @@ struct GramPart {
 };
 hipError_t launch_gram(const Problem& p, const GramPart* parts, int nparts, float* stats, hipStream_t s);
 hipError_t launch_solve(const Problem& p, const float* stats, float* pinv, hipStream_t s);
+// The bidirectional scan; with p.chunked, first every chunk's pair
+// (M_c, J_c) into chunk_m / chunk_j ([B, H, 2, n_c, d, d] each), then the scan
+// over chunks.
 hipError_t launch_scan(const Problem& p, const float* stats, const float* pinv, const float* alpha,
-                       float* s_text, float* fwd, float* rev, hipStream_t s);
+                       float* s_text, float* fwd, float* rev, float* chunk_m, float* chunk_j, hipStream_t s);
 hipError_t launch_gather(const Problem& p, const float* s_text, const float* fwd, const float* rev,
                          const float* alpha, void* rstates, hipStream_t s);
 hipError_t launch_readout(const Problem& p, const void* q, const void* gate, const float* rms_weight,

@@ -58,12 +58,27 @@ struct PFrag<D, true> {   // [e][ks]: fragment (2*wave + e, ks) of the hi and lo
   uint4 hi[2][D / 32], lo[2][D / 32];
 };
 
-template <int D, bool SPLIT>
+// Three uses of one frame-step machinery:
+//   SCAN_FRAMES  the bidirectional scan frame by frame (S_T first, then every
+//                absorbed frame, recording F_j / R_j at chunk boundaries);
+//   SCAN_COMPOSE each chunk's transition as one pair (M_c, J_c) with
+//                S_out = S_in M_c + J_c: the chunk's frames scanned from
+//                S = I with no writes (rows of M_c) and from S = 0 with the
+//                writes (rows of J_c), every chunk of every direction at once;
+//   SCAN_CHUNKS  the scan over those pairs, S <- S M_c + J_c, one step per
+//                chunk (n_c - 2 serial steps instead of one per frame).
+// Composing the frame updates of a chunk is exact in exact arithmetic, so the
+// two routes give the same F_j and R_j up to rounding.
+enum { SCAN_FRAMES = 0, SCAN_COMPOSE = 1, SCAN_CHUNKS = 2 };
+
+template <int D, bool SPLIT, int MODE>
 __global__ __launch_bounds__(64 * (D / (D >= 32 ? 32 : 16)))
 void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
-               const float* __restrict__ alpha, float* __restrict__ s_text,
-               float* __restrict__ fwd, float* __restrict__ rev, int B, int H, int T, int C, int nc) {
+               const float* __restrict__ alpha, float* __restrict__ s_text, float* __restrict__ fwd,
+               float* __restrict__ rev, float* __restrict__ chunk_m, float* __restrict__ chunk_j, int B, int H,
+               int T, int C, int nc) {
   static_assert(!SPLIT || D >= 32, "the bfloat16 split needs k-steps of 32");
+  constexpr bool COMPOSE = MODE == SCAN_COMPOSE, CHUNKS = MODE == SCAN_CHUNKS;
   constexpr int MT = scan_mtiles<SPLIT>();
   constexpr int RB = 16 * MT;            // state rows per workgroup
   constexpr int NV = D >= 32 ? 2 : 1;    // adjacent columns per lane
@@ -74,6 +89,7 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   constexpr int LDY = D + 4;             // fp32 Y row (floats)
   constexpr int LDYS = D + 8;            // bfloat16 Y row (elements; 16-B aligned rows)
   constexpr int NFR = D * D / 8;         // 16-B fragments per plane
+  constexpr int RBPU = COMPOSE ? 2 * NRB : NRB;  // row blocks per unit (COMPOSE: M rows, then J rows)
   typedef float vec_t __attribute__((ext_vector_type(NV)));
   constexpr int YBYTES = SPLIT ? 2 * 2 * RB * LDYS * 2 : 2 * RB * LDY * 4;
   __shared__ __attribute__((aligned(16))) unsigned char ybytes[YBYTES];
@@ -81,29 +97,39 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   __bf16* ysp = reinterpret_cast<__bf16*>(ybytes);           // [2 buf][2 plane][RB * LDYS]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // blockIdx -> (group, row block) with all row blocks of a group on one XCD
+  // blockIdx -> (unit, row block) with all row blocks of a unit on one XCD; a
+  // unit is a (batch, head, direction), with COMPOSE also a chunk
   const int nblk = gridDim.x;
   const int bid = blockIdx.x;
   const int groups = B * H * 2;
-  int g, rbi;
-  if (groups % 8 == 0 && nblk == groups * NRB) {
+  const int nch = nc > 2 ? nc - 2 : 0;   // chunks with a record, per direction
+  const int units = COMPOSE ? groups * nch : groups;
+  int u, rbi;
+  if (units % 8 == 0 && nblk == units * RBPU) {
     const int xcd = bid % 8, slot = bid / 8;
-    rbi = slot % NRB;
-    g = (slot / NRB) * 8 + xcd;
+    rbi = slot % RBPU;
+    u = (slot / RBPU) * 8 + xcd;
   } else {
-    rbi = bid % NRB;
-    g = bid / NRB;
+    rbi = bid % RBPU;
+    u = bid / RBPU;
   }
-  if (g >= groups) return;
+  if (u >= units) return;
+  const int g = COMPOSE ? u / nch : u;
   const int dir = g % 2;
   const int h = (g / 2) % H;
   const int b = g / (2 * H);
-  const int row0 = rbi * RB;
+  const bool mpart = COMPOSE && rbi < NRB;  // COMPOSE: this block forms rows of M_c
+  const int row0 = (COMPOSE && !mpart ? rbi - NRB : rbi) * RB;
 
   const size_t head = (size_t)(b * H + h);
   const float* P0 = pinv + head * (T + 1) * (size_t)(D * D);
   const float* S0 = stats + head * (T + 1) * (size_t)(2 * D * D) + (size_t)D * D;  // B part
   const float* A0 = alpha + (size_t)b * T * H * D + (size_t)h * D;                 // + s*H*D
+  // chunk pairs of this (batch, head, direction): slot j of [n_c][d][d] each
+  const size_t cslot = (head * 2 + dir) * (size_t)nc * (D * D);
+  const float* CM = CHUNKS ? chunk_m + cslot : P0;
+  const float* CJ = CHUNKS ? chunk_j + cslot : S0;
+  constexpr size_t BSTRIDE = CHUNKS ? (size_t)D * D : (size_t)2 * D * D;  // slot stride of CJ
 
   const int c0 = wave * WCOLS + NV * (lane & 15);
   const int rr = 4 * (lane >> 4);  // first of this lane's 4 rows in each m-tile
@@ -117,10 +143,10 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   // fp32 path: k-step ks of lane group g = lane / 16 covers channel (d/4) g + ks,
   // so each lane reads a contiguous run of Y (128-bit LDS loads) and of P^{-1} rows
   const int kg = (D / 4) * (lane >> 4);
-  // split path: the fragments of k-step ks of frame s (both column tiles, hi and lo)
-  auto ld_p_ks = [&](int s, int ks, PFrag<D, SPLIT>& dst) {
+  // split path: the fragments of k-step ks of slot s of `base` (both column tiles, hi and lo)
+  auto ld_p_ks = [&](const float* base, int s, int ks, PFrag<D, SPLIT>& dst) {
     if constexpr (SPLIT) {
-      const uint4* F = reinterpret_cast<const uint4*>(P0 + (size_t)s * D * D) + (size_t)(2 * wave * KS2) * 64 + lane;
+      const uint4* F = reinterpret_cast<const uint4*>(base + (size_t)s * D * D) + (size_t)(2 * wave * KS2) * 64 + lane;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         dst.hi[e][ks] = F[(e * KS2 + ks) * 64];
@@ -128,18 +154,18 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
       }
     }
   };
-  auto ld_p = [&](int s, PFrag<D, SPLIT>& dst) {
+  auto ld_p = [&](const float* base, int s, PFrag<D, SPLIT>& dst) {
     if constexpr (SPLIT) {
 #pragma unroll
-      for (int ks = 0; ks < KS2; ++ks) ld_p_ks(s, ks, dst);
+      for (int ks = 0; ks < KS2; ++ks) ld_p_ks(base, s, ks, dst);
     } else {
-      const float* P = P0 + (size_t)s * D * D + c0 + (size_t)kg * D;
+      const float* P = base + (size_t)s * D * D + c0 + (size_t)kg * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) dst.v[ks] = *reinterpret_cast<const vec_t*>(P + ks * D);
     }
   };
-  auto ld_bw = [&](int s, vec_t (&dst)[MT][4]) {
-    const float* Bs = S0 + (size_t)s * 2 * D * D + (size_t)(row0 + rr) * D + c0;
+  auto ld_bw = [&](const float* base, size_t stride, int s, vec_t (&dst)[MT][4]) {
+    const float* Bs = base + (size_t)s * stride + (size_t)(row0 + rr) * D + c0;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -148,13 +174,18 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   auto ld_al = [&](int s) -> vec_t {
     return *reinterpret_cast<const vec_t*>(A0 + (size_t)s * H * D + c0);
   };
-  // Y = S Diag(alpha) + B into buffer buf (alpha = 0 for the text frame)
+  // Y = S Diag(alpha) + B into buffer buf (alpha = 0 for the text frame; the
+  // rows of M_c take no writes)
   auto put_y = [&](int buf, const vec_t (&sv)[MT][4], vec_t a, const vec_t (&bv)[MT][4]) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const vec_t y = sv[mt][r] * a + bv[mt][r];
+        vec_t y;
+        if constexpr (COMPOSE)
+          y = mpart ? sv[mt][r] * a : sv[mt][r] * a + bv[mt][r];
+        else
+          y = sv[mt][r] * a + bv[mt][r];
         const int row = 16 * mt + rr + r;
         if constexpr (SPLIT) {
           __bf16* yh = ysp + (2 * buf) * (RB * LDYS);
@@ -169,10 +200,11 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
         }
       }
   };
-  // S = Y P^{-1} from buffer buf.  Split path: with sn >= 0, k-step ks also
-  // issues frame sn's fragments of k-step ks into pn, so the per-CU load path
-  // streams the next frame while the matrix cores work on this one.
-  auto mul = [&](int buf, const PFrag<D, SPLIT>& p, int sn, PFrag<D, SPLIT>& pn) {
+  // S = Y P from buffer buf (P^{-1} of a frame, or M_c).  Split path: with
+  // sn >= 0, k-step ks also issues slot sn's fragments of k-step ks (from
+  // pbase) into pn, so the per-CU load path streams the next step's operand
+  // while the matrix cores work on this one.
+  auto mul = [&](int buf, const PFrag<D, SPLIT>& p, const float* pbase, int sn, PFrag<D, SPLIT>& pn) {
     if constexpr (SPLIT) {
       // A operand of m-tile mt: row 16 mt + lane%16, k = 32 ks + 8 (lane/16) .. +7.
       // The three terms of a tile share one accumulator: four independent
@@ -184,7 +216,7 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
       for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS2; ++ks) {
-        if (sn >= 0) ld_p_ks(sn, ks, pn);
+        if (sn >= 0) ld_p_ks(pbase, sn, ks, pn);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const bf16x8 ah = *reinterpret_cast<const bf16x8*>(yh + 16 * mt * LDYS + 32 * ks);
@@ -239,47 +271,88 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
         *reinterpret_cast<vec_t*>(dst + (size_t)(row0 + 16 * mt + rr + r) * D + c0) = st[mt][r];
   };
 
-  // ---- frame list of this direction ------------------------------------------
-  // forward: frames 1 .. min(C*(nc-2)-1, T-2); reverse: T-2 .. max(2C, 1)
-  int first, last, step;
-  if (dir == 0) {
-    first = 1;
-    last = nc >= 3 ? min(C * (nc - 2) - 1, T - 2) : 0;
-    step = 1;
+  // ---- step list of this direction -------------------------------------------
+  // SCAN_FRAMES forward: frames 1 .. min(C*(nc-2)-1, T-2); reverse: T-2 .. max(2C, 1).
+  // SCAN_COMPOSE: the frames of one chunk j in this direction's order (forward
+  // chunks 0 .. nc-3, reverse chunks nc-1 .. 2; anchors excluded).
+  // SCAN_CHUNKS: the chunk indices themselves.
+  int first, last, step, nsteps, cj = 0;
+  if constexpr (COMPOSE) {
+    const int ci = u % nch;
+    cj = dir == 0 ? ci : nc - 1 - ci;
+    const int lo = max(C * cj, 1), hi = min(C * (cj + 1) - 1, T - 2);
+    first = dir == 0 ? lo : hi;
+    last = dir == 0 ? hi : lo;
+    step = dir == 0 ? 1 : -1;
+    nsteps = max(0, hi - lo + 1);
+  } else if constexpr (CHUNKS) {
+    first = dir == 0 ? 0 : nc - 1;
+    step = dir == 0 ? 1 : -1;
+    last = first + step * (nch - 1);
+    nsteps = nch;
   } else {
-    first = T - 2;
-    last = nc >= 3 ? max(2 * C, 1) : T - 1;
-    step = -1;
+    if (dir == 0) {
+      first = 1;
+      last = nc >= 3 ? min(C * (nc - 2) - 1, T - 2) : 0;
+      step = 1;
+    } else {
+      first = T - 2;
+      last = nc >= 3 ? max(2 * C, 1) : T - 1;
+      step = -1;
+    }
+    nsteps = (dir == 0) ? max(0, last - first + 1) : max(0, first - last + 1);
   }
-  const int nsteps = (dir == 0) ? max(0, last - first + 1) : max(0, first - last + 1);
+  (void)last;
   float* out0 = (dir == 0 ? fwd : rev) + head * (size_t)nc * D * D;
   const auto rec = make_rsrc(out0, (uint32_t)nc * D * D * 4);  // this head's nc records
 
-  // ---- text frame (slot T): S_T = B_T P_T^{-1} -------------------------------
-  // Set B holds the text frame.  The first absorbed frame's loads (set A) are
-  // in flight during its product; with no frame to absorb they re-read the
-  // text slot and frame 0's alpha (in bounds, never used).
   vec_t zero4[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) zero4[mt][r] = vec_t(0.f);
-  ld_bw(T, bwB);
-  ld_p(T, pfB);
-  put_y(0, zero4, vec_t(0.f), bwB);
-  {
+
+  if constexpr (COMPOSE) {
+    // ---- start: rows row0.. of I (M_c) or of 0 (J_c); first frame's loads --
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < NV; ++e) st[mt][r][e] = (mpart && row0 + 16 * mt + rr + r == c0 + e) ? 1.f : 0.f;
+    // with no frame in the chunk these re-read the text slot and frame 0's
+    // alpha (in bounds, never used)
     const int s1 = nsteps > 0 ? first : T;
-    ld_bw(s1, bwA);
+    ld_bw(S0, BSTRIDE, s1, bwA);
     alA = ld_al(nsteps > 0 ? first : 0);
-    ld_p(s1, pfA);
+    ld_p(P0, s1, pfA);
+  } else {
+    // ---- text frame (slot T): S_T = B_T P_T^{-1} -----------------------------
+    // Set B holds the text frame.  The first step's loads (set A) are in flight
+    // during its product; with no step to take they re-read the text slot
+    // (SCAN_CHUNKS: chunk slot 0) and frame 0's alpha (in bounds, never used).
+    ld_bw(S0, (size_t)2 * D * D, T, bwB);
+    ld_p(P0, T, pfB);
+    put_y(0, zero4, vec_t(0.f), bwB);
+    if constexpr (CHUNKS) {
+      const int j1 = nsteps > 0 ? first : 0;
+      ld_bw(CJ, BSTRIDE, j1, bwA);
+      alA = vec_t(1.f);
+      ld_p(CM, j1, pfA);
+    } else {
+      const int s1 = nsteps > 0 ? first : T;
+      ld_bw(S0, BSTRIDE, s1, bwA);
+      alA = ld_al(nsteps > 0 ? first : 0);
+      ld_p(P0, s1, pfA);
+    }
+    lds_barrier();
+    mul(0, pfB, P0, -1, pfA);
+    if (dir == 0) put_state(s_text + head * (size_t)(D * D));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[mt][r] *= 0.5f;
   }
-  lds_barrier();
-  mul(0, pfB, -1, pfA);
-  if (dir == 0) put_state(s_text + head * (size_t)(D * D));
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) st[mt][r] *= 0.5f;
 
   // the record index after absorbing frame s (or -1)
   auto rec_after = [&](int s) -> int {
@@ -292,49 +365,67 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
     const bool beg = (s == max(C * j, 1));
     return (beg && j >= 2) ? j : -1;
   };
-  // chunks whose recorded state precedes every absorbed frame (empty coverage)
-  if (dir == 0) {
-    for (int j = 0; j <= nc - 3; ++j)
-      if (min(C * (j + 1) - 1, T - 2) < 1) put_state(out0 + (size_t)j * D * D);
-  } else {
-    for (int j = nc - 1; j >= 2; --j)
-      if (max(C * j, 1) > T - 2) put_state(out0 + (size_t)j * D * D);
+  if constexpr (MODE == SCAN_FRAMES) {
+    // chunks whose recorded state precedes every absorbed frame (empty coverage)
+    if (dir == 0) {
+      for (int j = 0; j <= nc - 3; ++j)
+        if (min(C * (j + 1) - 1, T - 2) < 1) put_state(out0 + (size_t)j * D * D);
+    } else {
+      for (int j = nc - 1; j >= 2; --j)
+        if (max(C * j, 1) > T - 2) put_state(out0 + (size_t)j * D * D);
+    }
   }
 
-  // One frame step: form Y from the current set, load the next frame into the
-  // other set (unconditionally: the last step re-reads its own frame), and
-  // multiply.  The loop body runs two steps with the sets swapped, so no
-  // register copy waits for a load and the product only waits for the loads
-  // issued one step earlier (the load counter is in order).
+  // One step: form Y from the current set, load the next step into the other
+  // set (unconditionally: the last step re-reads its own slot), and multiply.
+  // The loop body runs two steps with the sets swapped, so no register copy
+  // waits for a load and the product only waits for the loads issued one step
+  // earlier (the load counter is in order).  SCAN_CHUNKS: Y = S, and the set's
+  // "B rows" are J_c, added after the product.
   auto frame = [&](int i, int s, int buf, const PFrag<D, SPLIT>& pc, const vec_t (&bc)[MT][4], vec_t ac,
                    PFrag<D, SPLIT>& pn, vec_t (&bn)[MT][4], vec_t& an) {
     const int sn = i + 1 < nsteps ? s + step : s;
-    put_y(buf, st, ac, bc);
-    ld_bw(sn, bn);  // needed first (next step's Y), so issued first
-    an = ld_al(sn);
-    if constexpr (!SPLIT) ld_p(sn, pn);  // the split path loads P^{-1} inside the product
+    if constexpr (CHUNKS)
+      put_y(buf, st, vec_t(1.f), zero4);
+    else
+      put_y(buf, st, ac, bc);
+    ld_bw(CJ, BSTRIDE, sn, bn);  // needed first (next step's Y), so issued first
+    if constexpr (CHUNKS)
+      an = vec_t(1.f);
+    else
+      an = ld_al(sn);
+    if constexpr (!SPLIT) ld_p(CM, sn, pn);  // the split path loads P inside the product
     // keep the loads here, ahead of the product (the compiler would otherwise
     // sink them below it, next to their first use)
     asm volatile("" ::: "memory");
     lds_barrier();
-    mul(buf, pc, SPLIT ? sn : -1, pn);
-    // record without a branch: the store is always issued and lands past the
-    // buffer's end (dropped by the buffer unit) unless frame s ends a record,
-    // so every step issues the same memory operations and the load waits need
-    // not allow for a store that may or may not be in flight
-    const int j = rec_after(s);
-    const uint32_t jo = j >= 0 ? (uint32_t)j * (uint32_t)(D * D * 4) : 0x80000000u;
+    mul(buf, pc, CM, SPLIT ? sn : -1, pn);
+    if constexpr (CHUNKS) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t o = jo + (uint32_t)(((row0 + 16 * mt + rr + r) * D + c0) * 4);
-        if constexpr (NV == 2)
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, st[mt][r]),
-                                                rec, o, 0, 0);
-        else
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, st[mt][r][0]), rec, o, 0, 0);
-      }
+        for (int r = 0; r < 4; ++r) st[mt][r] += bc[mt][r];
+    }
+    if constexpr (!COMPOSE) {
+      // record without a branch: the store is always issued and lands past the
+      // buffer's end (dropped by the buffer unit) unless frame s ends a record,
+      // so every step issues the same memory operations and the load waits need
+      // not allow for a store that may or may not be in flight.  SCAN_CHUNKS
+      // records after every step.
+      const int j = CHUNKS ? s : rec_after(s);
+      const uint32_t jo = j >= 0 ? (uint32_t)j * (uint32_t)(D * D * 4) : 0x80000000u;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t o = jo + (uint32_t)(((row0 + 16 * mt + rr + r) * D + c0) * 4);
+          if constexpr (NV == 2)
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, st[mt][r]),
+                                                  rec, o, 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, st[mt][r][0]), rec, o, 0, 0);
+        }
+    }
   };
   // drain every load and store of the prologue once, so that the wait counts
   // inside the loop only have to account for the loop's own memory operations
@@ -343,6 +434,46 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
     frame(i, s, 1, pfA, bwA, alA, pfB, bwB, alB);
     if (i + 1 >= nsteps) break;
     frame(i + 1, s + step, 0, pfB, bwB, alB, pfA, bwA, alA);
+  }
+
+  if constexpr (COMPOSE) {
+    // ---- the chunk's pair: J_c rows as fp32 [d][d]; M_c rows in the layout
+    // the product reads its right operand in (fp32 [d][d], or the two
+    // bfloat16 fragment planes of the split path) ---------------------------
+    const size_t off = cslot + (size_t)cj * (D * D);
+    if (!mpart || !SPLIT) {
+      put_state((mpart ? chunk_m : chunk_j) + off);
+    } else if constexpr (SPLIT) {
+      // This block's 32 rows are k-step rbi of M_c.  Each wave owns columns
+      // 32 wave .. +31 of all 32 rows, so the relayout stays inside the wave:
+      // rows go through the LDS buffer the last step did not use (every wave
+      // has passed that step's barrier, so no wave still reads it), then each
+      // lane gathers its fragments' 8 consecutive rows of one column.
+      const int buf = nsteps > 0 && ((nsteps - 1) & 1) == 0 ? 0 : 1;
+      put_y(buf, st, vec_t(1.f), zero4);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_wave_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      const __bf16* yh = ysp + (2 * buf) * (RB * LDYS);
+      const __bf16* yl = yh + RB * LDYS;
+      uint4* F = reinterpret_cast<uint4*>(chunk_m + off);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int col = 32 * wave + 2 * (lane & 15) + e;
+        uint16_t hv[8], lv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int row = 8 * (lane >> 4) + j;
+          hv[j] = __builtin_bit_cast(uint16_t, yh[row * LDYS + col]);
+          lv[j] = __builtin_bit_cast(uint16_t, yl[row * LDYS + col]);
+        }
+        const size_t f = (size_t)((2 * wave + e) * KS2 + rbi) * 64 + lane;
+        F[f] = make_uint4(hv[0] | (uint32_t)hv[1] << 16, hv[2] | (uint32_t)hv[3] << 16,
+                          hv[4] | (uint32_t)hv[5] << 16, hv[6] | (uint32_t)hv[7] << 16);
+        F[NFR + f] = make_uint4(lv[0] | (uint32_t)lv[1] << 16, lv[2] | (uint32_t)lv[3] << 16,
+                                lv[4] | (uint32_t)lv[5] << 16, lv[6] | (uint32_t)lv[7] << 16);
+      }
+    }
   }
 }
 
@@ -453,23 +584,38 @@ __global__ __launch_bounds__(256) void gather_states(const float* __restrict__ s
   }
 }
 
-template <int D>
-hipError_t launch_scan_d(const Problem& p, const float* stats, const float* pinv,
-                         const float* alpha, float* s_text, float* fwd, float* rev, hipStream_t s) {
+template <int D, bool SPLIT>
+hipError_t launch_scan_t(const Problem& p, const float* stats, const float* pinv, const float* alpha,
+                         float* s_text, float* fwd, float* rev, float* chunk_m, float* chunk_j, hipStream_t s) {
   constexpr int NV = D >= 32 ? 2 : 1;
   constexpr int threads = 64 * (D / (16 * NV));
-  if constexpr (D >= 32) {
-    if (pinv_split(p)) {
-      const unsigned grid = (unsigned)(p.B * p.H * 2 * (D / (16 * scan_mtiles<true>())));
-      hipLaunchKernelGGL((scan_rows<D, true>), dim3(grid), dim3(threads), 0, s, stats, pinv, alpha,
-                         s_text, fwd, rev, p.B, p.H, p.T, p.C, p.nc);
-      return hipGetLastError();
-    }
+  constexpr int NRB = D / (16 * scan_mtiles<SPLIT>());
+  const unsigned grid = (unsigned)(p.B * p.H * 2 * NRB);
+  if (!p.chunked) {
+    hipLaunchKernelGGL((scan_rows<D, SPLIT, SCAN_FRAMES>), dim3(grid), dim3(threads), 0, s, stats, pinv, alpha,
+                       s_text, fwd, rev, nullptr, nullptr, p.B, p.H, p.T, p.C, p.nc);
+    return hipGetLastError();
   }
-  const unsigned grid = (unsigned)(p.B * p.H * 2 * (D / (16 * scan_mtiles<false>())));
-  hipLaunchKernelGGL((scan_rows<D, false>), dim3(grid), dim3(threads), 0, s, stats, pinv, alpha,
-                     s_text, fwd, rev, p.B, p.H, p.T, p.C, p.nc);
+  const int nch = p.nc > 2 ? p.nc - 2 : 0;
+  if (nch > 0) {
+    const unsigned cgrid = (unsigned)(p.B * p.H * 2 * nch * 2 * NRB);
+    hipLaunchKernelGGL((scan_rows<D, SPLIT, SCAN_COMPOSE>), dim3(cgrid), dim3(threads), 0, s, stats, pinv, alpha,
+                       nullptr, nullptr, nullptr, chunk_m, chunk_j, p.B, p.H, p.T, p.C, p.nc);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((scan_rows<D, SPLIT, SCAN_CHUNKS>), dim3(grid), dim3(threads), 0, s, stats, pinv, alpha,
+                     s_text, fwd, rev, chunk_m, chunk_j, p.B, p.H, p.T, p.C, p.nc);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_scan_d(const Problem& p, const float* stats, const float* pinv, const float* alpha,
+                         float* s_text, float* fwd, float* rev, float* chunk_m, float* chunk_j, hipStream_t s) {
+  if constexpr (D >= 32) {
+    if (pinv_split(p)) return launch_scan_t<D, true>(p, stats, pinv, alpha, s_text, fwd, rev, chunk_m, chunk_j, s);
+  }
+  return launch_scan_t<D, false>(p, stats, pinv, alpha, s_text, fwd, rev, chunk_m, chunk_j, s);
 }
 
 template <int D>
@@ -495,12 +641,12 @@ size_t readout_slot_bytes(const Problem& p) {
 }
 
 hipError_t launch_scan(const Problem& p, const float* stats, const float* pinv, const float* alpha,
-                       float* s_text, float* fwd, float* rev, hipStream_t s) {
+                       float* s_text, float* fwd, float* rev, float* chunk_m, float* chunk_j, hipStream_t s) {
   switch (p.D) {
-    case 16: return launch_scan_d<16>(p, stats, pinv, alpha, s_text, fwd, rev, s);
-    case 32: return launch_scan_d<32>(p, stats, pinv, alpha, s_text, fwd, rev, s);
-    case 64: return launch_scan_d<64>(p, stats, pinv, alpha, s_text, fwd, rev, s);
-    case 128: return launch_scan_d<128>(p, stats, pinv, alpha, s_text, fwd, rev, s);
+    case 16: return launch_scan_d<16>(p, stats, pinv, alpha, s_text, fwd, rev, chunk_m, chunk_j, s);
+    case 32: return launch_scan_d<32>(p, stats, pinv, alpha, s_text, fwd, rev, chunk_m, chunk_j, s);
+    case 64: return launch_scan_d<64>(p, stats, pinv, alpha, s_text, fwd, rev, chunk_m, chunk_j, s);
+    case 128: return launch_scan_d<128>(p, stats, pinv, alpha, s_text, fwd, rev, chunk_m, chunk_j, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -12,6 +12,8 @@ namespace vda {
 namespace {
 
 constexpr size_t kAlign = 256;
+// without a scan flag, (batch, head) pairs up to which the chunk-composed scan is chosen
+constexpr size_t kChunkedScanMaxHeads = 8;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -30,8 +32,9 @@ vdn_status check(const vdn_vda_desc* d) {
   if (d->n_text < 0 || d->chunk < 1) return VDN_ERR_INVALID_ARG;
   if (d->dtype != VDN_F32 && d->dtype != VDN_BF16) return VDN_ERR_INVALID_ARG;
   if (d->flags & ~(uint32_t)(VDN_VDA_EPILOGUE | VDN_VDA_DEBUG_KEEP | VDN_VDA_DECAY_BRIDGE |
-                             VDN_VDA_QUERY_L2))
+                             VDN_VDA_QUERY_L2 | VDN_VDA_SCAN_FRAMES | VDN_VDA_SCAN_CHUNKS))
     return VDN_ERR_INVALID_ARG;
+  if ((d->flags & VDN_VDA_SCAN_FRAMES) && (d->flags & VDN_VDA_SCAN_CHUNKS)) return VDN_ERR_INVALID_ARG;
   if (!(d->l2_eps > 0.f) || !isfinite(d->l2_eps)) return VDN_ERR_INVALID_ARG;
   if (!(d->rms_eps > 0.f) || !isfinite(d->rms_eps)) return VDN_ERR_INVALID_ARG;
   // sizes must stay well inside 64-bit element counts and 32-bit grid dimensions
@@ -40,6 +43,9 @@ vdn_status check(const vdn_vda_desc* d) {
   if (U > 2147483647.0 || elems > 9.0e15) return VDN_ERR_INVALID_ARG;
   if ((double)d->B * d->T * d->H * d->grid_h > 4294967295.0) return VDN_ERR_INVALID_ARG;
   if ((double)d->B * d->n_text * d->H > 9.0e15) return VDN_ERR_INVALID_ARG;
+  // the chunk-composition launch: up to 16 row blocks per (batch, head, direction, chunk)
+  if ((double)d->B * d->H * 2 * ((d->T + d->chunk - 1) / d->chunk) * 16 > 2147483647.0)
+    return VDN_ERR_INVALID_ARG;
   // the scan's chunk records of one head must stay below 2^31 bytes: steps that
   // record nothing store at offset 2^31, past that buffer
   if ((double)((d->T + d->chunk - 1) / d->chunk) * d->d_k * d->d_v * 4.0 >= 2147483648.0)
@@ -63,6 +69,17 @@ Problem problem(const vdn_vda_desc* d) {
   p.epilogue = (d->flags & VDN_VDA_EPILOGUE) != 0;
   p.bridge = (d->flags & VDN_VDA_DECAY_BRIDGE) != 0;
   p.qnorm = (d->flags & VDN_VDA_QUERY_L2) != 0;
+  // The frame scan takes one workgroup per 32 (bfloat16) or 16 (float32) state
+  // rows of each (batch, head, direction) and its critical path is one serial
+  // step per frame; the chunk-composed scan adds a fully parallel composition
+  // pass but takes one serial step per chunk.  It pays where the frame scan
+  // leaves most compute units idle.
+  if (d->flags & VDN_VDA_SCAN_CHUNKS)
+    p.chunked = true;
+  else if (d->flags & VDN_VDA_SCAN_FRAMES)
+    p.chunked = false;
+  else
+    p.chunked = p.nc >= 3 && (size_t)p.B * p.H <= kChunkedScanMaxHeads;
   p.l2_eps = d->l2_eps;
   p.rms_eps = d->rms_eps;
   return p;
@@ -87,6 +104,10 @@ Layout make_layout(const Problem& p) {
   o = up(o + heads * p.nc * dd);
   l.rstates = o;
   o = up(o + heads * (p.nc + 1) * readout_slot_bytes(p));
+  l.chunk_m = o;
+  o = up(o + heads * 2 * p.nc * dd);
+  l.chunk_j = o;
+  o = up(o + heads * 2 * p.nc * dd);
   l.total = o;
   return l;
 }
@@ -115,6 +136,8 @@ vdn_status vdn_vda_workspace_layout(const vdn_vda_desc* d, vdn_vda_layout* out) 
   out->fwd = l.fwd;
   out->rev = l.rev;
   out->readout_states = l.rstates;
+  out->chunk_m = l.chunk_m;
+  out->chunk_j = l.chunk_j;
   out->total = l.total;
   return VDN_OK;
 }
@@ -173,6 +196,8 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d, const void* q, const void* k, 
   float* fwd = reinterpret_cast<float*>(ws + l.fwd);
   float* rev = reinterpret_cast<float*>(ws + l.rev);
   void* rstates = ws + l.rstates;
+  float* chunk_m = reinterpret_cast<float*>(ws + l.chunk_m);
+  float* chunk_j = reinterpret_cast<float*>(ws + l.chunk_j);
 
   const int n_video = p.T > 2 ? p.T - 2 : 0;
   hipError_t e = mark(0, stream);
@@ -186,7 +211,7 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d, const void* q, const void* k, 
   if (e == hipSuccess) e = mark(2, stream);  // the text statistics are part of the launch above
   if (e == hipSuccess) e = launch_solve(p, stats, pinv, stream);
   if (e == hipSuccess) e = mark(3, stream);
-  if (e == hipSuccess) e = launch_scan(p, stats, pinv, alpha, s_text, fwd, rev, stream);
+  if (e == hipSuccess) e = launch_scan(p, stats, pinv, alpha, s_text, fwd, rev, chunk_m, chunk_j, stream);
   if (e == hipSuccess) e = mark(4, stream);
   if (e == hipSuccess) e = launch_gather(p, s_text, fwd, rev, alpha, rstates, stream);
   if (e == hipSuccess) e = mark(5, stream);

@@ -80,6 +80,10 @@ WORKLOADS = {
     "long_prep_bf16": Workload("long_prep_bf16", B=1, H=24, T=120, grid_h=48,
                                grid_w=84, d=128, L=512, dtype="bf16",
                                alpha_mu=3.0, prep=True, conv_std=0.2),
+    # one GPU's share of the 768p clip when its 24 heads are split over 8 GPUs:
+    # the few-heads regime where the serial frame scan dominates
+    "768p_share8_bf16": Workload("768p_share8_bf16", B=1, H=3, T=60, grid_h=48,
+                                 grid_w=84, d=128, L=256, dtype="bf16", alpha_mu=3.0),
 }
 # the five workloads in their published order (the stress case twice: two noise readings)
 ORDER = ["tiny_f32", "small_bf16", "768p_bf16", "stress_f32", "long_prep_bf16"]

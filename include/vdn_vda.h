@@ -86,7 +86,17 @@ enum {
    * from the exact inputs, so q_hat is never materialised (nor rounded to
    * `dtype`).  vdn_vda_prepare leaves the query alone under this flag: its q
    * and q_hat are ignored and may be NULL. */
-  VDN_VDA_QUERY_L2 = 1u << 3
+  VDN_VDA_QUERY_L2 = 1u << 3,
+  /* How the bidirectional scan runs (at most one of the two; with neither the
+   * library picks).  Frame by frame: one serial step per absorbed frame.
+   * Chunk-composed ([VDN-summary] "전제와 한계": the chunk-parallel scan):
+   * every chunk's frames are first folded, all chunks at once, into one pair
+   * (M_c, J_c) with S_after = S_before M_c + J_c, then the scan takes one
+   * serial step per chunk.  Both give the same states up to rounding; the
+   * chunk-composed form shortens the serial path where few (batch, head)
+   * pairs leave most of the GPU idle. */
+  VDN_VDA_SCAN_FRAMES = 1u << 4,
+  VDN_VDA_SCAN_CHUNKS = 1u << 5
 };
 
 /* Problem descriptor: a host struct owned by the caller, passed by pointer. */
@@ -118,9 +128,14 @@ typedef struct {
  *   rev    [B, H, n_c, d_v, d_k]: reverse state after the first frame of chunk j.
  *   readout_states: the per-chunk states the readout reads, in the readout
  *          kernel's own packed operand order (not meant for callers).
+ *   chunk_m, chunk_j [B, H, 2 (forward, reverse), n_c, d_v, d_k]: the chunk
+ *          pairs (M_c, J_c) of the chunk-composed scan, written only when it
+ *          runs, for the chunks that end in a record (forward 0..n_c-3,
+ *          reverse 2..n_c-1).  J_c float32; M_c float32, or for VDN_BF16 with
+ *          d_k >= 32 in the two-plane bfloat16 format of pinv.
  *   n_c = ceil(T / chunk).  Entries a query never reads are left unspecified. */
 typedef struct {
-  size_t stats, pinv, s_text, fwd, rev, readout_states, total;
+  size_t stats, pinv, s_text, fwd, rev, readout_states, chunk_m, chunk_j, total;
 } vdn_vda_layout;
 
 /* Check a descriptor without touching the GPU.  Host only. */

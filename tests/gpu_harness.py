@@ -47,7 +47,7 @@ def oracle_view(x: dict, w: synth.Workload) -> dict:
 
 
 def run_forward(x: dict, w: synth.Workload, epilogue=True, rms_weight=None, dev_inputs=None, bridge=False,
-                query_l2=False):
+                query_l2=False, scan=None):
     """Run vdn_vda_forward on the inputs; returns (out, workspace, desc, device inputs)."""
     import torch
     d = dev_inputs or {k: to_device(v, w.dtype) for k, v in x.items()}
@@ -60,7 +60,7 @@ def run_forward(x: dict, w: synth.Workload, epilogue=True, rms_weight=None, dev_
                      d["k_text"] if L else None, d["v_text"] if L else None,
                      d["beta_text"] if L else None, d["gate"], rw,
                      grid=(w.grid_h, w.grid_w), chunk=w.chunk, epilogue=epilogue, workspace=ws,
-                     bridge=bridge, query_l2=query_l2)
+                     bridge=bridge, query_l2=query_l2, scan=scan)
     torch.cuda.synchronize()
     return out, ws, desc, d
 

@@ -48,7 +48,8 @@ def test_valid_descriptors():
 
 @pytest.mark.parametrize("field,value", [
     ("B", 0), ("H", 0), ("T", 0), ("grid_h", 0), ("grid_w", -1), ("n_text", -1), ("chunk", 0),
-    ("d_k", 0), ("d_k", 144), ("d_k", 24), ("dtype", 7), ("flags", 1 << 5)])
+    ("d_k", 0), ("d_k", 144), ("d_k", 24), ("dtype", 7), ("flags", 1 << 6),
+    ("flags", (1 << 4) | (1 << 5))])
 def test_invalid_descriptors(field, value):
     desc = good()
     setattr(desc, field, value)
@@ -79,13 +80,15 @@ def test_workspace_layout_is_consistent():
         B, H, T, d = desc.B, desc.H, desc.T, desc.d_k
         nc = -(-T // desc.chunk)
         f = 4 * d * d
-        offs = [L.stats, L.pinv, L.s_text, L.fwd, L.rev, L.readout_states, L.total]
+        offs = [L.stats, L.pinv, L.s_text, L.fwd, L.rev, L.readout_states, L.chunk_m, L.chunk_j, L.total]
         assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
         assert L.pinv - L.stats >= B * H * (T + 1) * 2 * f
         assert L.s_text - L.pinv >= B * H * (T + 1) * f
         assert L.fwd - L.s_text >= B * H * f
         assert L.rev - L.fwd >= B * H * nc * f
         assert L.readout_states - L.rev >= B * H * nc * f
+        assert L.chunk_j - L.chunk_m >= B * H * 2 * nc * f
+        assert L.total - L.chunk_j >= B * H * 2 * nc * f
         assert L.total == bd.workspace_bytes(desc)
 
 
@@ -209,3 +212,13 @@ def test_query_l2_flag():
     args = list(P)
     args[0] = None
     assert lib.vdn_vda_prepare(ctypes.byref(good(epilogue=False)), *args, None) == bd.VDN_ERR_INVALID_ARG
+
+
+def test_scan_flags():
+    """Either scan may be forced; both at once is an error."""
+    assert bd.validate(good(flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_SCAN_FRAMES)) == bd.VDN_OK
+    assert bd.validate(good(flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_SCAN_CHUNKS)) == bd.VDN_OK
+    assert bd.validate(good(flags=bd.VDN_VDA_SCAN_FRAMES | bd.VDN_VDA_SCAN_CHUNKS)) == bd.VDN_ERR_INVALID_ARG
+    # the scan flags change nothing in the workspace
+    a, b = good(flags=bd.VDN_VDA_SCAN_CHUNKS), good(flags=bd.VDN_VDA_SCAN_FRAMES)
+    assert bd.workspace_bytes(a) == bd.workspace_bytes(b) > 0

@@ -54,36 +54,50 @@ def _check_intermediates(inter, ref, w, heads, tol):
         assert G.mat_rel_err(inter["R"][:, hs, 2:], ref["R"][:, :, 2:]) <= tol, "R"
 
 
-def _run_case(w, heads=None, rms=False, check_inter=True, bridge=False):
+def _run_case(w, heads=None, rms=False, check_inter=True, bridge=False, scan=None):
     x = synth.make_inputs(w)
     heads = list(range(w.H)) if heads is None else heads
     rw = np.random.default_rng(5).uniform(0.5, 1.5, w.d) if rms else None
     tol = G.TOL[w.dtype]
     # raw readout, with intermediates
-    out, ws, desc, dev = G.run_forward(x, w, epilogue=False, bridge=bridge)
+    out, ws, desc, dev = G.run_forward(x, w, epilogue=False, bridge=bridge, scan=scan)
     ref = _oracle_heads(x, w, heads, gate=True, rms_weight=rw, bridge=bridge)
     got = G.to_host_f64(out[:, :, :, heads])
     err_o = G.slice_rel_err(got, ref["o"])
     if check_inter:
         _check_intermediates(G.intermediates(ws, desc, w), ref, w, heads, tol)
     # with RMSNorm + gate
-    out2, _, _, _ = G.run_forward(x, w, epilogue=True, rms_weight=rw, dev_inputs=dev, bridge=bridge)
+    out2, _, _, _ = G.run_forward(x, w, epilogue=True, rms_weight=rw, dev_inputs=dev, bridge=bridge, scan=scan)
     got2 = G.to_host_f64(out2[:, :, :, heads])
     err_y = G.slice_rel_err(got2, ref["y"])
-    G.say(f"{w.name} T={w.T} U={w.U} H={w.H} d={w.d}: err(o)={err_o:.3e} err(y)={err_y:.3e} tol={tol}")
+    G.say(f"{w.name} T={w.T} U={w.U} H={w.H} d={w.d} scan={scan}: err(o)={err_o:.3e} err(y)={err_y:.3e} tol={tol}")
     assert err_o <= tol, err_o
     assert err_y <= tol, err_y
     return err_o, err_y
 
 
+# Both scans (VDN_VDA_SCAN_FRAMES, VDN_VDA_SCAN_CHUNKS) on every workload and
+# edge case: without a flag the library picks by the number of (batch, head)
+# pairs, which would leave one of them untested on small shapes.
+SCANS = ["frames", "chunks"]
+
+
+@pytest.mark.parametrize("scan", SCANS)
 @pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "stress_f32", "stress_tight_f32"])
-def test_workload_full_oracle(name):
-    _run_case(synth.WORKLOADS[name], rms=(name == "small_bf16"))
+def test_workload_full_oracle(name, scan):
+    _run_case(synth.WORKLOADS[name], rms=(name == "small_bf16"), scan=scan)
 
 
 def test_768p_full_size_sampled_heads():
     """The benchmarked workload at full size; the oracle checks two whole heads."""
     _run_case(synth.WORKLOADS["768p_bf16"], heads=[0, 23])
+
+
+@pytest.mark.parametrize("scan", SCANS)
+def test_768p_share8_full_size(scan):
+    """One GPU's share of the 768p clip under an 8-way head split (3 heads), the
+    regime the chunk-composed scan is for; the oracle checks every head."""
+    _run_case(synth.WORKLOADS["768p_share8_bf16"], scan=scan)
 
 
 EDGE = {
@@ -104,9 +118,10 @@ EDGE = {
 }
 
 
+@pytest.mark.parametrize("scan", SCANS)
 @pytest.mark.parametrize("name", list(EDGE))
-def test_edge_cases(name):
-    _run_case(EDGE[name], rms=name.endswith("128") or name in ("d16_bf16", "d32_bf16"))
+def test_edge_cases(name, scan):
+    _run_case(EDGE[name], rms=name.endswith("128") or name in ("d16_bf16", "d32_bf16"), scan=scan)
 
 
 # VDA-Gather's decay bridge (VDN_VDA_DECAY_BRIDGE): every chunk position,
