@@ -97,15 +97,18 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   __bf16* ysp = reinterpret_cast<__bf16*>(ybytes);           // [2 buf][2 plane][RB * LDYS]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // blockIdx -> (unit, row block) with all row blocks of a unit on one XCD; a
-  // unit is a (batch, head, direction), with COMPOSE also a chunk
+  // blockIdx -> (unit, row block) with all row blocks of a unit on one XCD
+  // (blocks are dealt to the 8 XCDs round-robin), so the operand they all read
+  // is fetched once into that XCD's L2; a unit is a (batch, head, direction),
+  // with COMPOSE also a chunk.  The grid rounds the units up to a multiple of
+  // 8; the blocks past the last unit exit at once.
   const int nblk = gridDim.x;
   const int bid = blockIdx.x;
   const int groups = B * H * 2;
   const int nch = nc > 2 ? nc - 2 : 0;   // chunks with a record, per direction
   const int units = COMPOSE ? groups * nch : groups;
   int u, rbi;
-  if (units % 8 == 0 && nblk == units * RBPU) {
+  if (nblk == (units + 7) / 8 * 8 * RBPU) {
     const int xcd = bid % 8, slot = bid / 8;
     rbi = slot % RBPU;
     u = (slot / RBPU) * 8 + xcd;
@@ -590,7 +593,8 @@ hipError_t launch_scan_t(const Problem& p, const float* stats, const float* pinv
   constexpr int NV = D >= 32 ? 2 : 1;
   constexpr int threads = 64 * (D / (16 * NV));
   constexpr int NRB = D / (16 * scan_mtiles<SPLIT>());
-  const unsigned grid = (unsigned)(p.B * p.H * 2 * NRB);
+  const auto xcd_grid = [](int units, int rows) { return (unsigned)((units + 7) / 8 * 8 * rows); };
+  const unsigned grid = xcd_grid(p.B * p.H * 2, NRB);
   if (!p.chunked) {
     hipLaunchKernelGGL((scan_rows<D, SPLIT, SCAN_FRAMES>), dim3(grid), dim3(threads), 0, s, stats, pinv, alpha,
                        s_text, fwd, rev, nullptr, nullptr, p.B, p.H, p.T, p.C, p.nc);
@@ -598,7 +602,7 @@ hipError_t launch_scan_t(const Problem& p, const float* stats, const float* pinv
   }
   const int nch = p.nc > 2 ? p.nc - 2 : 0;
   if (nch > 0) {
-    const unsigned cgrid = (unsigned)(p.B * p.H * 2 * nch * 2 * NRB);
+    const unsigned cgrid = xcd_grid(p.B * p.H * 2 * nch, 2 * NRB);
     hipLaunchKernelGGL((scan_rows<D, SPLIT, SCAN_COMPOSE>), dim3(cgrid), dim3(threads), 0, s, stats, pinv, alpha,
                        nullptr, nullptr, nullptr, chunk_m, chunk_j, p.B, p.H, p.T, p.C, p.nc);
     const hipError_t e = hipGetLastError();

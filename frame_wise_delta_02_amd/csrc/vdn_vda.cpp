@@ -43,8 +43,9 @@ vdn_status check(const vdn_vda_desc* d) {
   if (U > 2147483647.0 || elems > 9.0e15) return VDN_ERR_INVALID_ARG;
   if ((double)d->B * d->T * d->H * d->grid_h > 4294967295.0) return VDN_ERR_INVALID_ARG;
   if ((double)d->B * d->n_text * d->H > 9.0e15) return VDN_ERR_INVALID_ARG;
-  // the chunk-composition launch: up to 16 row blocks per (batch, head, direction, chunk)
-  if ((double)d->B * d->H * 2 * ((d->T + d->chunk - 1) / d->chunk) * 16 > 2147483647.0)
+  // the scan launches: up to 16 row blocks per (batch, head, direction, chunk),
+  // the units rounded up to a multiple of 8
+  if (((double)d->B * d->H * 2 * ((d->T + d->chunk - 1) / d->chunk) + 8) * 16 > 2147483647.0)
     return VDN_ERR_INVALID_ARG;
   // the scan's chunk records of one head must stay below 2^31 bytes: steps that
   // record nothing store at offset 2^31, past that buffer
