@@ -131,6 +131,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="768p_bf16")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="run the workload with this many heads instead (0: as defined)")
     ap.add_argument("--scan", choices=["auto", "frames", "chunks"], default="auto",
                     help="force the frame-by-frame or the chunk-composed scan (auto: the library picks)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget; 0 skips it")
@@ -168,6 +170,8 @@ def main() -> int:
     from frame_wise_delta_02_amd import synth
 
     w = synth.WORKLOADS[args.workload]
+    if args.heads > 0:
+        w = w.scaled(name=f"{w.name}_h{args.heads}", H=args.heads)
     t_gen = time.perf_counter()
     x = synth.make_inputs(w)
     t_gen = time.perf_counter() - t_gen
