@@ -25,7 +25,8 @@ _SCAN_FLAGS = {None: 0, "frames": VDN_VDA_SCAN_FRAMES, "chunks": VDN_VDA_SCAN_CH
 
 EXPORTS = ("vdn_vda_validate", "vdn_vda_workspace_bytes", "vdn_vda_workspace_layout",
            "vdn_vda_prepare", "vdn_vda_forward", "vdn_vda_set_profile_events",
-           "vdn_vda_status_string")
+           "vdn_vda_status_string", "vdn_vda_backward_workspace_bytes",
+           "vdn_vda_backward_workspace_layout", "vdn_vda_backward_readout")
 STAGES = ("gram", "gram_text", "solve", "scan", "gather", "readout")
 
 
@@ -47,6 +48,10 @@ class Desc(ctypes.Structure):
 class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("stats", "pinv", "s_text", "fwd", "rev", "readout_states", "chunk_m", "chunk_j", "total")]
+
+
+class BackwardLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("readout_states_t", "d_out", "d_state_q", "total")]
 
 
 _lib = None
@@ -75,6 +80,12 @@ def lib() -> ctypes.CDLL:
         L.vdn_vda_set_profile_events.restype = ctypes.c_int
         L.vdn_vda_status_string.argtypes = [ctypes.c_int]
         L.vdn_vda_status_string.restype = ctypes.c_char_p
+        L.vdn_vda_backward_workspace_bytes.argtypes = [dp]
+        L.vdn_vda_backward_workspace_bytes.restype = sz
+        L.vdn_vda_backward_workspace_layout.argtypes = [dp, ctypes.POINTER(BackwardLayout)]
+        L.vdn_vda_backward_workspace_layout.restype = ctypes.c_int
+        L.vdn_vda_backward_readout.argtypes = [dp] + [p] * 6 + [sz] + [p] * 3 + [sz, p]
+        L.vdn_vda_backward_readout.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -213,3 +224,44 @@ def prepare(q, k, v, wk_s, wk_t, wv_s, wv_t, *, grid, l2_eps=1e-6, n_text=0, chu
     if st != VDN_OK:
         raise VdaError(st, "vdn_vda_prepare")
     return q_hat, k_hat, v_hat
+
+
+def backward_workspace_bytes(desc: Desc) -> int:
+    return lib().vdn_vda_backward_workspace_bytes(ctypes.byref(desc))
+
+
+def backward_layout(desc: Desc) -> BackwardLayout:
+    out = BackwardLayout()
+    st = lib().vdn_vda_backward_workspace_layout(ctypes.byref(desc), ctypes.byref(out))
+    if st != VDN_OK:
+        raise VdaError(st, "vdn_vda_backward_workspace_layout")
+    return out
+
+
+def backward_readout(q, gate, rms_weight, alpha, dy, fwd_workspace, *, grid, n_text=0, chunk=5, epilogue=True,
+                     bridge=False, rms_eps=1e-6, dq=None, dgate=None, workspace=None):
+    """First stage of the backward pass (vdn_vda_backward_readout): returns
+    (dq, dgate or None, workspace); the workspace holds do and dS_q at the
+    offsets of ``backward_layout``.  ``fwd_workspace`` is the forward's, for the
+    same descriptor and inputs."""
+    import torch
+    B, T, U, H, d = q.shape
+    dev = q.device
+    for name, x in (("q", q), ("gate", gate), ("rms_weight", rms_weight), ("alpha", alpha), ("dy", dy),
+                    ("fwd_workspace", fwd_workspace), ("dq", dq), ("dgate", dgate), ("workspace", workspace)):
+        _check(x, name, dev)
+    desc = make_desc(B, H, T, grid[0], grid[1], d, n_text, chunk, _dtype_of(q), epilogue, rms_eps=rms_eps,
+                     flags=(VDN_VDA_EPILOGUE if epilogue else 0) | (VDN_VDA_DECAY_BRIDGE if bridge else 0))
+    if dq is None:
+        dq = torch.empty_like(q)
+    if epilogue and dgate is None:
+        dgate = torch.empty_like(dy)
+    if workspace is None:
+        workspace = torch.empty(backward_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    st = lib().vdn_vda_backward_readout(ctypes.byref(desc), _ptr(q), _ptr(gate) if epilogue else None,
+                                        _ptr(rms_weight), _ptr(alpha), _ptr(dy), _ptr(fwd_workspace),
+                                        fwd_workspace.numel(), _ptr(dq), _ptr(dgate) if epilogue else None,
+                                        _ptr(workspace), workspace.numel(), _stream())
+    if st != VDN_OK:
+        raise VdaError(st, "vdn_vda_backward_readout")
+    return dq, (dgate if epilogue else None), workspace

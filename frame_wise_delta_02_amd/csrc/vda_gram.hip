@@ -32,6 +32,14 @@
 //
 // float32 inputs: v_mfma_f32_16x16x4f32 takes one token per lane, so tiles are
 // staged in natural token-major order (rows padded by 16 floats).
+//
+// PLAIN mode (the backward pass): V_t^T K_t only, with no beta, of two
+// bfloat16 tensors used as they are (the operands stay bfloat16, the product
+// runs on v_mfma_f32_16x16x32_bf16), written as one d_v x d_k slot per frame;
+// the waves that would form A_t stay idle.  The backward pass forms the
+// adjoint of the state a frame's queries read, dS = dO_t^T Q_t, this way.
+#include <type_traits>
+
 #include "vda_internal.h"
 
 namespace vda {
@@ -49,7 +57,7 @@ struct GramArgs {
   int T_in, U, t_first, n_frames, slot_offset;
 };
 
-template <int D>
+template <int D, bool PLAIN = false>
 __global__ __launch_bounds__(512, 1) void gram_bf16(GramArgs<uint16_t> part0, GramArgs<uint16_t> part1,
                                                     int nblk0, float* __restrict__ stats, int H,
                                                     int T_slots) {
@@ -99,7 +107,7 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(GramArgs<uint16_t> part0, Gr
     const uint32_t xbytes = U > 0 ? (uint32_t)(U - 1) * rowbytes + D * 2 : 0;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc((which ? V : K) + (tok0 * H + h) * (size_t)D, xbytes);
     const __amdgpu_buffer_rsrc_t br =
-        make_rsrc(beta + tok0 * H + h, U > 0 ? (uint32_t)(U - 1) * H * 2 + 2 : 0);
+        make_rsrc(PLAIN ? K : beta + tok0 * H + h, PLAIN || U <= 0 ? 0u : (uint32_t)(U - 1) * H * 2 + 2);
     const uint32_t xoff0 = (uint32_t)tok * rowbytes + cg * 16;
     // Each producer wave covers 32 consecutive tokens of a tile, so one beta load
     // per lane (lanes l and l+32 read the same token) and one square root serve
@@ -116,9 +124,35 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(GramArgs<uint16_t> part0, Gr
       const uint32_t xo = xoff0 + (uint32_t)(it * 64) * rowbytes;
 #pragma unroll
       for (int j = 0; j < TPT; ++j) x[s][j] = buf_load16(xr, xo + j * rowbytes);
-      sb[s] = __builtin_amdgcn_raw_buffer_load_b16(br, boff0 + (uint32_t)(it * 64) * H * 2, 0, 0);
+      if constexpr (!PLAIN) sb[s] = __builtin_amdgcn_raw_buffer_load_b16(br, boff0 + (uint32_t)(it * 64) * H * 2, 0, 0);
     };
     auto store = [&](int s, int buf) {
+      if constexpr (PLAIN) {
+        // raw bfloat16 halves: channel row i of tokens j, j+1 packed into one word
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t t16[TPT];
+#pragma unroll
+          for (int j = 0; j < TPT; ++j) {
+            const uint32_t wd = (i >> 1) == 0 ? x[s][j].x : (i >> 1) == 1 ? x[s][j].y : (i >> 1) == 2 ? x[s][j].z : x[s][j].w;
+            t16[j] = (i & 1) ? (wd >> 16) : (wd & 0xffffu);
+          }
+          const int r = row0 + i;
+          uint8_t* dst = lds[buf] + r * 128 + 16 * (q ^ swz(r)) + hb;
+          if constexpr (TPT == 8) {
+            *reinterpret_cast<uint4*>(dst) = make_uint4(t16[0] | t16[1] << 16, t16[2] | t16[3] << 16,
+                                                        t16[4] | t16[5] << 16, t16[6] | t16[7] << 16);
+          } else if constexpr (TPT == 4) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(t16[0] | t16[1] << 16, t16[2] | t16[3] << 16);
+          } else if constexpr (TPT == 2) {
+            *reinterpret_cast<uint32_t*>(dst) = t16[0] | t16[1] << 16;
+          } else {
+            *reinterpret_cast<uint16_t*>(dst) = (uint16_t)t16[0];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+      }
       const int sq = __float_as_int(__builtin_amdgcn_sqrtf(bf16_to_f32((uint16_t)sb[s])));
       float sc[TPT];
 #pragma unroll
@@ -166,7 +200,8 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(GramArgs<uint16_t> part0, Gr
   } else {
     // ---- consumers ----------------------------------------------------------
     const int wm = wave - 4;
-    const bool mma = wm < WM;
+    // PLAIN: only the waves holding rows of the second tensor (V^T K) multiply
+    const bool mma = wm < WM && (!PLAIN || 16 * wm * MTW >= D);
     f32x4 acc[MTW][NT];
 #pragma unroll
     for (int i = 0; i < MTW; ++i)
@@ -178,19 +213,24 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(GramArgs<uint16_t> part0, Gr
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int qq = 4 * ks + (lane >> 4);
-        f16x8 afr[MTW];
+        typedef std::conditional_t<PLAIN, bf16x8, f16x8> op_t;
+        op_t afr[MTW];
 #pragma unroll
         for (int mi = 0; mi < MTW; ++mi) {
           const int r = 16 * (wm * MTW + mi) + (lane & 15);
-          afr[mi] = *reinterpret_cast<const f16x8*>(base + r * 128 + 16 * (qq ^ swz(r)));
+          afr[mi] = *reinterpret_cast<const op_t*>(base + r * 128 + 16 * (qq ^ swz(r)));
         }
 #pragma unroll
         for (int nj = 0; nj < NT; ++nj) {
           const int r = 16 * nj + (lane & 15);
-          const f16x8 bfr = *reinterpret_cast<const f16x8*>(base + r * 128 + 16 * (qq ^ swz(r)));
+          const op_t bfr = *reinterpret_cast<const op_t*>(base + r * 128 + 16 * (qq ^ swz(r)));
 #pragma unroll
-          for (int mi = 0; mi < MTW; ++mi)
-            acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[mi], bfr, acc[mi][nj], 0, 0, 0);
+          for (int mi = 0; mi < MTW; ++mi) {
+            if constexpr (PLAIN)
+              acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mi], bfr, acc[mi][nj], 0, 0, 0);
+            else
+              acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[mi], bfr, acc[mi][nj], 0, 0, 0);
+          }
         }
         // one k-step of operands live at a time (beside 128 accumulators at d = 128)
         __builtin_amdgcn_sched_barrier(0);
@@ -207,14 +247,16 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(GramArgs<uint16_t> part0, Gr
     }
 
     if (mma) {
-      float* out = stats + ((size_t)(b * H + h) * T_slots + (t + slot_offset)) * (size_t)(R * D);
+      // slot of [A_t; B_t] (2d x d), or PLAIN: of V^T K alone (d x d)
+      constexpr int OUTR = PLAIN ? D : R, ROW0 = PLAIN ? D : 0;
+      float* out = stats + ((size_t)(b * H + h) * T_slots + (t + slot_offset)) * (size_t)(OUTR * D);
 #pragma unroll
       for (int mi = 0; mi < MTW; ++mi)
 #pragma unroll
         for (int nj = 0; nj < NT; ++nj)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            out[(16 * (wm * MTW + mi) + 4 * (lane >> 4) + r) * D + 16 * nj + (lane & 15)] = acc[mi][nj][r];
+            out[(16 * (wm * MTW + mi) + 4 * (lane >> 4) + r - ROW0) * D + 16 * nj + (lane & 15)] = acc[mi][nj][r];
     }
   }
 }
@@ -360,7 +402,29 @@ hipError_t launch_gram_d(const Problem& p, const GramPart* parts, int nparts, fl
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_gram_plain_d(const Problem& p, const void* k, const void* v, int n_frames, float* out,
+                               hipStream_t s) {
+  const unsigned grid = (unsigned)(p.B * n_frames * p.H);
+  if (grid == 0) return hipSuccess;
+  const GramArgs<uint16_t> a{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), nullptr, p.T, p.U, 0,
+                             n_frames, 0};
+  hipLaunchKernelGGL((gram_bf16<D, true>), dim3(grid), dim3(512), 0, s, a, a, (int)grid, out, p.H, n_frames);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_gram_plain(const Problem& p, const void* k, const void* v, float* out, hipStream_t s) {
+  if (!p.bf16) return hipErrorInvalidValue;
+  switch (p.D) {
+    case 16: return launch_gram_plain_d<16>(p, k, v, p.T, out, s);
+    case 32: return launch_gram_plain_d<32>(p, k, v, p.T, out, s);
+    case 64: return launch_gram_plain_d<64>(p, k, v, p.T, out, s);
+    case 128: return launch_gram_plain_d<128>(p, k, v, p.T, out, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_gram(const Problem& p, const GramPart* parts, int nparts, float* stats, hipStream_t s) {
   if (nparts < 1 || nparts > 2) return hipErrorInvalidValue;

@@ -120,6 +120,9 @@ struct GramPart {
   int T_in, U, t_first, n_frames, slot_offset;
 };
 hipError_t launch_gram(const Problem& p, const GramPart* parts, int nparts, float* stats, hipStream_t s);
+// V^T K per frame with no beta, both [B, T, U, H, d] bfloat16, every frame t into
+// out[B, H, T, d, d] (float32): the backward pass's dS_t = dO_t^T Q_t.
+hipError_t launch_gram_plain(const Problem& p, const void* k, const void* v, float* out, hipStream_t s);
 hipError_t launch_solve(const Problem& p, const float* stats, float* pinv, hipStream_t s);
 // The bidirectional scan; with p.chunked, first every chunk's pair
 // (M_c, J_c) into chunk_m / chunk_j ([B, H, 2, n_c, d, d] each), then the scan
@@ -130,6 +133,14 @@ hipError_t launch_gather(const Problem& p, const float* s_text, const float* fwd
                          const float* alpha, void* rstates, hipStream_t s);
 hipError_t launch_readout(const Problem& p, const void* q, const void* gate, const float* rms_weight,
                           const void* rstates, void* out, hipStream_t s);
+// First stage of the backward pass (bfloat16 inputs): rstates_t <- the
+// transposed query states; with p.epilogue dout <- do (bfloat16) and
+// dgate <- the gate's adjoint, else do = dy; dq <- S_q^T do; dsq [B, H, T, d, d]
+// <- do_t^T q_t.  rstates, s_text, fwd, rev: the forward's workspace sections.
+hipError_t launch_backward_readout(const Problem& p, const void* q, const void* gate, const float* rms_weight,
+                                   const void* dy, const void* rstates, const float* s_text, const float* fwd,
+                                   const float* rev, const float* alpha, void* rstates_t, void* dout, void* dq,
+                                   void* dgate, float* dsq, hipStream_t s);
 hipError_t launch_prep(const Problem& p, int grid_h, int grid_w, const void* q, const void* k,
                        const void* v, const float* wk_s, const float* wk_t, const float* wv_s,
                        const float* wv_t, void* q_hat, void* k_hat, void* v_hat, hipStream_t s);

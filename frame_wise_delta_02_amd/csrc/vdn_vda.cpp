@@ -116,6 +116,24 @@ Layout make_layout(const Problem& p) {
   return l;
 }
 
+// Workspace of the backward pass's first stage.
+struct BwdLayout {
+  size_t rstates_t, dout, dsq, total;
+};
+BwdLayout make_bwd_layout(const Problem& p) {
+  const size_t heads = (size_t)p.B * p.H;
+  BwdLayout l;
+  size_t o = 0;
+  l.rstates_t = o;
+  o = up(o + heads * (p.nc + 1) * readout_slot_bytes(p));
+  l.dout = o;
+  o = up(o + (size_t)p.B * p.T * p.U * p.H * p.D * 2);
+  l.dsq = o;
+  o = up(o + heads * p.T * (size_t)p.D * p.D * 4);
+  l.total = o;
+  return l;
+}
+
 }  // namespace vda
 
 using namespace vda;
@@ -221,6 +239,54 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d, const void* q, const void* k, 
   if (e == hipSuccess) e = mark(5, stream);
   if (e == hipSuccess) e = launch_readout(p, q, gate, rms_weight, rstates, out, stream);
   if (e == hipSuccess) e = mark(6, stream);
+  return e == hipSuccess ? VDN_OK : VDN_ERR_HIP;
+}
+
+size_t vdn_vda_backward_workspace_bytes(const vdn_vda_desc* d) {
+  if (check(d) != VDN_OK) return 0;
+  return make_bwd_layout(problem(d)).total;
+}
+
+vdn_status vdn_vda_backward_workspace_layout(const vdn_vda_desc* d, vdn_vda_backward_layout* out) {
+  const vdn_status st = check(d);
+  if (st != VDN_OK) return st;
+  if (!out) return VDN_ERR_INVALID_ARG;
+  const BwdLayout l = make_bwd_layout(problem(d));
+  out->readout_states_t = l.rstates_t;
+  out->d_out = l.dout;
+  out->d_state_q = l.dsq;
+  out->total = l.total;
+  return VDN_OK;
+}
+
+vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d, const void* q, const void* gate,
+                                    const float* rms_weight, const float* alpha, const void* dy,
+                                    const void* fwd_workspace, size_t fwd_workspace_bytes, void* dq,
+                                    void* dgate, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  const vdn_status st = check(d);
+  if (st != VDN_OK) return st;
+  const bool epi = (d->flags & VDN_VDA_EPILOGUE) != 0;
+  if (d->dtype != VDN_BF16 || (d->flags & VDN_VDA_QUERY_L2)) return VDN_ERR_UNSUPPORTED;
+  if (!q || !alpha || !dy || !dq || !fwd_workspace) return VDN_ERR_INVALID_ARG;
+  if (epi && (!gate || !dgate)) return VDN_ERR_INVALID_ARG;
+  const Problem p = problem(d);
+  const Layout fl = make_layout(p);
+  const BwdLayout bl = make_bwd_layout(p);
+  if (fwd_workspace_bytes < fl.total) return VDN_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < bl.total) return VDN_ERR_WORKSPACE;
+  const void* need16[] = {q, dy, dq, alpha, epi ? gate : nullptr, epi ? dgate : nullptr};
+  for (const void* ptr : need16)
+    if (ptr && !aligned(ptr, 16)) return VDN_ERR_ALIGNMENT;
+  if (rms_weight && !aligned(rms_weight, 4)) return VDN_ERR_ALIGNMENT;
+  if (!aligned(workspace, kAlign) || !aligned(fwd_workspace, kAlign)) return VDN_ERR_ALIGNMENT;
+  if (dq == q || dq == dy || (epi && (dgate == gate || dgate == dy || dgate == dq))) return VDN_ERR_INVALID_ARG;
+  const char* fw = static_cast<const char*>(fwd_workspace);
+  char* ws = static_cast<char*>(workspace);
+  const hipError_t e = launch_backward_readout(
+      p, q, gate, rms_weight, dy, fw + fl.rstates, reinterpret_cast<const float*>(fw + fl.s_text),
+      reinterpret_cast<const float*>(fw + fl.fwd), reinterpret_cast<const float*>(fw + fl.rev), alpha,
+      ws + bl.rstates_t, ws + bl.dout, dq, dgate, reinterpret_cast<float*>(ws + bl.dsq), stream);
   return e == hipSuccess ? VDN_OK : VDN_ERR_HIP;
 }
 

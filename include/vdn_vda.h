@@ -209,6 +209,59 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d,
                            void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/*
+ * Backward pass, first stage: back through the epilogue and the readout.
+ *
+ * The forward pass is differentiated with respect to its inputs (the training
+ * of the linear branch, [VDN-summary] "전제와 한계"); this stage covers the
+ * readout o_t = S_q(t) q_t (S_q(t) = the forward plus the reverse state the
+ * frame's queries read, [VDN-summary] "어떻게 동작하나") and, with
+ * VDN_VDA_EPILOGUE, y = rms_weight * o / sqrt(mean o^2 + rms_eps) * sigmoid(gate)
+ * ([VDN-summary] "무엇과 다른가").  Given the output's adjoint dy it writes
+ *   dq    [B, T, U, H, d_k] = S_q(t)^T do per token                (dtype),
+ *   dgate [B, T, U, H, d_v] = dy * rms_weight * n * s * (1 - s)     (dtype;
+ *         n = o / sqrt(mean o^2 + rms_eps), s = sigmoid(gate); with VDN_VDA_EPILOGUE),
+ * and leaves in its workspace, at the offsets vdn_vda_backward_workspace_layout()
+ * reports,
+ *   d_out     [B, T, U, H, d_v] bfloat16: do, the readout's adjoint
+ *             (= rms_weight * s * dy * r - n * r * mean(rms_weight * s * dy * n),
+ *             r = 1 / sqrt(mean o^2 + rms_eps)); written with VDN_VDA_EPILOGUE
+ *             only -- without it do is dy itself and dy is read in its place;
+ *   d_state_q [B, H, T, d_v, d_k] float32: sum over the frame's tokens of
+ *             do q^T, the adjoint of S_q(t), for every frame (the next stage
+ *             turns these into the adjoints of the records and of S_T);
+ *   readout_states_t: S_q^T per chunk slot in the readout kernel's operand
+ *             order (not meant for callers).
+ * The gradient of rms_weight is not formed by this stage.
+ * fwd_workspace must hold what vdn_vda_forward left there for the same
+ * descriptor and inputs (q, k, v, alpha, beta, text, gate, rms_weight); alpha
+ * is read for the decay bridge.  dy, dq, dgate are device buffers owned by the
+ * caller; dq and dgate must not alias any input.  Supported: VDN_BF16 without
+ * VDN_VDA_QUERY_L2 (else VDN_ERR_UNSUPPORTED).  Errors: VDN_ERR_INVALID_ARG
+ * (NULL pointer, gate or dgate missing with the epilogue, aliasing),
+ * VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE (either workspace too small or NULL),
+ * VDN_ERR_ALIGNMENT (16 B for tensors, 256 B for workspaces), VDN_ERR_HIP.
+ * Asynchronous on `stream`.
+ */
+typedef struct {
+  size_t readout_states_t, d_out, d_state_q, total;
+} vdn_vda_backward_layout;
+
+/* Workspace bytes vdn_vda_backward_readout needs for `d`; 0 if `d` is invalid. */
+size_t vdn_vda_backward_workspace_bytes(const vdn_vda_desc* d);
+
+/* Fill `out` (host) with the backward workspace's offsets for `d`. */
+vdn_status vdn_vda_backward_workspace_layout(const vdn_vda_desc* d, vdn_vda_backward_layout* out);
+
+vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d,
+                                    const void* q, const void* gate,
+                                    const float* rms_weight, const float* alpha,
+                                    const void* dy,
+                                    const void* fwd_workspace, size_t fwd_workspace_bytes,
+                                    void* dq, void* dgate,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
 /* Profiling hook for benchmarks.  While set, vdn_vda_forward records events[0]
  * on its stream before its first kernel and events[i] after stage i, for
  * i = 1..VDN_VDA_STAGES: frame statistics, text statistics, solve, scan,

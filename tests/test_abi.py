@@ -222,3 +222,41 @@ def test_scan_flags():
     # the scan flags change nothing in the workspace
     a, b = good(flags=bd.VDN_VDA_SCAN_CHUNKS), good(flags=bd.VDN_VDA_SCAN_FRAMES)
     assert bd.workspace_bytes(a) == bd.workspace_bytes(b) > 0
+
+
+def test_backward_readout_argument_errors_before_launch():
+    lib = bd.lib()
+    desc = good()
+    fw = bd.workspace_bytes(desc)
+    bw = bd.backward_workspace_bytes(desc)
+    assert bw == bd.backward_layout(desc).total > 0
+    L = bd.backward_layout(desc)
+    offs = [L.readout_states_t, L.d_out, L.d_state_q, L.total]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert L.d_state_q - L.d_out >= desc.B * desc.T * 48 * 84 * desc.H * desc.d_v * 2
+    assert L.total - L.d_state_q >= desc.B * desc.H * desc.T * desc.d_v * desc.d_k * 4
+    names = ["q", "gate", "rms", "alpha", "dy", "fws", "dq", "dgate", "ws"]
+    base = {n: A16 + 0x1000000 * i for i, n in enumerate(names)}
+
+    def call(d=desc, fwb=fw, bwb=bw, **over):
+        p = dict(base, rms=0)
+        p.update(over)
+        P = [ctypes.c_void_p(p[n]) if p[n] else None for n in names]
+        return lib.vdn_vda_backward_readout(ctypes.byref(d), P[0], P[1], P[2], P[3], P[4], P[5], fwb,
+                                            P[6], P[7], P[8], bwb, None)
+
+    assert call(q=0) == bd.VDN_ERR_INVALID_ARG
+    assert call(dy=0) == bd.VDN_ERR_INVALID_ARG
+    assert call(gate=0) == bd.VDN_ERR_INVALID_ARG           # the epilogue needs the gate ...
+    assert call(dgate=0) == bd.VDN_ERR_INVALID_ARG          # ... and its adjoint's buffer
+    assert call(dq=base["q"]) == bd.VDN_ERR_INVALID_ARG     # aliasing
+    assert call(fwb=fw - 1) == bd.VDN_ERR_WORKSPACE
+    assert call(bwb=bw - 1) == bd.VDN_ERR_WORKSPACE
+    assert call(ws=0) == bd.VDN_ERR_WORKSPACE
+    assert call(dy=base["dy"] + 8) == bd.VDN_ERR_ALIGNMENT
+    assert call(ws=base["ws"] + 16) == bd.VDN_ERR_ALIGNMENT
+    assert call(d=good(dtype="f32")) == bd.VDN_ERR_UNSUPPORTED
+    assert call(d=good(flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_QUERY_L2)) == bd.VDN_ERR_UNSUPPORTED
+    # without the epilogue the gate is not needed
+    raw = good(epilogue=False)
+    assert call(d=raw, gate=0, dgate=0, q=0) == bd.VDN_ERR_INVALID_ARG  # (q still is)
