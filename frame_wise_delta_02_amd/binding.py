@@ -26,7 +26,7 @@ _SCAN_FLAGS = {None: 0, "frames": VDN_VDA_SCAN_FRAMES, "chunks": VDN_VDA_SCAN_CH
 EXPORTS = ("vdn_vda_validate", "vdn_vda_workspace_bytes", "vdn_vda_workspace_layout",
            "vdn_vda_prepare", "vdn_vda_forward", "vdn_vda_set_profile_events",
            "vdn_vda_status_string", "vdn_vda_backward_workspace_bytes",
-           "vdn_vda_backward_workspace_layout", "vdn_vda_backward_readout")
+           "vdn_vda_backward_workspace_layout", "vdn_vda_backward_readout", "vdn_vda_backward_scan")
 STAGES = ("gram", "gram_text", "solve", "scan", "gather", "readout")
 
 
@@ -51,7 +51,8 @@ class Layout(ctypes.Structure):
 
 
 class BackwardLayout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("readout_states_t", "d_out", "d_state_q", "total")]
+    _fields_ = [(n, ctypes.c_size_t) for n in ("readout_states_t", "d_out", "d_state_q", "d_record_f", "d_record_r",
+                                               "d_text_q", "lam_f", "lam_r", "d_a", "d_b", "total")]
 
 
 _lib = None
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.vdn_vda_backward_workspace_layout.restype = ctypes.c_int
         L.vdn_vda_backward_readout.argtypes = [dp] + [p] * 6 + [sz] + [p] * 3 + [sz, p]
         L.vdn_vda_backward_readout.restype = ctypes.c_int
+        L.vdn_vda_backward_scan.argtypes = [dp, p, p, sz, p, p, sz, p]
+        L.vdn_vda_backward_scan.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -265,3 +268,22 @@ def backward_readout(q, gate, rms_weight, alpha, dy, fwd_workspace, *, grid, n_t
     if st != VDN_OK:
         raise VdaError(st, "vdn_vda_backward_readout")
     return dq, (dgate if epilogue else None), workspace
+
+
+def backward_scan(alpha, fwd_workspace, workspace, *, shape, grid, n_text=0, chunk=5, dtype="bf16", epilogue=True,
+                  dalpha=None):
+    """Second stage of the backward pass (vdn_vda_backward_scan) on the first
+    stage's workspace; returns dalpha [B, T, H, d] float32.  ``shape`` = (B, T, H, d)."""
+    import torch
+    B, T, H, d = shape
+    dev = alpha.device
+    for name, x in (("alpha", alpha), ("fwd_workspace", fwd_workspace), ("workspace", workspace), ("dalpha", dalpha)):
+        _check(x, name, dev)
+    desc = make_desc(B, H, T, grid[0], grid[1], d, n_text, chunk, dtype, epilogue)
+    if dalpha is None:
+        dalpha = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+    st = lib().vdn_vda_backward_scan(ctypes.byref(desc), _ptr(alpha), _ptr(fwd_workspace), fwd_workspace.numel(),
+                                     _ptr(dalpha), _ptr(workspace), workspace.numel(), _stream())
+    if st != VDN_OK:
+        raise VdaError(st, "vdn_vda_backward_scan")
+    return dalpha

@@ -22,6 +22,7 @@
 //    the epilogue's derivative in registers; do (bfloat16) and dgate stream
 //    out through the same per-wave LDS tiles that bring q, gate and dy in;
 //  * dS_q: the frame-statistics kernel in its PLAIN mode on (q, do).
+#include <algorithm>
 #include <type_traits>
 
 #include "vda_internal.h"
@@ -332,6 +333,185 @@ hipError_t backward_readout_d(const Problem& p, const void* q, const void* gate,
   return launch_gram_plain(p, q, do_, dsq, s);
 }
 
+// ---------------------------------------------------------------------------
+// second stage: from the query-state adjoints to dA_s, dB_s and dalpha_s
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void fill_zero(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// The coverage rules backwards (no bridge): the adjoint of record F_j is the
+// sum of dS_q over the non-anchor frames of chunk j + 2, that of R_j over
+// chunk j - 2; S_T receives dS_q of the anchors, half of dS_q where a side
+// reads S_T / 2, and half of the adjoint of every record the scan never
+// reaches (a record whose coverage is empty is S_T / 2 itself).  One thread
+// per 4 consecutive entries of the d x d matrices of one (batch, head).
+template <int D>
+__global__ __launch_bounds__(256) void backward_gather(const float* __restrict__ dsq, float* __restrict__ dF,
+                                                       float* __restrict__ dR, float* __restrict__ dST, int T,
+                                                       int C, int nc) {
+  constexpr int N4 = D * D / 4;
+  const int per = (N4 + 255) / 256;
+  const int head = blockIdx.x / per;
+  const int e4 = (blockIdx.x % per) * 256 + threadIdx.x;
+  if (e4 >= N4) return;
+  const float4* S = reinterpret_cast<const float4*>(dsq) + (size_t)head * T * N4 + e4;
+  float4* F = reinterpret_cast<float4*>(dF) + (size_t)head * nc * N4 + e4;
+  float4* R = reinterpret_cast<float4*>(dR) + (size_t)head * nc * N4 + e4;
+  auto add = [](float4& a, float4 b, float w) {
+    a.x += w * b.x; a.y += w * b.y; a.z += w * b.z; a.w += w * b.w;
+  };
+  float4 st = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < nc; ++j) {
+    // chunk j's non-anchor frames feed F_{j-2} and R_{j+2}
+    float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int t = C * j; t < min(C * (j + 1), T); ++t)
+      if (t != 0 && t != T - 1) add(g, S[(size_t)t * N4], 1.f);
+    if (j >= 2) F[(size_t)(j - 2) * N4] = g; else add(st, g, 0.5f);
+    if (j + 2 <= nc - 1) R[(size_t)(j + 2) * N4] = g; else add(st, g, 0.5f);
+  }
+  // slots no chunk feeds (F_{nc-2}, F_{nc-1}, R_0, R_1) are not records: zero,
+  // since the adjoint scan reads every slot (scaled by zero where it is none)
+  for (int j = max(nc - 2, 0); j < nc; ++j) F[(size_t)j * N4] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < min(2, nc); ++j) R[(size_t)j * N4] = make_float4(0.f, 0.f, 0.f, 0.f);
+  // records the scan never reaches (empty coverage) are S_T / 2 itself
+  for (int j = 0; j <= nc - 3; ++j)
+    if (min(C * (j + 1) - 1, T - 2) < 1) add(st, F[(size_t)j * N4], 0.5f);
+  for (int j = nc - 1; j >= 2; --j)
+    if (max(C * j, 1) > T - 2) add(st, R[(size_t)j * N4], 0.5f);
+  if (T >= 1) add(st, S[0], 1.f);
+  if (T >= 2) add(st, S[(size_t)(T - 1) * N4], 1.f);
+  reinterpret_cast<float4*>(dST)[(size_t)head * N4 + e4] = st;
+}
+
+// P = (I + A_s)^{-1} as float32 [d][d] from the solve's two bfloat16 planes
+// (hi + lo; fragment f = ((2w + e)(d/32) + ks)*64 + l holds
+// P[32 ks + 8 (l/16) + j][32 w + 2 (l%16) + e], j = 0..7).  One workgroup per slot.
+template <int D>
+__global__ __launch_bounds__(256) void decode_pinv(const uint4* __restrict__ planes, float* __restrict__ P) {
+  constexpr int KS = D / 32, NFR = D * D / 8;
+  const uint4* src = planes + (size_t)blockIdx.x * 2 * NFR;
+  float* dst = P + (size_t)blockIdx.x * D * D;
+  for (int f = threadIdx.x; f < NFR; f += 256) {
+    const int l = f % 64, ks = (f / 64) % KS, we = (f / 64) / KS;
+    const int col = 32 * (we / 2) + 2 * (l % 16) + we % 2, row0 = 32 * ks + 8 * (l / 16);
+    const uint4 h = src[f], lo = src[NFR + f];
+    const uint32_t hw[4] = {h.x, h.y, h.z, h.w}, lw[4] = {lo.x, lo.y, lo.z, lo.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dst[(row0 + 2 * e) * D + col] = bf16_lo(hw[e]) + bf16_lo(lw[e]);
+      dst[(row0 + 2 * e + 1) * D + col] = bf16_hi(hw[e]) + bf16_hi(lw[e]);
+    }
+  }
+}
+
+// One operand of a batched d x d product: matrix (head, slot) at
+// base + head * head_stride + (slot + slot_offset) * slot_stride (floats).
+struct MatArg {
+  const float* base;
+  size_t head_stride, slot_stride;
+  int slot_offset;
+};
+
+// C = alpha op(A) op(B) + beta C for every (head, slot), slots 1..T-2 (the
+// absorbed frames) and T (the text frame): workgroup i takes head i / n and
+// the (i % n)-th of those n slots.  float32 on v_mfma_f32_16x16x4f32;
+// both operands staged in LDS (rows padded by 4 floats); wave w forms output
+// rows (d / NWA) w .. of all columns.
+template <int D, bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_dd(MatArg A, MatArg B, float* __restrict__ Cb, size_t c_head,
+                                               size_t c_slot, float alpha, float beta, int T) {
+  constexpr int LD = D + 4;
+  constexpr int NWA = D / 16 >= 4 ? 4 : D / 16;  // waves with rows
+  constexpr int MTW = D / 16 / NWA;               // 16-row tiles per such wave
+  constexpr int NT = D / 16;
+  __shared__ float sa[D * LD], sb[D * LD];
+  const int nfr = T > 2 ? T - 2 : 0, nslot = nfr + 1;
+  const int head = blockIdx.x / nslot, k = blockIdx.x % nslot;
+  const int slot = k < nfr ? 1 + k : T;
+  const float* a = A.base + head * A.head_stride + (size_t)(slot + A.slot_offset) * A.slot_stride;
+  const float* b = B.base + head * B.head_stride + (size_t)(slot + B.slot_offset) * B.slot_stride;
+  float* c = Cb + head * c_head + (size_t)slot * c_slot;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < D * D / 4; i += 256) {
+    const int r = i / (D / 4), c4 = i % (D / 4);
+    const float4 va = *reinterpret_cast<const float4*>(a + (size_t)r * D + 4 * c4);
+    const float4 vb = *reinterpret_cast<const float4*>(b + (size_t)r * D + 4 * c4);
+    *reinterpret_cast<float4*>(&sa[r * LD + 4 * c4]) = va;
+    *reinterpret_cast<float4*>(&sb[r * LD + 4 * c4]) = vb;
+  }
+  __syncthreads();
+  if (wave >= NWA) return;
+  // op(A)[m][k] = TA ? A[k][m] : A[m][k]; op(B)[k][n] = TB ? B[n][k] : B[k][n]
+  auto opa = [&](int m, int kk) { return TA ? sa[kk * LD + m] : sa[m * LD + kk]; };
+  auto opb = [&](int kk, int n) { return TB ? sb[n * LD + kk] : sb[kk * LD + n]; };
+  f32x4 acc[MTW][NT];
+#pragma unroll
+  for (int mi = 0; mi < MTW; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < NT; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int m0 = 16 * MTW * wave;
+  for (int k4 = 0; k4 < D / 4; ++k4) {
+    const int kk = 4 * k4 + (lane >> 4);
+    float av[MTW], bv[NT];
+#pragma unroll
+    for (int mi = 0; mi < MTW; ++mi) av[mi] = opa(m0 + 16 * mi + (lane & 15), kk);
+#pragma unroll
+    for (int nj = 0; nj < NT; ++nj) bv[nj] = opb(kk, 16 * nj + (lane & 15));
+#pragma unroll
+    for (int mi = 0; mi < MTW; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < NT; ++nj)
+        acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi], bv[nj], acc[mi][nj], 0, 0, 0);
+  }
+  // tile (mi, nj), lane l, reg r: C[m0 + 16 mi + 4 (l/16) + r][16 nj + l%16]
+#pragma unroll
+  for (int mi = 0; mi < MTW; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < NT; ++nj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float* o = c + (size_t)(m0 + 16 * mi + 4 * (lane >> 4) + r) * D + 16 * nj + (lane & 15);
+        *o = alpha * acc[mi][nj][r] + (beta != 0.f ? beta * *o : 0.f);
+      }
+}
+
+// dPinv = Diag(alpha_s) M + N and dalpha_s[k] = sum_m M[k][m] P[k][m] (P is
+// symmetric: the diagonal of M P), for the absorbed frames; the text slot T
+// has no decay: dPinv = N.  One workgroup per (head, slot), one thread per row k.
+template <int D>
+__global__ __launch_bounds__(D) void combine_dpinv(const float* __restrict__ M, const float* __restrict__ N,
+                                                   const float* __restrict__ P, const float* __restrict__ alpha,
+                                                   float* __restrict__ dPinv, float* __restrict__ dalpha, int T,
+                                                   int H) {
+  const int nfr = T > 2 ? T - 2 : 0, nslot = nfr + 1;
+  const int head = blockIdx.x / nslot, k = blockIdx.x % nslot;
+  const int slot = k < nfr ? 1 + k : T;
+  const int b = head / H, h = head % H;
+  const int row = threadIdx.x;
+  const size_t base = ((size_t)head * (T + 1) + slot) * D * D + (size_t)row * D;
+  const bool frame = slot < T;
+  const float a = frame ? alpha[(((size_t)b * T + slot) * H + h) * D + row] : 0.f;
+  float dot = 0.f;
+  for (int m = 0; m < D; ++m) {
+    const float mv = M[base + m];
+    dot += mv * P[base + m];
+    dPinv[base + m] = a * mv + N[base + m];
+  }
+  if (frame) dalpha[(((size_t)b * T + slot) * H + h) * D + row] = dot;
+}
+
+// The text frame's adjoint: dS_T (from the queries) plus half the final
+// adjoint of each scan (both start from S_T / 2), into slot T of lam_f.
+__global__ __launch_bounds__(256) void text_adjoint(const float* __restrict__ dST, const float* __restrict__ fin,
+                                                    float* __restrict__ lam_f, int T, int DD) {
+  const int head = blockIdx.y;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < DD; i += gridDim.x * 256)
+    lam_f[((size_t)head * (T + 1) + T) * DD + i] =
+        dST[(size_t)head * DD + i] + 0.5f * (fin[((size_t)head * 2) * DD + i] + fin[((size_t)head * 2 + 1) * DD + i]);
+}
 }  // namespace
 
 hipError_t launch_backward_readout(const Problem& p, const void* q, const void* gate, const float* rms_weight,
@@ -344,6 +524,89 @@ hipError_t launch_backward_readout(const Problem& p, const void* q, const void* 
     case 32: return backward_readout_d<32>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, s);
     case 64: return backward_readout_d<64>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, s);
     case 128: return backward_readout_d<128>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// second stage orchestration -------------------------------------------------
+
+namespace {
+
+template <int D>
+hipError_t backward_scan_d(const Problem& p, const BwdScanBuffers& w, hipStream_t s) {
+  const size_t heads = (size_t)p.B * p.H, DD = (size_t)D * D;
+  const int T = p.T;
+  auto fill = [&](void* ptr, size_t bytes) {
+    const size_t n16 = bytes / 16;
+    const unsigned grid = (unsigned)std::min<size_t>((n16 + 255) / 256, 4096);
+    if (grid) hipLaunchKernelGGL(fill_zero, dim3(grid), dim3(256), 0, s, static_cast<uint4*>(ptr), n16);
+    return hipGetLastError();
+  };
+  hipError_t e;
+  if ((e = fill(w.states_f, heads * (T + 2) * DD * 4)) != hipSuccess) return e;
+  if ((e = fill(w.states_r, heads * (T + 2) * DD * 4)) != hipSuccess) return e;
+  if ((e = fill(w.lam_f, heads * (T + 1) * DD * 4)) != hipSuccess) return e;
+  if ((e = fill(w.lam_r, heads * (T + 1) * DD * 4)) != hipSuccess) return e;
+  if ((e = fill(w.dA, heads * (T + 1) * DD * 4)) != hipSuccess) return e;
+  if ((e = fill(w.dB, heads * (T + 1) * DD * 4)) != hipSuccess) return e;
+  if ((e = fill(w.dalpha, (size_t)p.B * T * p.H * D * 4)) != hipSuccess) return e;
+  // record adjoints and the queries' part of dS_T
+  hipLaunchKernelGGL(backward_gather<D>, dim3((unsigned)(heads * ((DD / 4 + 255) / 256))), dim3(256), 0, s,
+                     w.dsq, w.dF, w.dR, w.dST, T, p.C, p.nc);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // every frame's state, then the adjoint scans
+  if ((e = launch_scan_states(p, w.stats, w.pinv, w.alpha, w.states_f, w.states_r, s)) != hipSuccess) return e;
+  if ((e = launch_scan_adjoint(p, w.stats, w.pinv, w.alpha, w.dF, w.dR, w.lam_f, w.lam_r, w.lam_final, s)) !=
+      hipSuccess)
+    return e;
+  hipLaunchKernelGGL(text_adjoint, dim3(8, (unsigned)heads), dim3(256), 0, s, w.dST, w.lam_final, w.lam_f, T,
+                     (int)DD);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // P as float32
+  const float* P = w.pinv;
+  if (pinv_split(p)) {
+    if constexpr (D >= 32) {
+      hipLaunchKernelGGL(decode_pinv<D>, dim3((unsigned)(heads * (T + 1))), dim3(256), 0, s,
+                         reinterpret_cast<const uint4*>(w.pinv), w.p32);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      P = w.p32;
+    }
+  }
+  // the per-frame products over frames 1..T-2 and the text slot T
+  const unsigned grid = (unsigned)(heads * ((T > 2 ? T - 2 : 0) + 1));  // frames 1..T-2 and the text slot
+  const size_t hs1 = (T + 1) * DD, hs2 = (T + 2) * DD;
+  const MatArg Sf{w.states_f, hs2, DD, -1}, Sr{w.states_r, hs2, DD, 1}, Lf{w.lam_f, hs1, DD, 0},
+      Lr{w.lam_r, hs1, DD, 0}, Bs{w.stats + DD, (T + 1) * 2 * DD, 2 * DD, 0}, Pm{P, hs1, DD, 0},
+      DP{w.dPinv, hs1, DD, 0}, Tm{w.tmp, hs1, DD, 0};
+  auto gemm = [&](auto ta, auto tb, const MatArg& A, const MatArg& B, float* C, float alpha, float beta) {
+    hipLaunchKernelGGL((gemm_dd<D, decltype(ta)::value, decltype(tb)::value>), dim3(grid), dim3(256), 0, s, A, B,
+                       C, hs1, DD, alpha, beta, T);
+    return hipGetLastError();
+  };
+  using Tr = std::true_type;
+  using Nt = std::false_type;
+  if ((e = gemm(Tr(), Nt(), Sf, Lf, w.M, 1.f, 0.f)) != hipSuccess) return e;   // M = Sf^T lam_f
+  if ((e = gemm(Tr(), Nt(), Sr, Lr, w.M, 1.f, 1.f)) != hipSuccess) return e;   //   + Sr^T lam_r
+  if ((e = gemm(Tr(), Nt(), Bs, Lf, w.N, 1.f, 0.f)) != hipSuccess) return e;   // N = B^T lam_f
+  if ((e = gemm(Tr(), Nt(), Bs, Lr, w.N, 1.f, 1.f)) != hipSuccess) return e;   //   + B^T lam_r
+  if ((e = gemm(Nt(), Nt(), Lf, Pm, w.dB, 1.f, 0.f)) != hipSuccess) return e;  // dB = lam_f P
+  if ((e = gemm(Nt(), Nt(), Lr, Pm, w.dB, 1.f, 1.f)) != hipSuccess) return e;  //    + lam_r P
+  hipLaunchKernelGGL(combine_dpinv<D>, dim3(grid), dim3(D), 0, s, w.M, w.N, P, w.alpha, w.dPinv, w.dalpha, T,
+                     p.H);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = gemm(Nt(), Nt(), DP, Pm, w.tmp, 1.f, 0.f)) != hipSuccess) return e;   // dPinv P
+  return gemm(Nt(), Nt(), Pm, Tm, w.dA, -1.f, 0.f);                              // dA = -P dPinv P
+}
+
+}  // namespace
+
+hipError_t launch_backward_scan(const Problem& p, const BwdScanBuffers& w, hipStream_t s) {
+  if (p.T < 1) return hipErrorInvalidValue;
+  switch (p.D) {
+    case 16: return backward_scan_d<16>(p, w, s);
+    case 32: return backward_scan_d<32>(p, w, s);
+    case 64: return backward_scan_d<64>(p, w, s);
+    case 128: return backward_scan_d<128>(p, w, s);
     default: return hipErrorInvalidValue;
   }
 }

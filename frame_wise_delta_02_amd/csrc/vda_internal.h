@@ -129,6 +129,15 @@ hipError_t launch_solve(const Problem& p, const float* stats, float* pinv, hipSt
 // over chunks.
 hipError_t launch_scan(const Problem& p, const float* stats, const float* pinv, const float* alpha,
                        float* s_text, float* fwd, float* rev, float* chunk_m, float* chunk_j, hipStream_t s);
+// Backward pass: the frame scan recording every frame's state (states_f,
+// states_r: [B, H, T+2, d, d], start state S_T/2 in slot 0 / T-1), and the
+// adjoint scan (d_fwd, d_rev: record adjoints [B, H, n_c, d, d]; lam_f, lam_r:
+// adjoint at every frame [B, H, T+1, d, d]; lam_final [B, H, 2, d, d]).
+hipError_t launch_scan_states(const Problem& p, const float* stats, const float* pinv, const float* alpha,
+                              float* states_f, float* states_r, hipStream_t s);
+hipError_t launch_scan_adjoint(const Problem& p, const float* stats, const float* pinv, const float* alpha,
+                               const float* d_fwd, const float* d_rev, float* lam_f, float* lam_r,
+                               float* lam_final, hipStream_t s);
 hipError_t launch_gather(const Problem& p, const float* s_text, const float* fwd, const float* rev,
                          const float* alpha, void* rstates, hipStream_t s);
 hipError_t launch_readout(const Problem& p, const void* q, const void* gate, const float* rms_weight,
@@ -141,6 +150,23 @@ hipError_t launch_backward_readout(const Problem& p, const void* q, const void* 
                                    const void* dy, const void* rstates, const float* s_text, const float* fwd,
                                    const float* rev, const float* alpha, void* rstates_t, void* dout, void* dq,
                                    void* dgate, float* dsq, hipStream_t s);
+// Second stage of the backward pass: buffers (float32 unless noted).
+struct BwdScanBuffers {
+  const float* stats;   // forward workspace: [B, H, T+1, 2d, d]
+  const float* pinv;    // forward workspace (the two-plane format when split)
+  const float* alpha;   // [B, T, H, d]
+  const float* dsq;     // first stage: [B, H, T, d, d]
+  float *dF, *dR;       // [B, H, n_c, d, d]
+  float* dST;           // [B, H, d, d]
+  float *states_f, *states_r;  // [B, H, T+2, d, d]
+  float *lam_f, *lam_r;        // [B, H, T+1, d, d]
+  float* lam_final;            // [B, H, 2, d, d]
+  float* p32;                  // [B, H, T+1, d, d]
+  float *M, *N, *dPinv, *tmp;  // [B, H, T+1, d, d]
+  float *dA, *dB;              // [B, H, T+1, d, d] (out)
+  float* dalpha;               // [B, T, H, d] (out)
+};
+hipError_t launch_backward_scan(const Problem& p, const BwdScanBuffers& w, hipStream_t s);
 hipError_t launch_prep(const Problem& p, int grid_h, int grid_w, const void* q, const void* k,
                        const void* v, const float* wk_s, const float* wk_t, const float* wv_s,
                        const float* wv_t, void* q_hat, void* k_hat, void* v_hat, hipStream_t s);

@@ -69,7 +69,19 @@ struct PFrag<D, true> {   // [e][ks]: fragment (2*wave + e, ks) of the hi and lo
 //                chunk (n_c - 2 serial steps instead of one per frame).
 // Composing the frame updates of a chunk is exact in exact arithmetic, so the
 // two routes give the same F_j and R_j up to rounding.
-enum { SCAN_FRAMES = 0, SCAN_COMPOSE = 1, SCAN_CHUNKS = 2 };
+// Two more serve the backward pass (the derivative of the scan):
+//   SCAN_STATES  the frame scan recording the state after every frame s into
+//                slot s of fwd / rev ([B, H, T+2, d, d] each), the start state
+//                S_T / 2 in slot 0 (forward) and slot T-1 (reverse);
+//   SCAN_ADJOINT the adjoint recurrence, each direction in the reverse of its
+//                own order: lambda <- (lambda + dRec_j) P_s Diag(alpha_s), the
+//                record adjoints dF_j, dR_j (read from fwd / rev, [B, H, n_c, d, d])
+//                added at the frames whose state they record; the adjoint at
+//                frame s (after that addition, before the product) recorded in
+//                slot s of chunk_m (forward) / chunk_j (reverse) ([B, H, T+1, d, d]),
+//                the final adjoint (that of the start state) into s_text
+//                ([B, H, 2, d, d]).
+enum { SCAN_FRAMES = 0, SCAN_COMPOSE = 1, SCAN_CHUNKS = 2, SCAN_STATES = 3, SCAN_ADJOINT = 4 };
 
 template <int D, bool SPLIT, int MODE>
 __global__ __launch_bounds__(64 * (D / (D >= 32 ? 32 : 16)))
@@ -79,6 +91,7 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
                int T, int C, int nc) {
   static_assert(!SPLIT || D >= 32, "the bfloat16 split needs k-steps of 32");
   constexpr bool COMPOSE = MODE == SCAN_COMPOSE, CHUNKS = MODE == SCAN_CHUNKS;
+  constexpr bool STATES = MODE == SCAN_STATES, ADJ = MODE == SCAN_ADJOINT;
   constexpr int MT = scan_mtiles<SPLIT>();
   constexpr int RB = 16 * MT;            // state rows per workgroup
   constexpr int NV = D >= 32 ? 2 : 1;    // adjacent columns per lane
@@ -131,8 +144,9 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   // chunk pairs of this (batch, head, direction): slot j of [n_c][d][d] each
   const size_t cslot = (head * 2 + dir) * (size_t)nc * (D * D);
   const float* CM = CHUNKS ? chunk_m + cslot : P0;
-  const float* CJ = CHUNKS ? chunk_j + cslot : S0;
-  constexpr size_t BSTRIDE = CHUNKS ? (size_t)D * D : (size_t)2 * D * D;  // slot stride of CJ
+  // the per-step "B rows": B_s, J_c (SCAN_CHUNKS) or the record adjoints (SCAN_ADJOINT)
+  const float* CJ = CHUNKS ? chunk_j + cslot : ADJ ? (dir == 0 ? fwd : rev) + head * (size_t)nc * (D * D) : S0;
+  constexpr size_t BSTRIDE = (CHUNKS || ADJ) ? (size_t)D * D : (size_t)2 * D * D;  // slot stride of CJ
 
   const int c0 = wave * WCOLS + NV * (lane & 15);
   const int rr = 4 * (lane >> 4);  // first of this lane's 4 rows in each m-tile
@@ -293,6 +307,14 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
     step = dir == 0 ? 1 : -1;
     last = first + step * (nch - 1);
     nsteps = nch;
+  } else if constexpr (ADJ) {
+    // the forward scan's frames 1 .. e backwards, the reverse scan's b .. T-2 forwards
+    const int e = nc >= 3 ? min(C * (nc - 2) - 1, T - 2) : 0;
+    const int bl = nc >= 3 ? max(2 * C, 1) : T - 1;
+    first = dir == 0 ? e : bl;
+    last = dir == 0 ? 1 : T - 2;
+    step = dir == 0 ? -1 : 1;
+    nsteps = dir == 0 ? max(0, e) : max(0, T - 2 - bl + 1);
   } else {
     if (dir == 0) {
       first = 1;
@@ -306,8 +328,12 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
     nsteps = (dir == 0) ? max(0, last - first + 1) : max(0, first - last + 1);
   }
   (void)last;
-  float* out0 = (dir == 0 ? fwd : rev) + head * (size_t)nc * D * D;
-  const auto rec = make_rsrc(out0, (uint32_t)nc * D * D * 4);  // this head's nc records
+  // this head's records: n_c chunk states; SCAN_STATES T+2 frame states;
+  // SCAN_ADJOINT T+1 frame adjoints
+  constexpr int NREC_EXTRA = STATES ? 2 : 1;
+  const int nrec = (STATES || ADJ) ? T + NREC_EXTRA : nc;
+  float* out0 = (ADJ ? (dir == 0 ? chunk_m : chunk_j) : (dir == 0 ? fwd : rev)) + head * (size_t)nrec * D * D;
+  const auto rec = make_rsrc(out0, (uint32_t)nrec * D * D * 4);
 
   vec_t zero4[MT][4];
 #pragma unroll
@@ -315,7 +341,17 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
 #pragma unroll
     for (int r = 0; r < 4; ++r) zero4[mt][r] = vec_t(0.f);
 
-  if constexpr (COMPOSE) {
+  if constexpr (ADJ) {
+    // ---- start: lambda = 0; the first frame's loads (with no frame, the text
+    // slot and frame 0's alpha: in bounds, never used) -------------------------
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[mt][r] = vec_t(0.f);
+    ld_bw(CJ, BSTRIDE, nsteps > 0 ? min(first / C, nc - 1) : 0, bwA);
+    alA = ld_al(nsteps > 0 ? first : 0);
+    ld_p(P0, nsteps > 0 ? first : T, pfA);
+  } else if constexpr (COMPOSE) {
     // ---- start: rows row0.. of I (M_c) or of 0 (J_c); first frame's loads --
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -350,11 +386,12 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
     }
     lds_barrier();
     mul(0, pfB, P0, -1, pfA);
-    if (dir == 0) put_state(s_text + head * (size_t)(D * D));
+    if (dir == 0 && !STATES) put_state(s_text + head * (size_t)(D * D));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) st[mt][r] *= 0.5f;
+    if constexpr (STATES) put_state(out0 + (size_t)(dir == 0 ? 0 : T - 1) * (D * D));
   }
 
   // the record index after absorbing frame s (or -1)
@@ -388,15 +425,38 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   auto frame = [&](int i, int s, int buf, const PFrag<D, SPLIT>& pc, const vec_t (&bc)[MT][4], vec_t ac,
                    PFrag<D, SPLIT>& pn, vec_t (&bn)[MT][4], vec_t& an) {
     const int sn = i + 1 < nsteps ? s + step : s;
-    if constexpr (CHUNKS)
+    if constexpr (ADJ) {
+      // lambda at frame s: the propagated adjoint plus the record adjoint of
+      // the state frame s produces, if any; recorded, then Y = lambda
+      const float inj = rec_after(s) >= 0 ? 1.f : 0.f;
+      vec_t lam[MT][4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lam[mt][r] = st[mt][r] + bc[mt][r] * inj;
+      const uint32_t jo = (uint32_t)s * (uint32_t)(D * D * 4);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t o = jo + (uint32_t)(((row0 + 16 * mt + rr + r) * D + c0) * 4);
+          if constexpr (NV == 2)
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, lam[mt][r]),
+                                                  rec, o, 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, lam[mt][r][0]), rec, o, 0, 0);
+        }
+      put_y(buf, lam, vec_t(1.f), zero4);
+    } else if constexpr (CHUNKS) {
       put_y(buf, st, vec_t(1.f), zero4);
-    else
+    } else {
       put_y(buf, st, ac, bc);
-    ld_bw(CJ, BSTRIDE, sn, bn);  // needed first (next step's Y), so issued first
+    }
+    ld_bw(CJ, BSTRIDE, ADJ ? min(sn / C, nc - 1) : sn, bn);  // needed first (next step's Y), so issued first
     if constexpr (CHUNKS)
       an = vec_t(1.f);
     else
-      an = ld_al(sn);
+      an = ld_al(sn);  // SCAN_ADJOINT: applied after the product
     if constexpr (!SPLIT) ld_p(CM, sn, pn);  // the split path loads P inside the product
     // keep the loads here, ahead of the product (the compiler would otherwise
     // sink them below it, next to their first use)
@@ -409,13 +469,19 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
 #pragma unroll
         for (int r = 0; r < 4; ++r) st[mt][r] += bc[mt][r];
     }
-    if constexpr (!COMPOSE) {
+    if constexpr (ADJ) {  // lambda <- (lambda P_s) Diag(alpha_s)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[mt][r] *= ac;
+    }
+    if constexpr (!COMPOSE && !ADJ) {
       // record without a branch: the store is always issued and lands past the
       // buffer's end (dropped by the buffer unit) unless frame s ends a record,
       // so every step issues the same memory operations and the load waits need
       // not allow for a store that may or may not be in flight.  SCAN_CHUNKS
       // records after every step.
-      const int j = CHUNKS ? s : rec_after(s);
+      const int j = (CHUNKS || STATES) ? s : rec_after(s);
       const uint32_t jo = j >= 0 ? (uint32_t)j * (uint32_t)(D * D * 4) : 0x80000000u;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -438,6 +504,8 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
     if (i + 1 >= nsteps) break;
     frame(i + 1, s + step, 0, pfB, bwB, alB, pfA, bwA, alA);
   }
+
+  if constexpr (ADJ) put_state(s_text + (head * 2 + dir) * (size_t)(D * D));  // the start state's adjoint
 
   if constexpr (COMPOSE) {
     // ---- the chunk's pair: J_c rows as fp32 [d][d]; M_c rows in the layout
@@ -613,6 +681,25 @@ hipError_t launch_scan_t(const Problem& p, const float* stats, const float* pinv
   return hipGetLastError();
 }
 
+template <int D, int MODE>
+hipError_t launch_scan_mode(const Problem& p, const float* stats, const float* pinv, const float* alpha,
+                            float* s_text, float* fwd, float* rev, float* chunk_m, float* chunk_j, hipStream_t s) {
+  constexpr int NV = D >= 32 ? 2 : 1;
+  constexpr int threads = 64 * (D / (16 * NV));
+  const auto go = [&](auto split) {
+    constexpr bool SPLIT = decltype(split)::value;
+    constexpr int NRB = D / (16 * scan_mtiles<SPLIT>());
+    const unsigned grid = (unsigned)((p.B * p.H * 2 + 7) / 8 * 8 * NRB);
+    hipLaunchKernelGGL((scan_rows<D, SPLIT, MODE>), dim3(grid), dim3(threads), 0, s, stats, pinv, alpha, s_text,
+                       fwd, rev, chunk_m, chunk_j, p.B, p.H, p.T, p.C, p.nc);
+    return hipGetLastError();
+  };
+  if constexpr (D >= 32) {
+    if (pinv_split(p)) return go(std::true_type());
+  }
+  return go(std::false_type());
+}
+
 template <int D>
 hipError_t launch_scan_d(const Problem& p, const float* stats, const float* pinv, const float* alpha,
                          float* s_text, float* fwd, float* rev, float* chunk_m, float* chunk_j, hipStream_t s) {
@@ -642,6 +729,31 @@ size_t readout_slot_bytes(const Problem& p) {
   const int MT = DP / 32;
   if (p.bf16) return (size_t)2 * MT * (p.D / 16) * 64 * 16;
   return (size_t)MT * (p.D / 8) * 64 * 16;
+}
+
+hipError_t launch_scan_states(const Problem& p, const float* stats, const float* pinv, const float* alpha,
+                              float* states_f, float* states_r, hipStream_t s) {
+  switch (p.D) {
+    case 16: return launch_scan_mode<16, SCAN_STATES>(p, stats, pinv, alpha, nullptr, states_f, states_r, nullptr, nullptr, s);
+    case 32: return launch_scan_mode<32, SCAN_STATES>(p, stats, pinv, alpha, nullptr, states_f, states_r, nullptr, nullptr, s);
+    case 64: return launch_scan_mode<64, SCAN_STATES>(p, stats, pinv, alpha, nullptr, states_f, states_r, nullptr, nullptr, s);
+    case 128: return launch_scan_mode<128, SCAN_STATES>(p, stats, pinv, alpha, nullptr, states_f, states_r, nullptr, nullptr, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_scan_adjoint(const Problem& p, const float* stats, const float* pinv, const float* alpha,
+                               const float* d_fwd, const float* d_rev, float* lam_f, float* lam_r,
+                               float* lam_final, hipStream_t s) {
+  float* df = const_cast<float*>(d_fwd);  // read only in this mode
+  float* dr = const_cast<float*>(d_rev);
+  switch (p.D) {
+    case 16: return launch_scan_mode<16, SCAN_ADJOINT>(p, stats, pinv, alpha, lam_final, df, dr, lam_f, lam_r, s);
+    case 32: return launch_scan_mode<32, SCAN_ADJOINT>(p, stats, pinv, alpha, lam_final, df, dr, lam_f, lam_r, s);
+    case 64: return launch_scan_mode<64, SCAN_ADJOINT>(p, stats, pinv, alpha, lam_final, df, dr, lam_f, lam_r, s);
+    case 128: return launch_scan_mode<128, SCAN_ADJOINT>(p, stats, pinv, alpha, lam_final, df, dr, lam_f, lam_r, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_scan(const Problem& p, const float* stats, const float* pinv, const float* alpha,

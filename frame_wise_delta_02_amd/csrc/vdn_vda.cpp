@@ -118,18 +118,38 @@ Layout make_layout(const Problem& p) {
 
 // Workspace of the backward pass's first stage.
 struct BwdLayout {
-  size_t rstates_t, dout, dsq, total;
+  size_t rstates_t, dout, dsq;                                    // first stage
+  size_t dF, dR, dST, lam_f, lam_r, dA, dB;                       // second stage (documented)
+  size_t states_f, states_r, lam_final, p32, M, N, dPinv, tmp;    // second stage (internal)
+  size_t total;
 };
 BwdLayout make_bwd_layout(const Problem& p) {
   const size_t heads = (size_t)p.B * p.H;
+  const size_t dd = (size_t)p.D * p.D * 4;
   BwdLayout l;
   size_t o = 0;
-  l.rstates_t = o;
-  o = up(o + heads * (p.nc + 1) * readout_slot_bytes(p));
-  l.dout = o;
-  o = up(o + (size_t)p.B * p.T * p.U * p.H * p.D * 2);
-  l.dsq = o;
-  o = up(o + heads * p.T * (size_t)p.D * p.D * 4);
+  auto take = [&](size_t& field, size_t bytes) {
+    field = o;
+    o = up(o + bytes);
+  };
+  take(l.rstates_t, heads * (p.nc + 1) * readout_slot_bytes(p));
+  take(l.dout, (size_t)p.B * p.T * p.U * p.H * p.D * 2);
+  take(l.dsq, heads * p.T * dd);
+  take(l.dF, heads * p.nc * dd);
+  take(l.dR, heads * p.nc * dd);
+  take(l.dST, heads * dd);
+  take(l.lam_f, heads * (p.T + 1) * dd);
+  take(l.lam_r, heads * (p.T + 1) * dd);
+  take(l.dA, heads * (p.T + 1) * dd);
+  take(l.dB, heads * (p.T + 1) * dd);
+  take(l.states_f, heads * (p.T + 2) * dd);
+  take(l.states_r, heads * (p.T + 2) * dd);
+  take(l.lam_final, heads * 2 * dd);
+  take(l.p32, heads * (p.T + 1) * dd);
+  take(l.M, heads * (p.T + 1) * dd);
+  take(l.N, heads * (p.T + 1) * dd);
+  take(l.dPinv, heads * (p.T + 1) * dd);
+  take(l.tmp, heads * (p.T + 1) * dd);
   l.total = o;
   return l;
 }
@@ -255,6 +275,13 @@ vdn_status vdn_vda_backward_workspace_layout(const vdn_vda_desc* d, vdn_vda_back
   out->readout_states_t = l.rstates_t;
   out->d_out = l.dout;
   out->d_state_q = l.dsq;
+  out->d_record_f = l.dF;
+  out->d_record_r = l.dR;
+  out->d_text_q = l.dST;
+  out->lam_f = l.lam_f;
+  out->lam_r = l.lam_r;
+  out->d_a = l.dA;
+  out->d_b = l.dB;
   out->total = l.total;
   return VDN_OK;
 }
@@ -288,6 +315,49 @@ vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d, const void* q, const 
       reinterpret_cast<const float*>(fw + fl.fwd), reinterpret_cast<const float*>(fw + fl.rev), alpha,
       ws + bl.rstates_t, ws + bl.dout, dq, dgate, reinterpret_cast<float*>(ws + bl.dsq), stream);
   return e == hipSuccess ? VDN_OK : VDN_ERR_HIP;
+}
+
+vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha, const void* fwd_workspace,
+                                 size_t fwd_workspace_bytes, float* dalpha, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  const vdn_status st = check(d);
+  if (st != VDN_OK) return st;
+  if (d->dtype != VDN_BF16 || (d->flags & (VDN_VDA_QUERY_L2 | VDN_VDA_DECAY_BRIDGE))) return VDN_ERR_UNSUPPORTED;
+  if (!alpha || !fwd_workspace || !dalpha) return VDN_ERR_INVALID_ARG;
+  // every frame's state is recorded per head through one buffer descriptor
+  if ((double)(d->T + 2) * d->d_k * d->d_v * 4.0 >= 2147483648.0) return VDN_ERR_INVALID_ARG;
+  const Problem p = problem(d);
+  const Layout fl = make_layout(p);
+  const BwdLayout bl = make_bwd_layout(p);
+  if (fwd_workspace_bytes < fl.total) return VDN_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < bl.total) return VDN_ERR_WORKSPACE;
+  if (!aligned(alpha, 16) || !aligned(dalpha, 16)) return VDN_ERR_ALIGNMENT;
+  if (!aligned(workspace, kAlign) || !aligned(fwd_workspace, kAlign)) return VDN_ERR_ALIGNMENT;
+  const char* fw = static_cast<const char*>(fwd_workspace);
+  char* ws = static_cast<char*>(workspace);
+  auto f = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  BwdScanBuffers w;
+  w.stats = reinterpret_cast<const float*>(fw + fl.stats);
+  w.pinv = reinterpret_cast<const float*>(fw + fl.pinv);
+  w.alpha = alpha;
+  w.dsq = f(bl.dsq);
+  w.dF = f(bl.dF);
+  w.dR = f(bl.dR);
+  w.dST = f(bl.dST);
+  w.states_f = f(bl.states_f);
+  w.states_r = f(bl.states_r);
+  w.lam_f = f(bl.lam_f);
+  w.lam_r = f(bl.lam_r);
+  w.lam_final = f(bl.lam_final);
+  w.p32 = f(bl.p32);
+  w.M = f(bl.M);
+  w.N = f(bl.N);
+  w.dPinv = f(bl.dPinv);
+  w.tmp = f(bl.tmp);
+  w.dA = f(bl.dA);
+  w.dB = f(bl.dB);
+  w.dalpha = dalpha;
+  return launch_backward_scan(p, w, stream) == hipSuccess ? VDN_OK : VDN_ERR_HIP;
 }
 
 vdn_status vdn_vda_set_profile_events(hipEvent_t* events, int n) {

@@ -243,8 +243,25 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d,
  * VDN_ERR_ALIGNMENT (16 B for tensors, 256 B for workspaces), VDN_ERR_HIP.
  * Asynchronous on `stream`.
  */
+/* Offsets (bytes from the base) of the backward workspace's documented
+ * sections; the workspace also holds internal sections.  The second stage's
+ * (float32):
+ *   d_record_f, d_record_r [B, H, n_c, d_v, d_k]: adjoints of the records F_j, R_j
+ *             (zero where no record is read);
+ *   d_text_q  [B, H, d_v, d_k]: the part of S_T's adjoint that its direct
+ *             readers give (anchor queries, sides reading S_T / 2, records the
+ *             scan never reaches);
+ *   lam_f, lam_r [B, H, T+1, d_v, d_k]: slot s holds the adjoint of the state
+ *             each scan has after absorbing frame s, for the frames it absorbs,
+ *             zero elsewhere; slot T of lam_f is the adjoint of S_T as a whole;
+ *   d_a, d_b  [B, H, T+1, d_k, d_k] and [B, H, T+1, d_v, d_k]: dA_t, dB_t for the
+ *             absorbed frames and the text frame (slot T), zero for the anchors.
+ *             A_t is symmetric, so only dA_t + dA_t^T reaches an input; d_a
+ *             holds -P_t d(P_t) P_t with d(P_t) = sum over the scans of Y^T lambda. */
 typedef struct {
-  size_t readout_states_t, d_out, d_state_q, total;
+  size_t readout_states_t, d_out, d_state_q;
+  size_t d_record_f, d_record_r, d_text_q, lam_f, lam_r, d_a, d_b;
+  size_t total;
 } vdn_vda_backward_layout;
 
 /* Workspace bytes vdn_vda_backward_readout needs for `d`; 0 if `d` is invalid. */
@@ -261,6 +278,28 @@ vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d,
                                     void* dq, void* dgate,
                                     void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
+
+/*
+ * Backward pass, second stage: back through the coverage rules, the two scans
+ * and (I + A_t)^{-1}.  Reads the first stage's d_state_q from `workspace` and
+ * the forward's workspace; writes d_record_f / d_record_r / d_text_q, lam_f /
+ * lam_r and d_a / d_b into `workspace` (see vdn_vda_backward_layout) and
+ *   dalpha [B, T, H, d_k] float32: the gradient of alpha (zero for the anchors).
+ * Per absorbed frame s of a scan with adjoint lambda (the state's, after the
+ * record adjoint of the state frame s produces is added): dY = lambda P_s,
+ * dB_s += dY, dalpha_s += column sums of S_prev * dY, d(P_s) += Y_s^T lambda with
+ * Y_s = S_prev Diag(alpha_s) + B_s, and lambda <- dY Diag(alpha_s) for the state
+ * before; then dA_s = -P_s d(P_s) P_s (P_s = (I + A_s)^{-1}, [VDN-summary]
+ * "어떻게 쓰나").  The text frame S_T = B_T P_T takes lambda = the adjoint of
+ * S_T.  Supported: VDN_BF16 without VDN_VDA_QUERY_L2 or VDN_VDA_DECAY_BRIDGE
+ * (else VDN_ERR_UNSUPPORTED); (T + 2) d_k d_v 4 < 2^31.  Errors as
+ * vdn_vda_backward_readout.  Asynchronous on `stream`.
+ */
+vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha,
+                                 const void* fwd_workspace, size_t fwd_workspace_bytes,
+                                 float* dalpha,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /* Profiling hook for benchmarks.  While set, vdn_vda_forward records events[0]
  * on its stream before its first kernel and events[i] after stage i, for

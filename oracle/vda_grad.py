@@ -61,10 +61,12 @@ def forward_head_t(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, gate=None, gamm
     # text state (R4): the frame update from a zero state over the text tokens
     if k_txt.shape[0] == 0:
         S_T = torch.zeros((dv, dk), dtype=torch.float64)
+        A_T = B_T = None
     else:
-        A_T = k_txt.T @ (beta_txt[:, None] * k_txt)
-        B_T = v_txt.T @ (beta_txt[:, None] * k_txt)
+        A_T = _keep(k_txt.T @ (beta_txt[:, None] * k_txt))
+        B_T = _keep(v_txt.T @ (beta_txt[:, None] * k_txt))
         S_T = torch.linalg.solve(eye + A_T, B_T.T).T
+    keep["A_T"], keep["B_T"] = A_T, B_T
     S_T = _keep(S_T)
     keep["S_T"] = S_T
 
@@ -89,10 +91,11 @@ def forward_head_t(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, gate=None, gamm
     half = S_T / 2.0
     fwd = [half]
     for s in range(1, T - 1):
-        fwd.append(fwd[-1] @ M[s] + J[s])
+        fwd.append(_keep(fwd[-1] @ M[s] + J[s]))
     rev = {T - 1: half}
     for s in range(T - 2, 0, -1):
-        rev[s] = rev[s + 1] @ M[s] + J[s]
+        rev[s] = _keep(rev[s + 1] @ M[s] + J[s])
+    keep["fwd"], keep["rev"] = fwd, rev
     F, R = [], []
     for j in range(nc):
         last = min(C * (j + 1) - 1, T - 2)
@@ -173,6 +176,16 @@ def backward_head(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, dy, gate=None, g
     res["dS_T"] = grad_of(keep["S_T"], keep["S_T"].shape)
     for name in ("S_q", "F", "R", "A", "B", "Pinv"):
         res["d" + name] = np.stack([grad_of(x, x.shape) for x in keep[name]])
+    # adjoints of the scan states after each absorbed frame (zero elsewhere)
+    # and of the text statistics
+    T, dv, dk = len(keep["A"]), keep["S_T"].shape[0], keep["S_T"].shape[1]
+    res["dfwd"] = np.zeros((T, dv, dk))
+    res["drev"] = np.zeros((T, dv, dk))
+    for s in range(1, T - 1):
+        res["dfwd"][s] = grad_of(keep["fwd"][s], (dv, dk))
+        res["drev"][s] = grad_of(keep["rev"][s], (dv, dk))
+    res["dA_T"] = np.zeros((dk, dk)) if keep["A_T"] is None else grad_of(keep["A_T"], (dk, dk))
+    res["dB_T"] = np.zeros((dv, dk)) if keep["B_T"] is None else grad_of(keep["B_T"], (dv, dk))
     return res
 
 
@@ -211,7 +224,7 @@ def backward(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, dy, gate=None, rms_we
                 out["dgate"][b, :, :, h] = r["dgate"]
             if rms_weight is not None:
                 out["dgamma"] += r["dgamma"]
-            for name in ("do", "dS_q", "dF", "dR", "dS_T", "dA", "dB", "dPinv"):
+            for name in ("do", "dS_q", "dF", "dR", "dS_T", "dA", "dB", "dPinv", "dfwd", "drev", "dA_T", "dB_T"):
                 inter.setdefault(name, np.zeros((Bn, H) + r[name].shape))[b, h] = r[name]
     out.update(inter)
     return out

@@ -39,8 +39,9 @@ def _dy(w):
     return synth.f64_to_bf16_bits(rng.standard_normal((w.B, w.T, w.U, w.H, w.d)))
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_backward_readout(name):
+def _run(name, stage2=False):
+    """Forward, then the backward stages, on the case's seeded inputs; returns
+    the GPU results, the oracle's gradients and the case's description."""
     import torch
     from frame_wise_delta_02_amd import binding as bd
     case = CASES[name]
@@ -56,18 +57,34 @@ def test_backward_readout(name):
                                          grid=(w.grid_h, w.grid_w), n_text=w.L, chunk=w.chunk, epilogue=epi,
                                          bridge=bridge)
     torch.cuda.synchronize()
-    L = bd.backward_layout(bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L, w.chunk, w.dtype, epi))
-    n_do = w.B * w.T * w.U * w.H * w.d
-    do = bws[L.d_out:L.d_out + 2 * n_do].view(torch.int16).view(torch.bfloat16).reshape(
-        w.B, w.T, w.U, w.H, w.d).to(torch.float64).cpu().numpy()
-    n_s = w.B * w.H * w.T * w.d * w.d
-    dsq = bws[L.d_state_q:L.d_state_q + 4 * n_s].view(torch.float32).reshape(
-        w.B, w.H, w.T, w.d, w.d).to(torch.float64).cpu().numpy()
-
+    gpu = {"dq": dq, "dgate": dgate, "bws": bws}
+    if stage2:
+        G.say(f"backward_scan {name}")
+        gpu["dalpha"] = bd.backward_scan(dev["alpha"], ws, bws, shape=(w.B, w.T, w.H, w.d),
+                                         grid=(w.grid_h, w.grid_w), n_text=w.L, chunk=w.chunk, epilogue=epi)
+        torch.cuda.synchronize()
     f = G.oracle_view({k: x[k] for k in ("q", "k", "v", "beta", "k_text", "v_text", "beta_text", "gate")}, w)
     ref = vda_grad.backward(f["q"], f["k"], f["v"], x["alpha"].astype(np.float64), f["beta"], f["k_text"],
                             f["v_text"], f["beta_text"], G.oracle_view({"dy": dy}, w)["dy"],
                             gate=f["gate"] if epi else None, rms_weight=rw, chunk=w.chunk, bridge=bridge)
+    L = bd.backward_layout(bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L, w.chunk, w.dtype, epi))
+    return gpu, ref, L, w, epi, dy
+
+
+def _section(bws, off, shape, dtype="f32"):
+    import torch
+    n = int(np.prod(shape))
+    if dtype == "bf16":
+        return bws[off:off + 2 * n].view(torch.int16).view(torch.bfloat16).reshape(shape).to(torch.float64).cpu().numpy()
+    return bws[off:off + 4 * n].view(torch.float32).reshape(shape).to(torch.float64).cpu().numpy()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_readout(name):
+    gpu, ref, L, w, epi, dy = _run(name)
+    dq, dgate, bws = gpu["dq"], gpu["dgate"], gpu["bws"]
+    do = _section(bws, L.d_out, (w.B, w.T, w.U, w.H, w.d), "bf16")
+    dsq = _section(bws, L.d_state_q, (w.B, w.H, w.T, w.d, w.d))
     tol = G.TOL[w.dtype]
     # without the epilogue do is dy itself (the workspace copy is not written)
     errs = {"dq": G.slice_rel_err(G.to_host_f64(dq), ref["dq"]),
@@ -78,3 +95,63 @@ def test_backward_readout(name):
     G.say(f"{name}: " + " ".join(f"err({k})={v:.3e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert v <= tol, (k, v)
+
+
+def _rel(got, ref):
+    """max over leading axes of ||got - ref||_inf / ||ref||_inf of each trailing matrix
+    (or vector); slices where the reference is zero must be zero too."""
+    if got.size == 0:
+        return 0.0
+    axes = tuple(range(got.ndim - (2 if got.ndim >= 2 else 1), got.ndim))
+    diff = np.abs(got - ref).max(axis=axes)
+    scale = np.abs(ref).max(axis=axes)
+    return float(np.max(np.where(scale > 0, diff / np.maximum(scale, 1e-300), diff)))
+
+
+@pytest.mark.parametrize("name", [n for n in CASES if not CASES[n].get("bridge")])
+def test_backward_scan(name):
+    """Second stage: record adjoints, the scans' adjoints, dA, dB (frames and
+    text) and dalpha against the oracle."""
+    gpu, ref, L, w, epi, dy = _run(name, stage2=True)
+    B, H, T, d = w.B, w.H, w.T, w.d
+    nc = -(-T // w.chunk)
+    bws = gpu["bws"]
+    dF = _section(bws, L.d_record_f, (B, H, nc, d, d))
+    dR = _section(bws, L.d_record_r, (B, H, nc, d, d))
+    lam_f = _section(bws, L.lam_f, (B, H, T + 1, d, d))
+    lam_r = _section(bws, L.lam_r, (B, H, T + 1, d, d))
+    dA = _section(bws, L.d_a, (B, H, T + 1, d, d))
+    dB = _section(bws, L.d_b, (B, H, T + 1, d, d))
+    dalpha = gpu["dalpha"].to(dtype=__import__("torch").float64).cpu().numpy()
+    fr = slice(1, max(T - 1, 1))
+    sym = lambda a: a + np.swapaxes(a, -1, -2)
+    errs = {
+        "dF": _rel(dF[:, :, : max(nc - 2, 0)], ref["dF"][:, :, : max(nc - 2, 0)]),
+        "dR": _rel(dR[:, :, 2:], ref["dR"][:, :, 2:]),
+        "lam_f": _rel(lam_f[:, :, fr], ref["dfwd"][:, :, fr]),
+        "lam_r": _rel(lam_r[:, :, fr], ref["drev"][:, :, fr]),
+        "dS_T": _rel(lam_f[:, :, T], ref["dS_T"]),
+        # A_t is symmetric, so only dA + dA^T reaches an input: compare that
+        # (the oracle's text frame, S_T = solve(P, B^T)^T, gives the transpose)
+        "dA": _rel(sym(dA[:, :, fr]), sym(ref["dA"][:, :, fr])),
+        "dB": _rel(dB[:, :, fr], ref["dB"][:, :, fr]),
+        # (the text frame exists only with text tokens)
+        "dA_T": _rel(sym(dA[:, :, T]), sym(ref["dA_T"])) if w.L else 0.0,
+        "dB_T": _rel(dB[:, :, T], ref["dB_T"]) if w.L else 0.0,
+        "dalpha": _rel(dalpha[:, fr], ref["dalpha"][:, fr]),
+    }
+    # the anchors take no part in any scan
+    assert np.abs(dA[:, :, [0, T - 1]]).max() == 0 and np.abs(dB[:, :, [0, T - 1]]).max() == 0
+    assert np.abs(dalpha[:, [0, T - 1]]).max() == 0
+    G.say(f"{name}: " + " ".join(f"err({k})={v:.3e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= G.TOL[w.dtype], (k, v)
+
+
+def test_backward_scan_rejects_the_bridge():
+    from frame_wise_delta_02_amd import binding as bd
+    w = CASES["bwd_32_bridge"]["w"]
+    desc = bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L, w.chunk, w.dtype, True,
+                        flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_DECAY_BRIDGE)
+    st = bd.lib().vdn_vda_backward_scan(__import__("ctypes").byref(desc), None, None, 0, None, None, 0, None)
+    assert st == bd.VDN_ERR_UNSUPPORTED

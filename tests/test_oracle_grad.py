@@ -149,3 +149,31 @@ def test_g4_intermediate_adjoints(name):
             want_r = sum((g["dS_q"][t] for t in range(T) if t not in anchors and t // C + 2 == j), zero)
             assert np.abs(g["dF"][j] - want_f).max() <= tol
             assert np.abs(g["dR"][j] - want_r).max() <= tol
+
+
+@pytest.mark.parametrize("name", ["T12_C3", "T11_C5_ragged", "T16_C5_bridge", "T7_C2_no_text"])
+def test_g5_scan_adjoint_recurrence(name):
+    """The adjoint of the forward scan state after frame s-1 is that after
+    frame s times P_s Diag(alpha_s), plus the record adjoint where frame s-1
+    ends a chunk (the recurrence the staged backward runs); the reverse scan
+    likewise with the frame order reversed."""
+    x, bridge = _case(name)
+    T, C = x["q"].shape[0], x["chunk"]
+    nc = vda.num_chunks(T, C)
+    g = vg.backward_head(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["k_txt"], x["v_txt"], x["beta_txt"],
+                         x["dy"], x["gate"], x["gamma"], chunk=C, bridge=bridge)
+    f = vda.forward_head(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["k_txt"], x["v_txt"], x["beta_txt"],
+                         chunk=C, bridge=bridge)
+    tol = 1e-10 * max(1.0, np.abs(g["dfwd"]).max(), np.abs(g["drev"]).max())
+    for s in range(2, T - 1):
+        want = (g["dfwd"][s] @ f["Pinv"][s]) * x["alpha"][s][None, :]
+        for j in range(nc):  # F_j is the state after frame min(C(j+1)-1, T-2)
+            if min(C * (j + 1) - 1, T - 2) == s - 1:
+                want = want + g["dF"][j]
+        assert np.abs(g["dfwd"][s - 1] - want).max() <= tol, s
+    for s in range(1, T - 2):
+        want = (g["drev"][s] @ f["Pinv"][s]) * x["alpha"][s][None, :]
+        for j in range(nc):  # R_j is the state after frame max(C j, 1)
+            if max(C * j, 1) == s + 1:
+                want = want + g["dR"][j]
+        assert np.abs(g["drev"][s + 1] - want).max() <= tol, s
