@@ -26,7 +26,8 @@ _SCAN_FLAGS = {None: 0, "frames": VDN_VDA_SCAN_FRAMES, "chunks": VDN_VDA_SCAN_CH
 EXPORTS = ("vdn_vda_validate", "vdn_vda_workspace_bytes", "vdn_vda_workspace_layout",
            "vdn_vda_prepare", "vdn_vda_forward", "vdn_vda_set_profile_events",
            "vdn_vda_status_string", "vdn_vda_backward_workspace_bytes",
-           "vdn_vda_backward_workspace_layout", "vdn_vda_backward_readout", "vdn_vda_backward_scan")
+           "vdn_vda_backward_workspace_layout", "vdn_vda_backward_readout", "vdn_vda_backward_scan",
+           "vdn_vda_backward_gram")
 STAGES = ("gram", "gram_text", "solve", "scan", "gather", "readout")
 
 
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.vdn_vda_backward_readout.restype = ctypes.c_int
         L.vdn_vda_backward_scan.argtypes = [dp, p, p, sz, p, p, sz, p]
         L.vdn_vda_backward_scan.restype = ctypes.c_int
+        L.vdn_vda_backward_gram.argtypes = [dp] + [p] * 13 + [sz, p]
+        L.vdn_vda_backward_gram.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -287,3 +290,49 @@ def backward_scan(alpha, fwd_workspace, workspace, *, shape, grid, n_text=0, chu
     if st != VDN_OK:
         raise VdaError(st, "vdn_vda_backward_scan")
     return dalpha
+
+
+def backward_gram(k, v, beta, k_text, v_text, beta_text, workspace, *, grid, chunk=5, epilogue=True, out=None):
+    """Third stage of the backward pass (vdn_vda_backward_gram) on the second
+    stage's workspace; returns (dk, dv, dbeta, dk_text, dv_text, dbeta_text),
+    the text ones None without text tokens.  ``out`` may give the six output
+    tensors."""
+    import torch
+    B, T, U, H, d = k.shape
+    L = 0 if k_text is None else k_text.shape[1]
+    dev = k.device
+    if out is None:
+        out = (torch.empty_like(k), torch.empty_like(v), torch.empty_like(beta),
+               None if L == 0 else torch.empty_like(k_text), None if L == 0 else torch.empty_like(v_text),
+               None if L == 0 else torch.empty_like(beta_text))
+    for name, x in (("k", k), ("v", v), ("beta", beta), ("k_text", k_text), ("v_text", v_text),
+                    ("beta_text", beta_text), ("workspace", workspace)) + tuple(zip(
+                        ("dk", "dv", "dbeta", "dk_text", "dv_text", "dbeta_text"), out)):
+        _check(x, name, dev)
+    desc = make_desc(B, H, T, grid[0], grid[1], d, L, chunk, _dtype_of(k), epilogue)
+    text = [x if L else None for x in (k_text, v_text, beta_text)]
+    st = lib().vdn_vda_backward_gram(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(beta), *map(_ptr, text),
+                                     *(_ptr(x if (L or i < 3) else None) for i, x in enumerate(out)),
+                                     _ptr(workspace), workspace.numel(), _stream())
+    if st != VDN_OK:
+        raise VdaError(st, "vdn_vda_backward_gram")
+    return tuple(out[:3]) + (tuple(out[3:]) if L else (None, None, None))
+
+
+def backward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, dy, fwd_workspace, *, grid,
+             chunk=5, epilogue=True, rms_eps=1e-6, workspace=None):
+    """The whole backward pass (the three stages in order) after a forward
+    that left ``fwd_workspace``; returns a dict of input gradients dq, dk, dv,
+    dalpha, dbeta, dk_text, dv_text, dbeta_text, dgate (the last four None
+    where absent) and the workspace."""
+    B, T, U, H, d = q.shape
+    L = 0 if k_text is None else k_text.shape[1]
+    dq, dgate, workspace = backward_readout(q, gate, rms_weight, alpha, dy, fwd_workspace, grid=grid, n_text=L,
+                                            chunk=chunk, epilogue=epilogue, rms_eps=rms_eps, workspace=workspace)
+    dalpha = backward_scan(alpha, fwd_workspace, workspace, shape=(B, T, H, d), grid=grid, n_text=L,
+                           chunk=chunk, dtype=_dtype_of(q), epilogue=epilogue)
+    dk, dv, dbeta, dkt, dvt, dbt = backward_gram(k, v, beta, k_text, v_text, beta_text, workspace, grid=grid,
+                                                 chunk=chunk, epilogue=epilogue)
+    return dict(dq=dq, dk=dk, dv=dv, dalpha=dalpha, dbeta=dbeta, dk_text=dkt, dv_text=dvt, dbeta_text=dbt,
+                dgate=dgate, workspace=workspace)
+

@@ -611,4 +611,267 @@ hipError_t launch_backward_scan(const Problem& p, const BwdScanBuffers& w, hipSt
   }
 }
 
+namespace {
+
+// ---------------------------------------------------------------------------
+// third stage: dk, dv, dbeta per token from dA_s, dB_s of its frame
+// ---------------------------------------------------------------------------
+// A_s = sum_u beta_u k_u k_u^T and B_s = sum_u beta_u v_u k_u^T (the frame
+// statistics, section "어떻게 쓰나"), so with G = dA + dA^T
+//   dk_u = beta_u (G k_u + dB^T v_u),   dv_u = beta_u dB k_u,
+//   dbeta_u = k_u^T dA k_u + v_u^T dB k_u = 1/2 k_u . (G k_u) + v_u . (dB k_u).
+// dbeta is a sum of d^2 products that largely cancel, so the two products it
+// uses, G k and dB k, take their matrices as bfloat16 hi + lo planes (about
+// 2^-16 relative operand rounding); dB^T v enters dk only and takes the hi
+// plane alone (2^-9, below the bfloat16 output's own rounding).  The five
+// planes of a slot are the matrix-core A operands, shared through LDS (160 KB
+// at d = 128); the token operands come straight from global memory.
+
+// Planes of a slot, in the readout's operand order (fragment (mt, ks, lane)
+// holds M[dv_of(mt, lane % 32)][(d/2)(lane / 32) + 8 ks + j], j = 0..7).
+enum { GP_G_HI = 0, GP_G_LO, GP_DB_HI, GP_DB_LO, GP_DBT_HI, GP_PLANES };
+
+template <int D>
+__global__ __launch_bounds__(256) void pack_grad_mats(const float* __restrict__ dA, const float* __restrict__ dB,
+                                                      uint4* __restrict__ out) {
+  constexpr int DP = D < 32 ? 32 : D;
+  constexpr int HALF = DP / 2;
+  constexpr int MT = DP / 32;
+  constexpr int KS = D / 16;
+  constexpr int NF = MT * KS * 64;
+  const float* a = dA + (size_t)blockIdx.x * D * D;
+  const float* bm = dB + (size_t)blockIdx.x * D * D;
+  uint4* o = out + (size_t)blockIdx.x * GP_PLANES * NF;
+  auto dv_of = [&](int mt, int m) { return HALF * ((m >> 2) & 1) + 16 * mt + 4 * (m >> 3) + (m & 3); };
+  // one fragment of each matrix per iteration: G (hi, lo), dB (hi, lo), dB^T (hi)
+  for (int f = threadIdx.x; f < 3 * NF; f += 256) {
+    const int which = f / NF, g = f % NF;
+    const int lane = g % 64, ks = (g / 64) % KS, mt = g / (64 * KS);
+    const int row = dv_of(mt, lane & 31);
+    const int c0 = (D / 2) * (lane >> 5) + 8 * ks;
+    const bool live = row < D;
+    const int r = live ? row : 0;
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      __bf16 h2[2], l2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = c0 + 2 * e + h;
+        float v;
+        if (which == 0) v = a[(size_t)r * D + c] + a[(size_t)c * D + r];  // G = dA + dA^T
+        else if (which == 1) v = bm[(size_t)r * D + c];                   // dB
+        else v = bm[(size_t)c * D + r];                                   // dB^T
+        split_bf16(live ? v : 0.f, h2[h], l2[h]);
+      }
+      hi[e] = __builtin_bit_cast(uint32_t, bf16x2{h2[0], h2[1]});
+      lo[e] = __builtin_bit_cast(uint32_t, bf16x2{l2[0], l2[1]});
+    }
+    const uint4 H4 = make_uint4(hi[0], hi[1], hi[2], hi[3]), L4 = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    if (which == 0) {
+      o[GP_G_HI * NF + g] = H4;
+      o[GP_G_LO * NF + g] = L4;
+    } else if (which == 1) {
+      o[GP_DB_HI * NF + g] = H4;
+      o[GP_DB_LO * NF + g] = L4;
+    } else {
+      o[GP_DBT_HI * NF + g] = H4;
+    }
+  }
+}
+
+// One part of a launch: frames t_first .. t_first + n_frames - 1 of k, v,
+// beta laid out [B, T_in, U, H, d] (beta [B, T_in, U, H]) and their gradients,
+// reading the packed planes of slot t + slot_offset.
+struct GradPart {
+  const uint16_t *k, *v, *beta;
+  uint16_t *dk, *dv, *dbeta;
+  int T_in, U, t_first, n_frames, slot_offset;
+};
+
+// One (frame, head) per workgroup; 4 waves stream 32-token tiles, the next
+// tile's operands loading while the current one is multiplied.  Lane
+// (n = lane % 32, half = lane / 32) takes token n's channels
+// (d/2) half .. (d/2) half + d/2 - 1 as the B operand and, with
+// dv0 = HALF * half, holds outputs dv0 + 16 mt + r in acc[mt][r].
+template <int D>
+__global__ __launch_bounds__(256, 1) void gram_bwd_bf16(GradPart part0, GradPart part1, int nblk0,
+                                                        const uint4* __restrict__ mats, int H, int T_slots) {
+  constexpr int NW = 4;
+  constexpr int DP = D < 32 ? 32 : D;
+  constexpr int HALF = DP / 2;
+  constexpr int MT = DP / 32;
+  constexpr int KS = D / 16;
+  constexpr int NF = MT * KS * 64;
+  constexpr int NG = HALF / 8;
+  constexpr int NP = GP_PLANES * NF;
+  constexpr int STAGE = (NP + 64 * NW - 1) / (64 * NW);
+  __shared__ uint4 sm[NP];
+
+  const bool second = (int)blockIdx.x >= nblk0;
+  const GradPart g = second ? part1 : part0;
+  int blk = (int)blockIdx.x - (second ? nblk0 : 0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blk % H;
+  blk /= H;
+  const int fi = blk % g.n_frames;
+  const int b = blk / g.n_frames;
+  const int t = g.t_first + fi;
+  {
+    const uint4* src = mats + ((size_t)(b * H + h) * T_slots + (t + g.slot_offset)) * NP;
+    uint4 tmp[STAGE];
+#pragma unroll
+    for (int i = 0; i < STAGE; ++i) tmp[i] = src[min(tid + 64 * NW * i, NP - 1)];
+#pragma unroll
+    for (int i = 0; i < STAGE; ++i)
+      if (tid + 64 * NW * i < NP) sm[tid + 64 * NW * i] = tmp[i];
+  }
+  __syncthreads();
+
+  const int U = g.U;
+  const size_t tok0 = ((size_t)b * g.T_in + t) * (size_t)U;
+  const size_t fbase = (tok0 * H + h) * (size_t)D;
+  const uint32_t rowbytes = (uint32_t)H * D * 2;
+  const uint32_t nbytes = U > 0 ? (uint32_t)(U - 1) * rowbytes + D * 2 : 0;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(g.k + fbase, nbytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(g.v + fbase, nbytes);
+  const __amdgpu_buffer_rsrc_t dkr = make_rsrc(g.dk + fbase, nbytes);
+  const __amdgpu_buffer_rsrc_t dvr = make_rsrc(g.dv + fbase, nbytes);
+  const uint32_t bbytes = U > 0 ? (uint32_t)(U - 1) * H * 2 + 2 : 0;
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(g.beta + tok0 * H + h, bbytes);
+  const __amdgpu_buffer_rsrc_t dbr = make_rsrc(g.dbeta + tok0 * H + h, bbytes);
+
+  const int n = lane & 31, half = lane >> 5;
+  const int dv0 = HALF * half;
+  const bool owns = dv0 < D;
+  const uint32_t coff = (uint32_t)(D / 2) * half * 2;  // first operand byte of this lane in a row
+  const int ntiles = (U + 31) / 32;
+
+  struct Frag {
+    bf16x8 k[KS], v[KS];
+    uint16_t beta;
+  };
+  auto load = [&](int tile, Frag& f) {
+    const uint32_t ro = (uint32_t)(tile * 32 + n) * rowbytes + coff;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) f.k[ks] = __builtin_bit_cast(bf16x8, buf_load16(kr, ro + 16 * ks));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) f.v[ks] = __builtin_bit_cast(bf16x8, buf_load16(vr, ro + 16 * ks));
+    f.beta = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(br, (uint32_t)(tile * 32 + n) * H * 2, 0, 0);
+  };
+  // acc += plane w x operand, over the k-steps
+  auto chain = [&](f32x16 (&acc)[MT], int w, const bf16x8 (&op)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, sm[w * NF + (mt * KS + ks) * 64 + lane]);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, op[ks], acc[mt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // sum over this lane's outputs j of x_j acc[j] (x = the token operand's
+  // channel dv0 + j): for d >= 32 those channels are the lane's own operand
+  // words; at d = 16 half 0 owns all 16 outputs and takes channels 8..15 from
+  // lane n + 32
+  auto dotacc = [&](const bf16x8 (&op)[KS], const f32x16 (&acc)[MT]) {
+    float s = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 u = __builtin_bit_cast(uint4, op[ks]);
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 8 * ks + 2 * e;
+        s += bf16_lo(w4[e]) * acc[j / 16][j % 16] + bf16_hi(w4[e]) * acc[j / 16][(j + 1) % 16];
+        if constexpr (D == 16) {
+          const uint32_t o = (uint32_t)__shfl_xor((int)w4[e], 32);
+          s += bf16_lo(o) * acc[0][8 + 2 * e] + bf16_hi(o) * acc[0][9 + 2 * e];
+        }
+      }
+    }
+    return s;
+  };
+
+  auto process = [&](int tile, const Frag& f) {
+    f32x16 gk[MT], bk[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) gk[mt] = bk[mt] = f32x16{0.f};
+    chain(gk, GP_G_HI, f.k);  // G k
+    chain(gk, GP_G_LO, f.k);
+    chain(bk, GP_DB_HI, f.k);  // dB k
+    chain(bk, GP_DB_LO, f.k);
+    const float bt = bf16_to_f32(f.beta);
+    float dot = 0.5f * dotacc(f.k, gk) + dotacc(f.v, bk);
+    if (!owns) dot = 0.f;
+    dot += __shfl_xor(dot, 32);
+    if (half == 0)
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pack_bf16x2(dot, 0.f) & 0xffffu), dbr,
+                                            (uint32_t)(tile * 32 + n) * H * 2, 0, 0);
+    const uint32_t ro = (uint32_t)(tile * 32 + n) * rowbytes + (uint32_t)dv0 * 2;
+    // out: beta * acc over the lane's channels dv0 .. dv0 + HALF - 1
+    auto emit = [&](const f32x16 (&acc)[MT], const __amdgpu_buffer_rsrc_t& dst) {
+      if (!owns) return;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int m = (8 * i) / 16, r = (8 * i) % 16;
+        buf_store16(make_uint4(pack_bf16x2(bt * acc[m][r], bt * acc[m][r + 1]),
+                               pack_bf16x2(bt * acc[m][r + 2], bt * acc[m][r + 3]),
+                               pack_bf16x2(bt * acc[m][r + 4], bt * acc[m][r + 5]),
+                               pack_bf16x2(bt * acc[m][r + 6], bt * acc[m][r + 7])),
+                    dst, ro + 16 * i);
+      }
+    };
+    emit(bk, dvr);            // dv = beta dB k
+    chain(gk, GP_DBT_HI, f.v);  // G k + dB^T v
+    emit(gk, dkr);            // dk = beta (G k + dB^T v)
+  };
+
+  // two operand sets: tile i + NW loads while tile i is multiplied
+  Frag fa, fb;
+  int tile = wave;
+  if (tile < ntiles) load(tile, fa);
+  for (; tile < ntiles; tile += 2 * NW) {
+    if (tile + NW < ntiles) load(tile + NW, fb);
+    process(tile, fa);
+    if (tile + NW >= ntiles) break;
+    if (tile + 2 * NW < ntiles) load(tile + 2 * NW, fa);
+    process(tile + NW, fb);
+  }
+}
+
+template <int D>
+hipError_t backward_gram_d(const Problem& p, const BwdGramBuffers& w, hipStream_t s) {
+  const unsigned nslots = (unsigned)(p.B * p.H * (p.T + 1));
+  hipLaunchKernelGGL(pack_grad_mats<D>, dim3(nslots), dim3(256), 0, s, w.dA, w.dB, static_cast<uint4*>(w.mats));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  auto u16 = [](const void* x) { return static_cast<const uint16_t*>(x); };
+  auto w16 = [](void* x) { return static_cast<uint16_t*>(x); };
+  // every frame (the anchors' slots hold zero matrices, so their gradients are
+  // written as zero), then the text frame from slot T
+  const GradPart a{u16(w.k), u16(w.v), u16(w.beta), w16(w.dk), w16(w.dv), w16(w.dbeta), p.T, p.U, 0, p.T, 0};
+  const GradPart c{u16(w.k_text), u16(w.v_text), u16(w.beta_text), w16(w.dk_text), w16(w.dv_text),
+                   w16(w.dbeta_text), 1, p.L, 0, 1, p.T};
+  const int nblk0 = p.B * p.T * p.H;
+  const unsigned grid = (unsigned)(nblk0 + (p.L > 0 ? p.B * p.H : 0));
+  hipLaunchKernelGGL(gram_bwd_bf16<D>, dim3(grid), dim3(256), 0, s, a, c, nblk0,
+                     static_cast<const uint4*>(w.mats), p.H, p.T + 1);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_gram(const Problem& p, const BwdGramBuffers& w, hipStream_t s) {
+  if (!p.bf16) return hipErrorInvalidValue;
+  switch (p.D) {
+    case 16: return backward_gram_d<16>(p, w, s);
+    case 32: return backward_gram_d<32>(p, w, s);
+    case 64: return backward_gram_d<64>(p, w, s);
+    case 128: return backward_gram_d<128>(p, w, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace vda

@@ -167,6 +167,16 @@ struct BwdScanBuffers {
   float* dalpha;               // [B, T, H, d] (out)
 };
 hipError_t launch_backward_scan(const Problem& p, const BwdScanBuffers& w, hipStream_t s);
+// Third stage: dk, dv, dbeta of every frame and of the text tokens from dA, dB.
+struct BwdGramBuffers {
+  const float *dA, *dB;                     // [B, H, T+1, d, d] (second stage)
+  void* mats;                               // [B, H, T+1] x 5 d x d bfloat16 operand planes
+  const void *k, *v, *beta;                 // [B, T, U, H, d], [B, T, U, H]
+  const void *k_text, *v_text, *beta_text;  // [B, L, H, d], [B, L, H]
+  void *dk, *dv, *dbeta;                    // as k, v, beta (out)
+  void *dk_text, *dv_text, *dbeta_text;     // as the text inputs (out)
+};
+hipError_t launch_backward_gram(const Problem& p, const BwdGramBuffers& w, hipStream_t s);
 hipError_t launch_prep(const Problem& p, int grid_h, int grid_w, const void* q, const void* k,
                        const void* v, const float* wk_s, const float* wk_t, const float* wv_s,
                        const float* wv_t, void* q_hat, void* k_hat, void* v_hat, hipStream_t s);

@@ -1,6 +1,7 @@
 // Host side of the C ABI: descriptor validation, workspace layout and the launch
 // sequence of the VDA forward pass on the caller's stream.
 #include <math.h>
+#include <algorithm>
 #include <string.h>
 
 #include <hip/hip_runtime.h>
@@ -20,6 +21,17 @@ constexpr size_t kChunkedScanMaxHeads = 10;
 size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// A byte range [p, p + n) of a caller's buffer; NULL or empty ranges overlap nothing.
+struct Span {
+  const void* p;
+  size_t n;
+};
+bool overlaps(const Span& a, const Span& b) {
+  if (!a.p || !b.p || !a.n || !b.n) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
 
 hipEvent_t* g_events = nullptr;  // profiling hook (vdn_vda_set_profile_events)
 
@@ -54,6 +66,10 @@ vdn_status check(const vdn_vda_desc* d) {
   // record nothing store at offset 2^31, past that buffer
   if ((double)((d->T + d->chunk - 1) / d->chunk) * d->d_k * d->d_v * 4.0 >= 2147483648.0)
     return VDN_ERR_INVALID_ARG;
+  // a frame's (or the text's) token rows, plus a tile's overhang, are addressed
+  // with 32-bit byte offsets
+  if (((double)d->grid_h * d->grid_w + 64.0) * d->H * d->d_v * 4.0 > 4294967295.0) return VDN_ERR_INVALID_ARG;
+  if (((double)d->n_text + 64.0) * d->H * d->d_v * 4.0 > 4294967295.0) return VDN_ERR_INVALID_ARG;
   if (d->d_k != d->d_v) return VDN_ERR_UNSUPPORTED;
   if (d->d_k != 16 && d->d_k != 32 && d->d_k != 64 && d->d_k != 128) return VDN_ERR_UNSUPPORTED;
   return VDN_OK;
@@ -121,6 +137,7 @@ struct BwdLayout {
   size_t rstates_t, dout, dsq;                                    // first stage
   size_t dF, dR, dST, lam_f, lam_r, dA, dB;                       // second stage (documented)
   size_t states_f, states_r, lam_final, p32, M, N, dPinv, tmp;    // second stage (internal)
+  size_t gmats;                                                   // third stage (internal)
   size_t total;
 };
 BwdLayout make_bwd_layout(const Problem& p) {
@@ -150,6 +167,9 @@ BwdLayout make_bwd_layout(const Problem& p) {
   take(l.N, heads * (p.T + 1) * dd);
   take(l.dPinv, heads * (p.T + 1) * dd);
   take(l.tmp, heads * (p.T + 1) * dd);
+  // five bfloat16 operand planes per slot (G hi, lo; dB hi, lo; dB^T hi), the
+  // rows padded to 32 at d = 16
+  take(l.gmats, heads * (p.T + 1) * 5 * (size_t)std::max(p.D, 32) * p.D * 2);
   l.total = o;
   return l;
 }
@@ -358,6 +378,61 @@ vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha, cons
   w.dB = f(bl.dB);
   w.dalpha = dalpha;
   return launch_backward_scan(p, w, stream) == hipSuccess ? VDN_OK : VDN_ERR_HIP;
+}
+
+vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const void* v, const void* beta,
+                                 const void* k_text, const void* v_text, const void* beta_text, void* dk,
+                                 void* dv, void* dbeta, void* dk_text, void* dv_text, void* dbeta_text,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const vdn_status st = check(d);
+  if (st != VDN_OK) return st;
+  if (d->dtype != VDN_BF16 || (d->flags & (VDN_VDA_QUERY_L2 | VDN_VDA_DECAY_BRIDGE))) return VDN_ERR_UNSUPPORTED;
+  if (!k || !v || !beta || !dk || !dv || !dbeta) return VDN_ERR_INVALID_ARG;
+  const bool text = d->n_text > 0;
+  if (text && (!k_text || !v_text || !beta_text || !dk_text || !dv_text || !dbeta_text)) return VDN_ERR_INVALID_ARG;
+  const Problem p = problem(d);
+  const BwdLayout bl = make_bwd_layout(p);
+  if (!workspace || workspace_bytes < bl.total) return VDN_ERR_WORKSPACE;
+  const void* need16[] = {k, v, dk, dv, text ? k_text : nullptr, text ? v_text : nullptr,
+                          text ? dk_text : nullptr, text ? dv_text : nullptr};
+  for (const void* ptr : need16)
+    if (ptr && !aligned(ptr, 16)) return VDN_ERR_ALIGNMENT;
+  const void* need2[] = {beta, dbeta, text ? beta_text : nullptr, text ? dbeta_text : nullptr};
+  for (const void* ptr : need2)
+    if (ptr && !aligned(ptr, 2)) return VDN_ERR_ALIGNMENT;
+  if (!aligned(workspace, kAlign)) return VDN_ERR_ALIGNMENT;
+  // the outputs are written while the inputs are still read
+  const size_t tok = (size_t)p.B * p.T * p.U * p.H, ttok = (size_t)p.B * p.L * p.H;
+  const size_t xb = tok * p.D * 2, tb = ttok * p.D * 2;
+  const Span ins[] = {{k, xb}, {v, xb}, {beta, tok * 2}, {text ? k_text : nullptr, tb},
+                      {text ? v_text : nullptr, tb}, {text ? beta_text : nullptr, ttok * 2},
+                      {workspace, workspace_bytes}};
+  const Span outs[] = {{dk, xb}, {dv, xb}, {dbeta, tok * 2}, {text ? dk_text : nullptr, tb},
+                       {text ? dv_text : nullptr, tb}, {text ? dbeta_text : nullptr, ttok * 2}};
+  for (const Span& o : outs)
+    for (const Span& i : ins)
+      if (overlaps(o, i)) return VDN_ERR_INVALID_ARG;
+  for (size_t a = 0; a < 6; ++a)
+    for (size_t b = a + 1; b < 6; ++b)
+      if (overlaps(outs[a], outs[b])) return VDN_ERR_INVALID_ARG;
+  char* ws = static_cast<char*>(workspace);
+  BwdGramBuffers w;
+  w.dA = reinterpret_cast<const float*>(ws + bl.dA);
+  w.dB = reinterpret_cast<const float*>(ws + bl.dB);
+  w.mats = ws + bl.gmats;
+  w.k = k;
+  w.v = v;
+  w.beta = beta;
+  w.k_text = k_text;
+  w.v_text = v_text;
+  w.beta_text = beta_text;
+  w.dk = dk;
+  w.dv = dv;
+  w.dbeta = dbeta;
+  w.dk_text = dk_text;
+  w.dv_text = dv_text;
+  w.dbeta_text = dbeta_text;
+  return launch_backward_gram(p, w, stream) == hipSuccess ? VDN_OK : VDN_ERR_HIP;
 }
 
 vdn_status vdn_vda_set_profile_events(hipEvent_t* events, int n) {

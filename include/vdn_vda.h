@@ -301,6 +301,31 @@ vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha,
                                  void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
+/*
+ * Backward pass, third stage: back through the frame statistics
+ * A_t = K_t^T Diag(beta_t) K_t and B_t = V_t^T Diag(beta_t) K_t ([VDN-summary]
+ * "어떻게 쓰나") and the text frame's A_T, B_T.  Reads the second stage's d_a /
+ * d_b from `workspace` and writes, per token (G = dA_t + dA_t^T of its frame),
+ *   dk    = beta (G k + dB_t^T v),       dv = beta dB_t k,
+ *   dbeta = k^T dA_t k + v^T dB_t k,
+ * for every frame into dk, dv [B, T, U, H, d] and dbeta [B, T, U, H] (zero for
+ * the anchor frames, which no scan absorbs) and for the text tokens into
+ * dk_text, dv_text [B, L, H, d] and dbeta_text [B, L, H] (unused when
+ * n_text = 0), all bfloat16.  The three d x d matrices of a frame enter the
+ * matrix cores rounded once to bfloat16.  k, v, beta and the text inputs are
+ * those the forward pass read.  Outputs must overlap neither each other, the
+ * inputs nor the workspace.  Supported: VDN_BF16 without VDN_VDA_QUERY_L2 or
+ * VDN_VDA_DECAY_BRIDGE (else VDN_ERR_UNSUPPORTED).  Errors: VDN_ERR_INVALID_ARG
+ * (NULL pointer, overlap), VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE,
+ * VDN_ERR_ALIGNMENT (16 B for k, v and the d-wide outputs, 2 B for beta and the
+ * dbeta outputs, 256 B for the workspace), VDN_ERR_HIP.  Asynchronous on `stream`.
+ */
+vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const void* v, const void* beta,
+                                 const void* k_text, const void* v_text, const void* beta_text,
+                                 void* dk, void* dv, void* dbeta,
+                                 void* dk_text, void* dv_text, void* dbeta_text,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Profiling hook for benchmarks.  While set, vdn_vda_forward records events[0]
  * on its stream before its first kernel and events[i] after stage i, for
  * i = 1..VDN_VDA_STAGES: frame statistics, text statistics, solve, scan,

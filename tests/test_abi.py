@@ -260,3 +260,48 @@ def test_backward_readout_argument_errors_before_launch():
     # without the epilogue the gate is not needed
     raw = good(epilogue=False)
     assert call(d=raw, gate=0, dgate=0, q=0) == bd.VDN_ERR_INVALID_ARG  # (q still is)
+
+
+def test_backward_gram_argument_errors_before_launch():
+    lib = bd.lib()
+    desc = good()
+    bw = bd.backward_workspace_bytes(desc)
+    names = ["k", "v", "beta", "kt", "vt", "bt", "dk", "dv", "dbeta", "dkt", "dvt", "dbt", "ws"]
+    # 8 GiB apart: every tensor of the 768p clip fits between two bases
+    base = {n: A16 + (1 << 33) * i for i, n in enumerate(names)}
+
+    def call(d=desc, bwb=bw, **over):
+        p = dict(base)
+        p.update(over)
+        P = [ctypes.c_void_p(p[n]) if p[n] else None for n in names]
+        return lib.vdn_vda_backward_gram(ctypes.byref(d), *P, bwb, None)
+
+    assert call(k=0) == bd.VDN_ERR_INVALID_ARG
+    assert call(dbeta=0) == bd.VDN_ERR_INVALID_ARG
+    assert call(dkt=0) == bd.VDN_ERR_INVALID_ARG                    # text tokens need their outputs
+    assert call(dk=base["k"] + 4096) == bd.VDN_ERR_INVALID_ARG     # an output inside an input
+    assert call(dv=base["dk"] + 4096) == bd.VDN_ERR_INVALID_ARG    # two outputs overlapping
+    assert call(dbt=base["ws"] + 512) == bd.VDN_ERR_INVALID_ARG    # an output inside the workspace
+    assert call(bwb=bw - 1) == bd.VDN_ERR_WORKSPACE
+    assert call(ws=0) == bd.VDN_ERR_WORKSPACE
+    assert call(dk=base["dk"] + 8) == bd.VDN_ERR_ALIGNMENT
+    assert call(dbeta=base["dbeta"] + 1) == bd.VDN_ERR_ALIGNMENT
+    assert call(ws=base["ws"] + 16) == bd.VDN_ERR_ALIGNMENT
+    assert call(d=good(dtype="f32")) == bd.VDN_ERR_UNSUPPORTED
+    assert call(d=good(flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_DECAY_BRIDGE)) == bd.VDN_ERR_UNSUPPORTED
+    assert call(d=good(flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_QUERY_L2)) == bd.VDN_ERR_UNSUPPORTED
+    # without text tokens the text pointers are not needed: the call gets as
+    # far as the alignment checks
+    notext = good(n_text=0)
+    assert call(d=notext, kt=0, vt=0, bt=0, dkt=0, dvt=0, dbt=0, bwb=bd.backward_workspace_bytes(notext),
+                dk=base["dk"] + 8) == bd.VDN_ERR_ALIGNMENT
+    # the third stage's operands are an internal section: the workspace grew by them
+    assert bw >= bd.backward_layout(desc).d_b + desc.B * desc.H * (desc.T + 1) * (3 * 128 * 128 * 2 + 128 * 128 * 4)
+
+
+def test_frame_rows_stay_within_32_bit_offsets():
+    """A frame's token rows are addressed with 32-bit byte offsets."""
+    # (U + 64) H d 4 bytes must stay below 4 GiB
+    assert bd.validate(good(grid_h=1000, grid_w=1000, H=8, d=128)) == bd.VDN_OK
+    assert bd.validate(good(grid_h=1000, grid_w=1000, H=16, d=128)) == bd.VDN_ERR_INVALID_ARG
+    assert bd.validate(good(n_text=1 << 20, H=16, d=128)) == bd.VDN_ERR_INVALID_ARG

@@ -1,8 +1,10 @@
-"""GPU parity of the backward pass's first stage (vdn_vda_backward_readout)
-against the oracle's gradients (oracle/vda_grad.py): dq and dgate, and the
-intermediates it leaves in its workspace -- do and the per-frame adjoint of
-the query state dS_q.  Tolerance as for the forward's bfloat16 outputs: max
-relative error per (frame, head) slice (per matrix for dS_q) <= 2e-2."""
+"""GPU parity of the backward pass against the oracle's gradients
+(oracle/vda_grad.py), stage by stage: the first (vdn_vda_backward_readout: dq,
+dgate, and do and dS_q in its workspace), the second (vdn_vda_backward_scan:
+record and scan adjoints, dA, dB, dalpha) and the third
+(vdn_vda_backward_gram: dk, dv, dbeta and the text gradients).  Tolerance as
+for the forward's bfloat16 outputs: max relative error per (frame, head)
+slice (per matrix for the d x d intermediates) <= 2e-2."""
 
 import numpy as np
 import pytest
@@ -31,6 +33,11 @@ CASES = {
     "bwd_16": dict(w=BASE.scaled(name="bwd_16", d=16, H=2, T=9, grid_h=4, grid_w=4, L=4), gain=True),
     "bwd_B2_chunk3": dict(w=BASE.scaled(name="bwd_B2_chunk3", B=2, H=2, T=14, grid_h=4, grid_w=6, L=4, chunk=3)),
     "bwd_T2": dict(w=BASE.scaled(name="bwd_T2", H=2, T=2, grid_h=4, grid_w=8, L=16)),
+    # narrow heads with records in use (bwd_16 and bwd_128_gain have too few
+    # chunks for any record to be read), and a clip without text tokens
+    "bwd_16_chunk3": dict(w=BASE.scaled(name="bwd_16_chunk3", d=16, H=2, T=17, grid_h=4, grid_w=5, L=4, chunk=3)),
+    "bwd_32": dict(w=BASE.scaled(name="bwd_32", d=32, H=2, T=16, grid_h=4, grid_w=9, L=4)),
+    "bwd_64_no_text": dict(w=BASE.scaled(name="bwd_64_no_text", d=64, H=1, T=12, grid_h=3, grid_w=5, L=0, chunk=3)),
 }
 
 
@@ -39,7 +46,7 @@ def _dy(w):
     return synth.f64_to_bf16_bits(rng.standard_normal((w.B, w.T, w.U, w.H, w.d)))
 
 
-def _run(name, stage2=False):
+def _run(name, stage2=False, stage3=False):
     """Forward, then the backward stages, on the case's seeded inputs; returns
     the GPU results, the oracle's gradients and the case's description."""
     import torch
@@ -62,6 +69,12 @@ def _run(name, stage2=False):
         G.say(f"backward_scan {name}")
         gpu["dalpha"] = bd.backward_scan(dev["alpha"], ws, bws, shape=(w.B, w.T, w.H, w.d),
                                          grid=(w.grid_h, w.grid_w), n_text=w.L, chunk=w.chunk, epilogue=epi)
+        torch.cuda.synchronize()
+    if stage3:
+        G.say(f"backward_gram {name}")
+        gpu["gram"] = bd.backward_gram(dev["k"], dev["v"], dev["beta"], dev["k_text"], dev["v_text"],
+                                       dev["beta_text"], bws, grid=(w.grid_h, w.grid_w), chunk=w.chunk,
+                                       epilogue=epi)
         torch.cuda.synchronize()
     f = G.oracle_view({k: x[k] for k in ("q", "k", "v", "beta", "k_text", "v_text", "beta_text", "gate")}, w)
     ref = vda_grad.backward(f["q"], f["k"], f["v"], x["alpha"].astype(np.float64), f["beta"], f["k_text"],
@@ -155,3 +168,44 @@ def test_backward_scan_rejects_the_bridge():
                         flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_DECAY_BRIDGE)
     st = bd.lib().vdn_vda_backward_scan(__import__("ctypes").byref(desc), None, None, 0, None, None, 0, None)
     assert st == bd.VDN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", [n for n in CASES if not CASES[n].get("bridge")])
+def test_backward_gram(name):
+    """Third stage: dk, dv, dbeta of every frame and of the text tokens."""
+    gpu, ref, L, w, epi, dy = _run(name, stage2=True, stage3=True)
+    dk, dv, dbeta, dkt, dvt, dbt = (None if t is None else G.to_host_f64(t) for t in gpu["gram"])
+    B, T, H = w.B, w.T, w.H
+    errs = {"dk": G.slice_rel_err(dk, ref["dk"]), "dv": G.slice_rel_err(dv, ref["dv"]),
+            "dbeta": G.slice_rel_err(dbeta[..., None], ref["dbeta"][..., None])}
+    if w.L:
+        txt = lambda a: a.reshape((B, 1) + a.shape[1:] + ((1,) if a.ndim == 3 else ()))
+        errs.update({"dk_text": G.slice_rel_err(txt(dkt), txt(ref["dk_txt"])),
+                     "dv_text": G.slice_rel_err(txt(dvt), txt(ref["dv_txt"])),
+                     "dbeta_text": G.slice_rel_err(txt(dbt), txt(ref["dbeta_txt"]))})
+    # the anchors' tokens reach no state
+    for a in (dk, dv, dbeta):
+        assert np.abs(a[:, [0, T - 1]]).max() == 0
+    G.say(f"{name}: " + " ".join(f"err({k})={v:.3e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= G.TOL[w.dtype], (k, v)
+
+
+def test_backward_whole_matches_the_stages():
+    """binding.backward (the three entry points in order) gives the stages' results."""
+    import torch
+    from frame_wise_delta_02_amd import binding as bd
+    name = "bwd_64_ragged"
+    gpu, ref, L, w, epi, dy = _run(name, stage2=True, stage3=True)
+    x = synth.make_inputs(w)
+    out, ws, desc, dev = G.run_forward(x, w, epilogue=epi)
+    G.say(f"backward {name}")
+    r = bd.backward(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dev["k_text"], dev["v_text"],
+                    dev["beta_text"], dev["gate"], None, G.to_device(dy, w.dtype), ws, grid=(w.grid_h, w.grid_w),
+                    chunk=w.chunk, epilogue=epi)
+    torch.cuda.synchronize()
+    pairs = {"dq": gpu["dq"], "dgate": gpu["dgate"], "dalpha": gpu["dalpha"]}
+    pairs.update(zip(("dk", "dv", "dbeta", "dk_text", "dv_text", "dbeta_text"), gpu["gram"]))
+    for k, t in pairs.items():
+        assert torch.equal(r[k], t), k
+
