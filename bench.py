@@ -129,6 +129,109 @@ def cpu_baseline(x, w, budget_s: float):
                       f"scaled to the whole {w.H}-head job ({full:.1f} s)"}
 
 
+BWD_STAGES = ("bwd_readout", "bwd_scan", "bwd_gram")
+BWD_SOURCES = {"bwd_readout": "vda_backward.hip", "bwd_scan": "vda_backward.hip", "bwd_gram": "vda_backward.hip"}
+
+
+def bwd_algorithmic_bytes(w, stage: str) -> int:
+    """Bytes a backward stage must move at minimum per step."""
+    tok = w.B * w.T * w.U * w.H
+    ttok = w.B * w.L * w.H
+    dd = w.B * w.H * (w.T + 1) * w.d * w.d * 4
+    if stage == "bwd_readout":   # q, gate, dy in; dq, dgate out; dS_q (float32 per frame) out
+        return tok * 5 * w.d * 2 + w.B * w.H * w.T * w.d * w.d * 4
+    if stage == "bwd_scan":      # dS_q, the statistics A, B and P in; dA, dB, dalpha out
+        return dd * 6 + w.B * w.T * w.H * w.d * 4
+    if stage == "bwd_gram":      # k, v, beta in; dk, dv, dbeta out (frames and text); dA, dB in
+        return (tok + ttok) * (4 * w.d + 2) * 2 + 2 * dd
+    return 0
+
+
+def bench_backward(args, w, x, d, fwd, stream, hip, t_gen) -> int:
+    """A training step of the layer: the forward pass, then the three backward
+    stages; one JSON line with per-stage times (HIP events around each entry
+    point) and the roofline of the slowest backward stage."""
+    import numpy as np
+    import torch
+
+    from frame_wise_delta_02_amd import binding as bd
+    if w.prep or w.dtype != "bf16":
+        print("--backward runs bfloat16 workloads without prep", file=sys.stderr)
+        return 2
+    rng = np.random.default_rng(2024)
+    dy = torch.from_numpy(rng.standard_normal(d["q"].shape).astype(np.float32)).to("cuda").to(torch.bfloat16)
+    grid = (w.grid_h, w.grid_w)
+    desc = bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L, w.chunk, w.dtype, True)
+    fws = fwd.workspace  # the forward's workspace, which every fwd() call rewrites
+    bws = torch.empty(bd.backward_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    dq, dgate = torch.empty_like(d["q"]), torch.empty_like(d["gate"])
+    dalpha = torch.empty((w.B, w.T, w.H, w.d), dtype=torch.float32, device="cuda")
+    gout = tuple(torch.empty_like(d[k]) for k in ("k", "v", "beta", "k_text", "v_text", "beta_text"))
+
+    def bwd(evs=None):
+        if evs:
+            hip.record(evs[0], stream)
+        bd.backward_readout(d["q"], d["gate"], None, d["alpha"], dy, fws, grid=grid, n_text=w.L, chunk=w.chunk,
+                            dq=dq, dgate=dgate, workspace=bws)
+        if evs:
+            hip.record(evs[1], stream)
+        bd.backward_scan(d["alpha"], fws, bws, shape=(w.B, w.T, w.H, w.d), grid=grid, n_text=w.L,
+                         chunk=w.chunk, dalpha=dalpha)
+        if evs:
+            hip.record(evs[2], stream)
+        bd.backward_gram(d["k"], d["v"], d["beta"], d["k_text"], d["v_text"], d["beta_text"], bws, grid=grid,
+                         chunk=w.chunk, out=gout)
+        if evs:
+            hip.record(evs[3], stream)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    wall0 = time.perf_counter()
+    hip.record(e0, stream)
+    for _ in range(args.steps):
+        fwd()
+        bwd()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = hip.elapsed(e0, e1) / args.steps
+    # per-stage times: forward, then each backward stage
+    sets = [[hip.event() for _ in range(5)] for _ in range(args.steps)]
+    for evs in sets:
+        hip.record(evs[0], stream)
+        fwd()
+        bwd(evs[1:])
+    torch.cuda.synchronize()
+    st = {"forward": 0.0, **{k: 0.0 for k in BWD_STAGES}}
+    for evs in sets:
+        st["forward"] += hip.elapsed(evs[0], evs[1]) / args.steps
+        for i, k in enumerate(BWD_STAGES):
+            st[k] += hip.elapsed(evs[i + 1], evs[i + 2]) / args.steps
+    dom = max(BWD_STAGES, key=lambda k: st[k])
+    dom_bytes = bwd_algorithmic_bytes(w, dom)
+    ach = dom_bytes / (st[dom] * 1e-3) / 1e9
+    frames = w.B * w.T
+    rec = {
+        "metric": "VDA forward + backward (training step of the layer) frames/s per GPU",
+        "value": round(frames / (ms * 1e-3), 2), "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "U": w.U, "grid": f"{w.grid_h}x{w.grid_w}",
+                   "d": w.d, "text_tokens": w.L, "chunk": w.chunk, "state": "f32", "pass": "forward+backward"},
+        "tokens_per_s": round(frames * w.U / (ms * 1e-3), 1),
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": dom_bytes,
+                     "launch_ms": round(st[dom], 4), "note": "stage window: every launch of the entry point"},
+        "stages_ms": {k: round(v, 4) for k, v in st.items()},
+        "wall_s_timed": round(wall, 3), "input_gen_s": round(t_gen, 1), "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +243,9 @@ def main() -> int:
     ap.add_argument("--scan", choices=["auto", "frames", "chunks"], default="auto",
                     help="force the frame-by-frame or the chunk-composed scan (auto: the library picks)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle budget; 0 skips it")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step of the layer instead: the forward pass, then the three "
+                         "backward stages (bfloat16 workloads without prep)")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="instead of the forward pass, time a plain device copy of this many GiB "
                          "(the reference for scaling HBM byte counters)")
@@ -214,11 +320,15 @@ def main() -> int:
         bd.forward(*step_q, d["alpha"], d["beta"], d["k_text"], d["v_text"], d["beta_text"], d["gate"], None,
                    grid=grid, chunk=w.chunk, epilogue=True, out=out, workspace=ws, query_l2=w.prep,
                    scan=None if args.scan == "auto" else args.scan)
+    fwd.workspace = ws
 
     def step():
         if w.prep:
             prep_call()
         fwd()
+
+    if args.backward:
+        return bench_backward(args, w, x, d, fwd, stream, hip, t_gen)
 
     for _ in range(args.warmup):
         step()

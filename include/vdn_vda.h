@@ -311,8 +311,9 @@ vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha,
  * for every frame into dk, dv [B, T, U, H, d] and dbeta [B, T, U, H] (zero for
  * the anchor frames, which no scan absorbs) and for the text tokens into
  * dk_text, dv_text [B, L, H, d] and dbeta_text [B, L, H] (unused when
- * n_text = 0), all bfloat16.  The three d x d matrices of a frame enter the
- * matrix cores rounded once to bfloat16.  k, v, beta and the text inputs are
+ * n_text = 0), all bfloat16.  G and dB_t enter the matrix cores as bfloat16
+ * hi + lo pairs (dbeta sums d^2 products that largely cancel), dB_t^T (dk
+ * only) rounded once to bfloat16.  k, v, beta and the text inputs are
  * those the forward pass read.  Outputs must overlap neither each other, the
  * inputs nor the workspace.  Supported: VDN_BF16 without VDN_VDA_QUERY_L2 or
  * VDN_VDA_DECAY_BRIDGE (else VDN_ERR_UNSUPPORTED).  Errors: VDN_ERR_INVALID_ARG
