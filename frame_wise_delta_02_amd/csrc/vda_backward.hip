@@ -415,92 +415,151 @@ struct MatArg {
   int slot_offset;
 };
 
-// C = alpha op(A) op(B) + beta C for every (head, slot), slots 1..T-2 (the
-// absorbed frames) and T (the text frame): workgroup i takes head i / n and
-// the (i % n)-th of those n slots.  float32 on v_mfma_f32_16x16x4f32;
-// both operands staged in LDS (rows padded by 4 floats); wave w forms output
-// rows (d / NWA) w .. of all columns.
-template <int D, bool TA, bool TB>
-__global__ __launch_bounds__(256) void gemm_dd(MatArg A, MatArg B, float* __restrict__ Cb, size_t c_head,
-                                               size_t c_slot, float alpha, float beta, int T) {
-  constexpr int LD = D + 4;
+// The batched d x d products of the second stage, for every (head, slot) with
+// slots 1..T-2 (the absorbed frames) and T (the text frame); workgroup i takes
+// head i / n and the (i % n)-th of those n slots:
+//   C = alpha sum_p op(A_p) op(B_p) + epilogue,
+// with op(X) = X^T where the T flag is set, pair 0's A or B optionally the sum
+// of two matrices (ADDA / ADDB: the two scans' adjoints), and the epilogue
+//   EPI_PLAIN:  nothing more;
+//   EPI_DIAG:   + Diag(a) E, a = alpha_t of the frame (zero for the text slot);
+//   EPI_ROWDOT: C is written and, for frames, r[k] = sum_m C[k][m] E[k][m]
+//               into the per-frame vector out (dalpha).
+// float32 on v_mfma_f32_16x16x4f32.  K runs in panels of KP, both operands'
+// panels staged in LDS in their source orientation (rows padded by 4 floats),
+// small enough for several workgroups per CU; wave w forms output rows
+// (d / NWA) w .. of all columns.
+enum { EPI_PLAIN = 0, EPI_DIAG, EPI_ROWDOT };
+
+struct GemmArgs {
+  MatArg a[2], b[2];     // product pairs
+  MatArg a2, b2;         // pair 0's second summand (ADDA / ADDB)
+  MatArg e;              // epilogue operand
+  const float* alpha;    // [B, T, H, d] (EPI_DIAG)
+  float* out;            // [B, T, H, d] (EPI_ROWDOT)
+  float* c;              // C at c + head * c_head + slot * c_slot
+  size_t c_head, c_slot;
+  float scale;
+  int T, H;
+};
+
+template <int D, bool TA, bool TB, int NPAIR, bool ADDA, bool ADDB, int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_dd(GemmArgs g) {
+  constexpr int KP = D < 32 ? D : 32;
   constexpr int NWA = D / 16 >= 4 ? 4 : D / 16;  // waves with rows
   constexpr int MTW = D / 16 / NWA;               // 16-row tiles per such wave
   constexpr int NT = D / 16;
-  __shared__ float sa[D * LD], sb[D * LD];
+  // panel shapes: op(A) panel is A[k0.., all m] (TA) or A[all m][k0..] (!TA)
+  constexpr int LA = TA ? D + 4 : KP + 4, RA = TA ? KP : D, CA = TA ? D : KP;
+  constexpr int LB = TB ? KP + 4 : D + 4, RB = TB ? D : KP, CB = TB ? KP : D;
+  constexpr int NA4 = RA * CA / 4, NB4 = RB * CB / 4;
+  __shared__ float sa[RA * LA], sb[RB * LB];
+  const int T = g.T;
   const int nfr = T > 2 ? T - 2 : 0, nslot = nfr + 1;
-  const int head = blockIdx.x / nslot, k = blockIdx.x % nslot;
-  const int slot = k < nfr ? 1 + k : T;
-  const float* a = A.base + head * A.head_stride + (size_t)(slot + A.slot_offset) * A.slot_stride;
-  const float* b = B.base + head * B.head_stride + (size_t)(slot + B.slot_offset) * B.slot_stride;
-  float* c = Cb + head * c_head + (size_t)slot * c_slot;
+  const int head = blockIdx.x / nslot, kslot = blockIdx.x % nslot;
+  const int slot = kslot < nfr ? 1 + kslot : T;
+  auto mat = [&](const MatArg& m) {
+    return m.base + head * m.head_stride + (size_t)(slot + m.slot_offset) * m.slot_stride;
+  };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < D * D / 4; i += 256) {
-    const int r = i / (D / 4), c4 = i % (D / 4);
-    const float4 va = *reinterpret_cast<const float4*>(a + (size_t)r * D + 4 * c4);
-    const float4 vb = *reinterpret_cast<const float4*>(b + (size_t)r * D + 4 * c4);
-    *reinterpret_cast<float4*>(&sa[r * LD + 4 * c4]) = va;
-    *reinterpret_cast<float4*>(&sb[r * LD + 4 * c4]) = vb;
-  }
-  __syncthreads();
-  if (wave >= NWA) return;
-  // op(A)[m][k] = TA ? A[k][m] : A[m][k]; op(B)[k][n] = TB ? B[n][k] : B[k][n]
-  auto opa = [&](int m, int kk) { return TA ? sa[kk * LD + m] : sa[m * LD + kk]; };
-  auto opb = [&](int kk, int n) { return TB ? sb[n * LD + kk] : sb[kk * LD + n]; };
   f32x4 acc[MTW][NT];
 #pragma unroll
   for (int mi = 0; mi < MTW; ++mi)
 #pragma unroll
     for (int nj = 0; nj < NT; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int m0 = 16 * MTW * wave;
-  for (int k4 = 0; k4 < D / 4; ++k4) {
-    const int kk = 4 * k4 + (lane >> 4);
-    float av[MTW], bv[NT];
+  // stage one panel: n4 float4 of a block `cols` wide at row r0, column c0 of
+  // the source (plus the second source's)
+  auto stage = [&](float* dst, int ld, int cols, const float* s1, const float* s2, bool add, int r0, int c0,
+                   int n4) {
+    constexpr int MAXV = ((NA4 > NB4 ? NA4 : NB4) + 255) / 256;
+    float4 v[MAXV];
 #pragma unroll
-    for (int mi = 0; mi < MTW; ++mi) av[mi] = opa(m0 + 16 * mi + (lane & 15), kk);
+    for (int i = 0; i < MAXV; ++i) {
+      const int f = tid + 256 * i;
+      if (f < n4) {
+        const int r = f / (cols / 4), c4 = f % (cols / 4);
+        const size_t off = (size_t)(r0 + r) * D + c0 + 4 * c4;
+        v[i] = *reinterpret_cast<const float4*>(s1 + off);
+        if (add) {
+          const float4 w = *reinterpret_cast<const float4*>(s2 + off);
+          v[i].x += w.x; v[i].y += w.y; v[i].z += w.z; v[i].w += w.w;
+        }
+      }
+    }
 #pragma unroll
-    for (int nj = 0; nj < NT; ++nj) bv[nj] = opb(kk, 16 * nj + (lane & 15));
+    for (int i = 0; i < MAXV; ++i) {
+      const int f = tid + 256 * i;
+      if (f < n4) {
+        const int r = f / (cols / 4), c4 = f % (cols / 4);
+        *reinterpret_cast<float4*>(&dst[r * ld + 4 * c4]) = v[i];
+      }
+    }
+  };
+#pragma unroll 1
+  for (int pr = 0; pr < NPAIR; ++pr) {
+    const float* A1 = mat(g.a[pr]);
+    const float* B1 = mat(g.b[pr]);
+    const bool adda = ADDA && pr == 0, addb = ADDB && pr == 0;
+    const float* A2 = adda ? mat(g.a2) : A1;
+    const float* B2 = addb ? mat(g.b2) : B1;
+#pragma unroll 1
+    for (int k0 = 0; k0 < D; k0 += KP) {
+      __syncthreads();  // the previous panel has been read
+      stage(sa, LA, CA, A1, A2, adda, TA ? k0 : 0, TA ? 0 : k0, NA4);
+      stage(sb, LB, CB, B1, B2, addb, TB ? 0 : k0, TB ? k0 : 0, NB4);
+      __syncthreads();
+      if (wave < NWA) {
+        // op(A)[m][k] and op(B)[k][n] of the panel (k local)
+        auto opa = [&](int m, int kk) { return TA ? sa[kk * LA + m] : sa[m * LA + kk]; };
+        auto opb = [&](int kk, int n) { return TB ? sb[n * LB + kk] : sb[kk * LB + n]; };
+#pragma unroll 2
+        for (int k4 = 0; k4 < KP / 4; ++k4) {
+          const int kk = 4 * k4 + (lane >> 4);
+          float av[MTW], bv[NT];
 #pragma unroll
-    for (int mi = 0; mi < MTW; ++mi)
+          for (int mi = 0; mi < MTW; ++mi) av[mi] = opa(m0 + 16 * mi + (lane & 15), kk);
 #pragma unroll
-      for (int nj = 0; nj < NT; ++nj)
-        acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi], bv[nj], acc[mi][nj], 0, 0, 0);
+          for (int nj = 0; nj < NT; ++nj) bv[nj] = opb(kk, 16 * nj + (lane & 15));
+#pragma unroll
+          for (int mi = 0; mi < MTW; ++mi)
+#pragma unroll
+            for (int nj = 0; nj < NT; ++nj)
+              acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi], bv[nj], acc[mi][nj], 0, 0, 0);
+        }
+      }
+    }
   }
+  if (wave >= NWA) return;
   // tile (mi, nj), lane l, reg r: C[m0 + 16 mi + 4 (l/16) + r][16 nj + l%16]
+  float* c = g.c + head * g.c_head + (size_t)slot * g.c_slot;
+  const float* E = EPI != EPI_PLAIN ? mat(g.e) : nullptr;
+  const int b = head / g.H, h = head % g.H;
+  const bool frame = slot < T;
 #pragma unroll
   for (int mi = 0; mi < MTW; ++mi)
 #pragma unroll
-    for (int nj = 0; nj < NT; ++nj)
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + 16 * mi + 4 * (lane >> 4) + r;
+      float arow = 0.f;
+      if constexpr (EPI == EPI_DIAG) arow = frame ? g.alpha[(((size_t)b * T + slot) * g.H + h) * D + row] : 0.f;
+      float dot = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float* o = c + (size_t)(m0 + 16 * mi + 4 * (lane >> 4) + r) * D + 16 * nj + (lane & 15);
-        *o = alpha * acc[mi][nj][r] + (beta != 0.f ? beta * *o : 0.f);
+      for (int nj = 0; nj < NT; ++nj) {
+        const size_t o = (size_t)row * D + 16 * nj + (lane & 15);
+        float v = g.scale * acc[mi][nj][r];
+        if constexpr (EPI == EPI_DIAG) v += arow * E[o];
+        if constexpr (EPI == EPI_ROWDOT) dot += v * E[o];
+        c[o] = v;
       }
-}
-
-// dPinv = Diag(alpha_s) M + N and dalpha_s[k] = sum_m M[k][m] P[k][m] (P is
-// symmetric: the diagonal of M P), for the absorbed frames; the text slot T
-// has no decay: dPinv = N.  One workgroup per (head, slot), one thread per row k.
-template <int D>
-__global__ __launch_bounds__(D) void combine_dpinv(const float* __restrict__ M, const float* __restrict__ N,
-                                                   const float* __restrict__ P, const float* __restrict__ alpha,
-                                                   float* __restrict__ dPinv, float* __restrict__ dalpha, int T,
-                                                   int H) {
-  const int nfr = T > 2 ? T - 2 : 0, nslot = nfr + 1;
-  const int head = blockIdx.x / nslot, k = blockIdx.x % nslot;
-  const int slot = k < nfr ? 1 + k : T;
-  const int b = head / H, h = head % H;
-  const int row = threadIdx.x;
-  const size_t base = ((size_t)head * (T + 1) + slot) * D * D + (size_t)row * D;
-  const bool frame = slot < T;
-  const float a = frame ? alpha[(((size_t)b * T + slot) * H + h) * D + row] : 0.f;
-  float dot = 0.f;
-  for (int m = 0; m < D; ++m) {
-    const float mv = M[base + m];
-    dot += mv * P[base + m];
-    dPinv[base + m] = a * mv + N[base + m];
-  }
-  if (frame) dalpha[(((size_t)b * T + slot) * H + h) * D + row] = dot;
+      if constexpr (EPI == EPI_ROWDOT) {
+        dot += __shfl_xor(dot, 1);
+        dot += __shfl_xor(dot, 2);
+        dot += __shfl_xor(dot, 4);
+        dot += __shfl_xor(dot, 8);
+        if (frame && (lane & 15) == 0) g.out[(((size_t)b * T + slot) * g.H + h) * D + row] = dot;
+      }
+    }
 }
 
 // The text frame's adjoint: dS_T (from the queries) plus half the final
@@ -578,24 +637,43 @@ hipError_t backward_scan_d(const Problem& p, const BwdScanBuffers& w, hipStream_
   const MatArg Sf{w.states_f, hs2, DD, -1}, Sr{w.states_r, hs2, DD, 1}, Lf{w.lam_f, hs1, DD, 0},
       Lr{w.lam_r, hs1, DD, 0}, Bs{w.stats + DD, (T + 1) * 2 * DD, 2 * DD, 0}, Pm{P, hs1, DD, 0},
       DP{w.dPinv, hs1, DD, 0}, Tm{w.tmp, hs1, DD, 0};
-  auto gemm = [&](auto ta, auto tb, const MatArg& A, const MatArg& B, float* C, float alpha, float beta) {
-    hipLaunchKernelGGL((gemm_dd<D, decltype(ta)::value, decltype(tb)::value>), dim3(grid), dim3(256), 0, s, A, B,
-                       C, hs1, DD, alpha, beta, T);
+  const MatArg none{nullptr, 0, 0, 0};
+  auto args = [&](float* C, float scale) {
+    GemmArgs a;
+    a.a[0] = a.a[1] = a.b[0] = a.b[1] = a.a2 = a.b2 = a.e = none;
+    a.alpha = w.alpha;
+    a.out = w.dalpha;
+    a.c = C;
+    a.c_head = hs1;
+    a.c_slot = DD;
+    a.scale = scale;
+    a.T = T;
+    a.H = p.H;
+    return a;
+  };
+  auto launch = [&](auto kernel, const GemmArgs& a) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
   };
-  using Tr = std::true_type;
-  using Nt = std::false_type;
-  if ((e = gemm(Tr(), Nt(), Sf, Lf, w.M, 1.f, 0.f)) != hipSuccess) return e;   // M = Sf^T lam_f
-  if ((e = gemm(Tr(), Nt(), Sr, Lr, w.M, 1.f, 1.f)) != hipSuccess) return e;   //   + Sr^T lam_r
-  if ((e = gemm(Tr(), Nt(), Bs, Lf, w.N, 1.f, 0.f)) != hipSuccess) return e;   // N = B^T lam_f
-  if ((e = gemm(Tr(), Nt(), Bs, Lr, w.N, 1.f, 1.f)) != hipSuccess) return e;   //   + B^T lam_r
-  if ((e = gemm(Nt(), Nt(), Lf, Pm, w.dB, 1.f, 0.f)) != hipSuccess) return e;  // dB = lam_f P
-  if ((e = gemm(Nt(), Nt(), Lr, Pm, w.dB, 1.f, 1.f)) != hipSuccess) return e;  //    + lam_r P
-  hipLaunchKernelGGL(combine_dpinv<D>, dim3(grid), dim3(D), 0, s, w.M, w.N, P, w.alpha, w.dPinv, w.dalpha, T,
-                     p.H);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = gemm(Nt(), Nt(), DP, Pm, w.tmp, 1.f, 0.f)) != hipSuccess) return e;   // dPinv P
-  return gemm(Nt(), Nt(), Pm, Tm, w.dA, -1.f, 0.f);                              // dA = -P dPinv P
+  // M = Sf^T lam_f + Sr^T lam_r; dalpha = rowdot(M, P) (P is symmetric: the diagonal of M P)
+  GemmArgs g = args(w.M, 1.f);
+  g.a[0] = Sf, g.b[0] = Lf, g.a[1] = Sr, g.b[1] = Lr, g.e = Pm;
+  if ((e = launch(gemm_dd<D, true, false, 2, false, false, EPI_ROWDOT>, g)) != hipSuccess) return e;
+  // dPinv = B^T (lam_f + lam_r) + Diag(alpha) M
+  g = args(w.dPinv, 1.f);
+  g.a[0] = Bs, g.b[0] = Lf, g.b2 = Lr, g.e = MatArg{w.M, hs1, DD, 0};
+  if ((e = launch(gemm_dd<D, true, false, 1, false, true, EPI_DIAG>, g)) != hipSuccess) return e;
+  // dB = (lam_f + lam_r) P
+  g = args(w.dB, 1.f);
+  g.a[0] = Lf, g.a2 = Lr, g.b[0] = Pm;
+  if ((e = launch(gemm_dd<D, false, false, 1, true, false, EPI_PLAIN>, g)) != hipSuccess) return e;
+  // dA = -P dPinv P
+  g = args(w.tmp, 1.f);
+  g.a[0] = DP, g.b[0] = Pm;
+  if ((e = launch(gemm_dd<D, false, false, 1, false, false, EPI_PLAIN>, g)) != hipSuccess) return e;
+  g = args(w.dA, -1.f);
+  g.a[0] = Pm, g.b[0] = Tm;
+  return launch(gemm_dd<D, false, false, 1, false, false, EPI_PLAIN>, g);
 }
 
 }  // namespace

@@ -162,7 +162,7 @@ struct BwdScanBuffers {
   float *lam_f, *lam_r;        // [B, H, T+1, d, d]
   float* lam_final;            // [B, H, 2, d, d]
   float* p32;                  // [B, H, T+1, d, d]
-  float *M, *N, *dPinv, *tmp;  // [B, H, T+1, d, d]
+  float *M, *dPinv, *tmp;       // [B, H, T+1, d, d]
   float *dA, *dB;              // [B, H, T+1, d, d] (out)
   float* dalpha;               // [B, T, H, d] (out)
 };

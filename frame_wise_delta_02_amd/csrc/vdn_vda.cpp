@@ -136,7 +136,7 @@ Layout make_layout(const Problem& p) {
 struct BwdLayout {
   size_t rstates_t, dout, dsq;                                    // first stage
   size_t dF, dR, dST, lam_f, lam_r, dA, dB;                       // second stage (documented)
-  size_t states_f, states_r, lam_final, p32, M, N, dPinv, tmp;    // second stage (internal)
+  size_t states_f, states_r, lam_final, p32, M, dPinv, tmp;       // second stage (internal)
   size_t gmats;                                                   // third stage (internal)
   size_t total;
 };
@@ -164,7 +164,6 @@ BwdLayout make_bwd_layout(const Problem& p) {
   take(l.lam_final, heads * 2 * dd);
   take(l.p32, heads * (p.T + 1) * dd);
   take(l.M, heads * (p.T + 1) * dd);
-  take(l.N, heads * (p.T + 1) * dd);
   take(l.dPinv, heads * (p.T + 1) * dd);
   take(l.tmp, heads * (p.T + 1) * dd);
   // five bfloat16 operand planes per slot (G hi, lo; dB hi, lo; dB^T hi), the
@@ -371,7 +370,6 @@ vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha, cons
   w.lam_final = f(bl.lam_final);
   w.p32 = f(bl.p32);
   w.M = f(bl.M);
-  w.N = f(bl.N);
   w.dPinv = f(bl.dPinv);
   w.tmp = f(bl.tmp);
   w.dA = f(bl.dA);
