@@ -27,7 +27,7 @@ EXPORTS = ("vdn_vda_validate", "vdn_vda_workspace_bytes", "vdn_vda_workspace_lay
            "vdn_vda_prepare", "vdn_vda_forward", "vdn_vda_set_profile_events",
            "vdn_vda_status_string", "vdn_vda_backward_workspace_bytes",
            "vdn_vda_backward_workspace_layout", "vdn_vda_backward_readout", "vdn_vda_backward_scan",
-           "vdn_vda_backward_gram")
+           "vdn_vda_backward_gram", "vdn_vda_gates_workspace_bytes", "vdn_vda_gates", "vdn_vda_out_proj")
 STAGES = ("gram", "gram_text", "solve", "scan", "gather", "readout")
 
 
@@ -92,6 +92,12 @@ def lib() -> ctypes.CDLL:
         L.vdn_vda_backward_scan.restype = ctypes.c_int
         L.vdn_vda_backward_gram.argtypes = [dp] + [p] * 13 + [sz, p]
         L.vdn_vda_backward_gram.restype = ctypes.c_int
+        L.vdn_vda_gates_workspace_bytes.argtypes = [dp, ctypes.c_int32]
+        L.vdn_vda_gates_workspace_bytes.restype = sz
+        L.vdn_vda_gates.argtypes = [dp, ctypes.c_int32] + [p] * 7 + [sz, p]
+        L.vdn_vda_gates.restype = ctypes.c_int
+        L.vdn_vda_out_proj.argtypes = [dp, ctypes.c_int32] + [p] * 5
+        L.vdn_vda_out_proj.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -335,4 +341,48 @@ def backward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, 
                                                  chunk=chunk, epilogue=epilogue)
     return dict(dq=dq, dk=dk, dv=dv, dalpha=dalpha, dbeta=dbeta, dk_text=dkt, dv_text=dvt, dbeta_text=dbt,
                 dgate=dgate, workspace=workspace)
+
+
+def gates(x, w_gb, w_alpha, *, heads, d, grid, chunk=5, out=None, workspace=None):
+    """Gate logits, write gate and decay gate from the block input x
+    [B, T, U, d_model] (vdn_vda_gates): w_gb [heads * d + heads, d_model]
+    bfloat16 (the gate rows, then the beta rows), w_alpha [heads * d, d_model]
+    float32.  Returns (gate [B, T, U, H, d], beta [B, T, U, H], alpha [B, T, H, d])."""
+    import torch
+    B, T, U, Dm = x.shape
+    dev = x.device
+    desc = make_desc(B, heads, T, grid[0], grid[1], d, 0, chunk, "bf16", False)
+    if out is None:
+        out = (torch.empty((B, T, U, heads, d), dtype=torch.bfloat16, device=dev),
+               torch.empty((B, T, U, heads), dtype=torch.bfloat16, device=dev),
+               torch.empty((B, T, heads, d), dtype=torch.float32, device=dev))
+    if workspace is None:
+        workspace = torch.empty(max(1, lib().vdn_vda_gates_workspace_bytes(ctypes.byref(desc), Dm)), dtype=torch.uint8,
+                                device=dev)
+    for name, t in (("x", x), ("w_gb", w_gb), ("w_alpha", w_alpha), ("gate", out[0]), ("beta", out[1]),
+                    ("alpha", out[2]), ("workspace", workspace)):
+        _check(t, name, dev)
+    st = lib().vdn_vda_gates(ctypes.byref(desc), Dm, _ptr(x), _ptr(w_gb), _ptr(w_alpha), *map(_ptr, out),
+                             _ptr(workspace), workspace.numel(), _stream())
+    if st != VDN_OK:
+        raise VdaError(st, "vdn_vda_gates")
+    return out
+
+
+def out_proj(o, w_o, y_in=None, *, grid, chunk=5, out=None):
+    """Y = y_in + o W_O^T (vdn_vda_out_proj): o [B, T, U, H, d], w_o [d_model, H * d]
+    and y_in [B, T, U, d_model] bfloat16; ``out`` may be y_in itself."""
+    import torch
+    B, T, U, H, d = o.shape
+    Dm = w_o.shape[0]
+    dev = o.device
+    desc = make_desc(B, H, T, grid[0], grid[1], d, 0, chunk, "bf16", False)
+    if out is None:
+        out = torch.empty((B, T, U, Dm), dtype=torch.bfloat16, device=dev)
+    for name, t in (("o", o), ("w_o", w_o), ("y_in", y_in), ("out", out)):
+        _check(t, name, dev)
+    st = lib().vdn_vda_out_proj(ctypes.byref(desc), Dm, _ptr(o), _ptr(w_o), _ptr(y_in), _ptr(out), _stream())
+    if st != VDN_OK:
+        raise VdaError(st, "vdn_vda_out_proj")
+    return out
 

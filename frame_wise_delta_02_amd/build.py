@@ -23,7 +23,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvdn_vda.so")
 
 SOURCES = ["vdn_vda.cpp", "vda_gram.hip", "vda_solve.hip", "vda_scan.hip",
-           "vda_readout.hip", "vda_prep.hip", "vda_backward.hip"]
+           "vda_readout.hip", "vda_prep.hip", "vda_backward.hip",
+           "vda_proj.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -772,10 +772,9 @@ struct GradPart {
 // (n = lane % 32, half = lane / 32) takes token n's channels
 // (d/2) half .. (d/2) half + d/2 - 1 as the B operand and, with
 // dv0 = HALF * half, holds outputs dv0 + 16 mt + r in acc[mt][r].
-template <int D>
-__global__ __launch_bounds__(256, 1) void gram_bwd_bf16(GradPart part0, GradPart part1, int nblk0,
-                                                        const uint4* __restrict__ mats, int H, int T_slots) {
-  constexpr int NW = 4;
+template <int D, int NW, bool PREFETCH>
+__global__ __launch_bounds__(64 * NW, 1) void gram_bwd_bf16(GradPart part0, GradPart part1, int nblk0,
+                                                           const uint4* __restrict__ mats, int H, int T_slots) {
   constexpr int DP = D < 32 ? 32 : D;
   constexpr int HALF = DP / 2;
   constexpr int MT = DP / 32;
@@ -906,16 +905,25 @@ __global__ __launch_bounds__(256, 1) void gram_bwd_bf16(GradPart part0, GradPart
     emit(gk, dkr);            // dk = beta (G k + dB^T v)
   };
 
-  // two operand sets: tile i + NW loads while tile i is multiplied
-  Frag fa, fb;
-  int tile = wave;
-  if (tile < ntiles) load(tile, fa);
-  for (; tile < ntiles; tile += 2 * NW) {
-    if (tile + NW < ntiles) load(tile + NW, fb);
-    process(tile, fa);
-    if (tile + NW >= ntiles) break;
-    if (tile + 2 * NW < ntiles) load(tile + 2 * NW, fa);
-    process(tile + NW, fb);
+  if constexpr (PREFETCH) {
+    // two operand sets: tile i + NW loads while tile i is multiplied
+    Frag fa, fb;
+    int tile = wave;
+    if (tile < ntiles) load(tile, fa);
+    for (; tile < ntiles; tile += 2 * NW) {
+      if (tile + NW < ntiles) load(tile + NW, fb);
+      process(tile, fa);
+      if (tile + NW >= ntiles) break;
+      if (tile + 2 * NW < ntiles) load(tile + 2 * NW, fa);
+      process(tile + NW, fb);
+    }
+  } else {
+    // one operand set; the other wave on the SIMD covers the load latency
+    for (int tile = wave; tile < ntiles; tile += NW) {
+      Frag f;
+      load(tile, f);
+      process(tile, f);
+    }
   }
 }
 
@@ -934,7 +942,11 @@ hipError_t backward_gram_d(const Problem& p, const BwdGramBuffers& w, hipStream_
                    w16(w.dbeta_text), 1, p.L, 0, 1, p.T};
   const int nblk0 = p.B * p.T * p.H;
   const unsigned grid = (unsigned)(nblk0 + (p.L > 0 ? p.B * p.H : 0));
-  hipLaunchKernelGGL(gram_bwd_bf16<D>, dim3(grid), dim3(256), 0, s, a, c, nblk0,
+  // d = 128: the planes fill the LDS, one workgroup per CU, so two waves per
+  // SIMD share it and hide each other's latency; narrower heads fit several
+  // workgroups per CU and prefetch in registers instead
+  constexpr int NW = D == 128 ? 8 : 4;
+  hipLaunchKernelGGL((gram_bwd_bf16<D, NW, D != 128>), dim3(grid), dim3(64 * NW), 0, s, a, c, nblk0,
                      static_cast<const uint4*>(w.mats), p.H, p.T + 1);
   return hipGetLastError();
 }

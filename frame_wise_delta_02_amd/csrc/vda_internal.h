@@ -177,6 +177,14 @@ struct BwdGramBuffers {
   void *dk_text, *dv_text, *dbeta_text;     // as the text inputs (out)
 };
 hipError_t launch_backward_gram(const Problem& p, const BwdGramBuffers& w, hipStream_t s);
+// The linear maps either side of the path: gate logits and sigmoid(beta) from
+// one bfloat16 product with the stacked weights, the frames' mean tokens, and
+// sigmoid(W_alpha xbar) in float32; the output projection with Y_in added.
+int proj_mean_splits(const Problem& p);
+hipError_t launch_gates(const Problem& p, int d_model, const void* x, const void* w_gb, const float* w_alpha,
+                        void* gate, void* beta, float* alpha, float* partial, float* xbar, hipStream_t s);
+hipError_t launch_out_proj(const Problem& p, int d_model, const void* o, const void* w_o, const void* y_in, void* y,
+                           hipStream_t s);
 hipError_t launch_prep(const Problem& p, int grid_h, int grid_w, const void* q, const void* k,
                        const void* v, const float* wk_s, const float* wk_t, const float* wv_s,
                        const float* wv_t, void* q_hat, void* k_hat, void* v_hat, hipStream_t s);

@@ -173,6 +173,20 @@ BwdLayout make_bwd_layout(const Problem& p) {
   return l;
 }
 
+// The adjacent maps' own checks: bfloat16, a model width that 16-byte rows and
+// 32-bit panel offsets allow.
+vdn_status check_proj(const vdn_vda_desc* d, int32_t d_model) {
+  const vdn_status st = check(d);
+  if (st != VDN_OK) return st;
+  if (d->dtype != VDN_BF16) return VDN_ERR_UNSUPPORTED;
+  if (d_model < 8 || d_model % 8) return VDN_ERR_INVALID_ARG;
+  const double rows = 256.0;  // one tile's rows of either operand
+  if (rows * d_model * 2.0 >= 2147483648.0 || rows * d->H * d->d_v * 2.0 >= 2147483648.0) return VDN_ERR_INVALID_ARG;
+  if ((double)d->B * d->T * d->grid_h * d->grid_w * std::max<double>(d_model, (double)d->H * d->d_v) > 9.0e15)
+    return VDN_ERR_INVALID_ARG;
+  return VDN_OK;
+}
+
 }  // namespace vda
 
 using namespace vda;
@@ -431,6 +445,62 @@ vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const voi
   w.dv_text = dv_text;
   w.dbeta_text = dbeta_text;
   return launch_backward_gram(p, w, stream) == hipSuccess ? VDN_OK : VDN_ERR_HIP;
+}
+
+size_t vdn_vda_gates_workspace_bytes(const vdn_vda_desc* d, int32_t d_model) {
+  if (check_proj(d, d_model) != VDN_OK) return 0;
+  const Problem p = problem(d);
+  const size_t F = (size_t)p.B * p.T;
+  return up(F * proj_mean_splits(p) * d_model * 4) + up(F * d_model * 4);
+}
+
+vdn_status vdn_vda_gates(const vdn_vda_desc* d, int32_t d_model, const void* x, const void* w_gb,
+                         const float* w_alpha, void* gate, void* beta, float* alpha, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  const vdn_status st = check_proj(d, d_model);
+  if (st != VDN_OK) return st;
+  if (!x || !w_gb || !w_alpha || !gate || !beta || !alpha) return VDN_ERR_INVALID_ARG;
+  const Problem p = problem(d);
+  const size_t need = vdn_vda_gates_workspace_bytes(d, d_model);
+  if (!workspace || workspace_bytes < need) return VDN_ERR_WORKSPACE;
+  const void* need16[] = {x, w_gb, w_alpha, gate, alpha};
+  for (const void* ptr : need16)
+    if (!aligned(ptr, 16)) return VDN_ERR_ALIGNMENT;
+  if (!aligned(beta, 2)) return VDN_ERR_ALIGNMENT;
+  if (!aligned(workspace, kAlign)) return VDN_ERR_ALIGNMENT;
+  const size_t M = (size_t)p.B * p.T * p.U, F = (size_t)p.B * p.T, HD = (size_t)p.H * p.D;
+  const Span ins[] = {{x, M * d_model * 2}, {w_gb, (HD + p.H) * d_model * 2}, {w_alpha, HD * d_model * 4},
+                      {workspace, workspace_bytes}};
+  const Span outs[] = {{gate, M * HD * 2}, {beta, M * p.H * 2}, {alpha, F * HD * 4}};
+  for (const Span& o : outs)
+    for (const Span& i : ins)
+      if (overlaps(o, i)) return VDN_ERR_INVALID_ARG;
+  for (size_t a = 0; a < 3; ++a)
+    for (size_t b = a + 1; b < 3; ++b)
+      if (overlaps(outs[a], outs[b])) return VDN_ERR_INVALID_ARG;
+  char* ws = static_cast<char*>(workspace);
+  float* partial = reinterpret_cast<float*>(ws);
+  float* xbar = reinterpret_cast<float*>(ws + up(F * proj_mean_splits(p) * d_model * 4));
+  return launch_gates(p, d_model, x, w_gb, w_alpha, gate, beta, alpha, partial, xbar, stream) == hipSuccess
+             ? VDN_OK
+             : VDN_ERR_HIP;
+}
+
+vdn_status vdn_vda_out_proj(const vdn_vda_desc* d, int32_t d_model, const void* o, const void* w_o,
+                            const void* y_in, void* y, hipStream_t stream) {
+  const vdn_status st = check_proj(d, d_model);
+  if (st != VDN_OK) return st;
+  if (!o || !w_o || !y) return VDN_ERR_INVALID_ARG;
+  const void* need16[] = {o, w_o, y_in, y};
+  for (const void* ptr : need16)
+    if (ptr && !aligned(ptr, 16)) return VDN_ERR_ALIGNMENT;
+  const Problem p = problem(d);
+  const size_t M = (size_t)p.B * p.T * p.U, HD = (size_t)p.H * p.D;
+  // y may be y_in itself (each element is read before it is written), nothing else
+  const Span ys{y, M * d_model * 2};
+  if (overlaps(ys, Span{o, M * HD * 2}) || overlaps(ys, Span{w_o, (size_t)d_model * HD * 2})) return VDN_ERR_INVALID_ARG;
+  if (y_in && y_in != y && overlaps(ys, Span{y_in, M * d_model * 2})) return VDN_ERR_INVALID_ARG;
+  return launch_out_proj(p, d_model, o, w_o, y_in, y, stream) == hipSuccess ? VDN_OK : VDN_ERR_HIP;
 }
 
 vdn_status vdn_vda_set_profile_events(hipEvent_t* events, int n) {

@@ -29,7 +29,8 @@ import numpy as np
 
 # tensor ids in the spawn key (fixed: changing them changes every draw)
 _ID = dict(q=0, k=1, v=2, beta=3, alpha=4, k_text=5, v_text=6, beta_text=7,
-           gate=8, wk_s=9, wk_t=10, wv_s=11, wv_t=12, centres=13)
+           gate=8, wk_s=9, wk_t=10, wv_s=11, wv_t=12, centres=13,
+           x=14, x_frame=15, w_gb=16, w_alpha=17, w_o=18, o=19, y_in=20)
 
 
 @dataclass(frozen=True)
@@ -234,3 +235,35 @@ def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16" and x.dtype == np.uint16:
         return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
     return np.asarray(x, dtype=np.float64)
+
+
+def make_adjacent_inputs(w: Workload, d_model: int, threads: int = 0) -> dict:
+    """Inputs of the linear maps either side of the path, bfloat16 bits except
+    w_alpha (float32):
+
+    * x [B, T, U, d_model]: a per-frame offset ~ N(0, 1) plus per-token N(0, 1)
+      (so the frame means carry a signal for the decay gate);
+    * w_gb [H d + H, d_model] ~ N(0, 1 / d_model) (gate rows, then beta rows);
+    * w_alpha [H d, d_model] ~ N(0, 1 / d_model), float32;
+    * o [B, T, U, H, d] ~ N(0, 1) (a stand-in for the forward's output);
+    * w_o [d_model, H d] ~ N(0, 1 / (H d)); y_in [B, T, U, d_model] ~ N(0, 1).
+    """
+    B, T, U, H, d = w.B, w.T, w.U, w.H, w.d
+    out = {"x": np.empty((B, T, U, d_model), np.uint16), "o": np.empty((B, T, U, H, d), np.uint16),
+           "y_in": np.empty((B, T, U, d_model), np.uint16)}
+
+    def frame(bt):
+        b, t = bt
+        off = _normal(_rng(w.seed, "x_frame", b, t), (1, d_model))
+        out["x"][b, t] = f64_to_bf16_bits(off + _normal(_rng(w.seed, "x", b, t), (U, d_model)))
+        out["o"][b, t] = f64_to_bf16_bits(_normal(_rng(w.seed, "o", b, t), (U, H, d)))
+        out["y_in"][b, t] = f64_to_bf16_bits(_normal(_rng(w.seed, "y_in", b, t), (U, d_model)))
+
+    jobs = [(b, t) for b in range(B) for t in range(T)]
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        list(ex.map(frame, jobs))
+    out["w_gb"] = f64_to_bf16_bits(_normal(_rng(w.seed, "w_gb"), (H * d + H, d_model)) / np.sqrt(d_model))
+    out["w_alpha"] = (_normal(_rng(w.seed, "w_alpha"), (H * d, d_model)) / np.sqrt(d_model)).astype(np.float32)
+    out["w_o"] = f64_to_bf16_bits(_normal(_rng(w.seed, "w_o"), (d_model, H * d)) / np.sqrt(H * d))
+    return out
+

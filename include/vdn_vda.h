@@ -327,6 +327,48 @@ vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const voi
                                  void* dk_text, void* dv_text, void* dbeta_text,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * The linear maps either side of the path ([VDN-summary] "무엇과 다른가": the
+ * linear branch's sigmoid output gate, its separate decay and write gates, and
+ * its own output projection summed with the softmax branch's into the residual
+ * stream; "어떻게 쓰나": alpha per key channel per frame, beta per token;
+ * "전제와 한계": the decay module in FP32).  The pages give no form for these
+ * maps; the library takes linear maps of the attention block's input without
+ * bias, weights stored [out, in]:
+ *   gate  [B, T, U, H, d_v] bfloat16 = W_g x                (logits; the forward
+ *                                       pass applies the sigmoid in its epilogue)
+ *   beta  [B, T, U, H]      bfloat16 = sigmoid(w_beta x)
+ *   alpha [B, T, H, d_k]    float32  = sigmoid(W_alpha xbar_t), xbar_t the mean
+ *                                       of frame t's tokens, in float32
+ * x [B, T, U, d_model] bfloat16; w_gb [H d_v + H, d_model] bfloat16 holds W_g's
+ * rows then w_beta's; w_alpha [H d_k, d_model] float32.  Gate logits and beta
+ * come from one bfloat16 matrix-core product (float32 accumulation, the
+ * sigmoid applied before rounding).  The workspace (vdn_vda_gates_workspace_bytes)
+ * holds the frames' token sums.  d_model a multiple of 8; the descriptor's
+ * n_text, chunk and flags are ignored; VDN_BF16 only (else
+ * VDN_ERR_UNSUPPORTED).  Outputs must overlap neither each other, the inputs
+ * nor the workspace.  Errors: VDN_ERR_INVALID_ARG (NULL pointer, d_model,
+ * overlap), VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE, VDN_ERR_ALIGNMENT (16 B;
+ * 2 B for beta; 256 B for the workspace), VDN_ERR_HIP.  Asynchronous on `stream`.
+ */
+size_t vdn_vda_gates_workspace_bytes(const vdn_vda_desc* d, int32_t d_model);
+vdn_status vdn_vda_gates(const vdn_vda_desc* d, int32_t d_model, const void* x, const void* w_gb,
+                         const float* w_alpha, void* gate, void* beta, float* alpha,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The linear branch's output projection merged into what the caller adds:
+ *   y [B, T, U, d_model] = y_in + o W_O^T,
+ * o [B, T, U, H, d_v] the forward pass's output, w_o [d_model, H d_v], y_in
+ * [B, T, U, d_model] (NULL: zero; typically the softmax branch's projected
+ * output plus the residual stream), all bfloat16; the sum is rounded once from
+ * the bfloat16-rounded product.  y may be y_in itself and must overlap nothing
+ * else.  d_model a multiple of 8; VDN_BF16 only.  Errors as vdn_vda_gates.
+ * Asynchronous on `stream`.
+ */
+vdn_status vdn_vda_out_proj(const vdn_vda_desc* d, int32_t d_model, const void* o, const void* w_o,
+                            const void* y_in, void* y, hipStream_t stream);
+
 /* Profiling hook for benchmarks.  While set, vdn_vda_forward records events[0]
  * on its stream before its first kernel and events[i] after stage i, for
  * i = 1..VDN_VDA_STAGES: frame statistics, text statistics, solve, scan,

@@ -305,3 +305,50 @@ def test_frame_rows_stay_within_32_bit_offsets():
     assert bd.validate(good(grid_h=1000, grid_w=1000, H=8, d=128)) == bd.VDN_OK
     assert bd.validate(good(grid_h=1000, grid_w=1000, H=16, d=128)) == bd.VDN_ERR_INVALID_ARG
     assert bd.validate(good(n_text=1 << 20, H=16, d=128)) == bd.VDN_ERR_INVALID_ARG
+
+
+def test_adjacent_maps_argument_errors_before_launch():
+    lib = bd.lib()
+    desc = good(n_text=0)
+    dm = 3072
+    wsb = lib.vdn_vda_gates_workspace_bytes(ctypes.byref(desc), dm)
+    assert wsb >= desc.B * desc.T * dm * 4 * 2
+    assert lib.vdn_vda_gates_workspace_bytes(ctypes.byref(desc), 100) == 0      # not a multiple of 8
+    assert lib.vdn_vda_gates_workspace_bytes(ctypes.byref(good(dtype="f32")), dm) == 0
+    names = ["x", "wgb", "wa", "gate", "beta", "alpha", "ws"]
+    base = {n: A16 + (1 << 33) * i for i, n in enumerate(names)}
+
+    def gates(d=desc, dmodel=dm, wsbytes=wsb, **over):
+        p = dict(base)
+        p.update(over)
+        P = [ctypes.c_void_p(p[n]) if p[n] else None for n in names]
+        return lib.vdn_vda_gates(ctypes.byref(d), dmodel, *P[:6], P[6], wsbytes, None)
+
+    assert gates(x=0) == bd.VDN_ERR_INVALID_ARG
+    assert gates(alpha=0) == bd.VDN_ERR_INVALID_ARG
+    assert gates(dmodel=100) == bd.VDN_ERR_INVALID_ARG
+    assert gates(wsbytes=wsb - 1) == bd.VDN_ERR_WORKSPACE
+    assert gates(ws=0) == bd.VDN_ERR_WORKSPACE
+    assert gates(gate=base["gate"] + 8) == bd.VDN_ERR_ALIGNMENT
+    assert gates(beta=base["beta"] + 1) == bd.VDN_ERR_ALIGNMENT
+    assert gates(ws=base["ws"] + 16) == bd.VDN_ERR_ALIGNMENT
+    assert gates(beta=base["x"] + 4096) == bd.VDN_ERR_INVALID_ARG           # an output inside x
+    assert gates(alpha=base["gate"] + 4096) == bd.VDN_ERR_INVALID_ARG       # outputs overlapping
+    assert gates(d=good(n_text=0, dtype="f32")) == bd.VDN_ERR_UNSUPPORTED
+
+    onames = ["o", "wo", "yin", "y"]
+    obase = {n: A16 + (1 << 33) * i for i, n in enumerate(onames)}
+
+    def oproj(d=desc, dmodel=dm, **over):
+        p = dict(obase)
+        p.update(over)
+        P = [ctypes.c_void_p(p[n]) if p[n] else None for n in onames]
+        return lib.vdn_vda_out_proj(ctypes.byref(d), dmodel, *P, None)
+
+    assert oproj(o=0) == bd.VDN_ERR_INVALID_ARG
+    assert oproj(y=0) == bd.VDN_ERR_INVALID_ARG
+    assert oproj(dmodel=12) == bd.VDN_ERR_INVALID_ARG
+    assert oproj(y=obase["o"] + 4096) == bd.VDN_ERR_INVALID_ARG              # y inside o
+    assert oproj(y=obase["yin"] + 4096) == bd.VDN_ERR_INVALID_ARG            # y partly over y_in
+    assert oproj(yin=obase["yin"] + 8) == bd.VDN_ERR_ALIGNMENT
+    assert oproj(d=good(n_text=0, dtype="f32")) == bd.VDN_ERR_UNSUPPORTED
