@@ -232,6 +232,100 @@ def bench_backward(args, w, x, d, fwd, stream, hip, t_gen) -> int:
     return 0
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bfloat16
+
+
+def bench_adjacent(args, w, d, stream, hip, t_gen) -> int:
+    """The path with its adjacent maps: gate logits, beta and alpha from the
+    block input x (d_model = H d), the forward pass reading them, then the
+    output projection adding Y_in; one JSON line with per-stage times (HIP
+    events around each entry point) and the matrix-core roofline of the larger
+    GEMM."""
+    import numpy as np
+    import torch
+
+    from frame_wise_delta_02_amd import binding as bd
+    from frame_wise_delta_02_amd import synth
+    if w.prep or w.dtype != "bf16":
+        print("--adjacent runs bfloat16 workloads without prep", file=sys.stderr)
+        return 2
+    dm = w.H * w.d
+    t0 = time.perf_counter()
+    a = synth.make_adjacent_inputs(w, dm)
+    t_gen += time.perf_counter() - t0
+
+    def dev(arr):
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16) if arr.dtype == np.uint16 else torch.from_numpy(arr)
+        return t.to("cuda")
+
+    xa, wgb, wal, wo, yin = (dev(a[k]) for k in ("x", "w_gb", "w_alpha", "w_o", "y_in"))
+    del a
+    grid = (w.grid_h, w.grid_w)
+    gate, beta, alpha = torch.empty_like(d["gate"]), torch.empty_like(d["beta"]), torch.empty_like(d["alpha"])
+    gdesc = bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, 0, w.chunk, "bf16", False)
+    gws = torch.empty(bd.lib().vdn_vda_gates_workspace_bytes(ctypes.byref(gdesc), dm), dtype=torch.uint8,
+                      device="cuda")
+    desc = bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L, w.chunk, w.dtype, True)
+    fws = torch.empty(bd.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(d["q"])
+    y = torch.empty_like(yin)
+
+    def step(evs=None):
+        rec = (lambda i: hip.record(evs[i], stream)) if evs else (lambda i: None)
+        rec(0)
+        bd.gates(xa, wgb, wal, heads=w.H, d=w.d, grid=grid, chunk=w.chunk, out=(gate, beta, alpha), workspace=gws)
+        rec(1)
+        bd.forward(d["q"], d["k"], d["v"], alpha, beta, d["k_text"], d["v_text"], d["beta_text"], gate, None,
+                   grid=grid, chunk=w.chunk, epilogue=True, out=o, workspace=fws)
+        rec(2)
+        bd.out_proj(o, wo, yin, grid=grid, chunk=w.chunk, out=y)
+        rec(3)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    wall0 = time.perf_counter()
+    hip.record(e0, stream)
+    for _ in range(args.steps):
+        step()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = hip.elapsed(e0, e1) / args.steps
+    sets = [[hip.event() for _ in range(4)] for _ in range(args.steps)]
+    for evs in sets:
+        step(evs)
+    torch.cuda.synchronize()
+    names = ("gates", "forward", "out_proj")
+    st = {k: 0.0 for k in names}
+    for evs in sets:
+        for i, k in enumerate(names):
+            st[k] += hip.elapsed(evs[i], evs[i + 1]) / args.steps
+    M = w.B * w.T * w.U
+    flops = {"gates": 2.0 * M * (dm + w.H) * dm, "out_proj": 2.0 * M * dm * dm}
+    dom = max(flops, key=lambda k: st[k])
+    ach = flops[dom] / (st[dom] * 1e-3) / 1e12
+    frames = w.B * w.T
+    rec = {
+        "metric": "VDA forward with its adjacent linear maps (gates before, output projection after) frames/s per GPU",
+        "value": round(frames / (ms * 1e-3), 2), "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "U": w.U, "grid": f"{w.grid_h}x{w.grid_w}",
+                   "d": w.d, "d_model": dm, "text_tokens": w.L, "chunk": w.chunk, "pass": "gates+forward+out_proj"},
+        "tokens_per_s": round(frames * w.U / (ms * 1e-3), 1),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops": flops[dom], "launch_ms": round(st[dom], 4),
+                     "note": "stage window: every launch of the entry point"},
+        "stages_ms": {k: round(v, 4) for k, v in st.items()},
+        "wall_s_timed": round(wall, 3), "input_gen_s": round(t_gen, 1), "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +340,9 @@ def main() -> int:
     ap.add_argument("--backward", action="store_true",
                     help="time a training step of the layer instead: the forward pass, then the three "
                          "backward stages (bfloat16 workloads without prep)")
+    ap.add_argument("--adjacent", action="store_true",
+                    help="time the path with the linear maps either side of it: gates from the block "
+                         "input, the forward pass on them, the output projection (bfloat16 workloads without prep)")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="instead of the forward pass, time a plain device copy of this many GiB "
                          "(the reference for scaling HBM byte counters)")
@@ -329,6 +426,8 @@ def main() -> int:
 
     if args.backward:
         return bench_backward(args, w, x, d, fwd, stream, hip, t_gen)
+    if args.adjacent:
+        return bench_adjacent(args, w, d, stream, hip, t_gen)
 
     for _ in range(args.warmup):
         step()

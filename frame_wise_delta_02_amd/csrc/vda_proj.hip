@@ -15,13 +15,15 @@
 // Kernels:
 //  * gemm_nt_bf16: C = A W^T on v_mfma_f32_32x32x16_bf16, A [M, K] and W [N, K]
 //    bfloat16 (both K-contiguous), 256 x 256 tiles, K-panels of 64 double-
-//    buffered in LDS, four waves of 128 x 128 each, tiles ordered so that the
-//    N-tiles of an M-tile run together on one XCD (its L2 keeps the A panel);
+//    buffered in LDS and prefetched two panels ahead in registers, four waves
+//    of 128 x 128 each, tiles ordered in bands of 4 M-tiles so that the tiles
+//    an XCD runs at once share both operands' panels in its L2;
 //    the epilogue goes through LDS for row-contiguous stores and either splits
 //    the columns into gate logits and sigmoid(beta) or adds Y_in;
 //  * frame_col_sums / frame_mean: the frames' mean tokens in float32 (split
 //    over token ranges, then summed);
-//  * alpha_proj: sigmoid(W_alpha xbar) in float32, one wave per output channel.
+//  * alpha_proj: sigmoid(W_alpha xbar) in float32, 16 frames x 64 channels per
+//    workgroup with K-panels in LDS.
 #include <algorithm>
 
 #include "vda_internal.h"
@@ -30,6 +32,7 @@ namespace vda {
 namespace {
 
 constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int GROUP_M = 4;                // M-tiles per band of the tile order
 constexpr int GLD = GBK + 8;              // LDS row stride of a staged panel (bfloat16 elements)
 constexpr int GOLD = 128 + 8;             // LDS row stride of a wave's output tile
 constexpr int GPANEL = GBM * GLD;         // elements per staged operand panel
@@ -50,11 +53,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16(const uint16_t* __restric
                                                        int M, int N, int K, int mtiles, int ntiles, ProjOut out) {
   __shared__ uint4 lds4[2 * 2 * GPANEL / 8];  // two buffers of (A panel, W panel)
   uint16_t* lds = reinterpret_cast<uint16_t*>(lds4);
-  // tile order: blocks bid, bid + 8, ... share an XCD; within it the N-tiles of
-  // one M-tile are consecutive
+  // tile order: blocks bid, bid + 8, ... share an XCD, which takes a contiguous
+  // run of the tile sequence; the sequence walks bands of GROUP_M M-tiles, M-tile
+  // fastest, so the ~32 tiles an XCD runs at once cover a few M-tiles by several
+  // N-tiles and share both operands' panels in its L2
   const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
-  const int nt = slot % ntiles, mt = (slot / ntiles) * 8 + xcd;
-  if (mt >= mtiles) return;
+  const int ntot = mtiles * ntiles, per_xcd = (ntot + 7) / 8;
+  const int tau = xcd * per_xcd + slot;
+  if (slot >= per_xcd || tau >= ntot) return;
+  const int band = tau / (GROUP_M * ntiles), r = tau % (GROUP_M * ntiles);
+  const int gm = min(GROUP_M, mtiles - band * GROUP_M);
+  const int nt = r / gm, mt = band * GROUP_M + r % gm;
   const int m0 = mt * GBM, n0 = nt * GBN;
   const int mrows = min(GBM, M - m0), nrows = min(GBN, N - n0);
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(A + (size_t)m0 * K, (uint32_t)mrows * K * 2);
@@ -63,24 +72,27 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16(const uint16_t* __restric
   const int wm = wave >> 1, wn = wave & 1;
 
   // staging: thread t moves chunks c = t + 256 i (i < 8) of each panel: row c / 8,
-  // k-chunk c % 8 (8 bfloat16); chunks at or past K are zero
-  uint4 ra[8], rw[8];
-  auto gload = [&](int k0) {
+  // k-chunk c % 8 (8 bfloat16); chunks at or past K are zero.  Two register
+  // sets: while panel k is multiplied, panel k + 2 loads into one set and panel
+  // k + 1 (loaded one panel earlier) goes from the other set to LDS, both spread
+  // over the panel's k-steps so that the matrix cores keep issuing.
+  uint4 ra0[8], rw0[8], ra1[8], rw1[8];
+  auto gload = [&](uint4 (&ra)[8], uint4 (&rw)[8], int k0, int i0, int i1) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
       const int k = k0 + 8 * kc;
-      const uint32_t off = ((uint32_t)row * K + k) * 2;
-      const bool in = k < K;
-      ra[i] = in ? buf_load16(ar, off) : make_uint4(0, 0, 0, 0);
-      rw[i] = in ? buf_load16(wr, off) : make_uint4(0, 0, 0, 0);
+      // past K: an offset beyond either panel's range, which reads zero
+      const uint32_t off = k < K ? ((uint32_t)row * K + k) * 2 : 0x80000000u;
+      ra[i] = buf_load16(ar, off);
+      rw[i] = buf_load16(wr, off);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const uint4 (&ra)[8], const uint4 (&rw)[8], int buf, int i0, int i1) {
     uint16_t* pa = lds + buf * 2 * GPANEL;
     uint16_t* pw = pa + GPANEL;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
       *reinterpret_cast<uint4*>(pa + row * GLD + 8 * kc) = ra[i];
       *reinterpret_cast<uint4*>(pw + row * GLD + 8 * kc) = rw[i];
@@ -93,32 +105,63 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16(const uint16_t* __restric
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0.f};
 
-  const int nk = (K + GBK - 1) / GBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
   const int arow = 128 * wm + (lane & 31), wrow = 128 * wn + (lane & 31), kq = 8 * (lane >> 5);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * GBK);
+  // one panel from LDS buffer `buf` (four k-steps of 16, the next k-step's
+  // operands read while the current one's 16 products issue), with a quarter
+  // of the next loads (into set L) and of the LDS stores (from set S, into the
+  // other buffer) after each k-step
+  auto stage = [&](int buf, uint4 (&la)[8], uint4 (&lw)[8], int k0_load, const uint4 (&sa)[8],
+                   const uint4 (&sw)[8]) {
     const uint16_t* pa = lds + buf * 2 * GPANEL;
     const uint16_t* pw = pa + GPANEL;
-#pragma unroll
-    for (int s = 0; s < GBK / 16; ++s) {
-      bf16x8 af[4], wf[4];
+    auto frags = [&](int s, bf16x8 (&af)[4], bf16x8 (&wf)[4]) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         af[i] = *reinterpret_cast<const bf16x8*>(pa + (arow + 32 * i) * GLD + 16 * s + kq);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         wf[j] = *reinterpret_cast<const bf16x8*>(pw + (wrow + 32 * j) * GLD + 16 * s + kq);
+    };
+    bf16x8 af[4], wf[4], an[4], wn2[4];
+    frags(0, af, wf);
+#pragma unroll
+    for (int s = 0; s < GBK / 16; ++s) {
+      if (s + 1 < GBK / 16) frags(s + 1, an, wn2);
+      gload(la, lw, k0_load, 2 * s, 2 * s + 2);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wf[j], acc[i][j], 0, 0, 0);
+      lstore(sa, sw, buf ^ 1, 2 * s, 2 * s + 2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        af[i] = an[i];
+        wf[i] = wn2[i];
+      }
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+  };
+
+  const int nk = (K + GBK - 1) / GBK;
+  gload(ra0, rw0, 0, 0, 8);
+  lstore(ra0, rw0, 0, 0, 8);
+  gload(ra0, rw0, GBK, 0, 8);
+  __syncthreads();
+  // panels in pairs: panel kt (even) from buffer 0, loading panel kt + 2 into
+  // set 1 and storing panel kt + 1 (set 0) into buffer 1; then the same with the
+  // roles swapped.  Loads and stores are unconditional, so the code is
+  // straight-line and each wait leaves the newer panel's loads in flight; a
+  // panel past K reads zero and lands in a buffer nothing reads.
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    stage(0, ra1, rw1, (kt + 2) * GBK, ra0, rw0);
     __syncthreads();
+    stage(1, ra0, rw0, (kt + 3) * GBK, ra1, rw1);
+    __syncthreads();
+  }
+  if (kt < nk) {  // an odd last panel, already in buffer 0
+    stage(0, ra1, rw1, nk * GBK + GBK, ra0, rw0);
+    __syncthreads();  // before the epilogue reuses the buffers
   }
 
   // epilogue: the wave's 128 x 128 tile as bfloat16 rows in LDS (acc[i][j][r]
@@ -131,7 +174,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16(const uint16_t* __restric
     bool sig = false;
     if constexpr (EPI == PROJ_GATE) sig = n0 + 128 * wn + col >= out.n_split;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -139,6 +182,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16(const uint16_t* __restric
         if constexpr (EPI == PROJ_GATE) v = sig ? sigmoidf_(v) : v;
         po[row * GOLD + col] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
       }
+      __builtin_amdgcn_sched_barrier(0);  // one accumulator tile live at a time
+    }
   }
   __builtin_amdgcn_wave_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -149,6 +194,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16(const uint16_t* __restric
                                                 rbase < M ? (uint32_t)min(128, M - rbase) * ng * 2 : 0u);
     const __amdgpu_buffer_rsrc_t br = make_rsrc(out.c2 + (size_t)rbase * nb,
                                                 rbase < M ? (uint32_t)min(128, M - rbase) * nb * 2 : 0u);
+#pragma unroll 4
     for (int it = 0; it < 32; ++it) {
       const int c = lane + 64 * it, row = c >> 4, ch = c & 15;
       const int n = cbase + 8 * ch;
@@ -172,6 +218,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16(const uint16_t* __restric
     const uint32_t bytes = rbase < M ? (uint32_t)min(128, M - rbase) * N * 2 : 0u;
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(out.c + (size_t)rbase * N, bytes);
     const __amdgpu_buffer_rsrc_t ir = make_rsrc(out.y_in ? out.y_in + (size_t)rbase * N : out.c, out.y_in ? bytes : 0u);
+#pragma unroll 4
     for (int it = 0; it < 32; ++it) {
       const int c = lane + 64 * it, row = c >> 4, ch = c & 15;
       const int n = cbase + 8 * ch;
@@ -239,25 +286,45 @@ __global__ __launch_bounds__(256) void frame_mean(const float* __restrict__ part
   xbar[i] = s / (float)U;
 }
 
-// alpha [F, NA] = sigmoid(xbar W_alpha^T), one wave per output channel n.
+// alpha [F, NA] = sigmoid(xbar W_alpha^T) in float32.  Workgroup (fb, nb) forms
+// frames 16 fb .. + 15 and channels 64 nb .. + 63; K runs in panels of 64 staged
+// in LDS (xbar panel [16][64], W_alpha panel [64][64 + 1]); thread t owns
+// frame t / 16 and channels nb * 64 + (t % 16) + 16 j, j < 4.
 __global__ __launch_bounds__(256) void alpha_proj(const float* __restrict__ xbar, const float* __restrict__ wa,
                                                   float* __restrict__ alpha, int F, int K, int NA) {
-  const int n = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (n >= NA) return;
-  const float* w = wa + (size_t)n * K;
-  for (int f = 0; f < F; ++f) {
-    const float* xb = xbar + (size_t)f * K;
-    float s = 0.f;
-    for (int k = lane; k < K; k += 64) s += w[k] * xb[k];
+  __shared__ float sx[16][64];
+  __shared__ float sw[64][65];
+  const int f0 = blockIdx.x * 16, n0 = blockIdx.y * 64, tid = threadIdx.x;
+  const int fl = tid >> 4, nl = tid & 15;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    __syncthreads();
+    for (int i = tid; i < 16 * 64; i += 256) {
+      const int f = i >> 6, k = i & 63;
+      sx[f][k] = (f0 + f < F && k0 + k < K) ? xbar[(size_t)(f0 + f) * K + k0 + k] : 0.f;
+    }
+    for (int i = tid; i < 64 * 64; i += 256) {
+      const int n = i >> 6, k = i & 63;
+      sw[n][k] = (n0 + n < NA && k0 + k < K) ? wa[(size_t)(n0 + n) * K + k0 + k] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < 64; ++k) {
+      const float xv = sx[fl][k];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-    if (lane == 0) alpha[(size_t)f * NA + n] = sigmoidf_(s);
+      for (int j = 0; j < 4; ++j) acc[j] += xv * sw[nl + 16 * j][k];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int f = f0 + fl, n = n0 + nl + 16 * j;
+    if (f < F && n < NA) alpha[(size_t)f * NA + n] = sigmoidf_(acc[j]);
   }
 }
 
 hipError_t launch_gemm(int epi, int M, int N, int K, const void* a, const void* w, const ProjOut& out, hipStream_t s) {
   const int mtiles = (M + GBM - 1) / GBM, ntiles = (N + GBN - 1) / GBN;
-  const long long grid = (long long)((mtiles + 7) / 8 * 8) * ntiles;
+  const long long grid = ((long long)mtiles * ntiles + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   auto A = static_cast<const uint16_t*>(a);
@@ -290,7 +357,8 @@ hipError_t launch_gates(const Problem& p, int d_model, const void* x, const void
   hipLaunchKernelGGL(frame_mean, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, partial, xbar, p.U, K, S, F);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int NA = p.H * p.D;
-  hipLaunchKernelGGL(alpha_proj, dim3((unsigned)((NA + 3) / 4)), dim3(256), 0, s, xbar, w_alpha, alpha, F, K, NA);
+  hipLaunchKernelGGL(alpha_proj, dim3((unsigned)((F + 15) / 16), (unsigned)((NA + 63) / 64)), dim3(256), 0, s, xbar,
+                     w_alpha, alpha, F, K, NA);
   return hipGetLastError();
 }
 
