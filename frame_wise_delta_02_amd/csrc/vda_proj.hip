@@ -22,8 +22,8 @@
 //    the columns into gate logits and sigmoid(beta) or adds Y_in;
 //  * frame_col_sums / frame_mean: the frames' mean tokens in float32 (split
 //    over token ranges, then summed);
-//  * alpha_proj: sigmoid(W_alpha xbar) in float32, 16 frames x 64 channels per
-//    workgroup with K-panels in LDS.
+//  * alpha_proj: sigmoid(W_alpha xbar) in float32, 16 frames x 32 channels per
+//    workgroup with K-panels of 256 in LDS.
 #include <algorithm>
 
 #include "vda_internal.h"
@@ -287,36 +287,51 @@ __global__ __launch_bounds__(256) void frame_mean(const float* __restrict__ part
 }
 
 // alpha [F, NA] = sigmoid(xbar W_alpha^T) in float32.  Workgroup (fb, nb) forms
-// frames 16 fb .. + 15 and channels 64 nb .. + 63; K runs in panels of 64 staged
-// in LDS (xbar panel [16][64], W_alpha panel [64][64 + 1]); thread t owns
-// frame t / 16 and channels nb * 64 + (t % 16) + 16 j, j < 4.
+// frames 16 fb .. + 15 and channels 32 nb .. + 31; K runs in panels of 256
+// staged in LDS (xbar panel [16][256], W_alpha panel [32][256 + 1]), every load
+// of a panel in flight at once; thread t owns frame t / 16 and channels
+// 32 nb + (t % 16) + 16 j, j < 2.
+constexpr int AKP = 256, ANT = 32;
 __global__ __launch_bounds__(256) void alpha_proj(const float* __restrict__ xbar, const float* __restrict__ wa,
                                                   float* __restrict__ alpha, int F, int K, int NA) {
-  __shared__ float sx[16][64];
-  __shared__ float sw[64][65];
-  const int f0 = blockIdx.x * 16, n0 = blockIdx.y * 64, tid = threadIdx.x;
+  __shared__ float sx[16][AKP];
+  __shared__ float sw[ANT][AKP + 1];
+  const int f0 = blockIdx.x * 16, n0 = blockIdx.y * ANT, tid = threadIdx.x;
   const int fl = tid >> 4, nl = tid & 15;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < K; k0 += 64) {
-    __syncthreads();
-    for (int i = tid; i < 16 * 64; i += 256) {
-      const int f = i >> 6, k = i & 63;
-      sx[f][k] = (f0 + f < F && k0 + k < K) ? xbar[(size_t)(f0 + f) * K + k0 + k] : 0.f;
+  float acc[2] = {0.f, 0.f};
+  for (int k0 = 0; k0 < K; k0 += AKP) {
+    float vx[16 * AKP / 256], vw[ANT * AKP / 256];
+#pragma unroll
+    for (int j = 0; j < 16 * AKP / 256; ++j) {
+      const int i = tid + 256 * j, f = i / AKP, k = i % AKP;
+      vx[j] = (f0 + f < F && k0 + k < K) ? xbar[(size_t)(f0 + f) * K + k0 + k] : 0.f;
     }
-    for (int i = tid; i < 64 * 64; i += 256) {
-      const int n = i >> 6, k = i & 63;
-      sw[n][k] = (n0 + n < NA && k0 + k < K) ? wa[(size_t)(n0 + n) * K + k0 + k] : 0.f;
+#pragma unroll
+    for (int j = 0; j < ANT * AKP / 256; ++j) {
+      const int i = tid + 256 * j, n = i / AKP, k = i % AKP;
+      vw[j] = (n0 + n < NA && k0 + k < K) ? wa[(size_t)(n0 + n) * K + k0 + k] : 0.f;
+    }
+    __syncthreads();  // the previous panel has been read
+#pragma unroll
+    for (int j = 0; j < 16 * AKP / 256; ++j) {
+      const int i = tid + 256 * j;
+      sx[i / AKP][i % AKP] = vx[j];
+    }
+#pragma unroll
+    for (int j = 0; j < ANT * AKP / 256; ++j) {
+      const int i = tid + 256 * j;
+      sw[i / AKP][i % AKP] = vw[j];
     }
     __syncthreads();
 #pragma unroll 8
-    for (int k = 0; k < 64; ++k) {
+    for (int k = 0; k < AKP; ++k) {
       const float xv = sx[fl][k];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += xv * sw[nl + 16 * j][k];
+      acc[0] += xv * sw[nl][k];
+      acc[1] += xv * sw[nl + 16][k];
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int f = f0 + fl, n = n0 + nl + 16 * j;
     if (f < F && n < NA) alpha[(size_t)f * NA + n] = sigmoidf_(acc[j]);
   }
@@ -357,8 +372,8 @@ hipError_t launch_gates(const Problem& p, int d_model, const void* x, const void
   hipLaunchKernelGGL(frame_mean, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, partial, xbar, p.U, K, S, F);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int NA = p.H * p.D;
-  hipLaunchKernelGGL(alpha_proj, dim3((unsigned)((F + 15) / 16), (unsigned)((NA + 63) / 64)), dim3(256), 0, s, xbar,
-                     w_alpha, alpha, F, K, NA);
+  hipLaunchKernelGGL(alpha_proj, dim3((unsigned)((F + 15) / 16), (unsigned)((NA + ANT - 1) / ANT)), dim3(256), 0, s,
+                     xbar, w_alpha, alpha, F, K, NA);
   return hipGetLastError();
 }
 
