@@ -101,8 +101,10 @@ def decode_split_pinv(raw: np.ndarray, D: int) -> np.ndarray:
     row0 = 32 * ks + 8 * (lane // 16)
     rows = (row0[:, None] + np.arange(8)[None, :]).ravel()
     cols = np.repeat(col, 8)
-    bits = raw.astype(np.int64) & 0xFFFF
-    vals = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    bits = (raw.astype(np.int64) & 0xFFFF).astype(np.uint32)
+    # slots the forward never forms (anchors) hold arbitrary bits; nothing reads them
+    with np.errstate(invalid="ignore"):
+        vals = (bits << np.uint32(16)).view(np.float32).astype(np.float64)
     full = vals[:, 0] + vals[:, 1]
     out = np.empty((raw.shape[0], D, D))
     out[:, rows, cols] = full
