@@ -49,7 +49,7 @@ struct ProjOut {
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.f / (1.f + expf(-z)); }
 
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_nt_bf16(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+__global__ __launch_bounds__(512, 1) void gemm_nt_bf16(const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
                                                        int M, int N, int K, int mtiles, int ntiles, ProjOut out) {
   __shared__ uint4 lds4[2 * 2 * GPANEL / 8];  // two buffers of (A panel, W panel)
   uint16_t* lds = reinterpret_cast<uint16_t*>(lds4);
@@ -69,18 +69,18 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16(const uint16_t* __restric
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(A + (size_t)m0 * K, (uint32_t)mrows * K * 2);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(W + (size_t)n0 * K, (uint32_t)nrows * K * 2);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves of 128 x 64
 
-  // staging: thread t moves chunks c = t + 256 i (i < 8) of each panel: row c / 8,
+  // staging: thread t moves chunks c = t + 512 i (i < 4) of each panel: row c / 8,
   // k-chunk c % 8 (8 bfloat16); chunks at or past K are zero.  Two register
   // sets: while panel k is multiplied, panel k + 2 loads into one set and panel
   // k + 1 (loaded one panel earlier) goes from the other set to LDS, both spread
   // over the panel's k-steps so that the matrix cores keep issuing.
-  uint4 ra0[8], rw0[8], ra1[8], rw1[8];
-  auto gload = [&](uint4 (&ra)[8], uint4 (&rw)[8], int k0, int i0, int i1) {
+  uint4 ra0[4], rw0[4], ra1[4], rw1[4];
+  auto gload = [&](uint4 (&ra)[4], uint4 (&rw)[4], int k0, int i0, int i1) {
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
+      const int c = tid + 512 * i, row = c >> 3, kc = c & 7;
       const int k = k0 + 8 * kc;
       // past K: an offset beyond either panel's range, which reads zero
       const uint32_t off = k < K ? ((uint32_t)row * K + k) * 2 : 0x80000000u;
@@ -88,64 +88,54 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16(const uint16_t* __restric
       rw[i] = buf_load16(wr, off);
     }
   };
-  auto lstore = [&](const uint4 (&ra)[8], const uint4 (&rw)[8], int buf, int i0, int i1) {
+  auto lstore = [&](const uint4 (&ra)[4], const uint4 (&rw)[4], int buf, int i0, int i1) {
     uint16_t* pa = lds + buf * 2 * GPANEL;
     uint16_t* pw = pa + GPANEL;
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, kc = c & 7;
+      const int c = tid + 512 * i, row = c >> 3, kc = c & 7;
       *reinterpret_cast<uint4*>(pa + row * GLD + 8 * kc) = ra[i];
       *reinterpret_cast<uint4*>(pw + row * GLD + 8 * kc) = rw[i];
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0.f};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{0.f};
 
-  const int arow = 128 * wm + (lane & 31), wrow = 128 * wn + (lane & 31), kq = 8 * (lane >> 5);
-  // one panel from LDS buffer `buf` (four k-steps of 16, the next k-step's
-  // operands read while the current one's 16 products issue), with a quarter
-  // of the next loads (into set L) and of the LDS stores (from set S, into the
-  // other buffer) after each k-step
-  auto stage = [&](int buf, uint4 (&la)[8], uint4 (&lw)[8], int k0_load, const uint4 (&sa)[8],
-                   const uint4 (&sw)[8]) {
+  const int arow = 128 * wm + (lane & 31), wrow = 64 * wn + (lane & 31), kq = 8 * (lane >> 5);
+  // one panel from LDS buffer `buf`: four k-steps of 16, each with one of the
+  // four staging parts (loads into set L, LDS stores from set S into the other
+  // buffer) after its eight products
+  auto stage = [&](int buf, uint4 (&la)[4], uint4 (&lw)[4], int k0_load, const uint4 (&sa)[4],
+                   const uint4 (&sw)[4]) {
     const uint16_t* pa = lds + buf * 2 * GPANEL;
     const uint16_t* pw = pa + GPANEL;
-    auto frags = [&](int s, bf16x8 (&af)[4], bf16x8 (&wf)[4]) {
+#pragma unroll
+    for (int s = 0; s < GBK / 16; ++s) {
+      bf16x8 af[4], wf[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         af[i] = *reinterpret_cast<const bf16x8*>(pa + (arow + 32 * i) * GLD + 16 * s + kq);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         wf[j] = *reinterpret_cast<const bf16x8*>(pw + (wrow + 32 * j) * GLD + 16 * s + kq);
-    };
-    bf16x8 af[4], wf[4], an[4], wn2[4];
-    frags(0, af, wf);
-#pragma unroll
-    for (int s = 0; s < GBK / 16; ++s) {
-      if (s + 1 < GBK / 16) frags(s + 1, an, wn2);
-      gload(la, lw, k0_load, 2 * s, 2 * s + 2);
+      gload(la, lw, k0_load, s, s + 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wf[j], acc[i][j], 0, 0, 0);
-      lstore(sa, sw, buf ^ 1, 2 * s, 2 * s + 2);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wf[j], acc[i][j], 0, 0, 0);
+      lstore(sa, sw, buf ^ 1, s, s + 1);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = an[i];
-        wf[i] = wn2[i];
-      }
     }
   };
 
   const int nk = (K + GBK - 1) / GBK;
-  gload(ra0, rw0, 0, 0, 8);
-  lstore(ra0, rw0, 0, 0, 8);
-  gload(ra0, rw0, GBK, 0, 8);
+  gload(ra0, rw0, 0, 0, 4);
+  lstore(ra0, rw0, 0, 0, 4);
+  gload(ra0, rw0, GBK, 0, 4);
   __syncthreads();
   // panels in pairs: panel kt (even) from buffer 0, loading panel kt + 2 into
   // set 1 and storing panel kt + 1 (set 0) into buffer 1; then the same with the
@@ -164,15 +154,16 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16(const uint16_t* __restric
     __syncthreads();  // before the epilogue reuses the buffers
   }
 
-  // epilogue: the wave's 128 x 128 tile as bfloat16 rows in LDS (acc[i][j][r]
+  // epilogue: the wave's 128 x 64 tile as bfloat16 rows in LDS (acc[i][j][r]
   // is C[32 i + 8 (r / 4) + 4 (lane / 32) + r % 4][32 j + lane % 32]), then
   // row-contiguous 16-byte stores
-  uint16_t* po = lds + wave * 128 * GOLD;
+  constexpr int OLD = 64 + 8;
+  uint16_t* po = lds + wave * 128 * OLD;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int col = 32 * j + (lane & 31);
     bool sig = false;
-    if constexpr (EPI == PROJ_GATE) sig = n0 + 128 * wn + col >= out.n_split;
+    if constexpr (EPI == PROJ_GATE) sig = n0 + 64 * wn + col >= out.n_split;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -180,14 +171,14 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16(const uint16_t* __restric
         const int row = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         float v = acc[i][j][r];
         if constexpr (EPI == PROJ_GATE) v = sig ? sigmoidf_(v) : v;
-        po[row * GOLD + col] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
+        po[row * OLD + col] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
       }
       __builtin_amdgcn_sched_barrier(0);  // one accumulator tile live at a time
     }
   }
   __builtin_amdgcn_wave_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  const int rbase = m0 + 128 * wm, cbase = n0 + 128 * wn;
+  const int rbase = m0 + 128 * wm, cbase = n0 + 64 * wn;
   if constexpr (EPI == PROJ_GATE) {
     const int ng = out.n_split, nb = out.n2;
     const __amdgpu_buffer_rsrc_t gr = make_rsrc(out.c + (size_t)rbase * ng,
@@ -195,10 +186,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16(const uint16_t* __restric
     const __amdgpu_buffer_rsrc_t br = make_rsrc(out.c2 + (size_t)rbase * nb,
                                                 rbase < M ? (uint32_t)min(128, M - rbase) * nb * 2 : 0u);
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-      const int c = lane + 64 * it, row = c >> 4, ch = c & 15;
+    for (int it = 0; it < 16; ++it) {
+      const int c = lane + 64 * it, row = c >> 3, ch = c & 7;
       const int n = cbase + 8 * ch;
-      const uint4 v = *reinterpret_cast<const uint4*>(po + row * GOLD + 8 * ch);
+      const uint4 v = *reinterpret_cast<const uint4*>(po + row * OLD + 8 * ch);
       if (n + 8 <= ng) {
         buf_store16(v, gr, ((uint32_t)row * ng + n) * 2);
       } else if (n < ng + nb) {
@@ -219,12 +210,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nt_bf16(const uint16_t* __restric
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(out.c + (size_t)rbase * N, bytes);
     const __amdgpu_buffer_rsrc_t ir = make_rsrc(out.y_in ? out.y_in + (size_t)rbase * N : out.c, out.y_in ? bytes : 0u);
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-      const int c = lane + 64 * it, row = c >> 4, ch = c & 15;
+    for (int it = 0; it < 16; ++it) {
+      const int c = lane + 64 * it, row = c >> 3, ch = c & 7;
       const int n = cbase + 8 * ch;
       if (n + 8 > N) continue;
       const uint32_t off = ((uint32_t)row * N + n) * 2;
-      const uint4 v = *reinterpret_cast<const uint4*>(po + row * GOLD + 8 * ch);
+      const uint4 v = *reinterpret_cast<const uint4*>(po + row * OLD + 8 * ch);
       const uint4 y0 = buf_load16(ir, off);
       const uint32_t a4[4] = {v.x, v.y, v.z, v.w}, b4[4] = {y0.x, y0.y, y0.z, y0.w};
       uint32_t o4[4];
@@ -345,10 +336,10 @@ hipError_t launch_gemm(int epi, int M, int N, int K, const void* a, const void* 
   auto A = static_cast<const uint16_t*>(a);
   auto Wt = static_cast<const uint16_t*>(w);
   if (epi == PROJ_GATE)
-    hipLaunchKernelGGL(gemm_nt_bf16<PROJ_GATE>, dim3((unsigned)grid), dim3(256), 0, s, A, Wt, M, N, K, mtiles, ntiles,
+    hipLaunchKernelGGL(gemm_nt_bf16<PROJ_GATE>, dim3((unsigned)grid), dim3(512), 0, s, A, Wt, M, N, K, mtiles, ntiles,
                        out);
   else
-    hipLaunchKernelGGL(gemm_nt_bf16<PROJ_ADD>, dim3((unsigned)grid), dim3(256), 0, s, A, Wt, M, N, K, mtiles, ntiles,
+    hipLaunchKernelGGL(gemm_nt_bf16<PROJ_ADD>, dim3((unsigned)grid), dim3(512), 0, s, A, Wt, M, N, K, mtiles, ntiles,
                        out);
   return hipGetLastError();
 }
