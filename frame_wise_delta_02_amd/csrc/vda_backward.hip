@@ -110,8 +110,9 @@ __global__ __launch_bounds__(256) void pack_states_t(const float* __restrict__ s
 template <int D, bool GAMMA>
 __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ G, const uint16_t* __restrict__ DY,
-    const float* __restrict__ w, const uint4* __restrict__ rstates, uint16_t* __restrict__ DO,
-    uint16_t* __restrict__ DG, int T, int U, int H, int C, int nc, float eps) {
+    const float* __restrict__ w, const uint4* __restrict__ rstates, const uint4* __restrict__ rstates_t,
+    uint16_t* __restrict__ DO, uint16_t* __restrict__ DG, uint16_t* __restrict__ DQ, int T, int U, int H, int C,
+    int nc, float eps) {
   constexpr int NW = 4;              // waves per workgroup
   constexpr int DP = D < 32 ? 32 : D;
   constexpr int HALF = DP / 2;       // outputs per lane
@@ -124,11 +125,10 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
   constexpr int NL = 32 / RPI;       // coalesced accesses per 32-token tile
   constexpr int SWM = (CH < 8 ? CH : 8) - 1;
   constexpr int SWS = CH >= 8 ? 0 : (CH == 4 ? 1 : 2);
-  constexpr int STAGE = (2 * NF + 64 * NW - 1) / (64 * NW);
-  __shared__ uint4 sfrag[2 * NF];
+  constexpr int STAGE = (3 * NF + 64 * NW - 1) / (64 * NW);
+  __shared__ uint4 sfrag[3 * NF];    // S_q hi, S_q lo, S_q^T hi
   __shared__ uint4 xq[NW][32 * CH];  // q rows, then dy rows, then do rows
-  __shared__ uint4 xg[NW][32 * CH];  // gate rows, then dgate rows
-  __shared__ float4 sgam[GAMMA ? DP / 4 : 1];
+  __shared__ uint4 xg[NW][32 * CH];  // gate rows, then dgate rows, then dq rows
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int blk = blockIdx.x;
@@ -138,16 +138,18 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
   const int b = blk / T;
   const int slot = (t == 0 || t == T - 1) ? nc : t / C;
   {
-    const uint4* src = rstates + ((size_t)(b * H + h) * (nc + 1) + slot) * 2 * NF;
+    const size_t sl = (size_t)(b * H + h) * (nc + 1) + slot;
+    const uint4* src = rstates + sl * 2 * NF;
+    const uint4* srt = rstates_t + sl * 2 * NF;  // its hi plane only
     uint4 tmp[STAGE];
 #pragma unroll
-    for (int i = 0; i < STAGE; ++i) tmp[i] = src[min(tid + 64 * NW * i, 2 * NF - 1)];
+    for (int i = 0; i < STAGE; ++i) {
+      const int f = min(tid + 64 * NW * i, 3 * NF - 1);
+      tmp[i] = f < 2 * NF ? src[f] : srt[f - 2 * NF];
+    }
 #pragma unroll
     for (int i = 0; i < STAGE; ++i)
-      if (tid + 64 * NW * i < 2 * NF) sfrag[tid + 64 * NW * i] = tmp[i];
-    if constexpr (GAMMA) {
-      if (tid < DP) reinterpret_cast<float*>(sgam)[tid] = tid < D ? w[tid] : 1.f;
-    }
+      if (tid + 64 * NW * i < 3 * NF) sfrag[tid + 64 * NW * i] = tmp[i];
   }
   __syncthreads();
 
@@ -161,6 +163,7 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
   const __amdgpu_buffer_rsrc_t yr = make_rsrc(DY + fbase, nbytes);
   const __amdgpu_buffer_rsrc_t dor = make_rsrc(DO + fbase, nbytes);
   const __amdgpu_buffer_rsrc_t dgr = make_rsrc(DG + fbase, nbytes);
+  const __amdgpu_buffer_rsrc_t dqr = make_rsrc(DQ + fbase, nbytes);
 
   const int lrow = lane / CH, lch = lane % CH;
   const uint32_t loff = (uint32_t)lrow * rowbytes + 16 * lch;
@@ -233,10 +236,9 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
     auto gains = [&](int i, float (&gm)[8]) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) gm[e] = 1.f;
-      if constexpr (GAMMA) {
-        const float4 a = sgam[(dv0 + 8 * i) / 4], c = sgam[(dv0 + 8 * i) / 4 + 1];
-        gm[0] = a.x; gm[1] = a.y; gm[2] = a.z; gm[3] = a.w;
-        gm[4] = c.x; gm[5] = c.y; gm[6] = c.z; gm[7] = c.w;
+      if constexpr (GAMMA) {  // gains of channels dv0 + 8i .. + 7 (cached reads; LDS is full)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gm[e] = dv0 + 8 * i + e < D ? w[dv0 + 8 * i + e] : 1.f;
       }
     };
     // pass 1: mean over the token's channels of dn * n
@@ -258,7 +260,11 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
     }
     dot += __shfl_xor(dot, 32);
     const float m = dot / (float)D;
-    // pass 2: do and dgate, written over the chunks just read
+    // pass 2: do and dgate, written over the chunks just read; do's chunk i is
+    // also this lane's operand for k-step i of dq = S_q^T do
+    bf16x8 dof[NG];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) dof[i] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
     if (owns) {
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
@@ -279,6 +285,7 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
         }
         XQ[pos(n, dv0 / 8 + i)] = make_uint4(dow[0], dow[1], dow[2], dow[3]);
         XG[pos(n, dv0 / 8 + i)] = make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]);
+        dof[i] = __builtin_bit_cast(bf16x8, make_uint4(dow[0], dow[1], dow[2], dow[3]));
       }
     }
     fence();
@@ -287,6 +294,42 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
       buf_store16(XQ[pos(RPI * i + lrow, lch)], dor, tb + (uint32_t)(RPI * i) * rowbytes);
       buf_store16(XG[pos(RPI * i + lrow, lch)], dgr, tb + (uint32_t)(RPI * i) * rowbytes);
     }
+    fence();
+    // dq = S_q^T do: the B operand of k-step ks is do's channels
+    // (d/2) half + 8 ks .. + 7 of token n, this lane's dof[ks] for d >= 32; at
+    // d = 16 half 0 holds all 16 channels and half 1 takes the upper 8 from it
+    bf16x8 opf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) opf[ks] = dof[ks];
+    if constexpr (D == 16) {
+      const uint4 up = __builtin_bit_cast(uint4, dof[1]);
+      const uint4 got = make_uint4((uint32_t)__shfl_xor((int)up.x, 32), (uint32_t)__shfl_xor((int)up.y, 32),
+                                   (uint32_t)__shfl_xor((int)up.z, 32), (uint32_t)__shfl_xor((int)up.w, 32));
+      if (half == 1) opf[0] = __builtin_bit_cast(bf16x8, got);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 at = __builtin_bit_cast(bf16x8, sfrag[2 * NF + (mt * KS + ks) * 64 + lane]);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, opf[ks], acc[mt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (owns) {
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int m = (8 * i) / 16, r = (8 * i) % 16;
+        XG[pos(n, dv0 / 8 + i)] =
+            make_uint4(pack_bf16x2(acc[m][r], acc[m][r + 1]), pack_bf16x2(acc[m][r + 2], acc[m][r + 3]),
+                       pack_bf16x2(acc[m][r + 4], acc[m][r + 5]), pack_bf16x2(acc[m][r + 6], acc[m][r + 7]));
+      }
+    }
+    fence();
+#pragma unroll
+    for (int i = 0; i < NL; ++i) buf_store16(XG[pos(RPI * i + lrow, lch)], dqr, tb + (uint32_t)(RPI * i) * rowbytes);
     fence();
   };
 
@@ -306,29 +349,29 @@ hipError_t backward_readout_d(const Problem& p, const void* q, const void* gate,
   if (e != hipSuccess) return e;
   const void* do_ = dy;
   if (p.epilogue) {
+    // do, dgate and dq = S_q^T do in one pass
     const unsigned grid = (unsigned)(p.B * p.T * p.H);
+    auto u16 = [](const void* x) { return static_cast<const uint16_t*>(x); };
+    auto w16 = [](void* x) { return static_cast<uint16_t*>(x); };
     if (rms_weight)
-      hipLaunchKernelGGL((readout_bwd_bf16<D, true>), dim3(grid), dim3(256), 0, s,
-                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate),
-                         static_cast<const uint16_t*>(dy), rms_weight, static_cast<const uint4*>(rstates),
-                         static_cast<uint16_t*>(dout), static_cast<uint16_t*>(dgate), p.T, p.U, p.H, p.C, p.nc,
-                         p.rms_eps);
+      hipLaunchKernelGGL((readout_bwd_bf16<D, true>), dim3(grid), dim3(256), 0, s, u16(q), u16(gate), u16(dy),
+                         rms_weight, static_cast<const uint4*>(rstates), static_cast<const uint4*>(rstates_t),
+                         w16(dout), w16(dgate), w16(dq), p.T, p.U, p.H, p.C, p.nc, p.rms_eps);
     else
-      hipLaunchKernelGGL((readout_bwd_bf16<D, false>), dim3(grid), dim3(256), 0, s,
-                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate),
-                         static_cast<const uint16_t*>(dy), rms_weight, static_cast<const uint4*>(rstates),
-                         static_cast<uint16_t*>(dout), static_cast<uint16_t*>(dgate), p.T, p.U, p.H, p.C, p.nc,
-                         p.rms_eps);
+      hipLaunchKernelGGL((readout_bwd_bf16<D, false>), dim3(grid), dim3(256), 0, s, u16(q), u16(gate), u16(dy),
+                         rms_weight, static_cast<const uint4*>(rstates), static_cast<const uint4*>(rstates_t),
+                         w16(dout), w16(dgate), w16(dq), p.T, p.U, p.H, p.C, p.nc, p.rms_eps);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     do_ = dout;
+  } else {
+    // without the epilogue do is dy: dq = S_q^T dy is the forward readout, raw,
+    // on the transposed states
+    Problem raw = p;
+    raw.qnorm = false;
+    e = launch_readout(raw, dy, nullptr, nullptr, rstates_t, dq, s);
+    if (e != hipSuccess) return e;
   }
-  // dq = S_q^T do: the forward readout, raw, on the transposed states
-  Problem raw = p;
-  raw.epilogue = false;
-  raw.qnorm = false;
-  e = launch_readout(raw, do_, nullptr, nullptr, rstates_t, dq, s);
-  if (e != hipSuccess) return e;
   // dS_q(t) = do_t^T q_t for every frame
   return launch_gram_plain(p, q, do_, dsq, s);
 }
@@ -942,11 +985,10 @@ hipError_t backward_gram_d(const Problem& p, const BwdGramBuffers& w, hipStream_
                    w16(w.dbeta_text), 1, p.L, 0, 1, p.T};
   const int nblk0 = p.B * p.T * p.H;
   const unsigned grid = (unsigned)(nblk0 + (p.L > 0 ? p.B * p.H : 0));
-  // d = 128: the planes fill the LDS, one workgroup per CU, so two waves per
-  // SIMD share it and hide each other's latency; narrower heads fit several
-  // workgroups per CU and prefetch in registers instead
-  constexpr int NW = D == 128 ? 8 : 4;
-  hipLaunchKernelGGL((gram_bwd_bf16<D, NW, D != 128>), dim3(grid), dim3(64 * NW), 0, s, a, c, nblk0,
+  // four waves, each prefetching its next tile in registers (eight waves of one
+  // operand set each measured slower at d = 128: 2.06 against 1.84 ms at 768p)
+  constexpr int NW = 4;
+  hipLaunchKernelGGL((gram_bwd_bf16<D, NW, true>), dim3(grid), dim3(64 * NW), 0, s, a, c, nblk0,
                      static_cast<const uint4*>(w.mats), p.H, p.T + 1);
   return hipGetLastError();
 }
