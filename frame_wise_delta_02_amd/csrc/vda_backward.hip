@@ -970,10 +970,216 @@ __global__ __launch_bounds__(64 * NW, 1) void gram_bwd_bf16(GradPart part0, Grad
   }
 }
 
+// The same stage on v_mfma_f32_16x16x32_bf16 for d >= 32: lane (n, q) =
+// (lane % 16, lane / 16) takes token n's channels 32 ks + 8 q .. + 7 as the B
+// operand of k-step ks, so one load covers 16 tokens x 64 contiguous bytes
+// (a quarter of the rows the 32 x 32 layout touches per instruction).  The
+// planes' rows are permuted so that the lane's outputs of m-tiles 2p and
+// 2p + 1 are channels 32 p + 8 q .. + 7, the same channels as its operand of
+// k-step p: the stores are 16 bytes per lane with the loads' pattern, and
+// dbeta needs no other lane's operand.  Each A fragment serves two 16-token
+// groups (32 tokens per tile).
+//   A operand: lane l holds A[l % 16][8 (l / 16) + j]; output: lane l, reg r
+//   holds C[4 (l / 16) + r][l % 16]; row i of m-tile mt is channel
+//   32 (mt / 2) + 8 (i / 4) + 4 (mt % 2) + i % 4.
+template <int D>
+__global__ __launch_bounds__(256) void pack_grad_mats16(const float* __restrict__ dA, const float* __restrict__ dB,
+                                                        uint4* __restrict__ out) {
+  constexpr int MT = D / 16;
+  constexpr int KS = D / 32;
+  constexpr int NF = MT * KS * 64;
+  const float* a = dA + (size_t)blockIdx.x * D * D;
+  const float* bm = dB + (size_t)blockIdx.x * D * D;
+  uint4* o = out + (size_t)blockIdx.x * GP_PLANES * NF;
+  for (int f = threadIdx.x; f < 3 * NF; f += 256) {
+    const int which = f / NF, g = f % NF;
+    const int lane = g % 64, ks = (g / 64) % KS, mt = g / (64 * KS);
+    const int i = lane & 15;
+    const int r = 32 * (mt >> 1) + 8 * (i >> 2) + 4 * (mt & 1) + (i & 3);  // output channel
+    const int c0 = 32 * ks + 8 * (lane >> 4);                                // contraction channels
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      __bf16 h2[2], l2[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int c = c0 + 2 * e + hh;
+        float v;
+        if (which == 0) v = a[(size_t)r * D + c] + a[(size_t)c * D + r];  // G = dA + dA^T
+        else if (which == 1) v = bm[(size_t)r * D + c];                   // dB
+        else v = bm[(size_t)c * D + r];                                   // dB^T
+        split_bf16(v, h2[hh], l2[hh]);
+      }
+      hi[e] = __builtin_bit_cast(uint32_t, bf16x2{h2[0], h2[1]});
+      lo[e] = __builtin_bit_cast(uint32_t, bf16x2{l2[0], l2[1]});
+    }
+    const uint4 H4 = make_uint4(hi[0], hi[1], hi[2], hi[3]), L4 = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    if (which == 0) {
+      o[GP_G_HI * NF + g] = H4;
+      o[GP_G_LO * NF + g] = L4;
+    } else if (which == 1) {
+      o[GP_DB_HI * NF + g] = H4;
+      o[GP_DB_LO * NF + g] = L4;
+    } else {
+      o[GP_DBT_HI * NF + g] = H4;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void gram_bwd16(GradPart part0, GradPart part1, int nblk0,
+                                                     const uint4* __restrict__ mats, int H, int T_slots) {
+  constexpr int NW = 4;
+  constexpr int MT = D / 16;
+  constexpr int KS = D / 32;
+  constexpr int NF = MT * KS * 64;
+  constexpr int NP = GP_PLANES * NF;
+  constexpr int STAGE = (NP + 64 * NW - 1) / (64 * NW);
+  __shared__ uint4 sm[NP];
+
+  const bool second = (int)blockIdx.x >= nblk0;
+  const GradPart g = second ? part1 : part0;
+  int blk = (int)blockIdx.x - (second ? nblk0 : 0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blk % H;
+  blk /= H;
+  const int fi = blk % g.n_frames;
+  const int b = blk / g.n_frames;
+  const int t = g.t_first + fi;
+  {
+    const uint4* src = mats + ((size_t)(b * H + h) * T_slots + (t + g.slot_offset)) * NP;
+    uint4 tmp[STAGE];
+#pragma unroll
+    for (int i = 0; i < STAGE; ++i) tmp[i] = src[min(tid + 64 * NW * i, NP - 1)];
+#pragma unroll
+    for (int i = 0; i < STAGE; ++i)
+      if (tid + 64 * NW * i < NP) sm[tid + 64 * NW * i] = tmp[i];
+  }
+  __syncthreads();
+
+  const int U = g.U;
+  const size_t tok0 = ((size_t)b * g.T_in + t) * (size_t)U;
+  const size_t fbase = (tok0 * H + h) * (size_t)D;
+  const uint32_t rowbytes = (uint32_t)H * D * 2;
+  const uint32_t nbytes = U > 0 ? (uint32_t)(U - 1) * rowbytes + D * 2 : 0;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(g.k + fbase, nbytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(g.v + fbase, nbytes);
+  const __amdgpu_buffer_rsrc_t dkr = make_rsrc(g.dk + fbase, nbytes);
+  const __amdgpu_buffer_rsrc_t dvr = make_rsrc(g.dv + fbase, nbytes);
+  const uint32_t bbytes = U > 0 ? (uint32_t)(U - 1) * H * 2 + 2 : 0;
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(g.beta + tok0 * H + h, bbytes);
+  const __amdgpu_buffer_rsrc_t dbr = make_rsrc(g.dbeta + tok0 * H + h, bbytes);
+
+  const int n = lane & 15, q = lane >> 4;
+  const uint32_t coff = (uint32_t)q * 16;  // bytes of channel 8 q in a row
+  const int ntiles = (U + 31) / 32;
+
+  struct Frag {
+    bf16x8 k[2][KS], v[2][KS];
+    uint16_t beta[2];
+  };
+  auto load = [&](int tile, Frag& f) {
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const uint32_t tok = (uint32_t)(tile * 32 + 16 * gi + n);
+      const uint32_t ro = tok * rowbytes + coff;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) f.k[gi][ks] = __builtin_bit_cast(bf16x8, buf_load16(kr, ro + 64 * ks));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) f.v[gi][ks] = __builtin_bit_cast(bf16x8, buf_load16(vr, ro + 64 * ks));
+      f.beta[gi] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(br, tok * H * 2, 0, 0);
+    }
+  };
+  // acc[gi] += plane w x operand of token group gi, over the k-steps
+  auto chain = [&](f32x4 (&acc)[2][MT], int w, const bf16x8 (&op)[2][KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, sm[w * NF + (mt * KS + ks) * 64 + lane]);
+        acc[0][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, op[0][ks], acc[0][mt], 0, 0, 0);
+        acc[1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, op[1][ks], acc[1][mt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // sum over the lane's channels 32 p + 8 q + j of x_j acc (acc[2p + j / 4][j % 4])
+  auto dotacc = [&](const bf16x8 (&op)[KS], const f32x4 (&acc)[MT]) {
+    float s = 0.f;
+#pragma unroll
+    for (int p = 0; p < KS; ++p) {
+      const uint4 u = __builtin_bit_cast(uint4, op[p]);
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 2 * e;
+        s += bf16_lo(w4[e]) * acc[2 * p + j / 4][j % 4] + bf16_hi(w4[e]) * acc[2 * p + (j + 1) / 4][(j + 1) % 4];
+      }
+    }
+    return s;
+  };
+
+  auto process = [&](int tile, const Frag& f) {
+    f32x4 gk[2][MT], bk[2][MT];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) gk[gi][mt] = bk[gi][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    chain(gk, GP_G_HI, f.k);  // G k
+    chain(gk, GP_G_LO, f.k);
+    chain(bk, GP_DB_HI, f.k);  // dB k
+    chain(bk, GP_DB_LO, f.k);
+    float bt[2];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      bt[gi] = bf16_to_f32(f.beta[gi]);
+      float dot = 0.5f * dotacc(f.k[gi], gk[gi]) + dotacc(f.v[gi], bk[gi]);
+      dot += __shfl_xor(dot, 16);
+      dot += __shfl_xor(dot, 32);
+      if (q == 0)
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pack_bf16x2(dot, 0.f) & 0xffffu), dbr,
+                                              (uint32_t)(tile * 32 + 16 * gi + n) * H * 2, 0, 0);
+    }
+    // out: beta * acc over channels 32 p + 8 q .. + 7 (m-tiles 2p, 2p + 1)
+    auto emit = [&](const f32x4 (&acc)[2][MT], const __amdgpu_buffer_rsrc_t& dst) {
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const uint32_t ro = (uint32_t)(tile * 32 + 16 * gi + n) * rowbytes + coff;
+        const float s = bt[gi];
+#pragma unroll
+        for (int p = 0; p < KS; ++p) {
+          const f32x4 x = acc[gi][2 * p], y = acc[gi][2 * p + 1];
+          buf_store16(make_uint4(pack_bf16x2(s * x[0], s * x[1]), pack_bf16x2(s * x[2], s * x[3]),
+                                 pack_bf16x2(s * y[0], s * y[1]), pack_bf16x2(s * y[2], s * y[3])),
+                      dst, ro + 64 * p);
+        }
+      }
+    };
+    emit(bk, dvr);              // dv = beta dB k
+    chain(gk, GP_DBT_HI, f.v);  // G k + dB^T v
+    emit(gk, dkr);              // dk = beta (G k + dB^T v)
+  };
+
+  // two operand sets: tile i + NW loads while tile i is multiplied
+  Frag fa, fb;
+  int tile = wave;
+  if (tile < ntiles) load(tile, fa);
+  for (; tile < ntiles; tile += 2 * NW) {
+    if (tile + NW < ntiles) load(tile + NW, fb);
+    process(tile, fa);
+    if (tile + NW >= ntiles) break;
+    if (tile + 2 * NW < ntiles) load(tile + 2 * NW, fa);
+    process(tile + NW, fb);
+  }
+}
+
 template <int D>
 hipError_t backward_gram_d(const Problem& p, const BwdGramBuffers& w, hipStream_t s) {
   const unsigned nslots = (unsigned)(p.B * p.H * (p.T + 1));
-  hipLaunchKernelGGL(pack_grad_mats<D>, dim3(nslots), dim3(256), 0, s, w.dA, w.dB, static_cast<uint4*>(w.mats));
+  if constexpr (D >= 32)
+    hipLaunchKernelGGL(pack_grad_mats16<D>, dim3(nslots), dim3(256), 0, s, w.dA, w.dB, static_cast<uint4*>(w.mats));
+  else
+    hipLaunchKernelGGL(pack_grad_mats<D>, dim3(nslots), dim3(256), 0, s, w.dA, w.dB, static_cast<uint4*>(w.mats));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   auto u16 = [](const void* x) { return static_cast<const uint16_t*>(x); };
@@ -985,11 +1191,15 @@ hipError_t backward_gram_d(const Problem& p, const BwdGramBuffers& w, hipStream_
                    w16(w.dbeta_text), 1, p.L, 0, 1, p.T};
   const int nblk0 = p.B * p.T * p.H;
   const unsigned grid = (unsigned)(nblk0 + (p.L > 0 ? p.B * p.H : 0));
-  // four waves, each prefetching its next tile in registers (eight waves of one
-  // operand set each measured slower at d = 128: 2.06 against 1.84 ms at 768p)
-  constexpr int NW = 4;
-  hipLaunchKernelGGL((gram_bwd_bf16<D, NW, true>), dim3(grid), dim3(64 * NW), 0, s, a, c, nblk0,
-                     static_cast<const uint4*>(w.mats), p.H, p.T + 1);
+  // d >= 32: the 16 x 16 x 32 layout (16 rows per load and store instruction);
+  // d = 16: the 32 x 32 x 16 layout.  Four waves, each prefetching its next tile
+  // in registers.
+  if constexpr (D >= 32)
+    hipLaunchKernelGGL(gram_bwd16<D>, dim3(grid), dim3(256), 0, s, a, c, nblk0, static_cast<const uint4*>(w.mats),
+                       p.H, p.T + 1);
+  else
+    hipLaunchKernelGGL((gram_bwd_bf16<D, 4, true>), dim3(grid), dim3(256), 0, s, a, c, nblk0,
+                       static_cast<const uint4*>(w.mats), p.H, p.T + 1);
   return hipGetLastError();
 }
 
