@@ -209,3 +209,52 @@ def test_backward_whole_matches_the_stages():
     for k, t in pairs.items():
         assert torch.equal(r[k], t), k
 
+
+
+def test_backward_768p_two_heads():
+    """The 768p clip (B=1, T=60, 48 x 84 tokens, 24 heads of 128, 256 text
+    tokens) in the configuration bench.py --backward times: the whole backward
+    (binding.backward) on every head, checked against the oracle on heads 0
+    and 13 for every input gradient."""
+    import torch
+    from frame_wise_delta_02_amd import binding as bd
+    w = BASE
+    hs = [0, 13]
+    x = synth.make_inputs(w)
+    dy = _dy(w)
+    G.say("768p forward")
+    out, ws, desc, dev = G.run_forward(x, w, epilogue=True)
+    G.say("768p backward")
+    r = bd.backward(dev["q"], dev["k"], dev["v"], dev["alpha"], dev["beta"], dev["k_text"], dev["v_text"],
+                    dev["beta_text"], dev["gate"], None, G.to_device(dy, w.dtype), ws, grid=(w.grid_h, w.grid_w),
+                    chunk=w.chunk, epilogue=True)
+    torch.cuda.synchronize()
+    got = {k: r[k][..., hs, :] if r[k].dim() == 5 or k in ("dalpha", "dk_text", "dv_text") else r[k][..., hs]
+           for k in ("dq", "dk", "dv", "dgate", "dalpha", "dbeta", "dk_text", "dv_text", "dbeta_text")}
+    got = {k: v.to(torch.float64).cpu().numpy() for k, v in got.items()}
+    del r, out, ws, dev
+    G.say("768p oracle, heads 0 and 13")
+    wide = lambda a: synth.to_f64(a, w.dtype)
+    sub = {"q": wide(x["q"][:, :, :, hs]), "k": wide(x["k"][:, :, :, hs]), "v": wide(x["v"][:, :, :, hs]),
+           "gate": wide(x["gate"][:, :, :, hs]), "beta": wide(x["beta"][:, :, :, hs]),
+           "k_text": wide(x["k_text"][:, :, hs]), "v_text": wide(x["v_text"][:, :, hs]),
+           "beta_text": wide(x["beta_text"][:, :, hs]), "alpha": x["alpha"][:, :, hs].astype(np.float64),
+           "dy": wide(dy[:, :, :, hs])}
+    ref = vda_grad.backward(sub["q"], sub["k"], sub["v"], sub["alpha"], sub["beta"], sub["k_text"], sub["v_text"],
+                            sub["beta_text"], sub["dy"], gate=sub["gate"], chunk=w.chunk)
+    txt = lambda a: a.reshape((a.shape[0], 1) + a.shape[1:] + ((1,) if a.ndim == 3 else ()))
+    fr = slice(1, w.T - 1)
+    errs = {"dq": G.slice_rel_err(got["dq"], ref["dq"]), "dgate": G.slice_rel_err(got["dgate"], ref["dgate"]),
+            "dk": G.slice_rel_err(got["dk"][:, fr], ref["dk"][:, fr]),
+            "dv": G.slice_rel_err(got["dv"][:, fr], ref["dv"][:, fr]),
+            "dbeta": G.slice_rel_err(got["dbeta"][:, fr, ..., None], ref["dbeta"][:, fr, ..., None]),
+            "dalpha": _rel(got["dalpha"][:, fr], ref["dalpha"][:, fr]),
+            "dk_text": G.slice_rel_err(txt(got["dk_text"]), txt(ref["dk_txt"])),
+            "dv_text": G.slice_rel_err(txt(got["dv_text"]), txt(ref["dv_txt"])),
+            "dbeta_text": G.slice_rel_err(txt(got["dbeta_text"]), txt(ref["dbeta_txt"]))}
+    # the anchors' tokens reach no state
+    for k in ("dk", "dv", "dbeta"):
+        assert np.abs(got[k][:, [0, w.T - 1]]).max() == 0, k
+    G.say("768p heads 0, 13: " + " ".join(f"err({k})={v:.3e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= G.TOL[w.dtype], (k, v)
