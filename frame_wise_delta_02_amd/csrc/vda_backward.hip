@@ -470,7 +470,8 @@ struct MatArg {
 //               into the per-frame vector out (dalpha).
 // float32 on v_mfma_f32_16x16x4f32.  K runs in panels of KP, both operands'
 // panels staged in LDS in their source orientation (rows padded by 4 floats),
-// small enough for several workgroups per CU; wave w forms output rows
+// small enough for several workgroups per CU, the next panel loading into
+// registers while the current one is multiplied; wave w forms output rows
 // (d / NWA) w .. of all columns.
 enum { EPI_PLAIN = 0, EPI_DIAG, EPI_ROWDOT };
 
@@ -511,12 +512,15 @@ __global__ __launch_bounds__(256, 2) void gemm_dd(GemmArgs g) {
 #pragma unroll
     for (int nj = 0; nj < NT; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int m0 = 16 * MTW * wave;
-  // stage one panel: n4 float4 of a block `cols` wide at row r0, column c0 of
-  // the source (plus the second source's)
-  auto stage = [&](float* dst, int ld, int cols, const float* s1, const float* s2, bool add, int r0, int c0,
-                   int n4) {
-    constexpr int MAXV = ((NA4 > NB4 ? NA4 : NB4) + 255) / 256;
-    float4 v[MAXV];
+  // one panel of both operands in registers: n4 float4 of a block `cols` wide
+  // at row r0, column c0 of the source, and of the second source where the
+  // pair adds one (added when the panel goes to LDS)
+  constexpr int MAXV = ((NA4 > NB4 ? NA4 : NB4) + 255) / 256;
+  struct Panel {
+    float4 a[MAXV], a2[MAXV], b[MAXV], b2[MAXV];
+  };
+  auto fetch = [&](float4 (&v)[MAXV], float4 (&v2)[MAXV], int cols, const float* s1, const float* s2, bool add,
+                   int r0, int c0, int n4) {
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
       const int f = tid + 256 * i;
@@ -524,52 +528,62 @@ __global__ __launch_bounds__(256, 2) void gemm_dd(GemmArgs g) {
         const int r = f / (cols / 4), c4 = f % (cols / 4);
         const size_t off = (size_t)(r0 + r) * D + c0 + 4 * c4;
         v[i] = *reinterpret_cast<const float4*>(s1 + off);
-        if (add) {
-          const float4 w = *reinterpret_cast<const float4*>(s2 + off);
-          v[i].x += w.x; v[i].y += w.y; v[i].z += w.z; v[i].w += w.w;
-        }
+        if (add) v2[i] = *reinterpret_cast<const float4*>(s2 + off);
       }
     }
+  };
+  auto put = [&](float* dst, int ld, int cols, const float4 (&v)[MAXV], const float4 (&v2)[MAXV], bool add, int n4) {
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) {
       const int f = tid + 256 * i;
       if (f < n4) {
         const int r = f / (cols / 4), c4 = f % (cols / 4);
-        *reinterpret_cast<float4*>(&dst[r * ld + 4 * c4]) = v[i];
+        float4 x = v[i];
+        if (add) {
+          x.x += v2[i].x; x.y += v2[i].y; x.z += v2[i].z; x.w += v2[i].w;
+        }
+        *reinterpret_cast<float4*>(&dst[r * ld + 4 * c4]) = x;
       }
     }
   };
-#pragma unroll 1
-  for (int pr = 0; pr < NPAIR; ++pr) {
+  // panels in order: pair pr, K-offset k0; panel i + 1 loads into registers
+  // while panel i is multiplied
+  constexpr int PPP = D / KP;  // panels per pair
+  auto fetch_panel = [&](int idx, Panel& P) {
+    const int pr = idx / PPP, k0 = (idx % PPP) * KP;
+    const bool adda = ADDA && pr == 0, addb = ADDB && pr == 0;
     const float* A1 = mat(g.a[pr]);
     const float* B1 = mat(g.b[pr]);
-    const bool adda = ADDA && pr == 0, addb = ADDB && pr == 0;
-    const float* A2 = adda ? mat(g.a2) : A1;
-    const float* B2 = addb ? mat(g.b2) : B1;
+    fetch(P.a, P.a2, CA, A1, adda ? mat(g.a2) : A1, adda, TA ? k0 : 0, TA ? 0 : k0, NA4);
+    fetch(P.b, P.b2, CB, B1, addb ? mat(g.b2) : B1, addb, TB ? 0 : k0, TB ? k0 : 0, NB4);
+  };
+  Panel P;
+  fetch_panel(0, P);
 #pragma unroll 1
-    for (int k0 = 0; k0 < D; k0 += KP) {
-      __syncthreads();  // the previous panel has been read
-      stage(sa, LA, CA, A1, A2, adda, TA ? k0 : 0, TA ? 0 : k0, NA4);
-      stage(sb, LB, CB, B1, B2, addb, TB ? 0 : k0, TB ? k0 : 0, NB4);
-      __syncthreads();
-      if (wave < NWA) {
-        // op(A)[m][k] and op(B)[k][n] of the panel (k local)
-        auto opa = [&](int m, int kk) { return TA ? sa[kk * LA + m] : sa[m * LA + kk]; };
-        auto opb = [&](int kk, int n) { return TB ? sb[n * LB + kk] : sb[kk * LB + n]; };
+  for (int idx = 0; idx < NPAIR * PPP; ++idx) {
+    const bool adda = ADDA && idx < PPP, addb = ADDB && idx < PPP;
+    __syncthreads();  // the previous panel has been read
+    put(sa, LA, CA, P.a, P.a2, adda, NA4);
+    put(sb, LB, CB, P.b, P.b2, addb, NB4);
+    __syncthreads();
+    if (idx + 1 < NPAIR * PPP) fetch_panel(idx + 1, P);
+    if (wave < NWA) {
+      // op(A)[m][k] and op(B)[k][n] of the panel (k local)
+      auto opa = [&](int m, int kk) { return TA ? sa[kk * LA + m] : sa[m * LA + kk]; };
+      auto opb = [&](int kk, int n) { return TB ? sb[n * LB + kk] : sb[kk * LB + n]; };
 #pragma unroll 2
-        for (int k4 = 0; k4 < KP / 4; ++k4) {
-          const int kk = 4 * k4 + (lane >> 4);
-          float av[MTW], bv[NT];
+      for (int k4 = 0; k4 < KP / 4; ++k4) {
+        const int kk = 4 * k4 + (lane >> 4);
+        float av[MTW], bv[NT];
 #pragma unroll
-          for (int mi = 0; mi < MTW; ++mi) av[mi] = opa(m0 + 16 * mi + (lane & 15), kk);
+        for (int mi = 0; mi < MTW; ++mi) av[mi] = opa(m0 + 16 * mi + (lane & 15), kk);
 #pragma unroll
-          for (int nj = 0; nj < NT; ++nj) bv[nj] = opb(kk, 16 * nj + (lane & 15));
+        for (int nj = 0; nj < NT; ++nj) bv[nj] = opb(kk, 16 * nj + (lane & 15));
 #pragma unroll
-          for (int mi = 0; mi < MTW; ++mi)
+        for (int mi = 0; mi < MTW; ++mi)
 #pragma unroll
-            for (int nj = 0; nj < NT; ++nj)
-              acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi], bv[nj], acc[mi][nj], 0, 0, 0);
-        }
+          for (int nj = 0; nj < NT; ++nj)
+            acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[mi], bv[nj], acc[mi][nj], 0, 0, 0);
       }
     }
   }
