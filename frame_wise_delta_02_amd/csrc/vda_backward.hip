@@ -1002,8 +1002,36 @@ __global__ __launch_bounds__(256) void pack_grad_mats16(const float* __restrict_
   constexpr int MT = D / 16;
   constexpr int KS = D / 32;
   constexpr int NF = MT * KS * 64;
-  const float* a = dA + (size_t)blockIdx.x * D * D;
-  const float* bm = dB + (size_t)blockIdx.x * D * D;
+  constexpr int LD = D + 1;  // odd row stride: the transposed reads hit distinct banks
+  // the slot's dA and dB through LDS with coalesced loads (the fragments read
+  // both orientations)
+  __shared__ float sa[D * LD], sb[D * LD];
+  {
+    const float4* ga = reinterpret_cast<const float4*>(dA + (size_t)blockIdx.x * D * D);
+    const float4* gb = reinterpret_cast<const float4*>(dB + (size_t)blockIdx.x * D * D);
+    constexpr int N4 = D * D / 4, PER = (N4 + 255) / 256, BATCH = PER < 8 ? PER : 8;
+    for (int i0 = 0; i0 < PER; i0 += BATCH) {
+      float4 va[BATCH], vb[BATCH];
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const int i = threadIdx.x + 256 * (i0 + j);
+        va[j] = i < N4 ? ga[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        vb[j] = i < N4 ? gb[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const int i = threadIdx.x + 256 * (i0 + j);
+        if (i < N4) {
+          const int r = (4 * i) / D, c = (4 * i) % D;
+          sa[r * LD + c] = va[j].x; sa[r * LD + c + 1] = va[j].y; sa[r * LD + c + 2] = va[j].z; sa[r * LD + c + 3] = va[j].w;
+          sb[r * LD + c] = vb[j].x; sb[r * LD + c + 1] = vb[j].y; sb[r * LD + c + 2] = vb[j].z; sb[r * LD + c + 3] = vb[j].w;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const float* a = sa;
+  const float* bm = sb;
   uint4* o = out + (size_t)blockIdx.x * GP_PLANES * NF;
   for (int f = threadIdx.x; f < 3 * NF; f += 256) {
     const int which = f / NF, g = f % NF;
@@ -1019,9 +1047,9 @@ __global__ __launch_bounds__(256) void pack_grad_mats16(const float* __restrict_
       for (int hh = 0; hh < 2; ++hh) {
         const int c = c0 + 2 * e + hh;
         float v;
-        if (which == 0) v = a[(size_t)r * D + c] + a[(size_t)c * D + r];  // G = dA + dA^T
-        else if (which == 1) v = bm[(size_t)r * D + c];                   // dB
-        else v = bm[(size_t)c * D + r];                                   // dB^T
+        if (which == 0) v = a[r * LD + c] + a[c * LD + r];  // G = dA + dA^T
+        else if (which == 1) v = bm[r * LD + c];                // dB
+        else v = bm[c * LD + r];                                // dB^T
         split_bf16(v, h2[hh], l2[hh]);
       }
       hi[e] = __builtin_bit_cast(uint32_t, bf16x2{h2[0], h2[1]});
