@@ -126,3 +126,36 @@ def test_768p_sampled():
     errs["alpha_abs"] = float(np.abs(a_gpu - a_ref).max())
     G.say("768p: " + " ".join(f"err({k})={v:.3e}" for k, v in errs.items()))
     assert errs["gate"] <= 2e-2 and errs["beta"] <= 2e-2 and errs["y"] <= 2e-2 and errs["alpha_abs"] <= 1e-5, errs
+
+
+def test_layer_chain():
+    """The three entry points composed as a layer uses them: gates from x, the
+    forward pass on those gates (with the epilogue), then the output projection
+    adding Y_in, against the oracle's chain in float64 (the GPU's gates enter
+    its forward rounded to bfloat16, so the tolerance covers that too)."""
+    import torch
+    import oracle
+    from frame_wise_delta_02_amd import binding as bd
+    w = BASE.scaled(name="layer", B=1, T=11, grid_h=4, grid_w=6, H=2, d=64, L=8)
+    dm = 160
+    x = synth.make_inputs(w)
+    p = synth.make_adjacent_inputs(w, dm)
+    grid = (w.grid_h, w.grid_w)
+    gate, beta, alpha = bd.gates(_dev(p["x"]), _dev(p["w_gb"]), _dev(p["w_alpha"]), heads=w.H, d=w.d, grid=grid,
+                                 chunk=w.chunk)
+    d = {k: _dev(x[k]) for k in ("q", "k", "v", "k_text", "v_text", "beta_text")}
+    o = bd.forward(d["q"], d["k"], d["v"], alpha, beta, d["k_text"], d["v_text"], d["beta_text"], gate, None,
+                   grid=grid, chunk=w.chunk, epilogue=True)
+    y = bd.out_proj(o, _dev(p["w_o"]), _dev(p["y_in"]), grid=grid, chunk=w.chunk)
+    torch.cuda.synchronize()
+    wg = _f64(p["w_gb"])
+    HD = w.H * w.d
+    g_ref, b_ref, a_ref = adj.gate_proj(_f64(p["x"]), wg[:HD], wg[HD:], _f64(p["w_alpha"]), w.H, w.d)
+    f = {k: _f64(x[k]) for k in ("q", "k", "v", "k_text", "v_text", "beta_text")}
+    fw = oracle.forward(f["q"], f["k"], f["v"], a_ref, b_ref, f["k_text"], f["v_text"], f["beta_text"], gate=g_ref,
+                        chunk=w.chunk)
+    y_ref = adj.out_proj(fw["y"], _f64(p["w_o"]), _f64(p["y_in"]))
+    errs = {"o": G.slice_rel_err(G.to_host_f64(o), fw["y"]),
+            "y": G.slice_rel_err(_slices(G.to_host_f64(y)), _slices(y_ref))}
+    G.say("layer chain: " + " ".join(f"err({k})={v:.3e}" for k, v in errs.items()))
+    assert errs["o"] <= 2e-2 and errs["y"] <= 2e-2, errs
