@@ -32,6 +32,8 @@ CASES = {
     "adj_ragged": (BASE.scaled(name="adj_ragged", B=2, T=5, grid_h=6, grid_w=11, H=2, d=64, L=0), 320),
     # narrow heads, beta columns inside the first tile
     "adj_d16": (BASE.scaled(name="adj_d16", B=1, T=4, grid_h=4, grid_w=4, H=3, d=16, L=0), 64),
+    # one token per frame, the smallest model width (a single partial K-panel)
+    "adj_tiny": (BASE.scaled(name="adj_tiny", B=1, T=2, grid_h=1, grid_w=1, H=1, d=16, L=0), 8),
 }
 
 

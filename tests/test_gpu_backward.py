@@ -33,6 +33,7 @@ CASES = {
     "bwd_16": dict(w=BASE.scaled(name="bwd_16", d=16, H=2, T=9, grid_h=4, grid_w=4, L=4), gain=True),
     "bwd_B2_chunk3": dict(w=BASE.scaled(name="bwd_B2_chunk3", B=2, H=2, T=14, grid_h=4, grid_w=6, L=4, chunk=3)),
     "bwd_T2": dict(w=BASE.scaled(name="bwd_T2", H=2, T=2, grid_h=4, grid_w=8, L=16)),
+    "bwd_T1": dict(w=BASE.scaled(name="bwd_T1", d=64, H=2, T=1, grid_h=3, grid_w=5, L=8)),
     # narrow heads with records in use (bwd_16 and bwd_128_gain have too few
     # chunks for any record to be read), and a clip without text tokens
     "bwd_16_chunk3": dict(w=BASE.scaled(name="bwd_16_chunk3", d=16, H=2, T=17, grid_h=4, grid_w=5, L=4, chunk=3)),
