@@ -123,10 +123,13 @@ __global__ __launch_bounds__(512, 1) void gemm_nt_bf16(const uint16_t* __restric
       for (int j = 0; j < 2; ++j)
         wf[j] = *reinterpret_cast<const bf16x8*>(pw + (wrow + 32 * j) * GLD + 16 * s + kq);
       gload(la, lw, k0_load, s, s + 1);
+      // the SIMD's other wave yields to this one while its products issue
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wf[j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
       lstore(sa, sw, buf ^ 1, s, s + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
