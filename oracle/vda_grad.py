@@ -44,13 +44,18 @@ def _keep(x):
 
 
 def forward_head_t(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, gate=None, gamma=None,
-                   chunk=5, rms_eps=1e-6, bridge=False, keep=None):
+                   chunk=5, rms_eps=1e-6, bridge=False, keep=None, query_l2=None):
     """``vda.forward_head`` followed by ``vda.epilogue``, in torch ops.
 
     Same shapes as ``vda.forward_head``; gate [T, U, d_v] (None: return o only),
     gamma [d_v] or None.  ``keep`` (a dict) receives the intermediate tensors
     with ``retain_grad`` set, for reading their adjoints after ``backward``.
+    ``query_l2`` (an epsilon, or None) takes q raw and normalises each token
+    first, q / sqrt(sum q^2 + eps) (reading R8, the forward's fused query
+    normalisation).
     """
+    if query_l2 is not None:
+        q = q / torch.sqrt(torch.sum(q * q, dim=-1, keepdim=True) + query_l2)
     T, U, dk = k.shape
     dv = v.shape[-1]
     C = chunk
@@ -148,7 +153,7 @@ def forward_head_t(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, gate=None, gamm
 
 
 def backward_head(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, dy, gate=None, gamma=None,
-                  chunk=5, rms_eps=1e-6, bridge=False):
+                  chunk=5, rms_eps=1e-6, bridge=False, query_l2=None):
     """Gradients of sum(dy * y) (or sum(dy * o) without a gate) for one head.
 
     Inputs as ``forward_head_t`` (numpy float64); dy has the output's shape.
@@ -163,7 +168,8 @@ def backward_head(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, dy, gate=None, g
     gm = None if gamma is None else _t(gamma).requires_grad_(True)
     keep = {}
     out = forward_head_t(xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], xs["k_txt"], xs["v_txt"],
-                         xs["beta_txt"], g, gm, chunk=chunk, rms_eps=rms_eps, bridge=bridge, keep=keep)
+                         xs["beta_txt"], g, gm, chunk=chunk, rms_eps=rms_eps, bridge=bridge, keep=keep,
+                         query_l2=query_l2)
     (out * _t(dy)).sum().backward()
 
     def grad_of(x, shape):
@@ -190,7 +196,7 @@ def backward_head(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, dy, gate=None, g
 
 
 def backward(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, dy, gate=None, rms_weight=None,
-             chunk=5, rms_eps=1e-6, heads=None, bridge=False):
+             chunk=5, rms_eps=1e-6, heads=None, bridge=False, query_l2=None):
     """``backward_head`` over every batch element and head (or the listed heads).
 
     Layouts as ``vda.forward``.  Returns the input gradients in the input
@@ -211,7 +217,7 @@ def backward(q, k, v, alpha, beta, k_txt, v_txt, beta_txt, dy, gate=None, rms_we
             r = backward_head(q[b, :, :, h], k[b, :, :, h], v[b, :, :, h], alpha[b, :, h], beta[b, :, :, h],
                               k_txt[b, :, h], v_txt[b, :, h], beta_txt[b, :, h], dy[b, :, :, h],
                               None if gate is None else gate[b, :, :, h], rms_weight, chunk=chunk,
-                              rms_eps=rms_eps, bridge=bridge)
+                              rms_eps=rms_eps, bridge=bridge, query_l2=query_l2)
             out["dq"][b, :, :, h] = r["dq"]
             out["dk"][b, :, :, h] = r["dk"]
             out["dv"][b, :, :, h] = r["dv"]

@@ -36,6 +36,7 @@ def _inputs(seed, T=12, U=3, d=4, L=2, C=3):
 
 CASES = {
     "T12_C3": dict(seed=1),
+    "T12_C3_query_l2": dict(seed=7, query_l2=True),
     "T12_C3_bridge": dict(seed=2, bridge=True),
     "T7_C2_no_text": dict(seed=3, T=7, C=2, L=0),
     "T11_C5_ragged": dict(seed=4, T=11, C=5, U=2),
@@ -44,15 +45,25 @@ CASES = {
 }
 
 
+QL2_EPS = 1e-6
+
+
 def _case(name):
     kw = dict(CASES[name])
     bridge = kw.pop("bridge", False)
+    ql2 = kw.pop("query_l2", False)
     x = _inputs(**kw)
+    if ql2:  # raw queries of uneven length, normalised inside the forward
+        x["q"] = x["q"] * np.random.default_rng(kw["seed"] + 100).uniform(0.3, 3.0, x["q"].shape[:-1] + (1,))
+    x["query_l2"] = QL2_EPS if ql2 else None
     return x, bridge
 
 
 def _numpy_out(x, bridge, gate=True, gamma=True):
-    r = vda.forward_head(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["k_txt"], x["v_txt"],
+    q = x["q"]
+    if x.get("query_l2") is not None:  # the forward's fused query normalisation (R8), in numpy
+        q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + x["query_l2"])
+    r = vda.forward_head(q, x["k"], x["v"], x["alpha"], x["beta"], x["k_txt"], x["v_txt"],
                          x["beta_txt"], chunk=x["chunk"], bridge=bridge)
     if not gate:
         return r["o"]
@@ -66,9 +77,10 @@ def test_g1_transcription_matches_numpy(name):
     t = {k: torch.as_tensor(v) for k, v in x.items() if isinstance(v, np.ndarray)}
     with torch.no_grad():
         o = vg.forward_head_t(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["k_txt"], t["v_txt"],
-                              t["beta_txt"], chunk=x["chunk"], bridge=bridge).numpy()
+                              t["beta_txt"], chunk=x["chunk"], bridge=bridge, query_l2=x["query_l2"]).numpy()
         y = vg.forward_head_t(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["k_txt"], t["v_txt"],
-                              t["beta_txt"], t["gate"], t["gamma"], chunk=x["chunk"], bridge=bridge).numpy()
+                              t["beta_txt"], t["gate"], t["gamma"], chunk=x["chunk"], bridge=bridge,
+                              query_l2=x["query_l2"]).numpy()
     o_ref = _numpy_out(x, bridge, gate=False)
     y_ref = _numpy_out(x, bridge)
     assert np.abs(o - o_ref).max() <= 1e-12 * max(1.0, np.abs(o_ref).max())
@@ -85,7 +97,7 @@ def test_g2_gradients_match_finite_differences(name, gate):
     x, bridge = _case(name)
     g = vg.backward_head(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["k_txt"], x["v_txt"], x["beta_txt"],
                          x["dy"], x["gate"] if gate else None, x["gamma"] if gate else None,
-                         chunk=x["chunk"], bridge=bridge)
+                         chunk=x["chunk"], bridge=bridge, query_l2=x["query_l2"])
     rng = np.random.default_rng(99)
     h = 1e-5
     for inp, gname in GRAD_OF.items():
