@@ -251,7 +251,7 @@ def backward_layout(desc: Desc) -> BackwardLayout:
 
 
 def backward_readout(q, gate, rms_weight, alpha, dy, fwd_workspace, *, grid, n_text=0, chunk=5, epilogue=True,
-                     bridge=False, rms_eps=1e-6, dq=None, dgate=None, workspace=None):
+                     bridge=False, rms_eps=1e-6, dq=None, dgate=None, workspace=None, query_l2=False, l2_eps=1e-6):
     """First stage of the backward pass (vdn_vda_backward_readout): returns
     (dq, dgate or None, workspace); the workspace holds do and dS_q at the
     offsets of ``backward_layout``.  ``fwd_workspace`` is the forward's, for the
@@ -263,7 +263,8 @@ def backward_readout(q, gate, rms_weight, alpha, dy, fwd_workspace, *, grid, n_t
                     ("fwd_workspace", fwd_workspace), ("dq", dq), ("dgate", dgate), ("workspace", workspace)):
         _check(x, name, dev)
     desc = make_desc(B, H, T, grid[0], grid[1], d, n_text, chunk, _dtype_of(q), epilogue, rms_eps=rms_eps,
-                     flags=(VDN_VDA_EPILOGUE if epilogue else 0) | (VDN_VDA_DECAY_BRIDGE if bridge else 0))
+                     l2_eps=l2_eps, flags=(VDN_VDA_EPILOGUE if epilogue else 0) | (VDN_VDA_DECAY_BRIDGE if bridge else 0)
+                     | (VDN_VDA_QUERY_L2 if query_l2 else 0))
     if dq is None:
         dq = torch.empty_like(q)
     if epilogue and dgate is None:
@@ -326,15 +327,17 @@ def backward_gram(k, v, beta, k_text, v_text, beta_text, workspace, *, grid, chu
 
 
 def backward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, dy, fwd_workspace, *, grid,
-             chunk=5, epilogue=True, rms_eps=1e-6, workspace=None):
+             chunk=5, epilogue=True, rms_eps=1e-6, workspace=None, query_l2=False, l2_eps=1e-6):
     """The whole backward pass (the three stages in order) after a forward
-    that left ``fwd_workspace``; returns a dict of input gradients dq, dk, dv,
+    that left ``fwd_workspace`` (with ``query_l2`` the forward took the raw
+    query and dq is its gradient); returns a dict of input gradients dq, dk, dv,
     dalpha, dbeta, dk_text, dv_text, dbeta_text, dgate (the last four None
     where absent) and the workspace."""
     B, T, U, H, d = q.shape
     L = 0 if k_text is None else k_text.shape[1]
     dq, dgate, workspace = backward_readout(q, gate, rms_weight, alpha, dy, fwd_workspace, grid=grid, n_text=L,
-                                            chunk=chunk, epilogue=epilogue, rms_eps=rms_eps, workspace=workspace)
+                                            chunk=chunk, epilogue=epilogue, rms_eps=rms_eps, workspace=workspace,
+                                            query_l2=query_l2, l2_eps=l2_eps)
     dalpha = backward_scan(alpha, fwd_workspace, workspace, shape=(B, T, H, d), grid=grid, n_text=L,
                            chunk=chunk, dtype=_dtype_of(q), epilogue=epilogue)
     dk, dv, dbeta, dkt, dvt, dbt = backward_gram(k, v, beta, k_text, v_text, beta_text, workspace, grid=grid,

@@ -107,12 +107,12 @@ __global__ __launch_bounds__(256) void pack_states_t(const float* __restrict__ s
 // Back through the epilogue: o recomputed as the forward readout computes it,
 // then dgate and do per token (see the file comment).  4 waves, each streaming
 // 32-token tiles; per wave two LDS tiles (q then dy then do; gate then dgate).
-template <int D, bool GAMMA>
+template <int D, bool GAMMA, bool QN>
 __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ G, const uint16_t* __restrict__ DY,
     const float* __restrict__ w, const uint4* __restrict__ rstates, const uint4* __restrict__ rstates_t,
     uint16_t* __restrict__ DO, uint16_t* __restrict__ DG, uint16_t* __restrict__ DQ, int T, int U, int H, int C,
-    int nc, float eps) {
+    int nc, float eps, float l2eps) {
   constexpr int NW = 4;              // waves per workgroup
   constexpr int DP = D < 32 ? 32 : D;
   constexpr int HALF = DP / 2;       // outputs per lane
@@ -205,6 +205,24 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
     for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, XQ[pos(n, (CH / 2) * half + ks)]);
     fence();
     fetch_q(tile + NW, qv);
+    // raw query (fused L2 normalisation): 1 / |q| of token n; 1 otherwise
+    float qscale = 1.f;
+    if constexpr (QN) {
+      float qs = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 u = __builtin_bit_cast(uint4, qf[ks]);
+        const uint32_t q4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = bf16_lo(q4[e]), c = bf16_hi(q4[e]);
+          qs += a * a;
+          qs += c * c;
+        }
+      }
+      qs += __shfl_xor(qs, 32);
+      qscale = __builtin_amdgcn_rsqf(qs + l2eps);
+    }
     f32x16 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{0.f};
@@ -225,7 +243,13 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
 #pragma unroll
     for (int i = 0; i < NL; ++i) XQ[pos(RPI * i + lrow, lch)] = yv[i];
     fence();
-    // lane holds o[dv0 + 16 mt + r] of token n in acc[mt][r]
+    // lane holds o[dv0 + 16 mt + r] of token n in acc[mt][r] (o = S_q q / |q| for a raw query)
+    if constexpr (QN) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mt][r] *= qscale;
+    }
     float ss = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -283,9 +307,20 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
           dow[e] = pack_bf16x2(rinv * (dn0 - n0 * m), rinv * (dn1 - n1 * m));
           dgw[e] = pack_bf16x2(dn0 * n0 * (1.f - s0), dn1 * n1 * (1.f - s1));
         }
+        dof[i] = __builtin_bit_cast(bf16x8, make_uint4(dow[0], dow[1], dow[2], dow[3]));
+        if constexpr (QN) {
+          // the state's adjoint pass reads do / |q| against the raw query
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j0 = 8 * i + 2 * e, j1 = j0 + 1;
+            const float n0 = acc[j0 / 16][j0 % 16] * rinv, n1 = acc[j1 / 16][j1 % 16] * rinv;
+            const float s0 = sigmoid(bf16_lo(g4[e])), s1 = sigmoid(bf16_hi(g4[e]));
+            const float dn0 = bf16_lo(y4[e]) * gm[2 * e] * s0, dn1 = bf16_hi(y4[e]) * gm[2 * e + 1] * s1;
+            dow[e] = pack_bf16x2(qscale * rinv * (dn0 - n0 * m), qscale * rinv * (dn1 - n1 * m));
+          }
+        }
         XQ[pos(n, dv0 / 8 + i)] = make_uint4(dow[0], dow[1], dow[2], dow[3]);
         XG[pos(n, dv0 / 8 + i)] = make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]);
-        dof[i] = __builtin_bit_cast(bf16x8, make_uint4(dow[0], dow[1], dow[2], dow[3]));
       }
     }
     fence();
@@ -317,6 +352,36 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(at, opf[ks], acc[mt], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (QN) {
+      // back through q / |q|: dq = (dq_n - q_n (q_n . dq_n)) / |q| with q_n = q / |q|;
+      // the raw query's chunks of this lane's channels come again from L2
+      uint4 qc[NG];
+      const uint32_t ro = (uint32_t)(tile * 32 + n) * rowbytes + (uint32_t)dv0 * 2;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) qc[i] = owns ? buf_load16(qr, ro + 16 * i) : make_uint4(0, 0, 0, 0);
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const uint32_t q4[4] = {qc[i].x, qc[i].y, qc[i].z, qc[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j0 = 8 * i + 2 * e, j1 = j0 + 1;
+          dot += bf16_lo(q4[e]) * acc[j0 / 16][j0 % 16] + bf16_hi(q4[e]) * acc[j1 / 16][j1 % 16];
+        }
+      }
+      dot += __shfl_xor(dot, 32);
+      const float c3 = qscale * qscale * qscale * dot;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const uint32_t q4[4] = {qc[i].x, qc[i].y, qc[i].z, qc[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j0 = 8 * i + 2 * e, j1 = j0 + 1;
+          acc[j0 / 16][j0 % 16] = qscale * acc[j0 / 16][j0 % 16] - c3 * bf16_lo(q4[e]);
+          acc[j1 / 16][j1 % 16] = qscale * acc[j1 / 16][j1 % 16] - c3 * bf16_hi(q4[e]);
+        }
+      }
     }
     if (owns) {
 #pragma unroll
@@ -353,14 +418,18 @@ hipError_t backward_readout_d(const Problem& p, const void* q, const void* gate,
     const unsigned grid = (unsigned)(p.B * p.T * p.H);
     auto u16 = [](const void* x) { return static_cast<const uint16_t*>(x); };
     auto w16 = [](void* x) { return static_cast<uint16_t*>(x); };
+    auto launch = [&](auto gamma, auto qn) {
+      hipLaunchKernelGGL((readout_bwd_bf16<D, decltype(gamma)::value, decltype(qn)::value>), dim3(grid), dim3(256), 0,
+                         s, u16(q), u16(gate), u16(dy), rms_weight, static_cast<const uint4*>(rstates),
+                         static_cast<const uint4*>(rstates_t), w16(dout), w16(dgate), w16(dq), p.T, p.U, p.H, p.C,
+                         p.nc, p.rms_eps, p.l2_eps);
+    };
+    using Y = std::true_type;
+    using N = std::false_type;
     if (rms_weight)
-      hipLaunchKernelGGL((readout_bwd_bf16<D, true>), dim3(grid), dim3(256), 0, s, u16(q), u16(gate), u16(dy),
-                         rms_weight, static_cast<const uint4*>(rstates), static_cast<const uint4*>(rstates_t),
-                         w16(dout), w16(dgate), w16(dq), p.T, p.U, p.H, p.C, p.nc, p.rms_eps);
+      p.qnorm ? launch(Y(), Y()) : launch(Y(), N());
     else
-      hipLaunchKernelGGL((readout_bwd_bf16<D, false>), dim3(grid), dim3(256), 0, s, u16(q), u16(gate), u16(dy),
-                         rms_weight, static_cast<const uint4*>(rstates), static_cast<const uint4*>(rstates_t),
-                         w16(dout), w16(dgate), w16(dq), p.T, p.U, p.H, p.C, p.nc, p.rms_eps);
+      p.qnorm ? launch(N(), Y()) : launch(N(), N());
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     do_ = dout;

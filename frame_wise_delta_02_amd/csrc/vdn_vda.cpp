@@ -327,7 +327,8 @@ vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d, const void* q, const 
   const vdn_status st = check(d);
   if (st != VDN_OK) return st;
   const bool epi = (d->flags & VDN_VDA_EPILOGUE) != 0;
-  if (d->dtype != VDN_BF16 || (d->flags & VDN_VDA_QUERY_L2)) return VDN_ERR_UNSUPPORTED;
+  // the raw query's gradient is formed with the epilogue's backward only
+  if (d->dtype != VDN_BF16 || ((d->flags & VDN_VDA_QUERY_L2) && !epi)) return VDN_ERR_UNSUPPORTED;
   if (!q || !alpha || !dy || !dq || !fwd_workspace) return VDN_ERR_INVALID_ARG;
   if (epi && (!gate || !dgate)) return VDN_ERR_INVALID_ARG;
   const Problem p = problem(d);
@@ -355,7 +356,7 @@ vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha, cons
                                  size_t workspace_bytes, hipStream_t stream) {
   const vdn_status st = check(d);
   if (st != VDN_OK) return st;
-  if (d->dtype != VDN_BF16 || (d->flags & (VDN_VDA_QUERY_L2 | VDN_VDA_DECAY_BRIDGE))) return VDN_ERR_UNSUPPORTED;
+  if (d->dtype != VDN_BF16 || (d->flags & VDN_VDA_DECAY_BRIDGE)) return VDN_ERR_UNSUPPORTED;
   if (!alpha || !fwd_workspace || !dalpha) return VDN_ERR_INVALID_ARG;
   // every frame's state is recorded per head through one buffer descriptor
   if ((double)(d->T + 2) * d->d_k * d->d_v * 4.0 >= 2147483648.0) return VDN_ERR_INVALID_ARG;
@@ -398,7 +399,7 @@ vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const voi
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const vdn_status st = check(d);
   if (st != VDN_OK) return st;
-  if (d->dtype != VDN_BF16 || (d->flags & (VDN_VDA_QUERY_L2 | VDN_VDA_DECAY_BRIDGE))) return VDN_ERR_UNSUPPORTED;
+  if (d->dtype != VDN_BF16 || (d->flags & VDN_VDA_DECAY_BRIDGE)) return VDN_ERR_UNSUPPORTED;
   if (!k || !v || !beta || !dk || !dv || !dbeta) return VDN_ERR_INVALID_ARG;
   const bool text = d->n_text > 0;
   if (text && (!k_text || !v_text || !beta_text || !dk_text || !dv_text || !dbeta_text)) return VDN_ERR_INVALID_ARG;

@@ -225,8 +225,9 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d,
  * reports,
  *   d_out     [B, T, U, H, d_v] bfloat16: do, the readout's adjoint
  *             (= rms_weight * s * dy * r - n * r * mean(rms_weight * s * dy * n),
- *             r = 1 / sqrt(mean o^2 + rms_eps)); written with VDN_VDA_EPILOGUE
- *             only -- without it do is dy itself and dy is read in its place;
+ *             r = 1 / sqrt(mean o^2 + rms_eps)), divided by |q| per token with
+ *             VDN_VDA_QUERY_L2; written with VDN_VDA_EPILOGUE only -- without it
+ *             do is dy itself and dy is read in its place;
  *   d_state_q [B, H, T, d_v, d_k] float32: sum over the frame's tokens of
  *             do q^T, the adjoint of S_q(t), for every frame (the next stage
  *             turns these into the adjoints of the records and of S_T);
@@ -236,8 +237,12 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d,
  * fwd_workspace must hold what vdn_vda_forward left there for the same
  * descriptor and inputs (q, k, v, alpha, beta, text, gate, rms_weight); alpha
  * is read for the decay bridge.  dy, dq, dgate are device buffers owned by the
- * caller; dq and dgate must not alias any input.  Supported: VDN_BF16 without
- * VDN_VDA_QUERY_L2 (else VDN_ERR_UNSUPPORTED).  Errors: VDN_ERR_INVALID_ARG
+ * caller; dq and dgate must not alias any input.  With VDN_VDA_QUERY_L2 (the
+ * forward normalised the raw query, q_n = q / sqrt(sum q^2 + l2_eps)) dq is the
+ * gradient of the raw query, (dq_n - q_n (q_n . dq_n)) / |q| with dq_n = S_q^T do,
+ * and d_out holds do / |q| per token (so that d_state_q = sum d_out q^T reads
+ * the raw query).  Supported: VDN_BF16, and VDN_VDA_QUERY_L2 only with
+ * VDN_VDA_EPILOGUE (else VDN_ERR_UNSUPPORTED).  Errors: VDN_ERR_INVALID_ARG
  * (NULL pointer, gate or dgate missing with the epilogue, aliasing),
  * VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE (either workspace too small or NULL),
  * VDN_ERR_ALIGNMENT (16 B for tensors, 256 B for workspaces), VDN_ERR_HIP.
@@ -291,8 +296,8 @@ vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d,
  * Y_s = S_prev Diag(alpha_s) + B_s, and lambda <- dY Diag(alpha_s) for the state
  * before; then dA_s = -P_s d(P_s) P_s (P_s = (I + A_s)^{-1}, [VDN-summary]
  * "어떻게 쓰나").  The text frame S_T = B_T P_T takes lambda = the adjoint of
- * S_T.  Supported: VDN_BF16 without VDN_VDA_QUERY_L2 or VDN_VDA_DECAY_BRIDGE
- * (else VDN_ERR_UNSUPPORTED); (T + 2) d_k d_v 4 < 2^31.  Errors as
+ * S_T.  Supported: VDN_BF16 without VDN_VDA_DECAY_BRIDGE (else
+ * VDN_ERR_UNSUPPORTED); (T + 2) d_k d_v 4 < 2^31.  Errors as
  * vdn_vda_backward_readout.  Asynchronous on `stream`.
  */
 vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha,
@@ -315,8 +320,8 @@ vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha,
  * hi + lo pairs (dbeta sums d^2 products that largely cancel), dB_t^T (dk
  * only) rounded once to bfloat16.  k, v, beta and the text inputs are
  * those the forward pass read.  Outputs must overlap neither each other, the
- * inputs nor the workspace.  Supported: VDN_BF16 without VDN_VDA_QUERY_L2 or
- * VDN_VDA_DECAY_BRIDGE (else VDN_ERR_UNSUPPORTED).  Errors: VDN_ERR_INVALID_ARG
+ * inputs nor the workspace.  Supported: VDN_BF16 without VDN_VDA_DECAY_BRIDGE
+ * (else VDN_ERR_UNSUPPORTED).  Errors: VDN_ERR_INVALID_ARG
  * (NULL pointer, overlap), VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE,
  * VDN_ERR_ALIGNMENT (16 B for k, v and the d-wide outputs, 2 B for beta and the
  * dbeta outputs, 256 B for the workspace), VDN_ERR_HIP.  Asynchronous on `stream`.

@@ -256,7 +256,7 @@ def test_backward_readout_argument_errors_before_launch():
     assert call(dy=base["dy"] + 8) == bd.VDN_ERR_ALIGNMENT
     assert call(ws=base["ws"] + 16) == bd.VDN_ERR_ALIGNMENT
     assert call(d=good(dtype="f32")) == bd.VDN_ERR_UNSUPPORTED
-    assert call(d=good(flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_QUERY_L2)) == bd.VDN_ERR_UNSUPPORTED
+    assert call(d=good(flags=bd.VDN_VDA_QUERY_L2)) == bd.VDN_ERR_UNSUPPORTED   # the raw query needs the epilogue
     # without the epilogue the gate is not needed
     raw = good(epilogue=False)
     assert call(d=raw, gate=0, dgate=0, q=0) == bd.VDN_ERR_INVALID_ARG  # (q still is)
@@ -289,7 +289,8 @@ def test_backward_gram_argument_errors_before_launch():
     assert call(ws=base["ws"] + 16) == bd.VDN_ERR_ALIGNMENT
     assert call(d=good(dtype="f32")) == bd.VDN_ERR_UNSUPPORTED
     assert call(d=good(flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_DECAY_BRIDGE)) == bd.VDN_ERR_UNSUPPORTED
-    assert call(d=good(flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_QUERY_L2)) == bd.VDN_ERR_UNSUPPORTED
+    # the raw query's normalisation does not reach this stage: its arguments are still checked
+    assert call(d=good(flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_QUERY_L2), k=0) == bd.VDN_ERR_INVALID_ARG
     # without text tokens the text pointers are not needed: the call gets as
     # far as the alignment checks
     notext = good(n_text=0)

@@ -39,7 +39,22 @@ CASES = {
     "bwd_16_chunk3": dict(w=BASE.scaled(name="bwd_16_chunk3", d=16, H=2, T=17, grid_h=4, grid_w=5, L=4, chunk=3)),
     "bwd_32": dict(w=BASE.scaled(name="bwd_32", d=32, H=2, T=16, grid_h=4, grid_w=9, L=4)),
     "bwd_64_no_text": dict(w=BASE.scaled(name="bwd_64_no_text", d=64, H=1, T=12, grid_h=3, grid_w=5, L=0, chunk=3)),
+    # raw queries (the forward normalises them, VDN_VDA_QUERY_L2): per-token lengths 0.3 .. 3
+    "bwd_128_ql2": dict(w=BASE.scaled(name="bwd_128_ql2", H=2, T=12, grid_h=5, grid_w=7, L=8), query_l2=True),
+    "bwd_64_ql2_gain": dict(w=BASE.scaled(name="bwd_64_ql2_gain", d=64, H=3, T=13, grid_h=7, grid_w=9, L=4),
+                            query_l2=True, gain=True),
+    "bwd_16_ql2": dict(w=BASE.scaled(name="bwd_16_ql2", d=16, H=2, T=17, grid_h=4, grid_w=5, L=4, chunk=3),
+                       query_l2=True),
 }
+
+L2_EPS = 1e-6
+
+
+def _raw_queries(x, w):
+    """Replace the unit queries by raw ones of per-token length 0.3 .. 3."""
+    rng = np.random.default_rng(77)
+    scale = rng.uniform(0.3, 3.0, x["q"].shape[:-1] + (1,))
+    x["q"] = synth.f64_to_bf16_bits(synth.to_f64(x["q"], w.dtype) * scale)
 
 
 def _dy(w):
@@ -54,16 +69,19 @@ def _run(name, stage2=False, stage3=False):
     from frame_wise_delta_02_amd import binding as bd
     case = CASES[name]
     w, epi, bridge = case["w"], case.get("epilogue", True), case.get("bridge", False)
+    ql2 = case.get("query_l2", False)
     x = synth.make_inputs(w)
+    if ql2:
+        _raw_queries(x, w)
     dy = _dy(w)
     rw = np.random.default_rng(5).uniform(0.5, 1.5, w.d) if case.get("gain") else None
-    out, ws, desc, dev = G.run_forward(x, w, epilogue=epi, rms_weight=rw, bridge=bridge)
+    out, ws, desc, dev = G.run_forward(x, w, epilogue=epi, rms_weight=rw, bridge=bridge, query_l2=ql2)
     dy_d = G.to_device(dy, w.dtype)
     rw_d = None if rw is None else torch.from_numpy(rw.astype(np.float32)).cuda()
     G.say(f"backward_readout {name}")
     dq, dgate, bws = bd.backward_readout(dev["q"], dev["gate"], rw_d, dev["alpha"], dy_d, ws,
                                          grid=(w.grid_h, w.grid_w), n_text=w.L, chunk=w.chunk, epilogue=epi,
-                                         bridge=bridge)
+                                         bridge=bridge, query_l2=ql2, l2_eps=L2_EPS)
     torch.cuda.synchronize()
     gpu = {"dq": dq, "dgate": dgate, "bws": bws}
     if stage2:
@@ -80,8 +98,12 @@ def _run(name, stage2=False, stage3=False):
     f = G.oracle_view({k: x[k] for k in ("q", "k", "v", "beta", "k_text", "v_text", "beta_text", "gate")}, w)
     ref = vda_grad.backward(f["q"], f["k"], f["v"], x["alpha"].astype(np.float64), f["beta"], f["k_text"],
                             f["v_text"], f["beta_text"], G.oracle_view({"dy": dy}, w)["dy"],
-                            gate=f["gate"] if epi else None, rms_weight=rw, chunk=w.chunk, bridge=bridge)
+                            gate=f["gate"] if epi else None, rms_weight=rw, chunk=w.chunk, bridge=bridge,
+                            query_l2=L2_EPS if ql2 else None)
     L = bd.backward_layout(bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L, w.chunk, w.dtype, epi))
+    if ql2:  # the first stage's d_out holds do / |q| per token
+        q = f["q"]
+        ref["do_written"] = np.moveaxis(ref["do"], 1, 3) / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + L2_EPS)
     return gpu, ref, L, w, epi, dy
 
 
@@ -101,8 +123,9 @@ def test_backward_readout(name):
     dsq = _section(bws, L.d_state_q, (w.B, w.H, w.T, w.d, w.d))
     tol = G.TOL[w.dtype]
     # without the epilogue do is dy itself (the workspace copy is not written)
+    do_want = ref["do_written"] if "do_written" in ref else np.moveaxis(ref["do"], 1, 3)
     errs = {"dq": G.slice_rel_err(G.to_host_f64(dq), ref["dq"]),
-            "do": G.slice_rel_err(do if epi else G.oracle_view({"dy": dy}, w)["dy"], np.moveaxis(ref["do"], 1, 3)),
+            "do": G.slice_rel_err(do if epi else G.oracle_view({"dy": dy}, w)["dy"], do_want),
             "dS_q": G.mat_rel_err(dsq, ref["dS_q"])}
     if epi:
         errs["dgate"] = G.slice_rel_err(G.to_host_f64(dgate), ref["dgate"])
