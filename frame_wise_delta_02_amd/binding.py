@@ -281,7 +281,7 @@ def backward_readout(q, gate, rms_weight, alpha, dy, fwd_workspace, *, grid, n_t
 
 
 def backward_scan(alpha, fwd_workspace, workspace, *, shape, grid, n_text=0, chunk=5, dtype="bf16", epilogue=True,
-                  dalpha=None):
+                  dalpha=None, bridge=False):
     """Second stage of the backward pass (vdn_vda_backward_scan) on the first
     stage's workspace; returns dalpha [B, T, H, d] float32.  ``shape`` = (B, T, H, d)."""
     import torch
@@ -289,7 +289,8 @@ def backward_scan(alpha, fwd_workspace, workspace, *, shape, grid, n_text=0, chu
     dev = alpha.device
     for name, x in (("alpha", alpha), ("fwd_workspace", fwd_workspace), ("workspace", workspace), ("dalpha", dalpha)):
         _check(x, name, dev)
-    desc = make_desc(B, H, T, grid[0], grid[1], d, n_text, chunk, dtype, epilogue)
+    desc = make_desc(B, H, T, grid[0], grid[1], d, n_text, chunk, dtype, epilogue,
+                     flags=(VDN_VDA_EPILOGUE if epilogue else 0) | (VDN_VDA_DECAY_BRIDGE if bridge else 0))
     if dalpha is None:
         dalpha = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
     st = lib().vdn_vda_backward_scan(ctypes.byref(desc), _ptr(alpha), _ptr(fwd_workspace), fwd_workspace.numel(),
@@ -327,7 +328,7 @@ def backward_gram(k, v, beta, k_text, v_text, beta_text, workspace, *, grid, chu
 
 
 def backward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, dy, fwd_workspace, *, grid,
-             chunk=5, epilogue=True, rms_eps=1e-6, workspace=None, query_l2=False, l2_eps=1e-6):
+             chunk=5, epilogue=True, rms_eps=1e-6, workspace=None, query_l2=False, l2_eps=1e-6, bridge=False):
     """The whole backward pass (the three stages in order) after a forward
     that left ``fwd_workspace`` (with ``query_l2`` the forward took the raw
     query and dq is its gradient); returns a dict of input gradients dq, dk, dv,
@@ -337,9 +338,9 @@ def backward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, 
     L = 0 if k_text is None else k_text.shape[1]
     dq, dgate, workspace = backward_readout(q, gate, rms_weight, alpha, dy, fwd_workspace, grid=grid, n_text=L,
                                             chunk=chunk, epilogue=epilogue, rms_eps=rms_eps, workspace=workspace,
-                                            query_l2=query_l2, l2_eps=l2_eps)
+                                            query_l2=query_l2, l2_eps=l2_eps, bridge=bridge)
     dalpha = backward_scan(alpha, fwd_workspace, workspace, shape=(B, T, H, d), grid=grid, n_text=L,
-                           chunk=chunk, dtype=_dtype_of(q), epilogue=epilogue)
+                           chunk=chunk, dtype=_dtype_of(q), epilogue=epilogue, bridge=bridge)
     dk, dv, dbeta, dkt, dvt, dbt = backward_gram(k, v, beta, k_text, v_text, beta_text, workspace, grid=grid,
                                                  chunk=chunk, epilogue=epilogue)
     return dict(dq=dq, dk=dk, dv=dv, dalpha=dalpha, dbeta=dbeta, dk_text=dkt, dv_text=dvt, dbeta_text=dbt,

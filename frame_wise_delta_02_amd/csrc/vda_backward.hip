@@ -454,35 +454,54 @@ __global__ __launch_bounds__(256) void fill_zero(uint4* __restrict__ p, size_t n
     p[i] = make_uint4(0, 0, 0, 0);
 }
 
-// The coverage rules backwards (no bridge): the adjoint of record F_j is the
-// sum of dS_q over the non-anchor frames of chunk j + 2, that of R_j over
-// chunk j - 2; S_T receives dS_q of the anchors, half of dS_q where a side
-// reads S_T / 2, and half of the adjoint of every record the scan never
-// reaches (a record whose coverage is empty is S_T / 2 itself).  One thread
-// per 4 consecutive entries of the d x d matrices of one (batch, head).
+// The coverage rules backwards: the adjoint of record F_j is the sum of dS_q
+// over the non-anchor frames of chunk j + 2, that of R_j over chunk j - 2; S_T
+// receives dS_q of the anchors, half of dS_q where a side reads S_T / 2, and
+// half of the adjoint of every record the scan never reaches (a record whose
+// coverage is empty is S_T / 2 itself).  With the decay bridge a query chunk
+// c's side reads its state times Diag(df_c) (forward: alpha over chunk c - 1)
+// or Diag(dr_c) (reverse: alpha over chunk c + 1), so that chunk's sum reaches
+// the side column-scaled by the same products.  One thread per 4 consecutive
+// entries (one row, 4 columns) of the d x d matrices of one (batch, head).
 template <int D>
 __global__ __launch_bounds__(256) void backward_gather(const float* __restrict__ dsq, float* __restrict__ dF,
-                                                       float* __restrict__ dR, float* __restrict__ dST, int T,
-                                                       int C, int nc) {
+                                                       float* __restrict__ dR, float* __restrict__ dST,
+                                                       const float* __restrict__ alpha, int T, int C, int nc, int H,
+                                                       int bridge) {
   constexpr int N4 = D * D / 4;
   const int per = (N4 + 255) / 256;
   const int head = blockIdx.x / per;
   const int e4 = (blockIdx.x % per) * 256 + threadIdx.x;
   if (e4 >= N4) return;
+  const int b = head / H, h = head % H, col = (4 * e4) % D;
   const float4* S = reinterpret_cast<const float4*>(dsq) + (size_t)head * T * N4 + e4;
   float4* F = reinterpret_cast<float4*>(dF) + (size_t)head * nc * N4 + e4;
   float4* R = reinterpret_cast<float4*>(dR) + (size_t)head * nc * N4 + e4;
   auto add = [](float4& a, float4 b, float w) {
     a.x += w * b.x; a.y += w * b.y; a.z += w * b.z; a.w += w * b.w;
   };
+  // product of alpha over frames s0 .. s1 - 1 for this thread's 4 columns
+  auto decay = [&](int s0, int s1) {
+    float4 d = make_float4(1.f, 1.f, 1.f, 1.f);
+    for (int s = s0; s < s1; ++s) {
+      const float4 a = *reinterpret_cast<const float4*>(alpha + (((size_t)b * T + s) * H + h) * D + col);
+      d.x *= a.x; d.y *= a.y; d.z *= a.z; d.w *= a.w;
+    }
+    return d;
+  };
+  auto scaled = [](float4 g, float4 d) { return make_float4(g.x * d.x, g.y * d.y, g.z * d.z, g.w * d.w); };
   float4 st = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < nc; ++j) {
     // chunk j's non-anchor frames feed F_{j-2} and R_{j+2}
     float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int t = C * j; t < min(C * (j + 1), T); ++t)
       if (t != 0 && t != T - 1) add(g, S[(size_t)t * N4], 1.f);
-    if (j >= 2) F[(size_t)(j - 2) * N4] = g; else add(st, g, 0.5f);
-    if (j + 2 <= nc - 1) R[(size_t)(j + 2) * N4] = g; else add(st, g, 0.5f);
+    const float4 one = make_float4(1.f, 1.f, 1.f, 1.f);
+    const float4 df = bridge && j >= 1 ? decay(C * (j - 1), C * j) : one;
+    const float4 dr = bridge && j + 1 <= nc - 1 ? decay(C * (j + 1), min(C * (j + 2), T)) : one;
+    const float4 gf = scaled(g, df), gr = scaled(g, dr);
+    if (j >= 2) F[(size_t)(j - 2) * N4] = gf; else add(st, gf, 0.5f);
+    if (j + 2 <= nc - 1) R[(size_t)(j + 2) * N4] = gr; else add(st, gr, 0.5f);
   }
   // slots no chunk feeds (F_{nc-2}, F_{nc-1}, R_0, R_1) are not records: zero,
   // since the adjoint scan reads every slot (scaled by zero where it is none)
@@ -688,6 +707,65 @@ __global__ __launch_bounds__(256, 2) void gemm_dd(GemmArgs g) {
     }
 }
 
+// The decay bridge's own term of dalpha.  A query chunk c's forward side reads
+// wf F_{c-2} Diag(df_c), df_c the product of alpha over chunk c - 1, so frame
+// s of chunk c - 1 gets, per key channel k,
+//   dalpha_s[k] += sum_i G_c[i][k] wf F_{c-2}[i][k] prod_{s' != s} alpha_{s'}[k]
+// with G_c the sum of dS_q over chunk c's non-anchor frames (S_T / 2 for a
+// missing record); the reverse side likewise with chunk c + 1 and R_{c+2}.
+// Workgroup (head, chunk j) serves the frames of chunk j: the forward term
+// from query chunk j + 1 and the reverse term from query chunk j - 1, added
+// onto dalpha after the products have written it; thread k owns channel k.
+template <int D>
+__global__ __launch_bounds__(256) void bridge_dalpha(const float* __restrict__ dsq, const float* __restrict__ s_text,
+                                                     const float* __restrict__ fwd, const float* __restrict__ rev,
+                                                     const float* __restrict__ alpha, float* __restrict__ dalpha,
+                                                     int T, int C, int nc, int H) {
+  const int j = blockIdx.x % nc, head = blockIdx.x / nc;
+  const int b = head / H, h = head % H;
+  const int k = threadIdx.x;
+  if (k >= D) return;
+  const size_t DD = (size_t)D * D;
+  const float* S = dsq + (size_t)head * T * DD;
+  const float* ST = s_text + (size_t)head * DD;
+  auto al = [&](int s) { return alpha[(((size_t)b * T + s) * H + h) * D + k]; };
+  // sum over rows i of G_c[i][k] * w * side[i][k]
+  auto coldot = [&](int c, const float* side, float w) {
+    float acc = 0.f;
+    for (int i = 0; i < D; ++i) {
+      float g = 0.f;
+      for (int t = C * c; t < min(C * (c + 1), T); ++t)
+        if (t != 0 && t != T - 1) g += S[(size_t)t * DD + (size_t)i * D + k];
+      acc += g * w * side[(size_t)i * D + k];
+    }
+    return acc;
+  };
+  const int s0 = C * j, s1 = min(C * (j + 1), T);
+  float cf = 0.f, cr = 0.f;
+  bool hf = false, hr = false;
+  if (j + 1 <= nc - 1) {  // query chunk c = j + 1 bridges over chunk j forwards
+    const int c = j + 1;
+    const float* side = c >= 2 ? fwd + ((size_t)head * nc + (c - 2)) * DD : ST;
+    cf = coldot(c, side, c >= 2 ? 1.f : 0.5f);
+    hf = true;
+  }
+  if (j >= 1) {  // query chunk c = j - 1 bridges over chunk j backwards
+    const int c = j - 1;
+    const float* side = c + 2 <= nc - 1 ? rev + ((size_t)head * nc + (c + 2)) * DD : ST;
+    cr = coldot(c, side, c + 2 <= nc - 1 ? 1.f : 0.5f);
+    hr = true;
+  }
+  for (int s = s0; s < s1; ++s) {
+    float others = 1.f;  // product of alpha over the chunk's other frames
+    for (int u = s0; u < s1; ++u)
+      if (u != s) others *= al(u);
+    float d = 0.f;
+    if (hf) d += cf * others;
+    if (hr) d += cr * others;
+    dalpha[(((size_t)b * T + s) * H + h) * D + k] += d;
+  }
+}
+
 // The text frame's adjoint: dS_T (from the queries) plus half the final
 // adjoint of each scan (both start from S_T / 2), into slot T of lam_f.
 __global__ __launch_bounds__(256) void text_adjoint(const float* __restrict__ dST, const float* __restrict__ fin,
@@ -737,7 +815,7 @@ hipError_t backward_scan_d(const Problem& p, const BwdScanBuffers& w, hipStream_
   if ((e = fill(w.dalpha, (size_t)p.B * T * p.H * D * 4)) != hipSuccess) return e;
   // record adjoints and the queries' part of dS_T
   hipLaunchKernelGGL(backward_gather<D>, dim3((unsigned)(heads * ((DD / 4 + 255) / 256))), dim3(256), 0, s,
-                     w.dsq, w.dF, w.dR, w.dST, T, p.C, p.nc);
+                     w.dsq, w.dF, w.dR, w.dST, w.alpha, T, p.C, p.nc, p.H, p.bridge ? 1 : 0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // every frame's state, then the adjoint scans
   if ((e = launch_scan_states(p, w.stats, w.pinv, w.alpha, w.states_f, w.states_r, s)) != hipSuccess) return e;
@@ -799,7 +877,14 @@ hipError_t backward_scan_d(const Problem& p, const BwdScanBuffers& w, hipStream_
   if ((e = launch(gemm_dd<D, false, false, 1, false, false, EPI_PLAIN>, g)) != hipSuccess) return e;
   g = args(w.dA, -1.f);
   g.a[0] = Pm, g.b[0] = Tm;
-  return launch(gemm_dd<D, false, false, 1, false, false, EPI_PLAIN>, g);
+  if ((e = launch(gemm_dd<D, false, false, 1, false, false, EPI_PLAIN>, g)) != hipSuccess) return e;
+  // the decay bridge's own term of dalpha, after the products have written it
+  if (p.bridge) {
+    hipLaunchKernelGGL(bridge_dalpha<D>, dim3((unsigned)(heads * p.nc)), dim3(D < 64 ? 64 : D), 0, s, w.dsq, w.s_text,
+                       w.fwd, w.rev, w.alpha, w.dalpha, T, p.C, p.nc, p.H);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace

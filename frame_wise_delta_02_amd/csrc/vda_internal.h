@@ -165,6 +165,7 @@ struct BwdScanBuffers {
   float *M, *dPinv, *tmp;       // [B, H, T+1, d, d]
   float *dA, *dB;              // [B, H, T+1, d, d] (out)
   float* dalpha;               // [B, T, H, d] (out)
+  const float *s_text, *fwd, *rev;  // forward workspace (the decay bridge's term)
 };
 hipError_t launch_backward_scan(const Problem& p, const BwdScanBuffers& w, hipStream_t s);
 // Third stage: dk, dv, dbeta of every frame and of the text tokens from dA, dB.

@@ -356,7 +356,7 @@ vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha, cons
                                  size_t workspace_bytes, hipStream_t stream) {
   const vdn_status st = check(d);
   if (st != VDN_OK) return st;
-  if (d->dtype != VDN_BF16 || (d->flags & VDN_VDA_DECAY_BRIDGE)) return VDN_ERR_UNSUPPORTED;
+  if (d->dtype != VDN_BF16) return VDN_ERR_UNSUPPORTED;
   if (!alpha || !fwd_workspace || !dalpha) return VDN_ERR_INVALID_ARG;
   // every frame's state is recorded per head through one buffer descriptor
   if ((double)(d->T + 2) * d->d_k * d->d_v * 4.0 >= 2147483648.0) return VDN_ERR_INVALID_ARG;
@@ -390,6 +390,9 @@ vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha, cons
   w.dA = f(bl.dA);
   w.dB = f(bl.dB);
   w.dalpha = dalpha;
+  w.s_text = reinterpret_cast<const float*>(fw + fl.s_text);
+  w.fwd = reinterpret_cast<const float*>(fw + fl.fwd);
+  w.rev = reinterpret_cast<const float*>(fw + fl.rev);
   return launch_backward_scan(p, w, stream) == hipSuccess ? VDN_OK : VDN_ERR_HIP;
 }
 
@@ -399,7 +402,7 @@ vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const voi
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const vdn_status st = check(d);
   if (st != VDN_OK) return st;
-  if (d->dtype != VDN_BF16 || (d->flags & VDN_VDA_DECAY_BRIDGE)) return VDN_ERR_UNSUPPORTED;
+  if (d->dtype != VDN_BF16) return VDN_ERR_UNSUPPORTED;
   if (!k || !v || !beta || !dk || !dv || !dbeta) return VDN_ERR_INVALID_ARG;
   const bool text = d->n_text > 0;
   if (text && (!k_text || !v_text || !beta_text || !dk_text || !dv_text || !dbeta_text)) return VDN_ERR_INVALID_ARG;

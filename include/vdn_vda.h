@@ -289,15 +289,18 @@ vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d,
  * and (I + A_t)^{-1}.  Reads the first stage's d_state_q from `workspace` and
  * the forward's workspace; writes d_record_f / d_record_r / d_text_q, lam_f /
  * lam_r and d_a / d_b into `workspace` (see vdn_vda_backward_layout) and
- *   dalpha [B, T, H, d_k] float32: the gradient of alpha (zero for the anchors).
+ *   dalpha [B, T, H, d_k] float32: the gradient of alpha (zero for the anchors
+ *          without the decay bridge).
  * Per absorbed frame s of a scan with adjoint lambda (the state's, after the
  * record adjoint of the state frame s produces is added): dY = lambda P_s,
  * dB_s += dY, dalpha_s += column sums of S_prev * dY, d(P_s) += Y_s^T lambda with
  * Y_s = S_prev Diag(alpha_s) + B_s, and lambda <- dY Diag(alpha_s) for the state
  * before; then dA_s = -P_s d(P_s) P_s (P_s = (I + A_s)^{-1}, [VDN-summary]
  * "어떻게 쓰나").  The text frame S_T = B_T P_T takes lambda = the adjoint of
- * S_T.  Supported: VDN_BF16 without VDN_VDA_DECAY_BRIDGE (else
- * VDN_ERR_UNSUPPORTED); (T + 2) d_k d_v 4 < 2^31.  Errors as
+ * S_T.  With VDN_VDA_DECAY_BRIDGE a query chunk's adjoint reaches the records
+ * (and S_T / 2) column-scaled by its bridge's alpha products, and dalpha adds
+ * the bridge's own term (frames of the bridged chunks, anchors included).
+ * Supported: VDN_BF16 (else VDN_ERR_UNSUPPORTED); (T + 2) d_k d_v 4 < 2^31.  Errors as
  * vdn_vda_backward_readout.  Asynchronous on `stream`.
  */
 vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha,
@@ -320,8 +323,7 @@ vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha,
  * hi + lo pairs (dbeta sums d^2 products that largely cancel), dB_t^T (dk
  * only) rounded once to bfloat16.  k, v, beta and the text inputs are
  * those the forward pass read.  Outputs must overlap neither each other, the
- * inputs nor the workspace.  Supported: VDN_BF16 without VDN_VDA_DECAY_BRIDGE
- * (else VDN_ERR_UNSUPPORTED).  Errors: VDN_ERR_INVALID_ARG
+ * inputs nor the workspace.  Supported: VDN_BF16 (else VDN_ERR_UNSUPPORTED).  Errors: VDN_ERR_INVALID_ARG
  * (NULL pointer, overlap), VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE,
  * VDN_ERR_ALIGNMENT (16 B for k, v and the d-wide outputs, 2 B for beta and the
  * dbeta outputs, 256 B for the workspace), VDN_ERR_HIP.  Asynchronous on `stream`.

@@ -288,8 +288,9 @@ def test_backward_gram_argument_errors_before_launch():
     assert call(dbeta=base["dbeta"] + 1) == bd.VDN_ERR_ALIGNMENT
     assert call(ws=base["ws"] + 16) == bd.VDN_ERR_ALIGNMENT
     assert call(d=good(dtype="f32")) == bd.VDN_ERR_UNSUPPORTED
-    assert call(d=good(flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_DECAY_BRIDGE)) == bd.VDN_ERR_UNSUPPORTED
-    # the raw query's normalisation does not reach this stage: its arguments are still checked
+    # neither the decay bridge nor the raw query's normalisation reaches this
+    # stage: with either flag the arguments are still checked
+    assert call(d=good(flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_DECAY_BRIDGE), k=0) == bd.VDN_ERR_INVALID_ARG
     assert call(d=good(flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_QUERY_L2), k=0) == bd.VDN_ERR_INVALID_ARG
     # without text tokens the text pointers are not needed: the call gets as
     # far as the alignment checks

@@ -30,6 +30,9 @@ CASES = {
     "bwd_64_ragged": dict(w=BASE.scaled(name="bwd_64_ragged", d=64, H=3, T=13, grid_h=7, grid_w=9, L=4)),
     "bwd_32_bridge": dict(w=BASE.scaled(name="bwd_32_bridge", d=32, H=2, T=16, grid_h=4, grid_w=9, L=4),
                           bridge=True),
+    # the decay bridge with records in use on both sides (7 chunks of 3)
+    "bwd_64_bridge": dict(w=BASE.scaled(name="bwd_64_bridge", d=64, H=2, T=20, grid_h=4, grid_w=6, L=4, chunk=3),
+                          bridge=True, gain=True),
     "bwd_16": dict(w=BASE.scaled(name="bwd_16", d=16, H=2, T=9, grid_h=4, grid_w=4, L=4), gain=True),
     "bwd_B2_chunk3": dict(w=BASE.scaled(name="bwd_B2_chunk3", B=2, H=2, T=14, grid_h=4, grid_w=6, L=4, chunk=3)),
     "bwd_T2": dict(w=BASE.scaled(name="bwd_T2", H=2, T=2, grid_h=4, grid_w=8, L=16)),
@@ -87,7 +90,8 @@ def _run(name, stage2=False, stage3=False):
     if stage2:
         G.say(f"backward_scan {name}")
         gpu["dalpha"] = bd.backward_scan(dev["alpha"], ws, bws, shape=(w.B, w.T, w.H, w.d),
-                                         grid=(w.grid_h, w.grid_w), n_text=w.L, chunk=w.chunk, epilogue=epi)
+                                         grid=(w.grid_h, w.grid_w), n_text=w.L, chunk=w.chunk, epilogue=epi,
+                                         bridge=bridge)
         torch.cuda.synchronize()
     if stage3:
         G.say(f"backward_gram {name}")
@@ -145,7 +149,7 @@ def _rel(got, ref):
     return float(np.max(np.where(scale > 0, diff / np.maximum(scale, 1e-300), diff)))
 
 
-@pytest.mark.parametrize("name", [n for n in CASES if not CASES[n].get("bridge")])
+@pytest.mark.parametrize("name", list(CASES))
 def test_backward_scan(name):
     """Second stage: record adjoints, the scans' adjoints, dA, dB (frames and
     text) and dalpha against the oracle."""
@@ -175,26 +179,19 @@ def test_backward_scan(name):
         # (the text frame exists only with text tokens)
         "dA_T": _rel(sym(dA[:, :, T]), sym(ref["dA_T"])) if w.L else 0.0,
         "dB_T": _rel(dB[:, :, T], ref["dB_T"]) if w.L else 0.0,
-        "dalpha": _rel(dalpha[:, fr], ref["dalpha"][:, fr]),
+        # every frame: under the decay bridge the anchors' alpha has a gradient too
+        "dalpha": _rel(dalpha, ref["dalpha"]),
     }
     # the anchors take no part in any scan
     assert np.abs(dA[:, :, [0, T - 1]]).max() == 0 and np.abs(dB[:, :, [0, T - 1]]).max() == 0
-    assert np.abs(dalpha[:, [0, T - 1]]).max() == 0
+    if not CASES[name].get("bridge"):
+        assert np.abs(dalpha[:, [0, T - 1]]).max() == 0
     G.say(f"{name}: " + " ".join(f"err({k})={v:.3e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert v <= G.TOL[w.dtype], (k, v)
 
 
-def test_backward_scan_rejects_the_bridge():
-    from frame_wise_delta_02_amd import binding as bd
-    w = CASES["bwd_32_bridge"]["w"]
-    desc = bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L, w.chunk, w.dtype, True,
-                        flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_DECAY_BRIDGE)
-    st = bd.lib().vdn_vda_backward_scan(__import__("ctypes").byref(desc), None, None, 0, None, None, 0, None)
-    assert st == bd.VDN_ERR_UNSUPPORTED
-
-
-@pytest.mark.parametrize("name", [n for n in CASES if not CASES[n].get("bridge")])
+@pytest.mark.parametrize("name", list(CASES))
 def test_backward_gram(name):
     """Third stage: dk, dv, dbeta of every frame and of the text tokens."""
     gpu, ref, L, w, epi, dy = _run(name, stage2=True, stage3=True)
