@@ -34,7 +34,6 @@ namespace {
 constexpr int GBM = 256, GBN = 256, GBK = 64;
 constexpr int GROUP_M = 4;                // M-tiles per band of the tile order
 constexpr int GLD = GBK + 8;              // LDS row stride of a staged panel (bfloat16 elements)
-constexpr int GOLD = 128 + 8;             // LDS row stride of a wave's output tile
 constexpr int GPANEL = GBM * GLD;         // elements per staged operand panel
 
 enum { PROJ_GATE = 0, PROJ_ADD = 1 };
