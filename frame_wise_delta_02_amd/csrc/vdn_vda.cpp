@@ -70,6 +70,11 @@ vdn_status check(const vdn_vda_desc* d) {
   // with 32-bit byte offsets
   if (((double)d->grid_h * d->grid_w + 64.0) * d->H * d->d_v * 4.0 > 4294967295.0) return VDN_ERR_INVALID_ARG;
   if (((double)d->n_text + 64.0) * d->H * d->d_v * 4.0 > 4294967295.0) return VDN_ERR_INVALID_ARG;
+  // the statistics kernel's register prefetch reads a few tiles of 64 tokens
+  // past a frame's last token (zero through the buffer range check); with 640
+  // tokens of margin its 32-bit offsets cannot wrap back into the frame
+  if (((double)d->grid_h * d->grid_w + 640.0) * d->H * d->d_v * 2.0 > 4294967295.0) return VDN_ERR_INVALID_ARG;
+  if (((double)d->n_text + 640.0) * d->H * d->d_v * 2.0 > 4294967295.0) return VDN_ERR_INVALID_ARG;
   if (d->d_k != d->d_v) return VDN_ERR_UNSUPPORTED;
   if (d->d_k != 16 && d->d_k != 32 && d->d_k != 64 && d->d_k != 128) return VDN_ERR_UNSUPPORTED;
   return VDN_OK;

@@ -138,7 +138,14 @@ typedef struct {
   size_t stats, pinv, s_text, fwd, rev, readout_states, chunk_m, chunk_j, total;
 } vdn_vda_layout;
 
-/* Check a descriptor without touching the GPU.  Host only. */
+/* Check a descriptor without touching the GPU.  Host only.  Besides shapes,
+ * widths and flags it enforces the kernels' 32-bit byte-offset limits, with
+ * U = grid_h * grid_w and L = n_text: (U + 64) H d 4 and (L + 64) H d 4 bytes
+ * (a frame's or the text's token rows plus a tile's overhang) and
+ * (U + 640) H d 2 and (L + 640) H d 2 bytes (the statistics kernel's prefetch
+ * past the last token) below 4 GiB, and one head's chunk records below 2^31
+ * bytes.  VDN_ERR_INVALID_ARG when a limit fails, VDN_ERR_UNSUPPORTED for a
+ * width other than 16, 32, 64, 128 or d_k != d_v. */
 vdn_status vdn_vda_validate(const vdn_vda_desc* d);
 
 /* Workspace bytes vdn_vda_forward needs for `d`; 0 if `d` is invalid. */

@@ -307,6 +307,12 @@ def test_frame_rows_stay_within_32_bit_offsets():
     assert bd.validate(good(grid_h=1000, grid_w=1000, H=8, d=128)) == bd.VDN_OK
     assert bd.validate(good(grid_h=1000, grid_w=1000, H=16, d=128)) == bd.VDN_ERR_INVALID_ARG
     assert bd.validate(good(n_text=1 << 20, H=16, d=128)) == bd.VDN_ERR_INVALID_ARG
+    # the statistics kernel's prefetch reads a few tiles of 64 tokens past the
+    # last token: (U + 640) H d 2 bytes must stay below 4 GiB as well, which
+    # binds for wide rows of few tokens
+    assert bd.validate(good(grid_h=1, grid_w=1, H=16384, n_text=380, d=128)) == bd.VDN_OK
+    assert bd.validate(good(grid_h=1, grid_w=1, H=32768, n_text=0, d=128)) == bd.VDN_ERR_INVALID_ARG
+    assert bd.validate(good(grid_h=1, grid_w=1, H=16384, n_text=420, d=128)) == bd.VDN_ERR_INVALID_ARG
 
 
 def test_adjacent_maps_argument_errors_before_launch():
