@@ -72,6 +72,20 @@ def algorithmic_bytes(w, stage: str) -> int:
     return 0
 
 
+# the prep's arithmetic per output element: a 5 x 5 spatial and a 5-tap temporal
+# depthwise filter, 30 fp32 multiply-adds
+PREP_FLOP_PER_OUTPUT = 60
+# fp32 FMA without packed instructions (packed fp32 is off in every HIP build
+# here): 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz; with packed
+# instructions the chip's figure is twice this, 157.3 TFLOP/s
+VALU_F32_PEAK_TFLOPS = 78.6
+
+
+def prep_flops(w) -> int:
+    """fp32 FLOP of one prep launch (one of K, V)."""
+    return w.B * w.T * w.U * w.H * w.d * PREP_FLOP_PER_OUTPUT
+
+
 def job_bytes(w) -> int:
     """Whole-job algorithmic bytes: Q, K, V, gate, beta, alpha and text in; O out."""
     esz = 2 if w.dtype == "bf16" else 4
@@ -213,6 +227,20 @@ def bench_backward(args, w, x, d, fwd, stream, hip, t_gen) -> int:
     dom = max(BWD_STAGES, key=lambda k: st[k])
     dom_bytes = bwd_algorithmic_bytes(w, dom)
     ach = dom_bytes / (st[dom] * 1e-3) / 1e9
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes": dom_bytes,
+                "launch_ms": round(dom_ms, 4), "launches_per_step": launches}
+    if dom == "prep":
+        # the filter's fp32 arithmetic binds before its bytes do: 60 FLOP per
+        # 4 bytes moved (one bfloat16 in, one out) is above the 9.8 FLOP/B
+        # ridge of 78.6 TFLOP/s over 8 TB/s
+        tf = prep_flops(w) / (dom_ms * 1e-3) / 1e12
+        roofline.update({"bound": "alu", "achieved": round(tf, 2), "peak": VALU_F32_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / VALU_F32_PEAK_TFLOPS, 4),
+                         "flops": prep_flops(w),
+                         "hbm": {"achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(ach / HBM_PEAK_GBS, 4)}})
     frames = w.B * w.T
     rec = {
         "metric": "VDA forward + backward (training step of the layer) frames/s per GPU",
@@ -496,10 +524,7 @@ def main() -> int:
         "job_roofline": {"bound": "hbm", "algorithmic_bytes": job_bytes(w),
                          "achieved_GBs": round(job_bytes(w) / (ms * 1e-3) / 1e9, 1),
                          "frac": round(job_bytes(w) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": dom_bytes,
-                     "launch_ms": round(dom_ms, 4), "launches_per_step": launches},
+        "roofline": roofline,
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(t_gen, 1),

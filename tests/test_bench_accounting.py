@@ -1,0 +1,43 @@
+"""Host checks of bench.py's accounting: the algorithmic bytes and FLOP it
+divides by (the figures its roofline objects report), and that it refuses
+more than one GPU before touching any device."""
+
+import os
+import subprocess
+import sys
+
+import bench
+from frame_wise_delta_02_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_768p_bytes():
+    w = synth.WORKLOADS["768p_bf16"]
+    tok = 60 * 4032 * 24
+    # readout: Q and the gate logits in, O out, bfloat16, d = 128
+    assert bench.algorithmic_bytes(w, "readout") == tok * 3 * 128 * 2 == 4_459_069_440
+    # gram: K, V and beta of the 58 interior frames
+    assert bench.algorithmic_bytes(w, "gram") == 58 * 4032 * 24 * (2 * 128 + 1) * 2
+    # whole job: Q, K, V, gate, beta, O per token-head; alpha per frame (fp32);
+    # the 256 text tokens' K, V, beta
+    assert bench.job_bytes(w) == (tok * (5 * 128 + 1) * 2 + 60 * 24 * 128 * 4
+                                  + 256 * 24 * (2 * 128 + 1) * 2) == 7_447_289_856
+
+
+def test_long_clip_prep_accounting():
+    w = synth.WORKLOADS["long_prep_bf16"]
+    out = w.B * w.T * w.U * w.H * w.d
+    # per launch (one of K, V): 30 fp32 multiply-adds per output element
+    assert bench.prep_flops(w) == 60 * out
+    # both launches: K, V in and K^, V^ out in bfloat16
+    assert bench.algorithmic_bytes(w, "prep") == 4 * out * 2
+    # arithmetic intensity above the fp32 ridge: the prep is ALU-bound
+    ridge = bench.VALU_F32_PEAK_TFLOPS * 1e12 / (bench.HBM_PEAK_GBS * 1e9)
+    assert bench.prep_flops(w) / (bench.algorithmic_bytes(w, "prep") / 2) > ridge
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr and r.stdout == ""
