@@ -86,6 +86,28 @@ def prep_flops(w) -> int:
     return w.B * w.T * w.U * w.H * w.d * PREP_FLOP_PER_OUTPUT
 
 
+def dominant_roofline(w, dom: str, dom_ms: float, dom_bytes: int, traffic, launches: int) -> dict:
+    """The bench line's roofline object for the dominant kernel: one launch's
+    algorithmic bytes over its average duration against the HBM peak, or for
+    the prep, its fp32 FLOP against the ALU peak with the HBM rate beside it."""
+    ach = dom_bytes / (dom_ms * 1e-3) / 1e9
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes": dom_bytes,
+                "launch_ms": round(dom_ms, 4), "launches_per_step": launches}
+    if dom == "prep":
+        # the filter's fp32 arithmetic binds before its bytes do: 60 FLOP per
+        # 4 bytes moved (one bfloat16 in, one out) is above the 9.8 FLOP/B
+        # ridge of 78.6 TFLOP/s over 8 TB/s
+        tf = prep_flops(w) / (dom_ms * 1e-3) / 1e12
+        roofline.update({"bound": "alu", "achieved": round(tf, 2), "peak": VALU_F32_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / VALU_F32_PEAK_TFLOPS, 4),
+                         "flops": prep_flops(w),
+                         "hbm": {"achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(ach / HBM_PEAK_GBS, 4)}})
+    return roofline
+
+
 def job_bytes(w) -> int:
     """Whole-job algorithmic bytes: Q, K, V, gate, beta, alpha and text in; O out."""
     esz = 2 if w.dtype == "bf16" else 4
@@ -227,20 +249,6 @@ def bench_backward(args, w, x, d, fwd, stream, hip, t_gen) -> int:
     dom = max(BWD_STAGES, key=lambda k: st[k])
     dom_bytes = bwd_algorithmic_bytes(w, dom)
     ach = dom_bytes / (st[dom] * 1e-3) / 1e9
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "algorithmic_bytes": dom_bytes,
-                "launch_ms": round(dom_ms, 4), "launches_per_step": launches}
-    if dom == "prep":
-        # the filter's fp32 arithmetic binds before its bytes do: 60 FLOP per
-        # 4 bytes moved (one bfloat16 in, one out) is above the 9.8 FLOP/B
-        # ridge of 78.6 TFLOP/s over 8 TB/s
-        tf = prep_flops(w) / (dom_ms * 1e-3) / 1e12
-        roofline.update({"bound": "alu", "achieved": round(tf, 2), "peak": VALU_F32_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / VALU_F32_PEAK_TFLOPS, 4),
-                         "flops": prep_flops(w),
-                         "hbm": {"achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                 "frac": round(ach / HBM_PEAK_GBS, 4)}})
     frames = w.B * w.T
     rec = {
         "metric": "VDA forward + backward (training step of the layer) frames/s per GPU",
@@ -501,8 +509,8 @@ def main() -> int:
     launches = LAUNCHES_PER_STAGE.get(dom, 1)
     dom_bytes = algorithmic_bytes(w, dom) // launches
     dom_ms = stages[dom] / launches
-    ach = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = traffic_for(dom, w.name)
+    roofline = dominant_roofline(w, dom, dom_ms, dom_bytes, traffic, launches)
     frames = w.B * w.T
     rec = {
         "metric": METRIC,

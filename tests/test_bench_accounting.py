@@ -41,3 +41,41 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2 and "one GPU only" in r.stderr and r.stdout == ""
+
+
+def test_dominant_roofline_objects():
+    w = synth.WORKLOADS["long_prep_bf16"]
+    launch_bytes = bench.algorithmic_bytes(w, "prep") // 2
+    r = bench.dominant_roofline(w, "prep", 2.5, launch_bytes, None, 2)
+    assert r["bound"] == "alu" and r["unit"] == "TFLOP/s" and r["peak"] == bench.VALU_F32_PEAK_TFLOPS
+    assert abs(r["achieved"] - bench.prep_flops(w) / 2.5e-3 / 1e12) < 0.01
+    assert abs(r["frac"] - r["achieved"] / bench.VALU_F32_PEAK_TFLOPS) < 1e-3
+    assert abs(r["hbm"]["achieved"] - launch_bytes / 2.5e-3 / 1e9) < 0.1
+    w = synth.WORKLOADS["768p_bf16"]
+    r = bench.dominant_roofline(w, "readout", 0.9175, bench.algorithmic_bytes(w, "readout"), 123, 1)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["traffic"] == 123
+    assert abs(r["achieved"] - 4860.0) < 1.0 and abs(r["frac"] - 0.6075) < 1e-4
+
+
+def test_bench_names_are_defined():
+    """Every name a function of bench.py reads is a local, an enclosing
+    function's, a module-level name or a builtin (its GPU-only paths cannot run
+    here, so this catches a name left undefined there)."""
+    import builtins
+    import symtable
+    path = os.path.join(ROOT, "bench.py")
+    top = symtable.symtable(open(path).read(), path, "exec")
+    module = {s.get_name() for s in top.get_symbols() if s.is_assigned() or s.is_imported()}
+    known = module | set(dir(builtins))
+    missing = []
+
+    def walk(t):
+        for c in t.get_children():
+            if c.get_type() == "function":
+                for s in c.get_symbols():
+                    if s.is_referenced() and s.is_global() and s.get_name() not in known:
+                        missing.append((c.get_name(), s.get_name()))
+            walk(c)
+
+    walk(top)
+    assert not missing, missing
