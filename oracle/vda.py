@@ -8,7 +8,7 @@ U x d_k (rows are token keys k_{t,u}), V_t is U x d_v, beta_t holds one write
 strength per token, alpha_t one decay per key channel.  The state S is
 d_v x d_k, and a query q (length d_k) reads out S q (length d_v).
 
-Readings of points the pages leave open (each is listed again in the design doc):
+Readings of points the pages leave open:
 
 R1  Anchor query frames (0 and T-1) attend to everything in the softmax
     branch, so their linear coverage is empty in both directions and their
