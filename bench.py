@@ -358,8 +358,36 @@ def bench_adjacent(args, w, d, stream, hip, t_gen) -> int:
         "stages_ms": {k: round(v, 4) for k, v in st.items()},
         "wall_s_timed": round(wall, 3), "input_gen_s": round(t_gen, 1), "cpu_baseline": None,
     }
+    if args.library_ref:
+        rec["library_ref"] = library_ref(xa, wgb, wo, args.steps)
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def library_ref(x, w_gb, w_o, steps: int) -> dict:
+    """The platform's bfloat16 matmul (torch.matmul, hipBLASLt) on the two
+    GEMM shapes of the adjacent maps, without their epilogues: a reference
+    rate for the library's own GEMM kernels, not part of the path."""
+    import torch
+    out = {}
+    for name, w_ in (("gates_gemm", w_gb), ("out_proj_gemm", w_o)):
+        a = x.reshape(-1, x.shape[-1])
+        b = w_.t().contiguous()  # [K, N], materialised: no transposed view enters the product
+        for _ in range(2):
+            c = torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            c = torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = 2.0 * a.shape[0] * a.shape[1] * b.shape[1] / (ms * 1e-3) / 1e12
+        out[name] = {"shape": [a.shape[0], a.shape[1], b.shape[1]], "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        del b, c
+    return out
 
 
 def main() -> int:
@@ -379,6 +407,9 @@ def main() -> int:
     ap.add_argument("--adjacent", action="store_true",
                     help="time the path with the linear maps either side of it: gates from the block "
                          "input, the forward pass on them, the output projection (bfloat16 workloads without prep)")
+    ap.add_argument("--library-ref", action="store_true",
+                    help="with --adjacent: also time the platform's bfloat16 matmul on the two GEMM shapes "
+                         "(a reference rate, not part of the path)")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="instead of the forward pass, time a plain device copy of this many GiB "
                          "(the reference for scaling HBM byte counters)")
