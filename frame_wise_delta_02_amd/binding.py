@@ -24,11 +24,11 @@ VDN_VDA_SCAN_CHUNKS = 1 << 5
 _SCAN_FLAGS = {None: 0, "frames": VDN_VDA_SCAN_FRAMES, "chunks": VDN_VDA_SCAN_CHUNKS}
 
 EXPORTS = ("vdn_vda_validate", "vdn_vda_workspace_bytes", "vdn_vda_workspace_layout",
-           "vdn_vda_prepare", "vdn_vda_forward", "vdn_vda_set_profile_events",
+           "vdn_vda_prepare", "vdn_vda_forward", "vdn_vda_forward_timed",
            "vdn_vda_status_string", "vdn_vda_backward_workspace_bytes",
            "vdn_vda_backward_workspace_layout", "vdn_vda_backward_readout", "vdn_vda_backward_scan",
            "vdn_vda_backward_gram", "vdn_vda_gates_workspace_bytes", "vdn_vda_gates", "vdn_vda_out_proj")
-STAGES = ("gram", "gram_text", "solve", "scan", "gather", "readout")
+STAGES = ("gram", "solve", "scan", "gather", "readout")
 
 
 class VdaError(RuntimeError):
@@ -78,8 +78,8 @@ def lib() -> ctypes.CDLL:
         L.vdn_vda_prepare.restype = ctypes.c_int
         L.vdn_vda_forward.argtypes = [dp] + [p] * 12 + [sz, p]
         L.vdn_vda_forward.restype = ctypes.c_int
-        L.vdn_vda_set_profile_events.argtypes = [p, ctypes.c_int]
-        L.vdn_vda_set_profile_events.restype = ctypes.c_int
+        L.vdn_vda_forward_timed.argtypes = [dp] + [p] * 12 + [sz, p, p, ctypes.c_int32]
+        L.vdn_vda_forward_timed.restype = ctypes.c_int
         L.vdn_vda_status_string.argtypes = [ctypes.c_int]
         L.vdn_vda_status_string.restype = ctypes.c_char_p
         L.vdn_vda_backward_workspace_bytes.argtypes = [dp]
@@ -129,19 +129,6 @@ def workspace_layout(desc: Desc) -> Layout:
     return out
 
 
-def set_profile_events(handles):
-    """Install hipEvent_t handles (ints) for per-stage timing, or None to clear."""
-    if handles is None:
-        st = lib().vdn_vda_set_profile_events(None, 0)
-        set_profile_events._keep = None
-    else:
-        arr = (ctypes.c_void_p * len(handles))(*handles)
-        set_profile_events._keep = arr
-        st = lib().vdn_vda_set_profile_events(ctypes.cast(arr, ctypes.c_void_p), len(handles))
-    if st != VDN_OK:
-        raise VdaError(st, "vdn_vda_set_profile_events")
-
-
 # ----------------------------------------------------------------------------
 # torch marshalling
 # ----------------------------------------------------------------------------
@@ -176,7 +163,7 @@ def _check(x, name, dev):
 
 def forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weight=None, *,
             grid, chunk=5, epilogue=True, rms_eps=1e-6, out=None, workspace=None, bridge=False,
-            query_l2=False, l2_eps=1e-6, scan=None):
+            query_l2=False, l2_eps=1e-6, scan=None, events=None):
     """VDA forward on prepared features; returns ``out`` [B, T, U, H, d].
 
     Shapes as in include/vdn_vda.h.  ``grid`` = (grid_h, grid_w) with
@@ -184,6 +171,8 @@ def forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weig
     when not given.  ``bridge`` sets VDN_VDA_DECAY_BRIDGE; ``query_l2`` sets
     VDN_VDA_QUERY_L2 (``q`` is then the raw query, normalised with ``l2_eps``);
     ``scan`` = "frames" or "chunks" forces that scan (None: the library picks).
+    ``events``: hipEvent_t handles (ints), one before and one after each of the
+    ``STAGES``, recorded on the stream by vdn_vda_forward_timed.
     """
     import torch
     B, T, U, H, d = q.shape
@@ -205,10 +194,15 @@ def forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weig
     need = workspace_bytes(desc)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    st = lib().vdn_vda_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                               _ptr(k_text), _ptr(v_text), _ptr(beta_text),
-                               _ptr(gate) if epilogue else None, _ptr(rms_weight), _ptr(out),
-                               _ptr(workspace), workspace.numel(), _stream())
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+            _ptr(k_text), _ptr(v_text), _ptr(beta_text),
+            _ptr(gate) if epilogue else None, _ptr(rms_weight), _ptr(out),
+            _ptr(workspace), workspace.numel(), _stream())
+    if events is None:
+        st = lib().vdn_vda_forward(*args)
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        st = lib().vdn_vda_forward_timed(*args, ctypes.cast(arr, ctypes.c_void_p), len(events))
     if st != VDN_OK:
         raise VdaError(st, "vdn_vda_forward")
     return out

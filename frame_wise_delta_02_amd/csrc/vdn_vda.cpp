@@ -33,10 +33,34 @@ bool overlaps(const Span& a, const Span& b) {
   return a0 < b0 + b.n && b0 < a0 + a.n;
 }
 
-hipEvent_t* g_events = nullptr;  // profiling hook (vdn_vda_set_profile_events)
+// Per-call stage events (vdn_vda_forward_timed): events[i] is recorded after
+// stage i, events[0] before the first kernel; NULL records nothing.
+struct Marks {
+  hipEvent_t* ev;
+  hipError_t operator()(int i, hipStream_t s) const { return ev ? hipEventRecord(ev[i], s) : hipSuccess; }
+};
 
-hipError_t mark(int i, hipStream_t s) {
-  return g_events ? hipEventRecord(g_events[i], s) : hipSuccess;
+// Bytes of the [B, T, U, H, d] and related tensors of a problem.
+struct Sizes {
+  size_t x, beta, alpha, text, beta_text, weight;
+};
+Sizes sizes_of(const vdn_vda_desc* d) {
+  const size_t esz = d->dtype == VDN_BF16 ? 2 : 4;
+  const size_t tok = (size_t)d->B * d->T * d->grid_h * d->grid_w * d->H;
+  const size_t ttok = (size_t)d->B * d->n_text * d->H;
+  return Sizes{tok * d->d_v * esz, tok * esz, (size_t)d->B * d->T * d->H * d->d_k * 4, ttok * d->d_v * esz,
+               ttok * esz, (size_t)d->d_v * 4};
+}
+
+// True if any written range overlaps a read range or another written range.
+bool any_overlap(const Span* outs, size_t n_out, const Span* ins, size_t n_in) {
+  for (size_t a = 0; a < n_out; ++a) {
+    for (size_t b = 0; b < n_in; ++b)
+      if (overlaps(outs[a], ins[b])) return true;
+    for (size_t b = a + 1; b < n_out; ++b)
+      if (overlaps(outs[a], outs[b])) return true;
+  }
+  return false;
 }
 
 vdn_status check(const vdn_vda_desc* d) {
@@ -189,9 +213,80 @@ vdn_status check_proj(const vdn_vda_desc* d, int32_t d_model) {
   if (rows * d_model * 2.0 >= 2147483648.0 || rows * d->H * d->d_v * 2.0 >= 2147483648.0) return VDN_ERR_INVALID_ARG;
   if ((double)d->B * d->T * d->grid_h * d->grid_w * std::max<double>(d_model, (double)d->H * d->d_v) > 9.0e15)
     return VDN_ERR_INVALID_ARG;
+  // the GEMMs' row count B T U and their grids are 32-bit
+  if ((double)d->B * d->T * d->grid_h * d->grid_w >= 2147483648.0) return VDN_ERR_INVALID_ARG;
   return VDN_OK;
 }
 
+}  // namespace vda
+
+namespace vda {
+namespace {
+
+// The forward pass behind vdn_vda_forward and vdn_vda_forward_timed.
+vdn_status forward_impl(const vdn_vda_desc* d, const void* q, const void* k, const void* v, const float* alpha,
+                        const void* beta, const void* k_text, const void* v_text, const void* beta_text,
+                        const void* gate, const float* rms_weight, void* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream, const Marks& mark) {
+  const vdn_status st = check(d);
+  if (st != VDN_OK) return st;
+  const bool epi = (d->flags & VDN_VDA_EPILOGUE) != 0;
+  if (!q || !k || !v || !alpha || !beta || !out) return VDN_ERR_INVALID_ARG;
+  if (d->n_text > 0 && (!k_text || !v_text || !beta_text)) return VDN_ERR_INVALID_ARG;
+  if (epi && !gate) return VDN_ERR_INVALID_ARG;
+  const Problem p = problem(d);
+  const Layout l = make_layout(p);
+  if (!workspace || workspace_bytes < l.total) return VDN_ERR_WORKSPACE;
+  const void* need16[] = {q, k, v, alpha, out, epi ? gate : nullptr,
+                          d->n_text > 0 ? k_text : nullptr, d->n_text > 0 ? v_text : nullptr};
+  for (const void* ptr : need16)
+    if (ptr && !aligned(ptr, 16)) return VDN_ERR_ALIGNMENT;
+  const size_t esz = p.bf16 ? 2 : 4;
+  if (!aligned(beta, esz) || (d->n_text > 0 && !aligned(beta_text, esz)) ||
+      (rms_weight && !aligned(rms_weight, 4)))
+    return VDN_ERR_ALIGNMENT;
+  if (!aligned(workspace, kAlign)) return VDN_ERR_ALIGNMENT;
+  // the output and the workspace are written while the inputs are read
+  const Sizes z = sizes_of(d);
+  const bool text = d->n_text > 0;
+  const Span ins[] = {{q, z.x}, {k, z.x}, {v, z.x}, {alpha, z.alpha}, {beta, z.beta},
+                      {text ? k_text : nullptr, z.text}, {text ? v_text : nullptr, z.text},
+                      {text ? beta_text : nullptr, z.beta_text}, {epi ? gate : nullptr, z.x},
+                      {rms_weight, z.weight}};
+  const Span outs[] = {{out, z.x}, {workspace, l.total}};
+  if (any_overlap(outs, 2, ins, 10)) return VDN_ERR_INVALID_ARG;
+
+  char* ws = static_cast<char*>(workspace);
+  float* stats = reinterpret_cast<float*>(ws + l.stats);
+  float* pinv = reinterpret_cast<float*>(ws + l.pinv);
+  float* s_text = reinterpret_cast<float*>(ws + l.s_text);
+  float* fwd = reinterpret_cast<float*>(ws + l.fwd);
+  float* rev = reinterpret_cast<float*>(ws + l.rev);
+  void* rstates = ws + l.rstates;
+  float* chunk_m = reinterpret_cast<float*>(ws + l.chunk_m);
+  float* chunk_j = reinterpret_cast<float*>(ws + l.chunk_j);
+
+  const int n_video = p.T > 2 ? p.T - 2 : 0;
+  hipError_t e = mark(0, stream);
+  // frame statistics of frames 1..T-2 (anchors are never absorbed) and of the
+  // text frame (slot T) in one launch: the short text blocks run last, in the
+  // final round of the video blocks
+  const GramPart parts[2] = {{k, v, beta, p.T, p.U, 1, n_video, 0},
+                             {k_text, v_text, beta_text, 1, p.L, 0, 1, p.T}};
+  if (e == hipSuccess) e = launch_gram(p, parts, 2, stats, stream);
+  if (e == hipSuccess) e = mark(1, stream);
+  if (e == hipSuccess) e = launch_solve(p, stats, pinv, stream);
+  if (e == hipSuccess) e = mark(2, stream);
+  if (e == hipSuccess) e = launch_scan(p, stats, pinv, alpha, s_text, fwd, rev, chunk_m, chunk_j, stream);
+  if (e == hipSuccess) e = mark(3, stream);
+  if (e == hipSuccess) e = launch_gather(p, s_text, fwd, rev, alpha, rstates, stream);
+  if (e == hipSuccess) e = mark(4, stream);
+  if (e == hipSuccess) e = launch_readout(p, q, gate, rms_weight, rstates, out, stream);
+  if (e == hipSuccess) e = mark(5, stream);
+  return e == hipSuccess ? VDN_OK : VDN_ERR_HIP;
+}
+
+}  // namespace
 }  // namespace vda
 
 using namespace vda;
@@ -237,8 +332,12 @@ vdn_status vdn_vda_prepare(const vdn_vda_desc* d, const void* q, const void* k, 
     if (!ptrs[i]) return VDN_ERR_INVALID_ARG;
   for (int i = 0; i < nreq; ++i)
     if (!aligned(ptrs[i], 16)) return VDN_ERR_ALIGNMENT;
-  if (k_hat == k || v_hat == v || k_hat == v_hat) return VDN_ERR_INVALID_ARG;
-  if (!p.qnorm && (q_hat == q || q_hat == k_hat || q_hat == v_hat)) return VDN_ERR_INVALID_ARG;
+  // outputs are written while inputs are still read: no byte may be shared
+  const Sizes z = sizes_of(d);
+  const size_t ws_ = (size_t)p.H * p.D * 25 * 4, wt_ = (size_t)p.H * p.D * 5 * 4;
+  const Span ins[] = {{k, z.x}, {v, z.x}, {q, z.x}, {wk_s, ws_}, {wk_t, wt_}, {wv_s, ws_}, {wv_t, wt_}};
+  const Span outs[] = {{k_hat, z.x}, {v_hat, z.x}, {q_hat, z.x}};
+  if (any_overlap(outs, 3, ins, 7)) return VDN_ERR_INVALID_ARG;
   if (launch_prep(p, d->grid_h, d->grid_w, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat,
                   stream) != hipSuccess)
     return VDN_ERR_HIP;
@@ -250,54 +349,21 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d, const void* q, const void* k, 
                            const void* v_text, const void* beta_text, const void* gate,
                            const float* rms_weight, void* out, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
-  const vdn_status st = check(d);
-  if (st != VDN_OK) return st;
-  const bool epi = (d->flags & VDN_VDA_EPILOGUE) != 0;
-  if (!q || !k || !v || !alpha || !beta || !out) return VDN_ERR_INVALID_ARG;
-  if (d->n_text > 0 && (!k_text || !v_text || !beta_text)) return VDN_ERR_INVALID_ARG;
-  if (epi && !gate) return VDN_ERR_INVALID_ARG;
-  const Problem p = problem(d);
-  const Layout l = make_layout(p);
-  if (!workspace || workspace_bytes < l.total) return VDN_ERR_WORKSPACE;
-  const void* need16[] = {q, k, v, alpha, out, epi ? gate : nullptr,
-                          d->n_text > 0 ? k_text : nullptr, d->n_text > 0 ? v_text : nullptr};
-  for (const void* ptr : need16)
-    if (ptr && !aligned(ptr, 16)) return VDN_ERR_ALIGNMENT;
-  const size_t esz = p.bf16 ? 2 : 4;
-  if (!aligned(beta, esz) || (d->n_text > 0 && !aligned(beta_text, esz)) ||
-      (rms_weight && !aligned(rms_weight, 4)))
-    return VDN_ERR_ALIGNMENT;
-  if (!aligned(workspace, kAlign)) return VDN_ERR_ALIGNMENT;
+  return forward_impl(d, q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, out, workspace,
+                      workspace_bytes, stream, Marks{nullptr});
+}
 
-  char* ws = static_cast<char*>(workspace);
-  float* stats = reinterpret_cast<float*>(ws + l.stats);
-  float* pinv = reinterpret_cast<float*>(ws + l.pinv);
-  float* s_text = reinterpret_cast<float*>(ws + l.s_text);
-  float* fwd = reinterpret_cast<float*>(ws + l.fwd);
-  float* rev = reinterpret_cast<float*>(ws + l.rev);
-  void* rstates = ws + l.rstates;
-  float* chunk_m = reinterpret_cast<float*>(ws + l.chunk_m);
-  float* chunk_j = reinterpret_cast<float*>(ws + l.chunk_j);
-
-  const int n_video = p.T > 2 ? p.T - 2 : 0;
-  hipError_t e = mark(0, stream);
-  // frame statistics of frames 1..T-2 (anchors are never absorbed) and of the
-  // text frame (slot T) in one launch: the short text blocks run last, in the
-  // final round of the video blocks
-  const GramPart parts[2] = {{k, v, beta, p.T, p.U, 1, n_video, 0},
-                             {k_text, v_text, beta_text, 1, p.L, 0, 1, p.T}};
-  if (e == hipSuccess) e = launch_gram(p, parts, 2, stats, stream);
-  if (e == hipSuccess) e = mark(1, stream);
-  if (e == hipSuccess) e = mark(2, stream);  // the text statistics are part of the launch above
-  if (e == hipSuccess) e = launch_solve(p, stats, pinv, stream);
-  if (e == hipSuccess) e = mark(3, stream);
-  if (e == hipSuccess) e = launch_scan(p, stats, pinv, alpha, s_text, fwd, rev, chunk_m, chunk_j, stream);
-  if (e == hipSuccess) e = mark(4, stream);
-  if (e == hipSuccess) e = launch_gather(p, s_text, fwd, rev, alpha, rstates, stream);
-  if (e == hipSuccess) e = mark(5, stream);
-  if (e == hipSuccess) e = launch_readout(p, q, gate, rms_weight, rstates, out, stream);
-  if (e == hipSuccess) e = mark(6, stream);
-  return e == hipSuccess ? VDN_OK : VDN_ERR_HIP;
+vdn_status vdn_vda_forward_timed(const vdn_vda_desc* d, const void* q, const void* k, const void* v,
+                                 const float* alpha, const void* beta, const void* k_text,
+                                 const void* v_text, const void* beta_text, const void* gate,
+                                 const float* rms_weight, void* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+                                 int32_t n_events) {
+  if (!events || n_events < VDN_VDA_STAGES + 1) return VDN_ERR_INVALID_ARG;
+  for (int i = 0; i <= VDN_VDA_STAGES; ++i)
+    if (!events[i]) return VDN_ERR_INVALID_ARG;
+  return forward_impl(d, q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, out, workspace,
+                      workspace_bytes, stream, Marks{events});
 }
 
 size_t vdn_vda_backward_workspace_bytes(const vdn_vda_desc* d) {
@@ -346,7 +412,13 @@ vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d, const void* q, const 
     if (ptr && !aligned(ptr, 16)) return VDN_ERR_ALIGNMENT;
   if (rms_weight && !aligned(rms_weight, 4)) return VDN_ERR_ALIGNMENT;
   if (!aligned(workspace, kAlign) || !aligned(fwd_workspace, kAlign)) return VDN_ERR_ALIGNMENT;
-  if (dq == q || dq == dy || (epi && (dgate == gate || dgate == dy || dgate == dq))) return VDN_ERR_INVALID_ARG;
+  {
+    const Sizes z = sizes_of(d);
+    const Span ins[] = {{q, z.x}, {epi ? gate : nullptr, z.x}, {rms_weight, z.weight}, {alpha, z.alpha},
+                        {dy, z.x}, {fwd_workspace, fl.total}};
+    const Span outs[] = {{dq, z.x}, {epi ? dgate : nullptr, z.x}, {workspace, bl.total}};
+    if (any_overlap(outs, 3, ins, 6)) return VDN_ERR_INVALID_ARG;
+  }
   const char* fw = static_cast<const char*>(fwd_workspace);
   char* ws = static_cast<char*>(workspace);
   const hipError_t e = launch_backward_readout(
@@ -372,6 +444,12 @@ vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha, cons
   if (!workspace || workspace_bytes < bl.total) return VDN_ERR_WORKSPACE;
   if (!aligned(alpha, 16) || !aligned(dalpha, 16)) return VDN_ERR_ALIGNMENT;
   if (!aligned(workspace, kAlign) || !aligned(fwd_workspace, kAlign)) return VDN_ERR_ALIGNMENT;
+  {
+    const Sizes z = sizes_of(d);
+    const Span ins[] = {{alpha, z.alpha}, {fwd_workspace, fl.total}};
+    const Span outs[] = {{dalpha, z.alpha}, {workspace, bl.total}};
+    if (any_overlap(outs, 2, ins, 2)) return VDN_ERR_INVALID_ARG;
+  }
   const char* fw = static_cast<const char*>(fwd_workspace);
   char* ws = static_cast<char*>(workspace);
   auto f = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
@@ -512,16 +590,10 @@ vdn_status vdn_vda_out_proj(const vdn_vda_desc* d, int32_t d_model, const void* 
   return launch_out_proj(p, d_model, o, w_o, y_in, y, stream) == hipSuccess ? VDN_OK : VDN_ERR_HIP;
 }
 
-vdn_status vdn_vda_set_profile_events(hipEvent_t* events, int n) {
-  if (events && n < VDN_VDA_STAGES + 1) return VDN_ERR_INVALID_ARG;
-  g_events = events;
-  return VDN_OK;
-}
-
 const char* vdn_vda_status_string(vdn_status s) {
   switch (s) {
     case VDN_OK: return "VDN_OK";
-    case VDN_ERR_INVALID_ARG: return "VDN_ERR_INVALID_ARG: bad descriptor, size or NULL pointer";
+    case VDN_ERR_INVALID_ARG: return "VDN_ERR_INVALID_ARG: bad descriptor, size, NULL pointer or overlapping buffers";
     case VDN_ERR_UNSUPPORTED: return "VDN_ERR_UNSUPPORTED: head width not implemented (d_k = d_v in {16,32,64,128})";
     case VDN_ERR_WORKSPACE: return "VDN_ERR_WORKSPACE: workspace missing or too small";
     case VDN_ERR_ALIGNMENT: return "VDN_ERR_ALIGNMENT: pointer misaligned";

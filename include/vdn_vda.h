@@ -22,6 +22,10 @@
  *     anything is enqueued; on any error nothing is enqueued and outputs are
  *     untouched.  VDN_ERR_HIP reports a failed kernel launch (the stream may then
  *     hold part of the work).
+ *   - Every buffer a call writes (outputs and workspace) must share no byte with
+ *     any buffer it reads or with another buffer it writes; the byte ranges the
+ *     shapes give are compared and an overlap is VDN_ERR_INVALID_ARG.  The one
+ *     exception is stated with vdn_vda_out_proj.
  *   - Calls on distinct streams with distinct workspaces may run concurrently.
  *   - NaN/Inf inputs propagate; they are not detected.
  *
@@ -68,8 +72,9 @@ enum {
    * `out` receives the raw readout o = (S_fwd + S_rev) q. */
   VDN_VDA_EPILOGUE = 1u << 0,
   /* Keep every intermediate in the workspace at the offsets that
-   * vdn_vda_workspace_layout() reports.  This build always keeps them, so the
-   * flag changes nothing; it is accepted for callers that rely on it. */
+   * vdn_vda_workspace_layout() reports.  The forward pass always leaves them
+   * there, so the flag asks for nothing beyond the default; it is accepted for
+   * callers that state the requirement. */
   VDN_VDA_DEBUG_KEEP = 1u << 1,
   /* VDA-Gather's decay bridge ([VDN-summary] "전제와 한계" names it without a
    * definition; reading used here): a non-anchor query in chunk c reads
@@ -383,15 +388,26 @@ vdn_status vdn_vda_gates(const vdn_vda_desc* d, int32_t d_model, const void* x, 
 vdn_status vdn_vda_out_proj(const vdn_vda_desc* d, int32_t d_model, const void* o, const void* w_o,
                             const void* y_in, void* y, hipStream_t stream);
 
-/* Profiling hook for benchmarks.  While set, vdn_vda_forward records events[0]
- * on its stream before its first kernel and events[i] after stage i, for
- * i = 1..VDN_VDA_STAGES: frame statistics, text statistics, solve, scan,
- * gather, readout.  The caller creates the n >= VDN_VDA_STAGES + 1 events
- * (hipEventCreate) and keeps them alive while set; pass NULL to clear.
- * Process-wide and not thread-safe.  Returns VDN_ERR_INVALID_ARG if n is too
- * small. */
-enum { VDN_VDA_STAGES = 6 };
-vdn_status vdn_vda_set_profile_events(hipEvent_t* events, int n);
+/*
+ * vdn_vda_forward_timed -- vdn_vda_forward with per-stage timing events, for
+ * benchmarks.  Same arguments, checks and results as vdn_vda_forward; in
+ * addition it records events[0] on `stream` before its first kernel and
+ * events[i] after stage i, i = 1..VDN_VDA_STAGES: frame statistics (the text
+ * frame included), solve, scan, gather, readout.  The caller creates the
+ * n_events >= VDN_VDA_STAGES + 1 events (hipEventCreate); nothing is kept
+ * after the call returns.  Errors: those of vdn_vda_forward, and
+ * VDN_ERR_INVALID_ARG for a NULL events array, too few events or a NULL event.
+ */
+enum { VDN_VDA_STAGES = 5 };
+vdn_status vdn_vda_forward_timed(const vdn_vda_desc* d,
+                                 const void* q, const void* k, const void* v,
+                                 const float* alpha, const void* beta,
+                                 const void* k_text, const void* v_text,
+                                 const void* beta_text,
+                                 const void* gate, const float* rms_weight,
+                                 void* out,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream, hipEvent_t* events, int32_t n_events);
 
 /* Static, human-readable name of a status code. */
 const char* vdn_vda_status_string(vdn_status s);

@@ -360,3 +360,104 @@ def test_adjacent_maps_argument_errors_before_launch():
     assert oproj(y=obase["yin"] + 4096) == bd.VDN_ERR_INVALID_ARG            # y partly over y_in
     assert oproj(yin=obase["yin"] + 8) == bd.VDN_ERR_ALIGNMENT
     assert oproj(d=good(n_text=0, dtype="f32")) == bd.VDN_ERR_UNSUPPORTED
+
+
+def test_forward_rejects_overlapping_buffers():
+    """The output and the workspace are written while every input is read: any
+    shared byte is an error, found before a launch."""
+    desc = good()
+    need = bd.workspace_bytes(desc)
+    gib = 1 << 30
+    names = ["q", "k", "v", "alpha", "beta", "k_text", "v_text", "beta_text", "gate", "rms_weight", "out", "ws"]
+    # 4 GiB apart: every tensor of the 768p clip fits between two bases
+    base = {n: A16 + 4 * gib * i for i, n in enumerate(names)}
+    call = lambda **o: _fwd(desc, [dict(base, **o)[n] for n in names], need)
+    xbytes = 60 * 4032 * 24 * 128 * 2
+    assert call(out=base["q"] + xbytes - 4096) == bd.VDN_ERR_INVALID_ARG       # out's head over q's tail
+    assert call(out=base["gate"] - xbytes + 4096) == bd.VDN_ERR_INVALID_ARG    # out's tail over the gate
+    assert call(ws=base["k"] + 256 * 1024) == bd.VDN_ERR_INVALID_ARG           # workspace inside k
+    assert call(out=base["ws"] + need - 16) == bd.VDN_ERR_INVALID_ARG          # out over the workspace's end
+    assert call(ws=base["alpha"] + 256) == bd.VDN_ERR_INVALID_ARG              # workspace over alpha
+    assert call(out=base["rms_weight"] - xbytes + 16) == bd.VDN_ERR_INVALID_ARG  # out over the RMSNorm gain
+    # ranges that only touch (one ends where the next starts) do not overlap;
+    # the call then fails later, on a check that is independent of the ranges
+    assert call(out=base["q"] + xbytes, q=base["q"] + 8) == bd.VDN_ERR_ALIGNMENT
+
+
+def test_forward_timed_checks_its_events():
+    lib = bd.lib()
+    desc = good()
+    need = bd.workspace_bytes(desc)
+    P = [ctypes.c_void_p(p) for p in _ptrs()]
+    ev = (ctypes.c_void_p * 6)(*([0x1234] * 6))
+    few = (ctypes.c_void_p * 5)(*([0x1234] * 5))
+    nul = (ctypes.c_void_p * 6)(*([0x1234] * 5 + [0]))
+    call = lambda arr, n: lib.vdn_vda_forward_timed(ctypes.byref(desc), *P[:11], P[11], need, None,
+                                                    ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None, n)
+    assert call(None, 6) == bd.VDN_ERR_INVALID_ARG
+    assert call(few, 5) == bd.VDN_ERR_INVALID_ARG
+    assert call(nul, 6) == bd.VDN_ERR_INVALID_ARG
+    # valid events: the forward's own checks still run before anything is recorded
+    P2 = [ctypes.c_void_p(p) for p in _ptrs(q=0)]
+    assert lib.vdn_vda_forward_timed(ctypes.byref(desc), *P2[:11], P2[11], need, None,
+                                     ctypes.cast(ev, ctypes.c_void_p), 6) == bd.VDN_ERR_INVALID_ARG
+
+
+def test_prepare_rejects_overlapping_buffers():
+    lib = bd.lib()
+    desc = good(epilogue=False)
+    gib = 1 << 30
+    xbytes = 60 * 4032 * 24 * 128 * 2
+    base = [A16 + 4 * gib * i for i in range(10)]   # q k v wks wkt wvs wvt q_hat k_hat v_hat
+
+    def call(**o):
+        p = list(base)
+        for i, v in o.items():
+            p[int(i[1:])] = v
+        return lib.vdn_vda_prepare(ctypes.byref(desc), *[ctypes.c_void_p(x) for x in p], None)
+
+    assert call(a8=base[1] + 4096) == bd.VDN_ERR_INVALID_ARG          # k_hat inside k
+    assert call(a9=base[8] + xbytes - 4096) == bd.VDN_ERR_INVALID_ARG  # v_hat over k_hat's tail
+    assert call(a7=base[3] - xbytes + 64) == bd.VDN_ERR_INVALID_ARG    # q_hat over the spatial weights
+
+
+def test_backward_rejects_overlapping_buffers():
+    lib = bd.lib()
+    desc = good()
+    fw = bd.workspace_bytes(desc)
+    bw = bd.backward_workspace_bytes(desc)
+    names = ["q", "gate", "rms", "alpha", "dy", "fws", "dq", "dgate", "ws"]
+    base = {n: A16 + (1 << 34) * i for i, n in enumerate(names)}
+    xbytes = 60 * 4032 * 24 * 128 * 2
+
+    def call(**over):
+        p = dict(base, rms=0)
+        p.update(over)
+        P = [ctypes.c_void_p(p[n]) if p[n] else None for n in names]
+        return lib.vdn_vda_backward_readout(ctypes.byref(desc), P[0], P[1], P[2], P[3], P[4], P[5], fw,
+                                            P[6], P[7], P[8], bw, None)
+
+    assert call(dq=base["q"] + 4096) == bd.VDN_ERR_INVALID_ARG              # dq inside q
+    assert call(dgate=base["dq"] + xbytes - 4096) == bd.VDN_ERR_INVALID_ARG  # two outputs
+    assert call(ws=base["fws"] + 256) == bd.VDN_ERR_INVALID_ARG            # workspace over the forward's
+    assert call(dq=base["ws"] + bw - 4096) == bd.VDN_ERR_INVALID_ARG        # dq over the workspace's end
+    snames = ["alpha", "fws", "dalpha", "ws"]
+    sb = {n: A16 + (1 << 34) * i for i, n in enumerate(snames)}
+
+    def scall(**over):
+        p = dict(sb, **over)
+        return lib.vdn_vda_backward_scan(ctypes.byref(desc), ctypes.c_void_p(p["alpha"]), ctypes.c_void_p(p["fws"]),
+                                         fw, ctypes.c_void_p(p["dalpha"]), ctypes.c_void_p(p["ws"]), bw, None)
+
+    assert scall(dalpha=sb["alpha"] + 256) == bd.VDN_ERR_INVALID_ARG
+    assert scall(ws=sb["fws"] + fw - 256) == bd.VDN_ERR_INVALID_ARG
+
+
+def test_adjacent_row_count_is_32_bit():
+    """The adjacent maps' GEMMs take B T U rows in 32-bit arithmetic."""
+    lib = bd.lib()
+    ok = good(n_text=0, T=32767, grid_h=256, grid_w=256, H=1, d=16)     # B T U = 2^31 - 65536
+    assert lib.vdn_vda_gates_workspace_bytes(ctypes.byref(ok), 16) > 0
+    big = good(n_text=0, T=32768, grid_h=256, grid_w=256, H=1, d=16)    # B T U = 2^31
+    assert bd.validate(big) == bd.VDN_OK                      # the forward itself accepts it
+    assert lib.vdn_vda_gates_workspace_bytes(ctypes.byref(big), 16) == 0

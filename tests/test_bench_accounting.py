@@ -19,10 +19,18 @@ def test_768p_bytes():
     assert bench.algorithmic_bytes(w, "readout") == tok * 3 * 128 * 2 == 4_459_069_440
     # gram: K, V and beta of the 58 interior frames
     assert bench.algorithmic_bytes(w, "gram") == 58 * 4032 * 24 * (2 * 128 + 1) * 2
-    # whole job: Q, K, V, gate, beta, O per token-head; alpha per frame (fp32);
-    # the 256 text tokens' K, V, beta
-    assert bench.job_bytes(w) == (tok * (5 * 128 + 1) * 2 + 60 * 24 * 128 * 4
-                                  + 256 * 24 * (2 * 128 + 1) * 2) == 7_447_289_856
+    # whole job: Q, gate and O of every frame; K, V, beta and alpha (fp32) of
+    # the 58 frames the scans absorb (the anchors' are never read); the 256
+    # text tokens' K, V, beta
+    inner = 58 * 4032 * 24
+    assert bench.job_bytes(w) == (tok * 3 * 128 * 2 + inner * (2 * 128 + 1) * 2 + 58 * 24 * 128 * 4
+                                  + 256 * 24 * (2 * 128 + 1) * 2) == 7_347_787_776
+    # the job's gram share is exactly the gram stage's bytes plus the text tokens
+    assert bench.algorithmic_bytes(w, "gram") == inner * (2 * 128 + 1) * 2
+    # matrix-core work: [A; B] is 2d x d per token of the 58 frames and the
+    # text, the readout d x d per token
+    assert bench.mfma_flops(w, "gram") == 2 * (inner + 24 * 256) * 2 * 128 * 128
+    assert bench.mfma_flops(w, "readout") == 2 * tok * 128 * 128
 
 
 def test_long_clip_prep_accounting():
@@ -35,6 +43,33 @@ def test_long_clip_prep_accounting():
     # arithmetic intensity above the fp32 ridge: the prep is ALU-bound
     ridge = bench.VALU_F32_PEAK_TFLOPS * 1e12 / (bench.HBM_PEAK_GBS * 1e9)
     assert bench.prep_flops(w) / (bench.algorithmic_bytes(w, "prep") / 2) > ridge
+
+
+def test_long_clip_job_bytes():
+    """The long clip reads K and V of every frame (the temporal taps reach the
+    anchors); the prepared K^, V^ are intermediates and are not counted."""
+    w = synth.WORKLOADS["long_prep_bf16"]
+    tok = 120 * 4032 * 24
+    inner = 118 * 4032 * 24
+    want = tok * 5 * 128 * 2 + inner * 2 + 118 * 24 * 128 * 4 + 512 * 24 * (2 * 128 + 1) * 2
+    assert bench.job_bytes(w) == want == 14_894_168_064
+    # no K^, V^ round trip in the job's bytes
+    assert bench.job_bytes(w) < bench.algorithmic_bytes(w, "prep") + tok * 3 * 128 * 2
+
+
+def test_mfma_record_fields():
+    w = synth.WORKLOADS["768p_bf16"]
+    r = bench.mfma_record(w, "readout", 0.5)
+    assert r["peak_TFLOPs"] == 2500.0
+    assert abs(r["achieved_TFLOPs"] - bench.mfma_flops(w, "readout") / 0.5e-3 / 1e12) < 0.1
+    assert abs(r["frac"] - r["achieved_TFLOPs"] / 2500.0) < 1e-3
+    f = synth.WORKLOADS["stress_f32"]
+    assert bench.mfma_record(f, "gram", 1.0)["peak_TFLOPs"] == 157.3
+
+
+def test_host_info_fields():
+    h = bench.host_info()
+    assert set(h) == {"cpu_model", "blas"} and h["cpu_model"] and h["blas"]
 
 
 def test_more_than_one_gpu_is_refused():

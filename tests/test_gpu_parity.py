@@ -54,23 +54,29 @@ def _check_intermediates(inter, ref, w, heads, tol):
         assert G.mat_rel_err(inter["R"][:, hs, 2:], ref["R"][:, :, 2:]) <= tol, "R"
 
 
-def _run_case(w, heads=None, rms=False, check_inter=True, bridge=False, scan=None):
+def _run_case(w, heads=None, rms=False, check_inter=True, bridge=False, scan=None, group=None):
+    """Forward (raw readout with intermediates, then with RMSNorm + gate) against
+    the oracle on ``heads`` (all by default), the oracle called on ``group``
+    heads at a time to bound host memory."""
     x = synth.make_inputs(w)
     heads = list(range(w.H)) if heads is None else heads
+    groups = [heads] if group is None else [heads[i:i + group] for i in range(0, len(heads), group)]
     rw = np.random.default_rng(5).uniform(0.5, 1.5, w.d) if rms else None
     tol = G.TOL[w.dtype]
-    # raw readout, with intermediates
     out, ws, desc, dev = G.run_forward(x, w, epilogue=False, bridge=bridge, scan=scan)
-    ref = _oracle_heads(x, w, heads, gate=True, rms_weight=rw, bridge=bridge)
-    got = G.to_host_f64(out[:, :, :, heads])
-    err_o = G.slice_rel_err(got, ref["o"])
-    if check_inter:
-        _check_intermediates(G.intermediates(ws, desc, w), ref, w, heads, tol)
-    # with RMSNorm + gate
+    inter = G.intermediates(ws, desc, w) if check_inter else None
+    del ws
     out2, _, _, _ = G.run_forward(x, w, epilogue=True, rms_weight=rw, dev_inputs=dev, bridge=bridge, scan=scan)
-    got2 = G.to_host_f64(out2[:, :, :, heads])
-    err_y = G.slice_rel_err(got2, ref["y"])
-    G.say(f"{w.name} T={w.T} U={w.U} H={w.H} d={w.d} scan={scan}: err(o)={err_o:.3e} err(y)={err_y:.3e} tol={tol}")
+    err_o = err_y = 0.0
+    for grp in groups:
+        ref = _oracle_heads(x, w, grp, gate=True, rms_weight=rw, bridge=bridge)
+        err_o = max(err_o, G.slice_rel_err(G.to_host_f64(out[:, :, :, grp]), ref["o"]))
+        err_y = max(err_y, G.slice_rel_err(G.to_host_f64(out2[:, :, :, grp]), ref["y"]))
+        if check_inter:
+            _check_intermediates(inter, ref, w, grp, tol)
+        del ref
+    G.say(f"{w.name} T={w.T} U={w.U} H={w.H} d={w.d} scan={scan} heads={len(heads)}: "
+          f"err(o)={err_o:.3e} err(y)={err_y:.3e} tol={tol}")
     assert err_o <= tol, err_o
     assert err_y <= tol, err_y
     return err_o, err_y
@@ -88,9 +94,11 @@ def test_workload_full_oracle(name, scan):
     _run_case(synth.WORKLOADS[name], rms=(name == "small_bf16"), scan=scan)
 
 
-def test_768p_full_size_sampled_heads():
-    """The benchmarked workload at full size; the oracle checks two whole heads."""
-    _run_case(synth.WORKLOADS["768p_bf16"], heads=[0, 23])
+def test_768p_full_size_every_head():
+    """The benchmarked workload at full size, in the launch configuration the
+    benchmark times (the library's own scan choice): every one of the 24 heads
+    against the oracle, the output and every intermediate."""
+    _run_case(synth.WORKLOADS["768p_bf16"], group=4)
 
 
 @pytest.mark.parametrize("scan", SCANS)
@@ -115,6 +123,13 @@ EDGE = {
     "chunk3_bf16": synth.WORKLOADS["small_bf16"].scaled(name="chunk3_bf16", H=2, T=20, grid_h=4, grid_w=10, chunk=3, L=8),
     "chunk1_f32": synth.WORKLOADS["tiny_f32"].scaled(name="chunk1_f32", T=9, chunk=1),
     "batch2_bf16": synth.WORKLOADS["768p_bf16"].scaled(name="batch2_bf16", B=2, H=2, T=16, grid_h=6, grid_w=11, L=12),
+    # one and two tokens per frame: the one-token regime where a frame update is
+    # the token delta rule with beta / (1 + beta) ([VDN-summary] "어떻게 쓰나"),
+    # each a single valid row in a 64-token statistics tile and a 32-token readout tile
+    "U1_bf16_128": synth.WORKLOADS["768p_bf16"].scaled(name="U1_bf16_128", H=2, T=12, grid_h=1, grid_w=1, L=3),
+    "U2_bf16_128": synth.WORKLOADS["768p_bf16"].scaled(name="U2_bf16_128", H=2, T=13, grid_h=1, grid_w=2, L=3),
+    "U1_f32_16": synth.WORKLOADS["tiny_f32"].scaled(name="U1_f32_16", T=12, grid_h=1, grid_w=1, L=2),
+    "U2_f32_16": synth.WORKLOADS["tiny_f32"].scaled(name="U2_f32_16", T=11, grid_h=2, grid_w=1, L=2),
 }
 
 
@@ -138,21 +153,26 @@ BRIDGE = {
 @pytest.mark.parametrize("name", list(BRIDGE))
 def test_decay_bridge(name):
     w = BRIDGE[name]
-    _run_case(w, heads=[0, w.H - 1] if w.H > 4 else None, bridge=True)
+    _run_case(w, bridge=True, group=4)
 
 
 def test_zero_writes_give_text_only_readout():
-    """beta = 0 on every video token and alpha = 1: every frame reads S_T q."""
+    """beta = 0 on every video token and alpha = 1: every frame reads S_T q, with
+    S_T the oracle's text state (the frame update from a zero state over the
+    text tokens, [VDN-summary] "어떻게 동작하나")."""
     w = EDGE["ragged_bf16_128"]
     x = synth.make_inputs(w)
     x["beta"][:] = 0
     x["alpha"][:] = 1.0
-    out, ws, desc, _ = G.run_forward(x, w, epilogue=False)
-    ST = G.intermediates(ws, desc, w)["S_T"]
-    q = G.oracle_view({"q": x["q"]}, w)["q"]
-    want = np.einsum("btuhk,bhvk->btuhv", q, ST)
+    out, _, _, _ = G.run_forward(x, w, epilogue=False)
+    f = G.oracle_view({k: x[k] for k in ("q", "k_text", "v_text", "beta_text")}, w)
+    ST = np.stack([np.stack([oracle.text_state(f["k_text"][b, :, h], f["v_text"][b, :, h], f["beta_text"][b, :, h])
+                             for h in range(w.H)]) for b in range(w.B)])
+    want = np.einsum("btuhk,bhvk->btuhv", f["q"], ST)
     got = G.to_host_f64(out)
-    assert G.slice_rel_err(got, want) <= G.TOL[w.dtype]
+    err = G.slice_rel_err(got, want)
+    G.say(f"zero writes: err={err:.3e}")
+    assert err <= G.TOL[w.dtype]
 
 
 def test_deterministic_rerun():
@@ -237,23 +257,66 @@ def _fused_query_prepare(dev, w, kh, vh):
     return kf, vf
 
 
-def test_long_prep_full_size_sampled_head():
-    """The long clip at full size: prepare + forward, then the same with the query's
-    L2 normalisation fused into the readout; the oracle checks one whole head."""
+_LONG = {}
+
+
+def _long_clip():
+    """The long clip at full size, run once for the tests below: prepare, the
+    forward on the prepared features, the prepare that leaves the query to the
+    readout (checked bit-identical on K^, V^) and the forward with the fused
+    query normalisation.  Both forwards run in the benchmarked configuration."""
+    import torch
+    from frame_wise_delta_02_amd import binding as bd
+    if _LONG:
+        return _LONG
     w = synth.WORKLOADS["long_prep_bf16"]
-    x, dev, (qh, kh, vh), prepared = _prep_case(w, heads=[5])
-    dev2 = dict(dev, q=qh, k=kh, v=vh)
-    out, _, _, _ = G.run_forward(x, w, epilogue=True, dev_inputs=dev2)
-    ref = _oracle_heads(x, w, [5], gate=True, prepared={**prepared, "gate": x["gate"][:, :, :, [5]]})
-    err = G.slice_rel_err(G.to_host_f64(out[:, :, :, [5]]), ref["y"])
-    G.say(f"long_prep_bf16 head 5: err(y)={err:.3e}")
-    assert err <= G.TOL["bf16"], err
-    del out, qh
+    x = synth.make_inputs(w)
+    dev = {k: G.to_device(v, w.dtype) for k, v in x.items()}
+    G.say(f"prepare {w.name} T={w.T} grid={w.grid_h}x{w.grid_w} H={w.H}")
+    qh, kh, vh = bd.prepare(dev["q"], dev["k"], dev["v"], dev["wk_s"], dev["wk_t"], dev["wv_s"], dev["wv_t"],
+                            grid=(w.grid_h, w.grid_w))
+    torch.cuda.synchronize()
+    out, _, _, _ = G.run_forward(x, w, epilogue=True, dev_inputs=dict(dev, q=qh, k=kh, v=vh))
     kf, vf = _fused_query_prepare(dev, w, kh, vh)
+    del kh, vh
     out2, _, _, _ = G.run_forward(x, w, epilogue=True, dev_inputs=dict(dev, k=kf, v=vf), query_l2=True)
-    err2 = G.slice_rel_err(G.to_host_f64(out2[:, :, :, [5]]), ref["y"])
-    G.say(f"long_prep_bf16 head 5, fused query L2: err(y)={err2:.3e}")
-    assert err2 <= G.TOL["bf16"], err2
+    _LONG.update(w=w, x=x, prepared=(qh, kf, vf), out=out, out_fused=out2)
+    return _LONG
+
+
+def _long_clip_heads(heads):
+    L = _long_clip()
+    w, x = L["w"], L["x"]
+    qh, kh, vh = L["prepared"]
+    for h in heads:
+        f = G.oracle_view({n: x[n][:, :, :, h:h + 1] for n in ("q", "k", "v")}, w)
+        wsl = lambda n: x[n][h * w.d:(h + 1) * w.d].astype(np.float64)
+        rq, rk, rv = oracle.prep(f["q"][0], f["k"][0], f["v"][0], wsl("wk_s"), wsl("wk_t"), wsl("wv_s"),
+                                 wsl("wv_t"), w.grid_h, w.grid_w, l2_eps=1e-6)
+        perr = {n: G.slice_rel_err(G.to_host_f64(t[:, :, :, h:h + 1]), r[None])
+                for n, r, t in (("q", rq, qh), ("k", rk, kh), ("v", rv, vh))}
+        prepared = {"q": rq[None], "k": rk[None], "v": rv[None], "gate": x["gate"][:, :, :, [h]]}
+        ref = _oracle_heads(x, w, [h], gate=True, prepared=prepared)
+        e1 = G.slice_rel_err(G.to_host_f64(L["out"][:, :, :, [h]]), ref["y"])
+        e2 = G.slice_rel_err(G.to_host_f64(L["out_fused"][:, :, :, [h]]), ref["y"])
+        G.say(f"long_prep_bf16 head {h}: prep {perr}, err(y)={e1:.3e}, fused query L2 err(y)={e2:.3e}")
+        for n, e in perr.items():
+            assert e <= 1e-2, (h, n, e)
+        assert e1 <= G.TOL["bf16"], (h, e1)
+        assert e2 <= G.TOL["bf16"], (h, e2)
+
+
+# The long clip at full size: one head from each group of eight (the prep's and
+# the scan's blocks map heads to XCDs by h mod 8) and from both ends.
+def test_long_prep_full_size_heads_a():
+    _long_clip_heads([0, 5, 8])
+
+
+def test_long_prep_full_size_heads_b():
+    try:
+        _long_clip_heads([15, 16, 23])
+    finally:
+        _LONG.clear()
 
 
 # The query's L2 normalisation fused into the readout (VDN_VDA_QUERY_L2): raw q
