@@ -24,7 +24,7 @@ VDN_VDA_SCAN_CHUNKS = 1 << 5
 _SCAN_FLAGS = {None: 0, "frames": VDN_VDA_SCAN_FRAMES, "chunks": VDN_VDA_SCAN_CHUNKS}
 
 EXPORTS = ("vdn_vda_validate", "vdn_vda_workspace_bytes", "vdn_vda_workspace_layout",
-           "vdn_vda_prepare", "vdn_vda_forward", "vdn_vda_forward_timed",
+           "vdn_vda_prepare", "vdn_vda_forward", "vdn_vda_forward_timed", "vdn_vda_forward_noalloc",
            "vdn_vda_status_string", "vdn_vda_backward_workspace_bytes",
            "vdn_vda_backward_workspace_layout", "vdn_vda_backward_readout", "vdn_vda_backward_scan",
            "vdn_vda_backward_gram", "vdn_vda_gates_workspace_bytes", "vdn_vda_gates", "vdn_vda_out_proj")
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.vdn_vda_forward.restype = ctypes.c_int
         L.vdn_vda_forward_timed.argtypes = [dp] + [p] * 12 + [sz, p, p, ctypes.c_int32]
         L.vdn_vda_forward_timed.restype = ctypes.c_int
+        L.vdn_vda_forward_noalloc.argtypes = [dp] + [p] * 12
+        L.vdn_vda_forward_noalloc.restype = ctypes.c_int
         L.vdn_vda_status_string.argtypes = [ctypes.c_int]
         L.vdn_vda_status_string.restype = ctypes.c_char_p
         L.vdn_vda_backward_workspace_bytes.argtypes = [dp]
@@ -205,6 +207,33 @@ def forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weig
         st = lib().vdn_vda_forward_timed(*args, ctypes.cast(arr, ctypes.c_void_p), len(events))
     if st != VDN_OK:
         raise VdaError(st, "vdn_vda_forward")
+    return out
+
+
+def forward_noalloc(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weight=None, *,
+                    grid, chunk=5, epilogue=True, rms_eps=1e-6, out=None, bridge=False, query_l2=False,
+                    l2_eps=1e-6, scan=None):
+    """vdn_vda_forward_noalloc: the forward pass with the library's own device
+    array as its workspace (no workspace argument); returns ``out``."""
+    import torch
+    B, T, U, H, d = q.shape
+    L = 0 if k_text is None else k_text.shape[1]
+    dev = q.device
+    for name, x in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta),
+                    ("k_text", k_text), ("v_text", v_text), ("beta_text", beta_text),
+                    ("gate", gate), ("rms_weight", rms_weight), ("out", out)):
+        _check(x, name, dev)
+    desc = make_desc(B, H, T, grid[0], grid[1], d, L, chunk, _dtype_of(q), epilogue, l2_eps=l2_eps,
+                     rms_eps=rms_eps,
+                     flags=(VDN_VDA_EPILOGUE if epilogue else 0) | (VDN_VDA_DECAY_BRIDGE if bridge else 0)
+                     | (VDN_VDA_QUERY_L2 if query_l2 else 0) | _SCAN_FLAGS[scan])
+    if out is None:
+        out = torch.empty((B, T, U, H, d), dtype=q.dtype, device=dev)
+    st = lib().vdn_vda_forward_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                       _ptr(k_text), _ptr(v_text), _ptr(beta_text),
+                                       _ptr(gate) if epilogue else None, _ptr(rms_weight), _ptr(out), _stream())
+    if st != VDN_OK:
+        raise VdaError(st, "vdn_vda_forward_noalloc")
     return out
 
 

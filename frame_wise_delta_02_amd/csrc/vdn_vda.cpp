@@ -4,12 +4,44 @@
 #include <algorithm>
 #include <string.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "vda_internal.h"
 #include "vdn_vda.h"
 
 namespace vda {
+
+// Workspace of vdn_vda_forward_noalloc, for callers that cannot allocate: one
+// array per GPU, created when the library's code object is loaded on that GPU
+// and held until the process ends.  Host code never passes `scratch` itself to
+// a kernel (on the host the name is a stand-in, not the device address): the
+// address each GPU gives for it is looked up once per device and kept.
+__device__ __align__(256) uint8_t scratch[VDN_VDA_NOALLOC_MAX_WORKSPACE];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device.
+static hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -223,29 +255,29 @@ vdn_status check_proj(const vdn_vda_desc* d, int32_t d_model) {
 namespace vda {
 namespace {
 
-// The forward pass behind vdn_vda_forward and vdn_vda_forward_timed.
-vdn_status forward_impl(const vdn_vda_desc* d, const void* q, const void* k, const void* v, const float* alpha,
+// Every check of the forward pass's arguments; with have_ws false the
+// workspace is left out (the no-allocation entry point finds its own later).
+vdn_status forward_args(const vdn_vda_desc* d, const void* q, const void* k, const void* v, const float* alpha,
                         const void* beta, const void* k_text, const void* v_text, const void* beta_text,
-                        const void* gate, const float* rms_weight, void* out, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream, const Marks& mark) {
+                        const void* gate, const float* rms_weight, const void* out, const void* workspace,
+                        size_t workspace_bytes, bool have_ws) {
   const vdn_status st = check(d);
   if (st != VDN_OK) return st;
   const bool epi = (d->flags & VDN_VDA_EPILOGUE) != 0;
   if (!q || !k || !v || !alpha || !beta || !out) return VDN_ERR_INVALID_ARG;
   if (d->n_text > 0 && (!k_text || !v_text || !beta_text)) return VDN_ERR_INVALID_ARG;
   if (epi && !gate) return VDN_ERR_INVALID_ARG;
-  const Problem p = problem(d);
-  const Layout l = make_layout(p);
-  if (!workspace || workspace_bytes < l.total) return VDN_ERR_WORKSPACE;
+  const Layout l = make_layout(problem(d));
+  if (have_ws && (!workspace || workspace_bytes < l.total)) return VDN_ERR_WORKSPACE;
   const void* need16[] = {q, k, v, alpha, out, epi ? gate : nullptr,
                           d->n_text > 0 ? k_text : nullptr, d->n_text > 0 ? v_text : nullptr};
   for (const void* ptr : need16)
     if (ptr && !aligned(ptr, 16)) return VDN_ERR_ALIGNMENT;
-  const size_t esz = p.bf16 ? 2 : 4;
+  const size_t esz = d->dtype == VDN_BF16 ? 2 : 4;
   if (!aligned(beta, esz) || (d->n_text > 0 && !aligned(beta_text, esz)) ||
       (rms_weight && !aligned(rms_weight, 4)))
     return VDN_ERR_ALIGNMENT;
-  if (!aligned(workspace, kAlign)) return VDN_ERR_ALIGNMENT;
+  if (have_ws && !aligned(workspace, kAlign)) return VDN_ERR_ALIGNMENT;
   // the output and the workspace are written while the inputs are read
   const Sizes z = sizes_of(d);
   const bool text = d->n_text > 0;
@@ -253,8 +285,22 @@ vdn_status forward_impl(const vdn_vda_desc* d, const void* q, const void* k, con
                       {text ? k_text : nullptr, z.text}, {text ? v_text : nullptr, z.text},
                       {text ? beta_text : nullptr, z.beta_text}, {epi ? gate : nullptr, z.x},
                       {rms_weight, z.weight}};
-  const Span outs[] = {{out, z.x}, {workspace, l.total}};
+  const Span outs[] = {{out, z.x}, {have_ws ? workspace : nullptr, l.total}};
   if (any_overlap(outs, 2, ins, 10)) return VDN_ERR_INVALID_ARG;
+  return VDN_OK;
+}
+
+// The forward pass behind vdn_vda_forward, vdn_vda_forward_timed and
+// vdn_vda_forward_noalloc.
+vdn_status forward_impl(const vdn_vda_desc* d, const void* q, const void* k, const void* v, const float* alpha,
+                        const void* beta, const void* k_text, const void* v_text, const void* beta_text,
+                        const void* gate, const float* rms_weight, void* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream, const Marks& mark) {
+  const vdn_status st = forward_args(d, q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, out,
+                                     workspace, workspace_bytes, true);
+  if (st != VDN_OK) return st;
+  const Problem p = problem(d);
+  const Layout l = make_layout(p);
 
   char* ws = static_cast<char*>(workspace);
   float* stats = reinterpret_cast<float*>(ws + l.stats);
@@ -364,6 +410,22 @@ vdn_status vdn_vda_forward_timed(const vdn_vda_desc* d, const void* q, const voi
     if (!events[i]) return VDN_ERR_INVALID_ARG;
   return forward_impl(d, q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, out, workspace,
                       workspace_bytes, stream, Marks{events});
+}
+
+vdn_status vdn_vda_forward_noalloc(const vdn_vda_desc* d, const void* q, const void* k, const void* v,
+                                   const float* alpha, const void* beta, const void* k_text,
+                                   const void* v_text, const void* beta_text, const void* gate,
+                                   const float* rms_weight, void* out, hipStream_t stream) {
+  // every argument check first: nothing touches the GPU for a call that fails one
+  const vdn_status st = forward_args(d, q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, out,
+                                     nullptr, 0, false);
+  if (st != VDN_OK) return st;
+  const size_t need = make_layout(problem(d)).total;
+  if (need > (size_t)VDN_VDA_NOALLOC_MAX_WORKSPACE) return VDN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return VDN_ERR_HIP;
+  return forward_impl(d, q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, out, ws,
+                      (size_t)VDN_VDA_NOALLOC_MAX_WORKSPACE, stream, Marks{nullptr});
 }
 
 size_t vdn_vda_backward_workspace_bytes(const vdn_vda_desc* d) {

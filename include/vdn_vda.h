@@ -16,7 +16,8 @@
  *   - Pointers are DEVICE pointers unless marked "host".  Every tensor is dense,
  *     row-major, contiguous, and 16-byte aligned (the workspace 256-byte).
  *   - The caller owns every buffer, including the workspace.  The library never
- *     allocates or frees device memory and keeps no state between calls.
+ *     allocates or frees device memory and keeps no state between calls (the
+ *     one exception: vdn_vda_forward_noalloc's own device array).
  *   - Work is enqueued on `stream` and the call returns without synchronising.
  *   - The return value is the only error channel.  Arguments are checked before
  *     anything is enqueued; on any error nothing is enqueued and outputs are
@@ -408,6 +409,35 @@ vdn_status vdn_vda_forward_timed(const vdn_vda_desc* d,
                                  void* out,
                                  void* workspace, size_t workspace_bytes,
                                  hipStream_t stream, hipEvent_t* events, int32_t n_events);
+
+/*
+ * vdn_vda_forward_noalloc -- vdn_vda_forward without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments
+ * (less the workspace), checks and results as vdn_vda_forward; the forward's
+ * workspace is instead a device array inside the library, of
+ * VDN_VDA_NOALLOC_MAX_WORKSPACE bytes, that every GPU the library runs on
+ * holds from the library's load until the process ends.  The call allocates
+ * and frees nothing.  Problems whose workspace (vdn_vda_workspace_bytes) is
+ * larger return VDN_ERR_WORKSPACE before anything touches the GPU; 64 MiB
+ * covers, e.g., 8 heads x 40 frames x 1560 tokens at d = 64, or one GPU's
+ * 3-head share of the 768p clip.  The array's address on the current device is
+ * looked up on the first call on that device (VDN_ERR_HIP if that fails) and
+ * kept: this entry point, unlike the others, keeps that per-device address
+ * between calls.  Every call on one GPU shares that GPU's array and leaves
+ * its intermediates there (at vdn_vda_workspace_layout's offsets) until the
+ * next call: calls that overlap in time on one GPU (two streams, two threads)
+ * race on it and must be serialised by the caller.  The stream must belong to
+ * the current device.
+ */
+#define VDN_VDA_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+vdn_status vdn_vda_forward_noalloc(const vdn_vda_desc* d,
+                                   const void* q, const void* k, const void* v,
+                                   const float* alpha, const void* beta,
+                                   const void* k_text, const void* v_text,
+                                   const void* beta_text,
+                                   const void* gate, const float* rms_weight,
+                                   void* out, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* vdn_vda_status_string(vdn_status s);

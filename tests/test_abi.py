@@ -461,3 +461,27 @@ def test_adjacent_row_count_is_32_bit():
     big = good(n_text=0, T=32768, grid_h=256, grid_w=256, H=1, d=16)    # B T U = 2^31
     assert bd.validate(big) == bd.VDN_OK                      # the forward itself accepts it
     assert lib.vdn_vda_gates_workspace_bytes(ctypes.byref(big), 16) == 0
+
+
+def test_forward_noalloc_checks_before_touching_the_gpu():
+    """vdn_vda_forward_noalloc checks every argument, and its workspace against
+    the library's own array, before any HIP call."""
+    lib = bd.lib()
+    names = ["q", "k", "v", "alpha", "beta", "k_text", "v_text", "beta_text", "gate", "rms_weight", "out"]
+    gib = 1 << 30
+    base = {n: A16 + 4 * gib * i for i, n in enumerate(names)}
+
+    def call(desc, **over):
+        p = dict(base, **over)
+        return lib.vdn_vda_forward_noalloc(ctypes.byref(desc), *[ctypes.c_void_p(p[n]) if p[n] else None
+                                                                for n in names], None)
+
+    assert call(good(), q=0) == bd.VDN_ERR_INVALID_ARG
+    assert call(good(), q=base["q"] + 8) == bd.VDN_ERR_ALIGNMENT
+    assert call(good(), out=base["gate"] + 4096) == bd.VDN_ERR_INVALID_ARG
+    # the 768p clip needs ~400 MiB of workspace, beyond the 64 MiB array
+    assert bd.workspace_bytes(good()) > 64 << 20
+    assert call(good()) == bd.VDN_ERR_WORKSPACE
+    share = good(H=8, T=60)
+    assert bd.workspace_bytes(share) > 64 << 20 and call(share) == bd.VDN_ERR_WORKSPACE
+    assert call(good(d=48)) == bd.VDN_ERR_UNSUPPORTED
