@@ -653,7 +653,12 @@ vdn_status vdn_vda_out_proj(const vdn_vda_desc* d, int32_t d_model, const void* 
 }
 
 const char* vdn_vda_status_string(vdn_status s) {
-  switch (s) {
+  static_assert(sizeof(vdn_status) == sizeof(int), "vdn_status is an int-sized enum");
+  // callers may pass any integer (C, ctypes); read its bits rather than load an
+  // enum value outside the enumeration's range
+  int code;
+  memcpy(&code, &s, sizeof code);
+  switch (code) {
     case VDN_OK: return "VDN_OK";
     case VDN_ERR_INVALID_ARG: return "VDN_ERR_INVALID_ARG: bad descriptor, size, NULL pointer or overlapping buffers";
     case VDN_ERR_UNSUPPORTED: return "VDN_ERR_UNSUPPORTED: head width not implemented (d_k = d_v in {16,32,64,128})";

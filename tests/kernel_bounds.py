@@ -1,0 +1,468 @@
+"""Address-range model of the HIP kernels' global memory accesses, on the host.
+
+Each ``model_*`` function re-derives, from the kernel's own index arithmetic
+(``frame_wise_delta_02_amd/csrc``), every global address a launch can touch:
+the work-items are enumerated with numpy (every block, every thread), and loop
+indices are taken at the extremes the loop bounds allow (every offset below is
+non-decreasing in its loop index, which the model asserts where it matters).
+Two kinds of access are checked:
+
+* plain loads and stores through a pointer: the byte range must lie inside the
+  buffer the entry point passes;
+* loads and stores through a raw buffer descriptor (base, num_records): the
+  descriptor's range must lie inside the buffer, and every 32-bit offset the
+  kernel computes must not wrap (a wrapped offset could land back inside the
+  range); accesses past num_records read zero or are dropped by the hardware.
+
+The model has no knowledge of the kernels beyond what is written here: a kernel
+change that moves an address must be mirrored in its model, and the test then
+checks the new arithmetic for every shape the GPU tests and the benchmark run.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+U32 = 1 << 32
+
+
+@dataclass
+class Prob:
+    B: int
+    H: int
+    T: int
+    gh: int
+    gw: int
+    D: int
+    L: int
+    C: int = 5
+    bf16: bool = True
+    chunked: bool = False
+    epilogue: bool = True
+    gamma: bool = False
+    bridge: bool = False
+
+    @property
+    def U(self):
+        return self.gh * self.gw
+
+    @property
+    def nc(self):
+        return -(-self.T // self.C)
+
+    @property
+    def esz(self):
+        return 2 if self.bf16 else 4
+
+    @property
+    def split(self):
+        return self.bf16 and self.D >= 32
+
+
+@dataclass
+class Report:
+    """Every violation found, as readable strings."""
+    errors: list = field(default_factory=list)
+    checked: int = 0
+
+    def ptr(self, kernel, buf, size, lo, hi):
+        """[lo, hi) bytes through a pointer into a buffer of `size` bytes."""
+        self.checked += 1
+        lo, hi = int(np.min(lo)), int(np.max(hi))
+        if lo < 0 or hi > size:
+            self.errors.append(f"{kernel}: {buf} [{lo}, {hi}) outside [0, {size})")
+
+    def rsrc(self, kernel, buf, size, base, nrec, max_off, width):
+        """A buffer descriptor at byte `base` of `nrec` records; the largest
+        32-bit offset used is `max_off` for an access of `width` bytes."""
+        self.checked += 1
+        base = np.asarray(base, dtype=np.int64)
+        nrec = np.asarray(nrec, dtype=np.int64)
+        live = nrec > 0
+        if np.any(live):
+            lo = int(np.min(base[live] if base.ndim else base))
+            hi = int(np.max((base + nrec)[live] if (base + nrec).ndim else base + nrec))
+            if lo < 0 or hi > size:
+                self.errors.append(f"{kernel}: {buf} descriptor [{lo}, {hi}) outside [0, {size})")
+        if np.any(nrec >= U32):
+            self.errors.append(f"{kernel}: {buf} descriptor of {int(np.max(nrec))} records does not fit 32 bits")
+        if int(np.max(max_off)) + width > U32 - 1:
+            self.errors.append(f"{kernel}: {buf} offset {int(np.max(max_off))} + {width} wraps 32 bits")
+
+
+# ---------------------------------------------------------------------------
+# buffers of the forward pass (bytes), as the entry points size them
+# ---------------------------------------------------------------------------
+
+
+def sizes(p: Prob) -> dict:
+    tok = p.B * p.T * p.U * p.H
+    heads = p.B * p.H
+    dd = p.D * p.D * 4
+    DP = max(p.D, 32)
+    MT = DP // 32
+    slot = (2 * MT * (p.D // 16) * 64 * 16) if p.bf16 else (MT * (p.D // 8) * 64 * 16)
+    return dict(
+        q=tok * p.D * p.esz, k=tok * p.D * p.esz, v=tok * p.D * p.esz, gate=tok * p.D * p.esz,
+        out=tok * p.D * p.esz, beta=tok * p.esz, alpha=p.B * p.T * p.H * p.D * 4,
+        k_text=p.B * p.L * p.H * p.D * p.esz, v_text=p.B * p.L * p.H * p.D * p.esz,
+        beta_text=p.B * p.L * p.H * p.esz, rms=p.D * 4,
+        stats=heads * (p.T + 1) * 2 * dd, pinv=heads * (p.T + 1) * dd, s_text=heads * dd,
+        fwd=heads * p.nc * dd, rev=heads * p.nc * dd, rstates=heads * (p.nc + 1) * slot,
+        chunk_m=heads * 2 * p.nc * dd, chunk_j=heads * 2 * p.nc * dd,
+        wk_s=p.H * p.D * 25 * 4, wk_t=p.H * p.D * 5 * 4)
+
+
+def _grid(*dims):
+    """All index tuples of a launch, as flat int64 arrays."""
+    g = np.meshgrid(*[np.arange(n, dtype=np.int64) for n in dims], indexing="ij")
+    return [x.ravel() for x in g]
+
+
+# ---------------------------------------------------------------------------
+# vda_gram.hip
+# ---------------------------------------------------------------------------
+
+
+def model_gram(p: Prob, r: Report):
+    """gram_bf16<D> / gram_f32<D>: two parts in one launch -- frames 1..T-2 of
+    K, V, beta, then the text frame (slot T)."""
+    S = sizes(p)
+    D, H = p.D, p.H
+    parts = [("k", "v", "beta", p.T, p.U, 1, max(p.T - 2, 0), 0),
+             ("k_text", "v_text", "beta_text", 1, p.L, 0, 1, p.T)]
+    R = 2 * D
+    for kb, vb, bb, T_in, U, t_first, n_frames, slot_off in parts:
+        nblk = p.B * n_frames * H
+        if nblk == 0:
+            continue
+        (blk,) = _grid(nblk)
+        h = blk % H
+        fi = (blk // H) % n_frames
+        b = blk // (H * n_frames)
+        t = t_first + fi
+        tok0 = (b * T_in + t) * U
+        if p.bf16:
+            CGT, NS = D // 8, 2
+            TPT = CGT // 2
+            nstep = ((U + 63) // 64 + NS - 1) // NS * NS
+            rowbytes = H * D * 2
+            xbytes = (U - 1) * rowbytes + D * 2 if U > 0 else 0
+            blk2, wave, lane = _grid(nblk, 4, 64)
+            hh = blk2 % H
+            t2 = t_first + (blk2 // H) % n_frames
+            b2 = blk2 // (H * n_frames)
+            tok02 = (b2 * T_in + t2) * U
+            local = (wave & 1) * 64 + lane
+            cg, tq = local % CGT, local // CGT
+            tokk = TPT * tq
+            # loads of tiles 0 .. nstep + NS (the prefetch runs NS tiles ahead)
+            it_max = nstep + NS
+            max_off = (tokk + TPT - 1 + 64 * it_max) * rowbytes + cg * 16
+            base = (tok02 * H + hh) * D * 2
+            for buf in (kb, vb):
+                r.rsrc("gram_bf16", buf, S[buf], base, np.full_like(base, xbytes), max_off, 16)
+            bbase = (tok02 * H + hh) * 2
+            bbytes = (U - 1) * H * 2 + 2 if U > 0 else 0
+            boff = (32 * (wave & 1) + (lane & 31)) * H * 2 + 64 * it_max * H * 2
+            r.rsrc("gram_bf16", bb, S[bb], bbase, np.full_like(bbase, bbytes), boff, 2)
+        else:
+            TT = 16
+            ntile = (U + TT - 1) // TT
+            if ntile > 0:
+                # rows clamped to token 0 of the frame past U: read range of the frame's rows
+                lo = (tok0 * H + h) * D * 4
+                hi = ((tok0 + U - 1) * H + h) * D * 4 + D * 4
+                r.ptr("gram_f32", kb, S[kb], lo, hi)
+                r.ptr("gram_f32", vb, S[vb], lo, hi)
+                r.ptr("gram_f32", bb, S[bb], (tok0 * H + h) * 4, ((tok0 + U - 1) * H + h) * 4 + 4)
+        # consumer stores: one (2d x d) slot per (b, h, t + slot_off) of [B, H, T+1]
+        slot = (b * H + h) * (p.T + 1) + (t + slot_off)
+        r.ptr("gram", "stats", S["stats"], slot * R * D * 4, (slot + 1) * R * D * 4)
+        if p.bf16:
+            # the largest element index a consumer writes inside its slot
+            MT, NT = R // 16, D // 16
+            WM = 4 if MT >= 4 else MT
+            MTW = MT // WM
+            wm, mi, nj, lane, rr = _grid(WM, MTW, NT, 64, 4)
+            idx = (16 * (wm * MTW + mi) + 4 * (lane >> 4) + rr) * D + 16 * nj + (lane & 15)
+            assert idx.max() < R * D and idx.min() >= 0, "gram: a consumer store leaves its slot"
+
+
+# ---------------------------------------------------------------------------
+# vda_solve.hip
+# ---------------------------------------------------------------------------
+
+
+def model_solve(p: Prob, r: Report):
+    S = sizes(p)
+    D, H = p.D, p.H
+    n_video = max(p.T - 2, 0)
+    (blk,) = _grid(p.B * H * (n_video + 1))
+    si = blk % (n_video + 1)
+    h = (blk // (n_video + 1)) % H
+    b = blk // ((n_video + 1) * H)
+    slot = np.where(si < n_video, 1 + si, p.T)
+    mat = (b * H + h) * (p.T + 1) + slot
+    # loads of A: D*D floats from the slot's first row; stores: D*D floats
+    r.ptr("solve", "stats", S["stats"], mat * 2 * D * D * 4, mat * 2 * D * D * 4 + D * D * 4)
+    r.ptr("solve", "pinv", S["pinv"], mat * D * D * 4, (mat + 1) * D * D * 4)
+    if p.split:
+        NFR = D * D // 8
+        f = np.arange(NFR)
+        assert (NFR + f).max() * 16 + 16 <= D * D * 4
+
+
+# ---------------------------------------------------------------------------
+# vda_scan.hip
+# ---------------------------------------------------------------------------
+
+
+def _scan_steps(p: Prob, mode: str, dir_, cj=None):
+    """(frames or chunk slots visited incl. the prefetch of the last, alpha frames)."""
+    T, C, nc = p.T, p.C, p.nc
+    nch = max(nc - 2, 0)
+    if mode == "compose":
+        lo, hi = max(C * cj, 1), min(C * (cj + 1) - 1, T - 2)
+        n = max(0, hi - lo + 1)
+        s = list(range(lo, hi + 1))
+        return (s if n else [T]), (s if n else [0])
+    if mode == "chunks":
+        first = 0 if dir_ == 0 else nc - 1
+        step = 1 if dir_ == 0 else -1
+        s = [first + step * i for i in range(nch)]
+        return (s if nch else [0]), []
+    if dir_ == 0:
+        first, last = 1, (min(C * (nc - 2) - 1, T - 2) if nc >= 3 else 0)
+        s = list(range(first, last + 1))
+    else:
+        first, last = T - 2, (max(2 * C, 1) if nc >= 3 else T - 1)
+        s = list(range(first, last - 1, -1))
+    return (s if s else [T]), (s if s else [0])
+
+
+def model_scan(p: Prob, r: Report):
+    S = sizes(p)
+    D, H, T, nc = p.D, p.H, p.T, p.nc
+    split = p.split
+    NV = 2 if D >= 32 else 1
+    RB = 16 * (2 if split else 1)
+    NRB = D // RB
+    nch = max(nc - 2, 0)
+    modes = ["compose", "chunks"] if p.chunked and nch > 0 else (["chunks"] if p.chunked else ["frames"])
+    dd = D * D * 4
+    for mode in modes:
+        groups = p.B * H * 2
+        units = groups * nch if mode == "compose" else groups
+        rbpu = 2 * NRB if mode == "compose" else NRB
+        nblk = (units + 7) // 8 * 8 * rbpu
+        (bid,) = _grid(nblk)
+        xcd, sl = bid % 8, bid // 8
+        rbi = sl % rbpu
+        u = (sl // rbpu) * 8 + xcd
+        live = u < units
+        bid, rbi, u = bid[live], rbi[live], u[live]
+        g = u // nch if mode == "compose" else u
+        dir_ = g % 2
+        h = (g // 2) % H
+        b = g // (2 * H)
+        head = b * H + h
+        mpart = (rbi < NRB) if mode == "compose" else np.zeros_like(rbi, dtype=bool)
+        row0 = np.where((mode == "compose") & ~mpart, rbi - NRB, rbi) * RB
+        assert row0.max() + RB <= D
+        # in-slot offsets of one state block (rows row0..row0+RB-1, every column)
+        blk_hi = (row0 + RB) * D * 4
+        blk_lo = row0 * D * 4
+        for d_ in (0, 1):
+            sel = dir_ == d_
+            if not np.any(sel):
+                continue
+            hd = head[sel]
+            if mode == "compose":
+                cis = (u[sel] % nch)
+                cjs = np.where(d_ == 0, cis, nc - 1 - cis)
+                frames, alphas = set(), set()
+                for cj in np.unique(cjs):
+                    f, a = _scan_steps(p, mode, d_, int(cj))
+                    frames |= set(f)
+                    alphas |= set(a)
+            else:
+                f, a = _scan_steps(p, mode, d_)
+                frames, alphas = set(f), set(a)
+                if mode == "frames":
+                    frames.add(T)  # the text slot (S_T) first
+            fr = np.array(sorted(frames))
+            if mode == "chunks":
+                # products with M_c, rows of J_c: slots j of [B, H, 2, nc, d, d]
+                cs = (hd[:, None] * 2 + d_) * nc + fr[None, :]
+                assert fr.max() < nc and fr.min() >= 0
+                r.ptr("scan", "chunk_m", S["chunk_m"], cs * dd, (cs + 1) * dd)
+                r.ptr("scan", "chunk_j", S["chunk_j"], cs * dd, (cs + 1) * dd)
+                # the text frame from stats / pinv slot T
+                r.ptr("scan", "pinv", S["pinv"], (hd * (T + 1) + T) * dd, (hd * (T + 1) + T + 1) * dd)
+                r.ptr("scan", "stats", S["stats"], (hd * (T + 1) + T) * 2 * dd + dd,
+                      (hd * (T + 1) + T) * 2 * dd + 2 * dd)
+            else:
+                assert fr.min() >= 0 and fr.max() <= T
+                ps = hd[:, None] * (T + 1) + fr[None, :]
+                r.ptr("scan", "pinv", S["pinv"], ps * dd, (ps + 1) * dd)
+                r.ptr("scan", "stats", S["stats"], ps * 2 * dd + dd, ps * 2 * dd + 2 * dd)
+                al = np.array(sorted(alphas | {0}))
+                assert al.min() >= 0 and al.max() < T
+                # alpha [B, T, H, d]: row s of (b, h)
+                bb = (hd // H)[:, None]
+                hh = (hd % H)[:, None]
+                lo = ((bb * T + al[None, :]) * H + hh) * D * 4
+                r.ptr("scan", "alpha", S["alpha"], lo, lo + D * 4)
+            if mode == "compose":
+                cs = (hd * 2 + d_) * nc + cjs
+                r.ptr("scan", "chunk_m/j", S["chunk_m"], cs * dd, (cs + 1) * dd)
+            else:
+                # records through a descriptor over this head's n_c states; steps
+                # that record nothing store at offset 2^31
+                buf = "fwd" if d_ == 0 else "rev"
+                r.rsrc("scan", buf, S[buf], hd * nc * dd, np.full_like(hd, nc * dd),
+                       np.array([0x80000000 + D * D * 4 - 4 * NV, (nc - 1) * dd + D * D * 4 - 4 * NV]), 4 * NV)
+                if (1 << 31) < nc * dd:
+                    r.errors.append("scan: the no-record sentinel 2^31 lies inside a head's records")
+                if d_ == 0:
+                    r.ptr("scan", "s_text", S["s_text"], hd * dd, (hd + 1) * dd)
+
+
+def model_gather(p: Prob, r: Report):
+    S = sizes(p)
+    D, nc, T, H = p.D, p.nc, p.T, p.H
+    dd = D * D * 4
+    (blk,) = _grid(p.B * H * (nc + 1))
+    slot = blk % (nc + 1)
+    head = blk // (nc + 1)
+    r.ptr("gather", "s_text", S["s_text"], head * dd, (head + 1) * dd)
+    fsel = (slot < nc) & (slot >= 2)
+    if np.any(fsel):
+        j = head[fsel] * nc + slot[fsel] - 2
+        r.ptr("gather", "fwd", S["fwd"], j * dd, (j + 1) * dd)
+    rsel = (slot < nc) & (slot + 2 <= nc - 1)
+    if np.any(rsel):
+        j = head[rsel] * nc + slot[rsel] + 2
+        r.ptr("gather", "rev", S["rev"], j * dd, (j + 1) * dd)
+    if p.bridge:
+        frames = [s for c in range(nc) for s in list(range(p.C * (c - 1), p.C * c)) * (c >= 1)
+                  + list(range(p.C * (c + 1), min(p.C * (c + 2), T))) * (c + 1 <= nc - 1)]
+        if frames:
+            assert min(frames) >= 0 and max(frames) < T
+    slot_bytes = S["rstates"] // (p.B * H * (nc + 1))
+    r.ptr("gather", "rstates", S["rstates"], blk * slot_bytes, (blk + 1) * slot_bytes)
+
+
+def model_readout(p: Prob, r: Report):
+    S = sizes(p)
+    D, H, T, U = p.D, p.H, p.T, p.U
+    (blk,) = _grid(p.B * T * H)
+    h = blk % H
+    t = (blk // H) % T
+    b = blk // (H * T)
+    nc = p.nc
+    slot = np.where((t == 0) | (t == T - 1), nc, t // p.C)
+    slot_bytes = S["rstates"] // (p.B * H * (nc + 1))
+    rs = (b * H + h) * (nc + 1) + slot
+    r.ptr("readout", "rstates", S["rstates"], rs * slot_bytes, (rs + 1) * slot_bytes)
+    if p.gamma:
+        r.ptr("readout", "rms", S["rms"], 0, D * 4)
+    if p.bf16:
+        NW, CH = 8, D // 8
+        RPI = 64 // CH
+        NL = 32 // RPI
+        rowbytes = H * D * 2
+        nbytes = (U - 1) * rowbytes + D * 2 if U > 0 else 0
+        fbase = (((b * T + t) * U * H + h) * D) * 2
+        ntiles = (U + 31) // 32
+        per_wave = (ntiles + NW - 1) // NW
+        steps = (per_wave + 1) & ~1
+        # fetch(tile + 2 NW) at the last loop pass reaches tile wave + NW * steps;
+        # process(tile + NW) stores up to tile wave + NW * (steps - 1)
+        wave, lane = _grid(NW, 64)
+        loff = (lane // CH) * rowbytes + 16 * (lane % CH)
+        tile_max = wave + NW * max(steps, 0)
+        max_off = tile_max * 32 * rowbytes + loff + (RPI * (NL - 1)) * rowbytes
+        for buf in ["q", "out"] + (["gate"] if p.epilogue else []):
+            r.rsrc("readout_bf16", buf, S[buf], fbase, np.full_like(fbase, nbytes), max_off, 16)
+    else:
+        lo = (((b * T + t) * U) * H + h) * D * 4
+        hi = (((b * T + t) * U + U - 1) * H + h) * D * 4 + D * 4
+        for buf in ["q", "out"] + (["gate"] if p.epilogue else []):
+            r.ptr("readout_f32", buf, S[buf], lo, hi)
+
+
+# ---------------------------------------------------------------------------
+# vda_prep.hip
+# ---------------------------------------------------------------------------
+
+
+def model_prep(p: Prob, r: Report):
+    S = sizes(p)
+    D, H, T, gh, gw = p.D, p.H, p.T, p.gh, p.gw
+    U = gh * gw
+    tokstride = H * D
+    if p.bf16 and D == 128:
+        PTY, PTX = 8, 12
+        ntx, nty = -(-gw // PTX), -(-gh // PTY)
+        ntile = ntx * nty
+        (bid,) = _grid(p.B * H * ntile)
+        if H % 8 == 0:
+            xcd, j = bid % 8, bid // 8
+            tile = j % ntile
+            hq = j // ntile
+            h = (hq % (H // 8)) * 8 + xcd
+            b = hq // (H // 8)
+        else:
+            tile = bid % ntile
+            h = (bid // ntile) % H
+            b = bid // (ntile * H)
+        assert h.max() < H and b.max() < p.B and np.unique(b * H * ntile + h * ntile + tile).size == bid.size
+        # slab loads: positions clamped to the frame by the `ok` test; frames < T
+        y0, x0 = (tile // ntx) * PTY, (tile % ntx) * PTX
+        yy_lo, yy_hi = np.maximum(y0 - 2, 0), np.minimum(y0 + PTY + 1, gh - 1)
+        xx_lo, xx_hi = np.maximum(x0 - 2, 0), np.minimum(x0 + PTX + 1, gw - 1)
+        lo = ((b * T + 0) * U + yy_lo * gw + xx_lo) * tokstride + h * D
+        hi = ((b * T + T - 1) * U + yy_hi * gw + xx_hi) * tokstride + h * D + D
+        for buf in ("k", "v"):
+            r.ptr("prep_conv_tile", buf, S[buf], lo * 2, hi * 2)
+        # stores: positions inside the grid of frames 0..T-1
+        yo = np.minimum(y0 + PTY - 1, gh - 1)
+        xo = np.minimum(x0 + PTX - 1, gw - 1)
+        lo = ((b * T) * U + y0 * gw + x0) * tokstride + h * D
+        hi = ((b * T + T - 1) * U + yo * gw + xo) * tokstride + h * D + D
+        for buf in ("k", "v"):
+            r.ptr("prep_conv_tile", buf + "_hat", S[buf], lo * 2, hi * 2)
+        c = h * D
+        r.ptr("prep_conv_tile", "wk_s", S["wk_s"], c * 25 * 4, (c + D) * 25 * 4)
+        r.ptr("prep_conv_tile", "wk_t", S["wk_t"], c * 5 * 4, (c + D) * 5 * 4)
+    else:
+        (blk,) = _grid(p.B * T * H * gh)
+        y = blk % gh
+        h = (blk // gh) % H
+        t = (blk // (gh * H)) % T
+        b = blk // (gh * H * T)
+        lo = ((b * T + np.maximum(t - 2, 0)) * U + np.maximum(y - 2, 0) * gw) * H + h
+        hi = ((b * T + np.minimum(t + 2, T - 1)) * U + np.minimum(y + 2, gh - 1) * gw + gw - 1) * H + h
+        for buf in ("k", "v"):
+            r.ptr("prep_conv", buf, S[buf], lo * D * p.esz, (hi * D + D) * p.esz)
+        r.ptr("prep_conv", "wk_s", S["wk_s"], h * D * 25 * 4, (h * D + D) * 25 * 4)
+    # prep_l2: rows = B T U H, one thread per 8 channels, guarded by row < rows
+    rows = p.B * T * U * H
+    r.ptr("prep_l2", "q", S["q"], 0, rows * D * p.esz)
+
+
+def model_forward(p: Prob, prep: bool = False) -> Report:
+    """Every kernel of vdn_vda_forward (and vdn_vda_prepare) for one problem."""
+    r = Report()
+    if prep:
+        model_prep(p, r)
+    model_gram(p, r)
+    model_solve(p, r)
+    model_scan(p, r)
+    model_gather(p, r)
+    model_readout(p, r)
+    return r
