@@ -1,4 +1,6 @@
-// vda_solve: (I + A_t)^{-1} for every frame of every head, by Cholesky in LDS.
+// vda_solve: (I + A_t)^{-1} for every frame of every head, held in LDS: by a
+// symmetric block sweep for bfloat16 inputs (solve_sweep, further below), by
+// Cholesky for float32 inputs and d = 16 (solve_mfma).
 //
 // The frame update S_t = (S_{t-1} Diag(alpha_t) + B_t)(I + A_t)^{-1} is solved in
 // the d_k x d_k key space ("Video DeltaNet" summary, onedev.kr/papers/80, section
@@ -348,13 +350,227 @@ __global__ __launch_bounds__(256, 2) void solve_mfma(const float* __restrict__ s
   }
 }
 
+// ---------------------------------------------------------------------------
+// bfloat16 inputs (d >= 32): the inverse by a symmetric block sweep.
+//
+// Sweeping the 16 x 16 diagonal blocks of P in order (block Gauss-Jordan
+// without pivoting, which P = I + A_t, symmetric positive definite with every
+// Schur complement >= I, allows) leaves -P^{-1} in place: for pivot block k,
+// with X = (P_kk)^{-1},
+//     P_ij <- P_ij - (P_ik X) P_kj   (i, j != k),
+//     P_ik <- P_ik X,  P_kj <- X P_kj,  P_kk <- -X.
+// The sweep keeps P symmetric, so only the lower triangle of 16 x 16 tiles is
+// held (in LDS, rows padded to 17 floats: 40 KB at d = 128, four matrices per
+// compute unit).  Its only serial part is the chain of d/16 leaf inversions
+// (each a scalar sweep of the 16 x 16 block in one wave: lane = row, the pivot
+// row broadcast by readlane); everything else is 16 x 16 x 16 tile products on
+// v_mfma_f32_16x16x4f32, spread over the four waves by rows.  The products of
+// a step contract over a permuted k order (k = 4 (lane / 16) + s), so the
+// accumulator of C_i = P_ik X, computed transposed, is already the left
+// operand of the updates P_ij -= C_i P_kj and stays in registers.  All
+// arithmetic is fp32; the result is written as bfloat16 hi + lo planes in the
+// scan's operand order, as solve_mfma does.
+template <int D>
+__global__ __launch_bounds__(256) void solve_sweep(const float* __restrict__ stats, float* __restrict__ pinv,
+                                                   int H, int T, int n_video) {
+  constexpr int NB = D / 16;               // 16 x 16 blocks per side
+  constexpr int NT = NB * (NB + 1) / 2;    // lower-triangle tiles
+  constexpr int LDT = 17;                  // padded tile row (floats)
+  constexpr int TS = 16 * LDT;             // floats per tile
+  constexpr int RPW = NB == 8 ? 2 : 1;     // block rows per wave
+  __shared__ float tl[(NT + 1) * TS];      // tile (R, C), C <= R, at R (R + 1) / 2 + C; then X
+  float* XS = tl + NT * TS;
+  auto tile = [&](int R, int C) -> float* { return tl + (R * (R + 1) / 2 + C) * TS; };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lm = lane & 15, lg = lane >> 4;
+  const int n_slots = n_video + 1;
+  int blk = blockIdx.x;
+  const int si = blk % n_slots;
+  blk /= n_slots;
+  const int h = blk % H;
+  const int b = blk / H;
+  const int slot = (si < n_video) ? 1 + si : T;  // video frames 1..T-2, then the text slot T
+  const size_t mat = (size_t)(b * H + h) * (T + 1) + slot;
+  const float* A = stats + mat * (size_t)(2 * D * D);
+  float* Pout = pinv + mat * (size_t)(D * D);
+
+  // ---- the lower tiles of P = I + A into LDS (every load issued first) ------
+  {
+    constexpr int NV4 = NT * 64;  // float4 pieces of the lower tiles
+    constexpr int PER = (NV4 + 255) / 256;
+    float4 x[PER];
+    int dst[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int e = tid + 256 * q;
+      x[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      dst[q] = -1;
+      if (NV4 % 256 == 0 || e < NV4) {
+        const int t = e >> 6, w = e & 63;
+        int R = 0;
+        while ((R + 1) * (R + 2) / 2 <= t) ++R;
+        const int C = t - R * (R + 1) / 2;
+        const int row = w >> 2, c4 = w & 3;
+        x[q] = *reinterpret_cast<const float4*>(A + (size_t)(16 * R + row) * D + 16 * C + 4 * c4);
+        dst[q] = (t * 16 + row) * LDT + 4 * c4;
+        if (R == C) {
+          x[q].x += (row == 4 * c4) ? 1.f : 0.f;
+          x[q].y += (row == 4 * c4 + 1) ? 1.f : 0.f;
+          x[q].z += (row == 4 * c4 + 2) ? 1.f : 0.f;
+          x[q].w += (row == 4 * c4 + 3) ? 1.f : 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      if (dst[q] >= 0) {
+        tl[dst[q]] = x[q].x;
+        tl[dst[q] + 1] = x[q].y;
+        tl[dst[q] + 2] = x[q].z;
+        tl[dst[q] + 3] = x[q].w;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- leaf: the 16 x 16 block (k, k) swept in one wave ---------------------
+  // Lane i (of 16; the other lanes repeat the rows) holds row i.  For pivot p
+  // with d = a_pp and r = 1/d: a_ij -= (a_ip r) a_pj for i, j != p; a_pj *= r;
+  // a_ip *= r; a_pp = -r.  Row p's update is written in the same form with
+  // a multiplier 1 - r.  The result is -(block)^{-1}: written to the tile (its
+  // swept value -X) and, negated, to XS (X itself).
+  auto leaf = [&](int k) {
+    float* Tk = tile(k, k);
+    float a[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) a[j] = Tk[lm * LDT + j];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      float rowp[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) rowp[j] = rdlane(a[j], p);
+      const float d = rowp[p];
+      float r = __builtin_amdgcn_rcpf(d);
+      r = __builtin_fmaf(r, __builtin_fmaf(-d, r, 1.f), r);  // one Newton step
+      const bool me = lm == p;
+      const float t = me ? 1.f - r : a[p] * r;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j != p) a[j] = __builtin_fmaf(-t, rowp[j], a[j]);
+      a[p] = me ? -r : t;
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        Tk[lm * LDT + j] = a[j];
+        XS[lm * LDT + j] = -a[j];
+      }
+    }
+  };
+
+  // block rows of this wave: w, and with 8 blocks also 7 - w
+  auto row_of = [&](int u) { return u == 0 ? wave : NB - 1 - wave; };
+  f32x4 creg[RPW];
+  // wave 0 sweeps the diagonal blocks (rotating it over the waves measured no
+  // faster)
+  if (wave == 0) leaf(0);
+  __syncthreads();
+  for (int k = 0; k < NB; ++k) {
+#pragma unroll
+    for (int u = 0; u < RPW; ++u) {
+      const int i = row_of(u);
+      if (i >= NB || i == k) continue;
+      // C_i^T = X P_ik^T on the k order 4 s + (lane / 16): lane l, register r
+      // then holds C_i[l % 16][4 (l / 16) + r]
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      const float* Pik = i > k ? tile(i, k) : tile(k, i);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float xa = XS[lm * LDT + 4 * s + lg];
+        const float pb = i > k ? Pik[lm * LDT + 4 * s + lg] : Pik[(4 * s + lg) * LDT + lm];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, pb, acc, 0, 0, 0);
+      }
+      creg[u] = acc;
+      // P_ij -= C_i P_kj for every lower tile (i, j), j != k, of this row; the
+      // k order here is 4 (lane / 16) + s, so C_i's accumulator is the operand
+      for (int j = 0; j <= i; ++j) {
+        if (j == k) continue;
+        float* Tij = tile(i, j);
+        f32x4 c;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c[r] = Tij[(4 * lg + r) * LDT + lm];
+        const float* Pkj = j < k ? tile(k, j) : tile(j, k);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float pb = j < k ? Pkj[(4 * lg + s) * LDT + lm] : Pkj[lm * LDT + 4 * lg + s];
+          c = __builtin_amdgcn_mfma_f32_16x16x4f32(-creg[u][s], pb, c, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Tij[(4 * lg + r) * LDT + lm] = c[r];
+      }
+    }
+    __syncthreads();  // every read of block column k is done
+    // P_ik <- C_i (stored as tile (i, k) for i > k, as tile (k, i) = C_i^T for i < k)
+#pragma unroll
+    for (int u = 0; u < RPW; ++u) {
+      const int i = row_of(u);
+      if (i >= NB || i == k) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (i > k)
+          tile(i, k)[lm * LDT + 4 * lg + r] = creg[u][r];
+        else
+          tile(k, i)[(4 * lg + r) * LDT + lm] = creg[u][r];
+      }
+    }
+    if (k + 1 < NB && wave == 0) leaf(k + 1);
+    __syncthreads();
+  }
+
+  // ---- out: P^{-1} = -(swept P), as bfloat16 hi + lo planes -------------------
+  // fragment f = ((2w + e) (d/32) + s) 64 + l holds P^{-1}[32 s + 8 (l/16) + j]
+  // [32 w + 2 (l%16) + e], j = 0..7; the symmetric element comes from the
+  // lower tile that holds it
+  constexpr int NFR = D * D / 8;
+  constexpr int KS2 = D / 32;
+  uint4* Fo = reinterpret_cast<uint4*>(Pout);
+  for (int f = tid; f < NFR; f += 256) {
+    const int fl = f & 63, ks = (f >> 6) % KS2, we = (f >> 6) / KS2;
+    const int c = 32 * (we >> 1) + 2 * (fl & 15) + (we & 1);
+    const int r0 = 32 * ks + 8 * (fl >> 4);
+    const int R = r0 >> 4, rr = r0 & 15, Cb = c >> 4, cc = c & 15;
+    float v[8];
+    if (R >= Cb) {
+      const float* Tp = tile(R, Cb);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = -Tp[(rr + j) * LDT + cc];
+    } else {
+      const float* Tp = tile(Cb, R);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = -Tp[cc * LDT + rr + j];
+    }
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      __bf16 h0, l0, h1, l1;
+      split_bf16(v[2 * e], h0, l0);
+      split_bf16(v[2 * e + 1], h1, l1);
+      hw[e] = __builtin_bit_cast(uint32_t, bf16x2{h0, h1});
+      lw[e] = __builtin_bit_cast(uint32_t, bf16x2{l0, l1});
+    }
+    Fo[f] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    Fo[NFR + f] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  }
+}
+
 template <int D>
 hipError_t launch_solve_d(const Problem& p, const float* stats, float* pinv, hipStream_t s) {
   const int n_video = p.T > 2 ? p.T - 2 : 0;
   const unsigned grid = (unsigned)(p.B * p.H * (n_video + 1));
   if constexpr (D >= 32) {
     if (pinv_split(p)) {
-      hipLaunchKernelGGL((solve_mfma<D, true>), dim3(grid), dim3(256), 0, s, stats, pinv, p.H, p.T, n_video);
+      hipLaunchKernelGGL(solve_sweep<D>, dim3(grid), dim3(256), 0, s, stats, pinv, p.H, p.T, n_video);
       return hipGetLastError();
     }
   }

@@ -210,6 +210,14 @@ def model_solve(p: Prob, r: Report):
     r.ptr("solve", "stats", S["stats"], mat * 2 * D * D * 4, mat * 2 * D * D * 4 + D * D * 4)
     r.ptr("solve", "pinv", S["pinv"], mat * D * D * 4, (mat + 1) * D * D * 4)
     if p.split:
+        # solve_sweep: float4 loads of the lower 16 x 16 tiles of A only, rows
+        # 16 R + row, columns 16 C + 4 c4 (C <= R): a subset of the slot's first
+        # D x D floats; fragment stores f and NFR + f (16 B each)
+        NB = D // 16
+        RR, CC, row, c4 = _grid(NB, NB, 16, 4)
+        low = CC <= RR
+        off = ((16 * RR + row) * D + 16 * CC + 4 * c4)[low] * 4
+        assert off.min() >= 0 and off.max() + 16 <= D * D * 4
         NFR = D * D // 8
         f = np.arange(NFR)
         assert (NFR + f).max() * 16 + 16 <= D * D * 4
