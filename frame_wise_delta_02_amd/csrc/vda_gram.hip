@@ -13,8 +13,10 @@
 // accumulation.  The scaled operands sqrt(beta) k and sqrt(beta) v are rounded
 // to IEEE half, not bfloat16: the inputs are exact in either, but the products
 // keep 11 significant bits instead of 8 at the same matrix-core rate on gfx950
-// (keys are unit vectors, so |sqrt(beta) k| <= sqrt(beta); a value entry with
-// |sqrt(beta) v| beyond 65504 would overflow the half range).
+// (keys are unit vectors, so |sqrt(beta) k| <= sqrt(beta)).  A unit whose
+// operands leave the half range (|sqrt(beta) v| > 65504, which bfloat16 values
+// allow) shows non-finite sums; it is then contracted again on operands scaled
+// by powers of two, undone exactly in float32 (the recovery after the main loop).
 // The token axis is the contraction axis but is the strided axis in memory
 // ([.., U, H, d] layout), so each 64-token tile is staged through LDS
 // transposed, one row per channel (128 bytes = 64 tokens, the 16-byte chunk
@@ -47,6 +49,15 @@ namespace {
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
+// 2^-e with m 2^-e < 2^14 for m >= 2^14 (so scaled half operands stay far from
+// 65504 and their products far from the float32 range), else 1
+__device__ __forceinline__ float range_scale(float m) {
+  if (!(m >= 16384.f)) return 1.f;
+  const int E = ((__float_as_int(m) >> 23) & 0xff) - 127;  // floor(log2 m)
+  const int e = min(E - 13, 125);
+  return __int_as_float((127 - e) << 23);
+}
+
 // One part of a launch: frames t_first .. t_first + n_frames - 1 of inputs laid
 // out [B, T_in, U, H, d], written to stats slots t + slot_offset.
 template <typename TIO>
@@ -77,9 +88,13 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(GramArgs<uint16_t> part0, Gr
   constexpr int MTW = MT / WM;
   constexpr int NS = 2;             // producer register stages
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][R * 128];
+  // range recovery (see below): set when a consumer's sums are not finite
+  __shared__ int s_flag;
+  __shared__ float s_max[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid == 0) s_flag = 0;  // ordered before any use by the main loop's barriers
   // block decode kept in scalar registers: the buffer descriptors built from it
   // must be provably wave-uniform
   int blk = (int)blockIdx.x - (second ? nblk0 : 0);
@@ -126,7 +141,13 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(GramArgs<uint16_t> part0, Gr
       for (int j = 0; j < TPT; ++j) x[s][j] = buf_load16(xr, xo + j * rowbytes);
       if constexpr (!PLAIN) sb[s] = __builtin_amdgcn_raw_buffer_load_b16(br, boff0 + (uint32_t)(it * 64) * H * 2, 0, 0);
     };
-    auto store = [&](int s, int buf) {
+    // sqrt(beta) of this thread's TPT tokens of stage s, times xs
+    auto token_scales = [&](int s, float xs, float (&sc)[TPT]) {
+      const int sq = __float_as_int(__builtin_amdgcn_sqrtf(bf16_to_f32((uint16_t)sb[s])));
+#pragma unroll
+      for (int j = 0; j < TPT; ++j) sc[j] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (tl + j), sq)) * xs;
+    };
+    auto store_x = [&](int s, int buf, float xs) {
       if constexpr (PLAIN) {
         // raw bfloat16 halves: channel row i of tokens j, j+1 packed into one word
 #pragma unroll
@@ -153,10 +174,8 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(GramArgs<uint16_t> part0, Gr
         }
         return;
       }
-      const int sq = __float_as_int(__builtin_amdgcn_sqrtf(bf16_to_f32((uint16_t)sb[s])));
       float sc[TPT];
-#pragma unroll
-      for (int j = 0; j < TPT; ++j) sc[j] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (tl + j), sq));
+      token_scales(s, xs, sc);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         float v[TPT];
@@ -180,6 +199,7 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(GramArgs<uint16_t> part0, Gr
         __builtin_amdgcn_sched_barrier(0);  // one row's values live at a time
       }
     };
+    auto store = [&](int s, int buf) { store_x(s, buf, 1.f); };
 
     // tile i+1 is written while the consumers multiply tile i; the stage it
     // came from is refilled at once with tile i+1+NS
@@ -195,6 +215,37 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(GramArgs<uint16_t> part0, Gr
         store(s, (u + 1) & 1);
         load(s, it + u + 1 + NS);
         lds_barrier();
+      }
+    }
+    if constexpr (!PLAIN) {
+      lds_barrier();  // the consumers' verdict is in s_flag
+      if (s_flag) {
+        // the largest |sqrt(beta) x| of this tensor over the unit, every tile
+        float m = 0.f;
+        for (int it = 0; it < nstep; ++it) {
+          load(0, it);
+          float sc[TPT];
+          token_scales(0, 1.f, sc);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) {
+              const uint32_t wd = (i >> 1) == 0 ? x[0][j].x : (i >> 1) == 1 ? x[0][j].y : (i >> 1) == 2 ? x[0][j].z : x[0][j].w;
+              m = fmaxf(m, fabsf(((i & 1) ? bf16_hi(wd) : bf16_lo(wd)) * sc[j]));
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if (lane == 0) s_max[wave] = m;
+        lds_barrier();
+        const float xs = range_scale(fmaxf(s_max[2 * which], s_max[2 * which + 1]));
+        // the contraction again, one tile at a time, on operands scaled by xs
+        for (int it = 0; it < nstep; ++it) {
+          load(0, it);
+          store_x(0, 0, xs);
+          lds_barrier();
+          lds_barrier();
+        }
       }
     }
   } else {
@@ -246,6 +297,44 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(GramArgs<uint16_t> part0, Gr
       }
     }
 
+    // Range recovery.  The half-precision operands hold |sqrt(beta) x| up to
+    // 65504; a larger one turns into inf and the sums into inf or NaN.  Then
+    // the workgroup finds each tensor's largest |sqrt(beta) x| over the unit,
+    // contracts again on operands scaled by powers of two (2^-eK, 2^-eV) that
+    // bring it below 2^14, and undoes the scales exactly in float32:
+    // A = 2^(2 eK) (Z^T Z), B = 2^(eK + eV) (W^T Z).  Finite inputs in range
+    // never take this path; non-finite inputs take it and stay non-finite.
+    float unA = 1.f, unB = 1.f;
+    if constexpr (!PLAIN) {
+      bool bad = false;
+      if (mma) {
+#pragma unroll
+        for (int mi = 0; mi < MTW; ++mi)
+#pragma unroll
+          for (int nj = 0; nj < NT; ++nj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bad |= !(fabsf(acc[mi][nj][r]) <= 3.0e38f);
+      }
+      if (bad) s_flag = 1;
+      lds_barrier();
+      if (s_flag) {
+        lds_barrier();  // the producers' maxima are in s_max
+        const float sk = range_scale(fmaxf(s_max[0], s_max[1]));
+        const float sv = range_scale(fmaxf(s_max[2], s_max[3]));
+        unA = 1.f / (sk * sk);
+        unB = 1.f / (sv * sk);
+#pragma unroll
+        for (int i = 0; i < MTW; ++i)
+#pragma unroll
+          for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int it = 0; it < nstep; ++it) {
+          lds_barrier();
+          if (mma) compute(0);
+          lds_barrier();
+        }
+      }
+    }
+
     if (mma) {
       // slot of [A_t; B_t] (2d x d), or PLAIN: of V^T K alone (d x d)
       constexpr int OUTR = PLAIN ? D : R, ROW0 = PLAIN ? D : 0;
@@ -256,7 +345,8 @@ __global__ __launch_bounds__(512, 1) void gram_bf16(GramArgs<uint16_t> part0, Gr
         for (int nj = 0; nj < NT; ++nj)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            out[(16 * (wm * MTW + mi) + 4 * (lane >> 4) + r - ROW0) * D + 16 * nj + (lane & 15)] = acc[mi][nj][r];
+            out[(16 * (wm * MTW + mi) + 4 * (lane >> 4) + r - ROW0) * D + 16 * nj + (lane & 15)] =
+                acc[mi][nj][r] * (16 * (wm * MTW + mi) < D ? unA : unB);
     }
   }
 }

@@ -205,7 +205,12 @@ vdn_status vdn_vda_prepare(const vdn_vda_desc* d,
  * the raw query and the readout normalises it (see the flag).  k_text, v_text, beta_text
  * may be NULL when n_text = 0 (then S_T = 0).  gate is required with
  * VDN_VDA_EPILOGUE and ignored without it.  out is written in `dtype` with
- * round-to-nearest-even.  The state, statistics, inverse and scan are float32;
+ * round-to-nearest-even.  With VDN_BF16 the frame statistics take
+ * sqrt(beta) k and sqrt(beta) v as IEEE half operands (fp32 sums); a (frame,
+ * head) whose |sqrt(beta) v| or |sqrt(beta) k| exceeds the half range (65504)
+ * is recomputed on operands scaled by powers of two, so any finite bfloat16
+ * value is handled (only that unit pays a second pass).  The state,
+ * statistics, inverse and scan are float32;
  * with VDN_BF16 and d_k >= 32 the scan's product Y (I + A_t)^{-1} takes both
  * operands as bfloat16 hi + lo pairs (three bfloat16 matrix-core products,
  * fp32 accumulation, about 2^-16 relative per frame step).

@@ -347,3 +347,32 @@ def test_query_l2_fused(name):
         err = G.slice_rel_err(G.to_host_f64(out), ref["y" if epi else "o"])
         G.say(f"{name} epilogue={epi} gain={gain is not None}: err={err:.3e} tol={tol}")
         assert err <= tol, (epi, gain is not None, err)
+
+
+def test_values_beyond_the_half_range():
+    """Value entries with |sqrt(beta) v| far above 65504 (the largest IEEE half,
+    the statistics kernel's operand type) in two video frames and in the text
+    frame: the kernel rescales those units' operands by powers of two and the
+    result matches the oracle as for ordinary inputs."""
+    w = EDGE["ragged_bf16_128"]
+    x = synth.make_inputs(w)
+    v = oracle.widen_bf16_bits(x["v"])
+    v[:, 3, :30, 1] *= 1.0e5
+    v[:, 7, 50:, 0] *= 3.0e4
+    x["v"] = synth.f64_to_bf16_bits(v)
+    vt = oracle.widen_bf16_bits(x["v_text"])
+    vt[:, :5, 2] *= 2.0e5
+    x["v_text"] = synth.f64_to_bf16_bits(vt)
+    beta = oracle.widen_bf16_bits(x["beta"])
+    big = np.abs(np.sqrt(beta)[..., None] * v).max()
+    assert big > 1.0e5, big
+    out, ws, desc, _ = G.run_forward(x, w, epilogue=True)
+    inter = G.intermediates(ws, desc, w)
+    ref = _oracle_heads(x, w, list(range(w.H)), gate=True)
+    tol = G.TOL[w.dtype]
+    err = G.slice_rel_err(G.to_host_f64(out), ref["y"])
+    eb = G.mat_rel_err(inter["B"][:, :, 1:w.T - 1], ref["B"][:, :, 1:w.T - 1])
+    est = G.mat_rel_err(inter["S_T"], ref["S_T"])
+    G.say(f"values beyond half range (max |sqrt(beta) v| = {big:.3g}): err(y)={err:.3e} err(B)={eb:.3e} err(S_T)={est:.3e}")
+    assert np.isfinite(G.to_host_f64(out)).all()
+    assert err <= tol and eb <= tol and est <= tol, (err, eb, est)
