@@ -52,6 +52,16 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ void buf_store16(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, 0);
 }
+// The same with the non-temporal cache policy (bit 1 of the cache-policy
+// operand, NT on gfx950): for streams a kernel reads or writes exactly once,
+// so they do not displace data that other workgroups or the next kernel
+// re-read from L2 and the Infinity Cache.
+__device__ __forceinline__ uint4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+__device__ __forceinline__ void buf_store16_nt(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r, off, 0, 2);
+}
 
 // A wave-uniform value forced into a scalar register.  The optimiser drops
 // __builtin_amdgcn_readfirstlane on values it already considers uniform, and

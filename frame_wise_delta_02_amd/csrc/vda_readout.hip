@@ -89,6 +89,9 @@ __global__ __launch_bounds__(512, 1) void readout_bf16(
   const __amdgpu_buffer_rsrc_t orr = make_rsrc(O + fbase, nbytes);
   const __amdgpu_buffer_rsrc_t gr = make_rsrc(EPI ? G + fbase : Q + fbase, nbytes);
 
+  // Q, the gate and the output are each touched once: non-temporal accesses,
+  // so they do not evict the packed states that every frame of a chunk re-reads
+  // (and the statistics the next stages read) from L2 and the Infinity Cache.
   // Global traffic is coalesced: access i of a tile covers token rows
   // RPI*i .. RPI*i + RPI-1, consecutive lanes on consecutive 16-byte chunks.
   // The per-wave LDS tile turns rows into matrix-core operand order and back.
@@ -107,10 +110,10 @@ __global__ __launch_bounds__(512, 1) void readout_bf16(
   auto fetch = [&](int tile, uint4 (&qv)[NL], uint4 (&gv)[NL]) {
     const uint32_t tb = (uint32_t)tile * 32 * rowbytes + loff;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) qv[i] = buf_load16(qr, tb + (uint32_t)(RPI * i) * rowbytes);
+    for (int i = 0; i < NL; ++i) qv[i] = buf_load16_nt(qr, tb + (uint32_t)(RPI * i) * rowbytes);
     if constexpr (EPI) {
 #pragma unroll
-      for (int i = 0; i < NL; ++i) gv[i] = buf_load16(gr, tb + (uint32_t)(RPI * i) * rowbytes);
+      for (int i = 0; i < NL; ++i) gv[i] = buf_load16_nt(gr, tb + (uint32_t)(RPI * i) * rowbytes);
     }
   };
   // LDS accesses of one wave execute in order; these fences only keep the
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(512, 1) void readout_bf16(
     fence();
     const uint32_t tb = (uint32_t)tile * 32 * rowbytes + loff;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) buf_store16(X[pos(RPI * i + lrow, lch)], orr, tb + (uint32_t)(RPI * i) * rowbytes);
+    for (int i = 0; i < NL; ++i) buf_store16_nt(X[pos(RPI * i + lrow, lch)], orr, tb + (uint32_t)(RPI * i) * rowbytes);
     fence();
   };
 
