@@ -59,48 +59,53 @@ class BackwardLayout(ctypes.Structure):
 _lib = None
 
 
+def declare(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Set the argument and result types of every exported function on a
+    loaded library with this C ABI; returns it."""
+    p, sz = ctypes.c_void_p, ctypes.c_size_t
+    dp = ctypes.POINTER(Desc)
+    L.vdn_vda_validate.argtypes = [dp]
+    L.vdn_vda_validate.restype = ctypes.c_int
+    L.vdn_vda_workspace_bytes.argtypes = [dp]
+    L.vdn_vda_workspace_bytes.restype = sz
+    L.vdn_vda_workspace_layout.argtypes = [dp, ctypes.POINTER(Layout)]
+    L.vdn_vda_workspace_layout.restype = ctypes.c_int
+    L.vdn_vda_prepare.argtypes = [dp] + [p] * 11
+    L.vdn_vda_prepare.restype = ctypes.c_int
+    L.vdn_vda_forward.argtypes = [dp] + [p] * 12 + [sz, p]
+    L.vdn_vda_forward.restype = ctypes.c_int
+    L.vdn_vda_forward_timed.argtypes = [dp] + [p] * 12 + [sz, p, p, ctypes.c_int32]
+    L.vdn_vda_forward_timed.restype = ctypes.c_int
+    L.vdn_vda_forward_noalloc.argtypes = [dp] + [p] * 12
+    L.vdn_vda_forward_noalloc.restype = ctypes.c_int
+    L.vdn_vda_status_string.argtypes = [ctypes.c_int]
+    L.vdn_vda_status_string.restype = ctypes.c_char_p
+    L.vdn_vda_backward_workspace_bytes.argtypes = [dp]
+    L.vdn_vda_backward_workspace_bytes.restype = sz
+    L.vdn_vda_backward_workspace_layout.argtypes = [dp, ctypes.POINTER(BackwardLayout)]
+    L.vdn_vda_backward_workspace_layout.restype = ctypes.c_int
+    L.vdn_vda_backward_readout.argtypes = [dp] + [p] * 6 + [sz] + [p] * 3 + [sz, p]
+    L.vdn_vda_backward_readout.restype = ctypes.c_int
+    L.vdn_vda_backward_scan.argtypes = [dp, p, p, sz, p, p, sz, p]
+    L.vdn_vda_backward_scan.restype = ctypes.c_int
+    L.vdn_vda_backward_gram.argtypes = [dp] + [p] * 13 + [sz, p]
+    L.vdn_vda_backward_gram.restype = ctypes.c_int
+    L.vdn_vda_gates_workspace_bytes.argtypes = [dp, ctypes.c_int32]
+    L.vdn_vda_gates_workspace_bytes.restype = sz
+    L.vdn_vda_gates.argtypes = [dp, ctypes.c_int32] + [p] * 7 + [sz, p]
+    L.vdn_vda_gates.restype = ctypes.c_int
+    L.vdn_vda_out_proj.argtypes = [dp, ctypes.c_int32] + [p] * 5
+    L.vdn_vda_out_proj.restype = ctypes.c_int
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """The loaded library; raises if it has not been built."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: run `python -m frame_wise_delta_02_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        p, sz = ctypes.c_void_p, ctypes.c_size_t
-        dp = ctypes.POINTER(Desc)
-        L.vdn_vda_validate.argtypes = [dp]
-        L.vdn_vda_validate.restype = ctypes.c_int
-        L.vdn_vda_workspace_bytes.argtypes = [dp]
-        L.vdn_vda_workspace_bytes.restype = sz
-        L.vdn_vda_workspace_layout.argtypes = [dp, ctypes.POINTER(Layout)]
-        L.vdn_vda_workspace_layout.restype = ctypes.c_int
-        L.vdn_vda_prepare.argtypes = [dp] + [p] * 11
-        L.vdn_vda_prepare.restype = ctypes.c_int
-        L.vdn_vda_forward.argtypes = [dp] + [p] * 12 + [sz, p]
-        L.vdn_vda_forward.restype = ctypes.c_int
-        L.vdn_vda_forward_timed.argtypes = [dp] + [p] * 12 + [sz, p, p, ctypes.c_int32]
-        L.vdn_vda_forward_timed.restype = ctypes.c_int
-        L.vdn_vda_forward_noalloc.argtypes = [dp] + [p] * 12
-        L.vdn_vda_forward_noalloc.restype = ctypes.c_int
-        L.vdn_vda_status_string.argtypes = [ctypes.c_int]
-        L.vdn_vda_status_string.restype = ctypes.c_char_p
-        L.vdn_vda_backward_workspace_bytes.argtypes = [dp]
-        L.vdn_vda_backward_workspace_bytes.restype = sz
-        L.vdn_vda_backward_workspace_layout.argtypes = [dp, ctypes.POINTER(BackwardLayout)]
-        L.vdn_vda_backward_workspace_layout.restype = ctypes.c_int
-        L.vdn_vda_backward_readout.argtypes = [dp] + [p] * 6 + [sz] + [p] * 3 + [sz, p]
-        L.vdn_vda_backward_readout.restype = ctypes.c_int
-        L.vdn_vda_backward_scan.argtypes = [dp, p, p, sz, p, p, sz, p]
-        L.vdn_vda_backward_scan.restype = ctypes.c_int
-        L.vdn_vda_backward_gram.argtypes = [dp] + [p] * 13 + [sz, p]
-        L.vdn_vda_backward_gram.restype = ctypes.c_int
-        L.vdn_vda_gates_workspace_bytes.argtypes = [dp, ctypes.c_int32]
-        L.vdn_vda_gates_workspace_bytes.restype = sz
-        L.vdn_vda_gates.argtypes = [dp, ctypes.c_int32] + [p] * 7 + [sz, p]
-        L.vdn_vda_gates.restype = ctypes.c_int
-        L.vdn_vda_out_proj.argtypes = [dp, ctypes.c_int32] + [p] * 5
-        L.vdn_vda_out_proj.restype = ctypes.c_int
-        _lib = L
+        _lib = declare(ctypes.CDLL(LIB_PATH))
     return _lib
 
 

@@ -220,7 +220,9 @@ __global__ __launch_bounds__(256, 2) void solve_mfma(const float* __restrict__ s
   auto Wb = [&](int m, int j, int kk, int n) -> float {  // W_mj[kk][n], m >= j
     return (m == j) ? Wd[j][kk * WDS + n] : P[(16 * j + n) * LDP + 16 * m + kk];
   };
-  float* Tx = &P[16 * wave * LDP + 16 * wave];
+  // (with NB < 4 the waves that own no block column take wave 0's address,
+  // which they never use, instead of one past P)
+  float* Tx = &P[16 * (NB >= 4 || wave < NB ? wave : 0) * (LDP + 1)];
   for (int pass = 0; pass < 2; ++pass) {
     const int j = pass == 0 ? wave : NB - 1 - wave;
     if (j < 0 || j >= NB || (pass == 1 && j < 4)) continue;

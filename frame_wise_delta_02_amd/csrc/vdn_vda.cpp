@@ -317,8 +317,12 @@ vdn_status forward_impl(const vdn_vda_desc* d, const void* q, const void* k, con
   // frame statistics of frames 1..T-2 (anchors are never absorbed) and of the
   // text frame (slot T) in one launch: the short text blocks run last, in the
   // final round of the video blocks
+  // With no text tokens the text frame's units read nothing (their buffer
+  // ranges are empty) and leave A = B = 0; the video tensors stand in for the
+  // absent text pointers so that no address is formed from a null pointer.
+  const bool text = p.L > 0;
   const GramPart parts[2] = {{k, v, beta, p.T, p.U, 1, n_video, 0},
-                             {k_text, v_text, beta_text, 1, p.L, 0, 1, p.T}};
+                             {text ? k_text : k, text ? v_text : v, text ? beta_text : beta, 1, p.L, 0, 1, p.T}};
   if (e == hipSuccess) e = launch_gram(p, parts, 2, stats, stream);
   if (e == hipSuccess) e = mark(1, stream);
   if (e == hipSuccess) e = launch_solve(p, stats, pinv, stream);

@@ -1,0 +1,107 @@
+"""Build the CPU build of the library: every source of
+frame_wise_delta_02_amd/csrc compiled for the host with clang against the
+emulated device environment in this folder (simt.h), as
+
+* ``check`` -- the self-checking forward driver (check.cpp), with
+  AddressSanitizer and UndefinedBehaviorSanitizer, or
+* ``libvdn_vda_sim.so`` -- the C ABI as a host library, for tests that compare
+  the kernels' results with the oracle from Python.
+
+The kernel sources are used as they are, except for the one inline-asm line of
+vda_internal.h (sgpr(): v_readfirstlane_b32 into a scalar register), which is
+rewritten to the readfirstlane builtin the emulator provides.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+CSRC = os.path.join(ROOT, "frame_wise_delta_02_amd", "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+CXX_CANDIDATES = ("/opt/rocm/llvm/bin/clang++", "/opt/rocm/lib/llvm/bin/clang++", shutil.which("clang++") or "")
+
+SGPR_ASM = 'asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(r) : "v"(v));'
+SGPR_HOST = "r = __builtin_amdgcn_readfirstlane(v);"
+
+
+def compiler() -> str | None:
+    for c in CXX_CANDIDATES:
+        if c and os.path.exists(c):
+            return c
+    return None
+
+
+def _sources(out: str) -> list[str]:
+    src = os.path.join(out, "src")
+    os.makedirs(src, exist_ok=True)
+    files = []
+    for f in sorted(os.listdir(CSRC)):
+        if not f.endswith((".hip", ".h", ".cpp")):
+            continue
+        text = open(os.path.join(CSRC, f)).read()
+        if f == "vda_internal.h":
+            if SGPR_ASM not in text:
+                raise RuntimeError("vda_internal.h: the sgpr() asm line changed; update tests/cpu_build/build.py")
+            text = text.replace(SGPR_ASM, SGPR_HOST)
+        if "asm volatile(\"v_" in text or "asm volatile(\"s_" in text:
+            raise RuntimeError(f"{f}: inline asm the host build cannot compile")
+        dst = os.path.join(src, f)
+        if not os.path.exists(dst) or open(dst).read() != text:
+            with open(dst, "w") as fh:
+                fh.write(text)
+        if f.endswith((".hip", ".cpp")):
+            files.append(dst)
+    return files
+
+
+def build(out: str, sanitize: bool) -> str:
+    """Compile into ``out``; returns the path of ``check`` (sanitize=True) or of
+    ``libvdn_vda_sim.so`` (sanitize=False)."""
+    cxx = compiler()
+    if cxx is None:
+        raise RuntimeError("no clang++ for the host build")
+    files = _sources(out) + [os.path.join(HERE, "simt.cpp")]
+    flags = ["-x", "c++", "-std=c++17", "-g", "-fPIC", "-fno-omit-frame-pointer", "-I", HERE, "-I", INCLUDE,
+             "-I", os.path.join(out, "src"), "-Wno-unused-value", "-Wno-unknown-attributes",
+             "-Wno-ignored-attributes"]
+    if sanitize:
+        flags += ["-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
+    else:
+        flags += ["-O2"]
+
+    def compile_one(f):
+        o = os.path.join(out, os.path.splitext(os.path.basename(f))[0] + (".san.o" if sanitize else ".o"))
+        if os.path.exists(o) and os.path.getmtime(o) >= max(os.path.getmtime(f), os.path.getmtime(
+                os.path.join(HERE, "simt.h"))) and all(
+                os.path.getmtime(o) >= os.path.getmtime(os.path.join(out, "src", h))
+                for h in os.listdir(os.path.join(out, "src")) if h.endswith(".h")):
+            return o
+        r = subprocess.run([cxx, *flags, "-c", f, "-o", o], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"host build of {f} failed:\n{r.stderr[-4000:]}")
+        return o
+
+    with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
+        objs = list(ex.map(compile_one, files))
+    if sanitize:
+        target = os.path.join(out, "check")
+        cmd = [cxx, *flags[2:], os.path.join(HERE, "check.cpp"), *objs, "-o", target]
+    else:
+        target = os.path.join(out, "libvdn_vda_sim.so")
+        cmd = [cxx, "-shared", *flags[2:], *objs, "-o", target]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link of {target} failed:\n{r.stderr[-4000:]}")
+    return target
+
+
+if __name__ == "__main__":
+    import sys
+    out = sys.argv[1] if len(sys.argv) > 1 else os.path.join(ROOT, "_build", "cpu_build")
+    print(build(out, sanitize=True))
+    print(build(out, sanitize=False))

@@ -131,8 +131,10 @@ def model_gram(p: Prob, r: Report):
     K, V, beta, then the text frame (slot T)."""
     S = sizes(p)
     D, H = p.D, p.H
+    # with no text tokens the text units' (empty) descriptors sit on the video tensors
+    text = ("k_text", "v_text", "beta_text") if p.L > 0 else ("k", "v", "beta")
     parts = [("k", "v", "beta", p.T, p.U, 1, max(p.T - 2, 0), 0),
-             ("k_text", "v_text", "beta_text", 1, p.L, 0, 1, p.T)]
+             (*text, 1, p.L, 0, 1, p.T)]
     R = 2 * D
     for kb, vb, bb, T_in, U, t_first, n_frames, slot_off in parts:
         nblk = p.B * n_frames * H
