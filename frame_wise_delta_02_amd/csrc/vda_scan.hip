@@ -332,7 +332,10 @@ void scan_rows(const float* __restrict__ stats, const float* __restrict__ pinv,
   // SCAN_ADJOINT T+1 frame adjoints
   constexpr int NREC_EXTRA = STATES ? 2 : 1;
   const int nrec = (STATES || ADJ) ? T + NREC_EXTRA : nc;
-  float* out0 = (ADJ ? (dir == 0 ? chunk_m : chunk_j) : (dir == 0 ? fwd : rev)) + head * (size_t)nrec * D * D;
+  // (the composition pass writes no records, and its launch passes no record
+  // buffers: no address is formed for it)
+  float* out0 = COMPOSE ? nullptr
+                        : (ADJ ? (dir == 0 ? chunk_m : chunk_j) : (dir == 0 ? fwd : rev)) + head * (size_t)nrec * D * D;
   const auto rec = make_rsrc(out0, (uint32_t)nrec * D * D * 4);
 
   vec_t zero4[MT][4];

@@ -3,9 +3,12 @@ frame_wise_delta_02_amd/csrc compiled for the host with clang against the
 emulated device environment in this folder (simt.h), as
 
 * ``check`` -- the self-checking forward driver (check.cpp), with
-  AddressSanitizer and UndefinedBehaviorSanitizer, or
+  AddressSanitizer and UndefinedBehaviorSanitizer,
 * ``libvdn_vda_sim.so`` -- the C ABI as a host library, for tests that compare
-  the kernels' results with the oracle from Python.
+  the kernels' results with the oracle from Python, or
+* ``libvdn_vda_sim_san.so`` -- the same with both sanitizers, linked against the
+  shared sanitizer runtime (``sanitizer_runtime()``), which the loading process
+  must preload.
 
 The kernel sources are used as they are, except for the one inline-asm line of
 vda_internal.h (sgpr(): v_readfirstlane_b32 into a scalar register), which is
@@ -59,27 +62,40 @@ def _sources(out: str) -> list[str]:
     return files
 
 
-def build(out: str, sanitize: bool) -> str:
-    """Compile into ``out``; returns the path of ``check`` (sanitize=True) or of
-    ``libvdn_vda_sim.so`` (sanitize=False)."""
+def sanitizer_runtime() -> str:
+    """The shared AddressSanitizer runtime (with the UndefinedBehaviorSanitizer
+    handlers) that a process loading libvdn_vda_sim_san.so must preload."""
+    r = subprocess.run([compiler(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+KINDS = {"check": ("check", True), "lib": ("libvdn_vda_sim.so", False), "lib_san": ("libvdn_vda_sim_san.so", True)}
+
+
+def build(out: str, kind: str) -> str:
+    """Compile into ``out``; returns the path of the target ``kind`` ("check",
+    "lib" or "lib_san")."""
     cxx = compiler()
     if cxx is None:
         raise RuntimeError("no clang++ for the host build")
+    name, sanitize = KINDS[kind]
     files = _sources(out) + [os.path.join(HERE, "simt.cpp")]
     flags = ["-x", "c++", "-std=c++17", "-g", "-fPIC", "-fno-omit-frame-pointer", "-I", HERE, "-I", INCLUDE,
              "-I", os.path.join(out, "src"), "-Wno-unused-value", "-Wno-unknown-attributes",
              "-Wno-ignored-attributes"]
     if sanitize:
         flags += ["-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
+        if kind == "lib_san":
+            flags += ["-shared-libsan"]
     else:
         flags += ["-O2"]
+    suffix = {"check": ".san.o", "lib": ".o", "lib_san": ".dsan.o"}[kind]
+    headers = [os.path.join(out, "src", h) for h in os.listdir(os.path.join(out, "src")) if h.endswith(".h")]
+    newest_header = max([os.path.getmtime(os.path.join(HERE, "simt.h"))] + [os.path.getmtime(h) for h in headers])
 
     def compile_one(f):
-        o = os.path.join(out, os.path.splitext(os.path.basename(f))[0] + (".san.o" if sanitize else ".o"))
-        if os.path.exists(o) and os.path.getmtime(o) >= max(os.path.getmtime(f), os.path.getmtime(
-                os.path.join(HERE, "simt.h"))) and all(
-                os.path.getmtime(o) >= os.path.getmtime(os.path.join(out, "src", h))
-                for h in os.listdir(os.path.join(out, "src")) if h.endswith(".h")):
+        o = os.path.join(out, os.path.splitext(os.path.basename(f))[0] + suffix)
+        if os.path.exists(o) and os.path.getmtime(o) >= max(os.path.getmtime(f), newest_header):
             return o
         r = subprocess.run([cxx, *flags, "-c", f, "-o", o], capture_output=True, text=True)
         if r.returncode != 0:
@@ -88,11 +104,10 @@ def build(out: str, sanitize: bool) -> str:
 
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
         objs = list(ex.map(compile_one, files))
-    if sanitize:
-        target = os.path.join(out, "check")
+    target = os.path.join(out, name)
+    if kind == "check":
         cmd = [cxx, *flags[2:], os.path.join(HERE, "check.cpp"), *objs, "-o", target]
     else:
-        target = os.path.join(out, "libvdn_vda_sim.so")
         cmd = [cxx, "-shared", *flags[2:], *objs, "-o", target]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -103,5 +118,5 @@ def build(out: str, sanitize: bool) -> str:
 if __name__ == "__main__":
     import sys
     out = sys.argv[1] if len(sys.argv) > 1 else os.path.join(ROOT, "_build", "cpu_build")
-    print(build(out, sanitize=True))
-    print(build(out, sanitize=False))
+    for kind in KINDS:
+        print(build(out, kind))

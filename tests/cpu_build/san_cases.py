@@ -1,0 +1,94 @@
+"""Every C ABI entry point of the sanitized CPU build (libvdn_vda_sim_san.so)
+on small cases, in a process that preloads the sanitizer runtime:
+
+    LD_PRELOAD=<libclang_rt.asan> python tests/cpu_build/san_cases.py <library> [--full]
+
+(tests/test_cpu_build.py starts it so, with one case per kernel variant and
+mode; --full runs every forward edge case, every backward case and every
+adjacent-map case, about eight minutes).  Any AddressSanitizer or
+UndefinedBehaviorSanitizer report ends the process with a nonzero status; the
+results themselves are compared with the oracle by the unsanitized tests, so
+here they are only checked to be finite.
+"""
+
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path[:0] = [os.path.dirname(HERE), os.path.dirname(os.path.dirname(HERE))]
+
+import numpy as np  # noqa: E402
+
+import test_gpu_adjacent as GA  # noqa: E402
+import test_gpu_backward as GB  # noqa: E402
+import test_gpu_parity as P  # noqa: E402
+from cpu_build import sim as S  # noqa: E402
+from frame_wise_delta_02_amd import synth  # noqa: E402
+
+
+def finite(*arrays):
+    for a in arrays:
+        if a is not None:
+            assert np.isfinite(S.to_f64(a)).all()
+
+
+FORWARD = ("d32_bf16", "d16_bf16", "d32_f32", "ragged_f32_128", "no_text_bf16", "T1_bf16", "T2_f32",
+           "chunk3_bf16", "batch2_bf16", "U1_bf16_128", "U2_f32_16", "ragged_bf16_128")
+FORWARD_QUICK = ("d32_bf16", "d16_bf16", "d32_f32", "no_text_bf16", "T1_bf16", "U1_bf16_128", "U2_f32_16")
+BACKWARD_QUICK = ("bwd_64_ragged", "bwd_32_bridge", "bwd_16_chunk3", "bwd_64_no_text", "bwd_16_ql2", "bwd_T1")
+ADJACENT_QUICK = ("adj_small", "adj_d16", "adj_tiny")
+
+
+def main(path, full):
+    L = S.load(path)
+    done = []
+    for name in FORWARD if full else FORWARD_QUICK:
+        w = P.EDGE[name]
+        x = synth.make_inputs(w)
+        for scan in ("frames", "chunks"):
+            out, _, _ = S.run_forward(L, x, w, epilogue=True, scan=scan,
+                                      rms_weight=np.linspace(0.5, 1.5, w.d) if w.d == 128 else None)
+            finite(out)
+        out, _, _ = S.run_forward(L, x, w, epilogue=False, bridge=True)
+        finite(out)
+        done.append(f"forward {name}")
+    w = P.EDGE["ragged_bf16_128" if full else "d32_bf16"]
+    finite(S.run_forward_noalloc(L, synth.make_inputs(w), w))
+    done.append("forward_noalloc")
+    for name, kw in (("prep_small_bf16", dict(H=2, T=5, grid_h=6, grid_w=10, L=8)),
+                     ("prep_small_f32", dict(H=2, T=5, grid_h=6, grid_w=10, L=8, dtype="f32")),
+                     ("prep_T1_ragged", P.PREP_EDGE["prep_T1_ragged"]),
+                     ("prep_d64", dict(H=2, T=6, grid_h=5, grid_w=7, L=4, d=64))):
+        w = synth.WORKLOADS["long_prep_bf16"].scaled(name=name, **kw)
+        x = synth.make_inputs(w)
+        qh, kh, vh = S.run_prepare(L, x, w)
+        finite(qh, kh, vh)
+        _, kf, vf = S.run_prepare(L, x, w, query_l2=True)
+        out, _, _ = S.run_forward(L, x, w, epilogue=True, query_l2=True, inputs={"k": kf, "v": vf})
+        finite(out)
+        done.append(f"prepare + fused query {name}")
+    for name in GB.CASES if full else BACKWARD_QUICK:
+        case = GB.CASES[name]
+        w, epi = case["w"], case.get("epilogue", True)
+        bridge, ql2 = case.get("bridge", False), case.get("query_l2", False)
+        x = synth.make_inputs(w)
+        if ql2:
+            GB._raw_queries(x, w)
+        rw = np.linspace(0.5, 1.5, w.d) if case.get("gain") else None
+        _, fws, _ = S.run_forward(L, x, w, epilogue=epi, rms_weight=rw, bridge=bridge, query_l2=ql2)
+        got, _, _ = S.run_backward(L, x, w, GB._dy(w), fws, epilogue=epi, rms_weight=rw, bridge=bridge,
+                                   query_l2=ql2)
+        finite(*(v for v in got.values()))
+        done.append(f"backward {name}")
+    for name in GA.CASES if full else ADJACENT_QUICK:
+        w, dm = GA.CASES[name]
+        p = synth.make_adjacent_inputs(w, dm)
+        finite(*S.run_gates(L, p, w, dm))
+        for mode in ("y_in", "in_place", "no_y_in"):
+            finite(S.run_out_proj(L, p, w, mode))
+        done.append(f"gates + out_proj {name}")
+    print(f"all entry points ran: {len(done)} cases")
+
+
+if __name__ == "__main__":
+    main(sys.argv[1], "--full" in sys.argv[2:])

@@ -35,12 +35,12 @@ pytestmark = pytest.mark.skipif(CB.compiler() is None, reason="no host clang++ f
 
 @pytest.fixture(scope="module")
 def check_exe():
-    return CB.build(S.OUT, sanitize=True)
+    return CB.build(S.OUT, "check")
 
 
 @pytest.fixture(scope="module")
 def lib():
-    return S.load(CB.build(S.OUT, sanitize=False))
+    return S.load(CB.build(S.OUT, "lib"))
 
 
 # H, T, grid_h, grid_w, d, L, dtype
@@ -62,7 +62,7 @@ SAN_SHAPES = [
 
 @pytest.mark.parametrize("shape", SAN_SHAPES, ids=["x".join(map(str, s)) for s in SAN_SHAPES])
 def test_forward_under_sanitizers(check_exe, shape):
-    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1",
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:detect_stack_use_after_return=0",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
     r = subprocess.run([check_exe, *map(str, shape)], capture_output=True, text=True, timeout=900, env=env)
     out = r.stdout + r.stderr
@@ -92,8 +92,11 @@ def _case(lib, w, scan=None, bridge=False, rms=False):
     assert err_y <= tol, err_y
 
 
-@pytest.mark.parametrize("scan", P.SCANS)
-@pytest.mark.parametrize("name", list(PARITY))
+# both scans on every case but the two-batch one (the slowest; the frame scan)
+PARITY_RUNS = [(n, s) for n in PARITY for s in P.SCANS if not (n == "batch2_bf16" and s == "chunks")]
+
+
+@pytest.mark.parametrize("name,scan", PARITY_RUNS, ids=[f"{n}-{s}" for n, s in PARITY_RUNS])
 def test_forward_matches_oracle(lib, name, scan):
     _case(lib, PARITY[name], scan=scan, rms=name.endswith("128") or name == "d32_bf16")
 
@@ -174,3 +177,122 @@ def test_values_beyond_the_half_range(lib):
     assert G.slice_rel_err(S.to_f64(out), ref["y"]) <= tol
     assert G.mat_rel_err(inter["B"][:, :, 1:w.T - 1], ref["B"][:, :, 1:w.T - 1]) <= tol
     assert G.mat_rel_err(inter["S_T"], ref["S_T"]) <= tol
+
+
+# ---------------------------------------------------------------------------
+# the backward pass: the three stages against the oracle's gradients, with the
+# checks of the GPU backward tests
+# ---------------------------------------------------------------------------
+import test_gpu_backward as GB  # noqa: E402
+from oracle import vda_grad  # noqa: E402
+
+BWD = ["bwd_128", "bwd_128_raw", "bwd_64_ragged", "bwd_32_bridge", "bwd_64_bridge", "bwd_16_chunk3",
+       "bwd_64_no_text", "bwd_128_ql2", "bwd_16_ql2", "bwd_T1", "bwd_T2", "bwd_B2_chunk3"]
+
+
+@pytest.mark.parametrize("name", BWD)
+def test_backward_matches_oracle(lib, name):
+    case = GB.CASES[name]
+    w, epi, bridge, ql2 = case["w"], case.get("epilogue", True), case.get("bridge", False), case.get("query_l2", False)
+    x = synth.make_inputs(w)
+    if ql2:
+        GB._raw_queries(x, w)
+    dy = GB._dy(w)
+    rw = np.random.default_rng(5).uniform(0.5, 1.5, w.d) if case.get("gain") else None
+    _, fws, _ = S.run_forward(lib, x, w, epilogue=epi, rms_weight=rw, bridge=bridge, query_l2=ql2)
+    got, bws, lay = S.run_backward(lib, x, w, dy, fws, epilogue=epi, rms_weight=rw, bridge=bridge, query_l2=ql2,
+                                   l2_eps=GB.L2_EPS)
+    f = G.oracle_view({k: x[k] for k in ("q", "k", "v", "beta", "k_text", "v_text", "beta_text", "gate")}, w)
+    ref = vda_grad.backward(f["q"], f["k"], f["v"], x["alpha"].astype(np.float64), f["beta"], f["k_text"],
+                            f["v_text"], f["beta_text"], G.oracle_view({"dy": dy}, w)["dy"],
+                            gate=f["gate"] if epi else None, rms_weight=rw, chunk=w.chunk, bridge=bridge,
+                            query_l2=GB.L2_EPS if ql2 else None)
+    B, H, T, U, d, L = w.B, w.H, w.T, w.U, w.d, w.L
+    nc = -(-T // w.chunk)
+    do_want = np.moveaxis(ref["do"], 1, 3)
+    if ql2:
+        do_want = do_want / np.sqrt(np.sum(f["q"] ** 2, axis=-1, keepdims=True) + GB.L2_EPS)
+    fr = slice(1, max(T - 1, 1))
+    sym = lambda a: a + np.swapaxes(a, -1, -2)
+    sec = lambda off, shape, dt="f32": S.section(bws, off, shape, dt)
+    dA, dB = sec(lay.d_a, (B, H, T + 1, d, d)), sec(lay.d_b, (B, H, T + 1, d, d))
+    lam_f, lam_r = sec(lay.lam_f, (B, H, T + 1, d, d)), sec(lay.lam_r, (B, H, T + 1, d, d))
+    errs = {
+        "dq": G.slice_rel_err(S.to_f64(got["dq"]), ref["dq"]),
+        "do": G.slice_rel_err(sec(lay.d_out, (B, T, U, H, d), "bf16") if epi else G.oracle_view({"dy": dy}, w)["dy"],
+                              do_want),
+        "dS_q": G.mat_rel_err(sec(lay.d_state_q, (B, H, T, d, d)), ref["dS_q"]),
+        "dF": GB._rel(sec(lay.d_record_f, (B, H, nc, d, d))[:, :, :max(nc - 2, 0)], ref["dF"][:, :, :max(nc - 2, 0)]),
+        "dR": GB._rel(sec(lay.d_record_r, (B, H, nc, d, d))[:, :, 2:], ref["dR"][:, :, 2:]),
+        "lam_f": GB._rel(lam_f[:, :, fr], ref["dfwd"][:, :, fr]),
+        "lam_r": GB._rel(lam_r[:, :, fr], ref["drev"][:, :, fr]),
+        "dS_T": GB._rel(lam_f[:, :, T], ref["dS_T"]),
+        "dA": GB._rel(sym(dA[:, :, fr]), sym(ref["dA"][:, :, fr])),
+        "dB": GB._rel(dB[:, :, fr], ref["dB"][:, :, fr]),
+        "dA_T": GB._rel(sym(dA[:, :, T]), sym(ref["dA_T"])) if L else 0.0,
+        "dB_T": GB._rel(dB[:, :, T], ref["dB_T"]) if L else 0.0,
+        "dalpha": GB._rel(got["dalpha"].astype(np.float64), ref["dalpha"]),
+        "dk": G.slice_rel_err(S.to_f64(got["dk"]), ref["dk"]),
+        "dv": G.slice_rel_err(S.to_f64(got["dv"]), ref["dv"]),
+        "dbeta": G.slice_rel_err(S.to_f64(got["dbeta"])[..., None], ref["dbeta"][..., None]),
+    }
+    if epi:
+        errs["dgate"] = G.slice_rel_err(S.to_f64(got["dgate"]), ref["dgate"])
+    if L:
+        txt = lambda a: a.reshape((B, 1) + a.shape[1:] + ((1,) if a.ndim == 3 else ()))
+        errs.update({"dk_text": G.slice_rel_err(txt(S.to_f64(got["dk_text"])), txt(ref["dk_txt"])),
+                     "dv_text": G.slice_rel_err(txt(S.to_f64(got["dv_text"])), txt(ref["dv_txt"])),
+                     "dbeta_text": G.slice_rel_err(txt(S.to_f64(got["dbeta_text"])), txt(ref["dbeta_txt"]))})
+    bad = {k: v for k, v in errs.items() if not v <= G.TOL[w.dtype]}
+    assert not bad, bad
+    # the anchors take no part in any scan, and their tokens reach no state
+    assert np.abs(dA[:, :, [0, T - 1]]).max() == 0 and np.abs(dB[:, :, [0, T - 1]]).max() == 0
+    for k in ("dk", "dv", "dbeta"):
+        assert np.abs(S.to_f64(got[k])[:, [0, T - 1]]).max() == 0, k
+
+
+# ---------------------------------------------------------------------------
+# the adjacent linear maps, with the checks of the GPU adjacent-map tests
+# ---------------------------------------------------------------------------
+import test_gpu_adjacent as GA  # noqa: E402
+from oracle import vda_adjacent as adj  # noqa: E402
+
+
+@pytest.mark.parametrize("name", list(GA.CASES))
+def test_gates_match_oracle(lib, name):
+    w, dm = GA.CASES[name]
+    p = synth.make_adjacent_inputs(w, dm)
+    gate, beta, alpha = S.run_gates(lib, p, w, dm)
+    wg = GA._f64(p["w_gb"])
+    g_ref, b_ref, a_ref = adj.gate_proj(GA._f64(p["x"]), wg[: w.H * w.d], wg[w.H * w.d:], GA._f64(p["w_alpha"]),
+                                        w.H, w.d)
+    assert G.slice_rel_err(S.to_f64(gate), g_ref) <= 2e-2
+    assert G.slice_rel_err(GA._slices(S.to_f64(beta)), GA._slices(b_ref)) <= 2e-2
+    assert np.abs(alpha.astype(np.float64) - a_ref).max() <= 1e-5
+
+
+@pytest.mark.parametrize("mode", ["y_in", "in_place", "no_y_in"])
+@pytest.mark.parametrize("name", list(GA.CASES))
+def test_out_proj_matches_oracle(lib, name, mode):
+    w, dm = GA.CASES[name]
+    p = synth.make_adjacent_inputs(w, dm)
+    y = S.run_out_proj(lib, p, w, mode)
+    ref = adj.out_proj(GA._f64(p["o"]), GA._f64(p["w_o"]), None if mode == "no_y_in" else GA._f64(p["y_in"]))
+    assert G.slice_rel_err(GA._slices(S.to_f64(y)), GA._slices(ref)) <= 2e-2
+
+
+def test_every_entry_point_under_sanitizers():
+    """tests/cpu_build/san_cases.py on the sanitized library: every entry point
+    (forward in both scans, with the bridge and the fused query norm, the
+    no-allocation forward, prepare, the three backward stages, the gates and
+    the output projection) with AddressSanitizer and UndefinedBehaviorSanitizer."""
+    import sys
+    path = CB.build(S.OUT, "lib_san")
+    env = dict(os.environ, LD_PRELOAD=CB.sanitizer_runtime(),
+               ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:detect_stack_use_after_return=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(CB.__file__), "san_cases.py"), path],
+                       capture_output=True, text=True, timeout=1800, env=env)
+    out = r.stdout + r.stderr
+    assert r.returncode == 0 and "all entry points ran" in r.stdout, out[-6000:]
+    assert "runtime error" not in out and "Sanitizer" not in out and "[simt]" not in out, out[-6000:]
