@@ -296,3 +296,51 @@ def test_every_entry_point_under_sanitizers():
     out = r.stdout + r.stderr
     assert r.returncode == 0 and "all entry points ran" in r.stdout, out[-6000:]
     assert "runtime error" not in out and "Sanitizer" not in out and "[simt]" not in out, out[-6000:]
+
+
+# ---------------------------------------------------------------------------
+# seeded random shapes and flags, forward and backward against the oracle
+# ---------------------------------------------------------------------------
+def _random_case(seed):
+    rng = np.random.default_rng(seed)
+    dtype = str(rng.choice(["bf16", "f32"]))
+    base = synth.WORKLOADS["768p_bf16" if dtype == "bf16" else "stress_f32"]
+    # no single-token text frame: with one text token S_T has rank one, every
+    # output of the frames that read it points along that token's value, the
+    # RMSNorm output no longer depends on q there and the true dq is ~0, so a
+    # per-slice relative error measures rounding against zero
+    w = base.scaled(name=f"random_{seed}", dtype=dtype, d=int(rng.choice([16, 32, 64, 128])),
+                    B=int(rng.choice([1, 1, 2])), H=int(rng.integers(1, 5)), T=int(rng.integers(1, 14)),
+                    grid_h=int(rng.integers(1, 9)), grid_w=int(rng.integers(1, 12)),
+                    L=int(rng.choice([0, 3, 17, 40])), chunk=int(rng.integers(1, 7)))
+    fl = dict(bridge=bool(rng.random() < 0.3), scan=[None, "frames", "chunks"][int(rng.integers(3))],
+              epilogue=bool(rng.random() < 0.7), gain=bool(rng.random() < 0.3),
+              backward=bool(dtype == "bf16" and rng.random() < 0.6))
+    return w, fl
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_shapes_match_oracle(lib, seed):
+    w, fl = _random_case(4000 + seed)
+    x = synth.make_inputs(w)
+    rw = np.random.default_rng(5).uniform(0.5, 1.5, w.d) if fl["gain"] else None
+    out, ws, desc = S.run_forward(lib, x, w, epilogue=fl["epilogue"], rms_weight=rw, bridge=fl["bridge"],
+                                  scan=fl["scan"])
+    heads = list(range(w.H))
+    ref = P._oracle_heads(x, w, heads, gate=True, rms_weight=rw, bridge=fl["bridge"])
+    tol = G.TOL[w.dtype]
+    P._check_intermediates(S.intermediates(lib, ws, desc, w), ref, w, heads, tol)
+    assert G.slice_rel_err(S.to_f64(out), ref["y" if fl["epilogue"] else "o"]) <= tol, (w, fl)
+    if not fl["backward"]:
+        return
+    dy = GB._dy(w)
+    got, _, _ = S.run_backward(lib, x, w, dy, ws, epilogue=fl["epilogue"], rms_weight=rw, bridge=fl["bridge"])
+    f = G.oracle_view({k: x[k] for k in ("q", "k", "v", "beta", "k_text", "v_text", "beta_text", "gate")}, w)
+    gref = vda_grad.backward(f["q"], f["k"], f["v"], x["alpha"].astype(np.float64), f["beta"], f["k_text"],
+                             f["v_text"], f["beta_text"], G.oracle_view({"dy": dy}, w)["dy"],
+                             gate=f["gate"] if fl["epilogue"] else None, rms_weight=rw, chunk=w.chunk,
+                             bridge=fl["bridge"])
+    errs = {k: G.slice_rel_err(S.to_f64(got[k]), gref[k]) for k in ("dq", "dk", "dv")}
+    errs["dalpha"] = GB._rel(got["dalpha"].astype(np.float64), gref["dalpha"])
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, (w, fl, bad)
