@@ -55,6 +55,23 @@ def main(path, full):
     w = P.EDGE["ragged_bf16_128" if full else "d32_bf16"]
     finite(S.run_forward_noalloc(L, synth.make_inputs(w), w))
     done.append("forward_noalloc")
+    # arbitrary bit patterns in every input (negative, infinite and NaN beta and
+    # alpha included): the results are meaningless, but no access may leave its
+    # buffer and no operation may be undefined, whatever the data
+    rng = np.random.default_rng(99)
+    for name in ("ragged_bf16_128", "d32_bf16", "ragged_f32_128") if full else ("ragged_bf16_128", "d32_f32"):
+        w = P.EDGE[name]
+        x = synth.make_inputs(w)
+        for k, a in x.items():
+            if a.dtype == np.uint16:
+                x[k] = rng.integers(0, 1 << 16, a.shape, dtype=np.uint16)
+            elif a.dtype == np.float32:
+                x[k] = rng.integers(0, 1 << 32, a.shape, dtype=np.uint32).view(np.float32)
+        for scan in ("frames", "chunks"):
+            S.run_forward(L, x, w, epilogue=True, scan=scan)
+        S.run_forward(L, x, w, epilogue=False, bridge=True)
+        S.run_forward_noalloc(L, x, w)
+        done.append(f"forward on arbitrary bit patterns {name}")
     for name, kw in (("prep_small_bf16", dict(H=2, T=5, grid_h=6, grid_w=10, L=8)),
                      ("prep_small_f32", dict(H=2, T=5, grid_h=6, grid_w=10, L=8, dtype="f32")),
                      ("prep_T1_ragged", P.PREP_EDGE["prep_T1_ragged"]),
