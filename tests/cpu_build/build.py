@@ -69,17 +69,19 @@ def sanitizer_runtime() -> str:
     return r.stdout.strip()
 
 
-KINDS = {"check": ("check", True), "lib": ("libvdn_vda_sim.so", False), "lib_san": ("libvdn_vda_sim_san.so", True)}
+KINDS = {"check": ("check", True), "lib": ("libvdn_vda_sim.so", False), "lib_san": ("libvdn_vda_sim_san.so", True),
+         "selftest": ("selftest", True)}
 
 
 def build(out: str, kind: str) -> str:
     """Compile into ``out``; returns the path of the target ``kind`` ("check",
-    "lib" or "lib_san")."""
+    "lib", "lib_san", or "selftest": the emulator's own checks, selftest.cpp)."""
     cxx = compiler()
     if cxx is None:
         raise RuntimeError("no clang++ for the host build")
     name, sanitize = KINDS[kind]
-    files = _sources(out) + [os.path.join(HERE, "simt.cpp")]
+    files = ([] if kind == "selftest" else _sources(out)) + [os.path.join(HERE, "simt.cpp")]
+    os.makedirs(os.path.join(out, "src"), exist_ok=True)
     flags = ["-x", "c++", "-std=c++17", "-g", "-fPIC", "-fno-omit-frame-pointer", "-I", HERE, "-I", INCLUDE,
              "-I", os.path.join(out, "src"), "-Wno-unused-value", "-Wno-unknown-attributes",
              "-Wno-ignored-attributes"]
@@ -89,7 +91,7 @@ def build(out: str, kind: str) -> str:
             flags += ["-shared-libsan"]
     else:
         flags += ["-O2"]
-    suffix = {"check": ".san.o", "lib": ".o", "lib_san": ".dsan.o"}[kind]
+    suffix = {"check": ".san.o", "lib": ".o", "lib_san": ".dsan.o", "selftest": ".san.o"}[kind]
     headers = [os.path.join(out, "src", h) for h in os.listdir(os.path.join(out, "src")) if h.endswith(".h")]
     newest_header = max([os.path.getmtime(os.path.join(HERE, "simt.h"))] + [os.path.getmtime(h) for h in headers])
 
@@ -105,8 +107,8 @@ def build(out: str, kind: str) -> str:
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
         objs = list(ex.map(compile_one, files))
     target = os.path.join(out, name)
-    if kind == "check":
-        cmd = [cxx, *flags[2:], os.path.join(HERE, "check.cpp"), *objs, "-o", target]
+    if kind in ("check", "selftest"):
+        cmd = [cxx, *flags[2:], os.path.join(HERE, kind + ".cpp"), *objs, "-o", target]
     else:
         cmd = [cxx, "-shared", *flags[2:], *objs, "-o", target]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -344,3 +344,38 @@ def test_random_shapes_match_oracle(lib, seed):
     errs["dalpha"] = GB._rel(got["dalpha"].astype(np.float64), gref["dalpha"])
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, (w, fl, bad)
+
+
+# ---------------------------------------------------------------------------
+# the emulator's own checks fire (tests/cpu_build/selftest.cpp)
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def selftest_exe():
+    return CB.build(S.OUT, "selftest")
+
+
+def _selftest(exe, case):
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:detect_stack_use_after_return=0")
+    return subprocess.run([exe, case], capture_output=True, text=True, timeout=300, env=env)
+
+
+def test_emulated_mfma_layouts(selftest_exe):
+    """Every matrix-core shape against a float64 product of its operands in
+    the layout the emulator states (the library's kernels, built against the
+    same layouts, match the oracle through the emulator and on the GPU)."""
+    r = _selftest(selftest_exe, "mfma")
+    assert r.returncode == 0 and "0 mismatches" in r.stdout, r.stdout + r.stderr
+
+
+def test_emulator_reports_planted_faults(selftest_exe):
+    """A buffer offset that wraps 2^32, unequal barrier counts and a cross-lane
+    operation reached by half a wave are reported; loads past num_records read
+    zero and stores there are dropped."""
+    r = _selftest(selftest_exe, "wrap")
+    assert r.returncode == 0 and "wraps 2^32" in r.stderr, r.stdout + r.stderr
+    r = _selftest(selftest_exe, "range")
+    assert r.returncode == 0, r.stdout + r.stderr
+    r = _selftest(selftest_exe, "barriers")
+    assert r.returncode == 0 and "barriers" in r.stderr, r.stdout + r.stderr
+    r = _selftest(selftest_exe, "diverge")
+    assert r.returncode != 0 and "deadlock" in r.stderr, r.stdout + r.stderr
