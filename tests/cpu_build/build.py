@@ -62,36 +62,44 @@ def _sources(out: str) -> list[str]:
     return files
 
 
-def sanitizer_runtime() -> str:
-    """The shared AddressSanitizer runtime (with the UndefinedBehaviorSanitizer
-    handlers) that a process loading libvdn_vda_sim_san.so must preload."""
-    r = subprocess.run([compiler(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+def sanitizer_runtime(name: str = "asan") -> str:
+    """The shared sanitizer runtime a process loading libvdn_vda_sim_san.so
+    (``asan``: AddressSanitizer with the UndefinedBehaviorSanitizer handlers)
+    or libvdn_vda_sim_tsan.so (``tsan``) must preload."""
+    r = subprocess.run([compiler(), f"-print-file-name=libclang_rt.{name}-x86_64.so"], capture_output=True, text=True)
     return r.stdout.strip()
 
 
 KINDS = {"check": ("check", True), "lib": ("libvdn_vda_sim.so", False), "lib_san": ("libvdn_vda_sim_san.so", True),
-         "selftest": ("selftest", True)}
+         "selftest": ("selftest", True), "check_tsan": ("check_tsan", True), "selftest_tsan": ("selftest_tsan", True),
+         "lib_tsan": ("libvdn_vda_sim_tsan.so", True)}
 
 
 def build(out: str, kind: str) -> str:
     """Compile into ``out``; returns the path of the target ``kind`` ("check",
-    "lib", "lib_san", or "selftest": the emulator's own checks, selftest.cpp)."""
+    "lib", "lib_san", "selftest": the emulator's own checks, selftest.cpp,
+    "check_tsan" / "selftest_tsan": check.cpp / selftest.cpp with
+    ThreadSanitizer on the kernels and the emulator's schedule annotated for
+    it)."""
     cxx = compiler()
     if cxx is None:
         raise RuntimeError("no clang++ for the host build")
     name, sanitize = KINDS[kind]
-    files = ([] if kind == "selftest" else _sources(out)) + [os.path.join(HERE, "simt.cpp")]
+    files = ([] if kind.startswith("selftest") else _sources(out)) + [os.path.join(HERE, "simt.cpp")]
     os.makedirs(os.path.join(out, "src"), exist_ok=True)
     flags = ["-x", "c++", "-std=c++17", "-g", "-fPIC", "-fno-omit-frame-pointer", "-I", HERE, "-I", INCLUDE,
              "-I", os.path.join(out, "src"), "-Wno-unused-value", "-Wno-unknown-attributes",
              "-Wno-ignored-attributes"]
-    if sanitize:
+    tsan = kind in ("check_tsan", "selftest_tsan", "lib_tsan")
+    if tsan:
+        flags += ["-O1", "-fsanitize=thread"]
+    elif sanitize:
         flags += ["-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
-        if kind == "lib_san":
-            flags += ["-shared-libsan"]
     else:
         flags += ["-O2"]
-    suffix = {"check": ".san.o", "lib": ".o", "lib_san": ".dsan.o", "selftest": ".san.o"}[kind]
+    # the sanitized executables and shared libraries share their objects
+    # (-shared-libsan only chooses the runtime at link time)
+    suffix = ".tsan.o" if tsan else ".san.o" if sanitize else ".o"
     headers = [os.path.join(out, "src", h) for h in os.listdir(os.path.join(out, "src")) if h.endswith(".h")]
     newest_header = max([os.path.getmtime(os.path.join(HERE, "simt.h"))] + [os.path.getmtime(h) for h in headers])
 
@@ -99,7 +107,11 @@ def build(out: str, kind: str) -> str:
         o = os.path.join(out, os.path.splitext(os.path.basename(f))[0] + suffix)
         if os.path.exists(o) and os.path.getmtime(o) >= max(os.path.getmtime(f), newest_header):
             return o
-        r = subprocess.run([cxx, *flags, "-c", f, "-o", o], capture_output=True, text=True)
+        fl = flags
+        if kind in ("check_tsan", "selftest_tsan", "lib_tsan") and f.endswith("simt.cpp"):
+            # the emulator's bookkeeping is not instrumented; it annotates instead
+            fl = [x for x in flags if x != "-fsanitize=thread"] + ["-DSIMT_TSAN"]
+        r = subprocess.run([cxx, *fl, "-c", f, "-o", o], capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"host build of {f} failed:\n{r.stderr[-4000:]}")
         return o
@@ -107,10 +119,11 @@ def build(out: str, kind: str) -> str:
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
         objs = list(ex.map(compile_one, files))
     target = os.path.join(out, name)
-    if kind in ("check", "selftest"):
-        cmd = [cxx, *flags[2:], os.path.join(HERE, kind + ".cpp"), *objs, "-o", target]
+    if kind in ("check", "selftest", "check_tsan", "selftest_tsan"):
+        main = {"check_tsan": "check.cpp", "selftest_tsan": "selftest.cpp"}.get(kind, kind + ".cpp")
+        cmd = [cxx, *flags[2:], os.path.join(HERE, main), *objs, "-o", target]
     else:
-        cmd = [cxx, "-shared", *flags[2:], *objs, "-o", target]
+        cmd = [cxx, "-shared", *flags[2:], *(["-shared-libsan"] if sanitize else []), *objs, "-o", target]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link of {target} failed:\n{r.stderr[-4000:]}")

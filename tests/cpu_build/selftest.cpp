@@ -6,7 +6,10 @@
 // "range":     loads past num_records read zero and stores there are dropped;
 // "barriers":  one wave passes one barrier fewer than the others (reported);
 // "diverge":   half a wave reaches a cross-lane operation the other half
-//              skips (reported as a deadlock: the process aborts).
+//              skips (reported as a deadlock: the process aborts);
+// "race":      two waves write and read one __shared__ word with no barrier
+//              between them, then with one (built with ThreadSanitizer: the
+//              first must be reported, the second not).
 // Each planted case is a kernel written for this check alone; none is built
 // for a GPU.
 #include <cmath>
@@ -139,6 +142,17 @@ int main(int argc, char** argv) {
     });
     return 0;  // not reached: the scheduler reports the deadlock and aborts
   }
-  fprintf(stderr, "usage: selftest mfma|wrap|range|barriers|diverge\n");
+  if (!strcmp(what, "race") || !strcmp(what, "norace")) {
+    const bool fenced = !strcmp(what, "norace");
+    simt::launch(dim3(2), dim3(128), [&]() {
+      static int word;  // one word of LDS
+      if (threadIdx.x == 0) word = 1;
+      if (fenced) __syncthreads();
+      if (threadIdx.x == 64) printf("%s: wave 1 reads %d\n", fenced ? "norace" : "race", word);
+      if (!fenced) __syncthreads();
+    });
+    return 0;
+  }
+  fprintf(stderr, "usage: selftest mfma|wrap|range|barriers|diverge|race|norace\n");
   return 2;
 }

@@ -14,6 +14,18 @@
 #include <sanitizer/common_interface_defs.h>
 #endif
 #endif
+// SIMT_TSAN: the kernels are built with ThreadSanitizer and this file, which
+// is not instrumented, annotates the schedule: one TSan fiber per wave (its
+// lanes are one program order, as in lockstep), switches without implied
+// synchronisation, and a release/acquire pair per barrier generation of a
+// workgroup.  Accesses of two waves of a workgroup that no barrier orders are
+// then reported as data races.  Workgroups are ordered one after another: the
+// __shared__ arrays here are one static object that every workgroup reuses,
+// where the hardware gives each its own LDS.
+#ifdef SIMT_TSAN
+#include <sanitizer/tsan_interface.h>
+#include <deque>
+#endif
 
 hipError_t hipGetLastError() { return hipSuccess; }
 hipError_t hipGetDevice(int* d) {
@@ -108,11 +120,20 @@ static void* sched_fake = nullptr;
 static const void* sched_bottom = nullptr;
 static size_t sched_size = 0;
 #endif
+#ifdef SIMT_TSAN
+static void* tsan_host = nullptr;
+static void* tsan_wave[16];
+static std::deque<char>* tsan_bars = nullptr;  // one sync object per barrier generation
+static char tsan_order;  // orders workgroups and launches one after another
+#endif
 
 const Ids& ids() { return cur->ids; }
 int lane_id() { return (int)(cur->ids.tid.x & 63); }
 
 static void to_scheduler() {
+#ifdef SIMT_TSAN
+  __tsan_switch_to_fiber(tsan_host, __tsan_switch_to_fiber_no_sync);
+#endif
 #ifdef SIMT_ASAN
   __sanitizer_start_switch_fiber(&cur->fake, sched_bottom, sched_size);
 #endif
@@ -126,7 +147,14 @@ static void trampoline() {
 #ifdef SIMT_ASAN
   __sanitizer_finish_switch_fiber(nullptr, &sched_bottom, &sched_size);
 #endif
+#ifdef SIMT_TSAN
+  __tsan_acquire(&tsan_order);
+#endif
   body_fn();
+#ifdef SIMT_TSAN
+  __tsan_release(&tsan_order);
+  __tsan_switch_to_fiber(tsan_host, __tsan_switch_to_fiber_no_sync);
+#endif
   cur->st = DONE;
 #ifdef SIMT_ASAN
   __sanitizer_start_switch_fiber(nullptr, sched_bottom, sched_size);
@@ -138,6 +166,9 @@ static void trampoline() {
 
 static void resume(Fiber& f) {
   cur = &f;
+#ifdef SIMT_TSAN
+  __tsan_switch_to_fiber(tsan_wave[f.ids.tid.x / 64], __tsan_switch_to_fiber_no_sync);
+#endif
 #ifdef SIMT_ASAN
   __sanitizer_start_switch_fiber(&sched_fake, f.stack, STACK);
 #endif
@@ -164,7 +195,15 @@ void barrier(const char* site) {
   Fiber* f = cur;
   f->st = BARRIER;
   f->site = site;
+#ifdef SIMT_TSAN
+  while ((long)tsan_bars->size() <= f->barriers) tsan_bars->push_back(0);
+  char* sync = &(*tsan_bars)[f->barriers];
+  __tsan_release(sync);
+#endif
   to_scheduler();
+#ifdef SIMT_TSAN
+  __tsan_acquire(sync);
+#endif
   ++f->barriers;
 }
 
@@ -258,9 +297,19 @@ void launch(dim3 grid, dim3 block, std::function<void()> body) {
     }
   }
   body_fn = std::move(body);
+#ifdef SIMT_TSAN
+  tsan_host = __tsan_get_current_fiber();
+  __tsan_release(&tsan_order);
+#endif
   for (unsigned bz = 0; bz < grid.z; ++bz)
     for (unsigned by = 0; by < grid.y; ++by)
       for (unsigned bx = 0; bx < grid.x; ++bx) {
+#ifdef SIMT_TSAN
+        // each workgroup: its own wave contexts and barrier sync objects (the
+        // fibers' stacks are reused: workgroups are ordered one after another)
+        for (int w = 0; w < (nthreads + 63) / 64; ++w) tsan_wave[w] = __tsan_create_fiber(0);
+        tsan_bars = new std::deque<char>();
+#endif
         for (int t = 0; t < nthreads; ++t) {
           Fiber& f = F[t];
           f.ids = Ids{Dim{(unsigned)t, 0, 0}, Dim{bx, by, bz}, Dim{grid.x, grid.y, grid.z}, Dim{block.x, 1, 1}};
@@ -276,7 +325,14 @@ void launch(dim3 grid, dim3 block, std::function<void()> body) {
           f.sp = sp;
         }
         run_workgroup();
+#ifdef SIMT_TSAN
+        for (int w = 0; w < (nthreads + 63) / 64; ++w) __tsan_destroy_fiber(tsan_wave[w]);
+        delete tsan_bars;
+#endif
       }
+#ifdef SIMT_TSAN
+  __tsan_acquire(&tsan_order);
+#endif
 }
 
 // ---------------------------------------------------------------------------

@@ -379,3 +379,45 @@ def test_emulator_reports_planted_faults(selftest_exe):
     assert r.returncode == 0 and "barriers" in r.stderr, r.stdout + r.stderr
     r = _selftest(selftest_exe, "diverge")
     assert r.returncode != 0 and "deadlock" in r.stderr, r.stdout + r.stderr
+
+
+# ---------------------------------------------------------------------------
+# data races between the waves of a workgroup (ThreadSanitizer over the
+# emulator's schedule: one fiber context per wave, synchronised only by the
+# workgroup's barriers)
+# ---------------------------------------------------------------------------
+def _tsan_run(exe, args):
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=0:exitcode=66")
+    return subprocess.run([exe, *map(str, args)], capture_output=True, text=True, timeout=900, env=env)
+
+
+def test_race_detector_reports_planted_race():
+    exe = CB.build(S.OUT, "selftest_tsan")
+    r = _tsan_run(exe, ["race"])
+    assert r.returncode == 66 and "data race" in r.stderr, r.stdout + r.stderr[-3000:]
+    r = _tsan_run(exe, ["norace"])
+    assert r.returncode == 0 and "ThreadSanitizer" not in r.stderr, r.stdout + r.stderr[-3000:]
+
+
+TSAN_SHAPES = [(2, 6, 6, 11, 128, 12, "bf16"), (3, 7, 5, 9, 64, 37, "bf16"), (2, 6, 6, 11, 16, 12, "bf16"),
+               (2, 6, 6, 11, 128, 12, "f32")]
+
+
+@pytest.mark.parametrize("shape", TSAN_SHAPES, ids=["x".join(map(str, s)) for s in TSAN_SHAPES])
+def test_forward_has_no_race_between_waves(shape):
+    exe = CB.build(S.OUT, "check_tsan")
+    r = _tsan_run(exe, shape)
+    assert r.returncode == 0 and "ThreadSanitizer" not in r.stderr, r.stdout + r.stderr[-4000:]
+
+
+def test_every_entry_point_has_no_race_between_waves():
+    """tests/cpu_build/san_cases.py --tsan on the ThreadSanitizer build: every
+    entry point, no data race between the waves of a workgroup."""
+    import sys
+    path = CB.build(S.OUT, "lib_tsan")
+    env = dict(os.environ, LD_PRELOAD=CB.sanitizer_runtime("tsan"), TSAN_OPTIONS="halt_on_error=0:exitcode=66")
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(CB.__file__), "san_cases.py"), path, "--tsan"],
+                       capture_output=True, text=True, timeout=1800, env=env)
+    out = r.stdout + r.stderr
+    assert r.returncode == 0 and "all entry points ran" in r.stdout, out[-6000:]
+    assert "ThreadSanitizer" not in out, out[-6000:]
