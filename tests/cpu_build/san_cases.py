@@ -1,15 +1,16 @@
 """Every C ABI entry point of the sanitized CPU build (libvdn_vda_sim_san.so)
 on small cases, in a process that preloads the sanitizer runtime:
 
-    LD_PRELOAD=<libclang_rt.asan> python tests/cpu_build/san_cases.py <library> [--full] [--tsan]
+    LD_PRELOAD=<libclang_rt.asan> python tests/cpu_build/san_cases.py <library> [--full] [--tsan] [--shard=i/n]
 
 (tests/test_cpu_build.py starts it so, with one case per kernel variant and
 mode; --full runs every forward edge case, every backward case and every
-adjacent-map case, about eight minutes; --tsan, for the ThreadSanitizer
+adjacent-map case, about eight minutes in one process; --tsan, for the ThreadSanitizer
 build, leaves out the arbitrary bit patterns: they send the statistics kernel
 down its range recovery, where every consumer wave whose sums are not finite
 writes the same 1 to the shared flag before the barrier that orders its
-readers, a race only in form).  Any AddressSanitizer or
+readers, a race only in form; --shard=i/n runs every n-th case from the
+i-th, so that n processes share the sweep).  Any AddressSanitizer or
 UndefinedBehaviorSanitizer report ends the process with a nonzero status; the
 results themselves are compared with the oracle by the unsanitized tests, so
 here they are only checked to be finite.
@@ -17,6 +18,7 @@ here they are only checked to be finite.
 
 import os
 import sys
+import time
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path[:0] = [os.path.dirname(HERE), os.path.dirname(os.path.dirname(HERE))]
@@ -43,74 +45,122 @@ BACKWARD_QUICK = ("bwd_64_ragged", "bwd_32_bridge", "bwd_16_chunk3", "bwd_64_no_
 ADJACENT_QUICK = ("adj_small", "adj_d16", "adj_tiny")
 
 
-def main(path, full, tsan=False):
-    L = S.load(path)
-    done = []
+def cases(full, tsan=False):
+    """The sweep as a list of (label, run(L)) pairs, in a fixed order."""
+    out = []
+
+    def forward(name, mode):
+        def run(L):
+            w = P.EDGE[name]
+            x = synth.make_inputs(w)
+            if mode == "bridge":
+                o, _, _ = S.run_forward(L, x, w, epilogue=False, bridge=True)
+            else:
+                o, _, _ = S.run_forward(L, x, w, epilogue=True, scan=mode,
+                                        rms_weight=np.linspace(0.5, 1.5, w.d) if w.d == 128 else None)
+            finite(o)
+        return run
+
     for name in FORWARD if full else FORWARD_QUICK:
-        w = P.EDGE[name]
-        x = synth.make_inputs(w)
-        for scan in ("frames", "chunks"):
-            out, _, _ = S.run_forward(L, x, w, epilogue=True, scan=scan,
-                                      rms_weight=np.linspace(0.5, 1.5, w.d) if w.d == 128 else None)
-            finite(out)
-        out, _, _ = S.run_forward(L, x, w, epilogue=False, bridge=True)
-        finite(out)
-        done.append(f"forward {name}")
-    w = P.EDGE["ragged_bf16_128" if full else "d32_bf16"]
-    finite(S.run_forward_noalloc(L, synth.make_inputs(w), w))
-    done.append("forward_noalloc")
+        for mode in ("frames", "chunks", "bridge"):
+            out.append((f"forward {name} {mode}", forward(name, mode)))
+
+    def noalloc(L):
+        w = P.EDGE["ragged_bf16_128" if full else "d32_bf16"]
+        finite(S.run_forward_noalloc(L, synth.make_inputs(w), w))
+
+    out.append(("forward_noalloc", noalloc))
+
     # arbitrary bit patterns in every input (negative, infinite and NaN beta and
     # alpha included): the results are meaningless, but no access may leave its
     # buffer and no operation may be undefined, whatever the data
-    rng = np.random.default_rng(99)
-    for name in () if tsan else ("ragged_bf16_128", "d32_bf16", "ragged_f32_128") if full else ("ragged_bf16_128",
-                                                                                                 "d32_f32"):
-        w = P.EDGE[name]
-        x = synth.make_inputs(w)
-        for k, a in x.items():
-            if a.dtype == np.uint16:
-                x[k] = rng.integers(0, 1 << 16, a.shape, dtype=np.uint16)
-            elif a.dtype == np.float32:
-                x[k] = rng.integers(0, 1 << 32, a.shape, dtype=np.uint32).view(np.float32)
-        for scan in ("frames", "chunks"):
-            S.run_forward(L, x, w, epilogue=True, scan=scan)
-        S.run_forward(L, x, w, epilogue=False, bridge=True)
-        S.run_forward_noalloc(L, x, w)
-        done.append(f"forward on arbitrary bit patterns {name}")
+    def bit_patterns(name, seed, mode):
+        def run(L):
+            rng = np.random.default_rng(seed)
+            w = P.EDGE[name]
+            x = synth.make_inputs(w)
+            for k, a in x.items():
+                if a.dtype == np.uint16:
+                    x[k] = rng.integers(0, 1 << 16, a.shape, dtype=np.uint16)
+                elif a.dtype == np.float32:
+                    x[k] = rng.integers(0, 1 << 32, a.shape, dtype=np.uint32).view(np.float32)
+            if mode == "noalloc":
+                S.run_forward_noalloc(L, x, w)
+            elif mode == "bridge":
+                S.run_forward(L, x, w, epilogue=False, bridge=True)
+            else:
+                S.run_forward(L, x, w, epilogue=True, scan=mode)
+        return run
+
+    names = () if tsan else ("ragged_bf16_128", "d32_bf16", "ragged_f32_128") if full else ("ragged_bf16_128",
+                                                                                            "d32_f32")
+    for i, name in enumerate(names):
+        for mode in ("frames", "chunks", "bridge", "noalloc"):
+            out.append((f"forward on arbitrary bit patterns {name} {mode}", bit_patterns(name, 99 + i, mode)))
+
+    def prepare(name, kw):
+        def run(L):
+            w = synth.WORKLOADS["long_prep_bf16"].scaled(name=name, **kw)
+            x = synth.make_inputs(w)
+            qh, kh, vh = S.run_prepare(L, x, w)
+            finite(qh, kh, vh)
+            _, kf, vf = S.run_prepare(L, x, w, query_l2=True)
+            o, _, _ = S.run_forward(L, x, w, epilogue=True, query_l2=True, inputs={"k": kf, "v": vf})
+            finite(o)
+        return run
+
     for name, kw in (("prep_small_bf16", dict(H=2, T=5, grid_h=6, grid_w=10, L=8)),
                      ("prep_small_f32", dict(H=2, T=5, grid_h=6, grid_w=10, L=8, dtype="f32")),
                      ("prep_T1_ragged", P.PREP_EDGE["prep_T1_ragged"]),
                      ("prep_d64", dict(H=2, T=6, grid_h=5, grid_w=7, L=4, d=64))):
-        w = synth.WORKLOADS["long_prep_bf16"].scaled(name=name, **kw)
-        x = synth.make_inputs(w)
-        qh, kh, vh = S.run_prepare(L, x, w)
-        finite(qh, kh, vh)
-        _, kf, vf = S.run_prepare(L, x, w, query_l2=True)
-        out, _, _ = S.run_forward(L, x, w, epilogue=True, query_l2=True, inputs={"k": kf, "v": vf})
-        finite(out)
-        done.append(f"prepare + fused query {name}")
+        out.append((f"prepare + fused query {name}", prepare(name, kw)))
+
+    def backward(name):
+        def run(L):
+            case = GB.CASES[name]
+            w, epi = case["w"], case.get("epilogue", True)
+            bridge, ql2 = case.get("bridge", False), case.get("query_l2", False)
+            x = synth.make_inputs(w)
+            if ql2:
+                GB._raw_queries(x, w)
+            rw = np.linspace(0.5, 1.5, w.d) if case.get("gain") else None
+            _, fws, _ = S.run_forward(L, x, w, epilogue=epi, rms_weight=rw, bridge=bridge, query_l2=ql2)
+            got, _, _ = S.run_backward(L, x, w, GB._dy(w), fws, epilogue=epi, rms_weight=rw, bridge=bridge,
+                                       query_l2=ql2)
+            finite(*(v for v in got.values()))
+        return run
+
     for name in GB.CASES if full else BACKWARD_QUICK:
-        case = GB.CASES[name]
-        w, epi = case["w"], case.get("epilogue", True)
-        bridge, ql2 = case.get("bridge", False), case.get("query_l2", False)
-        x = synth.make_inputs(w)
-        if ql2:
-            GB._raw_queries(x, w)
-        rw = np.linspace(0.5, 1.5, w.d) if case.get("gain") else None
-        _, fws, _ = S.run_forward(L, x, w, epilogue=epi, rms_weight=rw, bridge=bridge, query_l2=ql2)
-        got, _, _ = S.run_backward(L, x, w, GB._dy(w), fws, epilogue=epi, rms_weight=rw, bridge=bridge,
-                                   query_l2=ql2)
-        finite(*(v for v in got.values()))
-        done.append(f"backward {name}")
+        out.append((f"backward {name}", backward(name)))
+
+    def adjacent(name):
+        def run(L):
+            w, dm = GA.CASES[name]
+            p = synth.make_adjacent_inputs(w, dm)
+            finite(*S.run_gates(L, p, w, dm))
+            for mode in ("y_in", "in_place", "no_y_in"):
+                finite(S.run_out_proj(L, p, w, mode))
+        return run
+
     for name in GA.CASES if full else ADJACENT_QUICK:
-        w, dm = GA.CASES[name]
-        p = synth.make_adjacent_inputs(w, dm)
-        finite(*S.run_gates(L, p, w, dm))
-        for mode in ("y_in", "in_place", "no_y_in"):
-            finite(S.run_out_proj(L, p, w, mode))
-        done.append(f"gates + out_proj {name}")
-    print(f"all entry points ran: {len(done)} cases")
+        out.append((f"gates + out_proj {name}", adjacent(name)))
+    return out
+
+
+def main(path, full, tsan=False, shard=0, shards=1):
+    L = S.load(path)
+    mine = cases(full, tsan)[shard::shards]
+    for label, run in mine:
+        t0 = time.time()
+        run(L)
+        print(f"ran {label} ({time.time() - t0:.1f} s)", flush=True)
+    print(f"all entry points ran: {len(mine)} cases")
 
 
 if __name__ == "__main__":
-    main(sys.argv[1], "--full" in sys.argv[2:], "--tsan" in sys.argv[2:])
+    args = sys.argv[2:]
+    shard, shards = 0, 1
+    for a in args:
+        if a.startswith("--shard="):
+            shard, shards = (int(v) for v in a[len("--shard="):].split("/"))
+    main(sys.argv[1], "--full" in args, "--tsan" in args, shard, shards)

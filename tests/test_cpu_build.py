@@ -281,21 +281,37 @@ def test_out_proj_matches_oracle(lib, name, mode):
     assert G.slice_rel_err(GA._slices(S.to_f64(y)), GA._slices(ref)) <= 2e-2
 
 
+def _sweep(path, args, env, shards=max(1, min(6, os.cpu_count() or 1))):
+    """tests/cpu_build/san_cases.py on the library at ``path``, its cases split
+    over ``shards`` processes run at once; (exit status, stdout + stderr) of
+    each."""
+    import sys
+    script = os.path.join(os.path.dirname(CB.__file__), "san_cases.py")
+    procs = [subprocess.Popen([sys.executable, script, path, *args, f"--shard={i}/{shards}"], stdout=subprocess.PIPE,
+                              stderr=subprocess.STDOUT, text=True, env=env) for i in range(shards)]
+    results = []
+    for p in procs:
+        try:
+            out, _ = p.communicate(timeout=1800)
+        except subprocess.TimeoutExpired:
+            p.kill()
+            out, _ = p.communicate()
+        results.append((p.returncode, out))
+    return results
+
+
 def test_every_entry_point_under_sanitizers():
     """tests/cpu_build/san_cases.py on the sanitized library: every entry point
     (forward in both scans, with the bridge and the fused query norm, the
     no-allocation forward, prepare, the three backward stages, the gates and
     the output projection) with AddressSanitizer and UndefinedBehaviorSanitizer."""
-    import sys
     path = CB.build(S.OUT, "lib_san")
     env = dict(os.environ, LD_PRELOAD=CB.sanitizer_runtime(),
                ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:detect_stack_use_after_return=0",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
-    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(CB.__file__), "san_cases.py"), path],
-                       capture_output=True, text=True, timeout=1800, env=env)
-    out = r.stdout + r.stderr
-    assert r.returncode == 0 and "all entry points ran" in r.stdout, out[-6000:]
-    assert "runtime error" not in out and "Sanitizer" not in out and "[simt]" not in out, out[-6000:]
+    for rc, out in _sweep(path, [], env):
+        assert rc == 0 and "all entry points ran" in out, out[-6000:]
+        assert "runtime error" not in out and "Sanitizer" not in out and "[simt]" not in out, out[-6000:]
 
 
 # ---------------------------------------------------------------------------
@@ -413,11 +429,8 @@ def test_forward_has_no_race_between_waves(shape):
 def test_every_entry_point_has_no_race_between_waves():
     """tests/cpu_build/san_cases.py --tsan on the ThreadSanitizer build: every
     entry point, no data race between the waves of a workgroup."""
-    import sys
     path = CB.build(S.OUT, "lib_tsan")
     env = dict(os.environ, LD_PRELOAD=CB.sanitizer_runtime("tsan"), TSAN_OPTIONS="halt_on_error=0:exitcode=66")
-    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(CB.__file__), "san_cases.py"), path, "--tsan"],
-                       capture_output=True, text=True, timeout=1800, env=env)
-    out = r.stdout + r.stderr
-    assert r.returncode == 0 and "all entry points ran" in r.stdout, out[-6000:]
-    assert "ThreadSanitizer" not in out, out[-6000:]
+    for rc, out in _sweep(path, ["--tsan"], env):
+        assert rc == 0 and "all entry points ran" in out, out[-6000:]
+        assert "ThreadSanitizer" not in out, out[-6000:]
