@@ -2,7 +2,11 @@
 
 Argument marshalling only: torch tensors supply device pointers and the
 current HIP stream; every step of the computation runs in the HIP kernels of
-libvdn_vda.so.  A missing library is an error: there is no fallback.
+libvdn_vda.so.  A missing library is an error: there is no fallback.  Since the
+library sizes every buffer from the descriptor, each wrapper first checks that
+every tensor holds exactly the elements and element type the descriptor
+implies, on the caller's device and contiguous, and that the grid tiles the
+frame's tokens.
 """
 
 from __future__ import annotations
@@ -168,6 +172,53 @@ def _check(x, name, dev):
         raise ValueError(f"{name} must be contiguous")
 
 
+# The library addresses every tensor from the descriptor alone, so each one must
+# hold exactly the elements and the element type the descriptor implies: a
+# smaller tensor would be read or written past its end.
+def _expect(x, name, numel, dtype):
+    if x is None:
+        return
+    if x.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {x.dtype}")
+    if x.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, not {x.numel()} (shape {tuple(x.shape)})")
+
+
+def _expect_grid(grid, U):
+    if len(grid) != 2 or grid[0] < 1 or grid[1] < 1 or grid[0] * grid[1] != U:
+        raise ValueError(f"grid {tuple(grid)} does not tile the {U} tokens of a frame")
+
+
+def _expect_bytes(x, name):
+    import torch
+    if x is not None and x.dtype != torch.uint8:
+        raise TypeError(f"{name} must be a uint8 tensor (its element count is passed as its size in bytes)")
+
+
+def _expect_forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, out, grid, epilogue):
+    """Shapes and types of the forward pass's tensors, those of [B, T, U, H, d]
+    taken from q; returns the text length."""
+    import torch
+    B, T, U, H, d = q.shape
+    _dtype_of(q)
+    _expect_grid(grid, U)
+    L = 0 if k_text is None else k_text.shape[1]
+    for name, x in (("k", k), ("v", v), ("gate", gate if epilogue else None), ("out", out)):
+        _expect(x, name, q.numel(), q.dtype)
+    if k is None or v is None or alpha is None or beta is None:
+        raise ValueError("k, v, alpha and beta are required")
+    _expect(alpha, "alpha", B * T * H * d, torch.float32)
+    _expect(beta, "beta", B * T * U * H, q.dtype)
+    if L:
+        _expect(k_text, "k_text", B * L * H * d, q.dtype)
+        _expect(v_text, "v_text", B * L * H * d, q.dtype)
+        _expect(beta_text, "beta_text", B * L * H, q.dtype)
+        if v_text is None or beta_text is None:
+            raise ValueError("v_text and beta_text are required with k_text")
+    _expect(rms_weight, "rms_weight", d, torch.float32)
+    return L
+
+
 def forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weight=None, *,
             grid, chunk=5, epilogue=True, rms_eps=1e-6, out=None, workspace=None, bridge=False,
             query_l2=False, l2_eps=1e-6, scan=None, events=None):
@@ -183,7 +234,8 @@ def forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, rms_weig
     """
     import torch
     B, T, U, H, d = q.shape
-    L = 0 if k_text is None else k_text.shape[1]
+    L = _expect_forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, out, grid, epilogue)
+    _expect_bytes(workspace, "workspace")
     dt = _dtype_of(q)
     dev = q.device
     for name, x in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta),
@@ -222,7 +274,7 @@ def forward_noalloc(q, k, v, alpha, beta, k_text, v_text, beta_text, gate=None, 
     array as its workspace (no workspace argument); returns ``out``."""
     import torch
     B, T, U, H, d = q.shape
-    L = 0 if k_text is None else k_text.shape[1]
+    L = _expect_forward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, out, grid, epilogue)
     dev = q.device
     for name, x in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta),
                     ("k_text", k_text), ("v_text", v_text), ("beta_text", beta_text),
@@ -250,6 +302,18 @@ def prepare(q, k, v, wk_s, wk_t, wv_s, wv_t, *, grid, l2_eps=1e-6, n_text=0, chu
     """
     import torch
     B, T, U, H, d = k.shape
+    _dtype_of(k)
+    _expect_grid(grid, U)
+    _expect(v, "v", k.numel(), k.dtype)
+    if query_l2:
+        q = None
+    elif q is None:
+        raise ValueError("q is required unless query_l2 is set")
+    _expect(q, "q", k.numel(), k.dtype)
+    for name, x, taps in (("wk_s", wk_s, 25), ("wk_t", wk_t, 5), ("wv_s", wv_s, 25), ("wv_t", wv_t, 5)):
+        if x is None:
+            raise ValueError(f"{name} is required")
+        _expect(x, name, H * d * taps, torch.float32)
     dev = k.device
     for name, x in (("q", q), ("k", k), ("v", v), ("wk_s", wk_s), ("wk_t", wk_t),
                     ("wv_s", wv_s), ("wv_t", wv_t)):
@@ -286,6 +350,15 @@ def backward_readout(q, gate, rms_weight, alpha, dy, fwd_workspace, *, grid, n_t
     same descriptor and inputs."""
     import torch
     B, T, U, H, d = q.shape
+    _dtype_of(q)
+    _expect_grid(grid, U)
+    for name, x in (("gate", gate if epilogue else None), ("dy", dy), ("dq", dq),
+                    ("dgate", dgate if epilogue else None)):
+        _expect(x, name, q.numel(), q.dtype)
+    _expect(alpha, "alpha", B * T * H * d, torch.float32)
+    _expect(rms_weight, "rms_weight", d, torch.float32)
+    _expect_bytes(fwd_workspace, "fwd_workspace")
+    _expect_bytes(workspace, "workspace")
     dev = q.device
     for name, x in (("q", q), ("gate", gate), ("rms_weight", rms_weight), ("alpha", alpha), ("dy", dy),
                     ("fwd_workspace", fwd_workspace), ("dq", dq), ("dgate", dgate), ("workspace", workspace)):
@@ -314,6 +387,10 @@ def backward_scan(alpha, fwd_workspace, workspace, *, shape, grid, n_text=0, chu
     stage's workspace; returns dalpha [B, T, H, d] float32.  ``shape`` = (B, T, H, d)."""
     import torch
     B, T, H, d = shape
+    _expect(alpha, "alpha", B * T * H * d, torch.float32)
+    _expect(dalpha, "dalpha", B * T * H * d, torch.float32)
+    _expect_bytes(fwd_workspace, "fwd_workspace")
+    _expect_bytes(workspace, "workspace")
     dev = alpha.device
     for name, x in (("alpha", alpha), ("fwd_workspace", fwd_workspace), ("workspace", workspace), ("dalpha", dalpha)):
         _check(x, name, dev)
@@ -336,6 +413,28 @@ def backward_gram(k, v, beta, k_text, v_text, beta_text, workspace, *, grid, chu
     import torch
     B, T, U, H, d = k.shape
     L = 0 if k_text is None else k_text.shape[1]
+    _dtype_of(k)
+    _expect_grid(grid, U)
+    _expect(v, "v", k.numel(), k.dtype)
+    _expect(beta, "beta", B * T * U * H, k.dtype)
+    if L:
+        _expect(k_text, "k_text", B * L * H * d, k.dtype)
+        _expect(v_text, "v_text", B * L * H * d, k.dtype)
+        _expect(beta_text, "beta_text", B * L * H, k.dtype)
+    _expect_bytes(workspace, "workspace")
+    if out is not None:
+        if len(out) != 6:
+            raise ValueError("out must give (dk, dv, dbeta, dk_text, dv_text, dbeta_text)")
+        for name, x, n in (("dk", out[0], k.numel()), ("dv", out[1], k.numel()), ("dbeta", out[2], B * T * U * H)):
+            if x is None:
+                raise ValueError(f"{name} is required")
+            _expect(x, name, n, k.dtype)
+        if L:
+            for name, x, n in (("dk_text", out[3], B * L * H * d), ("dv_text", out[4], B * L * H * d),
+                               ("dbeta_text", out[5], B * L * H)):
+                if x is None:
+                    raise ValueError(f"{name} is required with text tokens")
+                _expect(x, name, n, k.dtype)
     dev = k.device
     if out is None:
         out = (torch.empty_like(k), torch.empty_like(v), torch.empty_like(beta),
@@ -382,6 +481,16 @@ def gates(x, w_gb, w_alpha, *, heads, d, grid, chunk=5, out=None, workspace=None
     float32.  Returns (gate [B, T, U, H, d], beta [B, T, U, H], alpha [B, T, H, d])."""
     import torch
     B, T, U, Dm = x.shape
+    _expect(x, "x", x.numel(), torch.bfloat16)
+    _expect_grid(grid, U)
+    _expect(w_gb, "w_gb", (heads * d + heads) * Dm, torch.bfloat16)
+    _expect(w_alpha, "w_alpha", heads * d * Dm, torch.float32)
+    if out is not None:
+        for name, t, n, dt in (("gate", out[0], B * T * U * heads * d, torch.bfloat16),
+                               ("beta", out[1], B * T * U * heads, torch.bfloat16),
+                               ("alpha", out[2], B * T * heads * d, torch.float32)):
+            _expect(t, name, n, dt)
+    _expect_bytes(workspace, "workspace")
     dev = x.device
     desc = make_desc(B, heads, T, grid[0], grid[1], d, 0, chunk, "bf16", False)
     if out is None:
@@ -407,6 +516,11 @@ def out_proj(o, w_o, y_in=None, *, grid, chunk=5, out=None):
     import torch
     B, T, U, H, d = o.shape
     Dm = w_o.shape[0]
+    _expect(o, "o", o.numel(), torch.bfloat16)
+    _expect_grid(grid, U)
+    _expect(w_o, "w_o", Dm * H * d, torch.bfloat16)
+    _expect(y_in, "y_in", B * T * U * Dm, torch.bfloat16)
+    _expect(out, "out", B * T * U * Dm, torch.bfloat16)
     dev = o.device
     desc = make_desc(B, H, T, grid[0], grid[1], d, 0, chunk, "bf16", False)
     if out is None:

@@ -665,7 +665,10 @@ const char* vdn_vda_status_string(vdn_status s) {
   switch (code) {
     case VDN_OK: return "VDN_OK";
     case VDN_ERR_INVALID_ARG: return "VDN_ERR_INVALID_ARG: bad descriptor, size, NULL pointer or overlapping buffers";
-    case VDN_ERR_UNSUPPORTED: return "VDN_ERR_UNSUPPORTED: head width not implemented (d_k = d_v in {16,32,64,128})";
+    case VDN_ERR_UNSUPPORTED:
+      return "VDN_ERR_UNSUPPORTED: valid request not implemented (head widths other than d_k = d_v in "
+             "{16,32,64,128}; float32 in the backward pass and the adjacent maps; the query norm's backward "
+             "without the epilogue)";
     case VDN_ERR_WORKSPACE: return "VDN_ERR_WORKSPACE: workspace missing or too small";
     case VDN_ERR_ALIGNMENT: return "VDN_ERR_ALIGNMENT: pointer misaligned";
     case VDN_ERR_HIP: return "VDN_ERR_HIP: kernel launch failed";
