@@ -4,6 +4,8 @@ emulated device environment in this folder (simt.h), as
 
 * ``check`` -- the self-checking forward driver (check.cpp), with
   AddressSanitizer and UndefinedBehaviorSanitizer,
+* ``gram_launch`` -- the forward's statistics launch alone (gram_launch.cpp),
+  with both sanitizers, at any shape,
 * ``libvdn_vda_sim.so`` -- the C ABI as a host library, for tests that compare
   the kernels' results with the oracle from Python, or
 * ``libvdn_vda_sim_san.so`` -- the same with both sanitizers, linked against the
@@ -72,7 +74,7 @@ def sanitizer_runtime(name: str = "asan") -> str:
 
 KINDS = {"check": ("check", True), "lib": ("libvdn_vda_sim.so", False), "lib_san": ("libvdn_vda_sim_san.so", True),
          "selftest": ("selftest", True), "check_tsan": ("check_tsan", True), "selftest_tsan": ("selftest_tsan", True),
-         "lib_tsan": ("libvdn_vda_sim_tsan.so", True)}
+         "lib_tsan": ("libvdn_vda_sim_tsan.so", True), "gram_launch": ("gram_launch", True)}
 
 
 def build(out: str, kind: str) -> str:
@@ -80,7 +82,8 @@ def build(out: str, kind: str) -> str:
     "lib", "lib_san", "selftest": the emulator's own checks, selftest.cpp,
     "check_tsan" / "selftest_tsan": check.cpp / selftest.cpp with
     ThreadSanitizer on the kernels and the emulator's schedule annotated for
-    it)."""
+    it, "gram_launch": the forward's statistics launch alone, gram_launch.cpp,
+    with AddressSanitizer and UndefinedBehaviorSanitizer)."""
     cxx = compiler()
     if cxx is None:
         raise RuntimeError("no clang++ for the host build")
@@ -119,7 +122,7 @@ def build(out: str, kind: str) -> str:
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
         objs = list(ex.map(compile_one, files))
     target = os.path.join(out, name)
-    if kind in ("check", "selftest", "check_tsan", "selftest_tsan"):
+    if kind in ("check", "selftest", "check_tsan", "selftest_tsan", "gram_launch"):
         main = {"check_tsan": "check.cpp", "selftest_tsan": "selftest.cpp"}.get(kind, kind + ".cpp")
         cmd = [cxx, *flags[2:], os.path.join(HERE, main), *objs, "-o", target]
     else:

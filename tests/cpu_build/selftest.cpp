@@ -9,7 +9,9 @@
 //              skips (reported as a deadlock: the process aborts);
 // "race":      two waves write and read one __shared__ word with no barrier
 //              between them, then with one (built with ThreadSanitizer: the
-//              first must be reported, the second not).
+//              first must be reported, the second not);
+// "shard":     a launch split three ways runs workgroups 1, 4, 7 of nine in
+//              the shard with index 1, and all nine after the split is undone.
 // Each planted case is a kernel written for this check alone; none is built
 // for a GPU.
 #include <cmath>
@@ -153,6 +155,22 @@ int main(int argc, char** argv) {
     });
     return 0;
   }
-  fprintf(stderr, "usage: selftest mfma|wrap|range|barriers|diverge|race|norace\n");
+  if (!strcmp(what, "shard")) {
+    std::vector<int> ran;
+    simt::set_block_shard(1, 3);
+    simt::launch(dim3(3, 3), dim3(64), [&]() {
+      if (threadIdx.x == 0) ran.push_back((int)(blockIdx.x + 3 * blockIdx.y));
+    });
+    const bool split = ran == std::vector<int>{1, 4, 7} && simt::workgroups_run == 3;
+    ran.clear();
+    simt::set_block_shard(0, 1);
+    simt::launch(dim3(9), dim3(64), [&]() {
+      if (threadIdx.x == 0) ran.push_back((int)blockIdx.x);
+    });
+    const bool whole = ran.size() == 9 && simt::workgroups_run == 12;
+    printf("shard: %s\n", split && whole && simt::errors == 0 ? "ok" : "wrong");
+    return split && whole && simt::errors == 0 ? 0 : 1;
+  }
+  fprintf(stderr, "usage: selftest mfma|wrap|range|barriers|diverge|race|norace|shard\n");
   return 2;
 }

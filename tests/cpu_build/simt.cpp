@@ -78,6 +78,16 @@ simt_switch:
 namespace simt {
 
 int errors = 0;
+long workgroups_run = 0;
+static int shard_index = 0, shard_count = 1;
+void set_block_shard(int index, int count) {
+  if (count < 1 || index < 0 || index >= count) {
+    report("set_block_shard: index %d of %d", index, count);
+    return;
+  }
+  shard_index = index;
+  shard_count = count;
+}
 static int max_reports = 40;
 
 void report(const char* fmt, ...) {
@@ -304,6 +314,8 @@ void launch(dim3 grid, dim3 block, std::function<void()> body) {
   for (unsigned bz = 0; bz < grid.z; ++bz)
     for (unsigned by = 0; by < grid.y; ++by)
       for (unsigned bx = 0; bx < grid.x; ++bx) {
+        if ((bx + (uint64_t)grid.x * (by + (uint64_t)grid.y * bz)) % shard_count != (uint64_t)shard_index) continue;
+        ++workgroups_run;
 #ifdef SIMT_TSAN
         // each workgroup: its own wave contexts and barrier sync objects (the
         // fibers' stacks are reused: workgroups are ordered one after another)

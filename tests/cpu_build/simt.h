@@ -112,6 +112,12 @@ typedef void (*WaveFn)(const unsigned char (*in)[192], unsigned char (*out)[192]
 void wave_op(const char* site, WaveFn fn, const void* ctx, const void* in, size_t nin, void* out, size_t nout);
 void barrier(const char* site);
 void launch(dim3 grid, dim3 block, std::function<void()> body);
+// Split launches over `count` processes: from this call on, a launch runs only
+// the workgroups whose linear index (x fastest) is `index` modulo `count` (the
+// others are skipped whole, so each process gives the results of its share).
+void set_block_shard(int index, int count);
+// Workgroups run by every launch since the process started.
+extern long workgroups_run;
 
 template <class T>
 T wave_call(const char* site, WaveFn fn, const T& v, const void* ctx = nullptr) {

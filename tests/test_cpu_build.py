@@ -70,6 +70,59 @@ def test_forward_under_sanitizers(check_exe, shape):
     assert "runtime error" not in out and "Sanitizer" not in out and "[simt]" not in out, out[-4000:]
 
 
+def _gram_launches(args_list):
+    """gram_launch (the forward's statistics launch alone, sanitized) once per
+    argument list, all at once; asserts that each run is clean and returns
+    their report lines."""
+    exe = CB.build(S.OUT, "gram_launch")
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:detect_stack_use_after_return=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    procs = [subprocess.Popen([exe, *map(str, a)], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True,
+                              env=env) for a in args_list]
+    lines = []
+    for p in procs:
+        try:
+            out, _ = p.communicate(timeout=3600)
+        except subprocess.TimeoutExpired:
+            p.kill()
+            out, _ = p.communicate()
+        assert p.returncode == 0, out[-4000:]
+        assert "runtime error" not in out and "Sanitizer" not in out and "[simt]" not in out, out[-4000:]
+        lines.append(out.strip().splitlines()[-1])
+    return lines
+
+
+def _written(line):
+    return int(line.split("slots written ")[1].split(",")[0]), int(line.split("workgroups ")[1].split(",")[0])
+
+
+def test_statistics_launch_at_the_768p_frame_size():
+    """The statistics launch as the forward makes it, at the 768p clip's frame
+    (48 x 84 tokens, d = 128, 256 text tokens) on two heads and two absorbed
+    frames, with exact-size inputs: on arbitrary bit patterns nothing leaves its
+    buffer and nothing is undefined; on data the statistics agree with float64;
+    every formed slot is written whole, by one workgroup."""
+    shape = (1, 2, 4, 48, 84, 128, 256)
+    for line in _gram_launches([(*shape, "bits"), (*shape, "data")]):
+        assert _written(line) == (2 * 3, 2 * 3), line
+
+
+@pytest.mark.skipif(os.environ.get("VDA_CPU_BUILD_FULL") != "1",
+                    reason="the whole 768p statistics launch, about 8 minutes on 8 cores: set VDA_CPU_BUILD_FULL=1")
+@pytest.mark.parametrize("fill", ["bits", "data"])
+def test_statistics_launch_of_the_768p_clip(fill):
+    """The whole statistics launch of the 768p clip (1 x 24 heads x 60 frames,
+    48 x 84 tokens, d = 128, 256 text tokens: 1392 video and 24 text
+    workgroups), as the forward makes it, on exact-size inputs, its workgroups
+    shared by up to seven processes: every one of the 1416 slots written whole
+    by one workgroup, no sanitizer or emulator report (on arbitrary bit
+    patterns too), sampled statistics within float64 tolerance."""
+    n = max(1, min(7, os.cpu_count() or 1))
+    lines = _gram_launches([(1, 24, 60, 48, 84, 128, 256, fill, i, n) for i in range(n)])
+    written = [_written(line) for line in lines]
+    assert sum(w for w, _ in written) == 24 * 59 and sum(g for _, g in written) == 24 * 59, lines
+
+
 PARITY = {n: P.EDGE[n] for n in ("d32_bf16", "d64_bf16", "d16_bf16", "d32_f32", "ragged_f32_128", "no_text_bf16",
                                   "T1_bf16", "T2_f32", "chunk3_bf16", "batch2_bf16", "U1_bf16_128", "U2_f32_16")}
 PARITY["tiny_f32"] = synth.WORKLOADS["tiny_f32"]
@@ -395,6 +448,13 @@ def test_emulator_reports_planted_faults(selftest_exe):
     assert r.returncode == 0 and "barriers" in r.stderr, r.stdout + r.stderr
     r = _selftest(selftest_exe, "diverge")
     assert r.returncode != 0 and "deadlock" in r.stderr, r.stdout + r.stderr
+
+
+def test_emulator_splits_a_launch(selftest_exe):
+    """A launch split over processes runs, in each, exactly its share of the
+    workgroups (every third from the second), and all of them once undone."""
+    r = _selftest(selftest_exe, "shard")
+    assert r.returncode == 0 and "shard: ok" in r.stdout, r.stdout + r.stderr
 
 
 # ---------------------------------------------------------------------------
