@@ -9,8 +9,9 @@ adjacent-map case, about eight minutes in one process; --tsan, for the ThreadSan
 build, leaves out the arbitrary bit patterns: they send the statistics kernel
 down its range recovery, where every consumer wave whose sums are not finite
 writes the same 1 to the shared flag before the barrier that orders its
-readers, a race only in form; --shard=i/n runs every n-th case from the
-i-th, so that n processes share the sweep).  Any AddressSanitizer or
+readers, a race only in form, and the 768p-frame case, whose races do not
+depend on the frame size; --shard=i/n runs the i-th of n shares of the
+cases, balanced by their rough cost, so that n processes share the sweep).  Any AddressSanitizer or
 UndefinedBehaviorSanitizer report ends the process with a nonzero status; the
 results themselves are compared with the oracle by the unsanitized tests, so
 here they are only checked to be finite.
@@ -133,6 +134,20 @@ def cases(full, tsan=False):
     for name in GB.CASES if full else BACKWARD_QUICK:
         out.append((f"backward {name}", backward(name)))
 
+    # forward and backward at the 768p clip's frame size (48 x 84 tokens,
+    # d = 128, 256 text tokens), where the kernels' 32-bit row offsets are
+    # largest
+    def frame_768p(L):
+        w = synth.WORKLOADS["768p_bf16"].scaled(name="bwd_768p_frame", H=1, T=4, L=256)
+        x = synth.make_inputs(w)
+        o, fws, _ = S.run_forward(L, x, w, epilogue=True)
+        finite(o)
+        got, _, _ = S.run_backward(L, x, w, GB._dy(w), fws, epilogue=True)
+        finite(*(v for v in got.values()))
+
+    if not tsan:
+        out.append(("forward + backward at the 768p frame size", frame_768p))
+
     def adjacent(name):
         def run(L):
             w, dm = GA.CASES[name]
@@ -147,9 +162,34 @@ def cases(full, tsan=False):
     return out
 
 
+# rough cost of the slow cases in seconds under AddressSanitizer (the rest
+# take about one), for sharing the sweep evenly between processes
+COST = (("768p frame", 24.0), ("bit patterns ragged_bf16_128", 10.0), ("no_text_bf16", 6.5),
+        ("U1_bf16_128", 3.8), ("ragged_bf16_128", 3.0), ("bwd_64_ragged", 3.4), ("bwd_B2", 10.0),
+        ("ragged_f32_128", 2.0))
+
+
+def _cost(label):
+    return next((c for key, c in COST if key in label), 1.0)
+
+
+def share(all_cases, shard, shards):
+    """The cases of process ``shard`` of ``shards``: each case, the costliest
+    first, goes to the process with the least work so far (ties to the lowest
+    index); the same split in every process."""
+    load = [0.0] * shards
+    mine = {i: [] for i in range(shards)}
+    order = sorted(range(len(all_cases)), key=lambda i: (-_cost(all_cases[i][0]), i))
+    for i in order:
+        j = min(range(shards), key=lambda k: (load[k], k))
+        load[j] += _cost(all_cases[i][0])
+        mine[j].append(i)
+    return [all_cases[i] for i in sorted(mine[shard])]
+
+
 def main(path, full, tsan=False, shard=0, shards=1):
     L = S.load(path)
-    mine = cases(full, tsan)[shard::shards]
+    mine = share(cases(full, tsan), shard, shards)
     for label, run in mine:
         t0 = time.time()
         run(L)
