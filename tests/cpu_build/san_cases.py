@@ -2,19 +2,21 @@
 on small cases, in a process that preloads the sanitizer runtime:
 
     LD_PRELOAD=<libclang_rt.asan> python tests/cpu_build/san_cases.py <library> [--full] [--tsan] [--shard=i/n]
+    LD_PRELOAD=<libclang_rt.asan> python tests/cpu_build/san_cases.py <library> --heavy
 
 (tests/test_cpu_build.py starts it so, with one case per kernel variant and
 mode; --full runs every forward edge case, every backward case and every
-adjacent-map case, about eight minutes in one process; --tsan, for the ThreadSanitizer
-build, leaves out the arbitrary bit patterns: they send the statistics kernel
-down its range recovery, where every consumer wave whose sums are not finite
-writes the same 1 to the shared flag before the barrier that orders its
-readers, a race only in form, and the 768p-frame case, whose races do not
-depend on the frame size; --shard=i/n runs the i-th of n shares of the
-cases, balanced by their rough cost, so that n processes share the sweep).  Any AddressSanitizer or
-UndefinedBehaviorSanitizer report ends the process with a nonzero status; the
-results themselves are compared with the oracle by the unsanitized tests, so
-here they are only checked to be finite.
+adjacent-map case, about eight minutes in one process; --tsan, for the
+ThreadSanitizer build, leaves out the arbitrary bit patterns: they send the
+statistics kernel down its range recovery, where every consumer wave whose sums
+are not finite writes the same 1 to the shared flag before the barrier that
+orders its readers, a race only in form, and the 768p-frame case, whose races
+do not depend on the frame size; --shard=i/n runs the i-th of n shares of the
+cases, balanced by their rough cost, so that n processes share the sweep;
+--heavy runs only the heavy cases instead, all 24 heads of the 768p clip). Any
+AddressSanitizer or UndefinedBehaviorSanitizer report ends the process with a
+nonzero status; the results themselves are compared with the oracle by the
+unsanitized tests, so here they are only checked to be finite.
 """
 
 import os
@@ -187,9 +189,25 @@ def share(all_cases, shard, shards):
     return [all_cases[i] for i in sorted(mine[shard])]
 
 
-def main(path, full, tsan=False, shard=0, shards=1):
+def heavy_cases():
+    """Forward and backward with all 24 heads of the 768p clip at its frame size
+    (48 x 84 tokens, d = 128, 256 text tokens), four frames: every per-frame
+    32-bit offset and row stride of the full clip (frame bases are 64-bit, so
+    the frame count changes none of them).  About 13 minutes."""
+    def run(L):
+        w = synth.WORKLOADS["768p_bf16"].scaled(name="768p_frames4", T=4)
+        x = synth.make_inputs(w)
+        for scan in ("frames", "chunks"):
+            o, fws, _ = S.run_forward(L, x, w, epilogue=True, scan=scan)
+            finite(o)
+        got, _, _ = S.run_backward(L, x, w, GB._dy(w), fws, epilogue=True)
+        finite(*(v for v in got.values()))
+    return [("forward + backward, 24 heads at the 768p frame size", run)]
+
+
+def main(path, full, tsan=False, shard=0, shards=1, heavy=False):
     L = S.load(path)
-    mine = share(cases(full, tsan), shard, shards)
+    mine = heavy_cases() if heavy else share(cases(full, tsan), shard, shards)
     for label, run in mine:
         t0 = time.time()
         run(L)
@@ -203,4 +221,4 @@ if __name__ == "__main__":
     for a in args:
         if a.startswith("--shard="):
             shard, shards = (int(v) for v in a[len("--shard="):].split("/"))
-    main(sys.argv[1], "--full" in args, "--tsan" in args, shard, shards)
+    main(sys.argv[1], "--full" in args, "--tsan" in args, shard, shards, "--heavy" in args)

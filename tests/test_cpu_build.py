@@ -8,13 +8,23 @@ rendezvous points, buffer descriptors with their range checks).
   T = 1 and 2); A_t, B_t and (I + A_t)^{-1} against a float64 reference, and no
   out-of-range access, undefined behaviour, divergent cross-lane operation or
   unequal barrier count.
+* The forward's statistics launch alone (gram_launch.cpp) at the 768p frame
+  size on arbitrary bit patterns and on data; the whole 768p launch on request.
 * Through the C ABI from Python (libvdn_vda_sim.so): outputs and every
   intermediate against the oracle with the tolerances of the GPU parity tests,
-  both scans, the decay bridge, the prep kernels and the fused query norm.
+  both scans, the decay bridge, the prep kernels, the fused query norm, the
+  backward stages, the adjacent maps and seeded random shapes.
+* Every entry point of the sanitized library (tests/cpu_build/san_cases.py,
+  shared between processes), arbitrary bit patterns included; all 24 heads of
+  the 768p clip at its frame size on request.
+* ThreadSanitizer over the emulator's schedule: no data race between the
+  waves of a workgroup in any entry point.
+* The emulator's own checks (selftest.cpp).
 
 These run the kernels' code, not a model of it, but not the gfx950 binary:
 they check indexing, bounds, synchronisation counts and arithmetic, not the
-compiler's output or the hardware.  Parity proper is the GPU suite's.
+compiler's output or the hardware.  Parity proper is the GPU suite's.  Tests
+marked as needing VDA_CPU_BUILD_FULL=1 take five to fifteen minutes each.
 """
 
 import os
@@ -365,6 +375,25 @@ def test_every_entry_point_under_sanitizers():
     for rc, out in _sweep(path, [], env):
         assert rc == 0 and "all entry points ran" in out, out[-6000:]
         assert "runtime error" not in out and "Sanitizer" not in out and "[simt]" not in out, out[-6000:]
+
+
+@pytest.mark.skipif(os.environ.get("VDA_CPU_BUILD_FULL") != "1",
+                    reason="all 24 heads of the 768p clip through the sanitized build, about 13 minutes: "
+                           "set VDA_CPU_BUILD_FULL=1")
+def test_every_768p_head_under_sanitizers():
+    """tests/cpu_build/san_cases.py --heavy: the forward (both scans) and the
+    backward with all 24 heads of the 768p clip at its frame size, under
+    AddressSanitizer and UndefinedBehaviorSanitizer."""
+    import sys
+    path = CB.build(S.OUT, "lib_san")
+    env = dict(os.environ, LD_PRELOAD=CB.sanitizer_runtime(),
+               ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:detect_stack_use_after_return=0",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(CB.__file__), "san_cases.py"), path, "--heavy"],
+                       capture_output=True, text=True, timeout=3600, env=env)
+    out = r.stdout + r.stderr
+    assert r.returncode == 0 and "all entry points ran: 1 cases" in r.stdout, out[-6000:]
+    assert "runtime error" not in out and "Sanitizer" not in out and "[simt]" not in out, out[-6000:]
 
 
 # ---------------------------------------------------------------------------
