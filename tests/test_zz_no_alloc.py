@@ -7,7 +7,6 @@ smaller problem (so the array holds the first call's intermediates when the
 second starts), each with and without the epilogue.
 """
 
-import numpy as np
 import pytest
 
 from frame_wise_delta_02_amd import binding as bd
