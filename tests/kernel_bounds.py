@@ -14,6 +14,10 @@ Two kinds of access are checked:
   kernel computes must not wrap (a wrapped offset could land back inside the
   range); accesses past num_records read zero or are dropped by the hardware.
 
+Covered: the forward pass and the prep (``model_forward``) and the three
+backward stages (``model_backward``, every part of the backward workspace as a
+buffer of its own); the adjacent maps' GEMMs are not modelled.
+
 The model has no knowledge of the kernels beyond what is written here: a kernel
 change that moves an address must be mirrored in its model, and the test then
 checks the new arithmetic for every shape the GPU tests and the benchmark run.
@@ -126,16 +130,21 @@ def _grid(*dims):
 # ---------------------------------------------------------------------------
 
 
-def model_gram(p: Prob, r: Report):
+def model_gram(p: Prob, r: Report, S=None, parts=None, out="stats", t_slots=None):
     """gram_bf16<D> / gram_f32<D>: two parts in one launch -- frames 1..T-2 of
-    K, V, beta, then the text frame (slot T)."""
-    S = sizes(p)
+    K, V, beta, then the text frame (slot T).  With ``parts`` (bfloat16 only)
+    the backward's PLAIN mode: V^T K of each frame, no beta (``bb`` None), one
+    d x d slot per frame of ``out`` with ``t_slots`` slots per head."""
+    plain = parts is not None
+    S = S or sizes(p)
     D, H = p.D, p.H
-    # with no text tokens the text units' (empty) descriptors sit on the video tensors
-    text = ("k_text", "v_text", "beta_text") if p.L > 0 else ("k", "v", "beta")
-    parts = [("k", "v", "beta", p.T, p.U, 1, max(p.T - 2, 0), 0),
-             (*text, 1, p.L, 0, 1, p.T)]
-    R = 2 * D
+    if not plain:
+        # with no text tokens the text units' (empty) descriptors sit on the video tensors
+        text = ("k_text", "v_text", "beta_text") if p.L > 0 else ("k", "v", "beta")
+        parts = [("k", "v", "beta", p.T, p.U, 1, max(p.T - 2, 0), 0),
+                 (*text, 1, p.L, 0, 1, p.T)]
+        t_slots = p.T + 1
+    R = D if plain else 2 * D
     for kb, vb, bb, T_in, U, t_first, n_frames, slot_off in parts:
         nblk = p.B * n_frames * H
         if nblk == 0:
@@ -166,10 +175,11 @@ def model_gram(p: Prob, r: Report):
             base = (tok02 * H + hh) * D * 2
             for buf in (kb, vb):
                 r.rsrc("gram_bf16", buf, S[buf], base, np.full_like(base, xbytes), max_off, 16)
-            bbase = (tok02 * H + hh) * 2
-            bbytes = (U - 1) * H * 2 + 2 if U > 0 else 0
-            boff = (32 * (wave & 1) + (lane & 31)) * H * 2 + 64 * it_max * H * 2
-            r.rsrc("gram_bf16", bb, S[bb], bbase, np.full_like(bbase, bbytes), boff, 2)
+            if bb is not None:
+                bbase = (tok02 * H + hh) * 2
+                bbytes = (U - 1) * H * 2 + 2 if U > 0 else 0
+                boff = (32 * (wave & 1) + (lane & 31)) * H * 2 + 64 * it_max * H * 2
+                r.rsrc("gram_bf16", bb, S[bb], bbase, np.full_like(bbase, bbytes), boff, 2)
         else:
             TT = 16
             ntile = (U + TT - 1) // TT
@@ -181,9 +191,10 @@ def model_gram(p: Prob, r: Report):
                 r.ptr("gram_f32", vb, S[vb], lo, hi)
                 r.ptr("gram_f32", bb, S[bb], (tok0 * H + h) * 4, ((tok0 + U - 1) * H + h) * 4 + 4)
         # consumer stores: one (2d x d) slot per (b, h, t + slot_off) of [B, H, T+1]
-        slot = (b * H + h) * (p.T + 1) + (t + slot_off)
-        r.ptr("gram", "stats", S["stats"], slot * R * D * 4, (slot + 1) * R * D * 4)
-        if p.bf16:
+        # (PLAIN: one d x d slot of [B, H, T])
+        slot = (b * H + h) * t_slots + (t + slot_off)
+        r.ptr("gram", out, S[out], slot * R * D * 4, (slot + 1) * R * D * 4)
+        if p.bf16 and not plain:
             # the largest element index a consumer writes inside its slot
             MT, NT = R // 16, D // 16
             WM = 4 if MT >= 4 else MT
@@ -366,8 +377,10 @@ def model_gather(p: Prob, r: Report):
     r.ptr("gather", "rstates", S["rstates"], blk * slot_bytes, (blk + 1) * slot_bytes)
 
 
-def model_readout(p: Prob, r: Report):
-    S = sizes(p)
+def model_readout(p: Prob, r: Report, S=None, q="q", out="out", rstates="rstates"):
+    """readout_bf16 / readout_f32; the backward pass runs it on dy with the
+    transposed states (``q``, ``out``, ``rstates`` name those buffers)."""
+    S = S or sizes(p)
     D, H, T, U = p.D, p.H, p.T, p.U
     (blk,) = _grid(p.B * T * H)
     h = blk % H
@@ -375,9 +388,9 @@ def model_readout(p: Prob, r: Report):
     b = blk // (H * T)
     nc = p.nc
     slot = np.where((t == 0) | (t == T - 1), nc, t // p.C)
-    slot_bytes = S["rstates"] // (p.B * H * (nc + 1))
+    slot_bytes = S[rstates] // (p.B * H * (nc + 1))
     rs = (b * H + h) * (nc + 1) + slot
-    r.ptr("readout", "rstates", S["rstates"], rs * slot_bytes, (rs + 1) * slot_bytes)
+    r.ptr("readout", rstates, S[rstates], rs * slot_bytes, (rs + 1) * slot_bytes)
     if p.gamma:
         r.ptr("readout", "rms", S["rms"], 0, D * 4)
     if p.bf16:
@@ -396,12 +409,12 @@ def model_readout(p: Prob, r: Report):
         loff = (lane // CH) * rowbytes + 16 * (lane % CH)
         tile_max = wave + NW * max(steps, 0)
         max_off = tile_max * 32 * rowbytes + loff + (RPI * (NL - 1)) * rowbytes
-        for buf in ["q", "out"] + (["gate"] if p.epilogue else []):
+        for buf in [q, out] + (["gate"] if p.epilogue else []):
             r.rsrc("readout_bf16", buf, S[buf], fbase, np.full_like(fbase, nbytes), max_off, 16)
     else:
         lo = (((b * T + t) * U) * H + h) * D * 4
         hi = (((b * T + t) * U + U - 1) * H + h) * D * 4 + D * 4
-        for buf in ["q", "out"] + (["gate"] if p.epilogue else []):
+        for buf in [q, out] + (["gate"] if p.epilogue else []):
             r.ptr("readout_f32", buf, S[buf], lo, hi)
 
 
@@ -475,4 +488,287 @@ def model_forward(p: Prob, prep: bool = False) -> Report:
     model_scan(p, r)
     model_gather(p, r)
     model_readout(p, r)
+    return r
+
+
+# ---------------------------------------------------------------------------
+# the backward pass: vda_backward.hip, the scan's STATES and ADJOINT modes and
+# the statistics kernel's PLAIN mode, on the buffers vdn_vda_backward_readout,
+# _scan and _gram are given (every part of the backward workspace is checked
+# as a buffer of its own, so an access that runs from one part into the next
+# is caught, which a sanitizer watching the whole allocation would miss)
+# ---------------------------------------------------------------------------
+
+
+def bwd_sizes(p: Prob) -> dict:
+    """Bytes of every buffer the three backward stages touch (bfloat16 inputs)."""
+    S = dict(sizes(p))
+    tok, ttok, heads = p.B * p.T * p.U * p.H, p.B * p.L * p.H, p.B * p.H
+    dd = p.D * p.D * 4
+    x, xt = tok * p.D * 2, ttok * p.D * 2
+    S.update(dy=x, dq=x, dgate=x, dout=x, dk=x, dv=x, dbeta=tok * 2, dk_text=xt, dv_text=xt, dbeta_text=ttok * 2,
+             dalpha=p.B * p.T * p.H * p.D * 4, rstates_t=S["rstates"], dsq=heads * p.T * dd,
+             dF=heads * p.nc * dd, dR=heads * p.nc * dd, dST=heads * dd, lam_final=heads * 2 * dd,
+             states_f=heads * (p.T + 2) * dd, states_r=heads * (p.T + 2) * dd,
+             gmats=heads * (p.T + 1) * 5 * max(p.D, 32) * p.D * 2)
+    for n in ("lam_f", "lam_r", "dA", "dB", "p32", "M", "dPinv", "tmp"):
+        S[n] = heads * (p.T + 1) * dd
+    return S
+
+
+def _readout_frags(D):
+    """16-byte fragments of one plane of a readout state slot."""
+    DP = max(D, 32)
+    return (DP // 32) * (D // 16) * 64
+
+
+def model_pack_states_t(p: Prob, r: Report, S):
+    D, H, T, C, nc = p.D, p.H, p.T, p.C, p.nc
+    NF = _readout_frags(D)
+    dd = D * D * 4
+    (blk,) = _grid(p.B * H * (nc + 1))
+    slot = blk % (nc + 1)
+    bh = blk // (nc + 1)
+    h, b = bh % H, bh // H
+    r.ptr("pack_states_t", "rstates_t", S["rstates_t"], blk * 2 * NF * 16, (blk + 1) * 2 * NF * 16)
+    r.ptr("pack_states_t", "s_text", S["s_text"], bh * dd, (bh + 1) * dd)
+    has_f = (slot < nc) & (slot >= 2)
+    has_r = (slot < nc) & (slot + 2 <= nc - 1)
+    if np.any(has_f):
+        j = bh[has_f] * nc + slot[has_f] - 2
+        r.ptr("pack_states_t", "fwd", S["fwd"], j * dd, (j + 1) * dd)
+    if np.any(has_r):
+        j = bh[has_r] * nc + slot[has_r] + 2
+        r.ptr("pack_states_t", "rev", S["rev"], j * dd, (j + 1) * dd)
+    if p.bridge:
+        frames = []
+        for sl in range(nc):
+            if sl >= 1:
+                frames += list(range(C * (sl - 1), C * sl))
+            if sl + 1 <= nc - 1:
+                frames += list(range(C * (sl + 1), min(C * (sl + 2), T)))
+        if frames:
+            s_ = np.array(frames)
+            lo = ((b[:, None] * T + s_[None, :]) * H + h[:, None]) * D * 4
+            r.ptr("pack_states_t", "alpha", S["alpha"], lo, lo + D * 4)
+
+
+def model_readout_bwd(p: Prob, r: Report, S):
+    """readout_bwd_bf16 (with the epilogue), else the forward readout on dy."""
+    D, H, T, U, C, nc = p.D, p.H, p.T, p.U, p.C, p.nc
+    if not p.epilogue:
+        model_readout(p, r, S, q="dy", out="dq", rstates="rstates_t")
+        return
+    NF = _readout_frags(D)
+    (blk,) = _grid(p.B * T * H)
+    h = blk % H
+    t = (blk // H) % T
+    b = blk // (H * T)
+    slot = np.where((t == 0) | (t == T - 1), nc, t // C)
+    sl = (b * H + h) * (nc + 1) + slot
+    sb = 2 * NF * 16
+    r.ptr("readout_bwd", "rstates", S["rstates"], sl * sb, sl * sb + 2 * NF * 16)
+    r.ptr("readout_bwd", "rstates_t", S["rstates_t"], sl * sb, sl * sb + NF * 16)
+    if p.gamma:
+        r.ptr("readout_bwd", "rms", S["rms"], 0, D * 4)
+    NW, CH = 4, D // 8
+    RPI = 64 // CH
+    NL = 32 // RPI
+    HALF = max(D, 32) // 2
+    NG = HALF // 8
+    rowbytes = H * D * 2
+    nbytes = (U - 1) * rowbytes + D * 2 if U > 0 else 0
+    fbase = (((b * T + t) * U * H + h) * D) * 2
+    ntiles = (U + 31) // 32
+    per_wave = (ntiles + NW - 1) // NW
+    loff = (RPI - 1) * rowbytes + 16 * (CH - 1)
+    # fetch_q(tile + NW) inside the last process: tile (NW - 1) + NW per_wave
+    fetch_max = ((NW - 1) + NW * per_wave) * 32 * rowbytes + loff + RPI * (NL - 1) * rowbytes
+    tile_max = (NW - 1) + NW * max(per_wave - 1, 0)
+    row_max = tile_max * 32 * rowbytes + loff + RPI * (NL - 1) * rowbytes
+    # this tile's q again, by token: the lanes owning outputs (dv0 < D)
+    qc_max = (tile_max * 32 + 31) * rowbytes + max(dv0 for dv0 in (0, HALF) if dv0 < D) * 2 + 16 * (NG - 1)
+    n = np.full_like(fbase, nbytes)
+    r.rsrc("readout_bwd", "q", S["q"], fbase, n, max(fetch_max, qc_max), 16)
+    for buf in ("gate", "dy", "dout", "dgate", "dq"):
+        r.rsrc("readout_bwd", buf, S[buf], fbase, n, row_max, 16)
+
+
+def model_gram_plain(p: Prob, r: Report, S):
+    """dS_q(t) = do_t^T q_t for every frame: the statistics kernel's PLAIN mode."""
+    do = "dout" if p.epilogue else "dy"
+    model_gram(p, r, S, parts=[("q", do, None, p.T, p.U, 0, p.T, 0)], out="dsq", t_slots=p.T)
+
+
+def _ptr_heads(r, kern, S, buf, heads, per_head, lo_slot, hi_slot, dd):
+    """Slots lo_slot .. hi_slot - 1 of per_head-slot blocks of every head."""
+    lo = (heads * per_head + lo_slot) * dd
+    hi = (heads * per_head + hi_slot) * dd
+    r.ptr(kern, buf, S[buf], lo, hi)
+
+
+def model_backward_scan(p: Prob, r: Report, S):
+    D, H, T, C, nc = p.D, p.H, p.T, p.C, p.nc
+    heads = np.arange(p.B * H, dtype=np.int64)
+    dd = D * D * 4
+    # fill_zero over whole buffers (n16 = bytes / 16 entries of 16 bytes)
+    for buf in ("states_f", "states_r", "lam_f", "lam_r", "dA", "dB", "dalpha"):
+        assert S[buf] % 16 == 0
+        r.ptr("fill_zero", buf, S[buf], 0, S[buf] // 16 * 16)
+    # backward_gather: dsq of all T frames of a head; dF, dR of all n_c slots; dST
+    _ptr_heads(r, "backward_gather", S, "dsq", heads, T, 0, T, dd)
+    _ptr_heads(r, "backward_gather", S, "dF", heads, nc, 0, nc, dd)
+    _ptr_heads(r, "backward_gather", S, "dR", heads, nc, 0, nc, dd)
+    _ptr_heads(r, "backward_gather", S, "dST", heads, 1, 0, 1, dd)
+    if p.bridge:
+        frames = []
+        for j in range(nc):
+            if j >= 1:
+                frames += list(range(C * (j - 1), C * j))
+            if j + 1 <= nc - 1:
+                frames += list(range(C * (j + 1), min(C * (j + 2), T)))
+        if frames:
+            s_ = np.array(frames)
+            b, h = heads // H, heads % H
+            lo = ((b[:, None] * T + s_[None, :]) * H + h[:, None]) * D * 4
+            r.ptr("backward_gather", "alpha", S["alpha"], lo, lo + D * 4)
+    # the scan's STATES and ADJOINT modes: frame by frame, every frame's state
+    # (T + 2 slots) and every frame's adjoint (T + 1 slots) through a
+    # descriptor per (head, direction)
+    NV = 2 if D >= 32 else 1
+    for d_ in (0, 1):
+        frames, alphas = _scan_steps(p, "frames", d_)
+        fr = np.array(sorted(set(frames) | {T}))
+        assert fr.min() >= 0 and fr.max() <= T
+        ps = heads[:, None] * (T + 1) + fr[None, :]
+        for kern in ("scan_states", "scan_adjoint"):
+            r.ptr(kern, "pinv", S["pinv"], ps * dd, (ps + 1) * dd)
+            al = np.array(sorted(set(alphas) | {0}))
+            assert al.max() < T
+            b, h = (heads // H)[:, None], (heads % H)[:, None]
+            lo = ((b * T + al[None, :]) * H + h) * D * 4
+            r.ptr(kern, "alpha", S["alpha"], lo, lo + D * 4)
+        r.ptr("scan_states", "stats", S["stats"], ps * 2 * dd + dd, ps * 2 * dd + 2 * dd)
+        # STATES: the start state in slot 0 / T - 1, then slot s after frame s
+        rec = "states_f" if d_ == 0 else "states_r"
+        slots = [0 if d_ == 0 else T - 1] + [s for s in frames if s != T]
+        assert max(slots) <= T + 1
+        r.rsrc("scan_states", rec, S[rec], heads * (T + 2) * dd, np.full_like(heads, (T + 2) * dd),
+               np.array([max(slots) * dd + dd - 4 * NV]), 4 * NV)
+        # ADJOINT: the record adjoints of chunk min(s / C, n_c - 1) (or 0),
+        # lambda at frame s into slot s, the start state's adjoint into lam_final
+        real = [s for s in frames if s != T]
+        js = sorted({min(s // C, nc - 1) for s in real} | {0})
+        assert max(js) < nc
+        src = "dF" if d_ == 0 else "dR"
+        jj = heads[:, None] * nc + np.array(js)[None, :]
+        r.ptr("scan_adjoint", src, S[src], jj * dd, (jj + 1) * dd)
+        lam = "lam_f" if d_ == 0 else "lam_r"
+        top = max(real) if real else 0
+        r.rsrc("scan_adjoint", lam, S[lam], heads * (T + 1) * dd, np.full_like(heads, (T + 1) * dd),
+               np.array([top * dd + dd - 4 * NV]), 4 * NV)
+        _ptr_heads(r, "scan_adjoint", S, "lam_final", heads, 2, d_, d_ + 1, dd)
+    # text_adjoint: slot T of lam_f, dST, both final adjoints
+    _ptr_heads(r, "text_adjoint", S, "lam_f", heads, T + 1, T, T + 1, dd)
+    _ptr_heads(r, "text_adjoint", S, "dST", heads, 1, 0, 1, dd)
+    _ptr_heads(r, "text_adjoint", S, "lam_final", heads, 2, 0, 2, dd)
+    # decode_pinv: every slot's two planes into a float32 matrix
+    P = "pinv"
+    if p.split:
+        _ptr_heads(r, "decode_pinv", S, "pinv", heads, T + 1, 0, T + 1, dd)
+        _ptr_heads(r, "decode_pinv", S, "p32", heads, T + 1, 0, T + 1, dd)
+        P = "p32"
+    # gemm_dd: (head, slot) for slots 1 .. T-2 and T; matrix slot + shift of
+    # each operand, head strides of T + 2 (states), 2 (T + 1) (stats) or T + 1
+    slots = np.array(list(range(1, T - 1)) + [T])
+    hs = heads[:, None]
+    sl = slots[None, :]
+
+    def mat(kern, buf, per_head, shift, stride=1, off=0):
+        i = (hs * per_head + (sl + shift) * stride) * dd + off
+        r.ptr(kern, buf, S[buf], i, i + dd)
+
+    for buf, per, sh in (("states_f", T + 2, -1), ("lam_f", T + 1, 0), ("states_r", T + 2, 1), ("lam_r", T + 1, 0),
+                         (P, T + 1, 0), ("M", T + 1, 0)):
+        mat("gemm_dd rowdot", buf, per, sh)
+    mat("gemm_dd diag", "stats", 2 * (T + 1), 0, stride=2, off=dd)
+    for buf in ("lam_f", "lam_r", "M", "dPinv"):
+        mat("gemm_dd diag", buf, T + 1, 0)
+    for buf in ("lam_f", "lam_r", P, "dB", "dPinv", "tmp", "dA"):
+        mat("gemm_dd", buf, T + 1, 0)
+    frames_ = slots[slots < T]
+    if frames_.size:
+        b, h = (heads // H)[:, None], (heads % H)[:, None]
+        lo = ((b * T + frames_[None, :]) * H + h) * D * 4
+        r.ptr("gemm_dd diag", "alpha", S["alpha"], lo, lo + D * 4)
+        r.ptr("gemm_dd rowdot", "dalpha", S["dalpha"], lo, lo + D * 4)
+    # bridge_dalpha: (head, chunk j); query chunks j + 1 (forward) and j - 1 (reverse)
+    if p.bridge:
+        for j in range(nc):
+            if j + 1 <= nc - 1 and j + 1 >= 2:
+                _ptr_heads(r, "bridge_dalpha", S, "fwd", heads, nc, j - 1, j, dd)
+            if j >= 1 and j + 1 <= nc - 1:
+                _ptr_heads(r, "bridge_dalpha", S, "rev", heads, nc, j + 1, j + 2, dd)
+            cs = [c for c in (j + 1, j - 1) if 0 <= c <= nc - 1]
+            ts = [t for c in cs for t in range(C * c, min(C * (c + 1), T))]
+            if ts:
+                _ptr_heads(r, "bridge_dalpha", S, "dsq", heads, T, min(ts), max(ts) + 1, dd)
+            s_ = np.arange(C * j, min(C * (j + 1), T))
+            b, h = (heads // H)[:, None], (heads % H)[:, None]
+            lo = ((b * T + s_[None, :]) * H + h) * D * 4
+            r.ptr("bridge_dalpha", "alpha", S["alpha"], lo, lo + D * 4)
+            r.ptr("bridge_dalpha", "dalpha", S["dalpha"], lo, lo + D * 4)
+        _ptr_heads(r, "bridge_dalpha", S, "s_text", heads, 1, 0, 1, dd)
+
+
+def model_backward_gram(p: Prob, r: Report, S):
+    D, H, T, U, L = p.D, p.H, p.T, p.U, p.L
+    heads = np.arange(p.B * H, dtype=np.int64)
+    dd = D * D * 4
+    # pack_grad_mats(16): slot i of dA, dB into five bfloat16 planes of slot i
+    DP = max(D, 32)
+    NF = (DP // 16) * (D // 32) * 64 if D >= 32 else (DP // 32) * (D // 16) * 64
+    slot_b = 5 * NF * 16  # the layout gives each slot 5 max(d, 32) d bfloat16 values
+    for buf in ("dA", "dB"):
+        _ptr_heads(r, "pack_grad_mats", S, buf, heads, T + 1, 0, T + 1, dd)
+    _ptr_heads(r, "pack_grad_mats", S, "gmats", heads, T + 1, 0, T + 1, slot_b)
+    # gram_bwd16 (d >= 32) / gram_bwd_bf16 (d = 16): every frame, then the text
+    # frame (launched only with text tokens)
+    parts = [("k", "v", "beta", "dk", "dv", "dbeta", T, U, 0, T, 0)]
+    if L > 0:
+        parts.append(("k_text", "v_text", "beta_text", "dk_text", "dv_text", "dbeta_text", 1, L, 0, 1, T))
+    rowbytes = H * D * 2
+    for kb, vb, bb, dkb, dvb, dbb, T_in, Up, t_first, n_frames, slot_off in parts:
+        (blk,) = _grid(p.B * n_frames * H)
+        h = blk % H
+        fi = (blk // H) % n_frames
+        b = blk // (H * n_frames)
+        t = t_first + fi
+        src = (b * H + h) * (T + 1) + (t + slot_off)
+        r.ptr("gram_bwd", "gmats", S["gmats"], src * slot_b, (src + 1) * slot_b)
+        tok0 = (b * T_in + t) * Up
+        fbase = (tok0 * H + h) * D * 2
+        nbytes = (Up - 1) * rowbytes + D * 2 if Up > 0 else 0
+        ntiles = (Up + 31) // 32
+        row = max(ntiles * 32 - 1, 0)  # every load and store is guarded by tile < ntiles
+        max_off = row * rowbytes + (D * 2 - 16)
+        for buf in (kb, vb, dkb, dvb):
+            r.rsrc("gram_bwd", buf, S[buf], fbase, np.full_like(fbase, nbytes), max_off, 16)
+        bbase = (tok0 * H + h) * 2
+        bbytes = (Up - 1) * H * 2 + 2 if Up > 0 else 0
+        for buf in (bb, dbb):
+            r.rsrc("gram_bwd", buf, S[buf], bbase, np.full_like(bbase, bbytes), row * H * 2, 2)
+
+
+def model_backward(p: Prob) -> Report:
+    """Every kernel of vdn_vda_backward_readout, _scan and _gram for one
+    problem (bfloat16 inputs)."""
+    assert p.bf16
+    S = bwd_sizes(p)
+    r = Report()
+    model_pack_states_t(p, r, S)
+    model_readout_bwd(p, r, S)
+    model_gram_plain(p, r, S)
+    model_backward_scan(p, r, S)
+    model_backward_gram(p, r, S)
     return r

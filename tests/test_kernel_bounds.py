@@ -1,7 +1,8 @@
-"""Host check of every forward kernel's address ranges (tests/kernel_bounds.py)
-for every problem the GPU tests, the benchmark and smoke() launch, in both scan
-modes, with and without the decay bridge, the epilogue and the RMSNorm gain;
-and checks that the model itself catches planted mistakes."""
+"""Host check of the address ranges of every forward, prep and backward kernel
+(tests/kernel_bounds.py) for every problem the GPU tests, the benchmark and
+smoke() launch, in both scan modes, with and without the decay bridge, the
+epilogue and the RMSNorm gain; and checks that the model itself catches
+planted mistakes."""
 
 import pytest
 
@@ -65,3 +66,65 @@ def test_model_catches_planted_mistakes():
     r2 = KB.Report()
     KB.model_readout(big, r2)
     assert any("wraps" in e for e in r2.errors)
+
+
+def _bwd_shapes():
+    """(name, workload, flags) for every backward launch of the GPU suite and
+    the benchmark (bench.py --backward runs the 768p clip)."""
+    import test_gpu_backward as GB
+    out = [(n, c["w"], dict(epilogue=c.get("epilogue", True), bridge=c.get("bridge", False), gamma=c.get("gain", False)))
+           for n, c in GB.CASES.items()]
+    out.append(("768p", GB.BASE, {}))
+    out.append(("graphs", synth.WORKLOADS["768p_bf16"].scaled(name="graphs", H=2, T=12, grid_h=5, grid_w=7, L=8), {}))
+    out.append(("long_clip", synth.WORKLOADS["long_prep_bf16"], {}))
+    for h in (3, 8):
+        out.append((f"768p_h{h}", synth.WORKLOADS["768p_bf16"].scaled(name="h", H=h), {}))
+    return out
+
+
+BWD_SHAPES = _bwd_shapes()
+
+
+@pytest.mark.parametrize("name,w,flags", BWD_SHAPES, ids=[s[0] for s in BWD_SHAPES])
+def test_backward_kernels_stay_in_bounds(name, w, flags):
+    """Every kernel of the three backward stages, each workspace part checked
+    as a buffer of its own, with and without the epilogue and the bridge."""
+    checked = 0
+    for epi in (flags.get("epilogue", True), not flags.get("epilogue", True)):
+        for bridge in (flags.get("bridge", False), True):
+            r = KB.model_backward(_prob(w, epilogue=epi, bridge=bridge, gamma=flags.get("gamma", False) and epi))
+            assert not r.errors, (name, epi, bridge, r.errors[:5])
+            checked += r.checked
+    assert checked > 0
+
+
+def test_backward_slot_sizes_match_the_layout():
+    """The fragment counts the kernels use fill exactly the slots the
+    workspace layout sizes (readout states, gradient planes)."""
+    for d in (16, 32, 64, 128):
+        p = KB.Prob(B=1, H=2, T=7, gh=3, gw=4, D=d, L=2)
+        S = KB.bwd_sizes(p)
+        NF = KB._readout_frags(d)
+        assert 2 * NF * 16 * 2 * (p.nc + 1) == S["rstates_t"]
+        NFg = (d // 16) * (d // 32) * 64 if d >= 32 else 64
+        assert 5 * NFg * 16 * 2 * (p.T + 1) == S["gmats"]
+
+
+def test_backward_model_catches_planted_mistakes():
+    """Each workspace part one slot short is reported by the kernel that
+    addresses its last slot."""
+    w = synth.WORKLOADS["768p_bf16"].scaled(name="m", H=2, T=12, grid_h=5, grid_w=7, L=8)
+    p = _prob(w, bridge=True)
+    dd = p.D * p.D * 4
+    for part, short in (("states_r", dd), ("lam_f", dd), ("dsq", dd), ("dF", dd), ("lam_final", dd),
+                        ("gmats", 5 * p.D * p.D * 2), ("rstates_t", 16), ("dout", 2), ("p32", dd), ("tmp", dd)):
+        S = KB.bwd_sizes(p)
+        S[part] -= short
+        r = KB.Report()
+        KB.model_pack_states_t(p, r, S) if part == "rstates_t" else None
+        KB.model_readout_bwd(p, r, S)
+        KB.model_gram_plain(p, r, S)
+        KB.model_backward_scan(p, r, S)
+        if part not in ("rstates_t",):
+            KB.model_backward_gram(p, r, S)
+        assert any(part in e for e in r.errors), (part, r.errors[:3])
