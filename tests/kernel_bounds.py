@@ -14,9 +14,9 @@ Two kinds of access are checked:
   kernel computes must not wrap (a wrapped offset could land back inside the
   range); accesses past num_records read zero or are dropped by the hardware.
 
-Covered: the forward pass and the prep (``model_forward``) and the three
-backward stages (``model_backward``, every part of the backward workspace as a
-buffer of its own); the adjacent maps' GEMMs are not modelled.
+Covered: the forward pass and the prep (``model_forward``), the three backward
+stages (``model_backward``, every part of the backward workspace as a buffer of
+its own) and the adjacent maps (``model_gates``, ``model_out_proj``).
 
 The model has no knowledge of the kernels beyond what is written here: a kernel
 change that moves an address must be mirrored in its model, and the test then
@@ -771,4 +771,97 @@ def model_backward(p: Prob) -> Report:
     model_gram_plain(p, r, S)
     model_backward_scan(p, r, S)
     model_backward_gram(p, r, S)
+    return r
+
+
+# ---------------------------------------------------------------------------
+# vda_proj.hip: the gates before the path and the output projection after it
+# ---------------------------------------------------------------------------
+
+GBM = GBN = 256
+GROUP_M = 4
+
+
+def proj_sizes(p: Prob, dm: int) -> dict:
+    """Bytes of the adjacent maps' buffers (bfloat16, float32 where noted)."""
+    M, F, HD = p.B * p.T * p.U, p.B * p.T, p.H * p.D
+    S = min(8, max(1, p.U // 64))
+    return dict(x=M * dm * 2, w_gb=(HD + p.H) * dm * 2, w_alpha=HD * dm * 4, gate=M * HD * 2, beta=M * p.H * 2,
+                alpha=F * HD * 4, partial=F * S * dm * 4, xbar=F * dm * 4, o=M * HD * 2, w_o=dm * HD * 2,
+                y_in=M * dm * 2, y=M * dm * 2, splits=S)
+
+
+def model_gemm(r: Report, S, kern, M, N, K, a, w, epi, outs):
+    """gemm_nt_bf16: C [M, N] = A [M, K] W [N, K]^T, one 256 x 256 tile per live
+    block in the XCD-banded order; ``outs`` names (gate, beta) for PROJ_GATE
+    with the gate's column count first, else (y, y_in or None)."""
+    mtiles, ntiles = -(-M // GBM), -(-N // GBN)
+    ntot = mtiles * ntiles
+    grid = (ntot + 7) // 8 * 8
+    (bid,) = _grid(grid)
+    xcd, slot = bid & 7, bid >> 3
+    per_xcd = (ntot + 7) // 8
+    tau = xcd * per_xcd + slot
+    live = (slot < per_xcd) & (tau < ntot)
+    tau = tau[live]
+    band, rem = tau // (GROUP_M * ntiles), tau % (GROUP_M * ntiles)
+    gm = np.minimum(GROUP_M, mtiles - band * GROUP_M)
+    nt, mt = rem // gm, band * GROUP_M + rem % gm
+    tiles = mt * ntiles + nt
+    if not (mt.max() < mtiles and nt.max() < ntiles and np.unique(tiles).size == ntot == tiles.size):
+        r.errors.append(f"{kern}: the tile order does not visit every tile once")
+    m0, n0 = mt * GBM, nt * GBN
+    mrows, nrows = np.minimum(GBM, M - m0), np.minimum(GBN, N - n0)
+    # panel loads: row < 256, k <= K - 8 (16 bytes); past K the offset 2^31
+    kmax = (GBM * K - 8) * 2
+    r.rsrc(kern, a, S[a], m0 * K * 2, mrows * K * 2, np.array([kmax, 0x80000000]), 16)
+    r.rsrc(kern, w, S[w], n0 * K * 2, nrows * K * 2, np.array([kmax, 0x80000000]), 16)
+    if 0x80000000 < GBM * K * 2:
+        r.errors.append(f"{kern}: the past-K sentinel 2^31 lies inside a panel")
+    # epilogue: 128 rows per wave row, 16-byte stores inside a row
+    for wm in (0, 1):
+        rb = m0 + 128 * wm
+        rows = np.where(rb < M, np.minimum(128, M - rb), 0)
+        if epi == "gate":
+            (g, ng), (b_, nb) = outs
+            r.rsrc(kern, g, S[g], rb * ng * 2, rows * ng * 2, np.array([128 * ng * 2 - 16]), 16)
+            r.rsrc(kern, b_, S[b_], rb * nb * 2, rows * nb * 2, np.array([128 * nb * 2 - 2]), 2)
+        else:
+            y, yin = outs
+            for buf in [y] + ([yin] if yin else []):
+                r.rsrc(kern, buf, S[buf], rb * N * 2, rows * N * 2, np.array([128 * N * 2 - 16]), 16)
+
+
+def model_gates(p: Prob, dm: int) -> Report:
+    """vdn_vda_gates: the gate/beta GEMM, the frame means, the decay gate."""
+    S = proj_sizes(p, dm)
+    r = Report()
+    M, F, HD, U = p.B * p.T * p.U, p.B * p.T, p.H * p.D, p.U
+    model_gemm(r, S, "gemm_nt_bf16 gates", M, HD + p.H, dm, "x", "w_gb", "gate", (("gate", HD), ("beta", p.H)))
+    SP = S["splits"]
+    per = -(-U // SP)
+    f, s = _grid(F, SP)
+    u0 = s * per
+    u1 = np.minimum(U, u0 + per)
+    has = u1 > u0
+    # frame_col_sums: rows u0 .. u1 - 1 of frame f, columns 0 .. dm - 1
+    lo = (f[has] * U + u0[has]) * dm * 2
+    hi = (f[has] * U + u1[has] - 1) * dm * 2 + dm * 2
+    r.ptr("frame_col_sums", "x", S["x"], lo, hi)
+    r.ptr("frame_col_sums", "partial", S["partial"], (f * SP + s) * dm * 4, (f * SP + s + 1) * dm * 4)
+    r.ptr("frame_mean", "partial", S["partial"], 0, F * SP * dm * 4)
+    r.ptr("frame_mean", "xbar", S["xbar"], 0, F * dm * 4)
+    # alpha_proj: guarded reads of xbar [F, K] and W_alpha [HD, K], alpha [F, HD]
+    r.ptr("alpha_proj", "xbar", S["xbar"], 0, F * dm * 4)
+    r.ptr("alpha_proj", "w_alpha", S["w_alpha"], 0, HD * dm * 4)
+    r.ptr("alpha_proj", "alpha", S["alpha"], 0, F * HD * 4)
+    return r
+
+
+def model_out_proj(p: Prob, dm: int, y_in: bool = True) -> Report:
+    """vdn_vda_out_proj: Y = Y_in + O W_O^T."""
+    S = proj_sizes(p, dm)
+    r = Report()
+    model_gemm(r, S, "gemm_nt_bf16 out_proj", p.B * p.T * p.U, dm, p.H * p.D, "o", "w_o", "add",
+               ("y", "y_in" if y_in else None))
     return r

@@ -1,8 +1,8 @@
-"""Host check of the address ranges of every forward, prep and backward kernel
-(tests/kernel_bounds.py) for every problem the GPU tests, the benchmark and
-smoke() launch, in both scan modes, with and without the decay bridge, the
-epilogue and the RMSNorm gain; and checks that the model itself catches
-planted mistakes."""
+"""Host check of the address ranges of every kernel (forward, prep, backward
+and the adjacent maps; tests/kernel_bounds.py) for every problem the GPU
+tests, the benchmark and smoke() launch, in both scan modes, with and without
+the decay bridge, the epilogue and the RMSNorm gain; and checks that the model
+itself catches planted mistakes."""
 
 import pytest
 
@@ -128,3 +128,44 @@ def test_backward_model_catches_planted_mistakes():
         if part not in ("rstates_t",):
             KB.model_backward_gram(p, r, S)
         assert any(part in e for e in r.errors), (part, r.errors[:3])
+
+
+def _proj_shapes():
+    """(name, workload, d_model) for every launch of the adjacent maps in the
+    GPU suite and bench.py --adjacent."""
+    import test_gpu_adjacent as GA
+    out = [(n, w, dm) for n, (w, dm) in GA.CASES.items()]
+    base = GA.BASE
+    out.append(("768p", base, base.H * base.d))
+    out.append(("layer", base.scaled(name="layer", B=1, T=11, grid_h=4, grid_w=6, H=2, d=64, L=8), 160))
+    out.append(("graphs", base.scaled(name="graphs", H=2, T=12, grid_h=5, grid_w=7, L=8), 192))
+    return out
+
+
+PROJ_SHAPES = _proj_shapes()
+
+
+@pytest.mark.parametrize("name,w,dm", PROJ_SHAPES, ids=[s[0] for s in PROJ_SHAPES])
+def test_adjacent_maps_stay_in_bounds(name, w, dm):
+    p = _prob(w)
+    for r in (KB.model_gates(p, dm), KB.model_out_proj(p, dm, True), KB.model_out_proj(p, dm, False)):
+        assert not r.errors, (name, r.errors[:5])
+        assert r.checked > 0
+
+
+def test_adjacent_model_catches_planted_mistakes():
+    """A gate or beta output one row short, weights without the beta rows, a
+    partial-sum part one frame short: each is reported."""
+    w = synth.WORKLOADS["768p_bf16"].scaled(name="m", H=2, T=5, grid_h=9, grid_w=30, L=0)
+    p, dm = _prob(w), 96
+    M = w.B * w.T * w.U
+    for buf, short in (("gate", 2 * w.H * w.d), ("beta", 2 * w.H), ("w_gb", 2 * w.H * dm), ("partial", 4 * dm),
+                       ("x", 2), ("alpha", 4)):
+        real = KB.proj_sizes
+        KB.proj_sizes = lambda p_, dm_, b=buf, s=short: dict(real(p_, dm_), **{b: real(p_, dm_)[b] - s})
+        try:
+            r = KB.model_gates(p, dm)
+        finally:
+            KB.proj_sizes = real
+        assert any(buf in e for e in r.errors), (buf, r.errors[:3])
+    assert M > 256  # several M-tiles, a ragged last one
