@@ -189,3 +189,23 @@ def test_g5_scan_adjoint_recurrence(name):
             if max(C * j, 1) == s + 1:
                 want = want + g["dR"][j]
         assert np.abs(g["drev"][s + 1] - want).max() <= tol, s
+
+
+def test_one_text_token_leaves_dq_to_rmsnorms_epsilon():
+    """With one text token and every frame reading S_T (three frames in one
+    chunk: the anchors read S_T, the middle frame S_T / 2 from each side),
+    S_T q = v_T (beta / (1 + beta)) (k_T . q) points along one direction for
+    every query and RMSNorm removes its length: y depends on q only through
+    RMSNorm's epsilon, so dq is proportional to epsilon (and largest for the
+    tokens whose k_T . q is tiny).  This is why, in such clips, a bfloat16 dq
+    fails a bound relative to its own size.  With three text tokens dq does
+    not depend on epsilon."""
+    def dq_max(L, eps):
+        x = _inputs(seed=11, T=3, U=4, d=8, L=L, C=5)
+        r = vg.backward_head(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["k_txt"], x["v_txt"], x["beta_txt"],
+                             x["dy"], gate=x["gate"], gamma=x["gamma"], chunk=5, rms_eps=eps)
+        return np.abs(r["dq"]).max()
+
+    assert dq_max(1, 1e-9) / dq_max(1, 1e-6) == pytest.approx(1e-3, rel=0.05)
+    assert dq_max(1, 1e-12) / dq_max(1, 1e-9) == pytest.approx(1e-3, rel=0.05)
+    assert dq_max(3, 1e-9) / dq_max(3, 1e-6) == pytest.approx(1.0, rel=1e-3)
