@@ -10,6 +10,10 @@
 // "race":      two waves write and read one __shared__ word with no barrier
 //              between them, then with one (built with ThreadSanitizer: the
 //              first must be reported, the second not);
+// "lanerace" / "lanesync": lane 0 of a wave writes one __shared__ word and
+//              lane 1 of the same wave reads it, with no wave barrier between
+//              them, then with one (ThreadSanitizer with SIMT_TSAN_LANES=1:
+//              the first must be reported, the second not);
 // "shard":     a launch split three ways runs workgroups 1, 4, 7 of nine in
 //              the shard with index 1, and all nine after the split is undone.
 // Each planted case is a kernel written for this check alone; none is built
@@ -155,6 +159,17 @@ int main(int argc, char** argv) {
     });
     return 0;
   }
+  if (!strcmp(what, "lanerace") || !strcmp(what, "lanesync")) {
+    const bool synced = !strcmp(what, "lanesync");
+    simt::launch(dim3(1), dim3(64), [&]() {
+      static int word;  // one word of LDS
+      if (threadIdx.x == 0) word = 7;
+      if (synced) __builtin_amdgcn_wave_barrier();
+      if (threadIdx.x == 1) printf("%s: lane 1 reads %d\n", synced ? "lanesync" : "lanerace", word);
+      if (!synced) __builtin_amdgcn_wave_barrier();
+    });
+    return 0;
+  }
   if (!strcmp(what, "shard")) {
     std::vector<int> ran;
     simt::set_block_shard(1, 3);
@@ -171,6 +186,6 @@ int main(int argc, char** argv) {
     printf("shard: %s\n", split && whole && simt::errors == 0 ? "ok" : "wrong");
     return split && whole && simt::errors == 0 ? 0 : 1;
   }
-  fprintf(stderr, "usage: selftest mfma|wrap|range|barriers|diverge|race|norace|shard\n");
+  fprintf(stderr, "usage: selftest mfma|wrap|range|barriers|diverge|race|norace|lanerace|lanesync|shard\n");
   return 2;
 }

@@ -21,7 +21,14 @@
 // workgroup.  Accesses of two waves of a workgroup that no barrier orders are
 // then reported as data races.  Workgroups are ordered one after another: the
 // __shared__ arrays here are one static object that every workgroup reuses,
-// where the hardware gives each its own LDS.
+// where the hardware gives each its own LDS.  With SIMT_TSAN_LANES=1 in the
+// environment every lane is a fiber of its own, ordered with the other lanes
+// of its wave only by the wave's cross-lane operations and wave barriers (a
+// release/acquire pair per wave-operation generation) and by the workgroup's
+// barriers: an exchange between lanes of one wave through memory with no such
+// point between the write and the read is then reported too.  On the hardware
+// such an exchange relies on the compiler keeping the accesses in program
+// order, which nothing in the source asks of it.
 #ifdef SIMT_TSAN
 #include <sanitizer/tsan_interface.h>
 #include <deque>
@@ -111,6 +118,7 @@ struct Fiber {
   WaveFn fn = nullptr;
   const void* fctx = nullptr;
   long barriers = 0;
+  long waveops = 0;  // cross-lane operations and wave barriers passed
   void* fake = nullptr;
 };
 struct Wave {
@@ -132,8 +140,11 @@ static size_t sched_size = 0;
 #endif
 #ifdef SIMT_TSAN
 static void* tsan_host = nullptr;
-static void* tsan_wave[16];
+static void* tsan_wave[16] = {};
+static void* tsan_lane[1024] = {};
+static bool tsan_lanes = false;                // a fiber per lane (SIMT_TSAN_LANES=1)
 static std::deque<char>* tsan_bars = nullptr;  // one sync object per barrier generation
+static std::deque<char>* tsan_wops[16];        // per wave: one per wave-operation generation
 static char tsan_order;  // orders workgroups and launches one after another
 #endif
 
@@ -177,7 +188,8 @@ static void trampoline() {
 static void resume(Fiber& f) {
   cur = &f;
 #ifdef SIMT_TSAN
-  __tsan_switch_to_fiber(tsan_wave[f.ids.tid.x / 64], __tsan_switch_to_fiber_no_sync);
+  __tsan_switch_to_fiber(tsan_lanes ? tsan_lane[f.ids.tid.x] : tsan_wave[f.ids.tid.x / 64],
+                         __tsan_switch_to_fiber_no_sync);
 #endif
 #ifdef SIMT_ASAN
   __sanitizer_start_switch_fiber(&sched_fake, f.stack, STACK);
@@ -197,7 +209,20 @@ void wave_op(const char* site, WaveFn fn, const void* ctx, const void* in, size_
   f->site = site;
   f->fn = fn;
   f->fctx = ctx;
+#ifdef SIMT_TSAN
+  char* sync = nullptr;
+  if (tsan_lanes) {
+    std::deque<char>& gens = *tsan_wops[w];
+    while ((long)gens.size() <= f->waveops) gens.push_back(0);
+    sync = &gens[f->waveops];
+    __tsan_release(sync);
+  }
+#endif
   to_scheduler();
+#ifdef SIMT_TSAN
+  if (sync) __tsan_acquire(sync);
+#endif
+  ++f->waveops;
   memcpy(out, W[w].out[l], nout);
 }
 
@@ -309,6 +334,10 @@ void launch(dim3 grid, dim3 block, std::function<void()> body) {
   body_fn = std::move(body);
 #ifdef SIMT_TSAN
   tsan_host = __tsan_get_current_fiber();
+  {
+    const char* e = getenv("SIMT_TSAN_LANES");
+    tsan_lanes = e && e[0] == '1';
+  }
   __tsan_release(&tsan_order);
 #endif
   for (unsigned bz = 0; bz < grid.z; ++bz)
@@ -317,9 +346,17 @@ void launch(dim3 grid, dim3 block, std::function<void()> body) {
         if ((bx + (uint64_t)grid.x * (by + (uint64_t)grid.y * bz)) % shard_count != (uint64_t)shard_index) continue;
         ++workgroups_run;
 #ifdef SIMT_TSAN
-        // each workgroup: its own wave contexts and barrier sync objects (the
-        // fibers' stacks are reused: workgroups are ordered one after another)
-        for (int w = 0; w < (nthreads + 63) / 64; ++w) tsan_wave[w] = __tsan_create_fiber(0);
+        // each workgroup: its own sync objects.  The wave (or lane) contexts
+        // are created once and reused, like the fibers' stacks: workgroups are
+        // ordered one after another, and creating and destroying thousands of
+        // TSan fibers has crashed the runtime
+        for (int w = 0; w < (nthreads + 63) / 64; ++w) {
+          if (!tsan_wave[w]) tsan_wave[w] = __tsan_create_fiber(0);
+          tsan_wops[w] = new std::deque<char>();
+        }
+        if (tsan_lanes)
+          for (int t = 0; t < nthreads; ++t)
+            if (!tsan_lane[t]) tsan_lane[t] = __tsan_create_fiber(0);
         tsan_bars = new std::deque<char>();
 #endif
         for (int t = 0; t < nthreads; ++t) {
@@ -327,6 +364,7 @@ void launch(dim3 grid, dim3 block, std::function<void()> body) {
           f.ids = Ids{Dim{(unsigned)t, 0, 0}, Dim{bx, by, bz}, Dim{grid.x, grid.y, grid.z}, Dim{block.x, 1, 1}};
           f.st = RUNNABLE;
           f.barriers = 0;
+          f.waveops = 0;
           f.fake = nullptr;
           // initial frame: six zero registers, then the trampoline as the
           // return address (entered with rsp = 8 mod 16, as after a call)
@@ -338,7 +376,10 @@ void launch(dim3 grid, dim3 block, std::function<void()> body) {
         }
         run_workgroup();
 #ifdef SIMT_TSAN
-        for (int w = 0; w < (nthreads + 63) / 64; ++w) __tsan_destroy_fiber(tsan_wave[w]);
+        // every fiber released tsan_order as it finished: the scheduler frees
+        // the workgroup's sync objects after all their uses
+        __tsan_acquire(&tsan_order);
+        for (int w = 0; w < (nthreads + 63) / 64; ++w) delete tsan_wops[w];
         delete tsan_bars;
 #endif
       }

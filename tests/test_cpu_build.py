@@ -17,8 +17,9 @@ rendezvous points, buffer descriptors with their range checks).
 * Every entry point of the sanitized library (tests/cpu_build/san_cases.py,
   shared between processes), arbitrary bit patterns included; all 24 heads of
   the 768p clip at its frame size on request.
-* ThreadSanitizer over the emulator's schedule: no data race between the
-  waves of a workgroup in any entry point.
+* ThreadSanitizer over the emulator's schedule, a fiber per lane: no data race
+  between waves and no unsynchronised exchange between the lanes of a wave in
+  any entry point.
 * The emulator's own checks (selftest.cpp).
 
 These run the kernels' code, not a model of it, but not the gfx950 binary:
@@ -488,12 +489,15 @@ def test_emulator_splits_a_launch(selftest_exe):
 
 
 # ---------------------------------------------------------------------------
-# data races between the waves of a workgroup (ThreadSanitizer over the
-# emulator's schedule: one fiber context per wave, synchronised only by the
-# workgroup's barriers)
+# data races (ThreadSanitizer over the emulator's schedule): every lane a fiber
+# of its own, ordered with the other lanes of its wave only by the wave's
+# cross-lane operations and wave barriers and with the rest of the workgroup
+# only by its barriers -- so both a race between waves and an exchange between
+# lanes of one wave through memory with nothing between write and read (which
+# on the hardware relies on the compiler keeping program order) are reported
 # ---------------------------------------------------------------------------
-def _tsan_run(exe, args):
-    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=0:exitcode=66")
+def _tsan_run(exe, args, lanes=True):
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=0:exitcode=66", SIMT_TSAN_LANES="1" if lanes else "0")
     return subprocess.run([exe, *map(str, args)], capture_output=True, text=True, timeout=900, env=env)
 
 
@@ -505,22 +509,37 @@ def test_race_detector_reports_planted_race():
     assert r.returncode == 0 and "ThreadSanitizer" not in r.stderr, r.stdout + r.stderr[-3000:]
 
 
+def test_race_detector_reports_an_unsynchronised_exchange_between_lanes():
+    """Lane 0 writes a word that lane 1 of the same wave reads: reported with a
+    fiber per lane unless a wave barrier separates them; one fiber per wave (the
+    lockstep view) sees no race either way."""
+    exe = CB.build(S.OUT, "selftest_tsan")
+    r = _tsan_run(exe, ["lanerace"])
+    assert r.returncode == 66 and "data race" in r.stderr, r.stdout + r.stderr[-3000:]
+    r = _tsan_run(exe, ["lanesync"])
+    assert r.returncode == 0 and "ThreadSanitizer" not in r.stderr, r.stdout + r.stderr[-3000:]
+    r = _tsan_run(exe, ["lanerace"], lanes=False)
+    assert r.returncode == 0 and "ThreadSanitizer" not in r.stderr, r.stdout + r.stderr[-3000:]
+
+
 TSAN_SHAPES = [(2, 6, 6, 11, 128, 12, "bf16"), (3, 7, 5, 9, 64, 37, "bf16"), (2, 6, 6, 11, 16, 12, "bf16"),
                (2, 6, 6, 11, 128, 12, "f32")]
 
 
 @pytest.mark.parametrize("shape", TSAN_SHAPES, ids=["x".join(map(str, s)) for s in TSAN_SHAPES])
-def test_forward_has_no_race_between_waves(shape):
+def test_forward_has_no_race(shape):
     exe = CB.build(S.OUT, "check_tsan")
     r = _tsan_run(exe, shape)
     assert r.returncode == 0 and "ThreadSanitizer" not in r.stderr, r.stdout + r.stderr[-4000:]
 
 
-def test_every_entry_point_has_no_race_between_waves():
-    """tests/cpu_build/san_cases.py --tsan on the ThreadSanitizer build: every
-    entry point, no data race between the waves of a workgroup."""
+def test_every_entry_point_has_no_race():
+    """tests/cpu_build/san_cases.py --tsan on the ThreadSanitizer build, a fiber
+    per lane: every entry point, no data race between waves and no exchange
+    between lanes of a wave without a wave-level synchronisation."""
     path = CB.build(S.OUT, "lib_tsan")
-    env = dict(os.environ, LD_PRELOAD=CB.sanitizer_runtime("tsan"), TSAN_OPTIONS="halt_on_error=0:exitcode=66")
+    env = dict(os.environ, LD_PRELOAD=CB.sanitizer_runtime("tsan"), TSAN_OPTIONS="halt_on_error=0:exitcode=66",
+               SIMT_TSAN_LANES="1", OPENBLAS_NUM_THREADS="1")
     for rc, out in _sweep(path, ["--tsan"], env):
         assert rc == 0 and "all entry points ran" in out, out[-6000:]
         assert "ThreadSanitizer" not in out, out[-6000:]
