@@ -7,7 +7,9 @@ emulated device environment in this folder (simt.h), as
 * ``gram_launch`` -- the forward's statistics launch alone (gram_launch.cpp),
   with both sanitizers, at any shape,
 * ``libvdn_vda_sim.so`` -- the C ABI as a host library, for tests that compare
-  the kernels' results with the oracle from Python, or
+  the kernels' results with the oracle from Python, with every __shared__
+  array filled with all-ones bytes before each workgroup (a kernel must write
+  the LDS it reads), or
 * ``libvdn_vda_sim_san.so`` -- the same with both sanitizers, linked against the
   shared sanitizer runtime (``sanitizer_runtime()``), which the loading process
   must preload.
@@ -74,7 +76,8 @@ def sanitizer_runtime(name: str = "asan") -> str:
 
 KINDS = {"check": ("check", True), "lib": ("libvdn_vda_sim.so", False), "lib_san": ("libvdn_vda_sim_san.so", True),
          "selftest": ("selftest", True), "check_tsan": ("check_tsan", True), "selftest_tsan": ("selftest_tsan", True),
-         "lib_tsan": ("libvdn_vda_sim_tsan.so", True), "gram_launch": ("gram_launch", True)}
+         "lib_tsan": ("libvdn_vda_sim_tsan.so", True), "gram_launch": ("gram_launch", True),
+         "selftest_poison": ("selftest_poison", False)}
 
 
 def build(out: str, kind: str) -> str:
@@ -83,7 +86,9 @@ def build(out: str, kind: str) -> str:
     "check_tsan" / "selftest_tsan": check.cpp / selftest.cpp with
     ThreadSanitizer on the kernels and the emulator's schedule annotated for
     it, "gram_launch": the forward's statistics launch alone, gram_launch.cpp,
-    with AddressSanitizer and UndefinedBehaviorSanitizer)."""
+    with AddressSanitizer and UndefinedBehaviorSanitizer, "selftest_poison":
+    selftest.cpp with LDS poisoned before every workgroup, as the unsanitized
+    library is)."""
     cxx = compiler()
     if cxx is None:
         raise RuntimeError("no clang++ for the host build")
@@ -99,7 +104,9 @@ def build(out: str, kind: str) -> str:
     elif sanitize:
         flags += ["-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
     else:
-        flags += ["-O2"]
+        # the unsanitized library runs the parity tests: LDS poisoned before
+        # every workgroup (see simt.h)
+        flags += ["-O2", "-DSIMT_LDS_POISON"]
     # the sanitized executables and shared libraries share their objects
     # (-shared-libsan only chooses the runtime at link time)
     suffix = ".tsan.o" if tsan else ".san.o" if sanitize else ".o"
@@ -122,8 +129,9 @@ def build(out: str, kind: str) -> str:
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
         objs = list(ex.map(compile_one, files))
     target = os.path.join(out, name)
-    if kind in ("check", "selftest", "check_tsan", "selftest_tsan", "gram_launch"):
-        main = {"check_tsan": "check.cpp", "selftest_tsan": "selftest.cpp"}.get(kind, kind + ".cpp")
+    if kind in ("check", "selftest", "check_tsan", "selftest_tsan", "gram_launch", "selftest_poison"):
+        main = {"check_tsan": "check.cpp", "selftest_tsan": "selftest.cpp",
+                "selftest_poison": "selftest.cpp"}.get(kind, kind + ".cpp")
         cmd = [cxx, *flags[2:], os.path.join(HERE, main), *objs, "-o", target]
     else:
         cmd = [cxx, "-shared", *flags[2:], *(["-shared-libsan"] if sanitize else []), *objs, "-o", target]

@@ -14,6 +14,8 @@
 //              lane 1 of the same wave reads it, with no wave barrier between
 //              them, then with one (ThreadSanitizer with SIMT_TSAN_LANES=1:
 //              the first must be reported, the second not);
+// "poison":    (built with SIMT_LDS_POISON) a workgroup that reads LDS it did
+//              not write sees all-ones bytes, not what the previous one left;
 // "shard":     a launch split three ways runs workgroups 1, 4, 7 of nine in
 //              the shard with index 1, and all nine after the split is undone.
 // Each planted case is a kernel written for this check alone; none is built
@@ -170,6 +172,17 @@ int main(int argc, char** argv) {
     });
     return 0;
   }
+  if (!strcmp(what, "poison")) {
+    uint32_t got = 0;
+    simt::launch(dim3(2), dim3(64), [&]() {
+      __shared__ uint32_t w[64];
+      if (blockIdx.x == 0) w[threadIdx.x] = 5;
+      __syncthreads();
+      if (blockIdx.x == 1 && threadIdx.x == 0) got = w[7];
+    });
+    printf("poison: workgroup 1 reads %08x\n", got);
+    return got == 0xffffffffu ? 0 : 1;
+  }
   if (!strcmp(what, "shard")) {
     std::vector<int> ran;
     simt::set_block_shard(1, 3);
@@ -186,6 +199,6 @@ int main(int argc, char** argv) {
     printf("shard: %s\n", split && whole && simt::errors == 0 ? "ok" : "wrong");
     return split && whole && simt::errors == 0 ? 0 : 1;
   }
-  fprintf(stderr, "usage: selftest mfma|wrap|range|barriers|diverge|race|norace|lanerace|lanesync|shard\n");
+  fprintf(stderr, "usage: selftest mfma|wrap|range|barriers|diverge|race|norace|lanerace|lanesync|poison|shard\n");
   return 2;
 }

@@ -82,6 +82,12 @@ simt_switch:
 .size simt_switch, .-simt_switch
 )");
 
+#ifdef SIMT_LDS_POISON
+// the linker's bounds of the section holding every __shared__ array
+extern "C" char __start_simt_lds[] __attribute__((weak));
+extern "C" char __stop_simt_lds[] __attribute__((weak));
+#endif
+
 namespace simt {
 
 int errors = 0;
@@ -332,6 +338,8 @@ void launch(dim3 grid, dim3 block, std::function<void()> body) {
     }
   }
   body_fn = std::move(body);
+  const long wg_first = workgroups_run + 1;  // index of this launch's first workgroup, as counted below
+  (void)wg_first;
 #ifdef SIMT_TSAN
   tsan_host = __tsan_get_current_fiber();
   {
@@ -345,6 +353,16 @@ void launch(dim3 grid, dim3 block, std::function<void()> body) {
       for (unsigned bx = 0; bx < grid.x; ++bx) {
         if ((bx + (uint64_t)grid.x * (by + (uint64_t)grid.y * bz)) % shard_count != (uint64_t)shard_index) continue;
         ++workgroups_run;
+#ifdef SIMT_LDS_POISON
+        // before the first eight workgroups of a launch and every 32nd after
+        // (the section holds every kernel's arrays, 4.5 MB: poisoning before
+        // every workgroup nearly doubles the parity tests' time)
+        {
+          const long i = workgroups_run - wg_first;
+          if (__start_simt_lds && (i < 8 || i % 32 == 0))
+            memset(__start_simt_lds, 0xff, (size_t)(__stop_simt_lds - __start_simt_lds));
+        }
+#endif
 #ifdef SIMT_TSAN
         // each workgroup: its own sync objects.  The wave (or lane) contexts
         // are created once and reused, like the fibers' stacks: workgroups are

@@ -7,7 +7,9 @@
 // rendezvous points: once every live lane of the wave has arrived, the
 // operation runs on all their operands at once.  s_barrier / __syncthreads is a
 // rendezvous of every live lane of the workgroup.  __shared__ arrays are
-// function-local statics (workgroups run one after another), buffer
+// function-local statics (workgroups run one after another; with
+// SIMT_LDS_POISON filled with all-ones bytes before most of a launch's first
+// workgroups and a sample of the rest), buffer
 // descriptors keep their range checks (per dword against num_records, zero on
 // loads and dropped stores past it; an offset that wraps 2^32 is reported), and
 // plain pointers are host memory, so AddressSanitizer sees every global and LDS
@@ -39,7 +41,17 @@
 #define __host__
 #define __forceinline__ inline __attribute__((always_inline))
 #define __launch_bounds__(...)
+#ifdef SIMT_LDS_POISON
+// every __shared__ array in one section, which the launcher fills with
+// all-ones bytes (NaN as float32 and bfloat16, -1 as an integer) before the
+// first eight workgroups of each launch and every 32nd after: the hardware
+// gives a workgroup LDS of undefined contents, so a kernel must write what it
+// reads.  (AddressSanitizer leaves variables in a
+// named section unguarded, so the sanitized builds keep plain statics.)
+#define __shared__ static __attribute__((section("simt_lds")))
+#else
 #define __shared__ static
+#endif
 #define __align__(n) __attribute__((aligned(n)))
 
 typedef enum hipError_t {

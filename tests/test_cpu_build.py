@@ -481,6 +481,17 @@ def test_emulator_reports_planted_faults(selftest_exe):
     assert r.returncode != 0 and "deadlock" in r.stderr, r.stdout + r.stderr
 
 
+def test_emulator_poisons_lds_between_workgroups():
+    """In the library the parity tests run (built with SIMT_LDS_POISON), a
+    workgroup that reads LDS it did not write gets all-ones bytes, not the
+    previous workgroup's values (the first eight workgroups of a launch and
+    every 32nd after start poisoned): the parity tests then also check that no
+    kernel reads LDS it has not written."""
+    exe = CB.build(S.OUT, "selftest_poison")
+    r = subprocess.run([exe, "poison"], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "reads ffffffff" in r.stdout, r.stdout + r.stderr
+
+
 def test_emulator_splits_a_launch(selftest_exe):
     """A launch split over processes runs, in each, exactly its share of the
     workgroups (every third from the second), and all of them once undone."""
