@@ -88,7 +88,7 @@ def declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.vdn_vda_backward_workspace_bytes.restype = sz
     L.vdn_vda_backward_workspace_layout.argtypes = [dp, ctypes.POINTER(BackwardLayout)]
     L.vdn_vda_backward_workspace_layout.restype = ctypes.c_int
-    L.vdn_vda_backward_readout.argtypes = [dp] + [p] * 6 + [sz] + [p] * 3 + [sz, p]
+    L.vdn_vda_backward_readout.argtypes = [dp] + [p] * 6 + [sz] + [p] * 4 + [sz, p]
     L.vdn_vda_backward_readout.restype = ctypes.c_int
     L.vdn_vda_backward_scan.argtypes = [dp, p, p, sz, p, p, sz, p]
     L.vdn_vda_backward_scan.restype = ctypes.c_int
@@ -343,11 +343,13 @@ def backward_layout(desc: Desc) -> BackwardLayout:
 
 
 def backward_readout(q, gate, rms_weight, alpha, dy, fwd_workspace, *, grid, n_text=0, chunk=5, epilogue=True,
-                     bridge=False, rms_eps=1e-6, dq=None, dgate=None, workspace=None, query_l2=False, l2_eps=1e-6):
+                     bridge=False, rms_eps=1e-6, dq=None, dgate=None, workspace=None, query_l2=False, l2_eps=1e-6,
+                     d_rms_weight=None):
     """First stage of the backward pass (vdn_vda_backward_readout): returns
     (dq, dgate or None, workspace); the workspace holds do and dS_q at the
     offsets of ``backward_layout``.  ``fwd_workspace`` is the forward's, for the
-    same descriptor and inputs."""
+    same descriptor and inputs.  A float32 tensor of d elements given as
+    ``d_rms_weight`` (with the epilogue) receives the RMSNorm gain's gradient."""
     import torch
     B, T, U, H, d = q.shape
     _dtype_of(q)
@@ -357,11 +359,15 @@ def backward_readout(q, gate, rms_weight, alpha, dy, fwd_workspace, *, grid, n_t
         _expect(x, name, q.numel(), q.dtype)
     _expect(alpha, "alpha", B * T * H * d, torch.float32)
     _expect(rms_weight, "rms_weight", d, torch.float32)
+    _expect(d_rms_weight, "d_rms_weight", d, torch.float32)
+    if d_rms_weight is not None and not epilogue:
+        raise ValueError("d_rms_weight needs the epilogue")
     _expect_bytes(fwd_workspace, "fwd_workspace")
     _expect_bytes(workspace, "workspace")
     dev = q.device
     for name, x in (("q", q), ("gate", gate), ("rms_weight", rms_weight), ("alpha", alpha), ("dy", dy),
-                    ("fwd_workspace", fwd_workspace), ("dq", dq), ("dgate", dgate), ("workspace", workspace)):
+                    ("fwd_workspace", fwd_workspace), ("dq", dq), ("dgate", dgate), ("workspace", workspace),
+                    ("d_rms_weight", d_rms_weight)):
         _check(x, name, dev)
     desc = make_desc(B, H, T, grid[0], grid[1], d, n_text, chunk, _dtype_of(q), epilogue, rms_eps=rms_eps,
                      l2_eps=l2_eps, flags=(VDN_VDA_EPILOGUE if epilogue else 0) | (VDN_VDA_DECAY_BRIDGE if bridge else 0)
@@ -375,7 +381,7 @@ def backward_readout(q, gate, rms_weight, alpha, dy, fwd_workspace, *, grid, n_t
     st = lib().vdn_vda_backward_readout(ctypes.byref(desc), _ptr(q), _ptr(gate) if epilogue else None,
                                         _ptr(rms_weight), _ptr(alpha), _ptr(dy), _ptr(fwd_workspace),
                                         fwd_workspace.numel(), _ptr(dq), _ptr(dgate) if epilogue else None,
-                                        _ptr(workspace), workspace.numel(), _stream())
+                                        _ptr(d_rms_weight), _ptr(workspace), workspace.numel(), _stream())
     if st != VDN_OK:
         raise VdaError(st, "vdn_vda_backward_readout")
     return dq, (dgate if epilogue else None), workspace
@@ -455,23 +461,27 @@ def backward_gram(k, v, beta, k_text, v_text, beta_text, workspace, *, grid, chu
 
 
 def backward(q, k, v, alpha, beta, k_text, v_text, beta_text, gate, rms_weight, dy, fwd_workspace, *, grid,
-             chunk=5, epilogue=True, rms_eps=1e-6, workspace=None, query_l2=False, l2_eps=1e-6, bridge=False):
+             chunk=5, epilogue=True, rms_eps=1e-6, workspace=None, query_l2=False, l2_eps=1e-6, bridge=False,
+             gain_grad=False):
     """The whole backward pass (the three stages in order) after a forward
     that left ``fwd_workspace`` (with ``query_l2`` the forward took the raw
     query and dq is its gradient); returns a dict of input gradients dq, dk, dv,
     dalpha, dbeta, dk_text, dv_text, dbeta_text, dgate (the last four None
-    where absent) and the workspace."""
+    where absent), with ``gain_grad`` (and the epilogue) drms_weight, the
+    RMSNorm gain's gradient [d] float32, and the workspace."""
+    import torch
     B, T, U, H, d = q.shape
     L = 0 if k_text is None else k_text.shape[1]
+    drms = torch.empty(d, dtype=torch.float32, device=q.device) if gain_grad else None
     dq, dgate, workspace = backward_readout(q, gate, rms_weight, alpha, dy, fwd_workspace, grid=grid, n_text=L,
                                             chunk=chunk, epilogue=epilogue, rms_eps=rms_eps, workspace=workspace,
-                                            query_l2=query_l2, l2_eps=l2_eps, bridge=bridge)
+                                            query_l2=query_l2, l2_eps=l2_eps, bridge=bridge, d_rms_weight=drms)
     dalpha = backward_scan(alpha, fwd_workspace, workspace, shape=(B, T, H, d), grid=grid, n_text=L,
                            chunk=chunk, dtype=_dtype_of(q), epilogue=epilogue, bridge=bridge)
     dk, dv, dbeta, dkt, dvt, dbt = backward_gram(k, v, beta, k_text, v_text, beta_text, workspace, grid=grid,
                                                  chunk=chunk, epilogue=epilogue)
     return dict(dq=dq, dk=dk, dv=dv, dalpha=dalpha, dbeta=dbeta, dk_text=dkt, dv_text=dvt, dbeta_text=dbt,
-                dgate=dgate, workspace=workspace)
+                dgate=dgate, drms_weight=drms, workspace=workspace)
 
 
 def gates(x, w_gb, w_alpha, *, heads, d, grid, chunk=5, out=None, workspace=None):

@@ -8,6 +8,8 @@
 // Its derivative with respect to the output adjoint dy is, per token,
 //     r = 1 / sqrt(mean o^2 + eps),  n = o r,  s = sigmoid(g),  dn = dy gamma s
 //     dg = dn n (1 - s),             do = r (dn - n mean(dn n)),
+// and, summed over every token of every frame, head and batch, the gain's
+// gradient dgamma = sum dy s n;
 // then dq_t = S_q(t)^T do_t per token and dS_q(t) = sum_u do_{t,u} q_{t,u}^T per
 // frame (the adjoint of the state the frame's queries read).  The adjoints of
 // the records F_j, R_j and of S_T follow from dS_q by the coverage rules and
@@ -21,6 +23,8 @@
 //    recomputation of o (same matrix-core product, same operand) followed by
 //    the epilogue's derivative in registers; do (bfloat16) and dgate stream
 //    out through the same per-wave LDS tiles that bring q, gate and dy in;
+//  * gain_grad_sum: dgamma from the per-workgroup sums readout_bwd_bf16 leaves
+//    in the workspace when asked for it;
 //  * dS_q: the frame-statistics kernel in its PLAIN mode on (q, do).
 #include <algorithm>
 #include <type_traits>
@@ -104,15 +108,45 @@ __global__ __launch_bounds__(256) void pack_states_t(const float* __restrict__ s
   }
 }
 
+// Sums over the 32 lanes of one half of the wave (lanes l and l ^ M for M < 32),
+// scattered over those lanes: x holds K live values per lane; at the step with
+// mask M a lane with bit M set keeps the upper half of them (adding its
+// partner's), the other lane the lower half.  Once one value is left the
+// remaining steps add it whole.  With K = 2^k values to begin with, lane n
+// ends holding in x[0 .. max(K/32, 1) - 1] the sums of values
+// (n / max(32/K, 1)) * max(K/32, 1) + 0, 1, ...
+template <int N, int K, int M>
+__device__ __forceinline__ void fold_lanes(float (&x)[N], int lane) {
+  if constexpr (M >= 1) {
+    if constexpr (K > 1) {
+      const bool up = (lane & M) != 0;
+#pragma unroll
+      for (int i = 0; i < K / 2; ++i) {
+        const float send = up ? x[i] : x[i + K / 2];
+        const float keep = up ? x[i + K / 2] : x[i];
+        x[i] = keep + __shfl_xor(send, M);
+      }
+      fold_lanes<N, K / 2, M / 2>(x, lane);
+    } else {
+      x[0] += __shfl_xor(x[0], M);
+      fold_lanes<N, 1, M / 2>(x, lane);
+    }
+  }
+}
+
 // Back through the epilogue: o recomputed as the forward readout computes it,
 // then dgate and do per token (see the file comment).  4 waves, each streaming
 // 32-token tiles; per wave two LDS tiles (q then dy then do; gate then dgate).
-template <int D, bool GAMMA, bool QN>
+// With DGAIN each lane also sums dy s n over its tiles' tokens (folded over the
+// wave's tokens after every tile, two channels kept per lane at d = 128), and
+// the workgroup writes its (frame, head)'s sums, channel by channel, to
+// GP[blockIdx.x * d ..]; without it GP is not touched.
+template <int D, bool GAMMA, bool QN, bool DGAIN>
 __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ G, const uint16_t* __restrict__ DY,
     const float* __restrict__ w, const uint4* __restrict__ rstates, const uint4* __restrict__ rstates_t,
     uint16_t* __restrict__ DO, uint16_t* __restrict__ DG, uint16_t* __restrict__ DQ, int T, int U, int H, int C,
-    int nc, float eps, float l2eps) {
+    int nc, float eps, float l2eps, float* __restrict__ GP) {
   constexpr int NW = 4;              // waves per workgroup
   constexpr int DP = D < 32 ? 32 : D;
   constexpr int HALF = DP / 2;       // outputs per lane
@@ -176,6 +210,13 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
   const int per_wave = (ntiles + NW - 1) / NW;
   uint4* XQ = xq[wave];
   uint4* XG = xg[wave];
+  // DGAIN: this lane's share of the gain's gradient, channels
+  // dv0 + (n / GR) * GK + k, k < GK (lanes n and n + 1 share them at d <= 32)
+  constexpr int GK = HALF >= 32 ? HALF / 32 : 1;
+  constexpr int GR = HALF >= 32 ? 1 : 32 / HALF;
+  float gsum[GK];
+#pragma unroll
+  for (int k = 0; k < GK; ++k) gsum[k] = 0.f;
 
   auto fetch_q = [&](int tile, uint4 (&qv)[NL]) {
     const uint32_t tb = (uint32_t)tile * 32 * rowbytes + loff;
@@ -289,6 +330,9 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
     bf16x8 dof[NG];
 #pragma unroll
     for (int i = 0; i < NG; ++i) dof[i] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    float gx[DGAIN ? HALF : 1];  // dy s n of this lane's channels dv0 .. dv0 + HALF - 1
+#pragma unroll
+    for (int j = 0; j < (DGAIN ? HALF : 1); ++j) gx[j] = 0.f;
     if (owns) {
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
@@ -306,6 +350,10 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
           const float dn0 = bf16_lo(y4[e]) * gm[2 * e] * s0, dn1 = bf16_hi(y4[e]) * gm[2 * e + 1] * s1;
           dow[e] = pack_bf16x2(rinv * (dn0 - n0 * m), rinv * (dn1 - n1 * m));
           dgw[e] = pack_bf16x2(dn0 * n0 * (1.f - s0), dn1 * n1 * (1.f - s1));
+          if constexpr (DGAIN) {
+            gx[j0] = bf16_lo(y4[e]) * s0 * n0;
+            gx[j1] = bf16_hi(y4[e]) * s1 * n1;
+          }
         }
         dof[i] = __builtin_bit_cast(bf16x8, make_uint4(dow[0], dow[1], dow[2], dow[3]));
         if constexpr (QN) {
@@ -322,6 +370,12 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
         XQ[pos(n, dv0 / 8 + i)] = make_uint4(dow[0], dow[1], dow[2], dow[3]);
         XG[pos(n, dv0 / 8 + i)] = make_uint4(dgw[0], dgw[1], dgw[2], dgw[3]);
       }
+    }
+    if constexpr (DGAIN) {
+      // over this tile's 32 tokens (rows past U are zero and add nothing)
+      fold_lanes<HALF, HALF, 16>(gx, lane);
+#pragma unroll
+      for (int k = 0; k < GK; ++k) gsum[k] += gx[k];
     }
     fence();
 #pragma unroll
@@ -401,13 +455,51 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
   uint4 qv[NL];
   fetch_q(wave, qv);
   for (int k = 0; k < per_wave; ++k) process(wave + NW * k, qv);
+
+  if constexpr (DGAIN) {
+    // the four waves' sums through LDS (the tiles are free once every wave is
+    // done), added in wave order: one row of d sums per (frame, head)
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(&xq[0][0]);  // [NW][DP]
+    if (owns && n % GR == 0) {
+#pragma unroll
+      for (int k = 0; k < GK; ++k) red[wave * DP + dv0 + (n / GR) * GK + k] = gsum[k];
+    }
+    __syncthreads();
+    if (tid < D) {
+      float v = red[tid];
+#pragma unroll
+      for (int w2 = 1; w2 < NW; ++w2) v += red[w2 * DP + tid];
+      GP[(size_t)blockIdx.x * D + tid] = v;
+    }
+  }
+}
+
+// dgamma[j] = sum over the rows of GP [rows][D] (one row per (batch, frame,
+// head)): 1024 threads, thread (s, j) adding rows s, s + S, ... in order, then
+// the S partial sums added in order.
+template <int D>
+__global__ __launch_bounds__(1024) void gain_grad_sum(const float* __restrict__ GP, float* __restrict__ dgamma,
+                                                      int rows) {
+  constexpr int S = 1024 / D;
+  __shared__ float part[1024];
+  const int tid = threadIdx.x, j = tid % D, sl = tid / D;
+  float v = 0.f;
+  for (int r = sl; r < rows; r += S) v += GP[(size_t)r * D + j];
+  part[tid] = v;
+  __syncthreads();
+  if (tid < D) {
+    float a = part[tid];
+    for (int k = 1; k < S; ++k) a += part[k * D + tid];
+    dgamma[tid] = a;
+  }
 }
 
 template <int D>
 hipError_t backward_readout_d(const Problem& p, const void* q, const void* gate, const float* rms_weight,
                               const void* dy, const void* rstates, const float* s_text, const float* fwd, const float* rev,
                               const float* alpha, void* rstates_t, void* dout, void* dq, void* dgate,
-                              float* dsq, hipStream_t s) {
+                              float* dsq, float* gain_part, float* dgamma, hipStream_t s) {
   hipLaunchKernelGGL(pack_states_t<D>, dim3((unsigned)(p.B * p.H * (p.nc + 1))), dim3(256), 0, s, s_text, fwd,
                      rev, alpha, static_cast<uint4*>(rstates_t), p.nc, p.T, p.H, p.C, p.bridge ? 1 : 0);
   hipError_t e = hipGetLastError();
@@ -418,20 +510,30 @@ hipError_t backward_readout_d(const Problem& p, const void* q, const void* gate,
     const unsigned grid = (unsigned)(p.B * p.T * p.H);
     auto u16 = [](const void* x) { return static_cast<const uint16_t*>(x); };
     auto w16 = [](void* x) { return static_cast<uint16_t*>(x); };
-    auto launch = [&](auto gamma, auto qn) {
-      hipLaunchKernelGGL((readout_bwd_bf16<D, decltype(gamma)::value, decltype(qn)::value>), dim3(grid), dim3(256), 0,
-                         s, u16(q), u16(gate), u16(dy), rms_weight, static_cast<const uint4*>(rstates),
+    auto launch = [&](auto gamma, auto qn, auto dgain) {
+      constexpr bool GM = decltype(gamma)::value, QN = decltype(qn)::value;
+      hipLaunchKernelGGL((readout_bwd_bf16<D, GM, QN, decltype(dgain)::value>), dim3(grid), dim3(256), 0, s, u16(q),
+                         u16(gate), u16(dy), rms_weight, static_cast<const uint4*>(rstates),
                          static_cast<const uint4*>(rstates_t), w16(dout), w16(dgate), w16(dq), p.T, p.U, p.H, p.C,
-                         p.nc, p.rms_eps, p.l2_eps);
+                         p.nc, p.rms_eps, p.l2_eps, gain_part);
     };
     using Y = std::true_type;
     using N = std::false_type;
-    if (rms_weight)
-      p.qnorm ? launch(Y(), Y()) : launch(Y(), N());
-    else
-      p.qnorm ? launch(N(), Y()) : launch(N(), N());
+    auto launch_g = [&](auto dgain) {
+      if (rms_weight)
+        p.qnorm ? launch(Y(), Y(), dgain) : launch(Y(), N(), dgain);
+      else
+        p.qnorm ? launch(N(), Y(), dgain) : launch(N(), N(), dgain);
+    };
+    dgamma ? launch_g(Y()) : launch_g(N());
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (dgamma) {
+      hipLaunchKernelGGL(gain_grad_sum<D>, dim3(1), dim3(1024), 0, s, static_cast<const float*>(gain_part), dgamma,
+                         (int)grid);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     do_ = dout;
   } else {
     // without the epilogue do is dy: dq = S_q^T dy is the forward readout, raw,
@@ -780,13 +882,13 @@ __global__ __launch_bounds__(256) void text_adjoint(const float* __restrict__ dS
 hipError_t launch_backward_readout(const Problem& p, const void* q, const void* gate, const float* rms_weight,
                                    const void* dy, const void* rstates, const float* s_text, const float* fwd, const float* rev,
                                    const float* alpha, void* rstates_t, void* dout, void* dq, void* dgate,
-                                   float* dsq, hipStream_t s) {
-  if (!p.bf16) return hipErrorInvalidValue;
+                                   float* dsq, float* gain_part, float* dgamma, hipStream_t s) {
+  if (!p.bf16 || (dgamma && (!p.epilogue || !gain_part))) return hipErrorInvalidValue;
   switch (p.D) {
-    case 16: return backward_readout_d<16>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, s);
-    case 32: return backward_readout_d<32>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, s);
-    case 64: return backward_readout_d<64>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, s);
-    case 128: return backward_readout_d<128>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, s);
+    case 16: return backward_readout_d<16>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, gain_part, dgamma, s);
+    case 32: return backward_readout_d<32>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, gain_part, dgamma, s);
+    case 64: return backward_readout_d<64>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, gain_part, dgamma, s);
+    case 128: return backward_readout_d<128>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, gain_part, dgamma, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -67,9 +67,15 @@ __device__ __forceinline__ void buf_store16_nt(uint4 v, __amdgpu_buffer_rsrc_t r
 // __builtin_amdgcn_readfirstlane on values it already considers uniform, and
 // may then compute them in vector registers anyway; a buffer descriptor built
 // from such a value turns every load into a waterfall loop.  The asm is opaque.
+// It is opaque to the hazard recognizer too: v_readfirstlane is a vector ALU
+// instruction writing a scalar register, and on CDNA a vector memory
+// instruction that reads a scalar register so written needs 5 wait states in
+// between, which the hardware does not enforce.  The compiler inserts them for
+// its own instructions but cannot see this one, so the s_nop 4 (5 wait
+// states) comes with it, whatever the scheduler places after it.
 __device__ __forceinline__ int sgpr(int v) {
   int r;
-  asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(r) : "v"(v));
+  asm volatile("v_readfirstlane_b32 %0, %1\n\ts_nop 4" : "=s"(r) : "v"(v));
   return r;
 }
 
@@ -156,10 +162,12 @@ hipError_t launch_readout(const Problem& p, const void* q, const void* gate, con
 // transposed query states; with p.epilogue dout <- do (bfloat16) and
 // dgate <- the gate's adjoint, else do = dy; dq <- S_q^T do; dsq [B, H, T, d, d]
 // <- do_t^T q_t.  rstates, s_text, fwd, rev: the forward's workspace sections.
+// With dgamma (the epilogue only): gain_part [B T H, d] <- per-(frame, head)
+// sums, then dgamma [d] <- their sum.
 hipError_t launch_backward_readout(const Problem& p, const void* q, const void* gate, const float* rms_weight,
                                    const void* dy, const void* rstates, const float* s_text, const float* fwd,
                                    const float* rev, const float* alpha, void* rstates_t, void* dout, void* dq,
-                                   void* dgate, float* dsq, hipStream_t s);
+                                   void* dgate, float* dsq, float* gain_part, float* dgamma, hipStream_t s);
 // Second stage of the backward pass: buffers (float32 unless noted).
 struct BwdScanBuffers {
   const float* stats;   // forward workspace: [B, H, T+1, 2d, d]

@@ -199,6 +199,7 @@ struct BwdLayout {
   size_t dF, dR, dST, lam_f, lam_r, dA, dB;                       // second stage (documented)
   size_t states_f, states_r, lam_final, p32, M, dPinv, tmp;       // second stage (internal)
   size_t gmats;                                                   // third stage (internal)
+  size_t gain;                                                    // first stage (internal)
   size_t total;
 };
 BwdLayout make_bwd_layout(const Problem& p) {
@@ -230,6 +231,8 @@ BwdLayout make_bwd_layout(const Problem& p) {
   // five bfloat16 operand planes per slot (G hi, lo; dB hi, lo; dB^T hi), the
   // rows padded to 32 at d = 16
   take(l.gmats, heads * (p.T + 1) * 5 * (size_t)std::max(p.D, 32) * p.D * 2);
+  // the gain gradient's sums per (batch, frame, head), float32 [B T H][d]
+  take(l.gain, (size_t)p.B * p.T * p.H * p.D * 4);
   l.total = o;
   return l;
 }
@@ -459,7 +462,7 @@ vdn_status vdn_vda_backward_workspace_layout(const vdn_vda_desc* d, vdn_vda_back
 vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d, const void* q, const void* gate,
                                     const float* rms_weight, const float* alpha, const void* dy,
                                     const void* fwd_workspace, size_t fwd_workspace_bytes, void* dq,
-                                    void* dgate, void* workspace, size_t workspace_bytes,
+                                    void* dgate, float* d_rms_weight, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream) {
   const vdn_status st = check(d);
   if (st != VDN_OK) return st;
@@ -468,6 +471,7 @@ vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d, const void* q, const 
   if (d->dtype != VDN_BF16 || ((d->flags & VDN_VDA_QUERY_L2) && !epi)) return VDN_ERR_UNSUPPORTED;
   if (!q || !alpha || !dy || !dq || !fwd_workspace) return VDN_ERR_INVALID_ARG;
   if (epi && (!gate || !dgate)) return VDN_ERR_INVALID_ARG;
+  if (d_rms_weight && !epi) return VDN_ERR_INVALID_ARG;  // no gain without the epilogue
   const Problem p = problem(d);
   const Layout fl = make_layout(p);
   const BwdLayout bl = make_bwd_layout(p);
@@ -477,20 +481,22 @@ vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d, const void* q, const 
   for (const void* ptr : need16)
     if (ptr && !aligned(ptr, 16)) return VDN_ERR_ALIGNMENT;
   if (rms_weight && !aligned(rms_weight, 4)) return VDN_ERR_ALIGNMENT;
+  if (d_rms_weight && !aligned(d_rms_weight, 4)) return VDN_ERR_ALIGNMENT;
   if (!aligned(workspace, kAlign) || !aligned(fwd_workspace, kAlign)) return VDN_ERR_ALIGNMENT;
   {
     const Sizes z = sizes_of(d);
     const Span ins[] = {{q, z.x}, {epi ? gate : nullptr, z.x}, {rms_weight, z.weight}, {alpha, z.alpha},
                         {dy, z.x}, {fwd_workspace, fl.total}};
-    const Span outs[] = {{dq, z.x}, {epi ? dgate : nullptr, z.x}, {workspace, bl.total}};
-    if (any_overlap(outs, 3, ins, 6)) return VDN_ERR_INVALID_ARG;
+    const Span outs[] = {{dq, z.x}, {epi ? dgate : nullptr, z.x}, {workspace, bl.total}, {d_rms_weight, z.weight}};
+    if (any_overlap(outs, 4, ins, 6)) return VDN_ERR_INVALID_ARG;
   }
   const char* fw = static_cast<const char*>(fwd_workspace);
   char* ws = static_cast<char*>(workspace);
   const hipError_t e = launch_backward_readout(
       p, q, gate, rms_weight, dy, fw + fl.rstates, reinterpret_cast<const float*>(fw + fl.s_text),
       reinterpret_cast<const float*>(fw + fl.fwd), reinterpret_cast<const float*>(fw + fl.rev), alpha,
-      ws + bl.rstates_t, ws + bl.dout, dq, dgate, reinterpret_cast<float*>(ws + bl.dsq), stream);
+      ws + bl.rstates_t, ws + bl.dout, dq, dgate, reinterpret_cast<float*>(ws + bl.dsq),
+      reinterpret_cast<float*>(ws + bl.gain), d_rms_weight, stream);
   return e == hipSuccess ? VDN_OK : VDN_ERR_HIP;
 }
 

@@ -239,6 +239,11 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d,
  *   dq    [B, T, U, H, d_k] = S_q(t)^T do per token                (dtype),
  *   dgate [B, T, U, H, d_v] = dy * rms_weight * n * s * (1 - s)     (dtype;
  *         n = o / sqrt(mean o^2 + rms_eps), s = sigmoid(gate); with VDN_VDA_EPILOGUE),
+ *   d_rms_weight [d_v] = sum over every batch, frame, token and head of
+ *         dy * s * n, the gradient of the RMSNorm gain (float32; with
+ *         VDN_VDA_EPILOGUE, and only when d_rms_weight is not NULL; formed
+ *         whether or not rms_weight is given, a NULL rms_weight being a gain
+ *         of ones; overwritten, not accumulated),
  * and leaves in its workspace, at the offsets vdn_vda_backward_workspace_layout()
  * reports,
  *   d_out     [B, T, U, H, d_v] bfloat16: do, the readout's adjoint
@@ -251,7 +256,8 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d,
  *             turns these into the adjoints of the records and of S_T);
  *   readout_states_t: S_q^T per chunk slot in the readout kernel's operand
  *             order (not meant for callers).
- * The gradient of rms_weight is not formed by this stage.
+ * d_rms_weight is summed in a fixed order (per (frame, head) in the readout
+ * kernel, then over those sums), so it is the same from call to call.
  * fwd_workspace must hold what vdn_vda_forward left there for the same
  * descriptor and inputs (q, k, v, alpha, beta, text, gate, rms_weight); alpha
  * is read for the decay bridge.  dy, dq, dgate are device buffers owned by the
@@ -261,10 +267,10 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d,
  * and d_out holds do / |q| per token (so that d_state_q = sum d_out q^T reads
  * the raw query).  Supported: VDN_BF16, and VDN_VDA_QUERY_L2 only with
  * VDN_VDA_EPILOGUE (else VDN_ERR_UNSUPPORTED).  Errors: VDN_ERR_INVALID_ARG
- * (NULL pointer, gate or dgate missing with the epilogue, aliasing),
- * VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE (either workspace too small or NULL),
- * VDN_ERR_ALIGNMENT (16 B for tensors, 256 B for workspaces), VDN_ERR_HIP.
- * Asynchronous on `stream`.
+ * (NULL pointer, gate or dgate missing with the epilogue, d_rms_weight without
+ * it, aliasing), VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE (either workspace too
+ * small or NULL), VDN_ERR_ALIGNMENT (16 B for tensors, 4 B for d_rms_weight,
+ * 256 B for workspaces), VDN_ERR_HIP.  Asynchronous on `stream`.
  */
 /* Offsets (bytes from the base) of the backward workspace's documented
  * sections; the workspace also holds internal sections.  The second stage's
@@ -298,7 +304,7 @@ vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d,
                                     const float* rms_weight, const float* alpha,
                                     const void* dy,
                                     const void* fwd_workspace, size_t fwd_workspace_bytes,
-                                    void* dq, void* dgate,
+                                    void* dq, void* dgate, float* d_rms_weight,
                                     void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 

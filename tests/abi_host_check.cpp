@@ -70,7 +70,7 @@ int main() {
       EXPECT(vdn_vda_prepare(&d, fake(0), nullptr, fake(2), (const float*)fake(3), (const float*)fake(4),
                              (const float*)fake(5), (const float*)fake(6), fake(7), fake(8), fake(9), nullptr) != VDN_OK);
       EXPECT(vdn_vda_backward_readout(&d, nullptr, fake(1), nullptr, (const float*)fake(3), fake(4), fake(5), ws,
-                                      fake(6), fake(7), fake(8), 1u << 30, nullptr) != VDN_OK);
+                                      fake(6), fake(7), nullptr, fake(8), 1u << 30, nullptr) != VDN_OK);
       EXPECT(vdn_vda_backward_scan(&d, nullptr, fake(1), ws, (float*)fake(2), fake(3), 1u << 30, nullptr) != VDN_OK);
       EXPECT(vdn_vda_backward_gram(&d, nullptr, fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), fake(7),
                                    fake(8), fake(9), fake(10), fake(11), fake(12), 1u << 30, nullptr) != VDN_OK);

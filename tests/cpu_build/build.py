@@ -32,7 +32,7 @@ CSRC = os.path.join(ROOT, "frame_wise_delta_02_amd", "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 CXX_CANDIDATES = ("/opt/rocm/llvm/bin/clang++", "/opt/rocm/lib/llvm/bin/clang++", shutil.which("clang++") or "")
 
-SGPR_ASM = 'asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(r) : "v"(v));'
+SGPR_ASM = 'asm volatile("v_readfirstlane_b32 %0, %1\\n\\ts_nop 4" : "=s"(r) : "v"(v));'
 SGPR_HOST = "r = __builtin_amdgcn_readfirstlane(v);"
 
 

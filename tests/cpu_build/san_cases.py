@@ -44,7 +44,8 @@ def finite(*arrays):
 FORWARD = ("d32_bf16", "d16_bf16", "d32_f32", "ragged_f32_128", "no_text_bf16", "T1_bf16", "T2_f32",
            "chunk3_bf16", "batch2_bf16", "U1_bf16_128", "U2_f32_16", "ragged_bf16_128")
 FORWARD_QUICK = ("d32_bf16", "d16_bf16", "d32_f32", "no_text_bf16", "T1_bf16", "U1_bf16_128", "U2_f32_16")
-BACKWARD_QUICK = ("bwd_64_ragged", "bwd_32_bridge", "bwd_16_chunk3", "bwd_64_no_text", "bwd_16_ql2", "bwd_T1")
+BACKWARD_QUICK = ("bwd_64_ragged", "bwd_32_bridge", "bwd_16_chunk3", "bwd_64_no_text", "bwd_16_ql2", "bwd_T1",
+                  "bwd_16", "bwd_128_gain")
 ADJACENT_QUICK = ("adj_small", "adj_d16", "adj_tiny")
 
 
@@ -128,9 +129,11 @@ def cases(full, tsan=False):
                 GB._raw_queries(x, w)
             rw = np.linspace(0.5, 1.5, w.d) if case.get("gain") else None
             _, fws, _ = S.run_forward(L, x, w, epilogue=epi, rms_weight=rw, bridge=bridge, query_l2=ql2)
+            # the gain's gradient on the cases that give a gain: both readout
+            # variants run across the cases
             got, _, _ = S.run_backward(L, x, w, GB._dy(w), fws, epilogue=epi, rms_weight=rw, bridge=bridge,
-                                       query_l2=ql2)
-            finite(*(v for v in got.values()))
+                                       query_l2=ql2, gain=epi and case.get("gain", False))
+            finite(*(v for v in got.values() if v is not None))
         return run
 
     for name in GB.CASES if full else BACKWARD_QUICK:
@@ -144,7 +147,7 @@ def cases(full, tsan=False):
         x = synth.make_inputs(w)
         o, fws, _ = S.run_forward(L, x, w, epilogue=True)
         finite(o)
-        got, _, _ = S.run_backward(L, x, w, GB._dy(w), fws, epilogue=True)
+        got, _, _ = S.run_backward(L, x, w, GB._dy(w), fws, epilogue=True, gain=True)
         finite(*(v for v in got.values()))
 
     if not tsan:

@@ -107,10 +107,11 @@ def intermediates(L, ws: np.ndarray, desc, w: synth.Workload) -> dict:
 
 
 def run_backward(L, x: dict, w: synth.Workload, dy: np.ndarray, fwd_ws: np.ndarray, epilogue=True, rms_weight=None,
-                 bridge=False, query_l2=False, l2_eps=1e-6):
+                 bridge=False, query_l2=False, l2_eps=1e-6, gain=False):
     """The three backward stages (vdn_vda_backward_readout, _scan, _gram) after a
-    forward that left ``fwd_ws``; returns a dict of numpy results, the backward
-    workspace and its layout."""
+    forward that left ``fwd_ws``; returns a dict of numpy results (with ``gain``
+    the RMSNorm gain's gradient as dgamma), the backward workspace and its
+    layout."""
     flags = (bd.VDN_VDA_EPILOGUE if epilogue else 0) | (bd.VDN_VDA_DECAY_BRIDGE if bridge else 0) \
         | (bd.VDN_VDA_QUERY_L2 if query_l2 else 0)
     desc = bd.make_desc(w.B, w.H, w.T, w.grid_h, w.grid_w, w.d, w.L, w.chunk, w.dtype, epilogue, l2_eps=l2_eps,
@@ -125,9 +126,10 @@ def run_backward(L, x: dict, w: synth.Workload, dy: np.ndarray, fwd_ws: np.ndarr
     assert L.vdn_vda_backward_workspace_layout(ctypes.byref(desc), ctypes.byref(lay)) == bd.VDN_OK
     dq = np.zeros_like(a["q"])
     dgate = np.zeros_like(dy) if epilogue else None
+    dgamma = np.full(w.d, np.nan, np.float32) if gain else None
     st = L.vdn_vda_backward_readout(ctypes.byref(desc), _ptr(a["q"]), _ptr(a["gate"]) if epilogue else None,
                                     _ptr(rw), _ptr(a["alpha"]), _ptr(dy), _ptr(fwd_ws), fwd_ws.size, _ptr(dq),
-                                    _ptr(dgate), _ptr(bws), bws.size, None)
+                                    _ptr(dgate), _ptr(dgamma), _ptr(bws), bws.size, None)
     assert st == bd.VDN_OK, L.vdn_vda_status_string(st)
     dalpha = np.zeros((w.B, w.T, w.H, w.d), np.float32)
     st = L.vdn_vda_backward_scan(ctypes.byref(desc), _ptr(a["alpha"]), _ptr(fwd_ws), fwd_ws.size, _ptr(dalpha),
@@ -140,7 +142,7 @@ def run_backward(L, x: dict, w: synth.Workload, dy: np.ndarray, fwd_ws: np.ndarr
                                  _ptr(bws), bws.size, None)
     assert st == bd.VDN_OK, L.vdn_vda_status_string(st)
     return dict(dq=dq, dgate=dgate, dalpha=dalpha, dk=grads[0], dv=grads[1], dbeta=grads[2], dk_text=grads[3],
-                dv_text=grads[4], dbeta_text=grads[5]), bws, lay
+                dv_text=grads[4], dbeta_text=grads[5], dgamma=dgamma), bws, lay
 
 
 def section(ws: np.ndarray, off: int, shape, dtype="f32") -> np.ndarray:

@@ -47,6 +47,8 @@ class Prob:
     epilogue: bool = True
     gamma: bool = False
     bridge: bool = False
+    dgain: bool = False   # the backward readout also forms the gain's gradient
+    Du: int = 0           # the caller's head width where it lies between the built ones (D is then the built one)
 
     @property
     def U(self):
@@ -478,11 +480,44 @@ def model_prep(p: Prob, r: Report):
     r.ptr("prep_l2", "q", S["q"], 0, rows * D * p.esz)
 
 
+def model_copy_rows(r: Report, src, src_size, dst, dst_size, src_row, dst_row, copy, rows):
+    """copy_rows (vda_pad.hip): thread i of rows * dst_row / 16 writes 16 bytes
+    at 16 i and, for chunk c = i % (dst_row / 16) < copy / 16 of row
+    r = i / (dst_row / 16), reads 16 bytes at src_row r + 16 c."""
+    ss, ds, nc = src_row // 16, dst_row // 16, copy // 16
+    assert src_row % 16 == 0 and dst_row % 16 == 0 and copy % 16 == 0 and nc <= ds and nc <= ss
+    n = rows * ds
+    if n == 0:
+        return
+    r.ptr("copy_rows", dst, dst_size, np.array([0]), np.array([n * 16]))
+    if nc:
+        r.ptr("copy_rows", src, src_size, np.array([0]), np.array([((rows - 1) * ss + nc - 1) * 16 + 16]))
+
+
 def model_forward(p: Prob, prep: bool = False) -> Report:
-    """Every kernel of vdn_vda_forward (and vdn_vda_prepare) for one problem."""
+    """Every kernel of vdn_vda_forward (and vdn_vda_prepare) for one problem.
+    With Du set (a width between the built ones) the pipeline's kernels run at
+    p.D on zero-padded copies in the workspace: the caller's q, k, v, gate,
+    alpha and text tensors (width Du) are copied in and the output copied back."""
     r = Report()
     if prep:
         model_prep(p, r)
+    if p.Du and p.Du != p.D:
+        S = sizes(p)  # the padded copies
+        tok, trows = p.B * p.T * p.U * p.H, p.B * p.L * p.H
+        ub, pb = p.Du * p.esz, p.D * p.esz
+        for x in ("q", "k", "v") + (("gate",) if p.epilogue else ()):
+            model_copy_rows(r, "caller " + x, tok * ub, "padded " + x, S[x], ub, pb, ub, tok)
+        model_copy_rows(r, "caller alpha", p.B * p.T * p.H * p.Du * 4, "padded alpha", S["alpha"], p.Du * 4,
+                        p.D * 4, p.Du * 4, p.B * p.T * p.H)
+        if p.L:
+            for x in ("k_text", "v_text"):
+                model_copy_rows(r, "caller " + x, trows * ub, "padded " + x, S[x], ub, pb, ub, trows)
+        if p.epilogue:  # pad_gain: one workgroup, thread j < D writes dst[j], reads w[j] for j < Du
+            r.ptr("pad_gain", "padded rms", S["rms"], np.arange(p.D) * 4, np.arange(p.D) * 4 + 4)
+            if p.gamma:
+                r.ptr("pad_gain", "caller rms", p.Du * 4, np.arange(p.Du) * 4, np.arange(p.Du) * 4 + 4)
+        model_copy_rows(r, "padded out", S["out"], "caller out", tok * ub, pb, ub, ub, tok)
     model_gram(p, r)
     model_solve(p, r)
     model_scan(p, r)
@@ -510,7 +545,8 @@ def bwd_sizes(p: Prob) -> dict:
              dalpha=p.B * p.T * p.H * p.D * 4, rstates_t=S["rstates"], dsq=heads * p.T * dd,
              dF=heads * p.nc * dd, dR=heads * p.nc * dd, dST=heads * dd, lam_final=heads * 2 * dd,
              states_f=heads * (p.T + 2) * dd, states_r=heads * (p.T + 2) * dd,
-             gmats=heads * (p.T + 1) * 5 * max(p.D, 32) * p.D * 2)
+             gmats=heads * (p.T + 1) * 5 * max(p.D, 32) * p.D * 2,
+             gain=p.B * p.T * p.H * p.D * 4, dgamma=p.D * 4)
     for n in ("lam_f", "lam_r", "dA", "dB", "p32", "M", "dPinv", "tmp"):
         S[n] = heads * (p.T + 1) * dd
     return S
@@ -592,6 +628,18 @@ def model_readout_bwd(p: Prob, r: Report, S):
     r.rsrc("readout_bwd", "q", S["q"], fbase, n, max(fetch_max, qc_max), 16)
     for buf in ("gate", "dy", "dout", "dgate", "dq"):
         r.rsrc("readout_bwd", buf, S[buf], fbase, n, row_max, 16)
+    if p.dgain:
+        # readout_bwd_gain_bf16: threads tid < D store row blockIdx.x of the
+        # per-(frame, head) sums; gain_grad_sum: one workgroup of 1024 threads,
+        # thread (s, j) reading rows s, s + 1024 / D, ... < B T H, and dgamma[j]
+        r.ptr("readout_bwd", "gain", S["gain"], blk * D * 4, blk * D * 4 + D * 4)
+        rows = p.B * T * H
+        sl = np.arange(1024) // D
+        j = np.arange(1024) % D
+        last = sl + ((rows - 1 - sl) // (1024 // D)) * (1024 // D)
+        live = sl < rows
+        r.ptr("gain_grad_sum", "gain", S["gain"], (sl[live] * D + j[live]) * 4, (last[live] * D + j[live]) * 4 + 4)
+        r.ptr("gain_grad_sum", "dgamma", S["dgamma"], j[:D] * 4, j[:D] * 4 + 4)
 
 
 def model_gram_plain(p: Prob, r: Report, S):

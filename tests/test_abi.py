@@ -235,15 +235,15 @@ def test_backward_readout_argument_errors_before_launch():
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert L.d_state_q - L.d_out >= desc.B * desc.T * 48 * 84 * desc.H * desc.d_v * 2
     assert L.total - L.d_state_q >= desc.B * desc.H * desc.T * desc.d_v * desc.d_k * 4
-    names = ["q", "gate", "rms", "alpha", "dy", "fws", "dq", "dgate", "ws"]
+    names = ["q", "gate", "rms", "alpha", "dy", "fws", "dq", "dgate", "drms", "ws"]
     base = {n: A16 + 0x1000000 * i for i, n in enumerate(names)}
 
     def call(d=desc, fwb=fw, bwb=bw, **over):
-        p = dict(base, rms=0)
+        p = dict(base, rms=0, drms=0)
         p.update(over)
         P = [ctypes.c_void_p(p[n]) if p[n] else None for n in names]
         return lib.vdn_vda_backward_readout(ctypes.byref(d), P[0], P[1], P[2], P[3], P[4], P[5], fwb,
-                                            P[6], P[7], P[8], bwb, None)
+                                            P[6], P[7], P[8], P[9], bwb, None)
 
     assert call(q=0) == bd.VDN_ERR_INVALID_ARG
     assert call(dy=0) == bd.VDN_ERR_INVALID_ARG
@@ -257,9 +257,12 @@ def test_backward_readout_argument_errors_before_launch():
     assert call(ws=base["ws"] + 16) == bd.VDN_ERR_ALIGNMENT
     assert call(d=good(dtype="f32")) == bd.VDN_ERR_UNSUPPORTED
     assert call(d=good(flags=bd.VDN_VDA_QUERY_L2)) == bd.VDN_ERR_UNSUPPORTED   # the raw query needs the epilogue
+    # the gain's gradient: 4-byte aligned, and only with the epilogue
+    assert call(drms=base["drms"] + 2) == bd.VDN_ERR_ALIGNMENT
     # without the epilogue the gate is not needed
     raw = good(epilogue=False)
     assert call(d=raw, gate=0, dgate=0, q=0) == bd.VDN_ERR_INVALID_ARG  # (q still is)
+    assert call(d=raw, gate=0, dgate=0, drms=base["drms"]) == bd.VDN_ERR_INVALID_ARG  # no gain without it
 
 
 def test_backward_gram_argument_errors_before_launch():
@@ -426,21 +429,24 @@ def test_backward_rejects_overlapping_buffers():
     desc = good()
     fw = bd.workspace_bytes(desc)
     bw = bd.backward_workspace_bytes(desc)
-    names = ["q", "gate", "rms", "alpha", "dy", "fws", "dq", "dgate", "ws"]
+    names = ["q", "gate", "rms", "alpha", "dy", "fws", "dq", "dgate", "drms", "ws"]
     base = {n: A16 + (1 << 34) * i for i, n in enumerate(names)}
     xbytes = 60 * 4032 * 24 * 128 * 2
 
     def call(**over):
-        p = dict(base, rms=0)
+        p = dict(base, rms=0, drms=0)
         p.update(over)
         P = [ctypes.c_void_p(p[n]) if p[n] else None for n in names]
         return lib.vdn_vda_backward_readout(ctypes.byref(desc), P[0], P[1], P[2], P[3], P[4], P[5], fw,
-                                            P[6], P[7], P[8], bw, None)
+                                            P[6], P[7], P[8], P[9], bw, None)
 
     assert call(dq=base["q"] + 4096) == bd.VDN_ERR_INVALID_ARG              # dq inside q
     assert call(dgate=base["dq"] + xbytes - 4096) == bd.VDN_ERR_INVALID_ARG  # two outputs
     assert call(ws=base["fws"] + 256) == bd.VDN_ERR_INVALID_ARG            # workspace over the forward's
     assert call(dq=base["ws"] + bw - 4096) == bd.VDN_ERR_INVALID_ARG        # dq over the workspace's end
+    assert call(drms=base["dy"] + 64) == bd.VDN_ERR_INVALID_ARG              # the gain's gradient inside dy
+    assert call(drms=base["ws"] + bw - 256) == bd.VDN_ERR_INVALID_ARG        # ... over the workspace's end
+    assert call(drms=base["rms"], rms=base["rms"] + 256) == bd.VDN_ERR_INVALID_ARG  # ... over the gain
     snames = ["alpha", "fws", "dalpha", "ws"]
     sb = {n: A16 + (1 << 34) * i for i, n in enumerate(snames)}
 

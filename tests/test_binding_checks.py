@@ -175,7 +175,7 @@ def test_backward_stages_accept_and_refuse(lib):
     gout = tuple(torch.empty_like(d[k]) for k in ("k", "v", "beta", "k_text", "v_text", "beta_text"))
     rw = torch.ones(w.d, dtype=torch.float32)
     bd.backward_readout(d["q"], d["gate"], rw, d["alpha"], dy, fws, grid=grid, n_text=w.L, chunk=w.chunk, dq=dq,
-                        dgate=dg, workspace=bws)
+                        dgate=dg, workspace=bws, d_rms_weight=torch.empty(w.d, dtype=torch.float32))
     bd.backward_scan(d["alpha"], fws, bws, shape=(w.B, w.T, w.H, w.d), grid=grid, n_text=w.L, chunk=w.chunk,
                      dalpha=dalpha)
     bd.backward_gram(d["k"], d["v"], d["beta"], d["k_text"], d["v_text"], d["beta_text"], bws, grid=grid,
@@ -193,6 +193,12 @@ def test_backward_stages_accept_and_refuse(lib):
                                     dq=dq[:, 1:].contiguous()),
         lambda: bd.backward_readout(d["q"], d["gate"], None, d["alpha"], dy, fws.float(), grid=grid, n_text=w.L),
         lambda: bd.backward_readout(d["q"], d["gate"], None, d["alpha"], dy, fws, grid=(1, 1), n_text=w.L),
+        lambda: bd.backward_readout(d["q"], d["gate"], None, d["alpha"], dy, fws, grid=grid, n_text=w.L,
+                                    d_rms_weight=torch.empty(w.d + 1, dtype=torch.float32)),
+        lambda: bd.backward_readout(d["q"], d["gate"], None, d["alpha"], dy, fws, grid=grid, n_text=w.L,
+                                    d_rms_weight=torch.empty(w.d, dtype=torch.bfloat16)),
+        lambda: bd.backward_readout(d["q"], None, None, d["alpha"], dy, fws, grid=grid, n_text=w.L, epilogue=False,
+                                    d_rms_weight=torch.empty(w.d, dtype=torch.float32)),
         lambda: bd.backward_scan(d["alpha"], fws, bws, shape=(w.B, w.T, w.H, w.d), grid=grid,
                                  dalpha=dalpha[:, 1:].contiguous()),
         lambda: bd.backward_scan(d["alpha"].to(torch.bfloat16), fws, bws, shape=(w.B, w.T, w.H, w.d), grid=grid),

@@ -251,7 +251,7 @@ import test_gpu_backward as GB  # noqa: E402
 from oracle import vda_grad  # noqa: E402
 
 BWD = ["bwd_128", "bwd_128_raw", "bwd_64_ragged", "bwd_32_bridge", "bwd_64_bridge", "bwd_16_chunk3",
-       "bwd_64_no_text", "bwd_128_ql2", "bwd_16_ql2", "bwd_T1", "bwd_T2", "bwd_B2_chunk3"]
+       "bwd_64_no_text", "bwd_128_ql2", "bwd_16_ql2", "bwd_T1", "bwd_T2", "bwd_B2_chunk3", "bwd_128_gain", "bwd_16"]
 
 
 @pytest.mark.parametrize("name", BWD)
@@ -265,11 +265,13 @@ def test_backward_matches_oracle(lib, name):
     rw = np.random.default_rng(5).uniform(0.5, 1.5, w.d) if case.get("gain") else None
     _, fws, _ = S.run_forward(lib, x, w, epilogue=epi, rms_weight=rw, bridge=bridge, query_l2=ql2)
     got, bws, lay = S.run_backward(lib, x, w, dy, fws, epilogue=epi, rms_weight=rw, bridge=bridge, query_l2=ql2,
-                                   l2_eps=GB.L2_EPS)
+                                   l2_eps=GB.L2_EPS, gain=epi)
     f = G.oracle_view({k: x[k] for k in ("q", "k", "v", "beta", "k_text", "v_text", "beta_text", "gate")}, w)
+    # the gain's gradient is formed with the epilogue, at a gain of ones when none is given
+    gain = rw if rw is not None else (np.ones(w.d) if epi else None)
     ref = vda_grad.backward(f["q"], f["k"], f["v"], x["alpha"].astype(np.float64), f["beta"], f["k_text"],
                             f["v_text"], f["beta_text"], G.oracle_view({"dy": dy}, w)["dy"],
-                            gate=f["gate"] if epi else None, rms_weight=rw, chunk=w.chunk, bridge=bridge,
+                            gate=f["gate"] if epi else None, rms_weight=gain, chunk=w.chunk, bridge=bridge,
                             query_l2=GB.L2_EPS if ql2 else None)
     B, H, T, U, d, L = w.B, w.H, w.T, w.U, w.d, w.L
     nc = -(-T // w.chunk)
@@ -302,6 +304,7 @@ def test_backward_matches_oracle(lib, name):
     }
     if epi:
         errs["dgate"] = G.slice_rel_err(S.to_f64(got["dgate"]), ref["dgate"])
+        errs["dgamma"] = GB._rel(got["dgamma"].astype(np.float64), ref["dgamma"])
     if L:
         txt = lambda a: a.reshape((B, 1) + a.shape[1:] + ((1,) if a.ndim == 3 else ()))
         errs.update({"dk_text": G.slice_rel_err(txt(S.to_f64(got["dk_text"])), txt(ref["dk_txt"])),
@@ -313,6 +316,28 @@ def test_backward_matches_oracle(lib, name):
     assert np.abs(dA[:, :, [0, T - 1]]).max() == 0 and np.abs(dB[:, :, [0, T - 1]]).max() == 0
     for k in ("dk", "dv", "dbeta"):
         assert np.abs(S.to_f64(got[k])[:, [0, T - 1]]).max() == 0, k
+
+
+@pytest.mark.parametrize("name", ["bwd_128_gain", "bwd_16", "bwd_64_ql2_gain"])
+def test_gain_gradient_changes_nothing_else(lib, name):
+    """The readout variant that also forms the gain's gradient leaves dq, dgate
+    and every later gradient bit for bit as the variant without, and gives the
+    same gradient on a second call."""
+    case = GB.CASES[name]
+    w, bridge, ql2 = case["w"], case.get("bridge", False), case.get("query_l2", False)
+    x = synth.make_inputs(w)
+    if ql2:
+        GB._raw_queries(x, w)
+    dy = GB._dy(w)
+    rw = np.random.default_rng(5).uniform(0.5, 1.5, w.d)
+    _, fws, _ = S.run_forward(lib, x, w, epilogue=True, rms_weight=rw, bridge=bridge, query_l2=ql2)
+    runs = [S.run_backward(lib, x, w, dy, fws, epilogue=True, rms_weight=rw, bridge=bridge, query_l2=ql2,
+                           l2_eps=GB.L2_EPS, gain=g)[0] for g in (False, True, True)]
+    for k, v in runs[0].items():
+        if v is not None:
+            assert np.array_equal(v.view(np.uint8), runs[1][k].view(np.uint8)), k
+    assert np.array_equal(runs[1]["dgamma"], runs[2]["dgamma"])
+    assert np.isfinite(runs[1]["dgamma"]).all()
 
 
 # ---------------------------------------------------------------------------

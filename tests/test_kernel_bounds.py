@@ -92,7 +92,8 @@ def test_backward_kernels_stay_in_bounds(name, w, flags):
     checked = 0
     for epi in (flags.get("epilogue", True), not flags.get("epilogue", True)):
         for bridge in (flags.get("bridge", False), True):
-            r = KB.model_backward(_prob(w, epilogue=epi, bridge=bridge, gamma=flags.get("gamma", False) and epi))
+            r = KB.model_backward(_prob(w, epilogue=epi, bridge=bridge, gamma=flags.get("gamma", False) and epi,
+                                        dgain=epi))
             assert not r.errors, (name, epi, bridge, r.errors[:5])
             checked += r.checked
     assert checked > 0
@@ -114,10 +115,11 @@ def test_backward_model_catches_planted_mistakes():
     """Each workspace part one slot short is reported by the kernel that
     addresses its last slot."""
     w = synth.WORKLOADS["768p_bf16"].scaled(name="m", H=2, T=12, grid_h=5, grid_w=7, L=8)
-    p = _prob(w, bridge=True)
+    p = _prob(w, bridge=True, dgain=True)
     dd = p.D * p.D * 4
     for part, short in (("states_r", dd), ("lam_f", dd), ("dsq", dd), ("dF", dd), ("lam_final", dd),
-                        ("gmats", 5 * p.D * p.D * 2), ("rstates_t", 16), ("dout", 2), ("p32", dd), ("tmp", dd)):
+                        ("gmats", 5 * p.D * p.D * 2), ("rstates_t", 16), ("dout", 2), ("p32", dd), ("tmp", dd),
+                        ("gain", 4), ("dgamma", 4)):
         S = KB.bwd_sizes(p)
         S[part] -= short
         r = KB.Report()
