@@ -475,12 +475,12 @@ __global__ __launch_bounds__(256, 1) void readout_bwd_bf16(
   }
 }
 
-// dgamma[j] = sum over the rows of GP [rows][D] (one row per (batch, frame,
-// head)): 1024 threads, thread (s, j) adding rows s, s + S, ... in order, then
-// the S partial sums added in order.
+// dgamma[j] = scale * the sum over the rows of GP [rows][D] (one row per
+// (batch, frame, head)) for j < n: 1024 threads, thread (s, j) adding rows
+// s, s + S, ... in order, then the S partial sums added in order.
 template <int D>
 __global__ __launch_bounds__(1024) void gain_grad_sum(const float* __restrict__ GP, float* __restrict__ dgamma,
-                                                      int rows) {
+                                                      int rows, int n, float scale) {
   constexpr int S = 1024 / D;
   __shared__ float part[1024];
   const int tid = threadIdx.x, j = tid % D, sl = tid / D;
@@ -488,10 +488,10 @@ __global__ __launch_bounds__(1024) void gain_grad_sum(const float* __restrict__ 
   for (int r = sl; r < rows; r += S) v += GP[(size_t)r * D + j];
   part[tid] = v;
   __syncthreads();
-  if (tid < D) {
+  if (tid < n) {
     float a = part[tid];
     for (int k = 1; k < S; ++k) a += part[k * D + tid];
-    dgamma[tid] = a;
+    dgamma[tid] = a * scale;
   }
 }
 
@@ -499,7 +499,8 @@ template <int D>
 hipError_t backward_readout_d(const Problem& p, const void* q, const void* gate, const float* rms_weight,
                               const void* dy, const void* rstates, const float* s_text, const float* fwd, const float* rev,
                               const float* alpha, void* rstates_t, void* dout, void* dq, void* dgate,
-                              float* dsq, float* gain_part, float* dgamma, hipStream_t s) {
+                              float* dsq, float* gain_part, float* dgamma, int gain_n, float gain_scale,
+                              hipStream_t s) {
   hipLaunchKernelGGL(pack_states_t<D>, dim3((unsigned)(p.B * p.H * (p.nc + 1))), dim3(256), 0, s, s_text, fwd,
                      rev, alpha, static_cast<uint4*>(rstates_t), p.nc, p.T, p.H, p.C, p.bridge ? 1 : 0);
   hipError_t e = hipGetLastError();
@@ -530,7 +531,7 @@ hipError_t backward_readout_d(const Problem& p, const void* q, const void* gate,
     if (e != hipSuccess) return e;
     if (dgamma) {
       hipLaunchKernelGGL(gain_grad_sum<D>, dim3(1), dim3(1024), 0, s, static_cast<const float*>(gain_part), dgamma,
-                         (int)grid);
+                         (int)grid, gain_n, gain_scale);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -882,13 +883,14 @@ __global__ __launch_bounds__(256) void text_adjoint(const float* __restrict__ dS
 hipError_t launch_backward_readout(const Problem& p, const void* q, const void* gate, const float* rms_weight,
                                    const void* dy, const void* rstates, const float* s_text, const float* fwd, const float* rev,
                                    const float* alpha, void* rstates_t, void* dout, void* dq, void* dgate,
-                                   float* dsq, float* gain_part, float* dgamma, hipStream_t s) {
-  if (!p.bf16 || (dgamma && (!p.epilogue || !gain_part))) return hipErrorInvalidValue;
+                                   float* dsq, float* gain_part, float* dgamma, int gain_n, float gain_scale,
+                                   hipStream_t s) {
+  if (!p.bf16 || (dgamma && (!p.epilogue || !gain_part || gain_n < 1 || gain_n > p.D))) return hipErrorInvalidValue;
   switch (p.D) {
-    case 16: return backward_readout_d<16>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, gain_part, dgamma, s);
-    case 32: return backward_readout_d<32>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, gain_part, dgamma, s);
-    case 64: return backward_readout_d<64>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, gain_part, dgamma, s);
-    case 128: return backward_readout_d<128>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, gain_part, dgamma, s);
+    case 16: return backward_readout_d<16>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, gain_part, dgamma, gain_n, gain_scale, s);
+    case 32: return backward_readout_d<32>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, gain_part, dgamma, gain_n, gain_scale, s);
+    case 64: return backward_readout_d<64>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, gain_part, dgamma, gain_n, gain_scale, s);
+    case 128: return backward_readout_d<128>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, gain_part, dgamma, gain_n, gain_scale, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -96,7 +96,8 @@ __device__ __forceinline__ void lds_barrier() {
 // launch plumbing
 // ---------------------------------------------------------------------------
 struct Problem {
-  int B, H, T, U, D, L, C;  // d_k = d_v = D; C = frames per chunk
+  int B, H, T, U, D, L, C;  // D: the kernels' head width; C = frames per chunk
+  int Du;                   // the caller's d_k = d_v (D rounded up to 16, 32, 64 or 128)
   int nc;                   // number of chunks
   bool bf16;
   bool epilogue;
@@ -108,7 +109,11 @@ struct Problem {
 
 // Workspace offsets in bytes (see vdn_vda_layout).
 struct Layout {
-  size_t stats, pinv, s_text, fwd, rev, rstates, chunk_m, chunk_j, total;
+  size_t stats, pinv, s_text, fwd, rev, rstates, chunk_m, chunk_j;
+  // widths between the built ones (Du < D): the inputs copied with their
+  // channels zero-padded to D, the padded output, the padded gain
+  size_t pad_q, pad_k, pad_v, pad_gate, pad_out, pad_alpha, pad_k_text, pad_v_text, pad_gain;
+  size_t total;
 };
 Layout make_layout(const Problem& p);
 
@@ -163,11 +168,12 @@ hipError_t launch_readout(const Problem& p, const void* q, const void* gate, con
 // dgate <- the gate's adjoint, else do = dy; dq <- S_q^T do; dsq [B, H, T, d, d]
 // <- do_t^T q_t.  rstates, s_text, fwd, rev: the forward's workspace sections.
 // With dgamma (the epilogue only): gain_part [B T H, d] <- per-(frame, head)
-// sums, then dgamma [d] <- their sum.
+// sums, then dgamma[j] <- gain_scale * their sum, for j < gain_n.
 hipError_t launch_backward_readout(const Problem& p, const void* q, const void* gate, const float* rms_weight,
                                    const void* dy, const void* rstates, const float* s_text, const float* fwd,
                                    const float* rev, const float* alpha, void* rstates_t, void* dout, void* dq,
-                                   void* dgate, float* dsq, float* gain_part, float* dgamma, hipStream_t s);
+                                   void* dgate, float* dsq, float* gain_part, float* dgamma, int gain_n,
+                                   float gain_scale, hipStream_t s);
 // Second stage of the backward pass: buffers (float32 unless noted).
 struct BwdScanBuffers {
   const float* stats;   // forward workspace: [B, H, T+1, 2d, d]
@@ -204,6 +210,12 @@ hipError_t launch_gates(const Problem& p, int d_model, const void* x, const void
                         void* gate, void* beta, float* alpha, float* partial, float* xbar, hipStream_t s);
 hipError_t launch_out_proj(const Problem& p, int d_model, const void* o, const void* w_o, const void* y_in, void* y,
                            hipStream_t s);
+// Row copies for the widths between the built ones: dst row r = the first
+// copy_bytes of src row r, zero-filled to dst_row_bytes (all multiples of 16);
+// the padded gain (w or ones) * sqrt(d / D), zero beyond d.
+hipError_t launch_copy_rows(const void* src, size_t src_row_bytes, void* dst, size_t dst_row_bytes,
+                            size_t copy_bytes, size_t rows, hipStream_t s);
+hipError_t launch_pad_gain(const float* w, float* dst, int d, int D, hipStream_t s);
 hipError_t launch_prep(const Problem& p, int grid_h, int grid_w, const void* q, const void* k,
                        const void* v, const float* wk_s, const float* wk_t, const float* wv_s,
                        const float* wv_t, void* q_hat, void* k_hat, void* v_hat, hipStream_t s);

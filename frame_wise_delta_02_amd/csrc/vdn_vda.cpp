@@ -8,6 +8,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "vda_internal.h"
 #include "vdn_vda.h"
 
@@ -95,6 +97,9 @@ bool any_overlap(const Span* outs, size_t n_out, const Span* ins, size_t n_in) {
   return false;
 }
 
+// The built head width a caller's width runs at: 16, 32, 64 or 128.
+int padded_width(int d) { return d <= 16 ? 16 : d <= 32 ? 32 : d <= 64 ? 64 : 128; }
+
 vdn_status check(const vdn_vda_desc* d) {
   if (!d) return VDN_ERR_INVALID_ARG;
   if (d->B < 1 || d->H < 1 || d->T < 1 || d->grid_h < 1 || d->grid_w < 1) return VDN_ERR_INVALID_ARG;
@@ -112,6 +117,8 @@ vdn_status check(const vdn_vda_desc* d) {
   const double U = (double)d->grid_h * d->grid_w;
   const double elems = (double)d->B * d->T * U * d->H * d->d_v;
   if (U > 2147483647.0 || elems > 9.0e15) return VDN_ERR_INVALID_ARG;
+  // the kernels run at the built width D >= d (the offset limits below are theirs)
+  const double D = padded_width(d->d_k);
   if ((double)d->B * d->T * d->H * d->grid_h > 4294967295.0) return VDN_ERR_INVALID_ARG;
   if ((double)d->B * d->n_text * d->H > 9.0e15) return VDN_ERR_INVALID_ARG;
   // the scan launches: up to 16 row blocks per (batch, head, direction, chunk),
@@ -120,20 +127,26 @@ vdn_status check(const vdn_vda_desc* d) {
     return VDN_ERR_INVALID_ARG;
   // the scan's chunk records of one head must stay below 2^31 bytes: steps that
   // record nothing store at offset 2^31, past that buffer
-  if ((double)((d->T + d->chunk - 1) / d->chunk) * d->d_k * d->d_v * 4.0 >= 2147483648.0)
+  if ((double)((d->T + d->chunk - 1) / d->chunk) * D * D * 4.0 >= 2147483648.0)
     return VDN_ERR_INVALID_ARG;
   // a frame's (or the text's) token rows, plus a tile's overhang, are addressed
   // with 32-bit byte offsets
-  if (((double)d->grid_h * d->grid_w + 64.0) * d->H * d->d_v * 4.0 > 4294967295.0) return VDN_ERR_INVALID_ARG;
-  if (((double)d->n_text + 64.0) * d->H * d->d_v * 4.0 > 4294967295.0) return VDN_ERR_INVALID_ARG;
+  if (((double)d->grid_h * d->grid_w + 64.0) * d->H * D * 4.0 > 4294967295.0) return VDN_ERR_INVALID_ARG;
+  if (((double)d->n_text + 64.0) * d->H * D * 4.0 > 4294967295.0) return VDN_ERR_INVALID_ARG;
   // the statistics kernel's register prefetch reads a few tiles of 64 tokens
   // past a frame's last token (zero through the buffer range check); with 640
   // tokens of margin its 32-bit offsets cannot wrap back into the frame
-  if (((double)d->grid_h * d->grid_w + 640.0) * d->H * d->d_v * 2.0 > 4294967295.0) return VDN_ERR_INVALID_ARG;
-  if (((double)d->n_text + 640.0) * d->H * d->d_v * 2.0 > 4294967295.0) return VDN_ERR_INVALID_ARG;
+  if (((double)d->grid_h * d->grid_w + 640.0) * d->H * D * 2.0 > 4294967295.0) return VDN_ERR_INVALID_ARG;
+  if (((double)d->n_text + 640.0) * d->H * D * 2.0 > 4294967295.0) return VDN_ERR_INVALID_ARG;
   if (d->d_k != d->d_v) return VDN_ERR_UNSUPPORTED;
-  if (d->d_k != 16 && d->d_k != 32 && d->d_k != 64 && d->d_k != 128) return VDN_ERR_UNSUPPORTED;
   return VDN_OK;
+}
+
+// The entry points other than the forward pass run at the built widths only.
+vdn_status check_native(const vdn_vda_desc* d) {
+  const vdn_status st = check(d);
+  if (st != VDN_OK) return st;
+  return padded_width(d->d_k) == d->d_k ? VDN_OK : VDN_ERR_UNSUPPORTED;
 }
 
 Problem problem(const vdn_vda_desc* d) {
@@ -142,7 +155,8 @@ Problem problem(const vdn_vda_desc* d) {
   p.H = d->H;
   p.T = d->T;
   p.U = d->grid_h * d->grid_w;
-  p.D = d->d_k;
+  p.D = padded_width(d->d_k);
+  p.Du = d->d_k;
   p.L = d->n_text;
   p.C = d->chunk;
   p.nc = (d->T + d->chunk - 1) / d->chunk;
@@ -189,6 +203,24 @@ Layout make_layout(const Problem& p) {
   o = up(o + heads * 2 * p.nc * dd);
   l.chunk_j = o;
   o = up(o + heads * 2 * p.nc * dd);
+  // the zero-padded copies, at widths between the built ones only
+  const bool pad = p.Du != p.D;
+  const size_t esz = p.bf16 ? 2 : 4;
+  const size_t xb = pad ? (size_t)p.B * p.T * p.U * p.H * p.D * esz : 0;
+  const size_t tb = pad ? (size_t)p.B * p.L * p.H * p.D * esz : 0;
+  auto take = [&](size_t& field, size_t bytes) {
+    field = o;
+    o = up(o + bytes);
+  };
+  take(l.pad_q, xb);
+  take(l.pad_k, xb);
+  take(l.pad_v, xb);
+  take(l.pad_gate, p.epilogue ? xb : 0);
+  take(l.pad_out, xb);
+  take(l.pad_alpha, pad ? (size_t)p.B * p.T * p.H * p.D * 4 : 0);
+  take(l.pad_k_text, tb);
+  take(l.pad_v_text, tb);
+  take(l.pad_gain, pad && p.epilogue ? (size_t)p.D * 4 : 0);
   l.total = o;
   return l;
 }
@@ -200,6 +232,10 @@ struct BwdLayout {
   size_t states_f, states_r, lam_final, p32, M, dPinv, tmp;       // second stage (internal)
   size_t gmats;                                                   // third stage (internal)
   size_t gain;                                                    // first stage (internal)
+  // widths between the built ones: the zero-padded copies of the stages'
+  // inputs and outputs (the forward's workspace holds q, gate, alpha, the gain)
+  size_t pad_dy, pad_dq, pad_dgate, pad_dalpha, pad_k, pad_v, pad_dk, pad_dv, pad_k_text, pad_v_text,
+      pad_dk_text, pad_dv_text;
   size_t total;
 };
 BwdLayout make_bwd_layout(const Problem& p) {
@@ -233,6 +269,13 @@ BwdLayout make_bwd_layout(const Problem& p) {
   take(l.gmats, heads * (p.T + 1) * 5 * (size_t)std::max(p.D, 32) * p.D * 2);
   // the gain gradient's sums per (batch, frame, head), float32 [B T H][d]
   take(l.gain, (size_t)p.B * p.T * p.H * p.D * 4);
+  const bool pad = p.Du != p.D;
+  const size_t xb = pad ? (size_t)p.B * p.T * p.U * p.H * p.D * 2 : 0;
+  const size_t tb = pad ? (size_t)p.B * p.L * p.H * p.D * 2 : 0;
+  for (size_t* f : {&l.pad_dy, &l.pad_dq, &l.pad_dgate}) take(*f, xb);
+  take(l.pad_dalpha, pad ? (size_t)p.B * p.T * p.H * p.D * 4 : 0);
+  for (size_t* f : {&l.pad_k, &l.pad_v, &l.pad_dk, &l.pad_dv}) take(*f, xb);
+  for (size_t* f : {&l.pad_k_text, &l.pad_v_text, &l.pad_dk_text, &l.pad_dv_text}) take(*f, tb);
   l.total = o;
   return l;
 }
@@ -240,7 +283,7 @@ BwdLayout make_bwd_layout(const Problem& p) {
 // The adjacent maps' own checks: bfloat16, a model width that 16-byte rows and
 // 32-bit panel offsets allow.
 vdn_status check_proj(const vdn_vda_desc* d, int32_t d_model) {
-  const vdn_status st = check(d);
+  const vdn_status st = check_native(d);
   if (st != VDN_OK) return st;
   if (d->dtype != VDN_BF16) return VDN_ERR_UNSUPPORTED;
   if (d_model < 8 || d_model % 8) return VDN_ERR_INVALID_ARG;
@@ -306,6 +349,40 @@ vdn_status forward_impl(const vdn_vda_desc* d, const void* q, const void* k, con
   const Layout l = make_layout(p);
 
   char* ws = static_cast<char*>(workspace);
+  hipError_t e = mark(0, stream);
+  // a width between the built ones: the kernels run at p.D on zero-padded
+  // copies (vda_pad.hip), the epilogue with eps d / D and the gain scaled by
+  // sqrt(d / D), and the output's first d channels are copied back
+  const bool pad = p.Du != p.D;
+  Problem pr = p;  // the readout's problem
+  void* out_k = out;
+  if (pad) {
+    const size_t esz = p.bf16 ? 2 : 4;
+    const size_t rows = (size_t)p.B * p.T * p.U * p.H, trows = (size_t)p.B * p.L * p.H;
+    const size_t ub = (size_t)p.Du * esz, pb = (size_t)p.D * esz;
+    auto copy = [&](const void*& src, size_t off, size_t n, size_t srow, size_t drow) {
+      if (e == hipSuccess) e = launch_copy_rows(src, srow, ws + off, drow, srow, n, stream);
+      src = ws + off;
+    };
+    copy(q, l.pad_q, rows, ub, pb);
+    copy(k, l.pad_k, rows, ub, pb);
+    copy(v, l.pad_v, rows, ub, pb);
+    if (p.epilogue) copy(gate, l.pad_gate, rows, ub, pb);
+    const void* a = alpha;
+    copy(a, l.pad_alpha, (size_t)p.B * p.T * p.H, (size_t)p.Du * 4, (size_t)p.D * 4);
+    alpha = static_cast<const float*>(a);
+    if (p.L > 0) {
+      copy(k_text, l.pad_k_text, trows, ub, pb);
+      copy(v_text, l.pad_v_text, trows, ub, pb);
+    }
+    if (p.epilogue) {
+      float* g = reinterpret_cast<float*>(ws + l.pad_gain);
+      if (e == hipSuccess) e = launch_pad_gain(rms_weight, g, p.Du, p.D, stream);
+      rms_weight = g;
+      pr.rms_eps = p.rms_eps * (float)p.Du / (float)p.D;
+    }
+    out_k = ws + l.pad_out;
+  }
   float* stats = reinterpret_cast<float*>(ws + l.stats);
   float* pinv = reinterpret_cast<float*>(ws + l.pinv);
   float* s_text = reinterpret_cast<float*>(ws + l.s_text);
@@ -316,7 +393,6 @@ vdn_status forward_impl(const vdn_vda_desc* d, const void* q, const void* k, con
   float* chunk_j = reinterpret_cast<float*>(ws + l.chunk_j);
 
   const int n_video = p.T > 2 ? p.T - 2 : 0;
-  hipError_t e = mark(0, stream);
   // frame statistics of frames 1..T-2 (anchors are never absorbed) and of the
   // text frame (slot T) in one launch: the short text blocks run last, in the
   // final round of the video blocks
@@ -334,7 +410,12 @@ vdn_status forward_impl(const vdn_vda_desc* d, const void* q, const void* k, con
   if (e == hipSuccess) e = mark(3, stream);
   if (e == hipSuccess) e = launch_gather(p, s_text, fwd, rev, alpha, rstates, stream);
   if (e == hipSuccess) e = mark(4, stream);
-  if (e == hipSuccess) e = launch_readout(p, q, gate, rms_weight, rstates, out, stream);
+  if (e == hipSuccess) e = launch_readout(pr, q, gate, rms_weight, rstates, out_k, stream);
+  if (pad && e == hipSuccess) {
+    const size_t esz = p.bf16 ? 2 : 4;
+    e = launch_copy_rows(out_k, (size_t)p.D * esz, out, (size_t)p.Du * esz, (size_t)p.Du * esz,
+                         (size_t)p.B * p.T * p.U * p.H, stream);
+  }
   if (e == hipSuccess) e = mark(5, stream);
   return e == hipSuccess ? VDN_OK : VDN_ERR_HIP;
 }
@@ -374,7 +455,7 @@ vdn_status vdn_vda_prepare(const vdn_vda_desc* d, const void* q, const void* k, 
                            const float* wk_s, const float* wk_t, const float* wv_s,
                            const float* wv_t, void* q_hat, void* k_hat, void* v_hat,
                            hipStream_t stream) {
-  const vdn_status st = check(d);
+  const vdn_status st = check_native(d);
   if (st != VDN_OK) return st;
   const Problem p = problem(d);
   // under VDN_VDA_QUERY_L2 the query is normalised by the forward pass instead
@@ -492,11 +573,38 @@ vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d, const void* q, const 
   }
   const char* fw = static_cast<const char*>(fwd_workspace);
   char* ws = static_cast<char*>(workspace);
-  const hipError_t e = launch_backward_readout(
-      p, q, gate, rms_weight, dy, fw + fl.rstates, reinterpret_cast<const float*>(fw + fl.s_text),
-      reinterpret_cast<const float*>(fw + fl.fwd), reinterpret_cast<const float*>(fw + fl.rev), alpha,
-      ws + bl.rstates_t, ws + bl.dout, dq, dgate, reinterpret_cast<float*>(ws + bl.dsq),
-      reinterpret_cast<float*>(ws + bl.gain), d_rms_weight, stream);
+  hipError_t e = hipSuccess;
+  // a width between the built ones: the forward's padded q, gate, alpha and
+  // gain, dy padded here, dq and dgate padded then copied back; the gain's
+  // gradient is sqrt(d / D) times the padded gain's (gamma' = gamma sqrt(d / D))
+  Problem pr = p;
+  void *dq_k = dq, *dgate_k = dgate;
+  float gscale = 1.f;
+  const size_t rows = (size_t)p.B * p.T * p.U * p.H, ub = (size_t)p.Du * 2, pb = (size_t)p.D * 2;
+  if (p.Du != p.D) {
+    q = fw + fl.pad_q;
+    alpha = reinterpret_cast<const float*>(fw + fl.pad_alpha);
+    if (epi) {
+      gate = fw + fl.pad_gate;
+      rms_weight = reinterpret_cast<const float*>(fw + fl.pad_gain);
+      pr.rms_eps = p.rms_eps * (float)p.Du / (float)p.D;
+      gscale = std::sqrt((float)p.Du / (float)p.D);
+    }
+    e = launch_copy_rows(dy, ub, ws + bl.pad_dy, pb, ub, rows, stream);
+    dy = ws + bl.pad_dy;
+    dq_k = ws + bl.pad_dq;
+    dgate_k = epi ? ws + bl.pad_dgate : nullptr;
+  }
+  if (e == hipSuccess)
+    e = launch_backward_readout(
+        pr, q, gate, rms_weight, dy, fw + fl.rstates, reinterpret_cast<const float*>(fw + fl.s_text),
+        reinterpret_cast<const float*>(fw + fl.fwd), reinterpret_cast<const float*>(fw + fl.rev), alpha,
+        ws + bl.rstates_t, ws + bl.dout, dq_k, dgate_k, reinterpret_cast<float*>(ws + bl.dsq),
+        reinterpret_cast<float*>(ws + bl.gain), d_rms_weight, p.Du, gscale, stream);
+  if (p.Du != p.D && e == hipSuccess) {
+    e = launch_copy_rows(dq_k, pb, dq, ub, ub, rows, stream);
+    if (epi && e == hipSuccess) e = launch_copy_rows(dgate_k, pb, dgate, ub, ub, rows, stream);
+  }
   return e == hipSuccess ? VDN_OK : VDN_ERR_HIP;
 }
 
@@ -507,9 +615,9 @@ vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha, cons
   if (st != VDN_OK) return st;
   if (d->dtype != VDN_BF16) return VDN_ERR_UNSUPPORTED;
   if (!alpha || !fwd_workspace || !dalpha) return VDN_ERR_INVALID_ARG;
-  // every frame's state is recorded per head through one buffer descriptor
-  if ((double)(d->T + 2) * d->d_k * d->d_v * 4.0 >= 2147483648.0) return VDN_ERR_INVALID_ARG;
   const Problem p = problem(d);
+  // every frame's state is recorded per head through one buffer descriptor
+  if ((double)(d->T + 2) * p.D * p.D * 4.0 >= 2147483648.0) return VDN_ERR_INVALID_ARG;
   const Layout fl = make_layout(p);
   const BwdLayout bl = make_bwd_layout(p);
   if (fwd_workspace_bytes < fl.total) return VDN_ERR_WORKSPACE;
@@ -548,7 +656,16 @@ vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha, cons
   w.s_text = reinterpret_cast<const float*>(fw + fl.s_text);
   w.fwd = reinterpret_cast<const float*>(fw + fl.fwd);
   w.rev = reinterpret_cast<const float*>(fw + fl.rev);
-  return launch_backward_scan(p, w, stream) == hipSuccess ? VDN_OK : VDN_ERR_HIP;
+  const bool pad = p.Du != p.D;  // the forward's padded alpha, dalpha padded then copied back
+  if (pad) {
+    w.alpha = reinterpret_cast<const float*>(fw + fl.pad_alpha);
+    w.dalpha = f(bl.pad_dalpha);
+  }
+  hipError_t e = launch_backward_scan(p, w, stream);
+  if (pad && e == hipSuccess)
+    e = launch_copy_rows(w.dalpha, (size_t)p.D * 4, dalpha, (size_t)p.Du * 4, (size_t)p.Du * 4,
+                         (size_t)p.B * p.T * p.H, stream);
+  return e == hipSuccess ? VDN_OK : VDN_ERR_HIP;
 }
 
 vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const void* v, const void* beta,
@@ -574,7 +691,7 @@ vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const voi
   if (!aligned(workspace, kAlign)) return VDN_ERR_ALIGNMENT;
   // the outputs are written while the inputs are still read
   const size_t tok = (size_t)p.B * p.T * p.U * p.H, ttok = (size_t)p.B * p.L * p.H;
-  const size_t xb = tok * p.D * 2, tb = ttok * p.D * 2;
+  const size_t xb = tok * p.Du * 2, tb = ttok * p.Du * 2;
   const Span ins[] = {{k, xb}, {v, xb}, {beta, tok * 2}, {text ? k_text : nullptr, tb},
                       {text ? v_text : nullptr, tb}, {text ? beta_text : nullptr, ttok * 2},
                       {workspace, workspace_bytes}};
@@ -603,7 +720,40 @@ vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const voi
   w.dk_text = dk_text;
   w.dv_text = dv_text;
   w.dbeta_text = dbeta_text;
-  return launch_backward_gram(p, w, stream) == hipSuccess ? VDN_OK : VDN_ERR_HIP;
+  // a width between the built ones: k, v (and the text's) padded here, dk, dv
+  // padded then copied back (dbeta has no channel axis)
+  hipError_t e = hipSuccess;
+  const bool pad = p.Du != p.D;
+  const size_t ub = (size_t)p.Du * 2, pb = (size_t)p.D * 2;
+  if (pad) {
+    auto in = [&](const void*& x, size_t off, size_t n) {
+      if (e == hipSuccess) e = launch_copy_rows(x, ub, ws + off, pb, ub, n, stream);
+      x = ws + off;
+    };
+    in(w.k, bl.pad_k, tok);
+    in(w.v, bl.pad_v, tok);
+    w.dk = ws + bl.pad_dk;
+    w.dv = ws + bl.pad_dv;
+    if (text) {
+      in(w.k_text, bl.pad_k_text, ttok);
+      in(w.v_text, bl.pad_v_text, ttok);
+      w.dk_text = ws + bl.pad_dk_text;
+      w.dv_text = ws + bl.pad_dv_text;
+    }
+  }
+  if (e == hipSuccess) e = launch_backward_gram(p, w, stream);
+  if (pad) {
+    auto out = [&](const void* src, void* dst, size_t n) {
+      if (e == hipSuccess) e = launch_copy_rows(src, pb, dst, ub, ub, n, stream);
+    };
+    out(w.dk, dk, tok);
+    out(w.dv, dv, tok);
+    if (text) {
+      out(w.dk_text, dk_text, ttok);
+      out(w.dv_text, dv_text, ttok);
+    }
+  }
+  return e == hipSuccess ? VDN_OK : VDN_ERR_HIP;
 }
 
 size_t vdn_vda_gates_workspace_bytes(const vdn_vda_desc* d, int32_t d_model) {
@@ -672,9 +822,9 @@ const char* vdn_vda_status_string(vdn_status s) {
     case VDN_OK: return "VDN_OK";
     case VDN_ERR_INVALID_ARG: return "VDN_ERR_INVALID_ARG: bad descriptor, size, NULL pointer or overlapping buffers";
     case VDN_ERR_UNSUPPORTED:
-      return "VDN_ERR_UNSUPPORTED: valid request not implemented (head widths other than d_k = d_v in "
-             "{16,32,64,128}; float32 in the backward pass and the adjacent maps; the query norm's backward "
-             "without the epilogue)";
+      return "VDN_ERR_UNSUPPORTED: valid request not implemented (d_k != d_v; head widths other than "
+             "16, 32, 64, 128 in the prep and the adjacent maps; float32 in the backward pass and the adjacent maps; "
+             "the query norm's backward without the epilogue)";
     case VDN_ERR_WORKSPACE: return "VDN_ERR_WORKSPACE: workspace missing or too small";
     case VDN_ERR_ALIGNMENT: return "VDN_ERR_ALIGNMENT: pointer misaligned";
     case VDN_ERR_HIP: return "VDN_ERR_HIP: kernel launch failed";

@@ -109,7 +109,8 @@ enum {
 typedef struct {
   int32_t B, H, T;         /* batch, heads, latent frames (T >= 1) */
   int32_t grid_h, grid_w;  /* token grid of a latent frame; U = grid_h * grid_w */
-  int32_t d_k, d_v;        /* head widths: must be equal, one of 16, 32, 64, 128 */
+  int32_t d_k, d_v;        /* head widths: equal, a multiple of 16 up to 128 (see
+                              vdn_vda_validate for which entry points take which) */
   int32_t n_text;          /* L text tokens per batch element (may be 0) */
   int32_t chunk;           /* latent frames per VAE chunk (the pages use 5); >= 1 */
   vdn_dtype dtype;         /* dtype of q, k, v, beta, text tensors, gate and out */
@@ -139,7 +140,13 @@ typedef struct {
  *          runs, for the chunks that end in a record (forward 0..n_c-3,
  *          reverse 2..n_c-1).  J_c float32; M_c float32, or for VDN_BF16 with
  *          d_k >= 32 in the two-plane bfloat16 format of pinv.
- *   n_c = ceil(T / chunk).  Entries a query never reads are left unspecified. */
+ *   n_c = ceil(T / chunk).  Entries a query never reads are left unspecified.
+ *   At a head width d between the built ones (48, 80, 96, 112) every section
+ *   is laid out for the built width D the kernels run at (64 for 48, else 128)
+ *   in place of d_k and d_v: the matrices are D x D with their leading d x d
+ *   blocks those of the method and zeros elsewhere (the inverse's identity
+ *   outside the block); the workspace also holds the zero-padded copies of the
+ *   inputs and of the output (internal sections). */
 typedef struct {
   size_t stats, pinv, s_text, fwd, rev, readout_states, chunk_m, chunk_j, total;
 } vdn_vda_layout;
@@ -150,8 +157,21 @@ typedef struct {
  * (a frame's or the text's token rows plus a tile's overhang) and
  * (U + 640) H d 2 and (L + 640) H d 2 bytes (the statistics kernel's prefetch
  * past the last token) below 4 GiB, and one head's chunk records below 2^31
- * bytes.  VDN_ERR_INVALID_ARG when a limit fails, VDN_ERR_UNSUPPORTED for a
- * width other than 16, 32, 64, 128 or d_k != d_v. */
+ * bytes, where d is the built width the kernels run at (the caller's width,
+ * or the next of 16, 32, 64, 128).  VDN_ERR_INVALID_ARG when a limit fails or
+ * a width is not a multiple of 16 in 16 .. 128, VDN_ERR_UNSUPPORTED for
+ * d_k != d_v.  VDN_OK means the forward pass (vdn_vda_forward, _timed,
+ * _noalloc) takes the descriptor.  Widths 48, 80, 96 and 112 run only there:
+ * the kernels are built for 16, 32, 64 and 128 (matrix-core tiles of 16 and
+ * 32), and the forward pass runs them at the next built width D on copies of
+ * the inputs zero-padded to D channels, in its workspace, then copies the
+ * output's d channels back (zero channels leave every result unchanged; the
+ * epilogue takes rms_eps d / D and the gain scaled by sqrt(d / D), which
+ * gives the same RMSNorm over the d true channels).  The backward pass takes
+ * them the same way: it reads the forward's padded copies from the forward's
+ * workspace, pads dy, k and v in its own, and copies every gradient's d
+ * channels back (the gain's gradient scaled by sqrt(d / D)).  vdn_vda_prepare
+ * and the adjacent maps return VDN_ERR_UNSUPPORTED for them. */
 vdn_status vdn_vda_validate(const vdn_vda_desc* d);
 
 /* Workspace bytes vdn_vda_forward needs for `d`; 0 if `d` is invalid. */
@@ -173,7 +193,8 @@ vdn_status vdn_vda_workspace_layout(const vdn_vda_desc* d, vdn_vda_layout* out);
  * out of place (must not alias the inputs).  Weights as in the header comment.
  * With VDN_VDA_QUERY_L2 in d->flags q and q_hat are ignored (may be NULL) and
  * the forward pass normalises the query instead.
- * Errors: VDN_ERR_INVALID_ARG (descriptor, NULL pointer), VDN_ERR_ALIGNMENT,
+ * Errors: VDN_ERR_INVALID_ARG (descriptor, NULL pointer), VDN_ERR_UNSUPPORTED
+ * (a head width other than 16, 32, 64, 128), VDN_ERR_ALIGNMENT,
  * VDN_ERR_HIP.
  */
 vdn_status vdn_vda_prepare(const vdn_vda_desc* d,
@@ -324,7 +345,7 @@ vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d,
  * S_T.  With VDN_VDA_DECAY_BRIDGE a query chunk's adjoint reaches the records
  * (and S_T / 2) column-scaled by its bridge's alpha products, and dalpha adds
  * the bridge's own term (frames of the bridged chunks, anchors included).
- * Supported: VDN_BF16 (else VDN_ERR_UNSUPPORTED); (T + 2) d_k d_v 4 < 2^31.  Errors as
+ * Supported: VDN_BF16 (else VDN_ERR_UNSUPPORTED); (T + 2) D D 4 < 2^31 (D the built width).  Errors as
  * vdn_vda_backward_readout.  Asynchronous on `stream`.
  */
 vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha,
@@ -376,8 +397,8 @@ vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const voi
  * come from one bfloat16 matrix-core product (float32 accumulation, the
  * sigmoid applied before rounding).  The workspace (vdn_vda_gates_workspace_bytes)
  * holds the frames' token sums.  d_model a multiple of 8; the descriptor's
- * n_text, chunk and flags are ignored; VDN_BF16 only (else
- * VDN_ERR_UNSUPPORTED).  Outputs must overlap neither each other, the inputs
+ * n_text, chunk and flags are ignored; VDN_BF16 at d = 16, 32, 64, 128 only
+ * (else VDN_ERR_UNSUPPORTED).  Outputs must overlap neither each other, the inputs
  * nor the workspace.  Errors: VDN_ERR_INVALID_ARG (NULL pointer, d_model,
  * overlap), VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE, VDN_ERR_ALIGNMENT (16 B;
  * 2 B for beta; 256 B for the workspace), VDN_ERR_HIP.  Asynchronous on `stream`.

@@ -31,6 +31,7 @@ import numpy as np  # noqa: E402
 import test_gpu_adjacent as GA  # noqa: E402
 import test_gpu_backward as GB  # noqa: E402
 import test_gpu_parity as P  # noqa: E402
+import test_gpu_widths as GW  # noqa: E402
 from cpu_build import sim as S  # noqa: E402
 from frame_wise_delta_02_amd import synth  # noqa: E402
 
@@ -47,6 +48,9 @@ FORWARD_QUICK = ("d32_bf16", "d16_bf16", "d32_f32", "no_text_bf16", "T1_bf16", "
 BACKWARD_QUICK = ("bwd_64_ragged", "bwd_32_bridge", "bwd_16_chunk3", "bwd_64_no_text", "bwd_16_ql2", "bwd_T1",
                   "bwd_16", "bwd_128_gain")
 ADJACENT_QUICK = ("adj_small", "adj_d16", "adj_tiny")
+PADDED = ("d48_bf16", "d80_bf16", "d96_bf16_chunk3", "d112_bf16", "d48_f32", "d112_f32", "d80_no_text_bf16",
+          "d48_T1_bf16", "d96_batch2_bf16")
+PADDED_QUICK = ("d48_f32", "d80_no_text_bf16", "d48_T1_bf16")
 
 
 def cases(full, tsan=False):
@@ -69,11 +73,34 @@ def cases(full, tsan=False):
         for mode in ("frames", "chunks", "bridge"):
             out.append((f"forward {name} {mode}", forward(name, mode)))
 
+    # widths between the built ones: the zero-padded copies in, the output's
+    # channels back; with the gain, the raw readout, the bridge
+    def padded(name, mode):
+        def run(L):
+            w = GW.CASES[name]
+            x = synth.make_inputs(w)
+            if mode == "bridge":
+                o, _, _ = S.run_forward(L, x, w, epilogue=False, bridge=True)
+            else:
+                o, _, _ = S.run_forward(L, x, w, epilogue=True, scan=mode, rms_weight=np.linspace(0.5, 1.5, w.d))
+            finite(o)
+        return run
+
+    for name in (PADDED if full else PADDED_QUICK):
+        for mode in ("frames", "chunks", "bridge"):
+            out.append((f"forward {name} {mode}", padded(name, mode)))
+
     def noalloc(L):
         w = P.EDGE["ragged_bf16_128" if full else "d32_bf16"]
         finite(S.run_forward_noalloc(L, synth.make_inputs(w), w))
 
     out.append(("forward_noalloc", noalloc))
+
+    def noalloc_padded(L):
+        w = GW.CASES["d48_T1_bf16"]
+        finite(S.run_forward_noalloc(L, synth.make_inputs(w), w))
+
+    out.append(("forward_noalloc d48_T1_bf16", noalloc_padded))
 
     # arbitrary bit patterns in every input (negative, infinite and NaN beta and
     # alpha included): the results are meaningless, but no access may leave its
@@ -138,6 +165,23 @@ def cases(full, tsan=False):
 
     for name in GB.CASES if full else BACKWARD_QUICK:
         out.append((f"backward {name}", backward(name)))
+
+    # widths between the built ones: the forward's padded copies, dy, k, v in,
+    # every gradient out
+    def backward_padded(name):
+        def run(L):
+            case = GW.BWD_CASES[name]
+            w, epi, bridge = case["w"], case.get("epilogue", True), case.get("bridge", False)
+            x = synth.make_inputs(w)
+            rw = np.linspace(0.5, 1.5, w.d) if case.get("gain") else None
+            _, fws, _ = S.run_forward(L, x, w, epilogue=epi, rms_weight=rw, bridge=bridge)
+            got, _, _ = S.run_backward(L, x, w, GB._dy(w), fws, epilogue=epi, rms_weight=rw, bridge=bridge,
+                                       gain=epi)
+            finite(*(v for v in got.values() if v is not None))
+        return run
+
+    for name in GW.BWD_CASES if full else ("bwd_d48_gain", "bwd_d80_raw_bridge"):
+        out.append((f"backward {name}", backward_padded(name)))
 
     # forward and backward at the 768p clip's frame size (48 x 84 tokens,
     # d = 128, 256 text tokens), where the kernels' 32-bit row offsets are

@@ -546,7 +546,7 @@ def bwd_sizes(p: Prob) -> dict:
              dF=heads * p.nc * dd, dR=heads * p.nc * dd, dST=heads * dd, lam_final=heads * 2 * dd,
              states_f=heads * (p.T + 2) * dd, states_r=heads * (p.T + 2) * dd,
              gmats=heads * (p.T + 1) * 5 * max(p.D, 32) * p.D * 2,
-             gain=p.B * p.T * p.H * p.D * 4, dgamma=p.D * 4)
+             gain=p.B * p.T * p.H * p.D * 4, dgamma=(p.Du or p.D) * 4)
     for n in ("lam_f", "lam_r", "dA", "dB", "p32", "M", "dPinv", "tmp"):
         S[n] = heads * (p.T + 1) * dd
     return S
@@ -639,7 +639,8 @@ def model_readout_bwd(p: Prob, r: Report, S):
         last = sl + ((rows - 1 - sl) // (1024 // D)) * (1024 // D)
         live = sl < rows
         r.ptr("gain_grad_sum", "gain", S["gain"], (sl[live] * D + j[live]) * 4, (last[live] * D + j[live]) * 4 + 4)
-        r.ptr("gain_grad_sum", "dgamma", S["dgamma"], j[:D] * 4, j[:D] * 4 + 4)
+        n_out = p.Du or D  # the caller's channels only
+        r.ptr("gain_grad_sum", "dgamma", S["dgamma"], j[:n_out] * 4, j[:n_out] * 4 + 4)
 
 
 def model_gram_plain(p: Prob, r: Report, S):
@@ -814,11 +815,34 @@ def model_backward(p: Prob) -> Report:
     assert p.bf16
     S = bwd_sizes(p)
     r = Report()
+    pad = bool(p.Du) and p.Du != p.D
+    tok, trows, frames = p.B * p.T * p.U * p.H, p.B * p.L * p.H, p.B * p.T * p.H
+    ub, pb = p.Du * 2, p.D * 2
+    if pad:  # stage 1: dy in (q, gate, alpha and the gain are the forward's padded copies)
+        model_copy_rows(r, "caller dy", tok * ub, "padded dy", S["dy"], ub, pb, ub, tok)
     model_pack_states_t(p, r, S)
     model_readout_bwd(p, r, S)
     model_gram_plain(p, r, S)
+    if pad:  # dq, dgate out
+        for x in ("dq",) + (("dgate",) if p.epilogue else ()):
+            model_copy_rows(r, "padded " + x, S[x], "caller " + x, tok * ub, pb, ub, ub, tok)
     model_backward_scan(p, r, S)
+    if pad:  # dalpha out
+        model_copy_rows(r, "padded dalpha", S["dalpha"], "caller dalpha", frames * p.Du * 4, p.D * 4, p.Du * 4,
+                        p.Du * 4, frames)
+        # stage 3: k, v (and the text's) in
+        for x in ("k", "v"):
+            model_copy_rows(r, "caller " + x, tok * ub, "padded " + x, S[x], ub, pb, ub, tok)
+        if p.L:
+            for x in ("k_text", "v_text"):
+                model_copy_rows(r, "caller " + x, trows * ub, "padded " + x, S[x], ub, pb, ub, trows)
     model_backward_gram(p, r, S)
+    if pad:  # dk, dv (and the text's) out
+        for x in ("dk", "dv"):
+            model_copy_rows(r, "padded " + x, S[x], "caller " + x, tok * ub, pb, ub, ub, tok)
+        if p.L:
+            for x in ("dk_text", "dv_text"):
+                model_copy_rows(r, "padded " + x, S[x], "caller " + x, trows * ub, pb, ub, ub, trows)
     return r
 
 

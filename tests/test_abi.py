@@ -69,8 +69,42 @@ def test_bad_eps_and_unsupported_widths():
     d = good()
     d.d_v = 64
     assert bd.validate(d) == bd.VDN_ERR_UNSUPPORTED
-    assert bd.validate(good(d=48)) == bd.VDN_ERR_UNSUPPORTED
     assert bd.lib().vdn_vda_validate(None) == bd.VDN_ERR_INVALID_ARG
+
+
+def test_widths_between_the_built_ones():
+    """d = 48, 80, 96, 112: the forward and backward passes run them
+    (zero-padded to the next built width, the padded copies in their
+    workspaces); the prep and the adjacent maps refuse them."""
+    lib = bd.lib()
+    for w, D in ((48, 64), (80, 128), (96, 128), (112, 128)):
+        d = good(d=w)
+        assert bd.validate(d) == bd.VDN_OK
+        # the workspace holds the built width's sections plus the padded copies
+        L = bd.workspace_layout(d)
+        built = bd.workspace_layout(good(d=D))
+        assert L.readout_states == built.readout_states and L.chunk_j == built.chunk_j
+        x = 60 * 4032 * 24 * D * 2
+        assert L.total >= built.total + 5 * x
+        # the backward workspace: the built width's sections plus padded dy, dq,
+        # dgate, dalpha, k, v, dk, dv and the text's
+        bw, bw_built = bd.backward_workspace_bytes(d), bd.backward_workspace_bytes(good(d=D))
+        assert bw >= bw_built + 7 * x
+        assert bd.backward_layout(d).d_out == bd.backward_layout(good(d=D)).d_out
+        assert lib.vdn_vda_gates_workspace_bytes(ctypes.byref(d), 3072) == 0
+        P = [ctypes.c_void_p(A16 + (1 << 34) * i) for i in range(10)]
+        assert lib.vdn_vda_prepare(ctypes.byref(d), *P, None) == bd.VDN_ERR_UNSUPPORTED
+        # the backward's argument checks pass (no GPU here: the launch fails)
+        fw = bd.workspace_bytes(d)
+        assert lib.vdn_vda_backward_readout(ctypes.byref(d), *P[:6], fw, P[6], P[7], None, P[8], bw,
+                                            None) == bd.VDN_ERR_HIP
+    # d = 144 and widths that are not multiples of 16 stay invalid
+    assert bd.validate(good(d=144)) == bd.VDN_ERR_INVALID_ARG
+    assert bd.validate(good(d=40)) == bd.VDN_ERR_INVALID_ARG
+    # the 32-bit offset limits are those of the built width the kernels run at:
+    # 16384 heads of d = 112 run at 128, where a 48 x 84 frame's rows pass 4 GiB
+    assert bd.validate(good(H=16384, n_text=0, grid_h=1, grid_w=1, d=112)) == bd.VDN_OK
+    assert bd.validate(good(H=2048, n_text=0, d=112)) == bd.VDN_ERR_INVALID_ARG
 
 
 def test_workspace_layout_is_consistent():
@@ -129,7 +163,8 @@ def test_forward_argument_errors_before_launch():
     assert _fwd(desc, _ptrs(q=A16 + 8), need) == bd.VDN_ERR_ALIGNMENT
     assert _fwd(desc, _ptrs(ws=A16 + 0x40000000 + 64), need) == bd.VDN_ERR_ALIGNMENT
     assert _fwd(desc, _ptrs(beta=A16 + 1), need) == bd.VDN_ERR_ALIGNMENT
-    bad = good(d=48)
+    bad = good()
+    bad.d_v = 64
     assert _fwd(bad, _ptrs(), need) == bd.VDN_ERR_UNSUPPORTED
 
 
@@ -490,4 +525,10 @@ def test_forward_noalloc_checks_before_touching_the_gpu():
     assert call(good()) == bd.VDN_ERR_WORKSPACE
     share = good(H=8, T=60)
     assert bd.workspace_bytes(share) > 64 << 20 and call(share) == bd.VDN_ERR_WORKSPACE
-    assert call(good(d=48)) == bd.VDN_ERR_UNSUPPORTED
+    # a width between the built ones takes its padded copies from the array too
+    small = good(H=2, T=6, grid_h=6, grid_w=11, n_text=12, d=48)
+    assert bd.workspace_bytes(small) < 64 << 20
+    assert call(good(d=48)) == bd.VDN_ERR_WORKSPACE
+    bad = good()
+    bad.d_v = 64
+    assert call(bad) == bd.VDN_ERR_UNSUPPORTED

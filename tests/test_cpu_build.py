@@ -244,6 +244,48 @@ def test_values_beyond_the_half_range(lib):
 
 
 # ---------------------------------------------------------------------------
+# head widths between the built ones (zero-padded to the next), with the
+# checks of the GPU width tests
+# ---------------------------------------------------------------------------
+import test_gpu_widths as GW  # noqa: E402
+
+WIDTHS = [n for n in GW.CASES if n != "d112_768p_frame"]
+
+
+@pytest.mark.parametrize("name", WIDTHS)
+def test_padded_widths_match_oracle(lib, name):
+    w = GW.CASES[name]
+    x = synth.make_inputs(w)
+    heads = list(range(w.H))
+    rw = np.random.default_rng(5).uniform(0.5, 1.5, w.d)
+    tol = G.TOL[w.dtype]
+    scan = "chunks" if name.endswith("chunk3") else "frames"
+    out, _, _ = S.run_forward(lib, x, w, epilogue=False, scan=scan)
+    assert G.slice_rel_err(S.to_f64(out), P._oracle_heads(x, w, heads, gate=False)["o"]) <= tol
+    for gain in (None, rw):
+        y, _, _ = S.run_forward(lib, x, w, epilogue=True, rms_weight=gain, scan=scan,
+                                bridge=name == "d48_f32")
+        ref = P._oracle_heads(x, w, heads, gate=True, rms_weight=gain, bridge=name == "d48_f32")
+        assert G.slice_rel_err(S.to_f64(y), ref["y"]) <= tol, gain is not None
+
+
+@pytest.mark.parametrize("name", list(GW.BWD_CASES))
+def test_padded_width_backward_matches_oracle(lib, name):
+    import test_gpu_backward as GB
+    case = GW.BWD_CASES[name]
+    w, epi, bridge = case["w"], case.get("epilogue", True), case.get("bridge", False)
+    x = synth.make_inputs(w)
+    dy = GB._dy(w)
+    gain = np.random.default_rng(5).uniform(0.5, 1.5, w.d) if case.get("gain") else None
+    _, fws, _ = S.run_forward(lib, x, w, epilogue=epi, rms_weight=gain, bridge=bridge)
+    got, _, _ = S.run_backward(lib, x, w, dy, fws, epilogue=epi, rms_weight=gain, bridge=bridge, gain=epi)
+    got = {k: S.to_f64(v) for k, v in got.items() if v is not None}
+    errs = GW.backward_errors(got, GW.backward_reference(x, w, dy, epi, gain, bridge), w, epi)
+    bad = {k: v for k, v in errs.items() if not v <= G.TOL[w.dtype]}
+    assert not bad, bad
+
+
+# ---------------------------------------------------------------------------
 # the backward pass: the three stages against the oracle's gradients, with the
 # checks of the GPU backward tests
 # ---------------------------------------------------------------------------

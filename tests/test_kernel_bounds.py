@@ -26,6 +26,8 @@ def _shapes():
                 False))
     for h in (3, 4, 6, 8, 12, 16):  # bench.py --heads sweeps of the 768p clip
         out.append((f"768p_h{h}", synth.WORKLOADS["768p_bf16"].scaled(name="h", H=h), False))
+    import test_gpu_widths as W  # widths between the built ones
+    out += [(n, w, False) for n, w in W.CASES.items()]
     return out
 
 
@@ -33,7 +35,10 @@ SHAPES = _shapes()
 
 
 def _prob(w, **kw):
-    return KB.Prob(B=w.B, H=w.H, T=w.T, gh=w.grid_h, gw=w.grid_w, D=w.d, L=w.L, C=w.chunk, bf16=w.dtype == "bf16", **kw)
+    """The model's problem: a width between the built ones runs at the next."""
+    D = next(b for b in (16, 32, 64, 128) if b >= w.d)
+    return KB.Prob(B=w.B, H=w.H, T=w.T, gh=w.grid_h, gw=w.grid_w, D=D, L=w.L, C=w.chunk, bf16=w.dtype == "bf16",
+                   Du=w.d if D != w.d else 0, **kw)
 
 
 @pytest.mark.parametrize("name,w,prep", SHAPES, ids=[s[0] for s in SHAPES])
@@ -79,6 +84,9 @@ def _bwd_shapes():
     out.append(("long_clip", synth.WORKLOADS["long_prep_bf16"], {}))
     for h in (3, 8):
         out.append((f"768p_h{h}", synth.WORKLOADS["768p_bf16"].scaled(name="h", H=h), {}))
+    import test_gpu_widths as W  # widths between the built ones
+    out += [(n, c["w"], dict(epilogue=c.get("epilogue", True), bridge=c.get("bridge", False), gamma=c.get("gain", False)))
+            for n, c in W.BWD_CASES.items()]
     return out
 
 
@@ -97,6 +105,25 @@ def test_backward_kernels_stay_in_bounds(name, w, flags):
             assert not r.errors, (name, epi, bridge, r.errors[:5])
             checked += r.checked
     assert checked > 0
+
+
+def test_padded_copies_are_modelled():
+    """A width between the built ones adds the copies in and out, and a
+    padded buffer one chunk short is reported."""
+    import test_gpu_widths as W
+    p = _prob(W.CASES["d48_bf16"], gamma=True)
+    assert p.D == 64 and p.Du == 48
+    r = KB.model_forward(p)
+    assert not r.errors and r.checked
+    S = KB.sizes(p)
+    r2 = KB.Report()
+    KB.model_copy_rows(r2, "caller q", p.B * p.T * p.U * p.H * 48 * 2, "padded q", S["q"] - 16, 96, 128, 96,
+                       p.B * p.T * p.U * p.H)
+    assert any("padded q" in e for e in r2.errors)
+    r3 = KB.Report()
+    KB.model_copy_rows(r3, "padded out", S["out"], "caller out", p.B * p.T * p.U * p.H * 48 * 2 - 2, 128, 96, 96,
+                       p.B * p.T * p.U * p.H)
+    assert any("caller out" in e for e in r3.errors)
 
 
 def test_backward_slot_sizes_match_the_layout():
