@@ -529,12 +529,7 @@ hipError_t backward_readout_d(const Problem& p, const void* q, const void* gate,
     dgamma ? launch_g(Y()) : launch_g(N());
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (dgamma) {
-      hipLaunchKernelGGL(gain_grad_sum<D>, dim3(1), dim3(1024), 0, s, static_cast<const float*>(gain_part), dgamma,
-                         (int)grid, gain_n, gain_scale);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
+    if (dgamma && (e = launch_gain_grad_sum(p, gain_part, dgamma, gain_n, gain_scale, s)) != hipSuccess) return e;
     do_ = dout;
   } else {
     // without the epilogue do is dy: dq = S_q^T dy is the forward readout, raw,
@@ -885,7 +880,13 @@ hipError_t launch_backward_readout(const Problem& p, const void* q, const void* 
                                    const float* alpha, void* rstates_t, void* dout, void* dq, void* dgate,
                                    float* dsq, float* gain_part, float* dgamma, int gain_n, float gain_scale,
                                    hipStream_t s) {
-  if (!p.bf16 || (dgamma && (!p.epilogue || !gain_part || gain_n < 1 || gain_n > p.D))) return hipErrorInvalidValue;
+  if (dgamma && (!p.epilogue || !gain_part || gain_n < 1 || gain_n > p.D)) return hipErrorInvalidValue;
+  if (!p.bf16) {
+    auto f = [](const void* x) { return static_cast<const float*>(x); };
+    auto g = [](void* x) { return static_cast<float*>(x); };
+    return launch_backward_readout_f32(p, f(q), f(gate), rms_weight, f(dy), s_text, fwd, rev, alpha, g(rstates_t),
+                                       g(dout), g(dq), g(dgate), dsq, gain_part, dgamma, gain_n, gain_scale, s);
+  }
   switch (p.D) {
     case 16: return backward_readout_d<16>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, gain_part, dgamma, gain_n, gain_scale, s);
     case 32: return backward_readout_d<32>(p, q, gate, rms_weight, dy, rstates, s_text, fwd, rev, alpha, rstates_t, dout, dq, dgate, dsq, gain_part, dgamma, gain_n, gain_scale, s);
@@ -1505,8 +1506,21 @@ hipError_t backward_gram_d(const Problem& p, const BwdGramBuffers& w, hipStream_
 
 }  // namespace
 
+hipError_t launch_gain_grad_sum(const Problem& p, const float* gain_part, float* dgamma, int n, float scale,
+                                hipStream_t s) {
+  const int rows = p.B * p.T * p.H;
+  switch (p.D) {
+    case 16: hipLaunchKernelGGL(gain_grad_sum<16>, dim3(1), dim3(1024), 0, s, gain_part, dgamma, rows, n, scale); break;
+    case 32: hipLaunchKernelGGL(gain_grad_sum<32>, dim3(1), dim3(1024), 0, s, gain_part, dgamma, rows, n, scale); break;
+    case 64: hipLaunchKernelGGL(gain_grad_sum<64>, dim3(1), dim3(1024), 0, s, gain_part, dgamma, rows, n, scale); break;
+    case 128: hipLaunchKernelGGL(gain_grad_sum<128>, dim3(1), dim3(1024), 0, s, gain_part, dgamma, rows, n, scale); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_backward_gram(const Problem& p, const BwdGramBuffers& w, hipStream_t s) {
-  if (!p.bf16) return hipErrorInvalidValue;
+  if (!p.bf16) return launch_backward_gram_f32(p, w, s);
   switch (p.D) {
     case 16: return backward_gram_d<16>(p, w, s);
     case 32: return backward_gram_d<32>(p, w, s);

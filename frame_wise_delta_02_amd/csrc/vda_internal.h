@@ -174,6 +174,17 @@ hipError_t launch_backward_readout(const Problem& p, const void* q, const void* 
                                    const float* rev, const float* alpha, void* rstates_t, void* dout, void* dq,
                                    void* dgate, float* dsq, float* gain_part, float* dgamma, int gain_n,
                                    float gain_scale, hipStream_t s);
+// dgamma[j] = scale * sum over the B T H rows of gain_part [rows][D], j < n.
+hipError_t launch_gain_grad_sum(const Problem& p, const float* gain_part, float* dgamma, int n, float scale,
+                                hipStream_t s);
+// The first stage for float32 inputs (vda_backward_f32.hip): slots <- S_q per
+// chunk slot as plain float32 [d_v][d_k] (in the rstates_t section), the rest
+// as launch_backward_readout.
+hipError_t launch_backward_readout_f32(const Problem& p, const float* q, const float* gate, const float* rms_weight,
+                                       const float* dy, const float* s_text, const float* fwd, const float* rev,
+                                       const float* alpha, float* slots, float* dout, float* dq, float* dgate,
+                                       float* dsq, float* gain_part, float* dgamma, int gain_n, float gain_scale,
+                                       hipStream_t s);
 // Second stage of the backward pass: buffers (float32 unless noted).
 struct BwdScanBuffers {
   const float* stats;   // forward workspace: [B, H, T+1, 2d, d]
@@ -202,6 +213,7 @@ struct BwdGramBuffers {
   void *dk_text, *dv_text, *dbeta_text;     // as the text inputs (out)
 };
 hipError_t launch_backward_gram(const Problem& p, const BwdGramBuffers& w, hipStream_t s);
+hipError_t launch_backward_gram_f32(const Problem& p, const BwdGramBuffers& w, hipStream_t s);
 // The linear maps either side of the path: gate logits and sigmoid(beta) from
 // one bfloat16 product with the stacked weights, the frames' mean tokens, and
 // sigmoid(W_alpha xbar) in float32; the output projection with Y_in added.

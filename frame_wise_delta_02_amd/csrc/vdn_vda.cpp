@@ -248,7 +248,8 @@ BwdLayout make_bwd_layout(const Problem& p) {
     o = up(o + bytes);
   };
   take(l.rstates_t, heads * (p.nc + 1) * readout_slot_bytes(p));
-  take(l.dout, (size_t)p.B * p.T * p.U * p.H * p.D * 2);
+  const size_t esz = p.bf16 ? 2 : 4;
+  take(l.dout, (size_t)p.B * p.T * p.U * p.H * p.D * esz);
   take(l.dsq, heads * p.T * dd);
   take(l.dF, heads * p.nc * dd);
   take(l.dR, heads * p.nc * dd);
@@ -270,8 +271,8 @@ BwdLayout make_bwd_layout(const Problem& p) {
   // the gain gradient's sums per (batch, frame, head), float32 [B T H][d]
   take(l.gain, (size_t)p.B * p.T * p.H * p.D * 4);
   const bool pad = p.Du != p.D;
-  const size_t xb = pad ? (size_t)p.B * p.T * p.U * p.H * p.D * 2 : 0;
-  const size_t tb = pad ? (size_t)p.B * p.L * p.H * p.D * 2 : 0;
+  const size_t xb = pad ? (size_t)p.B * p.T * p.U * p.H * p.D * esz : 0;
+  const size_t tb = pad ? (size_t)p.B * p.L * p.H * p.D * esz : 0;
   for (size_t* f : {&l.pad_dy, &l.pad_dq, &l.pad_dgate}) take(*f, xb);
   take(l.pad_dalpha, pad ? (size_t)p.B * p.T * p.H * p.D * 4 : 0);
   for (size_t* f : {&l.pad_k, &l.pad_v, &l.pad_dk, &l.pad_dv}) take(*f, xb);
@@ -280,10 +281,18 @@ BwdLayout make_bwd_layout(const Problem& p) {
   return l;
 }
 
+// The adjacent maps are plain products over the H d channels of a token, with
+// no tiling of the head width: they run at the caller's width, whatever it is.
+Problem proj_problem(const vdn_vda_desc* d) {
+  Problem p = problem(d);
+  p.D = p.Du;
+  return p;
+}
+
 // The adjacent maps' own checks: bfloat16, a model width that 16-byte rows and
 // 32-bit panel offsets allow.
 vdn_status check_proj(const vdn_vda_desc* d, int32_t d_model) {
-  const vdn_status st = check_native(d);
+  const vdn_status st = check(d);
   if (st != VDN_OK) return st;
   if (d->dtype != VDN_BF16) return VDN_ERR_UNSUPPORTED;
   if (d_model < 8 || d_model % 8) return VDN_ERR_INVALID_ARG;
@@ -549,7 +558,7 @@ vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d, const void* q, const 
   if (st != VDN_OK) return st;
   const bool epi = (d->flags & VDN_VDA_EPILOGUE) != 0;
   // the raw query's gradient is formed with the epilogue's backward only
-  if (d->dtype != VDN_BF16 || ((d->flags & VDN_VDA_QUERY_L2) && !epi)) return VDN_ERR_UNSUPPORTED;
+  if ((d->flags & VDN_VDA_QUERY_L2) && !epi) return VDN_ERR_UNSUPPORTED;
   if (!q || !alpha || !dy || !dq || !fwd_workspace) return VDN_ERR_INVALID_ARG;
   if (epi && (!gate || !dgate)) return VDN_ERR_INVALID_ARG;
   if (d_rms_weight && !epi) return VDN_ERR_INVALID_ARG;  // no gain without the epilogue
@@ -580,7 +589,8 @@ vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d, const void* q, const 
   Problem pr = p;
   void *dq_k = dq, *dgate_k = dgate;
   float gscale = 1.f;
-  const size_t rows = (size_t)p.B * p.T * p.U * p.H, ub = (size_t)p.Du * 2, pb = (size_t)p.D * 2;
+  const size_t esz = p.bf16 ? 2 : 4;
+  const size_t rows = (size_t)p.B * p.T * p.U * p.H, ub = (size_t)p.Du * esz, pb = (size_t)p.D * esz;
   if (p.Du != p.D) {
     q = fw + fl.pad_q;
     alpha = reinterpret_cast<const float*>(fw + fl.pad_alpha);
@@ -613,7 +623,6 @@ vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha, cons
                                  size_t workspace_bytes, hipStream_t stream) {
   const vdn_status st = check(d);
   if (st != VDN_OK) return st;
-  if (d->dtype != VDN_BF16) return VDN_ERR_UNSUPPORTED;
   if (!alpha || !fwd_workspace || !dalpha) return VDN_ERR_INVALID_ARG;
   const Problem p = problem(d);
   // every frame's state is recorded per head through one buffer descriptor
@@ -674,7 +683,6 @@ vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const voi
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const vdn_status st = check(d);
   if (st != VDN_OK) return st;
-  if (d->dtype != VDN_BF16) return VDN_ERR_UNSUPPORTED;
   if (!k || !v || !beta || !dk || !dv || !dbeta) return VDN_ERR_INVALID_ARG;
   const bool text = d->n_text > 0;
   if (text && (!k_text || !v_text || !beta_text || !dk_text || !dv_text || !dbeta_text)) return VDN_ERR_INVALID_ARG;
@@ -685,18 +693,19 @@ vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const voi
                           text ? dk_text : nullptr, text ? dv_text : nullptr};
   for (const void* ptr : need16)
     if (ptr && !aligned(ptr, 16)) return VDN_ERR_ALIGNMENT;
+  const size_t esz = d->dtype == VDN_BF16 ? 2 : 4;
   const void* need2[] = {beta, dbeta, text ? beta_text : nullptr, text ? dbeta_text : nullptr};
   for (const void* ptr : need2)
-    if (ptr && !aligned(ptr, 2)) return VDN_ERR_ALIGNMENT;
+    if (ptr && !aligned(ptr, esz)) return VDN_ERR_ALIGNMENT;
   if (!aligned(workspace, kAlign)) return VDN_ERR_ALIGNMENT;
   // the outputs are written while the inputs are still read
   const size_t tok = (size_t)p.B * p.T * p.U * p.H, ttok = (size_t)p.B * p.L * p.H;
-  const size_t xb = tok * p.Du * 2, tb = ttok * p.Du * 2;
-  const Span ins[] = {{k, xb}, {v, xb}, {beta, tok * 2}, {text ? k_text : nullptr, tb},
-                      {text ? v_text : nullptr, tb}, {text ? beta_text : nullptr, ttok * 2},
+  const size_t xb = tok * p.Du * esz, tb = ttok * p.Du * esz;
+  const Span ins[] = {{k, xb}, {v, xb}, {beta, tok * esz}, {text ? k_text : nullptr, tb},
+                      {text ? v_text : nullptr, tb}, {text ? beta_text : nullptr, ttok * esz},
                       {workspace, workspace_bytes}};
-  const Span outs[] = {{dk, xb}, {dv, xb}, {dbeta, tok * 2}, {text ? dk_text : nullptr, tb},
-                       {text ? dv_text : nullptr, tb}, {text ? dbeta_text : nullptr, ttok * 2}};
+  const Span outs[] = {{dk, xb}, {dv, xb}, {dbeta, tok * esz}, {text ? dk_text : nullptr, tb},
+                       {text ? dv_text : nullptr, tb}, {text ? dbeta_text : nullptr, ttok * esz}};
   for (const Span& o : outs)
     for (const Span& i : ins)
       if (overlaps(o, i)) return VDN_ERR_INVALID_ARG;
@@ -724,7 +733,7 @@ vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const voi
   // padded then copied back (dbeta has no channel axis)
   hipError_t e = hipSuccess;
   const bool pad = p.Du != p.D;
-  const size_t ub = (size_t)p.Du * 2, pb = (size_t)p.D * 2;
+  const size_t ub = (size_t)p.Du * esz, pb = (size_t)p.D * esz;
   if (pad) {
     auto in = [&](const void*& x, size_t off, size_t n) {
       if (e == hipSuccess) e = launch_copy_rows(x, ub, ws + off, pb, ub, n, stream);
@@ -758,7 +767,7 @@ vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const voi
 
 size_t vdn_vda_gates_workspace_bytes(const vdn_vda_desc* d, int32_t d_model) {
   if (check_proj(d, d_model) != VDN_OK) return 0;
-  const Problem p = problem(d);
+  const Problem p = proj_problem(d);
   const size_t F = (size_t)p.B * p.T;
   return up(F * proj_mean_splits(p) * d_model * 4) + up(F * d_model * 4);
 }
@@ -769,7 +778,7 @@ vdn_status vdn_vda_gates(const vdn_vda_desc* d, int32_t d_model, const void* x, 
   const vdn_status st = check_proj(d, d_model);
   if (st != VDN_OK) return st;
   if (!x || !w_gb || !w_alpha || !gate || !beta || !alpha) return VDN_ERR_INVALID_ARG;
-  const Problem p = problem(d);
+  const Problem p = proj_problem(d);
   const size_t need = vdn_vda_gates_workspace_bytes(d, d_model);
   if (!workspace || workspace_bytes < need) return VDN_ERR_WORKSPACE;
   const void* need16[] = {x, w_gb, w_alpha, gate, alpha};
@@ -803,7 +812,7 @@ vdn_status vdn_vda_out_proj(const vdn_vda_desc* d, int32_t d_model, const void* 
   const void* need16[] = {o, w_o, y_in, y};
   for (const void* ptr : need16)
     if (ptr && !aligned(ptr, 16)) return VDN_ERR_ALIGNMENT;
-  const Problem p = problem(d);
+  const Problem p = proj_problem(d);
   const size_t M = (size_t)p.B * p.T * p.U, HD = (size_t)p.H * p.D;
   // y may be y_in itself (each element is read before it is written), nothing else
   const Span ys{y, M * d_model * 2};
@@ -823,7 +832,7 @@ const char* vdn_vda_status_string(vdn_status s) {
     case VDN_ERR_INVALID_ARG: return "VDN_ERR_INVALID_ARG: bad descriptor, size, NULL pointer or overlapping buffers";
     case VDN_ERR_UNSUPPORTED:
       return "VDN_ERR_UNSUPPORTED: valid request not implemented (d_k != d_v; head widths other than "
-             "16, 32, 64, 128 in the prep and the adjacent maps; float32 in the backward pass and the adjacent maps; "
+             "16, 32, 64, 128 in the prep; float32 in the backward pass and the adjacent maps; "
              "the query norm's backward without the epilogue)";
     case VDN_ERR_WORKSPACE: return "VDN_ERR_WORKSPACE: workspace missing or too small";
     case VDN_ERR_ALIGNMENT: return "VDN_ERR_ALIGNMENT: pointer misaligned";

@@ -170,8 +170,9 @@ typedef struct {
  * gives the same RMSNorm over the d true channels).  The backward pass takes
  * them the same way: it reads the forward's padded copies from the forward's
  * workspace, pads dy, k and v in its own, and copies every gradient's d
- * channels back (the gain's gradient scaled by sqrt(d / D)).  vdn_vda_prepare
- * and the adjacent maps return VDN_ERR_UNSUPPORTED for them. */
+ * channels back (the gain's gradient scaled by sqrt(d / D)).  The adjacent
+ * maps (plain products over a token's H d channels) run at the width itself.
+ * vdn_vda_prepare returns VDN_ERR_UNSUPPORTED for them. */
 vdn_status vdn_vda_validate(const vdn_vda_desc* d);
 
 /* Workspace bytes vdn_vda_forward needs for `d`; 0 if `d` is invalid. */
@@ -267,7 +268,7 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d,
  *         of ones; overwritten, not accumulated),
  * and leaves in its workspace, at the offsets vdn_vda_backward_workspace_layout()
  * reports,
- *   d_out     [B, T, U, H, d_v] bfloat16: do, the readout's adjoint
+ *   d_out     [B, T, U, H, d_v] in dtype: do, the readout's adjoint
  *             (= rms_weight * s * dy * r - n * r * mean(rms_weight * s * dy * n),
  *             r = 1 / sqrt(mean o^2 + rms_eps)), divided by |q| per token with
  *             VDN_VDA_QUERY_L2; written with VDN_VDA_EPILOGUE only -- without it
@@ -286,7 +287,8 @@ vdn_status vdn_vda_forward(const vdn_vda_desc* d,
  * forward normalised the raw query, q_n = q / sqrt(sum q^2 + l2_eps)) dq is the
  * gradient of the raw query, (dq_n - q_n (q_n . dq_n)) / |q| with dq_n = S_q^T do,
  * and d_out holds do / |q| per token (so that d_state_q = sum d_out q^T reads
- * the raw query).  Supported: VDN_BF16, and VDN_VDA_QUERY_L2 only with
+ * the raw query).  Supported: VDN_BF16 and VDN_F32 (do, dq, dgate and d_out
+ * then float32), and VDN_VDA_QUERY_L2 only with
  * VDN_VDA_EPILOGUE (else VDN_ERR_UNSUPPORTED).  Errors: VDN_ERR_INVALID_ARG
  * (NULL pointer, gate or dgate missing with the epilogue, d_rms_weight without
  * it, aliasing), VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE (either workspace too
@@ -345,7 +347,7 @@ vdn_status vdn_vda_backward_readout(const vdn_vda_desc* d,
  * S_T.  With VDN_VDA_DECAY_BRIDGE a query chunk's adjoint reaches the records
  * (and S_T / 2) column-scaled by its bridge's alpha products, and dalpha adds
  * the bridge's own term (frames of the bridged chunks, anchors included).
- * Supported: VDN_BF16 (else VDN_ERR_UNSUPPORTED); (T + 2) D D 4 < 2^31 (D the built width).  Errors as
+ * Supported: VDN_BF16 and VDN_F32; (T + 2) D D 4 < 2^31 (D the built width).  Errors as
  * vdn_vda_backward_readout.  Asynchronous on `stream`.
  */
 vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha,
@@ -368,7 +370,7 @@ vdn_status vdn_vda_backward_scan(const vdn_vda_desc* d, const float* alpha,
  * hi + lo pairs (dbeta sums d^2 products that largely cancel), dB_t^T (dk
  * only) rounded once to bfloat16.  k, v, beta and the text inputs are
  * those the forward pass read.  Outputs must overlap neither each other, the
- * inputs nor the workspace.  Supported: VDN_BF16 (else VDN_ERR_UNSUPPORTED).  Errors: VDN_ERR_INVALID_ARG
+ * inputs nor the workspace.  Supported: VDN_BF16 and VDN_F32 (beta and dbeta 4-byte aligned).  Errors: VDN_ERR_INVALID_ARG
  * (NULL pointer, overlap), VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE,
  * VDN_ERR_ALIGNMENT (16 B for k, v and the d-wide outputs, 2 B for beta and the
  * dbeta outputs, 256 B for the workspace), VDN_ERR_HIP.  Asynchronous on `stream`.
@@ -397,8 +399,8 @@ vdn_status vdn_vda_backward_gram(const vdn_vda_desc* d, const void* k, const voi
  * come from one bfloat16 matrix-core product (float32 accumulation, the
  * sigmoid applied before rounding).  The workspace (vdn_vda_gates_workspace_bytes)
  * holds the frames' token sums.  d_model a multiple of 8; the descriptor's
- * n_text, chunk and flags are ignored; VDN_BF16 at d = 16, 32, 64, 128 only
- * (else VDN_ERR_UNSUPPORTED).  Outputs must overlap neither each other, the inputs
+ * n_text, chunk and flags are ignored; any head width the descriptor allows;
+ * VDN_BF16 only (else VDN_ERR_UNSUPPORTED).  Outputs must overlap neither each other, the inputs
  * nor the workspace.  Errors: VDN_ERR_INVALID_ARG (NULL pointer, d_model,
  * overlap), VDN_ERR_UNSUPPORTED, VDN_ERR_WORKSPACE, VDN_ERR_ALIGNMENT (16 B;
  * 2 B for beta; 256 B for the workspace), VDN_ERR_HIP.  Asynchronous on `stream`.

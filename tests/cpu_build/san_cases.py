@@ -32,6 +32,7 @@ import test_gpu_adjacent as GA  # noqa: E402
 import test_gpu_backward as GB  # noqa: E402
 import test_gpu_parity as P  # noqa: E402
 import test_gpu_widths as GW  # noqa: E402
+import test_gpu_training_f32 as GT  # noqa: E402
 from cpu_build import sim as S  # noqa: E402
 from frame_wise_delta_02_amd import synth  # noqa: E402
 
@@ -47,7 +48,7 @@ FORWARD = ("d32_bf16", "d16_bf16", "d32_f32", "ragged_f32_128", "no_text_bf16", 
 FORWARD_QUICK = ("d32_bf16", "d16_bf16", "d32_f32", "no_text_bf16", "T1_bf16", "U1_bf16_128", "U2_f32_16")
 BACKWARD_QUICK = ("bwd_64_ragged", "bwd_32_bridge", "bwd_16_chunk3", "bwd_64_no_text", "bwd_16_ql2", "bwd_T1",
                   "bwd_16", "bwd_128_gain")
-ADJACENT_QUICK = ("adj_small", "adj_d16", "adj_tiny")
+ADJACENT_QUICK = ("adj_small", "adj_d16", "adj_tiny", "adj_d48")
 PADDED = ("d48_bf16", "d80_bf16", "d96_bf16_chunk3", "d112_bf16", "d48_f32", "d112_f32", "d80_no_text_bf16",
           "d48_T1_bf16", "d96_batch2_bf16")
 PADDED_QUICK = ("d48_f32", "d80_no_text_bf16", "d48_T1_bf16")
@@ -183,6 +184,25 @@ def cases(full, tsan=False):
     for name in GW.BWD_CASES if full else ("bwd_d48_gain", "bwd_d80_raw_bridge"):
         out.append((f"backward {name}", backward_padded(name)))
 
+    # float32 inputs: the float32 first and third stages
+    def backward_f32(name):
+        def run(L):
+            case = GT.CASES[name]
+            w, epi, bridge = case["w"], case.get("epilogue", True), case.get("bridge", False)
+            ql2 = case.get("query_l2", False)
+            x = synth.make_inputs(w)
+            if ql2:
+                GT.raw_queries(x, w)
+            rw = np.linspace(0.5, 1.5, w.d) if case.get("gain") else None
+            _, fws, _ = S.run_forward(L, x, w, epilogue=epi, rms_weight=rw, bridge=bridge, query_l2=ql2)
+            got, _, _ = S.run_backward(L, x, w, GT._dy(w), fws, epilogue=epi, rms_weight=rw, bridge=bridge,
+                                       query_l2=ql2, gain=epi)
+            finite(*(v for v in got.values() if v is not None))
+        return run
+
+    for name in GT.CASES if full else ("tiny_f32_gain", "d64_raw_chunk3", "d32_query_l2", "d48_gain"):
+        out.append((f"backward {name}", backward_f32(name)))
+
     # forward and backward at the 768p clip's frame size (48 x 84 tokens,
     # d = 128, 256 text tokens), where the kernels' 32-bit row offsets are
     # largest
@@ -197,16 +217,18 @@ def cases(full, tsan=False):
     if not tsan:
         out.append(("forward + backward at the 768p frame size", frame_768p))
 
+    adj_cases = dict(GA.CASES, **GW.ADJ_CASES)
+
     def adjacent(name):
         def run(L):
-            w, dm = GA.CASES[name]
+            w, dm = adj_cases[name]
             p = synth.make_adjacent_inputs(w, dm)
             finite(*S.run_gates(L, p, w, dm))
             for mode in ("y_in", "in_place", "no_y_in"):
                 finite(S.run_out_proj(L, p, w, mode))
         return run
 
-    for name in GA.CASES if full else ADJACENT_QUICK:
+    for name in adj_cases if full else ADJACENT_QUICK:
         out.append((f"gates + out_proj {name}", adjacent(name)))
     return out
 

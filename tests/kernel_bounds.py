@@ -536,12 +536,13 @@ def model_forward(p: Prob, prep: bool = False) -> Report:
 
 
 def bwd_sizes(p: Prob) -> dict:
-    """Bytes of every buffer the three backward stages touch (bfloat16 inputs)."""
+    """Bytes of every buffer the three backward stages touch."""
     S = dict(sizes(p))
     tok, ttok, heads = p.B * p.T * p.U * p.H, p.B * p.L * p.H, p.B * p.H
     dd = p.D * p.D * 4
-    x, xt = tok * p.D * 2, ttok * p.D * 2
-    S.update(dy=x, dq=x, dgate=x, dout=x, dk=x, dv=x, dbeta=tok * 2, dk_text=xt, dv_text=xt, dbeta_text=ttok * 2,
+    x, xt = tok * p.D * p.esz, ttok * p.D * p.esz
+    S.update(dy=x, dq=x, dgate=x, dout=x, dk=x, dv=x, dbeta=tok * p.esz, dk_text=xt, dv_text=xt,
+             dbeta_text=ttok * p.esz,
              dalpha=p.B * p.T * p.H * p.D * 4, rstates_t=S["rstates"], dsq=heads * p.T * dd,
              dF=heads * p.nc * dd, dR=heads * p.nc * dd, dST=heads * dd, lam_final=heads * 2 * dd,
              states_f=heads * (p.T + 2) * dd, states_r=heads * (p.T + 2) * dd,
@@ -654,6 +655,69 @@ def _ptr_heads(r, kern, S, buf, heads, per_head, lo_slot, hi_slot, dd):
     lo = (heads * per_head + lo_slot) * dd
     hi = (heads * per_head + hi_slot) * dd
     r.ptr(kern, buf, S[buf], lo, hi)
+
+
+def _token_rows(r, kern, buf, size, b, t, h, T_in, U, H, D, esz, per_token=None):
+    """Every token row [u < U] of frame t of batch b, head h, in a [B, T_in, U,
+    H, D] tensor (or, with per_token, one element per token: [B, T_in, U, H])."""
+    tok0 = (b * T_in + t) * U
+    first = (tok0 * H + h)
+    last = ((tok0 + U - 1) * H + h)
+    if per_token:
+        r.ptr(kern, buf, size, first * esz, last * esz + esz)
+    else:
+        r.ptr(kern, buf, size, first * D * esz, last * D * esz + D * esz)
+
+
+def model_backward_f32(p: Prob, r: Report, S):
+    """The float32 first and third stages (vda_backward_f32.hip)."""
+    D, H, T, U, C, nc = p.D, p.H, p.T, p.U, p.C, p.nc
+    dd = D * D * 4
+    # slot_states_f32: one workgroup per (batch, head, slot), the slot's D x D
+    # floats written, the records and S_T read as pack_states_t reads them
+    (blk,) = _grid(p.B * H * (nc + 1))
+    r.ptr("slot_states_f32", "rstates_t", S["rstates_t"], blk * dd, blk * dd + dd)
+    rr = Report()
+    model_pack_states_t(p, rr, dict(S, rstates_t=1 << 62))
+    r.errors += [e.replace("pack_states_t", "slot_states_f32") for e in rr.errors]
+    r.checked += rr.checked
+    # readout_bwd_f32 and state_adjoint_f32: one workgroup per (frame, head)
+    (blk,) = _grid(p.B * T * H)
+    h, t, b = blk % H, (blk // H) % T, blk // (H * T)
+    slot = np.where((t == 0) | (t == T - 1), nc, t // C)
+    sl = (b * H + h) * (nc + 1) + slot
+    r.ptr("readout_bwd_f32", "rstates_t", S["rstates_t"], sl * dd, sl * dd + dd)
+    ins = ("q", "gate", "dy") if p.epilogue else ("q", "dy")
+    outs = ("dq", "dgate", "dout") if p.epilogue else ("dq",)
+    for buf in ins + outs:
+        _token_rows(r, "readout_bwd_f32", buf, S[buf], b, t, h, T, U, H, D, 4)
+    if p.gamma:
+        r.ptr("readout_bwd_f32", "rms", S["rms"], np.array([0]), np.array([D * 4]))
+    if p.dgain and p.epilogue:
+        r.ptr("readout_bwd_f32", "gain", S["gain"], blk * D * 4, blk * D * 4 + D * 4)
+    for buf in ("q", "dout" if p.epilogue else "dy"):
+        _token_rows(r, "state_adjoint_f32", buf, S[buf], b, t, h, T, U, H, D, 4)
+    m = ((b * H + h) * T + t) * dd
+    r.ptr("state_adjoint_f32", "dsq", S["dsq"], m, m + dd)
+
+
+def model_gram_bwd_f32(p: Prob, r: Report, S):
+    """gram_bwd_f32: every frame (slots 0 .. T-1), then the text frame (slot T)."""
+    D, H, T, U, L = p.D, p.H, p.T, p.U, p.L
+    dd = D * D * 4
+    parts = [("k", "v", "beta", "dk", "dv", "dbeta", T, U, T, 0)]
+    if L:
+        parts.append(("k_text", "v_text", "beta_text", "dk_text", "dv_text", "dbeta_text", 1, L, 1, T))
+    for k, v, be, dk, dv, dbe, T_in, n_tok, n_frames, off in parts:
+        (blk,) = _grid(p.B * n_frames * H)
+        h, f, b = blk % H, (blk // H) % n_frames, blk // (H * n_frames)
+        m = ((b * H + h) * (T + 1) + f + off) * dd
+        for buf in ("dA", "dB"):
+            r.ptr("gram_bwd_f32", buf, S[buf], m, m + dd)
+        for buf in (k, v, dk, dv):
+            _token_rows(r, "gram_bwd_f32", buf, S[buf], b, f, h, T_in, n_tok, H, D, 4)
+        for buf in (be, dbe):
+            _token_rows(r, "gram_bwd_f32", buf, S[buf], b, f, h, T_in, n_tok, H, D, 4, per_token=True)
 
 
 def model_backward_scan(p: Prob, r: Report, S):
@@ -812,7 +876,6 @@ def model_backward_gram(p: Prob, r: Report, S):
 def model_backward(p: Prob) -> Report:
     """Every kernel of vdn_vda_backward_readout, _scan and _gram for one
     problem (bfloat16 inputs)."""
-    assert p.bf16
     S = bwd_sizes(p)
     r = Report()
     pad = bool(p.Du) and p.Du != p.D
@@ -820,9 +883,12 @@ def model_backward(p: Prob) -> Report:
     ub, pb = p.Du * 2, p.D * 2
     if pad:  # stage 1: dy in (q, gate, alpha and the gain are the forward's padded copies)
         model_copy_rows(r, "caller dy", tok * ub, "padded dy", S["dy"], ub, pb, ub, tok)
-    model_pack_states_t(p, r, S)
-    model_readout_bwd(p, r, S)
-    model_gram_plain(p, r, S)
+    if p.bf16:
+        model_pack_states_t(p, r, S)
+        model_readout_bwd(p, r, S)
+        model_gram_plain(p, r, S)
+    else:
+        model_backward_f32(p, r, S)
     if pad:  # dq, dgate out
         for x in ("dq",) + (("dgate",) if p.epilogue else ()):
             model_copy_rows(r, "padded " + x, S[x], "caller " + x, tok * ub, pb, ub, ub, tok)
@@ -836,7 +902,10 @@ def model_backward(p: Prob) -> Report:
         if p.L:
             for x in ("k_text", "v_text"):
                 model_copy_rows(r, "caller " + x, trows * ub, "padded " + x, S[x], ub, pb, ub, trows)
-    model_backward_gram(p, r, S)
+    if p.bf16:
+        model_backward_gram(p, r, S)
+    else:
+        model_gram_bwd_f32(p, r, S)
     if pad:  # dk, dv (and the text's) out
         for x in ("dk", "dv"):
             model_copy_rows(r, "padded " + x, S[x], "caller " + x, tok * ub, pb, ub, ub, tok)

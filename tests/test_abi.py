@@ -75,7 +75,7 @@ def test_bad_eps_and_unsupported_widths():
 def test_widths_between_the_built_ones():
     """d = 48, 80, 96, 112: the forward and backward passes run them
     (zero-padded to the next built width, the padded copies in their
-    workspaces); the prep and the adjacent maps refuse them."""
+    workspaces), the adjacent maps at the width itself; the prep refuses them."""
     lib = bd.lib()
     for w, D in ((48, 64), (80, 128), (96, 128), (112, 128)):
         d = good(d=w)
@@ -91,7 +91,9 @@ def test_widths_between_the_built_ones():
         bw, bw_built = bd.backward_workspace_bytes(d), bd.backward_workspace_bytes(good(d=D))
         assert bw >= bw_built + 7 * x
         assert bd.backward_layout(d).d_out == bd.backward_layout(good(d=D)).d_out
-        assert lib.vdn_vda_gates_workspace_bytes(ctypes.byref(d), 3072) == 0
+        # the adjacent maps run at the caller's width (their workspace: the frames' token sums)
+        assert lib.vdn_vda_gates_workspace_bytes(ctypes.byref(d), 3072) == \
+            lib.vdn_vda_gates_workspace_bytes(ctypes.byref(good()), 3072)
         P = [ctypes.c_void_p(A16 + (1 << 34) * i) for i in range(10)]
         assert lib.vdn_vda_prepare(ctypes.byref(d), *P, None) == bd.VDN_ERR_UNSUPPORTED
         # the backward's argument checks pass (no GPU here: the launch fails)
@@ -290,7 +292,11 @@ def test_backward_readout_argument_errors_before_launch():
     assert call(ws=0) == bd.VDN_ERR_WORKSPACE
     assert call(dy=base["dy"] + 8) == bd.VDN_ERR_ALIGNMENT
     assert call(ws=base["ws"] + 16) == bd.VDN_ERR_ALIGNMENT
-    assert call(d=good(dtype="f32")) == bd.VDN_ERR_UNSUPPORTED
+    # float32: do is kept in float32, so the workspace sized for bfloat16 is short
+    f32 = good(dtype="f32")
+    assert bd.backward_workspace_bytes(f32) > bw
+    assert call(d=f32, fwb=bd.workspace_bytes(f32)) == bd.VDN_ERR_WORKSPACE
+    assert call(d=f32, q=0) == bd.VDN_ERR_INVALID_ARG
     assert call(d=good(flags=bd.VDN_VDA_QUERY_L2)) == bd.VDN_ERR_UNSUPPORTED   # the raw query needs the epilogue
     # the gain's gradient: 4-byte aligned, and only with the epilogue
     assert call(drms=base["drms"] + 2) == bd.VDN_ERR_ALIGNMENT
@@ -325,7 +331,11 @@ def test_backward_gram_argument_errors_before_launch():
     assert call(dk=base["dk"] + 8) == bd.VDN_ERR_ALIGNMENT
     assert call(dbeta=base["dbeta"] + 1) == bd.VDN_ERR_ALIGNMENT
     assert call(ws=base["ws"] + 16) == bd.VDN_ERR_ALIGNMENT
-    assert call(d=good(dtype="f32")) == bd.VDN_ERR_UNSUPPORTED
+    # float32: 4-byte beta and dbeta, and the arguments pass to the launch
+    # (which fails here, with no GPU)
+    f32, bw32 = good(dtype="f32"), bd.backward_workspace_bytes(good(dtype="f32"))
+    assert call(d=f32, bwb=bw32, dbeta=base["dbeta"] + 2) == bd.VDN_ERR_ALIGNMENT
+    assert call(d=f32, bwb=bw32) == bd.VDN_ERR_HIP
     # neither the decay bridge nor the raw query's normalisation reaches this
     # stage: with either flag the arguments are still checked
     assert call(d=good(flags=bd.VDN_VDA_EPILOGUE | bd.VDN_VDA_DECAY_BRIDGE), k=0) == bd.VDN_ERR_INVALID_ARG

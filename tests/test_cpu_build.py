@@ -285,6 +285,29 @@ def test_padded_width_backward_matches_oracle(lib, name):
     assert not bad, bad
 
 
+import test_gpu_training_f32 as GT  # noqa: E402
+
+
+@pytest.mark.parametrize("name", list(GT.CASES))
+def test_f32_backward_matches_oracle(lib, name):
+    case = GT.CASES[name]
+    w, epi, bridge, ql2 = case["w"], case.get("epilogue", True), case.get("bridge", False), case.get("query_l2", False)
+    x = synth.make_inputs(w)
+    if ql2:
+        GT.raw_queries(x, w)
+    dy = GT._dy(w)
+    gain = np.random.default_rng(5).uniform(0.5, 1.5, w.d) if case.get("gain") else None
+    _, fws, _ = S.run_forward(lib, x, w, epilogue=epi, rms_weight=gain, bridge=bridge, query_l2=ql2)
+    got, _, _ = S.run_backward(lib, x, w, dy, fws, epilogue=epi, rms_weight=gain, bridge=bridge, query_l2=ql2,
+                               gain=epi)
+    got = {k: S.to_f64(v) for k, v in got.items() if v is not None}
+    errs = GW.backward_errors(got, GT.reference(x, w, dy, epi, gain, bridge, ql2), w, epi)
+    bad = {k: v for k, v in errs.items() if not v <= G.TOL["f32"]}
+    assert not bad, bad
+    # records are read in every case, so the frames' keys reach the output
+    assert np.abs(got["dk"]).max() > 0
+
+
 # ---------------------------------------------------------------------------
 # the backward pass: the three stages against the oracle's gradients, with the
 # checks of the GPU backward tests
@@ -389,9 +412,12 @@ import test_gpu_adjacent as GA  # noqa: E402
 from oracle import vda_adjacent as adj  # noqa: E402
 
 
-@pytest.mark.parametrize("name", list(GA.CASES))
+ADJ = dict(GA.CASES, **GW.ADJ_CASES)
+
+
+@pytest.mark.parametrize("name", list(ADJ))
 def test_gates_match_oracle(lib, name):
-    w, dm = GA.CASES[name]
+    w, dm = ADJ[name]
     p = synth.make_adjacent_inputs(w, dm)
     gate, beta, alpha = S.run_gates(lib, p, w, dm)
     wg = GA._f64(p["w_gb"])
@@ -403,9 +429,9 @@ def test_gates_match_oracle(lib, name):
 
 
 @pytest.mark.parametrize("mode", ["y_in", "in_place", "no_y_in"])
-@pytest.mark.parametrize("name", list(GA.CASES))
+@pytest.mark.parametrize("name", list(ADJ))
 def test_out_proj_matches_oracle(lib, name, mode):
-    w, dm = GA.CASES[name]
+    w, dm = ADJ[name]
     p = synth.make_adjacent_inputs(w, dm)
     y = S.run_out_proj(lib, p, w, mode)
     ref = adj.out_proj(GA._f64(p["o"]), GA._f64(p["w_o"]), None if mode == "no_y_in" else GA._f64(p["y_in"]))

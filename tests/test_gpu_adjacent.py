@@ -53,11 +53,10 @@ def _slices(a):
     return a.reshape(a.shape[0], a.shape[1], a.shape[2], 1, -1)
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_gates(name):
+def check_gates(w, dm, name):
+    """vdn_vda_gates on the case's seeded inputs against the oracle."""
     import torch
     from frame_wise_delta_02_amd import binding as bd
-    w, dm = CASES[name]
     p = synth.make_adjacent_inputs(w, dm)
     gate, beta, alpha = bd.gates(_dev(p["x"]), _dev(p["w_gb"]), _dev(p["w_alpha"]), heads=w.H, d=w.d,
                                  grid=(w.grid_h, w.grid_w))
@@ -72,11 +71,14 @@ def test_gates(name):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("mode", ["y_in", "in_place", "no_y_in"])
-def test_out_proj(name, mode):
+def test_gates(name):
+    check_gates(*CASES[name], name)
+
+
+def check_out_proj(w, dm, mode, name):
+    """vdn_vda_out_proj on the case's seeded inputs against the oracle."""
     import torch
     from frame_wise_delta_02_amd import binding as bd
-    w, dm = CASES[name]
     p = synth.make_adjacent_inputs(w, dm)
     o, wo, yin = _dev(p["o"]), _dev(p["w_o"]), _dev(p["y_in"])
     if mode == "y_in":
@@ -91,6 +93,12 @@ def test_out_proj(name, mode):
     err = G.slice_rel_err(_slices(G.to_host_f64(y)), _slices(ref))
     G.say(f"{name} {mode}: err(y)={err:.3e}")
     assert err <= 2e-2
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("mode", ["y_in", "in_place", "no_y_in"])
+def test_out_proj(name, mode):
+    check_out_proj(*CASES[name], mode, name)
 
 
 def test_768p_sampled():

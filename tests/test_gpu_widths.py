@@ -5,7 +5,9 @@ the inputs and copies the results' d channels back.  The forward's outputs
 and the backward's input gradients (the gain's included) against the oracle,
 which runs at the caller's width, with the tolerances of the other parity
 tests: max relative error per (frame, head) slice (per vector for dalpha and
-dgamma) <= 2e-2 for bfloat16 inputs, <= 1e-3 for float32."""
+dgamma) <= 2e-2 for bfloat16 inputs, <= 1e-3 for float32.  The adjacent maps,
+plain products over a token's H d channels, run at the caller's width itself
+and are checked as at the built widths."""
 
 import numpy as np
 import pytest
@@ -156,3 +158,22 @@ def test_padded_width_backward(name):
     G.say(f"{name}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= G.TOL[w.dtype]}
     assert not bad, bad
+
+
+# the adjacent maps: (workload, model width)
+ADJ_CASES = {
+    "adj_d48": (_BF.scaled(name="adj_d48", B=1, T=3, grid_h=5, grid_w=7, H=3, d=48, L=0), 200),
+    "adj_d112": (_BF.scaled(name="adj_d112", B=2, T=4, grid_h=6, grid_w=11, H=2, d=112, L=0), 320),
+}
+
+
+@pytest.mark.parametrize("name", list(ADJ_CASES))
+def test_padded_width_gates(name):
+    import test_gpu_adjacent as GA
+    GA.check_gates(*ADJ_CASES[name], name)
+
+
+@pytest.mark.parametrize("name", list(ADJ_CASES))
+def test_padded_width_out_proj(name):
+    import test_gpu_adjacent as GA
+    GA.check_out_proj(*ADJ_CASES[name], "y_in", name)

@@ -85,8 +85,11 @@ def _bwd_shapes():
     for h in (3, 8):
         out.append((f"768p_h{h}", synth.WORKLOADS["768p_bf16"].scaled(name="h", H=h), {}))
     import test_gpu_widths as W  # widths between the built ones
-    out += [(n, c["w"], dict(epilogue=c.get("epilogue", True), bridge=c.get("bridge", False), gamma=c.get("gain", False)))
-            for n, c in W.BWD_CASES.items()]
+    import test_gpu_training_f32 as F  # float32 inputs
+    for cases in (W.BWD_CASES, F.CASES):
+        out += [(n, c["w"], dict(epilogue=c.get("epilogue", True), bridge=c.get("bridge", False),
+                                 gamma=c.get("gain", False))) for n, c in cases.items()]
+    out.append(("stress_f32", synth.WORKLOADS["stress_f32"], {}))
     return out
 
 
@@ -124,6 +127,20 @@ def test_padded_copies_are_modelled():
     KB.model_copy_rows(r3, "padded out", S["out"], "caller out", p.B * p.T * p.U * p.H * 48 * 2 - 2, 128, 96, 96,
                        p.B * p.T * p.U * p.H)
     assert any("caller out" in e for e in r3.errors)
+
+
+def test_float32_backward_model_catches_planted_mistakes():
+    """The float32 stages' buffers one element short are reported."""
+    import test_gpu_training_f32 as F
+    p = _prob(F.CASES["stress_d128_bridge"]["w"], bridge=True, dgain=True, gamma=True)
+    assert not p.bf16
+    for part in ("rstates_t", "dout", "dsq", "dq", "dgate", "dk", "dv", "dbeta", "dbeta_text", "dA", "gain"):
+        S = KB.bwd_sizes(p)
+        S[part] -= 4
+        r = KB.Report()
+        KB.model_backward_f32(p, r, S)
+        KB.model_gram_bwd_f32(p, r, S)
+        assert any(part in e for e in r.errors), (part, r.errors[:3])
 
 
 def test_backward_slot_sizes_match_the_layout():
@@ -168,6 +185,8 @@ def _proj_shapes():
     out.append(("768p", base, base.H * base.d))
     out.append(("layer", base.scaled(name="layer", B=1, T=11, grid_h=4, grid_w=6, H=2, d=64, L=8), 160))
     out.append(("graphs", base.scaled(name="graphs", H=2, T=12, grid_h=5, grid_w=7, L=8), 192))
+    import test_gpu_widths as W  # the maps run at the caller's width, whatever it is
+    out += [(n, w, dm) for n, (w, dm) in W.ADJ_CASES.items()]
     return out
 
 
@@ -176,7 +195,8 @@ PROJ_SHAPES = _proj_shapes()
 
 @pytest.mark.parametrize("name,w,dm", PROJ_SHAPES, ids=[s[0] for s in PROJ_SHAPES])
 def test_adjacent_maps_stay_in_bounds(name, w, dm):
-    p = _prob(w)
+    # plain products over H d channels: the caller's width, not a built one
+    p = KB.Prob(B=w.B, H=w.H, T=w.T, gh=w.grid_h, gw=w.grid_w, D=w.d, L=w.L, C=w.chunk, bf16=True)
     for r in (KB.model_gates(p, dm), KB.model_out_proj(p, dm, True), KB.model_out_proj(p, dm, False)):
         assert not r.errors, (name, r.errors[:5])
         assert r.checked > 0
