@@ -647,3 +647,30 @@ def test_every_entry_point_has_no_race():
     for rc, out in _sweep(path, ["--tsan"], env):
         assert rc == 0 and "all entry points ran" in out, out[-6000:]
         assert "ThreadSanitizer" not in out, out[-6000:]
+
+
+# ---------------------------------------------------------------------------
+# the GPU suite's own Python on the host library (tests/cpu_build/gpu_suite_on_host.py)
+# ---------------------------------------------------------------------------
+ON_HOST = ["tests/test_gpu_rms_gain.py::test_gain_gradient[bwd_16]",
+           "tests/test_gpu_widths.py::test_padded_width_forward[d48_T1_bf16-frames]",
+           "tests/test_gpu_widths.py::test_padded_width_backward[bwd_d80_raw_bridge]",
+           "tests/test_gpu_widths.py::test_padded_width_gates[adj_d48]",
+           "tests/test_gpu_training_f32.py::test_backward_f32[tiny_f32_gain]",
+           "tests/test_gpu_backward.py::test_backward_readout[bwd_16]"]
+
+
+def test_gpu_test_code_runs_on_the_host_library():
+    """A few cases of each GPU test file run on the CPU build (the full
+    selection with VDA_CPU_BUILD_FULL=1: every case but the full-size ones)."""
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if os.environ.get("VDA_CPU_BUILD_FULL"):
+        args = ["tests/test_gpu_parity.py", "tests/test_gpu_backward.py", "tests/test_gpu_adjacent.py",
+                "tests/test_gpu_rms_gain.py", "tests/test_gpu_widths.py", "tests/test_gpu_training_f32.py",
+                "tests/test_zz_no_alloc.py", "-k", "not 768p and not long_prep and not stress and not workload_full"]
+    else:
+        args = ON_HOST
+    r = subprocess.run([sys.executable, "tests/cpu_build/gpu_suite_on_host.py", *args, "-m", "gpu"], cwd=root,
+                       capture_output=True, text=True, timeout=3600)
+    assert r.returncode == 0, r.stdout[-4000:] + r.stderr[-2000:]
