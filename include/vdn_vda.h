@@ -428,7 +428,9 @@ vdn_status vdn_vda_out_proj(const vdn_vda_desc* d, int32_t d_model, const void* 
  * benchmarks.  Same arguments, checks and results as vdn_vda_forward; in
  * addition it records events[0] on `stream` before its first kernel and
  * events[i] after stage i, i = 1..VDN_VDA_STAGES: frame statistics (the text
- * frame included), solve, scan, gather, readout.  The caller creates the
+ * frame included), solve, scan, gather, readout (at a width between the
+ * built ones the input copies fall in the first stage and the output's copy
+ * back in the last).  The caller creates the
  * n_events >= VDN_VDA_STAGES + 1 events (hipEventCreate); nothing is kept
  * after the call returns.  Errors: those of vdn_vda_forward, and
  * VDN_ERR_INVALID_ARG for a NULL events array, too few events or a NULL event.
