@@ -62,11 +62,15 @@ __device__ __forceinline__ float token_sum(float v) {
   return v;
 }
 
-template <int D, typename TIO>
+// DU: the caller's head width, D >= DU the power of two whose D / 8 lanes hold
+// one token's channels (DU < D for the widths between the built ones: the
+// lanes of channels DU .. D - 1 load zeros and store nothing).
+template <int D, typename TIO, int DU = D>
 __global__ __launch_bounds__(256) void prep_conv(const TIO* __restrict__ X, const float* __restrict__ ws,
                                                  const float* __restrict__ wt, TIO* __restrict__ Y,
                                                  int T, int gh, int gw, int H, int normalise,
                                                  float eps) {
+  constexpr bool MASK = DU != D;
   constexpr int CG = D / 8;     // channel groups (threads per token)
   constexpr int NX = 256 / CG;  // token runs per workgroup
   __shared__ float sw[D][32];   // per channel: 25 spatial taps, then 5 temporal taps
@@ -81,12 +85,16 @@ __global__ __launch_bounds__(256) void prep_conv(const TIO* __restrict__ X, cons
   const int tid = threadIdx.x;
   for (int i = tid; i < D * 30; i += 256) {
     const int c = i / 30, k = i % 30;
-    sw[c][k] = (k < 25) ? ws[((size_t)h * D + c) * 25 + k] : wt[((size_t)h * D + c) * 5 + (k - 25)];
+    if (MASK && c >= DU)
+      sw[c][k] = 0.f;
+    else
+      sw[c][k] = (k < 25) ? ws[((size_t)h * DU + c) * 25 + k] : wt[((size_t)h * DU + c) * 5 + (k - 25)];
   }
   __syncthreads();
 
   const int cg = tid % CG, xr = tid / CG;
   const int ch = cg * 8;
+  const bool live = !MASK || ch < DU;  // this lane's channels exist
   const size_t U = (size_t)gh * gw;
   for (int xb = 0; xb < gw; xb += NX * XPT) {
     const int x0 = xb + xr * XPT;
@@ -110,9 +118,9 @@ __global__ __launch_bounds__(256) void prep_conv(const TIO* __restrict__ X, cons
 #pragma unroll
         for (int j = 0; j < XPT + 4; ++j) {
           const int xx = x0 + j - 2;
-          if (xx >= 0 && xx < gw) {
+          if (live && xx >= 0 && xx < gw) {
             const size_t row = (((size_t)b * T + ti) * U + (size_t)yy * gw + xx) * H + h;
-            load8<D>(X + row * D + ch, in[j]);
+            load8<D>(X + row * DU + ch, in[j]);
           } else {
 #pragma unroll
             for (int c = 0; c < 8; ++c) in[j][c] = 0.f;
@@ -150,9 +158,9 @@ __global__ __launch_bounds__(256) void prep_conv(const TIO* __restrict__ X, cons
         for (int c = 0; c < 8; ++c) out[i][c] *= r;
       }
       const int x = x0 + i;
-      if (x < gw) {
+      if (live && x < gw) {
         const size_t row = (((size_t)b * T + t) * U + (size_t)y * gw + x) * H + h;
-        store8(Y + row * D + ch, out[i]);
+        store8(Y + row * DU + ch, out[i]);
       }
     }
   }
@@ -354,17 +362,19 @@ __global__ __launch_bounds__(64 * PNW) void prep_conv_tile(const uint16_t* __res
   }
 }
 
-// q_hat = q / sqrt(|q|^2 + eps) per (token, head); one thread per 8 channels.
-template <int D, typename TIO>
+// q_hat = q / sqrt(|q|^2 + eps) per (token, head); one thread per 8 channels
+// (D / 8 threads per row, those past the caller's DU channels idle).
+template <int D, typename TIO, int DU = D>
 __global__ __launch_bounds__(256) void prep_l2(const TIO* __restrict__ X, TIO* __restrict__ Y,
                                                size_t rows, float eps) {
+  constexpr bool MASK = DU != D;
   const size_t g = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t row = g / (D / 8);
   const int ch = (int)(g % (D / 8)) * 8;
-  const bool ok = row < rows;
+  const bool ok = row < rows && (!MASK || ch < DU);
   float x[8];
   if (ok) {
-    load8<D>(X + row * D + ch, x);
+    load8<D>(X + row * DU + ch, x);
   } else {
 #pragma unroll
     for (int c = 0; c < 8; ++c) x[c] = 0.f;
@@ -376,15 +386,15 @@ __global__ __launch_bounds__(256) void prep_l2(const TIO* __restrict__ X, TIO* _
   const float r = 1.f / __builtin_sqrtf(ss + eps);
 #pragma unroll
   for (int c = 0; c < 8; ++c) x[c] *= r;
-  if (ok) store8(Y + row * D + ch, x);
+  if (ok) store8(Y + row * DU + ch, x);
 }
 
-template <int D, typename TIO>
+template <int D, typename TIO, int DU = D>
 hipError_t launch_prep_t(const Problem& p, int gh, int gw, const void* q, const void* k,
                          const void* v, const float* wk_s, const float* wk_t, const float* wv_s,
                          const float* wv_t, void* q_hat, void* k_hat, void* v_hat, hipStream_t s) {
   hipError_t e = hipSuccess;
-  if constexpr (D == 128 && sizeof(TIO) == 2) {
+  if constexpr (D == 128 && DU == D && sizeof(TIO) == 2) {
     const unsigned tiles = (unsigned)(((gh + PTY - 1) / PTY) * ((gw + PTX - 1) / PTX));
     const unsigned grid = (unsigned)(p.B * p.H) * tiles;
     hipLaunchKernelGGL(prep_conv_tile<D>, dim3(grid), dim3(64 * PNW), 0, s, static_cast<const uint16_t*>(k),
@@ -397,11 +407,11 @@ hipError_t launch_prep_t(const Problem& p, int gh, int gw, const void* q, const 
     if (e != hipSuccess) return e;
   } else {
     const unsigned grid = (unsigned)(p.B * p.T * p.H * gh);
-    hipLaunchKernelGGL((prep_conv<D, TIO>), dim3(grid), dim3(256), 0, s, static_cast<const TIO*>(k),
+    hipLaunchKernelGGL((prep_conv<D, TIO, DU>), dim3(grid), dim3(256), 0, s, static_cast<const TIO*>(k),
                        wk_s, wk_t, static_cast<TIO*>(k_hat), p.T, gh, gw, p.H, 1, p.l2_eps);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prep_conv<D, TIO>), dim3(grid), dim3(256), 0, s, static_cast<const TIO*>(v),
+    hipLaunchKernelGGL((prep_conv<D, TIO, DU>), dim3(grid), dim3(256), 0, s, static_cast<const TIO*>(v),
                        wv_s, wv_t, static_cast<TIO*>(v_hat), p.T, gh, gw, p.H, 0, p.l2_eps);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -409,18 +419,18 @@ hipError_t launch_prep_t(const Problem& p, int gh, int gw, const void* q, const 
   if (p.qnorm) return hipSuccess;  // the readout normalises the query itself
   const size_t rows = (size_t)p.B * p.T * p.U * p.H;
   const size_t threads = rows * (D / 8);
-  hipLaunchKernelGGL((prep_l2<D, TIO>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL((prep_l2<D, TIO, DU>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                      static_cast<const TIO*>(q), static_cast<TIO*>(q_hat), rows, p.l2_eps);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int DU = D>
 hipError_t launch_prep_d(const Problem& p, int gh, int gw, const void* q, const void* k,
                          const void* v, const float* wk_s, const float* wk_t, const float* wv_s,
                          const float* wv_t, void* q_hat, void* k_hat, void* v_hat, hipStream_t s) {
   if (p.bf16)
-    return launch_prep_t<D, uint16_t>(p, gh, gw, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat, s);
-  return launch_prep_t<D, float>(p, gh, gw, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat, s);
+    return launch_prep_t<D, uint16_t, DU>(p, gh, gw, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat, s);
+  return launch_prep_t<D, float, DU>(p, gh, gw, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat, s);
 }
 
 }  // namespace
@@ -428,10 +438,16 @@ hipError_t launch_prep_d(const Problem& p, int gh, int gw, const void* q, const 
 hipError_t launch_prep(const Problem& p, int gh, int gw, const void* q, const void* k,
                        const void* v, const float* wk_s, const float* wk_t, const float* wv_s,
                        const float* wv_t, void* q_hat, void* k_hat, void* v_hat, hipStream_t s) {
-  switch (p.D) {
+  // the prep works on the caller's tensors at the caller's width: a width
+  // between the built ones runs the generic kernels with its last lanes idle
+  switch (p.Du) {
     case 16: return launch_prep_d<16>(p, gh, gw, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat, s);
     case 32: return launch_prep_d<32>(p, gh, gw, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat, s);
+    case 48: return launch_prep_d<64, 48>(p, gh, gw, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat, s);
     case 64: return launch_prep_d<64>(p, gh, gw, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat, s);
+    case 80: return launch_prep_d<128, 80>(p, gh, gw, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat, s);
+    case 96: return launch_prep_d<128, 96>(p, gh, gw, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat, s);
+    case 112: return launch_prep_d<128, 112>(p, gh, gw, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat, s);
     case 128: return launch_prep_d<128>(p, gh, gw, q, k, v, wk_s, wk_t, wv_s, wv_t, q_hat, k_hat, v_hat, s);
     default: return hipErrorInvalidValue;
   }

@@ -142,13 +142,6 @@ vdn_status check(const vdn_vda_desc* d) {
   return VDN_OK;
 }
 
-// The entry points other than the forward pass run at the built widths only.
-vdn_status check_native(const vdn_vda_desc* d) {
-  const vdn_status st = check(d);
-  if (st != VDN_OK) return st;
-  return padded_width(d->d_k) == d->d_k ? VDN_OK : VDN_ERR_UNSUPPORTED;
-}
-
 Problem problem(const vdn_vda_desc* d) {
   Problem p;
   p.B = d->B;
@@ -464,7 +457,7 @@ vdn_status vdn_vda_prepare(const vdn_vda_desc* d, const void* q, const void* k, 
                            const float* wk_s, const float* wk_t, const float* wv_s,
                            const float* wv_t, void* q_hat, void* k_hat, void* v_hat,
                            hipStream_t stream) {
-  const vdn_status st = check_native(d);
+  const vdn_status st = check(d);
   if (st != VDN_OK) return st;
   const Problem p = problem(d);
   // under VDN_VDA_QUERY_L2 the query is normalised by the forward pass instead
@@ -477,7 +470,7 @@ vdn_status vdn_vda_prepare(const vdn_vda_desc* d, const void* q, const void* k, 
     if (!aligned(ptrs[i], 16)) return VDN_ERR_ALIGNMENT;
   // outputs are written while inputs are still read: no byte may be shared
   const Sizes z = sizes_of(d);
-  const size_t ws_ = (size_t)p.H * p.D * 25 * 4, wt_ = (size_t)p.H * p.D * 5 * 4;
+  const size_t ws_ = (size_t)p.H * p.Du * 25 * 4, wt_ = (size_t)p.H * p.Du * 5 * 4;
   const Span ins[] = {{k, z.x}, {v, z.x}, {q, z.x}, {wk_s, ws_}, {wk_t, wt_}, {wv_s, ws_}, {wv_t, wt_}};
   const Span outs[] = {{k_hat, z.x}, {v_hat, z.x}, {q_hat, z.x}};
   if (any_overlap(outs, 3, ins, 7)) return VDN_ERR_INVALID_ARG;
@@ -831,8 +824,7 @@ const char* vdn_vda_status_string(vdn_status s) {
     case VDN_OK: return "VDN_OK";
     case VDN_ERR_INVALID_ARG: return "VDN_ERR_INVALID_ARG: bad descriptor, size, NULL pointer or overlapping buffers";
     case VDN_ERR_UNSUPPORTED:
-      return "VDN_ERR_UNSUPPORTED: valid request not implemented (d_k != d_v; head widths other than "
-             "16, 32, 64, 128 in the prep; float32 in the backward pass and the adjacent maps; "
+      return "VDN_ERR_UNSUPPORTED: valid request not implemented (d_k != d_v; float32 in the adjacent maps; "
              "the query norm's backward without the epilogue)";
     case VDN_ERR_WORKSPACE: return "VDN_ERR_WORKSPACE: workspace missing or too small";
     case VDN_ERR_ALIGNMENT: return "VDN_ERR_ALIGNMENT: pointer misaligned";

@@ -170,9 +170,9 @@ typedef struct {
  * gives the same RMSNorm over the d true channels).  The backward pass takes
  * them the same way: it reads the forward's padded copies from the forward's
  * workspace, pads dy, k and v in its own, and copies every gradient's d
- * channels back (the gain's gradient scaled by sqrt(d / D)).  The adjacent
- * maps (plain products over a token's H d channels) run at the width itself.
- * vdn_vda_prepare returns VDN_ERR_UNSUPPORTED for them. */
+ * channels back (the gain's gradient scaled by sqrt(d / D)).  The prep (a
+ * per-channel convolution and per-token norms) and the adjacent maps (plain
+ * products over a token's H d channels) run at the width itself. */
 vdn_status vdn_vda_validate(const vdn_vda_desc* d);
 
 /* Workspace bytes vdn_vda_forward needs for `d`; 0 if `d` is invalid. */
@@ -195,7 +195,7 @@ vdn_status vdn_vda_workspace_layout(const vdn_vda_desc* d, vdn_vda_layout* out);
  * With VDN_VDA_QUERY_L2 in d->flags q and q_hat are ignored (may be NULL) and
  * the forward pass normalises the query instead.
  * Errors: VDN_ERR_INVALID_ARG (descriptor, NULL pointer), VDN_ERR_UNSUPPORTED
- * (a head width other than 16, 32, 64, 128), VDN_ERR_ALIGNMENT,
+ * (d_k != d_v), VDN_ERR_ALIGNMENT,
  * VDN_ERR_HIP.
  */
 vdn_status vdn_vda_prepare(const vdn_vda_desc* d,

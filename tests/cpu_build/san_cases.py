@@ -144,7 +144,8 @@ def cases(full, tsan=False):
     for name, kw in (("prep_small_bf16", dict(H=2, T=5, grid_h=6, grid_w=10, L=8)),
                      ("prep_small_f32", dict(H=2, T=5, grid_h=6, grid_w=10, L=8, dtype="f32")),
                      ("prep_T1_ragged", P.PREP_EDGE["prep_T1_ragged"]),
-                     ("prep_d64", dict(H=2, T=6, grid_h=5, grid_w=7, L=4, d=64))):
+                     ("prep_d64", dict(H=2, T=6, grid_h=5, grid_w=7, L=4, d=64)),
+                     ("prep_d48", GW.PREP_CASES["prep_d48_bf16"]), ("prep_d80_f32", GW.PREP_CASES["prep_d80_f32"])):
         out.append((f"prepare + fused query {name}", prepare(name, kw)))
 
     def backward(name):

@@ -426,9 +426,13 @@ def model_readout(p: Prob, r: Report, S=None, q="q", out="out", rstates="rstates
 
 
 def model_prep(p: Prob, r: Report):
-    S = sizes(p)
-    D, H, T, gh, gw = p.D, p.H, p.T, p.gh, p.gw
+    """The prep runs on the caller's tensors at the caller's width (Du where it
+    lies between the built ones: the generic kernel, its last lanes idle)."""
+    D = p.Du or p.D
+    H, T, gh, gw = p.H, p.T, p.gh, p.gw
     U = gh * gw
+    tok = p.B * T * U * H
+    S = dict(q=tok * D * p.esz, k=tok * D * p.esz, v=tok * D * p.esz, wk_s=H * D * 25 * 4, wk_t=H * D * 5 * 4)
     tokstride = H * D
     if p.bf16 and D == 128:
         PTY, PTX = 8, 12

@@ -75,7 +75,7 @@ def test_bad_eps_and_unsupported_widths():
 def test_widths_between_the_built_ones():
     """d = 48, 80, 96, 112: the forward and backward passes run them
     (zero-padded to the next built width, the padded copies in their
-    workspaces), the adjacent maps at the width itself; the prep refuses them."""
+    workspaces), the prep and the adjacent maps at the width itself."""
     lib = bd.lib()
     for w, D in ((48, 64), (80, 128), (96, 128), (112, 128)):
         d = good(d=w)
@@ -95,7 +95,8 @@ def test_widths_between_the_built_ones():
         assert lib.vdn_vda_gates_workspace_bytes(ctypes.byref(d), 3072) == \
             lib.vdn_vda_gates_workspace_bytes(ctypes.byref(good()), 3072)
         P = [ctypes.c_void_p(A16 + (1 << 34) * i) for i in range(10)]
-        assert lib.vdn_vda_prepare(ctypes.byref(d), *P, None) == bd.VDN_ERR_UNSUPPORTED
+        # the prep runs at the width itself (its arguments pass; no GPU here)
+        assert lib.vdn_vda_prepare(ctypes.byref(d), *P, None) == bd.VDN_ERR_HIP
         # the backward's argument checks pass (no GPU here: the launch fails)
         fw = bd.workspace_bytes(d)
         assert lib.vdn_vda_backward_readout(ctypes.byref(d), *P[:6], fw, P[6], P[7], None, P[8], bw,

@@ -37,6 +37,7 @@ import pytest
 import oracle
 import gpu_harness as G
 import test_gpu_parity as P
+import test_gpu_widths as GW
 from cpu_build import build as CB
 from cpu_build import sim as S
 from frame_wise_delta_02_amd import synth
@@ -184,6 +185,7 @@ PREP = {
     "prep_T2_ragged": P.PREP_EDGE["prep_T2_ragged"],
     "prep_H8_tiles": dict(H=8, T=4, grid_h=9, grid_w=13, L=4),
 }
+PREP.update(GW.PREP_CASES)  # widths between the built ones
 
 
 @pytest.mark.parametrize("name", list(PREP))
@@ -247,8 +249,6 @@ def test_values_beyond_the_half_range(lib):
 # head widths between the built ones (zero-padded to the next), with the
 # checks of the GPU width tests
 # ---------------------------------------------------------------------------
-import test_gpu_widths as GW  # noqa: E402
-
 WIDTHS = [n for n in GW.CASES if n != "d112_768p_frame"]
 
 

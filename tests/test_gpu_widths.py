@@ -7,7 +7,8 @@ which runs at the caller's width, with the tolerances of the other parity
 tests: max relative error per (frame, head) slice (per vector for dalpha and
 dgamma) <= 2e-2 for bfloat16 inputs, <= 1e-3 for float32.  The adjacent maps,
 plain products over a token's H d channels, run at the caller's width itself
-and are checked as at the built widths."""
+and are checked as at the built widths; so does the prep (vdn_vda_prepare),
+whose convolution is per channel: its lanes past the caller's channels idle."""
 
 import numpy as np
 import pytest
@@ -177,3 +178,17 @@ def test_padded_width_gates(name):
 def test_padded_width_out_proj(name):
     import test_gpu_adjacent as GA
     GA.check_out_proj(*ADJ_CASES[name], "y_in", name)
+
+
+# the prep (depthwise convolutions, SiLU, L2 norms) at the caller's width
+PREP_CASES = {
+    "prep_d48_bf16": dict(d=48, H=2, T=7, grid_h=6, grid_w=10, L=4),
+    "prep_d112_bf16": dict(d=112, H=2, T=6, grid_h=9, grid_w=13, L=4),
+    "prep_d80_f32": dict(d=80, H=2, T=5, grid_h=5, grid_w=7, L=4, dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", list(PREP_CASES))
+def test_padded_width_prepare(name):
+    w = synth.WORKLOADS["long_prep_bf16"].scaled(name=name, **PREP_CASES[name])
+    P._prep_case(w, heads=list(range(w.H)))

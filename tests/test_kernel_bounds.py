@@ -28,6 +28,7 @@ def _shapes():
         out.append((f"768p_h{h}", synth.WORKLOADS["768p_bf16"].scaled(name="h", H=h), False))
     import test_gpu_widths as W  # widths between the built ones
     out += [(n, w, False) for n, w in W.CASES.items()]
+    out += [(n, base.scaled(name=n, **kw), True) for n, kw in W.PREP_CASES.items()]
     return out
 
 
