@@ -238,7 +238,7 @@ def cases(full, tsan=False):
 # take about one), for sharing the sweep evenly between processes
 COST = (("768p frame", 24.0), ("bit patterns ragged_bf16_128", 10.0), ("no_text_bf16", 6.5),
         ("U1_bf16_128", 3.8), ("ragged_bf16_128", 3.0), ("bwd_64_ragged", 3.4), ("bwd_B2", 10.0),
-        ("ragged_f32_128", 2.0))
+        ("ragged_f32_128", 2.0), ("bwd_d80", 12.0), ("bwd_128_gain", 8.0), ("bwd_d112", 8.0), ("bwd_d96", 6.0))
 
 
 def _cost(label):
