@@ -31,9 +31,11 @@ from cpu_build import sim as S  # noqa: E402
 _orig = {}
 
 
-def _aligned(t):
-    """The same values in a 256-byte aligned buffer."""
-    if t.numel() == 0 or t.data_ptr() % 256 == 0:
+def _aligned(t, copy=False):
+    """The same values in a 256-byte aligned buffer (always a new one with copy,
+    as a transfer to the device gives: the host array stays untouched when the
+    library writes the copy)."""
+    if t.numel() == 0 or (t.data_ptr() % 256 == 0 and not copy):
         return t
     es = t.element_size()
     raw = _orig["empty"](t.numel() + 256 // es + 1, dtype=t.dtype)
@@ -59,13 +61,14 @@ def install():
     to = torch.Tensor.to
 
     def to_host(self, *a, **k):
+        moves = any(str(x).startswith("cuda") for x in a) or str(k.get("device", "")).startswith("cuda")
         a = tuple(_host(x) for x in a)
         if "device" in k:
             k["device"] = _host(k["device"])
-        return _aligned(to(self, *a, **k).contiguous())
+        return _aligned(to(self, *a, **k).contiguous(), copy=moves)
 
     torch.Tensor.to = to_host
-    torch.Tensor.cuda = lambda self, *a, **k: _aligned(self.contiguous())
+    torch.Tensor.cuda = lambda self, *a, **k: _aligned(self.contiguous(), copy=True)
     torch.cuda.synchronize = lambda *a, **k: None
     for name in ("empty", "zeros", "ones", "full", "empty_like", "zeros_like", "full_like", "from_numpy"):
         f = _orig[name] = getattr(torch, name)
